@@ -1,0 +1,190 @@
+"""Seeded synthetic inputs for the Qwen3-0.6B-shaped KV-cache decoder.
+
+This module only draws numbers: weights, prompt ids, audio embedding rows and
+forced token streams. It holds none of the decoder's arithmetic, so both the
+CPU oracle (through the tests) and the HIP path consume exactly the same bits.
+
+Shapes follow the decoder described on the audio.cpp "Fun-ASR-Nano Native
+Runtime Implementation Plan" page (Task 1 Step 1 and Task 6 Step 4: hidden 1024,
+FFN 3072, 28 layers, 16 query / 8 KV heads, head_dim 128, vocab 151936,
+RoPE theta 1e6, tied embeddings) and on the transcribe.cpp "Forward map -
+funasr_nano" page (LLM decoder table: per-head Q/K-RMSNorm, packed gate_up).
+No checkpoint exists here, so weights are random: matrices 0.02*N(0,1), norm
+gains 1 + 0.02*N(0,1), drawn in one fixed tensor order.
+
+RNG contract: numpy Generator(PCG64(SeedSequence([seed_id, stream]))).
+stream 0 = weights, 1 = prompt ids, 2 = audio rows, 10+b = forced stream of
+branch b. The 0.6B workloads share one weight set (seed_id 2).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, List, Optional
+
+import numpy as np
+
+# Canonical per-layer tensor order (also the order of the C-ABI weight table).
+LAYER_TENSORS = (
+    "in_norm", "wq", "wk", "wv", "q_norm", "k_norm",
+    "wo", "post_norm", "w_gate", "w_up", "w_down",
+)
+NORM_TENSORS = ("in_norm", "q_norm", "k_norm", "post_norm")
+
+
+@dataclasses.dataclass(frozen=True)
+class ModelShape:
+    hidden: int
+    n_layer: int
+    n_q_head: int
+    n_kv_head: int
+    head_dim: int
+    ffn: int
+    vocab: int
+    rms_eps: float = 1e-6
+    rope_theta: float = 1e6
+    bf16: bool = True  # weights stored as bf16 (RNE); False = fp32
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    shape: ModelShape
+    weight_seed: int
+    prompt_seed: int
+    prompt_len: int
+    audio_begin: int
+    audio_len: int
+    n_decode: int
+    n_branch: int = 1  # >1: the prompt is prefilled once and cloned
+
+    @property
+    def max_ctx(self) -> int:
+        return self.prompt_len + self.n_decode
+
+
+TINY = ModelShape(hidden=128, n_layer=2, n_q_head=4, n_kv_head=2, head_dim=32,
+                  ffn=384, vocab=1024, bf16=False)
+QWEN3_0P6B = ModelShape(hidden=1024, n_layer=28, n_q_head=16, n_kv_head=8,
+                        head_dim=128, ffn=3072, vocab=151936, bf16=True)
+
+WORKLOADS: Dict[str, Workload] = {
+    # tiny fp32 decoder: 32-token prompt, rows 8..15 audio, 8 forced steps
+    "tiny": Workload("tiny", TINY, 1, 1, 32, 8, 8, 8),
+    # 0.6B: 48-token prompt, 23 audio rows, 64 greedy steps
+    "short": Workload("short", QWEN3_0P6B, 2, 2, 48, 8, 23, 64),
+    # 0.6B: 1024-token prompt, 750 audio rows, 256 steps
+    "long": Workload("long", QWEN3_0P6B, 2, 3, 1024, 8, 750, 256),
+    # 0.6B: 512-token shared prefix, 128 audio rows, 16 branches x 128 steps
+    "branch16": Workload("branch16", QWEN3_0P6B, 2, 4, 512, 8, 128, 128, n_branch=16),
+    # 0.6B: 8192-token prompt, 6000 audio rows, 64 steps
+    "prefill8k": Workload("prefill8k", QWEN3_0P6B, 2, 5, 8192, 8, 6000, 64),
+}
+
+
+def _rng(seed_id: int, stream: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed_id, stream])))
+
+
+def layer_shapes(s: ModelShape) -> Dict[str, tuple]:
+    H, D, F = s.hidden, s.head_dim, s.ffn
+    return {
+        "in_norm": (H,), "wq": (s.n_q_head * D, H), "wk": (s.n_kv_head * D, H),
+        "wv": (s.n_kv_head * D, H), "q_norm": (D,), "k_norm": (D,),
+        "wo": (H, s.n_q_head * D), "post_norm": (H,), "w_gate": (F, H),
+        "w_up": (F, H), "w_down": (H, F),
+    }
+
+
+def _round_bf16(a: np.ndarray):
+    """Round float32 -> bf16 (round to nearest even, torch on the CPU).
+    Returns (uint16 bit patterns, exact float32 upcast)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16), t.float().numpy()
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact upcast of bf16 bit patterns (uint16) to float32."""
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+class Weights:
+    """One weight set. ``f32[name]`` holds float32 arrays whose values are
+    exactly representable in the storage type; ``bits[name]`` holds the bf16
+    bit patterns (uint16) for bf16 shapes (None for fp32 shapes).
+    Names: "embed", "final_norm", and "L{i}.{tensor}" per layer."""
+
+    def __init__(self, shape: ModelShape, f32: Dict[str, np.ndarray],
+                 bits: Optional[Dict[str, np.ndarray]]):
+        self.shape = shape
+        self.f32 = f32
+        self.bits = bits
+
+    def names(self) -> List[str]:
+        out = ["embed"]
+        for i in range(self.shape.n_layer):
+            out += [f"L{i}.{t}" for t in LAYER_TENSORS]
+        out.append("final_norm")
+        return out
+
+    def layer(self, i: int) -> Dict[str, np.ndarray]:
+        return {t: self.f32[f"L{i}.{t}"] for t in LAYER_TENSORS}
+
+
+_WEIGHT_CACHE: Dict[tuple, Weights] = {}
+
+
+def make_weights(shape: ModelShape, seed_id: int, cache: bool = True) -> Weights:
+    """Draw one weight set in canonical order from stream 0."""
+    key = (shape, seed_id)
+    if cache and key in _WEIGHT_CACHE:
+        return _WEIGHT_CACHE[key]
+    rng = _rng(seed_id, 0)
+    scale = np.float32(0.02)
+    order = [("embed", (shape.vocab, shape.hidden), False)]
+    shp = layer_shapes(shape)
+    for i in range(shape.n_layer):
+        for t in LAYER_TENSORS:
+            order.append((f"L{i}.{t}", shp[t], t in NORM_TENSORS))
+    order.append(("final_norm", (shape.hidden,), True))
+    f32: Dict[str, np.ndarray] = {}
+    bits: Optional[Dict[str, np.ndarray]] = {} if shape.bf16 else None
+    for name, shp_, is_gain in order:
+        z = rng.standard_normal(shp_, dtype=np.float32)
+        w = (np.float32(1.0) + scale * z) if is_gain else (scale * z)
+        w = w.astype(np.float32, copy=False)
+        if shape.bf16:
+            bits[name], f32[name] = _round_bf16(w)
+        else:
+            f32[name] = w
+    out = Weights(shape, f32, bits)
+    if cache:
+        _WEIGHT_CACHE[key] = out
+    return out
+
+
+def make_prompt(w: Workload):
+    """Prompt ids (int32[T], uniform over the vocabulary, stream 1) and audio
+    rows (float32[La, H], N(0,1), stream 2) for span [audio_begin, +audio_len)."""
+    s = w.shape
+    ids = _rng(w.prompt_seed, 1).integers(0, s.vocab, size=w.prompt_len).astype(np.int32)
+    audio = _rng(w.prompt_seed, 2).standard_normal((w.audio_len, s.hidden), dtype=np.float32)
+    return ids, audio, w.audio_begin
+
+
+def branch_stream(w: Workload, b: int, n: Optional[int] = None) -> np.ndarray:
+    """Forced token stream of branch b (uniform ids, stream 10+b)."""
+    n = w.n_decode if n is None else n
+    return _rng(w.prompt_seed, 10 + b).integers(0, w.shape.vocab, size=n).astype(np.int32)
+
+
+def random_ids(seed: int, n: int, vocab: int) -> np.ndarray:
+    return _rng(1000 + seed, 1).integers(0, vocab, size=n).astype(np.int32)
+
+
+def random_rows(seed: int, n: int, width: int) -> np.ndarray:
+    return _rng(1000 + seed, 2).standard_normal((n, width), dtype=np.float32)
+
+
+def custom_shape(**kw) -> ModelShape:
+    return dataclasses.replace(TINY, **kw)
