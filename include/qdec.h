@@ -1,0 +1,181 @@
+/*
+ * qdec — Qwen3-0.6B-shaped causal decoder with a paged KV cache, for one
+ * AMD Instinct MI355X (gfx950). C ABI: plain pointers and sizes only.
+ *
+ * What the library computes (cited by page title and section/table):
+ *  - audio.cpp "Fun-ASR-Nano Native Runtime Implementation Plan", Task 6
+ *    Step 4: a Qwen causal decoder with hidden 1024, 28 layers, 16 query and
+ *    8 KV heads of dim 128, FFN 3072, RoPE theta 1e6, tied embeddings.
+ *  - transcribe.cpp "Forward map - funasr_nano", table "LLM decoder": token
+ *    embedding rows, audio rows overriding the span [fbank_beg, +L) of the
+ *    input embeddings, 28 blocks of rms_norm + GQA 16/8 + per-head Q/K-RMSNorm
+ *    + NeoX RoPE + SwiGLU, a final rms_norm and a tied LM head on the last
+ *    position; table "Generation / KV Path": prefill writes the KV cache for
+ *    [0, T), then one single-token step per position n_past >= T.
+ *  - NCNN "Qwen3ASR ncnn多平台移植", section 5: per step embed, RoPE at the
+ *    absolute position, attend over the history plus the current token,
+ *    append K/V, full-vocabulary logits, greedy pick; the context holding the
+ *    KV cache and position can be cloned to branch from one prefill.
+ *
+ * Arithmetic: weights bf16 (or fp32), activations, norms, softmax, logits and
+ * the KV cache fp32. RMSNorm is x / sqrt(mean(x^2) + eps) * g. Attention
+ * scale is 1/sqrt(head_dim); query head h reads KV head h / (n_q / n_kv).
+ * The greedy token is the lowest index among the maximal fp32 logits.
+ *
+ * Streams: every device operation is enqueued on the HIP stream given to
+ * qdec_create; outputs are valid once that stream has been synchronised.
+ * Calls are not thread-safe for one model; states of one model share its
+ * scratch memory and must be used from one host thread at a time.
+ *
+ * Errors: every int-returning call returns one of the QDEC_* codes below. On
+ * error nothing is enqueued and the state is unchanged; qdec_last_error()
+ * returns a description (thread-local, valid until the next call on the same
+ * thread).
+ */
+#ifndef QDEC_H
+#define QDEC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QDEC_OK 0
+#define QDEC_E_INVALID (-1)  /* null pointer, out-of-range argument, bad config */
+#define QDEC_E_POS (-2)      /* decode position != n_past */
+#define QDEC_E_CAPACITY (-3) /* position or prompt beyond the state's max_ctx */
+#define QDEC_E_STATE (-4)    /* wrong lifecycle (prefill on a non-empty state, destroy with live states) */
+#define QDEC_E_OOM (-5)      /* device allocation failed */
+#define QDEC_E_DEVICE (-6)   /* a HIP runtime error */
+
+/* Weight storage types. */
+#define QDEC_F32 0
+#define QDEC_BF16 1
+
+/* Per-layer tensors, in the order of the qdec_weights.layer table. Linear
+ * weights are row-major [out, in]; norm gains are vectors.
+ *   IN_NORM [hidden]            input RMSNorm gain
+ *   WQ [n_q*hd, hidden]         WK, WV [n_kv*hd, hidden]
+ *   Q_NORM, K_NORM [hd]         per-head RMSNorm gains, shared by all heads
+ *   WO [hidden, n_q*hd]
+ *   POST_NORM [hidden]          post-attention RMSNorm gain
+ *   W_GATE, W_UP [ffn, hidden]  W_DOWN [hidden, ffn]
+ * The block computes z = silu(W_GATE xn) * (W_UP xn) and x += W_DOWN z. */
+enum {
+  QDEC_W_IN_NORM = 0,
+  QDEC_W_Q,
+  QDEC_W_K,
+  QDEC_W_V,
+  QDEC_W_Q_NORM,
+  QDEC_W_K_NORM,
+  QDEC_W_O,
+  QDEC_W_POST_NORM,
+  QDEC_W_GATE,
+  QDEC_W_UP,
+  QDEC_W_DOWN,
+  QDEC_W_PER_LAYER
+};
+
+/* Model shape. Validated by qdec_create (QDEC_E_INVALID otherwise):
+ * n_layer >= 1; hidden a multiple of 64 and <= 8192; head_dim even, a
+ * multiple of 8 and <= 128; n_kv_head >= 1 and n_q_head a multiple of
+ * n_kv_head with n_q_head / n_kv_head <= 8; ffn a multiple of 16 and <= 16384;
+ * n_q_head * head_dim <= 8192; vocab >= 2; rms_eps > 0; rope_theta > 1;
+ * weight_dtype QDEC_F32 or QDEC_BF16; tied == 1 (the LM head is the token
+ * embedding table, audio.cpp plan Task 1 Step 3 rejects untied embeddings). */
+typedef struct {
+  int32_t n_layer, hidden, n_q_head, n_kv_head, head_dim, ffn, vocab;
+  float rms_eps, rope_theta;
+  int32_t weight_dtype;
+  int32_t tied;
+} qdec_config;
+
+/* Device pointers to the weights, all of the config's weight_dtype.
+ * embed [vocab, hidden] (also the tied LM head), final_norm [hidden].
+ * layer: HOST array of n_layer * QDEC_W_PER_LAYER device pointers, layer-major
+ * (layer[i * QDEC_W_PER_LAYER + QDEC_W_Q] is layer i's WQ).
+ * Ownership: qdec_create copies the per-layer tensors and final_norm into its
+ * own packed layout, so those may be freed afterwards; embed is borrowed and
+ * must stay valid until qdec_destroy. */
+typedef struct {
+  const void* embed;
+  const void* final_norm;
+  const void* const* layer;
+} qdec_weights;
+
+typedef struct qdec_model qdec_model;
+typedef struct qdec_state qdec_state;
+
+/* Validate the config and weights, pack the weights on `hip_stream` (a
+ * hipStream_t; NULL = the null stream) and build the RoPE tables. The stream
+ * is synchronised before return. */
+int qdec_create(const qdec_config* cfg, const qdec_weights* w, void* hip_stream, qdec_model** out);
+
+/* Free the model. Returns QDEC_E_STATE (and frees nothing) while states of
+ * this model are alive. Synchronises the model's stream. NULL is a no-op. */
+int qdec_destroy(qdec_model* m);
+
+/* New empty sequence state (n_past = 0) able to hold max_ctx positions,
+ * 1 <= max_ctx <= 1 << 20. Reserves all KV pages now, so decode never
+ * allocates. The KV cache is fp32, paged in pages of QDEC_PAGE positions. */
+int qdec_state_create(qdec_model* m, int32_t max_ctx, qdec_state** out);
+void qdec_state_destroy(qdec_state* s);
+
+#define QDEC_PAGE 16
+
+/* Prefill (NCNN page section 5; transcribe.cpp LLM decoder table).
+ * ids_host: HOST int32[n_tokens] token ids; ids in [audio_begin,
+ *   audio_begin + audio_len) are ignored, all others must lie in [0, vocab).
+ * audio_dev: DEVICE fp32 [audio_len, hidden] row-major rows that replace the
+ *   token embeddings of that span (may be NULL iff audio_len == 0).
+ * Requires n_past == 0 (else QDEC_E_STATE), 1 <= n_tokens <= max_ctx (else
+ * QDEC_E_CAPACITY / QDEC_E_INVALID), 0 <= audio_begin, audio_len >= 0,
+ * audio_begin + audio_len <= n_tokens.
+ * Writes the K/V of positions [0, n_tokens) and sets n_past = n_tokens.
+ * logits_dev: DEVICE fp32 [vocab] last-position logits, or NULL.
+ * argmax_dev: DEVICE int32 greedy token of the last position, or NULL. */
+int qdec_prefill(qdec_state* s, const int32_t* ids_host, int32_t n_tokens, const float* audio_dev,
+                 int32_t audio_begin, int32_t audio_len, float* logits_dev, int32_t* argmax_dev);
+
+/* One decode step (NCNN page section 5, steps 1-6): embeds `token`
+ * (0 <= token < vocab), runs all layers at position pos attending over
+ * [0, pos], appends K/V at pos and sets n_past = pos + 1.
+ * Requires pos == n_past (else QDEC_E_POS) and pos < max_ctx (else
+ * QDEC_E_CAPACITY). logits_dev / argmax_dev as for qdec_prefill. */
+int qdec_decode_step(qdec_state* s, int32_t token, int32_t pos, float* logits_dev, int32_t* argmax_dev);
+
+/* As qdec_decode_step, with the token read on the device from token_dev
+ * (DEVICE int32, e.g. the previous step's argmax_dev), so greedy decoding
+ * needs no host round trip. A token_dev value outside [0, vocab) is clamped
+ * into range on the device (the host cannot check it). */
+int qdec_decode_step_dev(qdec_state* s, const int32_t* token_dev, int32_t pos, float* logits_dev,
+                         int32_t* argmax_dev);
+
+/* n independent decode steps in one launch set (1 <= n <= 16), state i
+ * consuming tokens_host[i] at its own n_past. All states must belong to one
+ * model and be distinct. Results equal n separate qdec_decode_step calls
+ * within rounding. logits_dev: DEVICE fp32 [n, vocab] or NULL; argmax_dev:
+ * DEVICE int32 [n] or NULL. On any argument error no state changes. */
+int qdec_decode_batch(qdec_state* const* states, int32_t n, const int32_t* tokens_host, float* logits_dev,
+                      int32_t* argmax_dev);
+
+/* Clone a state (NCNN page section 5: generation clones the context so one
+ * prefill can seed several branches). dst gets src's n_past, max_ctx and a
+ * logically identical KV cache: full pages are shared (reference counted,
+ * never written again), the partly filled tail page is copied on the stream,
+ * and the remaining capacity gets fresh pages. src is unchanged; either may
+ * be destroyed first. */
+int qdec_clone_state(const qdec_state* src, qdec_state** dst);
+
+/* n_past of the state (-1 for NULL). */
+int32_t qdec_state_pos(const qdec_state* s);
+
+/* Description of the last error on this thread ("" if none). */
+const char* qdec_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QDEC_H */

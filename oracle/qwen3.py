@@ -200,28 +200,37 @@ class Qwen3Oracle:
             x[audio_begin:audio_begin + n_audio] = np.asarray(audio, dtype=self.dtype)
         return x
 
-    def block(self, i: int, x: np.ndarray, state: OracleState, pos0: int) -> np.ndarray:
-        """One Qwen3 block over rows at positions pos0..pos0+T-1 ([P2]: rms_norm
-        + GQA + per-head Q/K-RMSNorm + NeoX RoPE + SwiGLU). Appends this layer's
-        K/V to the cache before attending ([P3] section 5 step 4)."""
+    def qkv(self, i: int, x: np.ndarray, pos: np.ndarray):
+        """Row-wise first half of a Qwen3 block ([P2]: rms_norm, Q/K/V
+        projections, per-head Q/K-RMSNorm, NeoX RoPE at each row's absolute
+        position). Returns q [T,n_q,D], k, v [T,n_kv,D]."""
         c, p = self.cfg, self.p
-        T = x.shape[0]
-        D = c.head_dim
-        pos = np.arange(pos0, pos0 + T)
+        T, D = x.shape[0], c.head_dim
         xn = rms_norm(x, p[f"L{i}.in_norm"], c.rms_eps)
         q = (xn @ p[f"L{i}.wq"].T).reshape(T, c.n_q_head, D)
         k = (xn @ p[f"L{i}.wk"].T).reshape(T, c.n_kv_head, D)
         v = (xn @ p[f"L{i}.wv"].T).reshape(T, c.n_kv_head, D)
         q = rms_norm(q, p[f"L{i}.q_norm"], c.rms_eps)
         k = rms_norm(k, p[f"L{i}.k_norm"], c.rms_eps)
-        q = apply_rope(q, pos, c.rope_theta)
-        k = apply_rope(k, pos, c.rope_theta)
-        state.append(i, k, v, pos0)
-        o = attention(q, state.k[i], state.v[i], pos, pos0 + T)
-        x = x + o.reshape(T, c.n_q_head * D) @ p[f"L{i}.wo"].T
+        return apply_rope(q, pos, c.rope_theta), apply_rope(k, pos, c.rope_theta), v
+
+    def out_mlp(self, i: int, x: np.ndarray, o: np.ndarray) -> np.ndarray:
+        """Row-wise second half: X += O Wo^T; X += down(silu(gate Xn) * up Xn)
+        with Xn = rms_norm(X; post_norm) ([P2] "SwiGLU (packed gate_up)")."""
+        c, p = self.cfg, self.p
+        x = x + o.reshape(x.shape[0], c.n_q_head * c.head_dim) @ p[f"L{i}.wo"].T
         xn = rms_norm(x, p[f"L{i}.post_norm"], c.rms_eps)
         z = silu(xn @ p[f"L{i}.w_gate"].T) * (xn @ p[f"L{i}.w_up"].T)
         return x + z @ p[f"L{i}.w_down"].T
+
+    def block(self, i: int, x: np.ndarray, state: OracleState, pos0: int) -> np.ndarray:
+        """One Qwen3 block over rows at positions pos0..pos0+T-1. This layer's
+        K/V are appended to the cache before attending ([P3] section 5 step 4)."""
+        pos = np.arange(pos0, pos0 + x.shape[0])
+        q, k, v = self.qkv(i, x, pos)
+        state.append(i, k, v, pos0)
+        o = attention(q, state.k[i], state.v[i], pos, pos0 + x.shape[0])
+        return self.out_mlp(i, x, o)
 
     def head(self, x_last: np.ndarray) -> np.ndarray:
         """[P2] "Final RMSNorm" + "Tied lm_head": logits = E . rms_norm(x)."""
@@ -253,8 +262,21 @@ class Qwen3Oracle:
 
     def decode_many(self, states: Sequence[OracleState], tokens: Sequence[int]) -> np.ndarray:
         """Independent single-token steps for several sequences, each at its own
-        n_past (results equal separate decode() calls)."""
-        return np.stack([self.decode(s, int(t), s.n_past) for s, t in zip(states, tokens)])
+        n_past. The row-wise parts run on the stacked rows; attention runs per
+        sequence over its own cache, so each row equals a separate decode()."""
+        B = len(states)
+        pos = np.array([s.n_past for s in states])
+        x = self.embed(np.asarray(tokens), None, 0)
+        for i in range(self.cfg.n_layer):
+            q, k, v = self.qkv(i, x, pos)
+            o = np.empty_like(q)
+            for b, st in enumerate(states):
+                st.append(i, k[b:b + 1], v[b:b + 1], int(pos[b]))
+                o[b:b + 1] = attention(q[b:b + 1], st.k[i], st.v[i], pos[b:b + 1], int(pos[b]) + 1)
+            x = self.out_mlp(i, x, o)
+        for b, st in enumerate(states):
+            st.n_past = int(pos[b]) + 1
+        return self.head(x)
 
 
 def pick_token(logits: np.ndarray) -> int:

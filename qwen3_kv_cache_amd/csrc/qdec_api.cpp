@@ -1,0 +1,665 @@
+// Host side of the qdec C ABI: argument validation, weight packing, the
+// paged KV pool with reference-counted pages, sequence states and launch
+// sequencing. Everything device-side is enqueued on the model's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "qdec_internal.h"
+
+using namespace qdec;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return QDEC_OK;
+}
+
+#define HIP_TRY(expr)                                                                       \
+  do {                                                                                      \
+    hipError_t e_ = (expr);                                                                 \
+    if (e_ != hipSuccess) return fail(QDEC_E_DEVICE, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+// Checks that [p, p + bytes) lies inside one device allocation, so a kernel
+// never writes or reads past what the caller handed in.
+int check_dev(const void* p, size_t bytes, const char* what) {
+  if (!p) return fail(QDEC_E_INVALID, "%s is NULL", what);
+  hipPointerAttribute_t attr;
+  const hipError_t pe = hipPointerGetAttributes(&attr, p);
+  if (pe != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(QDEC_E_INVALID, "%s is not a device pointer (%s)", what, hipGetErrorString(pe));
+  }
+  if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)
+    return fail(QDEC_E_INVALID, "%s is not device memory", what);
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)p) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(QDEC_E_INVALID, "%s: cannot query its allocation", what);
+  }
+  const char* b = (const char*)base;
+  const char* q = (const char*)p;
+  if (q < b || q + bytes > b + size)
+    return fail(QDEC_E_INVALID, "%s: %zu bytes do not fit its allocation", what, bytes);
+  return QDEC_OK;
+}
+
+struct PagePool {
+  size_t page_bytes = 0;
+  std::vector<void*> chunks;
+  std::vector<char*> free_pages;
+  std::unordered_map<char*, int> refs;
+
+  int reserve(int n) {
+    if ((int)free_pages.size() >= n) return QDEC_OK;
+    const int want = n - (int)free_pages.size();
+    const int npages = want < 32 ? 32 : want;
+    void* p = nullptr;
+    if (hipMalloc(&p, (size_t)npages * page_bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(QDEC_E_OOM, "KV pool: cannot allocate %d pages of %zu bytes", npages, page_bytes);
+    }
+    chunks.push_back(p);
+    for (int i = npages - 1; i >= 0; --i) free_pages.push_back((char*)p + (size_t)i * page_bytes);
+    return QDEC_OK;
+  }
+  char* take() {
+    char* p = free_pages.back();
+    free_pages.pop_back();
+    refs[p] = 1;
+    return p;
+  }
+  void retain(char* p) { ++refs[p]; }
+  void release(char* p) {
+    auto it = refs.find(p);
+    if (it == refs.end()) return;
+    if (--it->second == 0) {
+      refs.erase(it);
+      free_pages.push_back(p);
+    }
+  }
+};
+
+template <typename T>
+int dev_alloc(T** p, size_t n, const char* what) {
+  *p = nullptr;
+  if (n == 0) return QDEC_OK;
+  if (hipMalloc((void**)p, n * sizeof(T)) != hipSuccess) {
+    (void)hipGetLastError();
+    *p = nullptr;
+    return fail(QDEC_E_OOM, "cannot allocate %s (%zu bytes)", what, n * sizeof(T));
+  }
+  return QDEC_OK;
+}
+
+}  // namespace
+
+struct qdec_model {
+  qdec_config cfg{};
+  Dims d{};
+  bool bf16 = true;
+  hipStream_t stream = nullptr;
+  const void* embed = nullptr;
+  float* final_norm = nullptr;
+  void* wbuf = nullptr;  // packed matrices of all layers
+  float* nbuf = nullptr; // fp32 norm gains of all layers
+  std::vector<LayerW> layers;
+  float* rope_cos = nullptr;
+  float* rope_sin = nullptr;
+  int rope_cap = 0;
+  // decode scratch (one sequence)
+  float* x = nullptr;
+  float* qkv = nullptr;
+  float* attn = nullptr;
+  float* z = nullptr;
+  float* partial = nullptr;
+  int partial_splits = 0;
+  unsigned long long* keys = nullptr;
+  int32_t* argmax_tmp = nullptr;
+  // prefill scratch, grown on demand
+  int pf_cap = 0;
+  int32_t* p_ids = nullptr;
+  float* pX = nullptr;
+  float* pQKV = nullptr;
+  float* pAttn = nullptr;
+  float* pZ = nullptr;
+  void* pA0 = nullptr;  // bf16 hi (or fp32 activations for fp32 weights)
+  void* pA1 = nullptr;  // bf16 lo
+  PagePool pool;
+  int live_states = 0;
+};
+
+struct qdec_state {
+  qdec_model* m = nullptr;
+  int max_ctx = 0;
+  int n_past = 0;
+  std::vector<char*> pages;
+  int64_t* pt_dev = nullptr;
+};
+
+namespace {
+
+int validate_config(const qdec_config* c) {
+  if (!c) return fail(QDEC_E_INVALID, "config is NULL");
+  if (c->n_layer < 1 || c->n_layer > 256) return fail(QDEC_E_INVALID, "n_layer %d out of range", c->n_layer);
+  if (c->hidden < 64 || c->hidden > 8192 || c->hidden % 64)
+    return fail(QDEC_E_INVALID, "hidden %d must be a multiple of 64 in [64, 8192]", c->hidden);
+  if (c->head_dim < 8 || c->head_dim > 128 || c->head_dim % 8)
+    return fail(QDEC_E_INVALID, "head_dim %d must be a multiple of 8 in [8, 128]", c->head_dim);
+  if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128)
+    return fail(QDEC_E_INVALID, "head_dim %d: kernels are built for 32, 64 and 128", c->head_dim);
+  if (c->n_kv_head < 1 || c->n_q_head < c->n_kv_head || c->n_q_head % c->n_kv_head)
+    return fail(QDEC_E_INVALID, "n_q_head %d must be a positive multiple of n_kv_head %d", c->n_q_head,
+                c->n_kv_head);
+  const int group = c->n_q_head / c->n_kv_head;
+  if (group != 1 && group != 2 && group != 4 && group != 8)
+    return fail(QDEC_E_INVALID, "GQA group %d must be 1, 2, 4 or 8", group);
+  if (c->n_q_head * c->head_dim > 8192) return fail(QDEC_E_INVALID, "n_q_head * head_dim exceeds 8192");
+  if (c->ffn < 16 || c->ffn > 16384 || c->ffn % 16)
+    return fail(QDEC_E_INVALID, "ffn %d must be a multiple of 16 in [16, 16384]", c->ffn);
+  if (c->vocab < 2) return fail(QDEC_E_INVALID, "vocab %d < 2", c->vocab);
+  if (!(c->rms_eps > 0.f) || !std::isfinite(c->rms_eps)) return fail(QDEC_E_INVALID, "rms_eps must be > 0");
+  if (!(c->rope_theta > 1.f) || !std::isfinite(c->rope_theta))
+    return fail(QDEC_E_INVALID, "rope_theta must be > 1");
+  if (c->weight_dtype != QDEC_F32 && c->weight_dtype != QDEC_BF16)
+    return fail(QDEC_E_INVALID, "weight_dtype %d unknown", c->weight_dtype);
+  if (c->tied != 1) return fail(QDEC_E_INVALID, "untied LM head is not supported (tied must be 1)");
+  return QDEC_OK;
+}
+
+void free_prefill(qdec_model* m) {
+  (void)hipFree(m->p_ids);
+  (void)hipFree(m->pX);
+  (void)hipFree(m->pQKV);
+  (void)hipFree(m->pAttn);
+  (void)hipFree(m->pZ);
+  (void)hipFree(m->pA0);
+  (void)hipFree(m->pA1);
+  m->p_ids = nullptr;
+  m->pX = m->pQKV = m->pAttn = m->pZ = nullptr;
+  m->pA0 = m->pA1 = nullptr;
+  m->pf_cap = 0;
+}
+
+void free_model(qdec_model* m) {
+  if (!m) return;
+  if (m->stream) (void)hipStreamSynchronize(m->stream);
+  (void)hipFree(m->final_norm);
+  (void)hipFree(m->wbuf);
+  (void)hipFree(m->nbuf);
+  (void)hipFree(m->rope_cos);
+  (void)hipFree(m->rope_sin);
+  (void)hipFree(m->x);
+  (void)hipFree(m->qkv);
+  (void)hipFree(m->attn);
+  (void)hipFree(m->z);
+  (void)hipFree(m->partial);
+  (void)hipFree(m->keys);
+  (void)hipFree(m->argmax_tmp);
+  free_prefill(m);
+  for (void* c : m->pool.chunks) (void)hipFree(c);
+  delete m;
+}
+
+int ensure_rope(qdec_model* m, int n_pos) {
+  if (n_pos <= m->rope_cap) return QDEC_OK;
+  int cap = m->rope_cap ? m->rope_cap : 1024;
+  while (cap < n_pos) cap *= 2;
+  const int half = m->d.D / 2;
+  std::vector<float> c((size_t)cap * half), s((size_t)cap * half);
+  // angle = p * theta^(-2j/D) in double precision, then rounded to float
+  std::vector<double> freq(half);
+  for (int j = 0; j < half; ++j) freq[j] = std::pow((double)m->cfg.rope_theta, -2.0 * j / m->d.D);
+  for (int p = 0; p < cap; ++p)
+    for (int j = 0; j < half; ++j) {
+      const double a = (double)p * freq[j];
+      c[(size_t)p * half + j] = (float)std::cos(a);
+      s[(size_t)p * half + j] = (float)std::sin(a);
+    }
+  float *dc = nullptr, *ds = nullptr;
+  if (int e = dev_alloc(&dc, c.size(), "RoPE table")) return e;
+  if (int e = dev_alloc(&ds, s.size(), "RoPE table")) {
+    (void)hipFree(dc);
+    return e;
+  }
+  HIP_TRY(hipMemcpy(dc, c.data(), c.size() * sizeof(float), hipMemcpyHostToDevice));
+  HIP_TRY(hipMemcpy(ds, s.data(), s.size() * sizeof(float), hipMemcpyHostToDevice));
+  // older tables may still be read by queued work
+  HIP_TRY(hipStreamSynchronize(m->stream));
+  (void)hipFree(m->rope_cos);
+  (void)hipFree(m->rope_sin);
+  m->rope_cos = dc;
+  m->rope_sin = ds;
+  m->rope_cap = cap;
+  return QDEC_OK;
+}
+
+int ensure_partial(qdec_model* m, int n_ctx) {
+  const int ns = (n_ctx + kAttnChunk - 1) / kAttnChunk;
+  if (ns <= m->partial_splits) return QDEC_OK;
+  float* p = nullptr;
+  if (int e = dev_alloc(&p, (size_t)m->d.NQ * ns * (m->d.D + 2), "attention partials")) return e;
+  HIP_TRY(hipStreamSynchronize(m->stream));
+  (void)hipFree(m->partial);
+  m->partial = p;
+  m->partial_splits = ns;
+  return QDEC_OK;
+}
+
+int ensure_prefill(qdec_model* m, int T) {
+  if (T <= m->pf_cap) return QDEC_OK;
+  HIP_TRY(hipStreamSynchronize(m->stream));
+  free_prefill(m);
+  const Dims& d = m->d;
+  const int kmax = std::max(std::max(d.H, d.NQ * d.D), d.F);
+  int e = 0;
+  if ((e = dev_alloc(&m->p_ids, T, "prefill ids")) || (e = dev_alloc(&m->pX, (size_t)T * d.H, "prefill X")) ||
+      (e = dev_alloc(&m->pQKV, (size_t)T * d.qkv(), "prefill QKV")) ||
+      (e = dev_alloc(&m->pAttn, (size_t)T * d.NQ * d.D, "prefill attention")) ||
+      (e = dev_alloc(&m->pZ, (size_t)T * d.F, "prefill FFN"))) {
+    free_prefill(m);
+    return e;
+  }
+  const size_t abytes = m->bf16 ? 2 : 4;
+  if (hipMalloc(&m->pA0, (size_t)T * kmax * abytes) != hipSuccess ||
+      (m->bf16 && hipMalloc(&m->pA1, (size_t)T * kmax * abytes) != hipSuccess)) {
+    (void)hipGetLastError();
+    free_prefill(m);
+    return fail(QDEC_E_OOM, "cannot allocate prefill activations for %d tokens", T);
+  }
+  m->pf_cap = T;
+  return QDEC_OK;
+}
+
+// ---------------------------------------------------------------- passes
+
+#define LAUNCH(expr)                                                                        \
+  do {                                                                                      \
+    hipError_t e_ = (expr);                                                                 \
+    if (e_ != hipSuccess) return fail(QDEC_E_DEVICE, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+// One decode step for one sequence; the state's n_past is updated by the caller.
+int run_decode(qdec_state* s, int token, const int32_t* token_dev, int pos, float* logits, int32_t* argmax) {
+  qdec_model* m = s->m;
+  const Dims& d = m->d;
+  hipStream_t st = m->stream;
+  const int n = pos + 1;
+  LAUNCH(launch_embed_decode(d, m->bf16, m->embed, token, token_dev, m->x, m->keys, st));
+  for (int l = 0; l < d.L; ++l) {
+    const LayerW& w = m->layers[l];
+    LAUNCH(launch_gemv(m->bf16, EPI_STORE, w.wqkv, d.qkv(), d.H, m->x, w.in_norm, d.eps, m->qkv, st));
+    LAUNCH(launch_qk_rope_append(d, m->qkv, 1, pos, w.q_norm, w.k_norm, m->rope_cos, m->rope_sin, s->pt_dev, l,
+                                 st));
+    LAUNCH(launch_attn_decode(d, m->qkv, n, s->pt_dev, l, m->partial, m->attn, st));
+    LAUNCH(launch_gemv(m->bf16, EPI_RESID, w.wo, d.H, d.NQ * d.D, m->attn, nullptr, d.eps, m->x, st));
+    LAUNCH(launch_gemv(m->bf16, EPI_SWIGLU, w.wgu, 2 * d.F, d.H, m->x, w.post_norm, d.eps, m->z, st));
+    LAUNCH(launch_gemv(m->bf16, EPI_RESID, w.wd, d.H, d.F, m->z, nullptr, d.eps, m->x, st));
+  }
+  LAUNCH(launch_lm_head(d, m->bf16, m->embed, m->x, m->final_norm, logits, m->keys, st));
+  LAUNCH(launch_argmax_final(m->keys, 1, argmax ? argmax : m->argmax_tmp, st));
+  return QDEC_OK;
+}
+
+int run_prefill(qdec_state* s, int T, const float* audio, int a0, int La, float* logits, int32_t* argmax) {
+  qdec_model* m = s->m;
+  const Dims& d = m->d;
+  hipStream_t st = m->stream;
+  const bool bf = m->bf16;
+  LAUNCH(launch_reset_keys(m->keys, 1, st));
+  LAUNCH(launch_embed_prefill(d, bf, m->embed, m->p_ids, T, audio, a0, La, m->pX, st));
+  auto norm_in = [&](const float* X, int K, const float* gain) -> hipError_t {
+    if (bf) return launch_rms_split(X, T, K, gain, d.eps, (uint16_t*)m->pA0, (uint16_t*)m->pA1, st);
+    return launch_rms_apply(X, T, K, gain, d.eps, (float*)m->pA0, st);
+  };
+  for (int l = 0; l < d.L; ++l) {
+    const LayerW& w = m->layers[l];
+    LAUNCH(norm_in(m->pX, d.H, w.in_norm));
+    LAUNCH(launch_gemm(bf, EPI_STORE, m->pA0, m->pA1, T, d.H, w.wqkv, d.qkv(), m->pQKV, d.qkv(), st));
+    LAUNCH(launch_qk_rope_append(d, m->pQKV, T, 0, w.q_norm, w.k_norm, m->rope_cos, m->rope_sin, s->pt_dev, l,
+                                 st));
+    LAUNCH(launch_attn_prefill(d, m->pQKV, T, m->pAttn, st));
+    LAUNCH(norm_in(m->pAttn, d.NQ * d.D, nullptr));
+    LAUNCH(launch_gemm(bf, EPI_RESID, m->pA0, m->pA1, T, d.NQ * d.D, w.wo, d.H, m->pX, d.H, st));
+    LAUNCH(norm_in(m->pX, d.H, w.post_norm));
+    LAUNCH(launch_gemm(bf, EPI_SWIGLU, m->pA0, m->pA1, T, d.H, w.wgu, 2 * d.F, m->pZ, d.F, st));
+    LAUNCH(norm_in(m->pZ, d.F, nullptr));
+    LAUNCH(launch_gemm(bf, EPI_RESID, m->pA0, m->pA1, T, d.F, w.wd, d.H, m->pX, d.H, st));
+  }
+  LAUNCH(launch_lm_head(d, bf, m->embed, m->pX + (size_t)(T - 1) * d.H, m->final_norm, logits, m->keys, st));
+  LAUNCH(launch_argmax_final(m->keys, 1, argmax ? argmax : m->argmax_tmp, st));
+  return QDEC_OK;
+}
+
+int check_outputs(const qdec_model* m, int n, const float* logits, const int32_t* argmax) {
+  if (logits) {
+    if (int e = check_dev(logits, (size_t)n * m->d.V * sizeof(float), "logits_dev")) return e;
+  }
+  if (argmax) {
+    if (int e = check_dev(argmax, (size_t)n * sizeof(int32_t), "argmax_dev")) return e;
+  }
+  return QDEC_OK;
+}
+
+int release_state_pages(qdec_state* s) {
+  for (char* p : s->pages) s->m->pool.release(p);
+  s->pages.clear();
+  return QDEC_OK;
+}
+
+int upload_page_table(qdec_state* s) {
+  std::vector<int64_t> pt(s->pages.size());
+  for (size_t i = 0; i < pt.size(); ++i) pt[i] = (int64_t)(intptr_t)s->pages[i];
+  HIP_TRY(hipMemcpyAsync(s->pt_dev, pt.data(), pt.size() * sizeof(int64_t), hipMemcpyHostToDevice, s->m->stream));
+  HIP_TRY(hipStreamSynchronize(s->m->stream));
+  return QDEC_OK;
+}
+
+}  // namespace
+
+// ================================================================= C ABI
+
+extern "C" {
+
+const char* qdec_last_error(void) { return g_err.c_str(); }
+
+int qdec_create(const qdec_config* cfg, const qdec_weights* w, void* hip_stream, qdec_model** out) {
+  if (!out) return fail(QDEC_E_INVALID, "out is NULL");
+  *out = nullptr;
+  if (int e = validate_config(cfg)) return e;
+  if (!w || !w->embed || !w->final_norm || !w->layer) return fail(QDEC_E_INVALID, "weights incomplete");
+  const qdec_config& c = *cfg;
+  Dims d{c.n_layer, c.hidden, c.n_q_head, c.n_kv_head, c.head_dim, c.ffn, c.vocab, c.rms_eps};
+  const size_t es = c.weight_dtype == QDEC_BF16 ? 2 : 4;
+  const size_t shp[QDEC_W_PER_LAYER] = {
+      (size_t)d.H, (size_t)d.NQ * d.D * d.H, (size_t)d.NKV * d.D * d.H, (size_t)d.NKV * d.D * d.H,
+      (size_t)d.D, (size_t)d.D, (size_t)d.H * d.NQ * d.D, (size_t)d.H, (size_t)d.F * d.H, (size_t)d.F * d.H,
+      (size_t)d.H * d.F};
+  if (int e = check_dev(w->embed, (size_t)d.V * d.H * es, "embed")) return e;
+  if (int e = check_dev(w->final_norm, (size_t)d.H * es, "final_norm")) return e;
+  for (int l = 0; l < d.L; ++l)
+    for (int t = 0; t < QDEC_W_PER_LAYER; ++t) {
+      char what[64];
+      snprintf(what, sizeof what, "layer %d tensor %d", l, t);
+      if (int e = check_dev(w->layer[l * QDEC_W_PER_LAYER + t], shp[t] * es, what)) return e;
+    }
+
+  qdec_model* m = new (std::nothrow) qdec_model();
+  if (!m) return fail(QDEC_E_OOM, "host allocation failed");
+  m->cfg = c;
+  m->d = d;
+  m->bf16 = c.weight_dtype == QDEC_BF16;
+  m->stream = (hipStream_t)hip_stream;
+  m->embed = w->embed;
+  m->pool.page_bytes = page_floats(d) * sizeof(float);
+  hipStream_t st = m->stream;
+
+  const size_t n_qkv = (size_t)d.qkv() * d.H, n_o = (size_t)d.H * d.NQ * d.D, n_gu = (size_t)2 * d.F * d.H,
+               n_d = (size_t)d.H * d.F;
+  const size_t per_layer = n_qkv + n_o + n_gu + n_d;
+  const size_t norms_per_layer = 2 * (size_t)d.H + 2 * (size_t)d.D;
+  int e = 0;
+  if (hipMalloc(&m->wbuf, per_layer * es * d.L) != hipSuccess) {
+    (void)hipGetLastError();
+    m->wbuf = nullptr;
+    free_model(m);
+    return fail(QDEC_E_OOM, "cannot allocate packed weights");
+  }
+  if ((e = dev_alloc(&m->nbuf, norms_per_layer * d.L, "norm gains")) ||
+      (e = dev_alloc(&m->final_norm, d.H, "final norm")) || (e = dev_alloc(&m->x, d.H, "x")) ||
+      (e = dev_alloc(&m->qkv, d.qkv(), "qkv")) || (e = dev_alloc(&m->attn, (size_t)d.NQ * d.D, "attn")) ||
+      (e = dev_alloc(&m->z, d.F, "z")) || (e = dev_alloc(&m->keys, kMaxBatch, "argmax keys")) ||
+      (e = dev_alloc(&m->argmax_tmp, kMaxBatch, "argmax scratch"))) {
+    free_model(m);
+    return e;
+  }
+  auto fail_dev = [&](const char* what, hipError_t he) {
+    const int r = fail(QDEC_E_DEVICE, "%s: %s", what, hipGetErrorString(he));
+    free_model(m);
+    return r;
+  };
+  hipError_t he;
+  char* wb = (char*)m->wbuf;
+  m->layers.resize(d.L);
+  for (int l = 0; l < d.L; ++l) {
+    const void* const* t = w->layer + (size_t)l * QDEC_W_PER_LAYER;
+    char* base = wb + per_layer * es * l;
+    char* qkv = base;
+    char* o = qkv + n_qkv * es;
+    char* gu = o + n_o * es;
+    char* dn = gu + n_gu * es;
+    const size_t row = (size_t)d.H * es;
+    size_t off = 0;
+    if ((he = hipMemcpyAsync(qkv + off, t[QDEC_W_Q], shp[QDEC_W_Q] * es, hipMemcpyDeviceToDevice, st)))
+      return fail_dev("pack wq", he);
+    off += shp[QDEC_W_Q] * es;
+    if ((he = hipMemcpyAsync(qkv + off, t[QDEC_W_K], shp[QDEC_W_K] * es, hipMemcpyDeviceToDevice, st)))
+      return fail_dev("pack wk", he);
+    off += shp[QDEC_W_K] * es;
+    if ((he = hipMemcpyAsync(qkv + off, t[QDEC_W_V], shp[QDEC_W_V] * es, hipMemcpyDeviceToDevice, st)))
+      return fail_dev("pack wv", he);
+    if ((he = hipMemcpyAsync(o, t[QDEC_W_O], n_o * es, hipMemcpyDeviceToDevice, st))) return fail_dev("pack wo", he);
+    // gate/up interleaved in groups of kGuGroup rows
+    const size_t grp = (size_t)kGuGroup * row;
+    if ((he = hipMemcpy2DAsync(gu, 2 * grp, t[QDEC_W_GATE], grp, grp, d.F / kGuGroup, hipMemcpyDeviceToDevice, st)))
+      return fail_dev("pack gate", he);
+    if ((he = hipMemcpy2DAsync(gu + grp, 2 * grp, t[QDEC_W_UP], grp, grp, d.F / kGuGroup, hipMemcpyDeviceToDevice,
+                               st)))
+      return fail_dev("pack up", he);
+    if ((he = hipMemcpyAsync(dn, t[QDEC_W_DOWN], n_d * es, hipMemcpyDeviceToDevice, st)))
+      return fail_dev("pack down", he);
+    float* nb = m->nbuf + norms_per_layer * l;
+    if ((he = launch_to_f32(t[QDEC_W_IN_NORM], m->bf16, d.H, nb, st))) return fail_dev("in_norm", he);
+    if ((he = launch_to_f32(t[QDEC_W_POST_NORM], m->bf16, d.H, nb + d.H, st))) return fail_dev("post_norm", he);
+    if ((he = launch_to_f32(t[QDEC_W_Q_NORM], m->bf16, d.D, nb + 2 * d.H, st))) return fail_dev("q_norm", he);
+    if ((he = launch_to_f32(t[QDEC_W_K_NORM], m->bf16, d.D, nb + 2 * d.H + d.D, st))) return fail_dev("k_norm", he);
+    m->layers[l] = LayerW{qkv, o, gu, dn, nb, nb + d.H, nb + 2 * d.H, nb + 2 * d.H + d.D};
+  }
+  if ((he = launch_to_f32(w->final_norm, m->bf16, d.H, m->final_norm, st))) return fail_dev("final_norm", he);
+  if ((he = hipStreamSynchronize(st))) return fail_dev("weight packing", he);
+  if ((e = ensure_rope(m, 4096)) || (e = ensure_partial(m, 4096))) {
+    free_model(m);
+    return e;
+  }
+  *out = m;
+  return ok();
+}
+
+int qdec_destroy(qdec_model* m) {
+  if (!m) return ok();
+  if (m->live_states > 0) return fail(QDEC_E_STATE, "%d states of this model are still alive", m->live_states);
+  free_model(m);
+  return ok();
+}
+
+int qdec_state_create(qdec_model* m, int32_t max_ctx, qdec_state** out) {
+  if (!out) return fail(QDEC_E_INVALID, "out is NULL");
+  *out = nullptr;
+  if (!m) return fail(QDEC_E_INVALID, "model is NULL");
+  if (max_ctx < 1 || max_ctx > (1 << 20)) return fail(QDEC_E_INVALID, "max_ctx %d out of range", max_ctx);
+  if (int e = ensure_rope(m, max_ctx)) return e;
+  if (int e = ensure_partial(m, max_ctx)) return e;
+  const int npages = (max_ctx + kPage - 1) / kPage;
+  if (int e = m->pool.reserve(npages)) return e;
+  qdec_state* s = new (std::nothrow) qdec_state();
+  if (!s) return fail(QDEC_E_OOM, "host allocation failed");
+  s->m = m;
+  s->max_ctx = max_ctx;
+  if (int e = dev_alloc(&s->pt_dev, npages, "page table")) {
+    delete s;
+    return e;
+  }
+  for (int i = 0; i < npages; ++i) s->pages.push_back(m->pool.take());
+  if (int e = upload_page_table(s)) {
+    release_state_pages(s);
+    (void)hipFree(s->pt_dev);
+    delete s;
+    return e;
+  }
+  ++m->live_states;
+  *out = s;
+  return ok();
+}
+
+void qdec_state_destroy(qdec_state* s) {
+  if (!s) return;
+  (void)hipStreamSynchronize(s->m->stream);
+  release_state_pages(s);
+  (void)hipFree(s->pt_dev);
+  --s->m->live_states;
+  delete s;
+}
+
+int32_t qdec_state_pos(const qdec_state* s) { return s ? s->n_past : -1; }
+
+int qdec_prefill(qdec_state* s, const int32_t* ids_host, int32_t n_tokens, const float* audio_dev,
+                 int32_t audio_begin, int32_t audio_len, float* logits_dev, int32_t* argmax_dev) {
+  if (!s) return fail(QDEC_E_INVALID, "state is NULL");
+  qdec_model* m = s->m;
+  if (s->n_past != 0) return fail(QDEC_E_STATE, "prefill needs an empty state (n_past = %d)", s->n_past);
+  if (n_tokens < 1) return fail(QDEC_E_INVALID, "n_tokens %d < 1", n_tokens);
+  if (n_tokens > s->max_ctx)
+    return fail(QDEC_E_CAPACITY, "n_tokens %d exceeds max_ctx %d", n_tokens, s->max_ctx);
+  if (!ids_host) return fail(QDEC_E_INVALID, "ids_host is NULL");
+  if (audio_begin < 0 || audio_len < 0 || (int64_t)audio_begin + audio_len > n_tokens)
+    return fail(QDEC_E_INVALID, "audio span [%d, %d + %d) outside the prompt of %d", audio_begin, audio_begin,
+                audio_len, n_tokens);
+  if (audio_len > 0) {
+    if (int e = check_dev(audio_dev, (size_t)audio_len * m->d.H * sizeof(float), "audio_dev")) return e;
+  }
+  for (int t = 0; t < n_tokens; ++t) {
+    if (t >= audio_begin && t < audio_begin + audio_len) continue;
+    if (ids_host[t] < 0 || ids_host[t] >= m->d.V)
+      return fail(QDEC_E_INVALID, "ids[%d] = %d outside [0, %d)", t, ids_host[t], m->d.V);
+  }
+  if (int e = check_outputs(m, 1, logits_dev, argmax_dev)) return e;
+  if (int e = ensure_prefill(m, n_tokens)) return e;
+  std::vector<int32_t> ids(ids_host, ids_host + n_tokens);
+  for (int t = audio_begin; t < audio_begin + audio_len; ++t) ids[t] = 0;  // never read
+  HIP_TRY(hipMemcpyAsync(m->p_ids, ids.data(), n_tokens * sizeof(int32_t), hipMemcpyHostToDevice, m->stream));
+  if (int e = run_prefill(s, n_tokens, audio_dev, audio_begin, audio_len, logits_dev, argmax_dev)) return e;
+  // the host copy source must outlive the async copy
+  HIP_TRY(hipStreamSynchronize(m->stream));
+  s->n_past = n_tokens;
+  return ok();
+}
+
+static int decode_common(qdec_state* s, int token, const int32_t* token_dev, int32_t pos, float* logits_dev,
+                         int32_t* argmax_dev) {
+  if (!s) return fail(QDEC_E_INVALID, "state is NULL");
+  if (pos != s->n_past) return fail(QDEC_E_POS, "pos %d != n_past %d", pos, s->n_past);
+  if (pos >= s->max_ctx) return fail(QDEC_E_CAPACITY, "pos %d >= max_ctx %d", pos, s->max_ctx);
+  if (int e = check_outputs(s->m, 1, logits_dev, argmax_dev)) return e;
+  if (int e = run_decode(s, token, token_dev, pos, logits_dev, argmax_dev)) return e;
+  s->n_past = pos + 1;
+  return ok();
+}
+
+int qdec_decode_step(qdec_state* s, int32_t token, int32_t pos, float* logits_dev, int32_t* argmax_dev) {
+  if (s && (token < 0 || token >= s->m->d.V))
+    return fail(QDEC_E_INVALID, "token %d outside [0, %d)", token, s->m->d.V);
+  return decode_common(s, token, nullptr, pos, logits_dev, argmax_dev);
+}
+
+int qdec_decode_step_dev(qdec_state* s, const int32_t* token_dev, int32_t pos, float* logits_dev,
+                         int32_t* argmax_dev) {
+  if (int e = check_dev(token_dev, sizeof(int32_t), "token_dev")) return e;
+  return decode_common(s, 0, token_dev, pos, logits_dev, argmax_dev);
+}
+
+int qdec_decode_batch(qdec_state* const* states, int32_t n, const int32_t* tokens_host, float* logits_dev,
+                      int32_t* argmax_dev) {
+  if (!states || !tokens_host) return fail(QDEC_E_INVALID, "states or tokens_host is NULL");
+  if (n < 1 || n > kMaxBatch) return fail(QDEC_E_INVALID, "batch %d outside [1, %d]", n, kMaxBatch);
+  qdec_model* m = states[0] ? states[0]->m : nullptr;
+  if (!m) return fail(QDEC_E_INVALID, "states[0] is NULL");
+  for (int i = 0; i < n; ++i) {
+    qdec_state* s = states[i];
+    if (!s || s->m != m) return fail(QDEC_E_INVALID, "states[%d] is NULL or of another model", i);
+    for (int j = 0; j < i; ++j)
+      if (states[j] == s) return fail(QDEC_E_INVALID, "states[%d] repeats states[%d]", i, j);
+    if (s->n_past >= s->max_ctx)
+      return fail(QDEC_E_CAPACITY, "states[%d]: n_past %d == max_ctx", i, s->n_past);
+    if (tokens_host[i] < 0 || tokens_host[i] >= m->d.V)
+      return fail(QDEC_E_INVALID, "tokens[%d] = %d outside [0, %d)", i, tokens_host[i], m->d.V);
+  }
+  if (int e = check_outputs(m, n, logits_dev, argmax_dev)) return e;
+  for (int i = 0; i < n; ++i) {
+    qdec_state* s = states[i];
+    if (int e = run_decode(s, tokens_host[i], nullptr, s->n_past, logits_dev ? logits_dev + (size_t)i * m->d.V : nullptr,
+                           argmax_dev ? argmax_dev + i : nullptr))
+      return e;
+    s->n_past += 1;
+  }
+  return ok();
+}
+
+int qdec_clone_state(const qdec_state* src, qdec_state** dst) {
+  if (!dst) return fail(QDEC_E_INVALID, "dst is NULL");
+  *dst = nullptr;
+  if (!src) return fail(QDEC_E_INVALID, "src is NULL");
+  qdec_model* m = src->m;
+  const int npages = (int)src->pages.size();
+  const int nfull = src->n_past / kPage;
+  const bool tail = src->n_past % kPage != 0;
+  if (int e = m->pool.reserve(npages - nfull)) return e;
+  qdec_state* s = new (std::nothrow) qdec_state();
+  if (!s) return fail(QDEC_E_OOM, "host allocation failed");
+  s->m = m;
+  s->max_ctx = src->max_ctx;
+  s->n_past = src->n_past;
+  if (int e = dev_alloc(&s->pt_dev, npages, "page table")) {
+    delete s;
+    return e;
+  }
+  for (int i = 0; i < nfull; ++i) {
+    m->pool.retain(src->pages[i]);
+    s->pages.push_back(src->pages[i]);
+  }
+  for (int i = nfull; i < npages; ++i) s->pages.push_back(m->pool.take());
+  if (tail) {
+    if (hipMemcpyAsync(s->pages[nfull], src->pages[nfull], m->pool.page_bytes, hipMemcpyDeviceToDevice, m->stream) !=
+        hipSuccess) {
+      (void)hipGetLastError();
+      release_state_pages(s);
+      (void)hipFree(s->pt_dev);
+      delete s;
+      return fail(QDEC_E_DEVICE, "tail page copy failed");
+    }
+  }
+  if (int e = upload_page_table(s)) {
+    release_state_pages(s);
+    (void)hipFree(s->pt_dev);
+    delete s;
+    return e;
+  }
+  ++m->live_states;
+  *dst = s;
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+// Internal declarations shared by the host library and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/qdec.h"
+
+namespace qdec {
+
+constexpr int kPage = QDEC_PAGE;   // positions per KV page
+constexpr int kGuGroup = 8;        // gate/up rows interleaved in groups of 8 in the packed weight
+constexpr int kAttnChunk = 256;    // positions per split in decode attention
+constexpr int kMaxBatch = 16;
+
+// Model dimensions as the kernels see them.
+struct Dims {
+  int L, H, NQ, NKV, D, F, V;
+  float eps;
+  int qkv() const { return (NQ + 2 * NKV) * D; }
+};
+
+// Packed per-layer weights (device). wqkv = [wq; wk; wv] rows; wgu holds
+// gate and up rows interleaved in groups of kGuGroup: packed rows
+// [16g, 16g+8) are gate rows [8g, 8g+8), packed rows [16g+8, 16g+16) the
+// matching up rows.
+struct LayerW {
+  const void* wqkv;
+  const void* wo;
+  const void* wgu;
+  const void* wd;
+  const float* in_norm;
+  const float* post_norm;
+  const float* q_norm;
+  const float* k_norm;
+};
+
+// KV page layout (fp32): page[layer][0=K,1=V][kv_head][slot][head_dim].
+__host__ __device__ inline size_t page_floats(const Dims& d) {
+  return (size_t)d.L * 2 * d.NKV * kPage * d.D;
+}
+__host__ __device__ inline size_t page_offset(const Dims& d, int layer, int kv, int head, int slot) {
+  return ((((size_t)layer * 2 + kv) * d.NKV + head) * kPage + slot) * d.D;
+}
+
+// ---- launchers (qdec_kernels.hip); all enqueue on `st`, return hipError_t
+hipError_t launch_embed_decode(const Dims& d, bool bf16, const void* E, int token, const int32_t* token_dev,
+                               float* x, unsigned long long* key, hipStream_t st);
+hipError_t launch_embed_prefill(const Dims& d, bool bf16, const void* E, const int32_t* ids, int T,
+                                const float* audio, int a0, int La, float* X, hipStream_t st);
+
+enum Epi { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
+hipError_t launch_gemv(bool bf16, Epi epi, const void* W, int R, int K, const float* x, const float* gain,
+                       float eps, float* out, hipStream_t st);
+hipError_t launch_lm_head(const Dims& d, bool bf16, const void* E, const float* x, const float* gain,
+                          float* logits, unsigned long long* key, hipStream_t st);
+hipError_t launch_argmax_final(const unsigned long long* key, int n, int32_t* out, hipStream_t st);
+hipError_t launch_reset_keys(unsigned long long* key, int n, hipStream_t st);
+
+hipError_t launch_qk_rope_append(const Dims& d, float* qkv, int T, int pos0, const float* q_norm,
+                                 const float* k_norm, const float* rope_cos, const float* rope_sin,
+                                 const int64_t* page_table, int layer, hipStream_t st);
+hipError_t launch_attn_decode(const Dims& d, const float* q, int n, const int64_t* page_table, int layer,
+                              float* partial, float* out, hipStream_t st);
+hipError_t launch_attn_prefill(const Dims& d, const float* qkv, int T, float* out, hipStream_t st);
+
+hipError_t launch_rms_split(const float* X, int T, int K, const float* gain, float eps, uint16_t* hi,
+                            uint16_t* lo, hipStream_t st);
+hipError_t launch_rms_apply(const float* X, int T, int K, const float* gain, float eps, float* out,
+                            hipStream_t st);
+hipError_t launch_gemm(bool bf16, Epi epi, const void* A0, const void* A1, int M, int K, const void* W, int N,
+                       float* C, int ldc, hipStream_t st);
+hipError_t launch_to_f32(const void* src, bool bf16, size_t n, float* dst, hipStream_t st);
+
+}  // namespace qdec

@@ -1,0 +1,974 @@
+// HIP kernels for the Qwen3 KV-cache decoder on gfx950 (CDNA4, wave64).
+//
+// Step map (transcribe.cpp "Forward map - funasr_nano", table "LLM decoder";
+// NCNN "Qwen3ASR ncnn多平台移植", section 5):
+//   embed + audio-row override   -> embed_decode_kernel / embed_prefill_kernel
+//   rms_norm + Q/K/V projection  -> gemv_kernel (decode), rms_split + gemm (prefill)
+//   per-head Q/K-RMSNorm + NeoX RoPE + KV append -> qk_rope_append_kernel
+//   causal GQA attention         -> attn_decode_kernel + attn_combine_kernel,
+//                                   attn_prefill_kernel
+//   O projection + residual      -> gemv / gemm with the residual epilogue
+//   rms_norm + gate_up + SiLU*up -> gemv / gemm with the SwiGLU epilogue
+//   down projection + residual   -> gemv / gemm with the residual epilogue
+//   final rms_norm + tied head + greedy argmax -> lm_head_kernel + argmax_final_kernel
+#include <hip/hip_runtime.h>
+
+#include <cfloat>
+#include <cmath>
+
+#include "qdec_internal.h"
+
+namespace qdec {
+namespace {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// float -> bf16 bits, round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Sum over the block (blockDim.x threads, multiple of 64); result in every thread.
+__device__ float block_sum(float v, float* red) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  v = wave_sum(v);
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float s = 0.f;
+  for (int i = 0; i < nw; ++i) s += red[i];
+  return s;
+}
+
+// 16-byte weight chunk: 8 bf16 or 4 fp32 values.
+template <typename WT>
+struct Chunk;
+template <>
+struct Chunk<uint16_t> {
+  static constexpr int N = 8;
+  uint4 raw;
+  __device__ __forceinline__ void load(const uint16_t* p) { raw = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ float dot(const float* x) const {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s = fmaf(__uint_as_float(w[i] << 16), x[2 * i], s);
+      s = fmaf(__uint_as_float(w[i] & 0xFFFF0000u), x[2 * i + 1], s);
+    }
+    return s;
+  }
+};
+template <>
+struct Chunk<float> {
+  static constexpr int N = 4;
+  float4 raw;
+  __device__ __forceinline__ void load(const float* p) { raw = *reinterpret_cast<const float4*>(p); }
+  __device__ __forceinline__ float dot(const float* x) const {
+    float s = raw.x * x[0];
+    s = fmaf(raw.y, x[1], s);
+    s = fmaf(raw.z, x[2], s);
+    return fmaf(raw.w, x[3], s);
+  }
+};
+
+template <typename WT>
+__device__ __forceinline__ float load_w(const WT* p, size_t i);
+template <>
+__device__ __forceinline__ float load_w<uint16_t>(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+template <>
+__device__ __forceinline__ float load_w<float>(const float* p, size_t i) { return p[i]; }
+
+__device__ __forceinline__ unsigned long long argmax_key(float v, int idx) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)o << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)idx);
+}
+
+// ------------------------------------------------------------------ embed
+
+template <typename WT>
+__global__ __launch_bounds__(256) void embed_decode_kernel(const WT* __restrict__ E, int H, int V, int token,
+                                                            const int32_t* __restrict__ token_dev,
+                                                            float* __restrict__ x, unsigned long long* key) {
+  int t = token_dev ? token_dev[0] : token;
+  t = t < 0 ? 0 : (t >= V ? V - 1 : t);
+  const WT* row = E + (size_t)t * H;
+  for (int i = threadIdx.x; i < H; i += blockDim.x) x[i] = load_w(row, i);
+  if (threadIdx.x == 0 && key) *key = 0ull;
+}
+
+template <typename WT>
+__global__ __launch_bounds__(256) void embed_prefill_kernel(const WT* __restrict__ E, int H,
+                                                             const int32_t* __restrict__ ids,
+                                                             const float* __restrict__ audio, int a0, int La,
+                                                             float* __restrict__ X) {
+  const int t = blockIdx.x;
+  float* out = X + (size_t)t * H;
+  if (t >= a0 && t < a0 + La) {
+    const float* src = audio + (size_t)(t - a0) * H;
+    for (int i = threadIdx.x; i < H; i += blockDim.x) out[i] = src[i];
+  } else {
+    const WT* row = E + (size_t)ids[t] * H;
+    for (int i = threadIdx.x; i < H; i += blockDim.x) out[i] = load_w(row, i);
+  }
+}
+
+// ------------------------------------------------------------------- GEMV
+// y[r] = sum_k W[r, k] * xin[k] for one activation row; xin optionally
+// RMS-normalised with `gain` first. Each wave owns ROWS consecutive rows; each
+// lane reads 16-byte weight chunks c = lane + 64 j. 4 waves per block.
+
+template <typename WT, int ROWS, int KCH, int EPI>
+__global__ __launch_bounds__(256) void gemv_kernel(const WT* __restrict__ W, int R, int K,
+                                                    const float* __restrict__ xin, const float* __restrict__ gain,
+                                                    float eps, float* __restrict__ out) {
+  extern __shared__ float smem[];
+  float* xs = smem;         // K floats
+  float* red = smem + K;    // 64 floats scratch
+  constexpr int VN = Chunk<WT>::N;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+
+  float inv = 1.f;
+  if (gain) {
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < K; i += blockDim.x) {
+      float v = xin[i];
+      ss = fmaf(v, v, ss);
+    }
+    ss = block_sum(ss, red);
+    inv = 1.f / sqrtf(ss / (float)K + eps);
+    for (int i = threadIdx.x; i < K; i += blockDim.x) xs[i] = xin[i] * inv * gain[i];
+  } else {
+    for (int i = threadIdx.x; i < K; i += blockDim.x) xs[i] = xin[i];
+  }
+  __syncthreads();
+
+  const int r0 = (blockIdx.x * 4 + wave) * ROWS;
+  const int nch = K / VN;
+  Chunk<WT> w[KCH][ROWS];
+#pragma unroll
+  for (int j = 0; j < KCH; ++j) {
+    const int c = lane + kWave * j;
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      if (c < nch && r0 + r < R) w[j][r].load(W + (size_t)(r0 + r) * K + (size_t)c * VN);
+    }
+  }
+  float acc[ROWS];
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int j = 0; j < KCH; ++j) {
+    const int c = lane + kWave * j;
+    if (c < nch) {
+      float xv[VN];
+#pragma unroll
+      for (int i = 0; i < VN; ++i) xv[i] = xs[c * VN + i];
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r)
+        if (r0 + r < R) acc[r] += w[j][r].dot(xv);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) acc[r] = wave_sum(acc[r]);
+
+  if (EPI == EPI_SWIGLU) {
+    // block rows = 4 * ROWS = 16 = one interleave group: 8 gate rows then 8 up rows
+    __syncthreads();
+    if (lane < ROWS) {
+      float v = acc[0];
+#pragma unroll
+      for (int r = 1; r < ROWS; ++r)
+        if (lane == r) v = acc[r];
+      red[wave * ROWS + lane] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < kGuGroup) {
+      const float g = red[threadIdx.x], u = red[kGuGroup + threadIdx.x];
+      const int grp = blockIdx.x;  // one group per block
+      if ((grp + 1) * 2 * kGuGroup <= R) out[grp * kGuGroup + threadIdx.x] = g / (1.f + expf(-g)) * u;
+    }
+  } else {
+    if (lane < ROWS) {
+      float v = acc[0];
+#pragma unroll
+      for (int r = 1; r < ROWS; ++r)
+        if (lane == r) v = acc[r];
+      const int row = r0 + lane;
+      if (row < R) {
+        if (EPI == EPI_RESID)
+          out[row] += v;
+        else
+          out[row] = v;
+      }
+    }
+  }
+}
+
+// LM head over the tied embedding with fused final RMSNorm and greedy argmax.
+template <typename WT, int ROWS, int KCH>
+__global__ __launch_bounds__(256) void lm_head_kernel(const WT* __restrict__ E, int V, int K,
+                                                       const float* __restrict__ xin,
+                                                       const float* __restrict__ gain, float eps,
+                                                       float* __restrict__ logits, unsigned long long* key) {
+  extern __shared__ float smem[];
+  float* xs = smem;
+  float* red = smem + K;
+  __shared__ unsigned long long bkey[4];
+  constexpr int VN = Chunk<WT>::N;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < K; i += blockDim.x) {
+    float v = xin[i];
+    ss = fmaf(v, v, ss);
+  }
+  ss = block_sum(ss, red);
+  const float inv = 1.f / sqrtf(ss / (float)K + eps);
+  for (int i = threadIdx.x; i < K; i += blockDim.x) xs[i] = xin[i] * inv * gain[i];
+  __syncthreads();
+
+  const int r0 = (blockIdx.x * 4 + wave) * ROWS;
+  const int nch = K / VN;
+  Chunk<WT> w[KCH][ROWS];
+#pragma unroll
+  for (int j = 0; j < KCH; ++j) {
+    const int c = lane + kWave * j;
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r)
+      if (c < nch && r0 + r < V) w[j][r].load(E + (size_t)(r0 + r) * K + (size_t)c * VN);
+  }
+  float acc[ROWS];
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int j = 0; j < KCH; ++j) {
+    const int c = lane + kWave * j;
+    if (c < nch) {
+      float xv[VN];
+#pragma unroll
+      for (int i = 0; i < VN; ++i) xv[i] = xs[c * VN + i];
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r)
+        if (r0 + r < V) acc[r] += w[j][r].dot(xv);
+    }
+  }
+  unsigned long long best = 0ull;
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) {
+    const float v = wave_sum(acc[r]);
+    const int row = r0 + r;
+    if (row < V) {
+      if (logits && lane == r) logits[row] = v;
+      const unsigned long long k = argmax_key(v, row);
+      best = k > best ? k : best;
+    }
+  }
+  if (lane == 0) bkey[wave] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long b = bkey[0];
+    for (int i = 1; i < 4; ++i) b = bkey[i] > b ? bkey[i] : b;
+    atomicMax(key, b);
+  }
+}
+
+__global__ void argmax_final_kernel(const unsigned long long* key, int n, int32_t* out) {
+  const int i = threadIdx.x;
+  if (i < n) out[i] = (int32_t)(0xFFFFFFFFu - (uint32_t)(key[i] & 0xFFFFFFFFull));
+}
+
+__global__ void reset_keys_kernel(unsigned long long* key, int n) {
+  const int i = threadIdx.x;
+  if (i < n) key[i] = 0ull;
+}
+
+// ------------------------------------------ per-head Q/K RMSNorm + RoPE + KV append
+// One wave per (row, head); heads [0, NQ) are query heads, [NQ, NQ+NKV) key
+// heads (which also copy the matching V head). Lane l < D/2 owns the rotate-
+// half pair (l, l + D/2). Q and K are rewritten in place (post-RoPE); K and V
+// of position pos0 + row go to the paged cache.
+
+__global__ __launch_bounds__(64) void qk_rope_append_kernel(float* __restrict__ qkv, int ld, int pos0, int NQ,
+                                                             int NKV, int D, int L, float eps,
+                                                             const float* __restrict__ q_norm,
+                                                             const float* __restrict__ k_norm,
+                                                             const float* __restrict__ rcos,
+                                                             const float* __restrict__ rsin,
+                                                             const int64_t* __restrict__ page_table, int layer) {
+  const int row = blockIdx.y, head = blockIdx.x, lane = threadIdx.x;
+  const int half = D / 2;
+  const int pos = pos0 + row;
+  const bool is_q = head < NQ;
+  float* vec = qkv + (size_t)row * ld + (size_t)head * D;  // q heads then k heads are contiguous
+  const float* g = is_q ? q_norm : k_norm;
+  float a = 0.f, b = 0.f;
+  if (lane < half) {
+    a = vec[lane];
+    b = vec[lane + half];
+  }
+  const float ss = wave_sum(a * a + b * b);
+  const float inv = 1.f / sqrtf(ss / (float)D + eps);
+  if (lane < half) {
+    a = a * inv * g[lane];
+    b = b * inv * g[lane + half];
+    const float c = rcos[(size_t)pos * half + lane], s = rsin[(size_t)pos * half + lane];
+    const float ra = a * c - b * s, rb = b * c + a * s;
+    vec[lane] = ra;
+    vec[lane + half] = rb;
+    if (!is_q) {
+      const int kh = head - NQ;
+      Dims d{L, 0, NQ, NKV, D, 0, 0, 0.f};
+      float* page = reinterpret_cast<float*>(page_table[pos / kPage]);
+      const int slot = pos % kPage;
+      float* kd = page + page_offset(d, layer, 0, kh, slot);
+      float* vd = page + page_offset(d, layer, 1, kh, slot);
+      const float* vs = qkv + (size_t)row * ld + (size_t)(NQ + NKV + kh) * D;
+      kd[lane] = ra;
+      kd[lane + half] = rb;
+      vd[lane] = vs[lane];
+      vd[lane + half] = vs[lane + half];
+    }
+  }
+}
+
+// ------------------------------------------------------- decode attention
+// Split-K flash decoding over the paged cache. Block = (kv head g, split s),
+// 4 waves. In a wave, lane = 8 * slot + part: 8 keys at a time, each key's
+// head_dim split over 8 lanes (DPL = D / 8 values per lane). All GROUP query
+// heads of the KV head share every K/V load. Output per (q head, split):
+// running max m, denominator l and the unnormalised D-vector.
+
+template <int D, int GROUP>
+__global__ __launch_bounds__(256) void attn_decode_kernel(const float* __restrict__ q, int n, int NKV, int L,
+                                                           const int64_t* __restrict__ page_table, int layer,
+                                                           float* __restrict__ partial, int nsplit, float scale) {
+  constexpr int DPL = D / 8;
+  __shared__ float sm_m[4][GROUP], sm_l[4][GROUP];
+  __shared__ float sm_o[4][GROUP][D];
+  const int g = blockIdx.x, s = blockIdx.y;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int slot = lane / 8, part = lane % 8;
+  const int u0 = s * kAttnChunk, u1 = min(n, u0 + kAttnChunk);
+  Dims d{L, 0, 0, NKV, D, 0, 0, 0.f};
+
+  float qr[GROUP][DPL];
+#pragma unroll
+  for (int h = 0; h < GROUP; ++h)
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) qr[h][i] = q[(size_t)(g * GROUP + h) * D + part * DPL + i] * scale;
+
+  float m[GROUP], l[GROUP], acc[GROUP][DPL];
+#pragma unroll
+  for (int h = 0; h < GROUP; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) acc[h][i] = 0.f;
+  }
+
+  for (int base = u0 + wave * 8; base < u1; base += 32) {
+    const int u = base + slot;
+    const bool valid = u < u1;
+    float kv[DPL], vv[DPL];
+    if (valid) {
+      const float* page = reinterpret_cast<const float*>(page_table[u / kPage]);
+      const float* kp = page + page_offset(d, layer, 0, g, u % kPage) + part * DPL;
+      const float* vp = page + page_offset(d, layer, 1, g, u % kPage) + part * DPL;
+#pragma unroll
+      for (int i = 0; i < DPL; i += 4) {
+        const float4 a = *reinterpret_cast<const float4*>(kp + i);
+        kv[i] = a.x; kv[i + 1] = a.y; kv[i + 2] = a.z; kv[i + 3] = a.w;
+        const float4 b = *reinterpret_cast<const float4*>(vp + i);
+        vv[i] = b.x; vv[i + 1] = b.y; vv[i + 2] = b.z; vv[i + 3] = b.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) kv[i] = vv[i] = 0.f;
+    }
+#pragma unroll
+    for (int h = 0; h < GROUP; ++h) {
+      float sc = 0.f;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) sc = fmaf(qr[h][i], kv[i], sc);
+      sc += __shfl_xor(sc, 1, kWave);
+      sc += __shfl_xor(sc, 2, kWave);
+      sc += __shfl_xor(sc, 4, kWave);
+      if (!valid) sc = -INFINITY;
+      float mx = fmaxf(sc, __shfl_xor(sc, 8, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const float mn = fmaxf(m[h], mx);
+      const float alpha = expf(m[h] - mn);
+      const float p = valid ? expf(sc - mn) : 0.f;
+      float ps = p + __shfl_xor(p, 8, kWave);
+      ps += __shfl_xor(ps, 16, kWave);
+      ps += __shfl_xor(ps, 32, kWave);
+      l[h] = l[h] * alpha + ps;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) acc[h][i] = fmaf(p, vv[i], acc[h][i] * alpha);
+      m[h] = mn;
+    }
+  }
+  // sum the 8 key slots (same running max within the wave)
+#pragma unroll
+  for (int h = 0; h < GROUP; ++h)
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) {
+      float v = acc[h][i];
+      v += __shfl_xor(v, 8, kWave);
+      v += __shfl_xor(v, 16, kWave);
+      v += __shfl_xor(v, 32, kWave);
+      acc[h][i] = v;
+    }
+  if (slot == 0) {
+#pragma unroll
+    for (int h = 0; h < GROUP; ++h)
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) sm_o[wave][h][part * DPL + i] = acc[h][i];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < GROUP; ++h) {
+      sm_m[wave][h] = m[h];
+      sm_l[wave][h] = l[h];
+    }
+  }
+  __syncthreads();
+  // combine the 4 waves; thread t handles (head h, dim i) pairs
+  for (int idx = threadIdx.x; idx < GROUP * D; idx += blockDim.x) {
+    const int h = idx / D, i = idx % D;
+    float M = -INFINITY;
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][h]);
+    float o = 0.f, lsum = 0.f;
+    for (int w = 0; w < 4; ++w) {
+      const float f = (sm_m[w][h] == -INFINITY) ? 0.f : expf(sm_m[w][h] - M);
+      o = fmaf(f, sm_o[w][h][i], o);
+      lsum = fmaf(f, sm_l[w][h], lsum);
+    }
+    float* dst = partial + ((size_t)(g * GROUP + h) * nsplit + s) * (D + 2);
+    dst[2 + i] = o;
+    if (i == 0) {
+      dst[0] = M;
+      dst[1] = lsum;
+    }
+  }
+}
+
+// out[h*D + i] = sum_s e^{m_s - M} o_s[i] / sum_s e^{m_s - M} l_s
+__global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ partial, int nsplit, int D,
+                                                            float* __restrict__ out) {
+  const int h = blockIdx.x;
+  const float* p = partial + (size_t)h * nsplit * (D + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, p[s * (D + 2)]);
+  for (int i = threadIdx.x; i < D; i += blockDim.x) {
+    float o = 0.f, l = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+      const float ms = p[s * (D + 2)];
+      const float f = (ms == -INFINITY) ? 0.f : expf(ms - M);
+      o = fmaf(f, p[s * (D + 2) + 2 + i], o);
+      l = fmaf(f, p[s * (D + 2) + 1], l);
+    }
+    out[(size_t)h * D + i] = o / l;
+  }
+}
+
+// ------------------------------------------------------ prefill attention
+// Causal GQA flash attention in fp32 on the vector units. Block = (query
+// tile of QT positions, kv head g); its 64 query rows are the GROUP heads x QT
+// positions, 4 threads per row. Thread part p owns the float4 chunks
+// c = 4 i + p of head_dim. K/V tiles of 32 keys are staged in LDS.
+
+template <int D, int GROUP>
+__global__ __launch_bounds__(256) void attn_prefill_kernel(const float* __restrict__ qkv, int T, int ld, int NQ,
+                                                            int NKV, float* __restrict__ out, int ldo,
+                                                            float scale) {
+  constexpr int QT = 64 / GROUP;
+  constexpr int KT = 32;
+  constexpr int NC = D / 16;  // float4 chunks per thread
+  __shared__ float4 Ks[KT][D / 4];
+  __shared__ float4 Vs[KT][D / 4];
+  const int g = blockIdx.y;
+  const int t0 = blockIdx.x * QT;
+  const int row = threadIdx.x / 4, part = threadIdx.x % 4;
+  const int hh = row / QT, tq = row % QT;
+  const int t = t0 + tq;
+  const int h = g * GROUP + hh;
+  const bool active = t < T;
+
+  float4 q[NC], o[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    o[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    q[c] = active ? *reinterpret_cast<const float4*>(qkv + (size_t)t * ld + (size_t)h * D + (c * 4 + part) * 4)
+                  : make_float4(0.f, 0.f, 0.f, 0.f);
+    q[c].x *= scale; q[c].y *= scale; q[c].z *= scale; q[c].w *= scale;
+  }
+  float m = -INFINITY, l = 0.f;
+  const int t_last = min(T, t0 + QT) - 1;
+  const size_t koff = (size_t)NQ * D + (size_t)g * D;
+  const size_t voff = (size_t)(NQ + NKV) * D + (size_t)g * D;
+  for (int k0 = 0; k0 <= t_last; k0 += KT) {
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < KT * D / 4; idx += blockDim.x) {
+      const int kr = idx / (D / 4), kc = idx % (D / 4);
+      const int u = k0 + kr;
+      if (u < T) {
+        Ks[kr][kc] = *reinterpret_cast<const float4*>(qkv + (size_t)u * ld + koff + kc * 4);
+        Vs[kr][kc] = *reinterpret_cast<const float4*>(qkv + (size_t)u * ld + voff + kc * 4);
+      } else {
+        Ks[kr][kc] = make_float4(0.f, 0.f, 0.f, 0.f);
+        Vs[kr][kc] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    __syncthreads();
+    float s[KT];
+    float mx = m;
+#pragma unroll
+    for (int j = 0; j < KT; ++j) {
+      float a = 0.f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const float4 kk = Ks[j][c * 4 + part];
+        a = fmaf(q[c].x, kk.x, a);
+        a = fmaf(q[c].y, kk.y, a);
+        a = fmaf(q[c].z, kk.z, a);
+        a = fmaf(q[c].w, kk.w, a);
+      }
+      a += __shfl_xor(a, 1, kWave);
+      a += __shfl_xor(a, 2, kWave);
+      s[j] = (k0 + j <= t) ? a : -INFINITY;
+      mx = fmaxf(mx, s[j]);
+    }
+    if (mx == -INFINITY) continue;  // inactive row (t >= T): nothing visible yet
+    const float alpha = expf(m - mx);
+    l *= alpha;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      o[c].x *= alpha; o[c].y *= alpha; o[c].z *= alpha; o[c].w *= alpha;
+    }
+#pragma unroll
+    for (int j = 0; j < KT; ++j) {
+      const float p = (s[j] == -INFINITY) ? 0.f : expf(s[j] - mx);
+      l += p;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const float4 vv = Vs[j][c * 4 + part];
+        o[c].x = fmaf(p, vv.x, o[c].x);
+        o[c].y = fmaf(p, vv.y, o[c].y);
+        o[c].z = fmaf(p, vv.z, o[c].z);
+        o[c].w = fmaf(p, vv.w, o[c].w);
+      }
+    }
+    m = mx;
+  }
+  if (active) {
+    const float il = 1.f / l;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      float4 r = o[c];
+      r.x *= il; r.y *= il; r.z *= il; r.w *= il;
+      *reinterpret_cast<float4*>(out + (size_t)t * ldo + (size_t)h * D + (c * 4 + part) * 4) = r;
+    }
+  }
+}
+
+// ------------------------------------------------ prefill activations / GEMM
+// Activations are fp32; the bf16 MFMA consumes them as hi + lo bf16 pairs
+// (hi = bf16(v), lo = bf16(v - hi)), two MFMAs per tile, which keeps about 16
+// mantissa bits of every product against the exact bf16 weights.
+
+__global__ __launch_bounds__(256) void rms_split_kernel(const float* __restrict__ X, int K,
+                                                         const float* __restrict__ gain, float eps,
+                                                         uint16_t* __restrict__ hi, uint16_t* __restrict__ lo) {
+  __shared__ float red[8];
+  const int t = blockIdx.x;
+  const float* x = X + (size_t)t * K;
+  float inv = 1.f;
+  if (gain) {
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < K; i += blockDim.x) ss = fmaf(x[i], x[i], ss);
+    ss = block_sum(ss, red);
+    inv = 1.f / sqrtf(ss / (float)K + eps);
+  }
+  for (int i = threadIdx.x; i < K; i += blockDim.x) {
+    const float v = gain ? x[i] * inv * gain[i] : x[i];
+    const uint16_t h = f32_to_bf16_rne(v);
+    hi[(size_t)t * K + i] = h;
+    lo[(size_t)t * K + i] = f32_to_bf16_rne(v - bf16_to_f32(h));
+  }
+}
+
+__global__ __launch_bounds__(256) void rms_apply_kernel(const float* __restrict__ X, int K,
+                                                         const float* __restrict__ gain, float eps,
+                                                         float* __restrict__ out) {
+  __shared__ float red[8];
+  const int t = blockIdx.x;
+  const float* x = X + (size_t)t * K;
+  float inv = 1.f;
+  if (gain) {
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < K; i += blockDim.x) ss = fmaf(x[i], x[i], ss);
+    ss = block_sum(ss, red);
+    inv = 1.f / sqrtf(ss / (float)K + eps);
+  }
+  for (int i = threadIdx.x; i < K; i += blockDim.x) out[(size_t)t * K + i] = gain ? x[i] * inv * gain[i] : x[i];
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.f + expf(-g)) * u; }
+
+// C[M, N] (+)= (Ahi + Alo)[M, K] . W[N, K]^T with bf16 MFMA 16x16x32.
+// Block tile 64 x 64, 4 waves in 2 x 2, each wave 2 x 2 MFMA tiles.
+// MFMA operand layout (16x16x32): lane l supplies A[l % 16][8 (l / 16) + 0..7]
+// and B[8 (l / 16) + 0..7][l % 16]; it receives D[4 (l / 16) + 0..3][l % 16].
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_bf16x2_kernel(const uint16_t* __restrict__ Ahi,
+                                                           const uint16_t* __restrict__ Alo, int M, int K,
+                                                           const uint16_t* __restrict__ W, int N,
+                                                           float* __restrict__ C, int ldc) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int m0 = blockIdx.y * 64 + (wave / 2) * 32;
+  const int n0 = blockIdx.x * 64 + (wave % 2) * 32;
+  const int r = lane % 16, kq = (lane / 16) * 8;
+  f32x4_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const uint4 zero = make_uint4(0, 0, 0, 0);
+  for (int k = 0; k < K; k += 32) {
+    uint4 ah[2], al[2], b[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = m0 + i * 16 + r;
+      ah[i] = row < M ? *reinterpret_cast<const uint4*>(Ahi + (size_t)row * K + k + kq) : zero;
+      al[i] = row < M ? *reinterpret_cast<const uint4*>(Alo + (size_t)row * K + k + kq) : zero;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = n0 + j * 16 + r;
+      b[j] = col < N ? *reinterpret_cast<const uint4*>(W + (size_t)col * K + k + kq) : zero;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ah[i]),
+                                                            __builtin_bit_cast(bf16x8_t, b[j]), acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, al[i]),
+                                                            __builtin_bit_cast(bf16x8_t, b[j]), acc[i][j], 0, 0, 0);
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = n0 + j * 16 + (lane % 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = m0 + i * 16 + 4 * (lane / 16) + e;
+        const float v = acc[i][j][e];
+        if (EPI == EPI_SWIGLU) {
+          const float u = __shfl_xor(v, 8, kWave);
+          if ((lane % 16) < kGuGroup && row < M && col < N)
+            C[(size_t)row * ldc + (col / 16) * kGuGroup + (lane % 8)] = silu_mul(v, u);
+        } else if (row < M && col < N) {
+          if (EPI == EPI_RESID)
+            C[(size_t)row * ldc + col] += v;
+          else
+            C[(size_t)row * ldc + col] = v;
+        }
+      }
+    }
+}
+
+// fp32 weights: C[M, N] (+)= A[M, K] . W[N, K]^T on the vector units.
+// Block 16 x 16 threads computes a 32 x 32 tile (2 x 2 per thread); K tiles of
+// 16 staged in LDS. For the SwiGLU epilogue the tile's columns hold whole
+// interleave groups (32 = 2 groups of 16).
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ A, int M, int K,
+                                                        const float* __restrict__ W, int N, float* __restrict__ C,
+                                                        int ldc) {
+  __shared__ float As[32][17];
+  __shared__ float Ws[32][17];
+  __shared__ float Cs[32][33];
+  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+  const int m0 = blockIdx.y * 32, n0 = blockIdx.x * 32;
+  float acc[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    for (int idx = threadIdx.x; idx < 32 * 16; idx += 256) {
+      const int rr = idx / 16, kk = idx % 16;
+      As[rr][kk] = (m0 + rr < M && k0 + kk < K) ? A[(size_t)(m0 + rr) * K + k0 + kk] : 0.f;
+      Ws[rr][kk] = (n0 + rr < N && k0 + kk < K) ? W[(size_t)(n0 + rr) * K + k0 + kk] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = fmaf(As[ty * 2 + i][kk], Ws[tx * 2 + j][kk], acc[i][j]);
+    __syncthreads();
+  }
+  if (EPI == EPI_SWIGLU) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) Cs[ty * 2 + i][tx * 2 + j] = acc[i][j];
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 32 * 16; idx += 256) {
+      const int rr = idx / 16, jj = idx % 16;  // 16 outputs per row: 2 groups x 8
+      const int grp = jj / kGuGroup, e = jj % kGuGroup;
+      const int row = m0 + rr, pc = n0 + grp * 16 + e;
+      if (row < M && pc + kGuGroup < N + kGuGroup && pc < N)
+        C[(size_t)row * ldc + (pc / 16) * kGuGroup + e] = silu_mul(Cs[rr][grp * 16 + e], Cs[rr][grp * 16 + 8 + e]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int row = m0 + ty * 2 + i, col = n0 + tx * 2 + j;
+        if (row < M && col < N) {
+          if (EPI == EPI_RESID)
+            C[(size_t)row * ldc + col] += acc[i][j];
+          else
+            C[(size_t)row * ldc + col] = acc[i][j];
+        }
+      }
+  }
+}
+
+template <typename WT>
+__global__ void to_f32_kernel(const WT* __restrict__ src, size_t n, float* __restrict__ dst) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = load_w(src, i);
+}
+
+}  // namespace
+
+// ================================================================ launchers
+
+hipError_t launch_embed_decode(const Dims& d, bool bf16, const void* E, int token, const int32_t* token_dev,
+                               float* x, unsigned long long* key, hipStream_t st) {
+  if (bf16)
+    embed_decode_kernel<uint16_t><<<1, 256, 0, st>>>((const uint16_t*)E, d.H, d.V, token, token_dev, x, key);
+  else
+    embed_decode_kernel<float><<<1, 256, 0, st>>>((const float*)E, d.H, d.V, token, token_dev, x, key);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed_prefill(const Dims& d, bool bf16, const void* E, const int32_t* ids, int T,
+                                const float* audio, int a0, int La, float* X, hipStream_t st) {
+  if (bf16)
+    embed_prefill_kernel<uint16_t><<<T, 256, 0, st>>>((const uint16_t*)E, d.H, ids, audio, a0, La, X);
+  else
+    embed_prefill_kernel<float><<<T, 256, 0, st>>>((const float*)E, d.H, ids, audio, a0, La, X);
+  return hipGetLastError();
+}
+
+template <typename WT, int ROWS, int EPI>
+static hipError_t gemv_dispatch(const WT* W, int R, int K, const float* x, const float* gain, float eps, float* out,
+                                hipStream_t st) {
+  constexpr int VN = Chunk<WT>::N;
+  const int kch = (K / VN + kWave - 1) / kWave;
+  const int blocks = (R + 4 * ROWS - 1) / (4 * ROWS);
+  const size_t sh = (size_t)(K + 64) * sizeof(float);
+#define QDEC_GEMV_CASE(KC)                                                                           \
+  case KC:                                                                                           \
+    gemv_kernel<WT, ROWS, KC, EPI><<<blocks, 256, sh, st>>>(W, R, K, x, gain, eps, out);             \
+    break;
+  switch (kch) {
+    QDEC_GEMV_CASE(1)
+    QDEC_GEMV_CASE(2)
+    QDEC_GEMV_CASE(3)
+    QDEC_GEMV_CASE(4)
+    QDEC_GEMV_CASE(5)
+    QDEC_GEMV_CASE(6)
+    QDEC_GEMV_CASE(8)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef QDEC_GEMV_CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv(bool bf16, Epi epi, const void* W, int R, int K, const float* x, const float* gain,
+                       float eps, float* out, hipStream_t st) {
+  // SwiGLU needs 16 rows per block (one gate/up group): 4 waves x 4 rows.
+  if (bf16) {
+    const uint16_t* w = (const uint16_t*)W;
+    if (epi == EPI_STORE) return gemv_dispatch<uint16_t, 4, EPI_STORE>(w, R, K, x, gain, eps, out, st);
+    if (epi == EPI_RESID) return gemv_dispatch<uint16_t, 4, EPI_RESID>(w, R, K, x, gain, eps, out, st);
+    return gemv_dispatch<uint16_t, 4, EPI_SWIGLU>(w, R, K, x, gain, eps, out, st);
+  }
+  const float* w = (const float*)W;
+  if (epi == EPI_STORE) return gemv_dispatch<float, 4, EPI_STORE>(w, R, K, x, gain, eps, out, st);
+  if (epi == EPI_RESID) return gemv_dispatch<float, 4, EPI_RESID>(w, R, K, x, gain, eps, out, st);
+  return gemv_dispatch<float, 4, EPI_SWIGLU>(w, R, K, x, gain, eps, out, st);
+}
+
+hipError_t launch_lm_head(const Dims& d, bool bf16, const void* E, const float* x, const float* gain,
+                          float* logits, unsigned long long* key, hipStream_t st) {
+  constexpr int ROWS = 8;
+  const int blocks = (d.V + 4 * ROWS - 1) / (4 * ROWS);
+  const size_t sh = (size_t)(d.H + 64) * sizeof(float);
+  if (bf16) {
+    const int kch = (d.H / 8 + 63) / 64;
+    if (kch == 1)
+      lm_head_kernel<uint16_t, ROWS, 1><<<blocks, 256, sh, st>>>((const uint16_t*)E, d.V, d.H, x, gain, d.eps, logits, key);
+    else if (kch == 2)
+      lm_head_kernel<uint16_t, ROWS, 2><<<blocks, 256, sh, st>>>((const uint16_t*)E, d.V, d.H, x, gain, d.eps, logits, key);
+    else if (kch <= 4)
+      lm_head_kernel<uint16_t, ROWS, 4><<<blocks, 256, sh, st>>>((const uint16_t*)E, d.V, d.H, x, gain, d.eps, logits, key);
+    else if (kch <= 8)
+      lm_head_kernel<uint16_t, ROWS, 8><<<blocks, 256, sh, st>>>((const uint16_t*)E, d.V, d.H, x, gain, d.eps, logits, key);
+    else
+      return hipErrorInvalidValue;
+  } else {
+    const int kch = (d.H / 4 + 63) / 64;
+    if (kch == 1)
+      lm_head_kernel<float, ROWS, 1><<<blocks, 256, sh, st>>>((const float*)E, d.V, d.H, x, gain, d.eps, logits, key);
+    else if (kch == 2)
+      lm_head_kernel<float, ROWS, 2><<<blocks, 256, sh, st>>>((const float*)E, d.V, d.H, x, gain, d.eps, logits, key);
+    else if (kch <= 4)
+      lm_head_kernel<float, ROWS, 4><<<blocks, 256, sh, st>>>((const float*)E, d.V, d.H, x, gain, d.eps, logits, key);
+    else
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax_final(const unsigned long long* key, int n, int32_t* out, hipStream_t st) {
+  argmax_final_kernel<<<1, 64, 0, st>>>(key, n, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_reset_keys(unsigned long long* key, int n, hipStream_t st) {
+  reset_keys_kernel<<<1, 64, 0, st>>>(key, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_qk_rope_append(const Dims& d, float* qkv, int T, int pos0, const float* q_norm,
+                                 const float* k_norm, const float* rope_cos, const float* rope_sin,
+                                 const int64_t* page_table, int layer, hipStream_t st) {
+  dim3 grid(d.NQ + d.NKV, T);
+  qk_rope_append_kernel<<<grid, 64, 0, st>>>(qkv, d.qkv(), pos0, d.NQ, d.NKV, d.D, d.L, d.eps, q_norm, k_norm,
+                                             rope_cos, rope_sin, page_table, layer);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_decode(const Dims& d, const float* q, int n, const int64_t* page_table, int layer,
+                              float* partial, float* out, hipStream_t st) {
+  const int nsplit = (n + kAttnChunk - 1) / kAttnChunk;
+  const int group = d.NQ / d.NKV;
+  const float scale = 1.f / sqrtf((float)d.D);
+  dim3 grid(d.NKV, nsplit);
+#define QDEC_ATTN_CASE(DD, GG)                                                                             \
+  if (d.D == DD && group == GG) {                                                                          \
+    attn_decode_kernel<DD, GG><<<grid, 256, 0, st>>>(q, n, d.NKV, d.L, page_table, layer, partial, nsplit, scale); \
+  } else
+  QDEC_ATTN_CASE(128, 2)
+  QDEC_ATTN_CASE(128, 1)
+  QDEC_ATTN_CASE(128, 4)
+  QDEC_ATTN_CASE(128, 8)
+  QDEC_ATTN_CASE(64, 2)
+  QDEC_ATTN_CASE(32, 2)
+  QDEC_ATTN_CASE(32, 1)
+  QDEC_ATTN_CASE(32, 4)
+  return hipErrorInvalidValue;
+#undef QDEC_ATTN_CASE
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  attn_combine_kernel<<<d.NQ, 128, 0, st>>>(partial, nsplit, d.D, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_prefill(const Dims& d, const float* qkv, int T, float* out, hipStream_t st) {
+  const int group = d.NQ / d.NKV;
+  const float scale = 1.f / sqrtf((float)d.D);
+#define QDEC_PATTN_CASE(DD, GG)                                                                      \
+  if (d.D == DD && group == GG) {                                                                    \
+    dim3 grid((T + 64 / GG - 1) / (64 / GG), d.NKV);                                                \
+    attn_prefill_kernel<DD, GG><<<grid, 256, 0, st>>>(qkv, T, d.qkv(), d.NQ, d.NKV, out, d.NQ * d.D, scale); \
+  } else
+  QDEC_PATTN_CASE(128, 2)
+  QDEC_PATTN_CASE(128, 1)
+  QDEC_PATTN_CASE(128, 4)
+  QDEC_PATTN_CASE(128, 8)
+  QDEC_PATTN_CASE(64, 2)
+  QDEC_PATTN_CASE(32, 2)
+  QDEC_PATTN_CASE(32, 1)
+  QDEC_PATTN_CASE(32, 4)
+  return hipErrorInvalidValue;
+#undef QDEC_PATTN_CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_rms_split(const float* X, int T, int K, const float* gain, float eps, uint16_t* hi,
+                            uint16_t* lo, hipStream_t st) {
+  rms_split_kernel<<<T, 256, 0, st>>>(X, K, gain, eps, hi, lo);
+  return hipGetLastError();
+}
+
+hipError_t launch_rms_apply(const float* X, int T, int K, const float* gain, float eps, float* out,
+                            hipStream_t st) {
+  rms_apply_kernel<<<T, 256, 0, st>>>(X, K, gain, eps, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(bool bf16, Epi epi, const void* A0, const void* A1, int M, int K, const void* W, int N,
+                       float* C, int ldc, hipStream_t st) {
+  if (bf16) {
+    if (K % 32 != 0) return hipErrorInvalidValue;
+    dim3 grid((N + 63) / 64, (M + 63) / 64);
+    const uint16_t *hi = (const uint16_t*)A0, *lo = (const uint16_t*)A1, *w = (const uint16_t*)W;
+    if (epi == EPI_STORE)
+      gemm_bf16x2_kernel<EPI_STORE><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc);
+    else if (epi == EPI_RESID)
+      gemm_bf16x2_kernel<EPI_RESID><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc);
+    else
+      gemm_bf16x2_kernel<EPI_SWIGLU><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc);
+  } else {
+    dim3 grid((N + 31) / 32, (M + 31) / 32);
+    const float *a = (const float*)A0, *w = (const float*)W;
+    if (epi == EPI_STORE)
+      gemm_f32_kernel<EPI_STORE><<<grid, 256, 0, st>>>(a, M, K, w, N, C, ldc);
+    else if (epi == EPI_RESID)
+      gemm_f32_kernel<EPI_RESID><<<grid, 256, 0, st>>>(a, M, K, w, N, C, ldc);
+    else
+      gemm_f32_kernel<EPI_SWIGLU><<<grid, 256, 0, st>>>(a, M, K, w, N, C, ldc);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_to_f32(const void* src, bool bf16, size_t n, float* dst, hipStream_t st) {
+  const int blocks = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
+  if (bf16)
+    to_f32_kernel<uint16_t><<<blocks, 256, 0, st>>>((const uint16_t*)src, n, dst);
+  else
+    to_f32_kernel<float><<<blocks, 256, 0, st>>>((const float*)src, n, dst);
+  return hipGetLastError();
+}
+
+}  // namespace qdec

@@ -1,0 +1,187 @@
+"""Python binding of the qdec C ABI (include/qdec.h): argument marshalling only.
+
+Every function has the C name and raises QdecError(code, message) when the C
+call returns a non-zero status. Device buffers are passed as integer device
+addresses (e.g. ``tensor.data_ptr()`` of a torch tensor on the GPU); streams
+as ``torch.cuda.current_stream().cuda_stream``. The library must have been
+built (``python -m qwen3_kv_cache_amd.build``); there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqdec.so")
+
+QDEC_OK = 0
+QDEC_E_INVALID = -1
+QDEC_E_POS = -2
+QDEC_E_CAPACITY = -3
+QDEC_E_STATE = -4
+QDEC_E_OOM = -5
+QDEC_E_DEVICE = -6
+
+QDEC_F32 = 0
+QDEC_BF16 = 1
+QDEC_PAGE = 16
+
+(QDEC_W_IN_NORM, QDEC_W_Q, QDEC_W_K, QDEC_W_V, QDEC_W_Q_NORM, QDEC_W_K_NORM, QDEC_W_O,
+ QDEC_W_POST_NORM, QDEC_W_GATE, QDEC_W_UP, QDEC_W_DOWN, QDEC_W_PER_LAYER) = range(12)
+
+EXPORTS = ("qdec_create", "qdec_destroy", "qdec_state_create", "qdec_state_destroy", "qdec_prefill",
+           "qdec_decode_step", "qdec_decode_step_dev", "qdec_decode_batch", "qdec_clone_state",
+           "qdec_state_pos", "qdec_last_error")
+
+
+class QdecError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"qdec error {code}: {msg}")
+        self.code = code
+
+
+class qdec_config(ctypes.Structure):
+    _fields_ = [("n_layer", ctypes.c_int32), ("hidden", ctypes.c_int32), ("n_q_head", ctypes.c_int32),
+                ("n_kv_head", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("ffn", ctypes.c_int32),
+                ("vocab", ctypes.c_int32), ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
+                ("weight_dtype", ctypes.c_int32), ("tied", ctypes.c_int32)]
+
+
+class qdec_weights(ctypes.Structure):
+    _fields_ = [("embed", ctypes.c_void_p), ("final_norm", ctypes.c_void_p),
+                ("layer", ctypes.POINTER(ctypes.c_void_p))]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqdec.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} not built; run python -m qwen3_kv_cache_amd.build")
+    # torch's ROCm wheel carries its own HIP runtime, loaded under the bare
+    # name libamdhip64.so. Load it first: libqdec.so then binds to that same
+    # runtime by soname, and the process holds a single HIP runtime (two
+    # runtimes side by side do not share devices, streams or allocations).
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    sig = {
+        "qdec_create": (ctypes.c_int, [ctypes.POINTER(qdec_config), ctypes.POINTER(qdec_weights), vp,
+                                       ctypes.POINTER(vp)]),
+        "qdec_destroy": (ctypes.c_int, [vp]),
+        "qdec_state_create": (ctypes.c_int, [vp, i32, ctypes.POINTER(vp)]),
+        "qdec_state_destroy": (None, [vp]),
+        "qdec_prefill": (ctypes.c_int, [vp, ctypes.POINTER(i32), i32, vp, i32, i32, vp, vp]),
+        "qdec_decode_step": (ctypes.c_int, [vp, i32, i32, vp, vp]),
+        "qdec_decode_step_dev": (ctypes.c_int, [vp, vp, i32, vp, vp]),
+        "qdec_decode_batch": (ctypes.c_int, [ctypes.POINTER(vp), i32, ctypes.POINTER(i32), vp, vp]),
+        "qdec_clone_state": (ctypes.c_int, [vp, ctypes.POINTER(vp)]),
+        "qdec_state_pos": (i32, [vp]),
+        "qdec_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype, f.argtypes = res, args
+    _lib = L
+    return L
+
+
+def qdec_last_error() -> str:
+    return lib().qdec_last_error().decode()
+
+
+def _check(code: int) -> None:
+    if code != QDEC_OK:
+        raise QdecError(code, qdec_last_error())
+
+
+def _ptr(p) -> Optional[int]:
+    return None if p is None or p == 0 else int(p)
+
+
+def qdec_create(cfg: qdec_config, weights: qdec_weights, stream: int = 0) -> int:
+    out = ctypes.c_void_p()
+    _check(lib().qdec_create(ctypes.byref(cfg), ctypes.byref(weights), _ptr(stream), ctypes.byref(out)))
+    return out.value
+
+
+def qdec_destroy(model: int) -> None:
+    _check(lib().qdec_destroy(_ptr(model)))
+
+
+def qdec_state_create(model: int, max_ctx: int) -> int:
+    out = ctypes.c_void_p()
+    _check(lib().qdec_state_create(_ptr(model), int(max_ctx), ctypes.byref(out)))
+    return out.value
+
+
+def qdec_state_destroy(state: int) -> None:
+    lib().qdec_state_destroy(_ptr(state))
+
+
+def qdec_prefill(state: int, ids_host, n_tokens: int, audio_dev, audio_begin: int, audio_len: int,
+                 logits_dev=None, argmax_dev=None) -> None:
+    ids = np.ascontiguousarray(ids_host, dtype=np.int32)
+    if ids.size < n_tokens:
+        raise ValueError("ids_host shorter than n_tokens")
+    p = ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    _check(lib().qdec_prefill(_ptr(state), p, int(n_tokens), _ptr(audio_dev), int(audio_begin), int(audio_len),
+                              _ptr(logits_dev), _ptr(argmax_dev)))
+
+
+def qdec_decode_step(state: int, token: int, pos: int, logits_dev=None, argmax_dev=None) -> None:
+    _check(lib().qdec_decode_step(_ptr(state), int(token), int(pos), _ptr(logits_dev), _ptr(argmax_dev)))
+
+
+def qdec_decode_step_dev(state: int, token_dev, pos: int, logits_dev=None, argmax_dev=None) -> None:
+    _check(lib().qdec_decode_step_dev(_ptr(state), _ptr(token_dev), int(pos), _ptr(logits_dev),
+                                      _ptr(argmax_dev)))
+
+
+def qdec_decode_batch(states: Sequence[int], tokens_host, logits_dev=None, argmax_dev=None) -> None:
+    n = len(states)
+    arr = (ctypes.c_void_p * max(n, 1))(*[_ptr(s) for s in states])
+    toks = np.ascontiguousarray(tokens_host, dtype=np.int32)
+    if toks.size < n:
+        raise ValueError("tokens_host shorter than the batch")
+    _check(lib().qdec_decode_batch(arr, n, toks.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                   _ptr(logits_dev), _ptr(argmax_dev)))
+
+
+def qdec_clone_state(src: int) -> int:
+    out = ctypes.c_void_p()
+    _check(lib().qdec_clone_state(_ptr(src), ctypes.byref(out)))
+    return out.value
+
+
+def qdec_state_pos(state: int) -> int:
+    return lib().qdec_state_pos(_ptr(state))
+
+
+# ---------------------------------------------------------------- helpers
+
+def make_config(hidden, n_layer, n_q_head, n_kv_head, head_dim, ffn, vocab, rms_eps=1e-6, rope_theta=1e6,
+                bf16=True, tied=1) -> qdec_config:
+    return qdec_config(n_layer, hidden, n_q_head, n_kv_head, head_dim, ffn, vocab, rms_eps, rope_theta,
+                       QDEC_BF16 if bf16 else QDEC_F32, tied)
+
+
+class WeightTable:
+    """qdec_weights built from device addresses; keeps the host pointer table
+    alive. `layer_ptrs[i][t]` is layer i's tensor t (QDEC_W_* order)."""
+
+    def __init__(self, embed: int, final_norm: int, layer_ptrs: Sequence[Sequence[int]]):
+        flat = [int(p) for row in layer_ptrs for p in row]
+        self._arr = (ctypes.c_void_p * max(len(flat), 1))(*flat)
+        self.c = qdec_weights(int(embed), int(final_norm),
+                              ctypes.cast(self._arr, ctypes.POINTER(ctypes.c_void_p)))

@@ -1,0 +1,57 @@
+"""GPU parity at sizes the float64 oracle finishes in seconds, spanning several
+tiles and ragged tails: teacher-forced prefill + decode logits and argmax."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+from .gpu_harness import check_steps, device_model, mid_workload, oracle_forced, run_forced
+
+pytestmark = pytest.mark.gpu
+
+MID = {
+    # D=64, GQA 2, context crosses the 256-position split and many pages;
+    # T=300 leaves a ragged GEMM tile, V=5003 a ragged LM-head block
+    "d64_g2": (synth.custom_shape(hidden=256, n_layer=2, n_q_head=4, n_kv_head=2, head_dim=64, ffn=768,
+                                  vocab=5003, bf16=True), 300, 17, 100, 12),
+    # D=128, GQA 2 (the 0.6B head geometry), 3 layers
+    "d128_g2": (synth.custom_shape(hidden=512, n_layer=3, n_q_head=8, n_kv_head=4, head_dim=128, ffn=1536,
+                                   vocab=4099, bf16=True), 77, 8, 20, 10),
+    # GQA 4 with fp32 weights
+    "d32_g4_f32": (synth.custom_shape(hidden=128, n_layer=2, n_q_head=8, n_kv_head=2, head_dim=32, ffn=384,
+                                      vocab=777, bf16=False), 45, 3, 9, 6),
+    # MHA (group 1), D=128, one layer, prompt of one token
+    "d128_g1_T1": (synth.custom_shape(hidden=256, n_layer=1, n_q_head=4, n_kv_head=4, head_dim=128, ffn=512,
+                                      vocab=1000, bf16=True), 1, 0, 0, 20),
+}
+
+
+def test_tiny_teacher_forced():
+    w = synth.WORKLOADS["tiny"]
+    W = synth.make_weights(w.shape, w.weight_seed)
+    ids, audio, a0 = synth.make_prompt(w)
+    orc = oracle.Qwen3Oracle(oracle.OracleConfig.from_shape(w.shape), W.f32)
+    toks, ref = oracle.greedy_trajectory(orc, ids, audio, a0, w.n_decode)
+    m = device_model(w.shape, W)
+    try:
+        gpu, amax = run_forced(m, ids, audio, a0, toks[:-1])
+    finally:
+        m.close()
+    worst = check_steps(gpu, amax, ref, fp32=True, label="tiny")
+    print("tiny", worst)
+
+
+@pytest.mark.parametrize("name", sorted(MID))
+def test_mid_shapes(name):
+    shape, T, a0, La, n = MID[name]
+    W, ids, audio, a0, forced = mid_workload(shape, 7, T, a0, La, n)
+    orc = oracle.Qwen3Oracle(oracle.OracleConfig.from_shape(shape), W.f32)
+    ref = oracle_forced(orc, ids, audio, a0, forced)
+    m = device_model(shape, W)
+    try:
+        gpu, amax = run_forced(m, ids, audio, a0, forced)
+    finally:
+        m.close()
+    worst = check_steps(gpu, amax, ref, fp32=not shape.bf16, label=name)
+    print(name, worst)
