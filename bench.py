@@ -1,0 +1,192 @@
+"""Benchmark: decode tok/s (B=1) and prefill tok/s of the Qwen3-0.6B-shaped
+KV-cache decoder on one MI355X, with a roofline figure and the CPU oracle
+timed on the host as a reported baseline.
+
+One step = one pass of the whole path over one synthetic request of the
+default workload: prefill a 48-token prompt whose rows 8..30 are audio
+embedding rows, then 64 greedy decode steps, each feeding the previous
+step's device argmax (no host round trip). Inputs and weights are resident in
+HBM before timing; states are created before the timed region.
+
+Usage: python bench.py [--steps K] [--warmup W] [--workload short|long|prefill8k|branch16]
+       python bench.py --copy-probe   (plain copy kernel for counter calibration)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+METRIC = "decode tok/s (B=1,B=16) + prefill tok/s, Qwen3-0.6B bf16; % HBM peak"
+
+
+def decode_bytes(shape, ctx_lens) -> float:
+    """Algorithmic HBM bytes of one decode token at each attended length p:
+    every bf16 weight once (layers + tied head), the fp32 K and V of p
+    positions, the new K/V row, and the embedding row."""
+    H, L, D = shape.hidden, shape.n_layer, shape.head_dim
+    layer_w = (shape.n_q_head * D * H + 2 * shape.n_kv_head * D * H + H * shape.n_q_head * D + 3 * shape.ffn * H) * 2
+    norms = (2 * H + 2 * D) * 2
+    head = shape.vocab * H * 2
+    kv_row = 2 * shape.n_kv_head * D * 4
+    w = L * (layer_w + norms) + head + H * 2
+    return float(np.mean([w + L * kv_row * p + L * kv_row for p in ctx_lens]))
+
+
+def copy_probe():
+    import torch
+    n = 1 << 28  # 1 GiB of fp32
+    a = torch.empty(n, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "launches": 5}))
+
+
+def cpu_baseline(w, W, n_decode_sample: int):
+    """The float64 oracle on the host: prefill of the same prompt and a bounded
+    number of greedy decode steps; returns decode tok/s and prefill tok/s."""
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    orc = oracle.Qwen3Oracle(oracle.OracleConfig.from_shape(w.shape), W.f32)
+    ids, audio, a0 = synth.make_prompt(w)
+    st = orc.new_state()
+    t0 = time.perf_counter()
+    lg = orc.prefill(st, ids, audio, a0)
+    t_pre = time.perf_counter() - t0
+    tok = oracle.pick_token(lg)
+    t0 = time.perf_counter()
+    for s in range(n_decode_sample):
+        lg = orc.decode(st, tok, w.prompt_len + s)
+        tok = oracle.pick_token(lg)
+    t_dec = time.perf_counter() - t0
+    return {"value": n_decode_sample / t_dec, "unit": "decode tok/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 numpy oracle: prefill of the {w.prompt_len}-token prompt "
+                      f"({w.prompt_len / t_pre:.1f} prefill tok/s) then {n_decode_sample} greedy decode steps, B=1"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="short")
+    ap.add_argument("--cpu-sample", type=int, default=24, help="oracle decode steps for the CPU baseline (0 = skip)")
+    ap.add_argument("--copy-probe", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {a.gpus}); the decoder is single-GPU by design.",
+              file=sys.stderr)
+        sys.exit(2)
+    if a.copy_probe:
+        copy_probe()
+        return
+
+    import torch
+
+    import synth
+    from qwen3_kv_cache_amd import qdec
+    from qwen3_kv_cache_amd.device import Model
+
+    w = synth.WORKLOADS[a.workload]
+    dev = torch.device("cuda:0")
+    W = synth.make_weights(w.shape, w.weight_seed)
+    model = Model(w.shape, W.bits if w.shape.bf16 else W.f32, bf16=w.shape.bf16)
+    ids, audio, a0 = synth.make_prompt(w)
+    audio_d = torch.from_numpy(audio).to(dev)
+    V = w.shape.vocab
+    B = w.n_branch
+    n = w.n_decode
+    logits = torch.zeros((B, V), dtype=torch.float32, device=dev)
+    toks = torch.zeros((n + 1, B), dtype=torch.int32, device=dev)
+    streams = np.stack([synth.branch_stream(w, b) for b in range(B)]) if B > 1 else None
+    total = a.warmup + a.steps
+    states = [qdec.qdec_state_create(model.handle, w.max_ctx) for _ in range(total)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(total)]
+    torch.cuda.synchronize()
+
+    def one_step(i):
+        st = states[i]
+        e0, e1, e2 = ev[i]
+        e0.record()
+        qdec.qdec_prefill(st, ids, len(ids), audio_d.data_ptr(), a0, len(audio), None, toks[0].data_ptr())
+        e1.record()
+        if B == 1:
+            for s in range(n):
+                qdec.qdec_decode_step_dev(st, toks[s].data_ptr(), w.prompt_len + s, None, toks[s + 1].data_ptr())
+        else:
+            br = [qdec.qdec_clone_state(st) for _ in range(B)]
+            for s in range(n):
+                qdec.qdec_decode_batch(br, streams[:, s], None, toks[s + 1].data_ptr())
+            e2.record()
+            torch.cuda.synchronize()
+            for b in br:
+                qdec.qdec_state_destroy(b)
+            return
+        e2.record()
+
+    for i in range(a.warmup):
+        one_step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.warmup, total):
+        one_step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(a.warmup, total)])
+    dec_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(a.warmup, total)])
+    for st in states:
+        qdec.qdec_state_destroy(st)
+
+    decode_tok_s = n * B * a.steps / (dec_ms.sum() / 1e3)
+    prefill_tok_s = w.prompt_len * a.steps / (pre_ms.sum() / 1e3)
+    ctx = [w.prompt_len + s + 1 for s in range(n)]
+    bytes_tok = decode_bytes(w.shape, ctx)
+    per_tok_s = dec_ms.mean() / 1e3 / n
+    achieved = bytes_tok / per_tok_s / 1e9 if B == 1 else None
+    line = {
+        "metric": METRIC,
+        "value": round(decode_tok_s, 2),
+        "unit": "decode tok/s" if B == 1 else "decode tok/s (B=16, summed over branches)",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(wall / a.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 weights, fp32 activations/KV",
+        "data": "synthetic (seeded random-init weights of the Qwen3-0.6B shape, uniform ids, N(0,1) audio rows)",
+        "config": {"workload": f"{w.name}: Qwen3-0.6B shape, {w.prompt_len}-token prompt with {w.audio_len} audio rows, "
+                               f"prefill then {n} greedy decode steps" + (f" x {B} cloned branches" if B > 1 else ", B=1"),
+                   "prompt_len": w.prompt_len, "audio_rows": w.audio_len, "decode_steps": n, "batch": B},
+        "prefill_tok_s": round(prefill_tok_s, 1),
+        "prefill_ms": round(float(pre_ms.mean()), 4),
+        "decode_ms_per_token": round(float(dec_ms.mean()) / n, 5),
+    }
+    if achieved is not None:
+        line["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                            "kernel": "whole decode step", "bytes_per_unit": round(bytes_tok)}
+    if a.cpu_sample > 0:
+        line["cpu_baseline"] = cpu_baseline(w, W, a.cpu_sample)
+    model.close()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

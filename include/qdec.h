@@ -78,7 +78,7 @@ enum {
 };
 
 /* Model shape. Validated by qdec_create (QDEC_E_INVALID otherwise):
- * n_layer >= 1; hidden a multiple of 64 and <= 8192; head_dim even, a
+ * 1 <= n_layer <= 127; hidden a multiple of 64 and <= 8192; head_dim even, a
  * multiple of 8 and <= 128; n_kv_head >= 1 and n_q_head a multiple of
  * n_kv_head with n_q_head / n_kv_head <= 8; ffn a multiple of 16 and <= 16384;
  * n_q_head * head_dim <= 8192; vocab >= 2; rms_eps > 0; rope_theta > 1;

@@ -6,7 +6,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqdec.so")
-SOURCES = ["qdec_api.cpp", "qdec_kernels.hip"]
+SOURCES = ["qdec_api.cpp", "qdec_kernels.hip", "qdec_decode_mk.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -17,20 +17,20 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str = LIB, extra=()) -> str:
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *srcs, "-o", tmp]
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *FLAGS, *extra, *srcs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
-    out = (r.stdout + r.stderr).replace(
+    log = (r.stdout + r.stderr).replace(
         "'-packed-fp32-ops' is not a recognized feature for this target (ignoring feature)\n", "")
     if r.returncode != 0:
-        sys.stderr.write(out)
+        sys.stderr.write(log)
         raise RuntimeError("hipcc failed: " + " ".join(cmd))
-    if verbose and out.strip():
-        sys.stderr.write(out)
-    os.replace(tmp, LIB)
-    return LIB
+    if verbose and log.strip():
+        sys.stderr.write(log)
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -151,6 +151,16 @@ struct qdec_model {
   void* pA1 = nullptr;  // bf16 lo
   PagePool pool;
   int live_states = 0;
+  // persistent decode step
+  int mk_blocks = 0;
+  int mk_split_max = 1;
+  unsigned long long* ll = nullptr;
+  size_t ll_words = 0, o_qkv = 0, o_att = 0, o_atto = 0, o_xb = 0, o_z = 0, o_xa = 0, o_key = 0;
+  unsigned mk_seq = 0;
+  int* err_host = nullptr;
+  int* err_dev = nullptr;
+  size_t layer_elems = 0, off_o = 0, off_gu = 0, off_d = 0;
+  int norm_elems = 0;
 };
 
 struct qdec_state {
@@ -165,7 +175,7 @@ namespace {
 
 int validate_config(const qdec_config* c) {
   if (!c) return fail(QDEC_E_INVALID, "config is NULL");
-  if (c->n_layer < 1 || c->n_layer > 256) return fail(QDEC_E_INVALID, "n_layer %d out of range", c->n_layer);
+  if (c->n_layer < 1 || c->n_layer > 127) return fail(QDEC_E_INVALID, "n_layer %d out of range", c->n_layer);
   if (c->hidden < 64 || c->hidden > 8192 || c->hidden % 64)
     return fail(QDEC_E_INVALID, "hidden %d must be a multiple of 64 in [64, 8192]", c->hidden);
   if (c->head_dim < 8 || c->head_dim > 128 || c->head_dim % 8)
@@ -221,6 +231,8 @@ void free_model(qdec_model* m) {
   (void)hipFree(m->keys);
   (void)hipFree(m->argmax_tmp);
   free_prefill(m);
+  (void)hipFree(m->ll);
+  if (m->err_host) (void)hipHostFree(m->err_host);
   for (void* c : m->pool.chunks) (void)hipFree(c);
   delete m;
 }
@@ -303,25 +315,55 @@ int ensure_prefill(qdec_model* m, int T) {
     if (e_ != hipSuccess) return fail(QDEC_E_DEVICE, "%s: %s", #expr, hipGetErrorString(e_)); \
   } while (0)
 
-// One decode step for one sequence; the state's n_past is updated by the caller.
+// Exchange tags must not repeat between launches while stale words could
+// still hold them; the word buffer is cleared once per tag period.
+constexpr unsigned kTagPeriod = 4000000u;
+
+// One decode step for one sequence as a single cooperative launch; the
+// state's n_past is updated by the caller.
 int run_decode(qdec_state* s, int token, const int32_t* token_dev, int pos, float* logits, int32_t* argmax) {
   qdec_model* m = s->m;
   const Dims& d = m->d;
   hipStream_t st = m->stream;
-  const int n = pos + 1;
-  LAUNCH(launch_embed_decode(d, m->bf16, m->embed, token, token_dev, m->x, m->keys, st));
-  for (int l = 0; l < d.L; ++l) {
-    const LayerW& w = m->layers[l];
-    LAUNCH(launch_gemv(m->bf16, EPI_STORE, w.wqkv, d.qkv(), d.H, m->x, w.in_norm, d.eps, m->qkv, st));
-    LAUNCH(launch_qk_rope_append(d, m->qkv, 1, pos, w.q_norm, w.k_norm, m->rope_cos, m->rope_sin, s->pt_dev, l,
-                                 st));
-    LAUNCH(launch_attn_decode(d, m->qkv, n, s->pt_dev, l, m->partial, m->attn, st));
-    LAUNCH(launch_gemv(m->bf16, EPI_RESID, w.wo, d.H, d.NQ * d.D, m->attn, nullptr, d.eps, m->x, st));
-    LAUNCH(launch_gemv(m->bf16, EPI_SWIGLU, w.wgu, 2 * d.F, d.H, m->x, w.post_norm, d.eps, m->z, st));
-    LAUNCH(launch_gemv(m->bf16, EPI_RESID, w.wd, d.H, d.F, m->z, nullptr, d.eps, m->x, st));
-  }
-  LAUNCH(launch_lm_head(d, m->bf16, m->embed, m->x, m->final_norm, logits, m->keys, st));
-  LAUNCH(launch_argmax_final(m->keys, 1, argmax ? argmax : m->argmax_tmp, st));
+  if (__atomic_load_n(m->err_host, __ATOMIC_ACQUIRE))
+    return fail(QDEC_E_DEVICE, "an earlier decode launch hit its time limit; the model must be recreated");
+  const unsigned k = m->mk_seq % kTagPeriod;
+  if (k == 0 && m->mk_seq != 0) HIP_TRY(hipMemsetAsync(m->ll, 0, m->ll_words * sizeof(unsigned long long), st));
+  ++m->mk_seq;
+  MkLaunch a{};
+  a.d = d;
+  a.bf16 = m->bf16;
+  a.nblocks = m->mk_blocks;
+  a.wbuf = m->wbuf;
+  a.layer_elems = m->layer_elems;
+  a.off_o = m->off_o;
+  a.off_gu = m->off_gu;
+  a.off_d = m->off_d;
+  a.nbuf = m->nbuf;
+  a.norm_elems = m->norm_elems;
+  a.embed = m->embed;
+  a.final_norm = m->final_norm;
+  a.rope_cos = m->rope_cos;
+  a.rope_sin = m->rope_sin;
+  a.page_table = s->pt_dev;
+  a.pos = pos;
+  a.token = token;
+  a.token_dev = token_dev;
+  const int want = (pos + 63) / 64;
+  a.nsplit = std::max(1, std::min(want, m->mk_split_max));
+  a.logits = logits;
+  a.argmax_out = argmax ? argmax : m->argmax_tmp;
+  a.ll = m->ll;
+  a.o_qkv = m->o_qkv;
+  a.o_att = m->o_att;
+  a.o_atto = m->o_atto;
+  a.o_xb = m->o_xb;
+  a.o_z = m->o_z;
+  a.o_xa = m->o_xa;
+  a.o_key = m->o_key;
+  a.tag0 = (k + 1u) * 1024u;
+  a.err = m->err_dev;
+  LAUNCH(launch_decode_mk(a, st));
   return QDEC_OK;
 }
 
@@ -480,6 +522,47 @@ int qdec_create(const qdec_config* cfg, const qdec_weights* w, void* hip_stream,
     m->layers[l] = LayerW{qkv, o, gu, dn, nb, nb + d.H, nb + 2 * d.H, nb + 2 * d.H + d.D};
   }
   if ((he = launch_to_f32(w->final_norm, m->bf16, d.H, m->final_norm, st))) return fail_dev("final_norm", he);
+  m->layer_elems = per_layer;
+  m->off_o = n_qkv;
+  m->off_gu = n_qkv + n_o;
+  m->off_d = n_qkv + n_o + n_gu;
+  m->norm_elems = (int)norms_per_layer;
+  // persistent decode: one workgroup per CU, all resident (cooperative launch)
+  {
+    int dev = 0;
+    hipDeviceProp_t prop;
+    if ((he = hipGetDevice(&dev)) || (he = hipGetDeviceProperties(&prop, dev))) return fail_dev("device query", he);
+    m->mk_blocks = prop.multiProcessorCount;
+    m->mk_split_max = std::max(1, std::min(64, m->mk_blocks / d.NKV));
+    const size_t lds = std::max(mk_lds_bytes(d, 1), std::max(mk_lds_bytes(d, 2), mk_lds_bytes(d, m->mk_split_max)));
+    int occ = 0;
+    if ((he = mk_prepare(m->bf16, d, lds, &occ))) return fail_dev("decode kernel setup", he);
+    if (occ < 1) {
+      free_model(m);
+      return fail(QDEC_E_INVALID, "decode kernel does not fit one workgroup per CU (LDS %zu bytes)", lds);
+    }
+    const size_t QKV = (size_t)d.qkv();
+    size_t o = 0;
+    m->o_qkv = o; o += 2 * QKV;
+    m->o_att = o; o += 2 * (size_t)d.NQ * m->mk_split_max * (d.D + 2);
+    m->o_atto = o; o += 2 * (size_t)d.NQ * d.D;
+    m->o_xb = o; o += 2 * (size_t)d.H;
+    m->o_z = o; o += 2 * (size_t)d.F;
+    m->o_xa = o; o += 2 * (size_t)d.H;
+    m->o_key = o; o += 2 * (size_t)m->mk_blocks;
+    m->ll_words = o;
+    if ((e = dev_alloc(&m->ll, o, "exchange words"))) {
+      free_model(m);
+      return e;
+    }
+    if ((he = hipMemsetAsync(m->ll, 0, o * sizeof(unsigned long long), st))) return fail_dev("exchange init", he);
+    if ((he = hipHostMalloc((void**)&m->err_host, sizeof(int), hipHostMallocMapped))) {
+      m->err_host = nullptr;
+      return fail_dev("error flag", he);
+    }
+    *m->err_host = 0;
+    if ((he = hipHostGetDevicePointer((void**)&m->err_dev, m->err_host, 0))) return fail_dev("error flag map", he);
+  }
   if ((he = hipStreamSynchronize(st))) return fail_dev("weight packing", he);
   if ((e = ensure_rope(m, 4096)) || (e = ensure_partial(m, 4096))) {
     free_model(m);

@@ -73,4 +73,32 @@ hipError_t launch_gemm(bool bf16, Epi epi, const void* A0, const void* A1, int M
                        float* C, int ldc, hipStream_t st);
 hipError_t launch_to_f32(const void* src, bool bf16, size_t n, float* dst, hipStream_t st);
 
+// ---- persistent decode step (qdec_decode_mk.hip)
+struct MkLaunch {
+  Dims d;
+  bool bf16;
+  int nblocks;                      // one workgroup per CU
+  const void* wbuf;                 // packed layer weights, layer l at wbuf + l * layer_elems
+  size_t layer_elems, off_o, off_gu, off_d;
+  const float* nbuf;                // fp32 norm gains, layer l at nbuf + l * norm_elems
+  int norm_elems;
+  const void* embed;
+  const float* final_norm;
+  const float* rope_cos;
+  const float* rope_sin;
+  const int64_t* page_table;
+  int pos, token;
+  const int32_t* token_dev;
+  int nsplit;                       // attention splits per KV head
+  float* logits;
+  int32_t* argmax_out;
+  unsigned long long* ll;           // exchange words
+  size_t o_qkv, o_att, o_atto, o_xb, o_z, o_xa, o_key;
+  unsigned tag0;
+  int* err;                         // device address of a host-visible int
+};
+size_t mk_lds_bytes(const Dims& d, int nsplit);
+hipError_t mk_prepare(bool bf16, const Dims& d, size_t lds_max, int* max_blocks_per_cu);
+hipError_t launch_decode_mk(const MkLaunch& a, hipStream_t st);
+
 }  // namespace qdec

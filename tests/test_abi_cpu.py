@@ -1,0 +1,106 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before touching the device."""
+import os
+import re
+
+import pytest
+
+from qwen3_kv_cache_amd import qdec
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "qdec.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qdec_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(qdec.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = qdec.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_header_compiles_as_c():
+    import shutil
+    import subprocess
+    import tempfile
+    gcc = shutil.which("gcc")
+    if not gcc:
+        pytest.skip("gcc missing")
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "t.c")
+        open(c, "w").write('#include "qdec.h"\nint main(void){qdec_config c; (void)c; return QDEC_OK;}\n')
+        r = subprocess.run([gcc, "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER), c, "-o",
+                            os.path.join(d, "t")], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+
+
+def good_cfg(**kw):
+    base = dict(hidden=128, n_layer=2, n_q_head=4, n_kv_head=2, head_dim=32, ffn=384, vocab=1024)
+    base.update(kw)
+    bf16 = base.pop("bf16", True)
+    tied = base.pop("tied", 1)
+    return qdec.make_config(bf16=bf16, tied=tied, **base)
+
+
+BAD = [
+    dict(tied=0), dict(hidden=100), dict(hidden=0), dict(head_dim=48), dict(head_dim=256), dict(n_kv_head=3),
+    dict(n_q_head=32, n_kv_head=2), dict(ffn=100), dict(vocab=1), dict(n_layer=0),
+    dict(rms_eps=0.0), dict(rope_theta=0.5),
+]
+
+
+@pytest.mark.parametrize("kw", BAD, ids=[str(k) for k in BAD])
+def test_create_rejects_bad_config(kw):
+    cfg = good_cfg(**kw)
+    table = qdec.WeightTable(0, 0, [[0] * qdec.QDEC_W_PER_LAYER] * 2)
+    with pytest.raises(qdec.QdecError) as e:
+        qdec.qdec_create(cfg, table.c, 0)
+    assert e.value.code == qdec.QDEC_E_INVALID
+    assert qdec.qdec_last_error()
+
+
+def test_create_rejects_bad_dtype_and_null_weights():
+    cfg = good_cfg()
+    cfg.weight_dtype = 7
+    table = qdec.WeightTable(0, 0, [[0] * qdec.QDEC_W_PER_LAYER] * 2)
+    with pytest.raises(qdec.QdecError) as e:
+        qdec.qdec_create(cfg, table.c, 0)
+    assert e.value.code == qdec.QDEC_E_INVALID and "weight_dtype" in qdec.qdec_last_error()
+    with pytest.raises(qdec.QdecError) as e:
+        qdec.qdec_create(good_cfg(), table.c, 0)
+    assert e.value.code == qdec.QDEC_E_INVALID and "weights" in qdec.qdec_last_error()
+
+
+def test_null_handles_are_rejected():
+    L = qdec.lib()
+    assert L.qdec_state_pos(None) == -1
+    assert L.qdec_destroy(None) == qdec.QDEC_OK
+    L.qdec_state_destroy(None)  # no-op
+    with pytest.raises(qdec.QdecError) as e:
+        qdec.qdec_state_create(0, 16)
+    assert e.value.code == qdec.QDEC_E_INVALID
+    with pytest.raises(qdec.QdecError) as e:
+        qdec.qdec_prefill(0, [1, 2], 2, None, 0, 0)
+    assert e.value.code == qdec.QDEC_E_INVALID
+    with pytest.raises(qdec.QdecError) as e:
+        qdec.qdec_decode_step(0, 1, 0)
+    assert e.value.code == qdec.QDEC_E_INVALID
+    with pytest.raises(qdec.QdecError) as e:
+        qdec.qdec_decode_batch([], [])
+    assert e.value.code == qdec.QDEC_E_INVALID
+    with pytest.raises(qdec.QdecError) as e:
+        qdec.qdec_clone_state(0)
+    assert e.value.code == qdec.QDEC_E_INVALID
+
+
+def test_batch_size_limit():
+    with pytest.raises(qdec.QdecError) as e:
+        qdec.qdec_decode_batch([1] * 17, [0] * 17)
+    assert e.value.code == qdec.QDEC_E_INVALID
