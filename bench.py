@@ -5,8 +5,10 @@ timed on the host as a reported baseline.
 One step = one pass of the whole path over one synthetic request of the
 default workload: prefill a 48-token prompt whose rows 8..30 are audio
 embedding rows, then 64 greedy decode steps, each feeding the previous
-step's device argmax (no host round trip). Inputs and weights are resident in
-HBM before timing; states are created before the timed region.
+step's device argmax (no host round trip). The 64 steps run as one
+multi-step launch (qdec_decode_greedy); --per-step launches once per token.
+Inputs and weights are resident in HBM before timing; states are created
+before the timed region.
 
 Usage: python bench.py [--steps K] [--warmup W] [--workload short|long|prefill8k|branch16]
        python bench.py --copy-probe   (plain copy kernel for counter calibration)
@@ -87,6 +89,8 @@ def main():
     ap.add_argument("--workload", default="short")
     ap.add_argument("--cpu-sample", type=int, default=24, help="oracle decode steps for the CPU baseline (0 = skip)")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--per-step", action="store_true",
+                    help="decode with one launch per token (qdec_decode_step_dev) instead of one launch for all steps")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {a.gpus}); the decoder is single-GPU by design.",
@@ -126,8 +130,11 @@ def main():
         qdec.qdec_prefill(st, ids, len(ids), audio_d.data_ptr(), a0, len(audio), None, toks[0].data_ptr())
         e1.record()
         if B == 1:
-            for s in range(n):
-                qdec.qdec_decode_step_dev(st, toks[s].data_ptr(), w.prompt_len + s, None, toks[s + 1].data_ptr())
+            if a.per_step:
+                for s in range(n):
+                    qdec.qdec_decode_step_dev(st, toks[s].data_ptr(), w.prompt_len + s, None, toks[s + 1].data_ptr())
+            else:
+                qdec.qdec_decode_greedy(st, toks[0].data_ptr(), w.prompt_len, n, None, toks[1].data_ptr())
         else:
             br = [qdec.qdec_clone_state(st) for _ in range(B)]
             for s in range(n):
@@ -181,7 +188,8 @@ def main():
     if achieved is not None:
         line["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                            "kernel": "whole decode step", "bytes_per_unit": round(bytes_tok)}
+                            "kernel": "decode_kernel (%d steps per launch)" % (1 if a.per_step else n),
+                            "bytes_per_unit": round(bytes_tok)}
     if a.cpu_sample > 0:
         line["cpu_baseline"] = cpu_baseline(w, W, a.cpu_sample)
     model.close()

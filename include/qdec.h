@@ -78,10 +78,11 @@ enum {
 };
 
 /* Model shape. Validated by qdec_create (QDEC_E_INVALID otherwise):
- * 1 <= n_layer <= 127; hidden a multiple of 64 and <= 8192; head_dim even, a
- * multiple of 8 and <= 128; n_kv_head >= 1 and n_q_head a multiple of
- * n_kv_head with n_q_head / n_kv_head <= 8; ffn a multiple of 16 and <= 16384;
- * n_q_head * head_dim <= 8192; vocab >= 2; rms_eps > 0; rope_theta > 1;
+ * 1 <= n_layer <= 127; hidden a multiple of 64 and <= 1024; head_dim 32, 64
+ * or 128; 1 <= n_kv_head <= 8 and n_q_head = 1, 2 or 4 times n_kv_head; ffn a
+ * multiple of 64 and <= 16384; n_q_head * head_dim <= 8192; vocab >= 2;
+ * rms_eps > 0; rope_theta > 1; each layer's rows per CU fit the decode
+ * kernel's LDS staging (true for the Qwen3-0.6B shape on 256 CUs);
  * weight_dtype QDEC_F32 or QDEC_BF16; tied == 1 (the LM head is the token
  * embedding table, audio.cpp plan Task 1 Step 3 rejects untied embeddings). */
 typedef struct {
@@ -151,6 +152,19 @@ int qdec_decode_step(qdec_state* s, int32_t token, int32_t pos, float* logits_de
  * into range on the device (the host cannot check it). */
 int qdec_decode_step_dev(qdec_state* s, const int32_t* token_dev, int32_t pos, float* logits_dev,
                          int32_t* argmax_dev);
+
+/* n_steps greedy decode steps in one launch (NCNN page section 5: the
+ * autoregressive loop of embed, one-token decoder, LM head and pick; section 6:
+ * greedy by default). Step 0 consumes *token_dev (DEVICE int32) at position
+ * pos; step i > 0 consumes the greedy token of step i-1 at pos + i, without a
+ * host round trip. tokens_dev: DEVICE int32 [n_steps], receives each step's
+ * greedy token. logits_dev: DEVICE fp32 [n_steps, vocab] or NULL.
+ * Requires pos == n_past (else QDEC_E_POS), 1 <= n_steps <= 4096 and
+ * pos + n_steps <= max_ctx (else QDEC_E_CAPACITY). Sets n_past = pos +
+ * n_steps. End-of-sequence handling stays with the caller: every step runs.
+ * A *token_dev outside [0, vocab) is clamped into range on the device. */
+int qdec_decode_greedy(qdec_state* s, const int32_t* token_dev, int32_t pos, int32_t n_steps, float* logits_dev,
+                       int32_t* tokens_dev);
 
 /* n independent decode steps in one launch set (1 <= n <= 16), state i
  * consuming tokens_host[i] at its own n_past. All states must belong to one

@@ -6,7 +6,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqdec.so")
-SOURCES = ["qdec_api.cpp", "qdec_kernels.hip", "qdec_decode_mk.hip"]
+SOURCES = ["qdec_api.cpp", "qdec_kernels.hip", "qdec_decode.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -131,14 +131,7 @@ struct qdec_model {
   float* rope_cos = nullptr;
   float* rope_sin = nullptr;
   int rope_cap = 0;
-  // decode scratch (one sequence)
-  float* x = nullptr;
-  float* qkv = nullptr;
-  float* attn = nullptr;
-  float* z = nullptr;
-  float* partial = nullptr;
-  int partial_splits = 0;
-  unsigned long long* keys = nullptr;
+  unsigned long long* keys = nullptr;  // prefill argmax key
   int32_t* argmax_tmp = nullptr;
   // prefill scratch, grown on demand
   int pf_cap = 0;
@@ -151,12 +144,14 @@ struct qdec_model {
   void* pA1 = nullptr;  // bf16 lo
   PagePool pool;
   int live_states = 0;
-  // persistent decode step
-  int mk_blocks = 0;
-  int mk_split_max = 1;
+  // persistent decode
+  int dec_blocks = 0;
+  size_t dec_lds = 0;
+  int nsplit_max = 1, whole_max = 64;
   unsigned long long* ll = nullptr;
-  size_t ll_words = 0, o_qkv = 0, o_att = 0, o_atto = 0, o_xb = 0, o_z = 0, o_xa = 0, o_key = 0;
-  unsigned mk_seq = 0;
+  size_t ll_words = 0;
+  DecOffsets off{};
+  unsigned tag_next = 1;  // next unused exchange tag (0 marks a cleared word)
   int* err_host = nullptr;
   int* err_dev = nullptr;
   size_t layer_elems = 0, off_o = 0, off_gu = 0, off_d = 0;
@@ -176,8 +171,8 @@ namespace {
 int validate_config(const qdec_config* c) {
   if (!c) return fail(QDEC_E_INVALID, "config is NULL");
   if (c->n_layer < 1 || c->n_layer > 127) return fail(QDEC_E_INVALID, "n_layer %d out of range", c->n_layer);
-  if (c->hidden < 64 || c->hidden > 8192 || c->hidden % 64)
-    return fail(QDEC_E_INVALID, "hidden %d must be a multiple of 64 in [64, 8192]", c->hidden);
+  if (c->hidden < 64 || c->hidden > 1024 || c->hidden % 64)
+    return fail(QDEC_E_INVALID, "hidden %d must be a multiple of 64 in [64, 1024]", c->hidden);
   if (c->head_dim < 8 || c->head_dim > 128 || c->head_dim % 8)
     return fail(QDEC_E_INVALID, "head_dim %d must be a multiple of 8 in [8, 128]", c->head_dim);
   if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128)
@@ -186,11 +181,12 @@ int validate_config(const qdec_config* c) {
     return fail(QDEC_E_INVALID, "n_q_head %d must be a positive multiple of n_kv_head %d", c->n_q_head,
                 c->n_kv_head);
   const int group = c->n_q_head / c->n_kv_head;
-  if (group != 1 && group != 2 && group != 4 && group != 8)
-    return fail(QDEC_E_INVALID, "GQA group %d must be 1, 2, 4 or 8", group);
+  if (group != 1 && group != 2 && group != 4)
+    return fail(QDEC_E_INVALID, "GQA group %d must be 1, 2 or 4", group);
+  if (c->n_kv_head > 8) return fail(QDEC_E_INVALID, "n_kv_head %d > 8", c->n_kv_head);
   if (c->n_q_head * c->head_dim > 8192) return fail(QDEC_E_INVALID, "n_q_head * head_dim exceeds 8192");
-  if (c->ffn < 16 || c->ffn > 16384 || c->ffn % 16)
-    return fail(QDEC_E_INVALID, "ffn %d must be a multiple of 16 in [16, 16384]", c->ffn);
+  if (c->ffn < 64 || c->ffn > 16384 || c->ffn % 64)
+    return fail(QDEC_E_INVALID, "ffn %d must be a multiple of 64 in [64, 16384]", c->ffn);
   if (c->vocab < 2) return fail(QDEC_E_INVALID, "vocab %d < 2", c->vocab);
   if (!(c->rms_eps > 0.f) || !std::isfinite(c->rms_eps)) return fail(QDEC_E_INVALID, "rms_eps must be > 0");
   if (!(c->rope_theta > 1.f) || !std::isfinite(c->rope_theta))
@@ -223,11 +219,6 @@ void free_model(qdec_model* m) {
   (void)hipFree(m->nbuf);
   (void)hipFree(m->rope_cos);
   (void)hipFree(m->rope_sin);
-  (void)hipFree(m->x);
-  (void)hipFree(m->qkv);
-  (void)hipFree(m->attn);
-  (void)hipFree(m->z);
-  (void)hipFree(m->partial);
   (void)hipFree(m->keys);
   (void)hipFree(m->argmax_tmp);
   free_prefill(m);
@@ -270,18 +261,6 @@ int ensure_rope(qdec_model* m, int n_pos) {
   return QDEC_OK;
 }
 
-int ensure_partial(qdec_model* m, int n_ctx) {
-  const int ns = (n_ctx + kAttnChunk - 1) / kAttnChunk;
-  if (ns <= m->partial_splits) return QDEC_OK;
-  float* p = nullptr;
-  if (int e = dev_alloc(&p, (size_t)m->d.NQ * ns * (m->d.D + 2), "attention partials")) return e;
-  HIP_TRY(hipStreamSynchronize(m->stream));
-  (void)hipFree(m->partial);
-  m->partial = p;
-  m->partial_splits = ns;
-  return QDEC_OK;
-}
-
 int ensure_prefill(qdec_model* m, int T) {
   if (T <= m->pf_cap) return QDEC_OK;
   HIP_TRY(hipStreamSynchronize(m->stream));
@@ -315,25 +294,27 @@ int ensure_prefill(qdec_model* m, int T) {
     if (e_ != hipSuccess) return fail(QDEC_E_DEVICE, "%s: %s", #expr, hipGetErrorString(e_)); \
   } while (0)
 
-// Exchange tags must not repeat between launches while stale words could
-// still hold them; the word buffer is cleared once per tag period.
-constexpr unsigned kTagPeriod = 4000000u;
-
-// One decode step for one sequence as a single cooperative launch; the
-// state's n_past is updated by the caller.
-int run_decode(qdec_state* s, int token, const int32_t* token_dev, int pos, float* logits, int32_t* argmax) {
+// One launch of `nsteps` greedy decode steps of one sequence; the state's
+// n_past is updated by the caller.
+int run_decode(qdec_state* s, int token, const int32_t* token_dev, int pos, int nsteps, float* logits,
+               int32_t* tokens_out) {
   qdec_model* m = s->m;
   const Dims& d = m->d;
   hipStream_t st = m->stream;
   if (__atomic_load_n(m->err_host, __ATOMIC_ACQUIRE))
     return fail(QDEC_E_DEVICE, "an earlier decode launch hit its time limit; the model must be recreated");
-  const unsigned k = m->mk_seq % kTagPeriod;
-  if (k == 0 && m->mk_seq != 0) HIP_TRY(hipMemsetAsync(m->ll, 0, m->ll_words * sizeof(unsigned long long), st));
-  ++m->mk_seq;
-  MkLaunch a{};
+  // tags never repeat while stale words could still hold them: before the
+  // counter would wrap, every word is cleared and tags restart at 1
+  const unsigned need = (unsigned)nsteps * dec_tags_per_step(d);
+  if (m->tag_next + (unsigned long long)need >= 0x7FFFFFFFull) {
+    LAUNCH(launch_clear_words(m->ll, m->ll_words, st));
+    m->tag_next = 1;
+  }
+  DecLaunch a{};
   a.d = d;
   a.bf16 = m->bf16;
-  a.nblocks = m->mk_blocks;
+  a.nblocks = m->dec_blocks;
+  a.lds_bytes = m->dec_lds;
   a.wbuf = m->wbuf;
   a.layer_elems = m->layer_elems;
   a.off_o = m->off_o;
@@ -347,23 +328,19 @@ int run_decode(qdec_state* s, int token, const int32_t* token_dev, int pos, floa
   a.rope_sin = m->rope_sin;
   a.page_table = s->pt_dev;
   a.pos = pos;
+  a.nsteps = nsteps;
   a.token = token;
   a.token_dev = token_dev;
-  const int want = (pos + 63) / 64;
-  a.nsplit = std::max(1, std::min(want, m->mk_split_max));
   a.logits = logits;
-  a.argmax_out = argmax ? argmax : m->argmax_tmp;
+  a.tokens_out = tokens_out ? tokens_out : m->argmax_tmp;
   a.ll = m->ll;
-  a.o_qkv = m->o_qkv;
-  a.o_att = m->o_att;
-  a.o_atto = m->o_atto;
-  a.o_xb = m->o_xb;
-  a.o_z = m->o_z;
-  a.o_xa = m->o_xa;
-  a.o_key = m->o_key;
-  a.tag0 = (k + 1u) * 1024u;
+  a.off = m->off;
+  a.tag0 = m->tag_next;
+  a.nsplit_max = m->nsplit_max;
+  a.whole_max = m->whole_max;
   a.err = m->err_dev;
-  LAUNCH(launch_decode_mk(a, st));
+  LAUNCH(launch_decode(a, st));
+  m->tag_next += need;
   return QDEC_OK;
 }
 
@@ -472,9 +449,7 @@ int qdec_create(const qdec_config* cfg, const qdec_weights* w, void* hip_stream,
     return fail(QDEC_E_OOM, "cannot allocate packed weights");
   }
   if ((e = dev_alloc(&m->nbuf, norms_per_layer * d.L, "norm gains")) ||
-      (e = dev_alloc(&m->final_norm, d.H, "final norm")) || (e = dev_alloc(&m->x, d.H, "x")) ||
-      (e = dev_alloc(&m->qkv, d.qkv(), "qkv")) || (e = dev_alloc(&m->attn, (size_t)d.NQ * d.D, "attn")) ||
-      (e = dev_alloc(&m->z, d.F, "z")) || (e = dev_alloc(&m->keys, kMaxBatch, "argmax keys")) ||
+      (e = dev_alloc(&m->final_norm, d.H, "final norm")) || (e = dev_alloc(&m->keys, kMaxBatch, "argmax keys")) ||
       (e = dev_alloc(&m->argmax_tmp, kMaxBatch, "argmax scratch"))) {
     free_model(m);
     return e;
@@ -532,30 +507,34 @@ int qdec_create(const qdec_config* cfg, const qdec_weights* w, void* hip_stream,
     int dev = 0;
     hipDeviceProp_t prop;
     if ((he = hipGetDevice(&dev)) || (he = hipGetDeviceProperties(&prop, dev))) return fail_dev("device query", he);
-    m->mk_blocks = prop.multiProcessorCount;
-    m->mk_split_max = std::max(1, std::min(64, m->mk_blocks / d.NKV));
-    const size_t lds = std::max(mk_lds_bytes(d, 1), std::max(mk_lds_bytes(d, 2), mk_lds_bytes(d, m->mk_split_max)));
-    int occ = 0;
-    if ((he = mk_prepare(m->bf16, d, lds, &occ))) return fail_dev("decode kernel setup", he);
-    if (occ < 1) {
+    m->dec_blocks = prop.multiProcessorCount;
+    if (m->dec_blocks < 8 || m->dec_blocks % 8) {
       free_model(m);
-      return fail(QDEC_E_INVALID, "decode kernel does not fit one workgroup per CU (LDS %zu bytes)", lds);
+      return fail(QDEC_E_INVALID, "decode needs a multiple of 8 compute units (device has %d)", m->dec_blocks);
     }
-    const size_t QKV = (size_t)d.qkv();
-    size_t o = 0;
-    m->o_qkv = o; o += 2 * QKV;
-    m->o_att = o; o += 2 * (size_t)d.NQ * m->mk_split_max * (d.D + 2);
-    m->o_atto = o; o += 2 * (size_t)d.NQ * d.D;
-    m->o_xb = o; o += 2 * (size_t)d.H;
-    m->o_z = o; o += 2 * (size_t)d.F;
-    m->o_xa = o; o += 2 * (size_t)d.H;
-    m->o_key = o; o += 2 * (size_t)m->mk_blocks;
-    m->ll_words = o;
-    if ((e = dev_alloc(&m->ll, o, "exchange words"))) {
+    const int R = m->dec_blocks / 8;
+    if (!dec_fits(m->bf16, d, m->dec_blocks)) {
+      free_model(m);
+      return fail(QDEC_E_INVALID, "shape too large for the decode kernel's LDS staging on %d CUs", m->dec_blocks);
+    }
+    m->nsplit_max = dec_split_limit(d, m->dec_blocks);
+    m->whole_max = 64;
+    // dynamic LDS; the kernel's static weight rings (96 KB) already keep the
+    // runtime from placing two workgroups on one CU
+    m->dec_lds = dec_lds_bytes(d, R, m->nsplit_max);
+    int occ = 0;
+    if ((he = dec_prepare(m->bf16, d, m->dec_lds, &occ))) return fail_dev("decode kernel setup", he);
+    if (occ != 1) {
+      free_model(m);
+      return fail(QDEC_E_INVALID, "decode kernel must fit exactly one workgroup per CU (got %d, LDS %zu bytes)", occ,
+                  m->dec_lds);
+    }
+    m->ll_words = dec_words(d, m->dec_blocks, m->nsplit_max, &m->off);
+    if ((e = dev_alloc(&m->ll, m->ll_words, "exchange words"))) {
       free_model(m);
       return e;
     }
-    if ((he = hipMemsetAsync(m->ll, 0, o * sizeof(unsigned long long), st))) return fail_dev("exchange init", he);
+    if ((he = launch_clear_words(m->ll, m->ll_words, st))) return fail_dev("exchange init", he);
     if ((he = hipHostMalloc((void**)&m->err_host, sizeof(int), hipHostMallocMapped))) {
       m->err_host = nullptr;
       return fail_dev("error flag", he);
@@ -564,7 +543,7 @@ int qdec_create(const qdec_config* cfg, const qdec_weights* w, void* hip_stream,
     if ((he = hipHostGetDevicePointer((void**)&m->err_dev, m->err_host, 0))) return fail_dev("error flag map", he);
   }
   if ((he = hipStreamSynchronize(st))) return fail_dev("weight packing", he);
-  if ((e = ensure_rope(m, 4096)) || (e = ensure_partial(m, 4096))) {
+  if ((e = ensure_rope(m, 4096))) {
     free_model(m);
     return e;
   }
@@ -585,7 +564,6 @@ int qdec_state_create(qdec_model* m, int32_t max_ctx, qdec_state** out) {
   if (!m) return fail(QDEC_E_INVALID, "model is NULL");
   if (max_ctx < 1 || max_ctx > (1 << 20)) return fail(QDEC_E_INVALID, "max_ctx %d out of range", max_ctx);
   if (int e = ensure_rope(m, max_ctx)) return e;
-  if (int e = ensure_partial(m, max_ctx)) return e;
   const int npages = (max_ctx + kPage - 1) / kPage;
   if (int e = m->pool.reserve(npages)) return e;
   qdec_state* s = new (std::nothrow) qdec_state();
@@ -657,7 +635,7 @@ static int decode_common(qdec_state* s, int token, const int32_t* token_dev, int
   if (pos != s->n_past) return fail(QDEC_E_POS, "pos %d != n_past %d", pos, s->n_past);
   if (pos >= s->max_ctx) return fail(QDEC_E_CAPACITY, "pos %d >= max_ctx %d", pos, s->max_ctx);
   if (int e = check_outputs(s->m, 1, logits_dev, argmax_dev)) return e;
-  if (int e = run_decode(s, token, token_dev, pos, logits_dev, argmax_dev)) return e;
+  if (int e = run_decode(s, token, token_dev, pos, 1, logits_dev, argmax_dev)) return e;
   s->n_past = pos + 1;
   return ok();
 }
@@ -672,6 +650,23 @@ int qdec_decode_step_dev(qdec_state* s, const int32_t* token_dev, int32_t pos, f
                          int32_t* argmax_dev) {
   if (int e = check_dev(token_dev, sizeof(int32_t), "token_dev")) return e;
   return decode_common(s, 0, token_dev, pos, logits_dev, argmax_dev);
+}
+
+int qdec_decode_greedy(qdec_state* s, const int32_t* token_dev, int32_t pos, int32_t n_steps, float* logits_dev,
+                       int32_t* tokens_dev) {
+  if (!s) return fail(QDEC_E_INVALID, "state is NULL");
+  if (n_steps < 1 || n_steps > 4096) return fail(QDEC_E_INVALID, "n_steps %d outside [1, 4096]", n_steps);
+  if (pos != s->n_past) return fail(QDEC_E_POS, "pos %d != n_past %d", pos, s->n_past);
+  if ((int64_t)pos + n_steps > s->max_ctx)
+    return fail(QDEC_E_CAPACITY, "pos %d + n_steps %d exceeds max_ctx %d", pos, n_steps, s->max_ctx);
+  if (int e = check_dev(token_dev, sizeof(int32_t), "token_dev")) return e;
+  if (int e = check_dev(tokens_dev, (size_t)n_steps * sizeof(int32_t), "tokens_dev")) return e;
+  if (logits_dev) {
+    if (int e = check_dev(logits_dev, (size_t)n_steps * s->m->d.V * sizeof(float), "logits_dev")) return e;
+  }
+  if (int e = run_decode(s, 0, token_dev, pos, n_steps, logits_dev, tokens_dev)) return e;
+  s->n_past = pos + n_steps;
+  return ok();
 }
 
 int qdec_decode_batch(qdec_state* const* states, int32_t n, const int32_t* tokens_host, float* logits_dev,
@@ -693,8 +688,8 @@ int qdec_decode_batch(qdec_state* const* states, int32_t n, const int32_t* token
   if (int e = check_outputs(m, n, logits_dev, argmax_dev)) return e;
   for (int i = 0; i < n; ++i) {
     qdec_state* s = states[i];
-    if (int e = run_decode(s, tokens_host[i], nullptr, s->n_past, logits_dev ? logits_dev + (size_t)i * m->d.V : nullptr,
-                           argmax_dev ? argmax_dev + i : nullptr))
+    if (int e = run_decode(s, tokens_host[i], nullptr, s->n_past, 1,
+                           logits_dev ? logits_dev + (size_t)i * m->d.V : nullptr, argmax_dev ? argmax_dev + i : nullptr))
       return e;
     s->n_past += 1;
   }

@@ -73,11 +73,16 @@ hipError_t launch_gemm(bool bf16, Epi epi, const void* A0, const void* A1, int M
                        float* C, int ldc, hipStream_t st);
 hipError_t launch_to_f32(const void* src, bool bf16, size_t n, float* dst, hipStream_t st);
 
-// ---- persistent decode step (qdec_decode_mk.hip)
-struct MkLaunch {
+// ---- persistent decode (qdec_decode.hip)
+// Word offsets of the exchange regions inside the model's word buffer.
+struct DecOffsets {
+  size_t q, att, o, z, x, key;
+};
+struct DecLaunch {
   Dims d;
   bool bf16;
-  int nblocks;                      // one workgroup per CU
+  int nblocks;                      // one workgroup per CU, a multiple of 8
+  size_t lds_bytes;
   const void* wbuf;                 // packed layer weights, layer l at wbuf + l * layer_elems
   size_t layer_elems, off_o, off_gu, off_d;
   const float* nbuf;                // fp32 norm gains, layer l at nbuf + l * norm_elems
@@ -87,18 +92,23 @@ struct MkLaunch {
   const float* rope_cos;
   const float* rope_sin;
   const int64_t* page_table;
-  int pos, token;
+  int pos, nsteps, token;
   const int32_t* token_dev;
-  int nsplit;                       // attention splits per KV head
-  float* logits;
-  int32_t* argmax_out;
+  float* logits;                    // [nsteps, V] or null
+  int32_t* tokens_out;              // [nsteps]
   unsigned long long* ll;           // exchange words
-  size_t o_qkv, o_att, o_atto, o_xb, o_z, o_xa, o_key;
+  DecOffsets off;
   unsigned tag0;
+  int nsplit_max, whole_max;
   int* err;                         // device address of a host-visible int
 };
-size_t mk_lds_bytes(const Dims& d, int nsplit);
-hipError_t mk_prepare(bool bf16, const Dims& d, size_t lds_max, int* max_blocks_per_cu);
-hipError_t launch_decode_mk(const MkLaunch& a, hipStream_t st);
+size_t dec_lds_bytes(const Dims& d, int R, int nsplit_max);
+size_t dec_words(const Dims& d, int nblocks, int nsplit_max, DecOffsets* off);
+unsigned dec_tags_per_step(const Dims& d);
+int dec_split_limit(const Dims& d, int nblocks);
+bool dec_fits(bool bf16, const Dims& d, int nblocks);
+hipError_t dec_prepare(bool bf16, const Dims& d, size_t lds, int* blocks_per_cu);
+hipError_t launch_decode(const DecLaunch& a, hipStream_t st);
+hipError_t launch_clear_words(unsigned long long* w, size_t n, hipStream_t st);
 
 }  // namespace qdec

@@ -33,7 +33,7 @@ QDEC_PAGE = 16
  QDEC_W_POST_NORM, QDEC_W_GATE, QDEC_W_UP, QDEC_W_DOWN, QDEC_W_PER_LAYER) = range(12)
 
 EXPORTS = ("qdec_create", "qdec_destroy", "qdec_state_create", "qdec_state_destroy", "qdec_prefill",
-           "qdec_decode_step", "qdec_decode_step_dev", "qdec_decode_batch", "qdec_clone_state",
+           "qdec_decode_step", "qdec_decode_step_dev", "qdec_decode_greedy", "qdec_decode_batch", "qdec_clone_state",
            "qdec_state_pos", "qdec_last_error")
 
 
@@ -84,6 +84,7 @@ def lib() -> ctypes.CDLL:
         "qdec_prefill": (ctypes.c_int, [vp, ctypes.POINTER(i32), i32, vp, i32, i32, vp, vp]),
         "qdec_decode_step": (ctypes.c_int, [vp, i32, i32, vp, vp]),
         "qdec_decode_step_dev": (ctypes.c_int, [vp, vp, i32, vp, vp]),
+        "qdec_decode_greedy": (ctypes.c_int, [vp, vp, i32, i32, vp, vp]),
         "qdec_decode_batch": (ctypes.c_int, [ctypes.POINTER(vp), i32, ctypes.POINTER(i32), vp, vp]),
         "qdec_clone_state": (ctypes.c_int, [vp, ctypes.POINTER(vp)]),
         "qdec_state_pos": (i32, [vp]),
@@ -146,6 +147,11 @@ def qdec_decode_step(state: int, token: int, pos: int, logits_dev=None, argmax_d
 def qdec_decode_step_dev(state: int, token_dev, pos: int, logits_dev=None, argmax_dev=None) -> None:
     _check(lib().qdec_decode_step_dev(_ptr(state), _ptr(token_dev), int(pos), _ptr(logits_dev),
                                       _ptr(argmax_dev)))
+
+
+def qdec_decode_greedy(state: int, token_dev, pos: int, n_steps: int, logits_dev=None, tokens_dev=None) -> None:
+    _check(lib().qdec_decode_greedy(_ptr(state), _ptr(token_dev), int(pos), int(n_steps), _ptr(logits_dev),
+                                    _ptr(tokens_dev)))
 
 
 def qdec_decode_batch(states: Sequence[int], tokens_host, logits_dev=None, argmax_dev=None) -> None:

@@ -147,3 +147,30 @@ def test_branch16_clone_decode():
         worst = max(worst, wb)
     full_vector_check("branch 0 last", L[n - 1, 0], z["full_last_b0"])
     print(f"[branch16] sampled max abs {worst:.3g}", flush=True)
+
+
+def test_short_greedy_one_launch():
+    """The short workload's 64 greedy steps as one multi-step launch: the device
+    feeds each argmax forward, so every token must equal the oracle's greedy
+    trajectory and every step's logits must match the stored samples."""
+    from qwen3_kv_cache_amd import qdec
+    torch, dev = torch_dev()
+    w = synth.WORKLOADS["short"]
+    z = teacher("short")
+    m = model_06b()
+    ids, audio, a0 = synth.make_prompt(w)
+    n = w.n_decode
+    print(f"[short greedy] T={w.prompt_len} steps={n} in one launch", flush=True)
+    st = qdec.qdec_state_create(m.handle, w.max_ctx)
+    logits = torch.full((n + 1, w.shape.vocab), float("nan"), dtype=torch.float32, device=dev)
+    toks = torch.full((n + 1,), -1, dtype=torch.int32, device=dev)
+    audio_d = torch.from_numpy(audio).to(dev)
+    qdec.qdec_prefill(st, ids, len(ids), audio_d.data_ptr(), a0, len(audio), logits[0].data_ptr(), toks[0].data_ptr())
+    qdec.qdec_decode_greedy(st, toks[0].data_ptr(), w.prompt_len, n, logits[1].data_ptr(), toks[1].data_ptr())
+    torch.cuda.synchronize()
+    assert qdec.qdec_state_pos(st) == w.max_ctx
+    qdec.qdec_state_destroy(st)
+    L, A = logits.cpu().numpy(), toks.cpu().numpy()
+    assert list(A) == list(z["tokens"]), f"greedy tokens differ from the oracle trajectory"
+    worst, cos_min = check_against_teacher("short greedy", L, A, z, range(n + 1))
+    print(f"[short greedy] sampled max abs {worst:.3g}, min cos {cos_min:.7f}", flush=True)
