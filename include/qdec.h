@@ -80,7 +80,7 @@ enum {
 /* Model shape. Validated by qdec_create (QDEC_E_INVALID otherwise):
  * 1 <= n_layer <= 127; hidden a multiple of 64 and <= 1024; head_dim 32, 64
  * or 128; 1 <= n_kv_head <= 8 and n_q_head = 1, 2 or 4 times n_kv_head; ffn a
- * multiple of 64 and <= 16384; n_q_head * head_dim <= 8192; vocab >= 2;
+ * multiple of 64 and <= 8192; n_q_head * head_dim <= 8192; vocab >= 2;
  * rms_eps > 0; rope_theta > 1; each layer's rows per CU fit the decode
  * kernel's LDS staging (true for the Qwen3-0.6B shape on 256 CUs);
  * weight_dtype QDEC_F32 or QDEC_BF16; tied == 1 (the LM head is the token

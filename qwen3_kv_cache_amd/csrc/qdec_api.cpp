@@ -185,8 +185,8 @@ int validate_config(const qdec_config* c) {
     return fail(QDEC_E_INVALID, "GQA group %d must be 1, 2 or 4", group);
   if (c->n_kv_head > 8) return fail(QDEC_E_INVALID, "n_kv_head %d > 8", c->n_kv_head);
   if (c->n_q_head * c->head_dim > 8192) return fail(QDEC_E_INVALID, "n_q_head * head_dim exceeds 8192");
-  if (c->ffn < 64 || c->ffn > 16384 || c->ffn % 64)
-    return fail(QDEC_E_INVALID, "ffn %d must be a multiple of 64 in [64, 16384]", c->ffn);
+  if (c->ffn < 64 || c->ffn > 8192 || c->ffn % 64)
+    return fail(QDEC_E_INVALID, "ffn %d must be a multiple of 64 in [64, 8192]", c->ffn);
   if (c->vocab < 2) return fail(QDEC_E_INVALID, "vocab %d < 2", c->vocab);
   if (!(c->rms_eps > 0.f) || !std::isfinite(c->rms_eps)) return fail(QDEC_E_INVALID, "rms_eps must be > 0");
   if (!(c->rope_theta > 1.f) || !std::isfinite(c->rope_theta))
@@ -512,7 +512,6 @@ int qdec_create(const qdec_config* cfg, const qdec_weights* w, void* hip_stream,
       free_model(m);
       return fail(QDEC_E_INVALID, "decode needs a multiple of 8 compute units (device has %d)", m->dec_blocks);
     }
-    const int R = m->dec_blocks / 8;
     if (!dec_fits(m->bf16, d, m->dec_blocks)) {
       free_model(m);
       return fail(QDEC_E_INVALID, "shape too large for the decode kernel's LDS staging on %d CUs", m->dec_blocks);
@@ -521,7 +520,7 @@ int qdec_create(const qdec_config* cfg, const qdec_weights* w, void* hip_stream,
     m->whole_max = 64;
     // dynamic LDS; the kernel's static weight rings (96 KB) already keep the
     // runtime from placing two workgroups on one CU
-    m->dec_lds = dec_lds_bytes(d, R, m->nsplit_max);
+    m->dec_lds = dec_lds_bytes(m->bf16, d, m->dec_blocks, m->nsplit_max);
     int occ = 0;
     if ((he = dec_prepare(m->bf16, d, m->dec_lds, &occ))) return fail_dev("decode kernel setup", he);
     if (occ != 1) {

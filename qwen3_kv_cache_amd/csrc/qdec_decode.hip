@@ -19,16 +19,25 @@
 // low half, a tag unique to (launch, step, layer, phase) in the high half,
 // stored and loaded as device-scope relaxed atomics. A consumer polls until
 // every word it needs carries the expected tag. Regions are double-buffered by
-// layer parity. Every wait has a time limit; on expiry the launch raises a
-// host-visible error flag and all workgroups return.
+// layer parity. Every wait has a time limit; on expiry the workgroup raises a
+// host-visible error flag and stops waiting for the rest of the launch, so
+// every workgroup still runs to the end and the launch always drains.
 //
 // Two roles per workgroup. A wave's vector-memory counter retires loads in
 // issue order, so a load needed now cannot complete before an earlier
-// prefetch. Waves 0-3 (memory waves) therefore hold the weights: they issue
-// each phase's weight loads one or two phases ahead and compute the dot
-// products. Waves 4-7 (exchange waves) issue only latency-critical loads: the
-// exchange polls, norm gains, RoPE rows and the KV cache; they also run the
-// norms, Q/K-norm + RoPE and attention. The roles meet at workgroup barriers.
+// prefetch. Waves 0-3 (memory waves) therefore only stream weights: each
+// phase's rows are copied straight into LDS two phases ahead, and each wave
+// reduces them against the phase input into per-slot partial dot products.
+// Waves 4-7 (exchange waves) hold the residual stream in registers and do
+// everything latency-bound: exchange polls and publishes, norm statistics,
+// Q/K-norm + RoPE, attention, SiLU and the argmax. The roles meet at exactly
+// two workgroup barriers per weight unit: "input ready" and "partials ready".
+// The exchange waves synchronise among themselves through an LDS counter, so
+// the memory waves never wait on exchange-internal steps.
+//
+// RMSNorm folding: the memory waves dot the weights with x * g (gain applied,
+// not yet scaled) and the exchange waves multiply each combined row by
+// 1 / sqrt(mean(x^2) + eps) when they publish it.
 //
 // Phases of layer l for workgroup (x, r); G = n_q / n_kv query heads per KV
 // head, QD = G * D, FS = ffn / 8:
@@ -65,9 +74,18 @@ constexpr int kExWaves = kWaves - kMemWaves;
 constexpr int kEx = kExWaves * kWave;     // exchange threads
 constexpr int kExBase = kMemWaves * kWave;  // first exchange thread
 constexpr int kGroups = 8;                // XCDs
+constexpr int kMaxBlocks = kEx;           // one argmax key per exchange thread
 constexpr u64 kWaitTicks = 200000000ull;  // 2 s of the 100 MHz realtime counter
 constexpr int kTagSlots = 8;              // tags per (step, layer)
 enum { PH_Q = 0, PH_ATT = 1, PH_O = 2, PH_Z = 3, PH_X = 4, PH_KEY = 5 };
+
+// Weight staging. Each memory wave owns an LDS ring of two regions of kSlots
+// slots; a slot holds one 16-byte chunk per lane (1 KB). A unit (one phase's
+// rows of this wave, or one batch of LM-head rows) is copied into a region by
+// direct global-to-LDS loads (lane i's 16 bytes land at slot + 16 i).
+constexpr int kSlots = 12;
+constexpr int kSlotBytes = kWave * 16;
+constexpr int kMaxK = 1024;  // longest GEMV input: max(hidden, G * D, ffn / 8)
 
 __device__ __forceinline__ u64 now() { return __builtin_amdgcn_s_memrealtime(); }
 
@@ -80,19 +98,20 @@ __device__ u64 g_trace[2048 * kTraceN];
   do {                                                                                                   \
     if ((step) == 0 && tid == kExBase && (idx) < kTraceN) g_trace[blockIdx.x * kTraceN + (idx)] = now(); \
   } while (0)
-// the same from the first memory-wave thread
-#define TRACEM(step, idx)                                                                       \
-  do {                                                                                          \
-    if ((step) == 0 && tid0 == 0 && (idx) >= 0 && (idx) < kTraceN) g_trace[blockIdx.x * kTraceN + (idx)] = now(); \
-  } while (0)
 #else
 #define TRACE(step, idx) \
   do {                   \
   } while (0)
-#define TRACEM(step, idx) \
-  do {                    \
-  } while (0)
 #endif
+
+// Re-define per-thread indices and the parameter pointer as opaque values:
+// everything derived from them is recomputed after this point instead of being
+// hoisted out of the enclosing loops and held in registers.
+#define QDEC_OPAQUE()                  \
+  do {                                 \
+    asm volatile("" : "+v"(et), "+v"(ln)); \
+    asm volatile("" : "+s"(pp));       \
+  } while (0)
 
 __device__ __forceinline__ void put(u64* p, float v, unsigned tag) {
   __hip_atomic_store(p, ((u64)tag << 32) | (u64)__float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -115,14 +134,16 @@ constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within each 8
 constexpr int kDppMirror = 0x140;     // lane i <-> 15 - i within each 16
 constexpr int kDppXor8 = 0x128;       // row_ror:8, i.e. lane i <-> i ^ 8 within each 16
-// (value of lane i, value of lane i ^ 16) and (lane i, lane i ^ 32) as an
-// ordered pair (lower lane first), so sums and maxima are bit-identical in both lanes
-__device__ __forceinline__ float sum16(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+// permlane32_swap(a, b) exchanges lanes 32-63 of a with lanes 0-31 of b;
+// permlane16_swap(a, b) exchanges the odd 16-lane rows of a with the even rows
+// of b. pair32(a, b): lanes 0-31 hold a[i] + a[i+32], lanes 32-63 b[i-32] + b[i].
+// pair16(a, b): 16-lane rows hold [a.r0+a.r1, b.r0+b.r1, a.r2+a.r3, b.r2+b.r3].
+__device__ __forceinline__ float pair32(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-__device__ __forceinline__ float sum32(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+__device__ __forceinline__ float pair16(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 __device__ __forceinline__ float max16(float v) {
@@ -133,6 +154,10 @@ __device__ __forceinline__ float max32(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+// (value of lane i) + (value of lane i ^ 16), then the same for i ^ 32: a
+// 64-lane sum once the 16-lane rows are reduced
+__device__ __forceinline__ float sum16(float v) { return pair16(v, v); }
+__device__ __forceinline__ float sum32(float v) { return pair32(v, v); }
 
 // Sum over the 64 lanes; every lane gets the same value.
 __device__ __forceinline__ float wave_sum(float v) {
@@ -143,10 +168,49 @@ __device__ __forceinline__ float wave_sum(float v) {
   return sum32(sum16(v));
 }
 
+// Twelve independent 64-lane sums s[0..11] reduced together: pairs of values
+// share one register after each cross-lane step, so the whole batch costs
+// about as much as two single sums. Slot q's total goes to dst[q].
+__device__ __forceinline__ void reduce12_store(const float (&s)[kSlots], float* dst, int lane) {
+  const float p0 = pair32(s[0], s[1]), p1 = pair32(s[2], s[3]);
+  const float p2 = pair32(s[4], s[5]), p3 = pair32(s[6], s[7]);
+  const float p4 = pair32(s[8], s[9]), p5 = pair32(s[10], s[11]);
+  // 16-lane rows of q01: slots 0, 2, 1, 3; of q23: 4, 6, 5, 7; of q45: 8, 10, 9, 11
+  const float q01 = pair16(p0, p1), q23 = pair16(p2, p3), q45 = pair16(p4, p5);
+  const float t = q01 + dpp<kDppXor8>(q01), u = q23 + dpp<kDppXor8>(q23);
+  float r8 = (lane & 8) ? u : t;  // 8-lane group g: slot (g & 1) * 4 + perm(g >> 1)
+  r8 += dpp<kDppXor1>(r8);
+  r8 += dpp<kDppXor2>(r8);
+  r8 += dpp<kDppHalfMirror>(r8);
+  float r4 = q45;  // 16-lane row w: slot 8 + perm(w)
+  r4 += dpp<kDppXor1>(r4);
+  r4 += dpp<kDppXor2>(r4);
+  r4 += dpp<kDppHalfMirror>(r4);
+  r4 += dpp<kDppMirror>(r4);
+  // perm(i) = [0, 2, 1, 3][i]
+  if ((lane & 7) == 0) {
+    const int g = lane >> 3;
+    dst[((g & 1) << 2) | (((g >> 1) & 1) << 1) | (g >> 2)] = r8;
+  }
+  if ((lane & 15) == 0) {
+    const int w = lane >> 4;
+    dst[8 + (((w & 1) << 1) | (w >> 1))] = r4;
+  }
+}
+
 __device__ __forceinline__ u64 argmax_key(float v, int idx) {
   uint32_t u = __float_as_uint(v);
   uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return ((u64)o << 32) | (u64)(0xFFFFFFFFu - (uint32_t)idx);
+}
+__device__ __forceinline__ u64 umax64(u64 a, u64 b) { return a > b ? a : b; }
+__device__ __forceinline__ u64 wave_max64(u64 k) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const unsigned lo = __shfl_xor((unsigned)k, o), hi = __shfl_xor((unsigned)(k >> 32), o);
+    k = umax64(k, ((u64)hi << 32) | lo);
+  }
+  return k;
 }
 
 // even split of n items over `parts`: [s, e) of part i
@@ -154,6 +218,13 @@ __device__ __forceinline__ void split(int n, int parts, int i, int& s, int& e) {
   const int per = (n + parts - 1) / parts;
   s = min(n, i * per);
   e = min(n, s + per);
+}
+
+// log2 of the 64-lane chunk rows a GEMV input of k elements needs (chunks of vn)
+__host__ __device__ __forceinline__ int chunk_lg(int k, int vn) {
+  const int nch = k / vn;
+  const int cpl = (nch + kWave - 1) / kWave;
+  return cpl <= 1 ? 0 : cpl <= 2 ? 1 : cpl <= 4 ? 2 : 3;
 }
 
 struct DecParams {
@@ -179,121 +250,17 @@ struct DecParams {
   int R;              // ranks per group
   int nsplit_max;     // attention splits per group
   int whole_max;      // cached positions up to which each rank runs the whole attention
-  int lds_x, lds_xn, lds_stage, lds_att, lds_red, lds_rbuf, lds_lgb, lds_ring;
+  int nhu;            // LM-head units per memory wave (the largest over waves)
+  int lds_stage, lds_att, lds_sbuf;
 };
 
-// ------------------------------------------------------------------ waits
-// All waits are called by every thread of the workgroup (they end in a
-// barrier); only threads with `act` (the exchange waves) poll. et = exchange
-// thread index in [0, kEx).
-
-// x[e] += sum_{q < P} W[q * n + e] for e < n (P <= 8), in that order.
-template <int NE>
-__device__ __forceinline__ bool gather_sum(bool act, const u64* W, int P, int n, unsigned tag, float* x, int et) {
-  bool ok = true;
-  if (act) {
-    const u64 t0 = now();
-    u64 w[NE][kGroups];
-    while (true) {
-#pragma unroll
-      for (int k = 0; k < NE; ++k) {
-        const int e = min(et + k * kEx, n - 1);
-#pragma unroll
-        for (int q = 0; q < kGroups; ++q)
-          if (q < P) w[k][q] = get(W + (size_t)q * n + e);
-      }
-      bool done = true;
-#pragma unroll
-      for (int k = 0; k < NE; ++k)
-#pragma unroll
-        for (int q = 0; q < kGroups; ++q)
-          if (q < P) done = done && tagged(w[k][q], tag);
-      if (done) break;
-      if (now() - t0 > kWaitTicks) {
-        ok = false;
-        break;
-      }
-    }
-    if (ok) {
-#pragma unroll
-      for (int k = 0; k < NE; ++k) {
-        const int e = et + k * kEx;
-        if (e < n) {
-          float s = x[e];
-#pragma unroll
-          for (int q = 0; q < kGroups; ++q)
-            if (q < P) s += val(w[k][q]);
-          x[e] = s;
-        }
-      }
-    }
-  }
-  return __syncthreads_and(ok);
-}
-
-// dst[i] = value of W[i] for i < n (n <= J * kEx).
-template <int J>
-__device__ __forceinline__ bool gather_vec(bool act, const u64* W, int n, unsigned tag, float* dst, int et) {
-  bool ok = true;
-  if (act) {
-    const u64 t0 = now();
-    u64 w[J];
-    while (true) {
-#pragma unroll
-      for (int j = 0; j < J; ++j) w[j] = get(W + min(et + j * kEx, n - 1));
-      bool done = true;
-#pragma unroll
-      for (int j = 0; j < J; ++j) done = done && tagged(w[j], tag);
-      if (done) break;
-      if (now() - t0 > kWaitTicks) {
-        ok = false;
-        break;
-      }
-    }
-    if (ok) {
-#pragma unroll
-      for (int j = 0; j < J; ++j)
-        if (et + j * kEx < n) dst[et + j * kEx] = val(w[j]);
-    }
-  }
-  return __syncthreads_and(ok);
-}
-
-__device__ __forceinline__ bool gather_any(bool act, const u64* W, int n, unsigned tag, float* dst, int et) {
-  if (n <= 2 * kEx) return gather_vec<2>(act, W, n, tag, dst, et);
-  if (n <= 8 * kEx) return gather_vec<8>(act, W, n, tag, dst, et);
-  return gather_vec<32>(act, W, n, tag, dst, et);
-}
-
-__device__ __forceinline__ void fail_launch(int* err, int tid) {
-  if (tid == 0) __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-}
-
-// ------------------------------------------------------------------ helpers
-
-__device__ __forceinline__ float block_sum(float v, float* red, int tid) {
-  v = wave_sum(v);
-  __syncthreads();
-  if (tid % kWave == 0) red[tid / kWave] = v;
-  __syncthreads();
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) s += red[i];
-  return s;
-}
-
-// xn[i] = x[i] / sqrt(mean(x^2) + eps) * g[i]; elementwise work by the `act` threads.
-__device__ __forceinline__ void rms_norm(bool act, const float* x, const float* g, int n, float eps, float* xn,
-                                         float* red, int tid, int et) {
-  float ss = 0.f;
-  if (act)
-    for (int i = et; i < n; i += kEx) ss = fmaf(x[i], x[i], ss);
-  ss = block_sum(ss, red, tid);
-  const float inv = 1.f / sqrtf(ss / (float)n + eps);
-  if (act)
-    for (int i = et; i < n; i += kEx) xn[i] = x[i] * inv * g[i];
-  __syncthreads();
-}
+// Workgroup-shared control words.
+struct Ctl {
+  int abort;                 // a wait of this workgroup timed out: skip all later waits
+  int exbar;                 // arrivals at exchange-wave barriers
+  float red[kExWaves];       // per exchange wave: sum of squares of its residual elements
+  u64 best[2][kExWaves];     // per exchange wave: argmax keys
+};
 
 template <typename WT>
 __device__ __forceinline__ float wload(const WT* p, size_t i);
@@ -304,43 +271,150 @@ __device__ __forceinline__ float wload<uint16_t>(const uint16_t* p, size_t i) {
 template <>
 __device__ __forceinline__ float wload<float>(const float* p, size_t i) { return p[i]; }
 
+// Workgroup barrier that orders LDS only. __syncthreads() carries workgroup
+// release/acquire fences, and the compiler makes a release wait for every
+// outstanding direct-to-LDS load, which would drain the memory waves' weight
+// prefetch at each barrier. No data crosses waves through global memory or
+// through direct-to-LDS loads here (each memory wave reads only its own ring
+// after waiting on its own counter), so LDS completion is all a barrier needs.
+__device__ __forceinline__ void bar() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// ------------------------------------------------------------------ waits
+// Exchange threads only. A wait ends when every word carries the tag, when it
+// runs out of time (then the workgroup's abort flag and the launch's error
+// flag are raised), or at once after an abort: later values are then garbage
+// and only the error flag matters.
+
+__device__ __forceinline__ bool give_up(u64 t0, Ctl* ctl, int* err) {
+  if (__hip_atomic_load(&ctl->abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) return true;
+  if (now() - t0 > kWaitTicks) {
+    __hip_atomic_store(&ctl->abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    return true;
+  }
+  return false;
+}
+
+// x[k] += sum_{q < P} W[q * n + e] for e = et + k * kEx < n (P <= 8), in that order.
+template <int NE>
+__device__ __forceinline__ void gather_sum(const u64* W, int P, int n, unsigned tag, float (&x)[NE], int et,
+                                           Ctl* ctl, int* err) {
+  const u64 t0 = now();
+  u64 w[NE][kGroups];
+  // a wave-uniform base per part plus one 32-bit byte offset per element
+  unsigned eo[NE];
+#pragma unroll
+  for (int k = 0; k < NE; ++k) eo[k] = (unsigned)min(et + k * kEx, n - 1) * 8u;
+  while (true) {
+#pragma unroll
+    for (int q = 0; q < kGroups; ++q) {
+      if (q < P) {
+        const char* wq = (const char*)(W + (size_t)q * n);
+#pragma unroll
+        for (int k = 0; k < NE; ++k) w[k][q] = get((const u64*)(wq + eo[k]));
+      }
+    }
+    bool done = true;
+#pragma unroll
+    for (int k = 0; k < NE; ++k)
+#pragma unroll
+      for (int q = 0; q < kGroups; ++q)
+        if (q < P) done = done && tagged(w[k][q], tag);
+    if (done || give_up(t0, ctl, err)) break;
+  }
+#pragma unroll
+  for (int k = 0; k < NE; ++k) {
+    if (et + k * kEx < n) {
+      float s = x[k];
+#pragma unroll
+      for (int q = 0; q < kGroups; ++q)
+        if (q < P) s += val(w[k][q]);
+      x[k] = s;
+    }
+  }
+}
+
+// dst[i] = value of W[i] for i = et + j * kEx < n (n <= J * kEx).
+template <int J>
+__device__ __forceinline__ void gather_vec(const u64* W, int n, unsigned tag, float* dst, int et, Ctl* ctl,
+                                           int* err) {
+  const u64 t0 = now();
+  u64 w[J];
+  const unsigned last = (unsigned)(n - 1) * 8u;
+  while (true) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) w[j] = get((const u64*)((const char*)W + min((unsigned)(et + j * kEx) * 8u, last)));
+    bool done = true;
+#pragma unroll
+    for (int j = 0; j < J; ++j) done = done && tagged(w[j], tag);
+    if (done || give_up(t0, ctl, err)) break;
+  }
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+    if (et + j * kEx < n) dst[et + j * kEx] = val(w[j]);
+}
+
+__device__ __forceinline__ void gather_any(const u64* W, int n, unsigned tag, float* dst, int et, Ctl* ctl, int* err) {
+  if (n <= 4 * kEx)
+    gather_vec<4>(W, n, tag, dst, et, ctl, err);
+  else
+    gather_vec<32>(W, n, tag, dst, et, ctl, err);
+}
+
+// Barrier of the four exchange waves (the memory waves do not take part):
+// each wave adds one arrival to an LDS counter and waits for the generation's
+// total. `gen` counts arrivals expected so far (same sequence in every exchange wave).
+__device__ __forceinline__ void ex_sync(int& gen, int lane, Ctl* ctl, int* err) {
+  gen += kExWaves;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's LDS writes are done
+  if (lane == 0) __hip_atomic_fetch_add(&ctl->exbar, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  const u64 t0 = now();
+  while (__hip_atomic_load(&ctl->exbar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < gen) {
+    if (now() - t0 > kWaitTicks) {
+      __hip_atomic_store(&ctl->abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");
+}
+
 // --------------------------------------------------------------- weights
 
 template <typename WT>
 __device__ __forceinline__ float dot_chunk(const u32x4& raw, const float* x);
 template <>
 __device__ __forceinline__ float dot_chunk<uint16_t>(const u32x4& raw, const float* x) {
-  const float4 a = *reinterpret_cast<const float4*>(x);
-  const float4 b = *reinterpret_cast<const float4*>(x + 4);
-  float s = __uint_as_float(raw.x << 16) * a.x;
-  s = fmaf(__uint_as_float(raw.x & 0xFFFF0000u), a.y, s);
-  s = fmaf(__uint_as_float(raw.y << 16), a.z, s);
-  s = fmaf(__uint_as_float(raw.y & 0xFFFF0000u), a.w, s);
-  s = fmaf(__uint_as_float(raw.z << 16), b.x, s);
-  s = fmaf(__uint_as_float(raw.z & 0xFFFF0000u), b.y, s);
-  s = fmaf(__uint_as_float(raw.w << 16), b.z, s);
-  return fmaf(__uint_as_float(raw.w & 0xFFFF0000u), b.w, s);
+  float s = __uint_as_float(raw.x << 16) * x[0];
+  s = fmaf(__uint_as_float(raw.x & 0xFFFF0000u), x[1], s);
+  s = fmaf(__uint_as_float(raw.y << 16), x[2], s);
+  s = fmaf(__uint_as_float(raw.y & 0xFFFF0000u), x[3], s);
+  s = fmaf(__uint_as_float(raw.z << 16), x[4], s);
+  s = fmaf(__uint_as_float(raw.z & 0xFFFF0000u), x[5], s);
+  s = fmaf(__uint_as_float(raw.w << 16), x[6], s);
+  return fmaf(__uint_as_float(raw.w & 0xFFFF0000u), x[7], s);
 }
 template <>
 __device__ __forceinline__ float dot_chunk<float>(const u32x4& raw, const float* x) {
-  const float4 a = *reinterpret_cast<const float4*>(x);
-  float s = __uint_as_float(raw.x) * a.x;
-  s = fmaf(__uint_as_float(raw.y), a.y, s);
-  s = fmaf(__uint_as_float(raw.z), a.z, s);
-  return fmaf(__uint_as_float(raw.w), a.w, s);
+  float s = __uint_as_float(raw.x) * x[0];
+  s = fmaf(__uint_as_float(raw.y), x[1], s);
+  s = fmaf(__uint_as_float(raw.z), x[2], s);
+  return fmaf(__uint_as_float(raw.w), x[3], s);
 }
 
 // Rows of one phase for this workgroup. Local row j of the job maps to a
-// physical row of a row-major matrix `base` (row stride ld elements); the dot
-// covers columns [col0, col0 + K). kind: 0 linear (row0 + j), 1 Q/K/V rows of
-// KV head g (local index row0 + j inside the head's (G+2)*D rows), 2 gate/up
-// pairs of z index row0 + j/2 (gate when j is even) in the interleaved layout.
-template <typename WT>
+// physical row of a row-major matrix (row stride ld elements); the dot covers
+// columns [col0, col0 + K). kind: 0 linear (row0 + j), 1 Q/K/V rows of KV head
+// g (local index row0 + j inside the head's (G+2)*D rows), 2 gate/up pairs of
+// z index row0 + j/2 (gate when j is even) in the interleaved layout.
 struct Job {
-  const WT* base;
   int ld, col0, K, nrows, kind, row0;
-  int qd, d, nq_d, nkv_d, g;  // kind 1 mapping
-  __device__ __forceinline__ int phys(int j) const {
+  __device__ __forceinline__ int phys(int j, int qd, int d, int nq_d, int nkv_d, int g) const {
     if (kind == 0) return row0 + j;
     if (kind == 1) {
       const int i = row0 + j;
@@ -353,41 +427,7 @@ struct Job {
   }
 };
 
-// Memory-wave weight staging. Each memory wave owns an LDS ring of two regions
-// of kSlots slots; a slot holds one 16-byte chunk per lane (1 KB). A unit (one
-// phase's rows of this wave, or one batch of LM-head rows) is copied into a
-// region by direct global-to-LDS loads (lane i's 16 bytes land at slot + 16 i)
-// and later read back by the same lanes for the dot products. Unit k uses
-// region k & 1; after computing unit k the wave issues unit k + 2, so one unit
-// is always in flight while another is consumed. The wave issues no other
-// vector-memory operations, so the count of its loads issued after a unit
-// tells exactly how far the vector-memory counter may lag when that unit is
-// needed.
-//
-// Slot q of a unit covers the wave's job row i = bt * rpb + (q >> lg) and
-// chunk c = lane + 64 * (q & (cpl - 1)), with cpl = 2^lg chunks per lane per
-// row and rpb = kSlots >> lg rows per unit; the wave owns job rows w + 4 i.
-constexpr int kSlots = 12;
-constexpr int kMaxVec = 2048;  // longest GEMV input: max(hidden, G * D, ffn / 8)
-constexpr int kSlotBytes = kWave * 16;
-
 typedef __attribute__((address_space(3))) void lds_void;
-
-template <typename WT>
-__device__ __forceinline__ int job_lg(const Job<WT>& jb) {
-  const int nch = jb.K / (16 / (int)sizeof(WT));
-  const int cpl = (nch + kWave - 1) / kWave;
-  return cpl <= 1 ? 0 : cpl <= 2 ? 1 : cpl <= 4 ? 2 : 3;
-}
-template <typename WT>
-__device__ __forceinline__ int job_rows_of_wave(const Job<WT>& jb, int w) {
-  return jb.nrows > w ? (jb.nrows - w + kMemWaves - 1) / kMemWaves : 0;
-}
-template <typename WT>
-__device__ __forceinline__ int job_units(const Job<WT>& jb, int w) {
-  const int rpb = kSlots >> job_lg(jb);
-  return (job_rows_of_wave(jb, w) + rpb - 1) / rpb;
-}
 
 // s_waitcnt vmcnt(n) for a wave-uniform n (loads issued after the needed ones)
 __device__ __forceinline__ void wait_vm(int n) {
@@ -404,104 +444,81 @@ __device__ __forceinline__ void wait_vm(int n) {
   }
 }
 
-// The two regions are distinct LDS arrays so that the compiler, which must
-// wait for outstanding direct-to-LDS loads before an LDS read that may alias
-// them, can tell a read of one region (or of any other LDS data) from the
-// loads in flight into the other.
+// A memory wave's ring. The two regions are distinct LDS arrays so that the
+// compiler, which must wait for outstanding direct-to-LDS loads before an LDS
+// read that may alias them, can tell a read of one region from the loads in
+// flight into the other. The wave issues no other vector-memory operations,
+// so the count of loads issued after a unit tells exactly how far the
+// vector-memory counter may lag when that unit is needed.
 struct Ring {
-  char* r0;    // this wave's slots in region 0
-  char* r1;    // this wave's slots in region 1
-  int issued;  // loads issued by this wave
+  char* r0;
+  char* r1;
+  int issued;        // loads issued by this wave
   int mark0, mark1;  // `issued` right after the unit of each region was issued
 };
 
-template <int PAR, int LG, typename WT>
-__device__ __forceinline__ void ring_issue_lg(Ring& rg, const Job<WT>& jb, int bt, int w, int lane) {
-  constexpr int VN = 16 / sizeof(WT);
-  constexpr int RPB = kSlots >> LG;
-  const int nch = jb.K / VN;
-  const int nrw = job_rows_of_wave(jb, w);
-  char* region = PAR ? rg.r1 : rg.r0;
+// Issue one unit into region P: slot q (q < ns) holds chunk c = lane + 64 (q & (2^lg - 1))
+// (clamped to the row's last chunk) of the row starting ro(q) bytes after
+// `base`, where ro(q) is lane q of `tab`.
+template <int P>
+__device__ __forceinline__ void issue_unit(Ring& rg, const char* base, int tab, int ns, int lg, int nchm1,
+                                           int lane) {
+  char* region = P ? rg.r1 : rg.r0;
+  const int jm = (1 << lg) - 1;
 #pragma unroll
-  for (int ii = 0; ii < RPB; ++ii) {
-    const int i = bt * RPB + ii;
-    if (i < nrw) {  // wave-uniform: every lane issues, so the count is exact
-      const WT* rowp = jb.base + (size_t)jb.phys(w + kMemWaves * i) * jb.ld + jb.col0;
-#pragma unroll
-      for (int jj = 0; jj < (1 << LG); ++jj) {
-        const int c = lane + kWave * jj;
-        const WT* src = rowp + (size_t)(c < nch ? c : 0) * VN;
-        __builtin_amdgcn_global_load_lds((const void*)src,
-                                         (lds_void*)(region + (ii * (1 << LG) + jj) * kSlotBytes), 16, 0, 0);
-      }
-      rg.issued += 1 << LG;
+  for (int q = 0; q < kSlots; ++q) {
+    if (q < ns) {
+      const int ro = __builtin_amdgcn_readlane(tab, q);
+      const int c = min(lane + ((q & jm) << 6), nchm1);
+      __builtin_amdgcn_global_load_lds((const void*)(base + ro + c * 16), (lds_void*)(region + q * kSlotBytes), 16,
+                                       0, 0);
     }
   }
-  if (PAR)
+  rg.issued += ns;
+  if (P)
     rg.mark1 = rg.issued;
   else
     rg.mark0 = rg.issued;
 }
 
-template <int PAR, typename WT>
-__device__ __forceinline__ void ring_issue(Ring& rg, const Job<WT>& jb, int bt, int w, int lane) {
-  switch (job_lg(jb)) {
-    case 0: ring_issue_lg<PAR, 0>(rg, jb, bt, w, lane); break;
-    case 1: ring_issue_lg<PAR, 1>(rg, jb, bt, w, lane); break;
-    case 2: ring_issue_lg<PAR, 2>(rg, jb, bt, w, lane); break;
-    default: ring_issue_lg<PAR, 3>(rg, jb, bt, w, lane); break;
-  }
-}
-
-template <int PAR>
-__device__ __forceinline__ void ring_wait(const Ring& rg) {
-  wait_vm(rg.issued - (PAR ? rg.mark1 : rg.mark0));
-}
-
-// Dot products of a unit whose loads are complete (ring_wait): f(j, value)
-// for every job row j of this wave in batch bt (value wave-reduced and
-// wave-uniform; called by all lanes).
-template <int PAR, int LG, typename WT, typename Fn>
-__device__ __forceinline__ void ring_dot_lg(const Ring& rg, const Job<WT>& jb, int bt, const float* x, int w, int lane,
-                                            Fn f) {
+// Partial dot products of the unit in region P (all kSlots slots; slots past
+// the unit's count hold stale data whose results nobody reads): slot q's
+// chunk times this lane's input chunk (q & (2^LG - 1)), summed over the wave.
+// The input must be zero past the GEMV's length up to 64 * VN * 2^LG.
+template <int P, int LG, typename WT>
+__device__ __forceinline__ void dot_unit(const Ring& rg, const float* xin, float* dst, int lane) {
   constexpr int VN = 16 / sizeof(WT);
-  constexpr int RPB = kSlots >> LG;
-  const int nch = jb.K / VN;
-  const int nrw = job_rows_of_wave(jb, w);
-  const char* region = PAR ? rg.r1 : rg.r0;
-  // this lane's input chunks are the same for every row of the unit
-  float xv[1 << LG][VN];
+  constexpr int CPL = 1 << LG;
+  const char* region = P ? rg.r1 : rg.r0;
+  float xr[CPL][VN];
 #pragma unroll
-  for (int jj = 0; jj < (1 << LG); ++jj) {
-    const int c = lane + kWave * jj;
+  for (int jj = 0; jj < CPL; ++jj)
 #pragma unroll
     for (int e = 0; e < VN; e += 4) {
-      const float4 t = c < nch ? *reinterpret_cast<const float4*>(x + c * VN + e) : make_float4(0.f, 0.f, 0.f, 0.f);
-      xv[jj][e] = t.x; xv[jj][e + 1] = t.y; xv[jj][e + 2] = t.z; xv[jj][e + 3] = t.w;
+      const float4 t = *reinterpret_cast<const float4*>(xin + (lane + kWave * jj) * VN + e);
+      xr[jj][e] = t.x;
+      xr[jj][e + 1] = t.y;
+      xr[jj][e + 2] = t.z;
+      xr[jj][e + 3] = t.w;
     }
-  }
+  u32x4 raw[kSlots];
 #pragma unroll
-  for (int ii = 0; ii < RPB; ++ii) {
-    if (bt * RPB + ii < nrw) {
-      float acc = 0.f;
+  for (int q = 0; q < kSlots; ++q) raw[q] = *reinterpret_cast<const u32x4*>(region + q * kSlotBytes + lane * 16);
+  float s[kSlots];
 #pragma unroll
-      for (int jj = 0; jj < (1 << LG); ++jj) {
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(region + (ii * (1 << LG) + jj) * kSlotBytes + lane * 16);
-        acc += dot_chunk<WT>(raw, xv[jj]);
-      }
-      f(w + kMemWaves * (bt * RPB + ii), wave_sum(acc));
-    }
-  }
+  for (int q = 0; q < kSlots; ++q) s[q] = dot_chunk<WT>(raw[q], xr[q & (CPL - 1)]);
+  reduce12_store(s, dst, lane);
 }
 
-template <int PAR, typename WT, typename Fn>
-__device__ __forceinline__ void ring_dot(const Ring& rg, const Job<WT>& jb, int bt, const float* x, int w, int lane,
-                                         Fn f) {
-  switch (job_lg(jb)) {
-    case 0: ring_dot_lg<PAR, 0>(rg, jb, bt, x, w, lane, f); break;
-    case 1: ring_dot_lg<PAR, 1>(rg, jb, bt, x, w, lane, f); break;
-    case 2: ring_dot_lg<PAR, 2>(rg, jb, bt, x, w, lane, f); break;
-    default: ring_dot_lg<PAR, 3>(rg, jb, bt, x, w, lane, f); break;
+template <int P, typename WT>
+__device__ __forceinline__ void consume_unit(Ring& rg, int lg, const float* xin, float* dst, int lane) {
+  wait_vm(rg.issued - (P ? rg.mark1 : rg.mark0));
+  if (lg == 0) {
+    dot_unit<P, 0, WT>(rg, xin, dst, lane);
+  } else if (sizeof(WT) == 2 || lg == 1) {
+    dot_unit<P, 1, WT>(rg, xin, dst, lane);
+  } else {
+    dot_unit<P, (sizeof(WT) == 2 ? 1 : 2), WT>(rg, xin, dst, lane);
   }
 }
 
@@ -538,11 +555,10 @@ __device__ __forceinline__ void load_kv(const DecParams& p, int l, int g, int u,
 
 // Online-softmax attention of the G query heads of KV head g over the keys
 // [u0, u0 + n_cached) of the cache plus (if with_cur) the current token held
-// in LDS, run by the exchange waves. Lane layout: key slot = lane / 8 (8 keys
-// per wave per iteration), part = lane % 8 owns DPL = D/8 dims. Result per head
-// (combined over the waves): M, Lsum and the unnormalised O, written to
-// res[h * (D + 2) + {0, 1, 2..}]. The first two iterations' K/V come from
-// prefetch().
+// in LDS, one exchange wave's share. Lane layout: key slot = lane / 8 (8 keys
+// per wave per iteration), part = lane % 8 owns DPL = D/8 dims. The wave's
+// result per head: running max, sum and unnormalised output in wm, wl, wo.
+// The first two iterations' K/V come from prefetch().
 template <int D, int G>
 struct Attn {
   static constexpr int DPL = D / 8;
@@ -606,486 +622,589 @@ struct Attn {
     }
   }
 
-  // All threads call; only `act` threads compute. q_l: [G][D] (scaled), k_l,
-  // v_l: [D] current token; wbuf scratch: 2 * kExWaves * G + kExWaves * G * D.
-  __device__ __forceinline__ void run(bool act, const DecParams& p, int l, int g, int u0, int n_cached,
-                                      bool with_cur, const float* q_l, const float* k_l, const float* v_l,
-                                      float* wbuf, float* res, int ew, int lane, int et) {
-    float* wm = wbuf;                     // [kExWaves][G]
-    float* wl = wm + kExWaves * G;        // [kExWaves][G]
-    float* wo = wl + kExWaves * G;        // [kExWaves][G][D]
-    if (act) {
-      const int slot = lane / 8, part = lane % 8;
-      float m[G], ls[G], acc[G][DPL];
+  // q_l: [G][D] (scaled), k_l, v_l: [D] current token; writes wm[ew*G + h],
+  // wl[ew*G + h], wo[(ew*G + h)*D + d].
+  __device__ __forceinline__ void partial(const DecParams& p, int l, int g, int u0, int n_cached, bool with_cur,
+                                          const float* q_l, const float* k_l, const float* v_l, float* wm, float* wl,
+                                          float* wo, int ew, int lane) {
+    const int slot = lane / 8, part = lane % 8;
+    float m[G], ls[G], acc[G][DPL];
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        m[h] = -INFINITY;
-        ls[h] = 0.f;
+    for (int h = 0; h < G; ++h) {
+      m[h] = -INFINITY;
+      ls[h] = 0.f;
 #pragma unroll
-        for (int i = 0; i < DPL; ++i) acc[h][i] = 0.f;
+      for (int i = 0; i < DPL; ++i) acc[h][i] = 0.f;
+    }
+    const int n_keys = n_cached + (with_cur ? 1 : 0);
+    for (int base = 0; base < n_keys; base += 2 * kPerIt) {
+      const int ka = base + ew * 8 + slot;
+      step(q_l, k_l, v_l, kv0, vv0, ka, n_cached, n_keys, part, m, ls, acc);
+      const int kn0 = ka + 2 * kPerIt;
+      if (kn0 < n_cached) load_kv<DPL>(p, l, g, u0 + kn0, part, u0 + kn0 >= p.pos0, kv0, vv0);
+      const int kb = ka + kPerIt;
+      if (base + kPerIt < n_keys) step(q_l, k_l, v_l, kv1, vv1, kb, n_cached, n_keys, part, m, ls, acc);
+      const int kn1 = kb + 2 * kPerIt;
+      if (kn1 < n_cached) load_kv<DPL>(p, l, g, u0 + kn1, part, u0 + kn1 >= p.pos0, kv1, vv1);
+    }
+    // sum the 8 key slots of the wave (same running max within the wave)
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) {
+        float v = acc[h][i];
+        v += dpp<kDppXor8>(v);  // same part of the other key slot in the row
+        v = sum32(sum16(v));
+        acc[h][i] = v;
       }
-      const int n_keys = n_cached + (with_cur ? 1 : 0);
-      for (int base = 0; base < n_keys; base += 2 * kPerIt) {
-        const int ka = base + ew * 8 + slot;
-        step(q_l, k_l, v_l, kv0, vv0, ka, n_cached, n_keys, part, m, ls, acc);
-        const int kn0 = ka + 2 * kPerIt;
-        if (kn0 < n_cached) load_kv<DPL>(p, l, g, u0 + kn0, part, u0 + kn0 >= p.pos0, kv0, vv0);
-        const int kb = ka + kPerIt;
-        if (base + kPerIt < n_keys) step(q_l, k_l, v_l, kv1, vv1, kb, n_cached, n_keys, part, m, ls, acc);
-        const int kn1 = kb + 2 * kPerIt;
-        if (kn1 < n_cached) load_kv<DPL>(p, l, g, u0 + kn1, part, u0 + kn1 >= p.pos0, kv1, vv1);
-      }
-      // sum the 8 key slots of the wave (same running max within the wave)
+    if (slot == 0) {
 #pragma unroll
       for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int i = 0; i < DPL; ++i) {
-          float v = acc[h][i];
-          v += dpp<kDppXor8>(v);  // same part of the other key slot in the row
-          v = sum32(sum16(v));
-          acc[h][i] = v;
-        }
-      if (slot == 0) {
+        for (int i = 0; i < DPL; ++i) wo[(ew * G + h) * D + part * DPL + i] = acc[h][i];
+    }
+    if (lane == 0) {
 #pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-          for (int i = 0; i < DPL; ++i) wo[(ew * G + h) * D + part * DPL + i] = acc[h][i];
-      }
-      if (lane == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          wm[ew * G + h] = m[h];
-          wl[ew * G + h] = ls[h];
-        }
+      for (int h = 0; h < G; ++h) {
+        wm[ew * G + h] = m[h];
+        wl[ew * G + h] = ls[h];
       }
     }
-    __syncthreads();
-    if (act) {
-      for (int idx = et; idx < G * (D + 2); idx += kEx) {
-        const int h = idx / (D + 2), e = idx % (D + 2);
-        float M = -INFINITY;
-#pragma unroll
-        for (int w2 = 0; w2 < kExWaves; ++w2) M = fmaxf(M, wm[w2 * G + h]);
-        float v = 0.f;
-        if (e == 0) {
-          v = M;
-        } else {
-#pragma unroll
-          for (int w2 = 0; w2 < kExWaves; ++w2) {
-            const float mw = wm[w2 * G + h];
-            const float f = (mw == -INFINITY) ? 0.f : expf(mw - M);
-            v = fmaf(f, e == 1 ? wl[w2 * G + h] : wo[(w2 * G + h) * D + (e - 2)], v);
-          }
-        }
-        res[idx] = v;
-      }
-    }
-    __syncthreads();
   }
 };
 
 // ------------------------------------------------------------------- kernel
 
-using P0 = std::integral_constant<int, 0>;
-using P1 = std::integral_constant<int, 1>;
-
 template <typename WT, int D, int G, int NE>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
   extern __shared__ float sm[];
   constexpr int QD = G * D, GW = (G + 2) * D;
-  float* xres = sm + p.lds_x;      // residual stream [H], identical in every workgroup
-  // GEMV input (normalised x, o_g or z slice): its own LDS array, read while
-  // weight loads into the rings are in flight
-  __shared__ __attribute__((aligned(16))) float xn[kMaxVec];
-  float* stage = sm + p.lds_stage; // raw q/k/v, split partials, argmax keys
-  float* att = sm + p.lds_att;     // q_l [G][D] | k_l [D] | v_l [D] | res [G][D+2] | wave scratch
-  float* red = sm + p.lds_red;     // [64] reductions
-  float* rbuf = sm + p.lds_rbuf;   // [64] dot results of the memory waves
-  float* lgb = sm + p.lds_lgb;     // this workgroup's logits of one step
+  constexpr int VN = 16 / sizeof(WT);
+  constexpr int ES = sizeof(WT);
+  // GEMV input of the current phase (x * g, o_x or z_x), zero past its length
+  __shared__ __attribute__((aligned(16))) float xin[kMaxK];
+  __shared__ __attribute__((aligned(16))) char ring0[kMemWaves * kSlots * kSlotBytes];
+  __shared__ __attribute__((aligned(16))) char ring1[kMemWaves * kSlots * kSlotBytes];
+  __shared__ Ctl ctl;
+  float* stage = sm + p.lds_stage;  // split-attention partials of all ranks
+  float* att = sm + p.lds_att;      // q_l [G][D] | k_l [D] | v_l [D] | wm | wl | wo
+  float* sbuf = sm + p.lds_sbuf;    // per-slot partial dots [wave][unit][kSlots]
   float* q_l = att;
   float* k_l = q_l + QD;
   float* v_l = k_l + D;
-  float* ares = v_l + D;
-  float* wscr = ares + G * (D + 2);
+  float* wm = v_l + D;
+  float* wl = wm + kExWaves * G;
+  float* wo = wl + kExWaves * G;
 
-  const int tid0 = threadIdx.x;
-  const int lane0 = tid0 % kWave;
-  const int wave0 = __builtin_amdgcn_readfirstlane(tid0 / kWave);
-  const bool mem = wave0 < kMemWaves;  // wave-uniform role
-  const bool ex = !mem;
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const bool mem = wave < kMemWaves;  // wave-uniform role
   const int b = blockIdx.x, nb = gridDim.x;
   const int X = b % kGroups, r = b / kGroups, R = p.R;
   const int H = p.H, F = p.F, NKV = p.NKV, NQ = p.NQ, L = p.L;
   const int FS = F / kGroups;
   const bool has_att = X < NKV;
-  const WT* embed = (const WT*)p.embed;
+  const int per_layer = has_att ? 4 : 2;  // weight units per layer: A, C, D, E or D, E
+  const int nlu = per_layer * L;
 
   // this workgroup's row ranges (fixed for all layers)
-  int a0_, a1_, c0_, c1_, z0_, z1_, e0_, e1_, h0_, h1_;
-  split(GW, R, r, a0_, a1_);
-  split(H, R, r, c0_, c1_);
-  split(FS, R, r, z0_, z1_);
-  split(H, R, r, e0_, e1_);
-  split(p.V, nb, b, h0_, h1_);
+  int a0, a1, c0, c1, z0, z1, e0, e1, h0, h1;
+  split(GW, R, r, a0, a1);
+  split(H, R, r, c0, c1);
+  split(FS, R, r, z0, z1);
+  split(H, R, r, e0, e1);
+  split(p.V, nb, b, h0, h1);
+  const int lgH = chunk_lg(H, VN), rpbH = kSlots >> lgH;
+  const int NHU = p.nhu;
 
-  auto WL = [&](int l) { return (const WT*)p.wbuf + (size_t)l * p.layer_elems; };
-  // weight units of one step, in the order the memory waves consume them:
-  // with attention A, C, D, E per layer, else D, E per layer; then LM-head batches
-  const int per_layer = has_att ? 4 : 2;
-  const int n_layer_units = per_layer * L;
-  auto unit_job = [&](int k, int a0, int a1, int c0, int c1, int z0, int z1, int e0, int e1, int h0, int h1,
-                      int& bt) __attribute__((always_inline)) {
-    bt = 0;
-    if (k >= n_layer_units) {
-      bt = k - n_layer_units;
-      return Job<WT>{embed, H, 0, H, h1 - h0, 0, h0, 0, 0, 0, 0, 0};
+  if (tid == 0) {
+    ctl.abort = 0;
+    ctl.exbar = 0;
+  }
+
+  if (mem) {
+    // ================================================================ memory waves
+    const int w = wave;
+    Ring rg{ring0 + w * kSlots * kSlotBytes, ring1 + w * kSlots * kSlotBytes, 0, 0, 0};
+    // the four layer jobs A, C, D, E: slots issued, chunk rows per row (lg),
+    // last chunk, and lane q of tab = byte offset of slot q's row from the matrix base
+    const Job jobs[4] = {Job{H, 0, H, a1 - a0, 1, a0}, Job{NQ * D, X * QD, QD, c1 - c0, 0, c0},
+                         Job{H, 0, H, 2 * (z1 - z0), 2, X * FS + z0}, Job{F, X * FS, FS, e1 - e0, 0, e0}};
+    int tab[4], ns[4], lgs[4], nchm1[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const Job& jb = jobs[t];
+      const int lg = chunk_lg(jb.K, VN);
+      const int nrw = jb.nrows > w ? (jb.nrows - w + kMemWaves - 1) / kMemWaves : 0;
+      lgs[t] = lg;
+      ns[t] = __builtin_amdgcn_readfirstlane(nrw << lg);
+      nchm1[t] = jb.K / VN - 1;
+      int ro = 0;
+      if (lane < (nrw << lg)) {
+        const int j = w + kMemWaves * (lane >> lg);
+        ro = (jb.phys(j, QD, D, NQ * D, NKV * D, X) * jb.ld + jb.col0) * ES;
+      }
+      tab[t] = ro;
     }
-    const int l = k / per_layer;
-    int t = k % per_layer;
-    if (!has_att) t += 2;
-    if (t == 0) return Job<WT>{WL(l), H, 0, H, a1 - a0, 1, a0, QD, D, NQ * D, NKV * D, X};
-    if (t == 1) return Job<WT>{WL(l) + p.off_o, NQ * D, X * QD, QD, c1 - c0, 0, c0, 0, 0, 0, 0, 0};
-    if (t == 2) return Job<WT>{WL(l) + p.off_gu, H, 0, H, 2 * (z1 - z0), 2, X * FS + z0, 0, 0, 0, 0, 0};
-    return Job<WT>{WL(l) + p.off_d, F, X * FS, FS, e1 - e0, 0, e0, 0, 0, 0, 0, 0};
-  };
+    const int nrwH = (h1 - h0) > w ? ((h1 - h0) - w + kMemWaves - 1) / kMemWaves : 0;
+    const int n_units = nlu + NHU;
+    const char* wbase = (const char*)p.wbuf;
+    const char* ebase = (const char*)p.embed;
+    const int rowH = H * ES;
+    const int nchH = H / VN - 1;
+    int ml = lane;  // made opaque per unit, like the exchange waves' indices
 
-  __shared__ __attribute__((aligned(16))) char ring0[kMemWaves * kSlots * kSlotBytes];
-  __shared__ __attribute__((aligned(16))) char ring1[kMemWaves * kSlots * kSlotBytes];
-  const int rw = mem ? wave0 : 0;
-  Ring rg{ring0 + rw * kSlots * kSlotBytes, ring1 + rw * kSlots * kSlotBytes, 0, 0, 0};
-  int token = p.token_dev ? p.token_dev[0] : p.token;
-  token = token < 0 ? 0 : (token >= p.V ? p.V - 1 : token);
-
-  for (int step = 0; step < p.nsteps; ++step) {
-    const int pos = p.pos0 + step;
-    const int n_hist = pos;  // cached positions 0 .. pos-1
-    int n_units = 0;
-    {
-      // Index bases made opaque per iteration: keeps per-row address arithmetic
-      // from being hoisted out of the loops and held in registers.
-      int tid = tid0, lane = lane0, wave = wave0, a0 = a0_, a1 = a1_, c0 = c0_, c1 = c1_, z0 = z0_, z1 = z1_,
-          e0 = e0_, e1 = e1_, h0 = h0_, h1 = h1_;
-      asm volatile("" : "+v"(tid), "+v"(lane));
-      asm volatile("" : "+s"(wave), "+s"(a0), "+s"(a1), "+s"(c0), "+s"(c1), "+s"(z0), "+s"(z1));
-      asm volatile("" : "+s"(e0), "+s"(e1), "+s"(h0), "+s"(h1));
-      TRACE(step, 0);
-      if (mem) {
-        const Job<WT> jh{embed, H, 0, H, h1 - h0, 0, h0, 0, 0, 0, 0, 0};
-        n_units = n_layer_units + job_units(jh, wave);
-        int bt;
-        const Job<WT> j0 = unit_job(0, a0, a1, c0, c1, z0, z1, e0, e1, h0, h1, bt);
-        ring_issue<0>(rg, j0, bt, wave, lane);
-        const Job<WT> j1 = unit_job(1, a0, a1, c0, c1, z0, z1, e0, e1, h0, h1, bt);
-        ring_issue<1>(rg, j1, bt, wave, lane);
+    // issue unit k of a step (weights do not change between steps) into region P
+    auto issue = [&](auto par_tag, int k) __attribute__((always_inline)) {
+      constexpr int P = decltype(par_tag)::value;
+      if (k < nlu) {
+        const int l = k / per_layer;
+        const int t = k % per_layer + (has_att ? 0 : 2);
+        const int tb = t == 0 ? tab[0] : t == 1 ? tab[1] : t == 2 ? tab[2] : tab[3];
+        const int n = t == 0 ? ns[0] : t == 1 ? ns[1] : t == 2 ? ns[2] : ns[3];
+        const int lg = t == 0 ? lgs[0] : t == 1 ? lgs[1] : t == 2 ? lgs[2] : lgs[3];
+        const int cm = t == 0 ? nchm1[0] : t == 1 ? nchm1[1] : t == 2 ? nchm1[2] : nchm1[3];
+        const size_t toff = t == 0 ? 0 : t == 1 ? p.off_o : t == 2 ? p.off_gu : p.off_d;
+        const char* base = wbase + ((size_t)l * p.layer_elems + toff) * ES;
+        issue_unit<P>(rg, base, tb, n, lg, cm, ml);
       } else {
-        for (int i = tid - kExBase; i < H; i += kEx) xres[i] = wload(embed, (size_t)token * H + i);
+        const int u = k - nlu;
+        const int i0 = u * rpbH;  // first local head row of the unit
+        int n = nrwH - i0;
+        n = n < 0 ? 0 : (n > rpbH ? rpbH : n);
+        const int ro = (h0 + w + kMemWaves * (i0 + (ml >> lgH))) * rowH;
+        issue_unit<P>(rg, ebase, ro, __builtin_amdgcn_readfirstlane(n << lgH), lgH, nchH, ml);
       }
-      __syncthreads();
-    }
-
-    // Consume unit k (its region is PAR = k & 1), then issue unit k + 2 into that region.
-    auto unit = [&](auto par_tag, int k, const float* x, auto f, int ti = -1) __attribute__((always_inline)) {
-      constexpr int PAR = decltype(par_tag)::value;
-      (void)ti;
-      TRACEM(step, ti);
-      int lane = lane0, wave = wave0, a0 = a0_, a1 = a1_, c0 = c0_, c1 = c1_, z0 = z0_, z1 = z1_, e0 = e0_,
-          e1 = e1_, h0 = h0_, h1 = h1_;
-      asm volatile("" : "+v"(lane));
-      asm volatile("" : "+s"(wave), "+s"(a0), "+s"(a1), "+s"(c0), "+s"(c1), "+s"(z0), "+s"(z1));
-      asm volatile("" : "+s"(e0), "+s"(e1), "+s"(h0), "+s"(h1));
-      int bt;
-      const Job<WT> j = unit_job(k, a0, a1, c0, c1, z0, z1, e0, e1, h0, h1, bt);
-      ring_wait<PAR>(rg);
-      TRACEM(step, ti < 0 ? -1 : ti + 1);
-      ring_dot<PAR>(rg, j, bt, x, wave, lane, f);
-      TRACEM(step, ti < 0 ? -1 : ti + 2);
-      if (k + 2 < n_units) {
-        int bt2;
-        const Job<WT> j2 = unit_job(k + 2, a0, a1, c0, c1, z0, z1, e0, e1, h0, h1, bt2);
-        ring_issue<PAR>(rg, j2, bt2, wave, lane);
-      }
-      TRACEM(step, ti < 0 ? -1 : ti + 3);
+    };
+    auto unit_lg = [&](int k) __attribute__((always_inline)) {
+      if (k >= nlu) return lgH;
+      const int t = k % per_layer + (has_att ? 0 : 2);
+      return t == 0 ? lgs[0] : t == 1 ? lgs[1] : t == 2 ? lgs[2] : lgs[3];
     };
 
-    // attention mode for this step
-    const bool whole = n_hist <= p.whole_max;
-    int nsplit = 1;
-    if (!whole) nsplit = min(p.nsplit_max, (n_hist + p.whole_max - 1) / p.whole_max);
+    if (p.nsteps > 0) issue(std::integral_constant<int, 0>{}, 0);
+    if (p.nsteps > 0 && n_units > 1) issue(std::integral_constant<int, 1>{}, 1);
+    bar();  // start
+    int g = 0;        // units consumed so far (ring parity)
+    for (int step = 0; step < p.nsteps; ++step) {
+      for (int k = 0; k < n_units; ++k) {
+        asm volatile("" : "+v"(ml));
+        const bool head = k >= nlu;
+        if (!head || k == nlu) bar();  // input ready
+        float* dst = sbuf + (head ? (w * NHU + (k - nlu)) * kSlots : w * kSlots);
+        const int lg = unit_lg(k);
+        int kk = k + 2, st = step;
+        if (kk >= n_units) {
+          kk -= n_units;
+          ++st;
+        }
+        if (g & 1) {
+          consume_unit<1, WT>(rg, lg, xin, dst, ml);
+          if (!head) bar();  // partials ready
+          if (st < p.nsteps) issue(std::integral_constant<int, 1>{}, kk);
+        } else {
+          consume_unit<0, WT>(rg, lg, xin, dst, ml);
+          if (!head) bar();  // partials ready
+          if (st < p.nsteps) issue(std::integral_constant<int, 0>{}, kk);
+        }
+        if (head && k == n_units - 1) bar();  // LM-head partials ready
+        ++g;
+      }
+    }
+    return;
+  }
 
-    for (int l = 0; l < L; ++l) {
-      int tid = tid0, lane = lane0, wave = wave0, a0 = a0_, a1 = a1_, c0 = c0_, c1 = c1_, z0 = z0_, z1 = z1_,
-          e0 = e0_, e1 = e1_;
-      asm volatile("" : "+v"(tid), "+v"(lane));
-      asm volatile("" : "+s"(wave), "+s"(a0), "+s"(a1), "+s"(c0), "+s"(c1), "+s"(z0), "+s"(z1));
-      asm volatile("" : "+s"(e0), "+s"(e1));
-      const int et = tid - kExBase;  // exchange thread index (meaningful when ex)
-      const int ew = wave - kMemWaves;
-      const int ku = l * per_layer;  // this layer's first unit
+  // ================================================================== exchange waves
+  // Per-thread indices and the parameter block are made opaque at the top of
+  // every layer: keeps address arithmetic from being hoisted out of the loops
+  // and pinned in registers for the whole launch.
+  int et = tid - kExBase;
+  int ln = lane;
+  const int ew = wave - kMemWaves;
+  int exgen = 0;
+  // the kernel's only argument sits at the start of the kernel-argument segment;
+  // reading it through a constant-address-space pointer keeps the loads scalar
+  typedef const __attribute__((address_space(4))) DecParams* ParamPtr;
+  ParamPtr pp = (ParamPtr)__builtin_amdgcn_kernarg_segment_ptr();
+  constexpr int half = D / 2;
+  // gains (loaded one use ahead): in-norm (or final) and post-norm of this
+  // thread's residual elements, and Q/K-norm gains of this wave's head vectors
+  float gi[NE], gp[NE], gq[2][2];
+  auto load_in = [&](int l) __attribute__((always_inline)) {
+    const float* g = l < L ? pp->nbuf + (size_t)l * pp->norm_elems : pp->final_norm;
+#pragma unroll
+    for (int k = 0; k < NE; ++k) gi[k] = g[min(et + k * kEx, H - 1)];
+  };
+  auto load_post = [&](int l) __attribute__((always_inline)) {
+    const float* g = pp->nbuf + (size_t)l * pp->norm_elems + H;
+#pragma unroll
+    for (int k = 0; k < NE; ++k) gp[k] = g[min(et + k * kEx, H - 1)];
+  };
+  // this wave's head vectors hv = ew, ew + 4 of the (G + 2) in Lq: q heads, k, v
+  auto load_qk = [&](int l) __attribute__((always_inline)) {
+    const float* g = pp->nbuf + (size_t)l * pp->norm_elems + 2 * H;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int hv = ew + kExWaves * i;
+      const float* gg = hv < G ? g : g + D;  // q_norm, else k_norm
+      const int hl = ln < half ? ln : 0;
+      gq[i][0] = gg[hl];
+      gq[i][1] = gg[hl + half];
+    }
+  };
+  float x[NE];  // residual stream: elements et + k * kEx
+  const float inv_h = 1.f / (float)H;
+  // GEMV input x * g and this wave's sum of squares of x
+  auto norm_input = [&](const float (&g)[NE]) __attribute__((always_inline)) {
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < NE; ++k) {
+      const int e = et + k * kEx;
+      if (e < H) {
+        ss = fmaf(x[k], x[k], ss);
+        xin[e] = x[k] * g[k];
+      }
+    }
+    ss = wave_sum(ss);
+    if (ln == 0) ctl.red[ew] = ss;
+  };
+  auto norm_scale = [&]() __attribute__((always_inline)) {
+    const float ss = 0.f + ctl.red[0] + ctl.red[1] + ctl.red[2] + ctl.red[3];
+    return 1.f / sqrtf(ss * inv_h + pp->eps);
+  };
+  // zero the GEMV input from n to the end of its last 64-lane chunk row
+  auto pad = [&](int n) __attribute__((always_inline)) {
+    const int end = (kWave * VN) << chunk_lg(n, VN);
+    for (int i = n + et; i < end; i += kEx) xin[i] = 0.f;
+  };
+  // combined dot of local row j of a layer unit with 2^lg chunk rows per row
+  auto row_val = [&](int j, int lg) __attribute__((always_inline)) {
+    const int w = j & (kMemWaves - 1), i = j >> 2;
+    const float* s = sbuf + w * kSlots + (i << lg);
+    float v = s[0];
+    for (int jj = 1; jj < (1 << lg); ++jj) v += s[jj];
+    return v;
+  };
+
+  load_in(0);
+  load_post(0);
+  load_qk(0);
+  int token = pp->token_dev ? pp->token_dev[0] : pp->token;
+  token = token < 0 ? 0 : (token >= pp->V ? pp->V - 1 : token);
+  bar();  // start
+
+  for (int step = 0; step < pp->nsteps; ++step) {
+    const int pos = pp->pos0 + step;
+    const int n_hist = pos;  // cached positions 0 .. pos-1
+    float rc = 1.f, rs = 0.f;
+    if (ln < half) {
+      rc = pp->rope_cos[(size_t)pos * half + ln];
+      rs = pp->rope_sin[(size_t)pos * half + ln];
+    }
+#pragma unroll
+    for (int k = 0; k < NE; ++k) x[k] = wload((const WT*)pp->embed, (size_t)token * H + min(et + k * kEx, H - 1));
+    TRACE(step, 0);
+    // attention mode for this step
+    const bool whole = n_hist <= pp->whole_max;
+    int nsplit = 1;
+    if (!whole) nsplit = min(pp->nsplit_max, (n_hist + pp->whole_max - 1) / pp->whole_max);
+    const bool att_rank = whole || r < nsplit;
+    int u0 = 0, n_cached = n_hist;
+    if (!whole) {
+      int su, se;
+      split(n_hist, nsplit, r, su, se);
+      u0 = su;
+      n_cached = se - su;
+    }
+
+    for (int l = 0; l <= L; ++l) {
+      QDEC_OPAQUE();
       const int gl = step * L + l;
       const int par = gl & 1, ppar = par ^ 1;
-      const unsigned tg = p.tag0 + (unsigned)((step * (L + 1) + l) * kTagSlots);
+      const unsigned tg = pp->tag0 + (unsigned)((step * (L + 1) + l) * kTagSlots);
       const unsigned tgp = tg - kTagSlots;  // layer l-1 of this step
-      u64* Lq = p.ll + p.o_q + ((size_t)par * NKV + X) * GW;
-      u64* La = p.ll + p.o_att + ((size_t)par * NKV + X) * R * G * (D + 2);
-      u64* Lo = p.ll + p.o_o + (size_t)par * NKV * H;
-      u64* Lz = p.ll + p.o_z + ((size_t)par * kGroups + X) * FS;
-      u64* Lx = p.ll + p.o_x + (size_t)par * kGroups * H;
-      const u64* Lx_prev = p.ll + p.o_x + (size_t)ppar * kGroups * H;
-      const float* nrm = p.nbuf + (size_t)l * p.norm_elems;
-      const float *g_in = nrm, *g_post = nrm + H, *g_q = nrm + 2 * H, *g_k = nrm + 2 * H + D;
-      auto to_rbuf = [&](int j, float v) __attribute__((always_inline)) {
-        if (lane == 0) rbuf[j] = v;
-      };
-
-      TRACE(step, 1 + l * 12 + 0);
       if (l > 0) {
-        if (!gather_sum<NE>(ex, Lx_prev, kGroups, H, tgp + PH_X, xres, et)) {
-          fail_launch(p.err, tid);
-          return;
-        }
+        const u64* Lx_prev = pp->ll + pp->o_x + (size_t)ppar * kGroups * H;
+        gather_sum<NE>(Lx_prev, kGroups, H, tgp + PH_X, x, et, &ctl, pp->err);
       }
-      TRACE(step, 1 + l * 12 + 1);
+      TRACE(step, 1 + l * 10 + 0);
+      if (l == L) break;
+      u64* Lq = pp->ll + pp->o_q + ((size_t)par * NKV + X) * GW;
+      u64* La = pp->ll + pp->o_att + ((size_t)par * NKV + X) * R * G * (D + 2);
+      u64* Lo = pp->ll + pp->o_o + (size_t)par * NKV * H;
+      u64* Lz = pp->ll + pp->o_z + ((size_t)par * kGroups + X) * FS;
+      u64* Lx = pp->ll + pp->o_x + (size_t)par * kGroups * H;
+
       if (has_att) {
         // ---------------- A
-        int u0 = 0, n_cached = n_hist;
-        const bool att_rank = whole || r < nsplit;
-        if (!whole) {
-          int su, se;
-          split(n_hist, nsplit, r, su, se);
-          u0 = su;
-          n_cached = se - su;
-        }
-        rms_norm(ex, xres, g_in, H, p.eps, xn, red, tid, et);
+        norm_input(gi);
+        pad(H);
+        load_in(l + 1);
         Attn<D, G> at;
-        if (mem) {
-          unit(P0{}, ku + 0, xn, to_rbuf, 200 + 4 * l);
-        } else if (att_rank) {
-          // cached K/V of the first two iterations do not depend on this token:
-          // their loads overlap the wait for the group's Q/K/V rows
-          at.prefetch(p, l, X, u0, n_cached, ew, lane);
+        // cached K/V of the first two iterations do not depend on this token:
+        // their loads overlap the wait for the group's Q/K/V rows
+        if (att_rank) at.prefetch(p, l, X, u0, n_cached, ew, ln);
+        bar();  // input ready
+        bar();  // partials ready
+        TRACE(step, 1 + l * 10 + 1);
+        {
+          const float inv = norm_scale();
+          const int lg = chunk_lg(H, VN);
+          for (int j = et; j < a1 - a0; j += kEx) put(Lq + a0 + j, inv * row_val(j, lg), tg + PH_Q);
         }
-        __syncthreads();
-        if (ex)
-          for (int i = et; i < a1 - a0; i += kEx) put(Lq + a0 + i, rbuf[i], tg + PH_Q);
-        TRACE(step, 1 + l * 12 + 2);
-
-        // ---------------- B
-        if (!gather_vec<(GW + kEx - 1) / kEx>(ex, Lq, GW, tg + PH_Q, stage, et)) {
-          fail_launch(p.err, tid);
-          return;
-        }
-        TRACE(step, 1 + l * 12 + 3);
-        if (ex) {
-          // per-head RMSNorm + RoPE: head vectors 0..G-1 are q, G is k; v copied
-          for (int hv = ew; hv <= G + 1; hv += kExWaves) {
-            const float* src = stage + hv * D;
-            if (hv == G + 1) {
-              for (int i = lane; i < D; i += kWave) v_l[i] = src[i];
-              continue;
+        // ---------------- B: this wave's head vectors from the group's Q/K/V rows
+        QDEC_OPAQUE();
+        float va[2], vb[2];
+        {
+          const u64 t0 = now();
+          u64 w[2][2];
+          const int hl = ln < half ? ln : 0;
+          while (true) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+              const int hv = min(ew + kExWaves * i, G + 1);
+              w[i][0] = get(Lq + hv * D + hl);
+              w[i][1] = get(Lq + hv * D + hl + half);
             }
-            const float* gg = hv < G ? g_q : g_k;
-            constexpr int half = D / 2;
-            float va = 0.f, vb = 0.f;
-            if (lane < half) {
-              va = src[lane];
-              vb = src[lane + half];
-            }
-            const float ss = wave_sum(va * va + vb * vb);
-            const float inv = 1.f / sqrtf(ss / (float)D + p.eps);
-            if (lane < half) {
-              va = va * inv * gg[lane];
-              vb = vb * inv * gg[lane + half];
-              const float c = p.rope_cos[(size_t)pos * half + lane], sn = p.rope_sin[(size_t)pos * half + lane];
-              const float ra = va * c - vb * sn, rb = vb * c + va * sn;
-              if (hv < G) {
-                q_l[hv * D + lane] = ra * p.scale;
-                q_l[hv * D + lane + half] = rb * p.scale;
-              } else {
-                k_l[lane] = ra;
-                k_l[lane + half] = rb;
-              }
-            }
+            const bool done = tagged(w[0][0], tg + PH_Q) && tagged(w[0][1], tg + PH_Q) &&
+                              tagged(w[1][0], tg + PH_Q) && tagged(w[1][1], tg + PH_Q);
+            if (done || give_up(t0, &ctl, pp->err)) break;
+          }
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            va[i] = val(w[i][0]);
+            vb[i] = val(w[i][1]);
           }
         }
-        __syncthreads();
-        if (ex && r == 0) {  // append K and V at pos (write-through; completion awaited before phase C ends)
-          float* page = reinterpret_cast<float*>(p.page_table[pos / kPage]);
+        TRACE(step, 1 + l * 10 + 2);
+        // per-head RMSNorm + RoPE (q heads, k); v copied; rank 0 appends K and V at pos
+        {
+          float* page = reinterpret_cast<float*>(pp->page_table[pos / kPage]);
           Dims dd{L, 0, 0, NKV, D, 0, 0, 0.f};
-          for (int i = et; i < 2 * D; i += kEx) {
-            const int sel = i / D, d = i % D;
-            __hip_atomic_store(page + page_offset(dd, l, sel, X, pos % kPage) + d, sel ? v_l[d] : k_l[d],
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-        }
-        at.run(ex && att_rank, p, l, X, u0, n_cached, whole || r == nsplit - 1, q_l, k_l, v_l, wscr, ares, ew,
-               lane, et);
-        TRACE(step, 1 + l * 12 + 4);
-        // ---------------- C
-        if (whole) {
-          if (ex) {
-            for (int idx = et; idx < QD; idx += kEx) {
-              const int h = idx / D, d = idx % D;
-              xn[idx] = ares[h * (D + 2) + 2 + d] / ares[h * (D + 2) + 1];
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const int hv = ew + kExWaves * i;
+            if (hv > G + 1) continue;  // wave-uniform
+            float a = ln < half ? va[i] : 0.f, c = ln < half ? vb[i] : 0.f;
+            if (hv <= G) {
+              const float ssq = wave_sum(a * a + c * c);
+              const float inv = 1.f / sqrtf(ssq / (float)D + pp->eps);
+              a = a * inv * gq[i][0];
+              c = c * inv * gq[i][1];
+              const float ra = a * rc - c * rs, rb = c * rc + a * rs;
+              a = ra;
+              c = rb;
             }
-            if (r == 0) __builtin_amdgcn_s_waitcnt(0x0F70);  // KV append stores complete
-          }
-          __syncthreads();
-        } else {
-          if (ex && r < nsplit) {
-            for (int idx = et; idx < G * (D + 2); idx += kEx)
-              put(La + (size_t)r * G * (D + 2) + idx, ares[idx], tg + PH_ATT);
-          }
-          if (ex && r == 0) __builtin_amdgcn_s_waitcnt(0x0F70);  // KV append stores complete
-          if (!gather_any(ex, La, nsplit * G * (D + 2), tg + PH_ATT, stage, et)) {
-            fail_launch(p.err, tid);
-            return;
-          }
-          if (ex) {
-            for (int idx = et; idx < QD; idx += kEx) {
-              const int h = idx / D, d = idx % D;
-              float M = -INFINITY;
-              for (int s = 0; s < nsplit; ++s) M = fmaxf(M, stage[(s * G + h) * (D + 2)]);
-              float o = 0.f, lt = 0.f;
-              for (int s = 0; s < nsplit; ++s) {
-                const float* ps = stage + (s * G + h) * (D + 2);
-                const float f = (ps[0] == -INFINITY) ? 0.f : expf(ps[0] - M);
-                o = fmaf(f, ps[2 + d], o);
-                lt = fmaf(f, ps[1], lt);
+            if (ln < half) {
+              if (hv < G) {
+                q_l[hv * D + ln] = a * pp->scale;
+                q_l[hv * D + ln + half] = c * pp->scale;
+              } else {
+                float* dstv = hv == G ? k_l : v_l;
+                dstv[ln] = a;
+                dstv[ln + half] = c;
+                if (r == 0) {  // write-through; completion awaited before the partials are merged
+                  float* kvp = page + page_offset(dd, l, hv == G ? 0 : 1, X, pos % kPage);
+                  __hip_atomic_store(kvp + ln, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                  __hip_atomic_store(kvp + ln + half, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
               }
-              xn[idx] = o / lt;
             }
           }
-          __syncthreads();
         }
-        TRACE(step, 1 + l * 12 + 5);
-        if (mem) unit(P1{}, ku + 1, xn, to_rbuf);
-        __syncthreads();
-        if (ex)
-          for (int i = et; i < c1 - c0; i += kEx) put(Lo + (size_t)X * H + c0 + i, rbuf[i], tg + PH_O);
+        if (l + 1 < L) load_qk(l + 1);
+        ex_sync(exgen, ln, &ctl, pp->err);
+        if (att_rank)
+          at.partial(p, l, X, u0, n_cached, whole || r == nsplit - 1, q_l, k_l, v_l, wm, wl, wo, ew, ln);
+        if (r == 0) __builtin_amdgcn_s_waitcnt(0x0F70);  // KV append stores complete
+        ex_sync(exgen, ln, &ctl, pp->err);
+        TRACE(step, 1 + l * 10 + 3);
+        // ---------------- C input: o of the G heads, merged over waves (and splits)
+        QDEC_OPAQUE();
+        if (whole) {
+          for (int idx = et; idx < QD; idx += kEx) {
+            const int h = idx / D, d = idx % D;
+            float M = -INFINITY;
+#pragma unroll
+            for (int w2 = 0; w2 < kExWaves; ++w2) M = fmaxf(M, wm[w2 * G + h]);
+            float lt = 0.f, o = 0.f;
+#pragma unroll
+            for (int w2 = 0; w2 < kExWaves; ++w2) {
+              const float mw = wm[w2 * G + h];
+              const float f = (mw == -INFINITY) ? 0.f : expf(mw - M);
+              lt = fmaf(f, wl[w2 * G + h], lt);
+              o = fmaf(f, wo[(w2 * G + h) * D + d], o);
+            }
+            xin[idx] = o / lt;
+          }
+        } else {
+          if (r < nsplit) {
+            for (int idx = et; idx < G * (D + 2); idx += kEx) {
+              const int h = idx / (D + 2), e = idx % (D + 2);
+              float M = -INFINITY;
+#pragma unroll
+              for (int w2 = 0; w2 < kExWaves; ++w2) M = fmaxf(M, wm[w2 * G + h]);
+              float v = M;
+              if (e > 0) {
+                v = 0.f;
+#pragma unroll
+                for (int w2 = 0; w2 < kExWaves; ++w2) {
+                  const float mw = wm[w2 * G + h];
+                  const float f = (mw == -INFINITY) ? 0.f : expf(mw - M);
+                  v = fmaf(f, e == 1 ? wl[w2 * G + h] : wo[(w2 * G + h) * D + (e - 2)], v);
+                }
+              }
+              put(La + (size_t)r * G * (D + 2) + idx, v, tg + PH_ATT);
+            }
+          }
+          gather_any(La, nsplit * G * (D + 2), tg + PH_ATT, stage, et, &ctl, pp->err);
+          ex_sync(exgen, ln, &ctl, pp->err);
+          for (int idx = et; idx < QD; idx += kEx) {
+            const int h = idx / D, d = idx % D;
+            float M = -INFINITY;
+            for (int s = 0; s < nsplit; ++s) M = fmaxf(M, stage[(s * G + h) * (D + 2)]);
+            float o = 0.f, lt = 0.f;
+            for (int s = 0; s < nsplit; ++s) {
+              const float* ps = stage + (s * G + h) * (D + 2);
+              const float f = (ps[0] == -INFINITY) ? 0.f : expf(ps[0] - M);
+              o = fmaf(f, ps[2 + d], o);
+              lt = fmaf(f, ps[1], lt);
+            }
+            xin[idx] = o / lt;
+          }
+        }
+        pad(QD);
+        TRACE(step, 1 + l * 10 + 4);
+        bar();  // input ready
+        bar();  // partials ready
+        {
+          const int lg = chunk_lg(QD, VN);
+          for (int j = et; j < c1 - c0; j += kEx) put(Lo + (size_t)X * H + c0 + j, row_val(j, lg), tg + PH_O);
+        }
+      } else {
+        load_in(l + 1);
       }
 
       // ---------------- D
-      TRACE(step, 1 + l * 12 + 6);
-      if (!gather_sum<NE>(ex, Lo, NKV, H, tg + PH_O, xres, et)) {
-        fail_launch(p.err, tid);
-        return;
-      }
-      TRACE(step, 1 + l * 12 + 7);
-      rms_norm(ex, xres, g_post, H, p.eps, xn, red, tid, et);
-      if (mem) unit(P0{}, ku + per_layer - 2, xn, to_rbuf);
-      __syncthreads();
-      if (ex) {
+      QDEC_OPAQUE();
+      TRACE(step, 1 + l * 10 + 5);
+      gather_sum<NE>(Lo, NKV, H, tg + PH_O, x, et, &ctl, pp->err);
+      TRACE(step, 1 + l * 10 + 6);
+      norm_input(gp);
+      pad(H);
+      if (l + 1 < L) load_post(l + 1);
+      bar();  // input ready
+      bar();  // partials ready
+      {
+        const float inv = norm_scale();
+        const int lg = chunk_lg(H, VN);
         for (int i = et; i < z1 - z0; i += kEx) {
-          const float gt = rbuf[2 * i], up = rbuf[2 * i + 1];
+          const float gt = inv * row_val(2 * i, lg), up = inv * row_val(2 * i + 1, lg);
           put(Lz + z0 + i, gt / (1.f + expf(-gt)) * up, tg + PH_Z);
         }
       }
-      TRACE(step, 1 + l * 12 + 8);
+      TRACE(step, 1 + l * 10 + 7);
 
       // ---------------- E
-      if (!gather_any(ex, Lz, FS, tg + PH_Z, xn, et)) {
-        fail_launch(p.err, tid);
-        return;
+      QDEC_OPAQUE();
+      gather_any(Lz, FS, tg + PH_Z, xin, et, &ctl, pp->err);
+      pad(FS);
+      TRACE(step, 1 + l * 10 + 8);
+      bar();  // input ready
+      bar();  // partials ready
+      {
+        const int lg = chunk_lg(FS, VN);
+        for (int j = et; j < e1 - e0; j += kEx) put(Lx + (size_t)X * H + e0 + j, row_val(j, lg), tg + PH_X);
       }
-      TRACE(step, 1 + l * 12 + 9);
-      if (mem) unit(P1{}, ku + per_layer - 1, xn, to_rbuf);
-      __syncthreads();
-      if (ex)
-        for (int i = et; i < e1 - e0; i += kEx) put(Lx + (size_t)X * H + e0 + i, rbuf[i], tg + PH_X);
-      TRACE(step, 1 + l * 12 + 10);
+      TRACE(step, 1 + l * 10 + 9);
     }
 
     // ---------------- final RMSNorm + tied LM head + greedy argmax
+    QDEC_OPAQUE();
+    norm_input(gi);
+    pad(H);
+    load_in(0);
+    load_post(0);
+    load_qk(0);
+    bar();  // input ready
+    bar();  // LM-head partials ready
+    TRACE(step, 300);
+    u64 best = 0ull;
     {
-      int tid = tid0, lane = lane0, wave = wave0, h0 = h0_, h1 = h1_;
-      asm volatile("" : "+v"(tid), "+v"(lane));
-      asm volatile("" : "+s"(wave), "+s"(h0), "+s"(h1));
-      const int et = tid - kExBase;
-      const int gl_last = step * L + L - 1;
-      const unsigned tgl = p.tag0 + (unsigned)((step * (L + 1) + L - 1) * kTagSlots);
-      const u64* Lx_last = p.ll + p.o_x + (size_t)(gl_last & 1) * kGroups * H;
-      if (!gather_sum<NE>(ex, Lx_last, kGroups, H, tgl + PH_X, xres, et)) {
-        fail_launch(p.err, tid);
-        return;
+      const float inv = norm_scale();
+      float* lg_out = pp->logits ? pp->logits + (size_t)step * pp->V + h0 : nullptr;
+      for (int j = et; j < h1 - h0; j += kEx) {
+        const int w = j & (kMemWaves - 1), i = j >> 2;
+        const int u = i / rpbH, ii = i - u * rpbH;
+        const float* s = sbuf + (w * NHU + u) * kSlots + (ii << lgH);
+        float v = s[0];
+        for (int jj = 1; jj < (1 << lgH); ++jj) v += s[jj];
+        v *= inv;
+        if (lg_out) lg_out[j] = v;
+        best = umax64(best, argmax_key(v, h0 + j));
       }
-      TRACE(step, 400);
-      rms_norm(ex, xres, p.final_norm, H, p.eps, xn, red, tid, et);
-      u64* bk = reinterpret_cast<u64*>(red);
-      if (mem) {
-        u64 best = 0ull;
-        auto logit = [&](int j, float v) __attribute__((always_inline)) {
-          if (lane == 0) lgb[j] = v;
-          const u64 key = argmax_key(v, h0 + j);
-          best = key > best ? key : best;
-        };
-        // head units start at an even index: regions alternate 0, 1, 0, ...
-        for (int k = n_layer_units; k < n_units; k += 2) {
-          const int hu = k - n_layer_units;
-          unit(P0{}, k, xn, logit, hu < 16 ? 320 + 4 * hu : -1);
-          if (k + 1 < n_units) unit(P1{}, k + 1, xn, logit, hu + 1 < 16 ? 320 + 4 * (hu + 1) : -1);
+    }
+    best = wave_max64(best);
+    if (ln == 0) ctl.best[0][ew] = best;
+    ex_sync(exgen, ln, &ctl, pp->err);
+    const int kpar = step & 1;
+    u64* Lk = pp->ll + pp->o_key + (size_t)kpar * 2 * nb;
+    const unsigned ktag = pp->tag0 + (unsigned)((step * (L + 1) + L) * kTagSlots) + PH_KEY;
+    if (et == 0) {
+      u64 b2 = ctl.best[0][0];
+      for (int i = 1; i < kExWaves; ++i) b2 = umax64(b2, ctl.best[0][i]);
+      put(Lk + 2 * b, __uint_as_float((unsigned)(b2 >> 32)), ktag);
+      put(Lk + 2 * b + 1, __uint_as_float((unsigned)b2), ktag);
+    }
+    TRACE(step, 301);
+    const bool need = (step + 1 < pp->nsteps) || b == 0;
+    if (need) {
+      // thread et < nb reads workgroup et's key
+      u64 kb;
+      {
+        const int i = min(et, nb - 1);
+        const u64 t0 = now();
+        u64 w0, w1;
+        while (true) {
+          w0 = get(Lk + 2 * i);
+          w1 = get(Lk + 2 * i + 1);
+          if ((tagged(w0, ktag) && tagged(w1, ktag)) || give_up(t0, &ctl, pp->err)) break;
         }
-        if (lane == 0) bk[wave] = best;
+        kb = ((u64)(unsigned)w0 << 32) | (u64)(unsigned)w1;
       }
-      __syncthreads();
-      TRACE(step, 401);
-      const int kpar = step & 1;
-      u64* Lk = p.ll + p.o_key + (size_t)kpar * 2 * nb;
-      const unsigned ktag = p.tag0 + (unsigned)((step * (L + 1) + L) * kTagSlots) + PH_KEY;
-      if (ex) {
-        if (p.logits) {
-          float* lg = p.logits + (size_t)step * p.V;
-          for (int j = et; j < h1 - h0; j += kEx) lg[h0 + j] = lgb[j];
-        }
-        if (et == 0) {
-          u64 b2 = bk[0];
-          for (int i = 1; i < kMemWaves; ++i) b2 = bk[i] > b2 ? bk[i] : b2;
-          put(Lk + 2 * b, __uint_as_float((unsigned)(b2 >> 32)), ktag);
-          put(Lk + 2 * b + 1, __uint_as_float((unsigned)b2), ktag);
-        }
-      }
-      const bool need = (step + 1 < p.nsteps) || b == 0;
-      if (need) {
-        float* kw = stage;
-        if (!gather_any(ex, Lk, 2 * nb, ktag, kw, et)) {
-          fail_launch(p.err, tid);
-          return;
-        }
-        TRACE(step, 402);
-        u64 b3 = 0ull;
-        for (int i = 0; i < nb; ++i) {
-          const u64 k = ((u64)__float_as_uint(kw[2 * i]) << 32) | (u64)__float_as_uint(kw[2 * i + 1]);
-          b3 = k > b3 ? k : b3;
-        }
-        token = (int)(0xFFFFFFFFu - (uint32_t)(b3 & 0xFFFFFFFFull));
-        if (b == 0 && et == 0) p.tokens_out[step] = token;
-        __syncthreads();
-      }
+      kb = wave_max64(kb);
+      if (ln == 0) ctl.best[1][ew] = kb;
+      ex_sync(exgen, ln, &ctl, pp->err);
+      u64 b3 = ctl.best[1][0];
+      for (int i = 1; i < kExWaves; ++i) b3 = umax64(b3, ctl.best[1][i]);
+      token = (int)(0xFFFFFFFFu - (uint32_t)(b3 & 0xFFFFFFFFull));
+      token = token < 0 ? 0 : (token >= pp->V ? pp->V - 1 : token);
+      if (b == 0 && et == 0) pp->tokens_out[step] = token;
+      TRACE(step, 302);
     }
   }
 }
 
-// Dynamic LDS layout (floats): x[H] | xn[max(H, QD, FS)] | stage | att | red[64] | rbuf[64] | lgb
+// Dynamic LDS layout (floats): stage | att | sbuf
 struct Layout {
-  int x, xn, stage, att, red, rbuf, lgb, ring, total;
+  int stage, att, sbuf, total, nhu;
 };
-Layout layout(const Dims& d, int R, int nsplit_max, int nb) {
+Layout layout(bool bf16, const Dims& d, int nsplit_max, int nb) {
   const int G = d.NQ / d.NKV;
-  const int QD = G * d.D, GW = (G + 2) * d.D;
-  const int xn = 0;  // the GEMV input vector is a static LDS array of the kernel
-  int stage = std::max(GW, nsplit_max * G * (d.D + 2));
-  stage = std::max(stage, 2 * nb);  // argmax keys
-  const int att = QD + 2 * d.D + G * (d.D + 2) + 2 * kExWaves * G + kExWaves * G * d.D;
-  (void)R;
+  const int QD = G * d.D;
+  const int VN = bf16 ? 8 : 4;
+  const int stage = std::max(8, nsplit_max * G * (d.D + 2));
+  const int att = QD + 2 * d.D + 2 * kExWaves * G + kExWaves * G * d.D;
+  const int hrows = (d.V + nb - 1) / nb;
+  const int rows_w = (hrows + kMemWaves - 1) / kMemWaves;
+  const int rpb = kSlots >> chunk_lg(d.H, VN);
   Layout o;
-  o.x = 0;
-  o.xn = o.x + d.H;
-  o.stage = o.xn + xn;
-  o.att = o.stage + stage;
-  o.red = o.att + att;
-  o.rbuf = o.red + 64;
-  o.lgb = o.rbuf + 64;
-  o.ring = 0;  // the rings are static LDS arrays of the kernel
-  o.total = o.lgb + (d.V + nb - 1) / nb;
+  o.nhu = std::max(1, (rows_w + rpb - 1) / rpb);
+  o.stage = 0;
+  o.att = o.stage + ((stage + 3) & ~3);
+  o.sbuf = o.att + ((att + 3) & ~3);
+  o.total = o.sbuf + kMemWaves * o.nhu * kSlots;
   return o;
 }
 
@@ -1116,8 +1235,8 @@ const void* kernel_for(bool bf16, const Dims& d) {
 
 }  // namespace
 
-size_t dec_lds_bytes(const Dims& d, int R, int nsplit_max) {
-  return (size_t)layout(d, R, nsplit_max, R * kGroups).total * sizeof(float);
+size_t dec_lds_bytes(bool bf16, const Dims& d, int nblocks, int nsplit_max) {
+  return (size_t)layout(bf16, d, nsplit_max, nblocks).total * sizeof(float);
 }
 
 size_t dec_words(const Dims& d, int nb, int nsplit_max, DecOffsets* off) {
@@ -1137,23 +1256,23 @@ size_t dec_words(const Dims& d, int nb, int nsplit_max, DecOffsets* off) {
 
 unsigned dec_tags_per_step(const Dims& d) { return (unsigned)((d.L + 1) * kTagSlots); }
 
-// Every layer phase of a workgroup must fit one ring region per memory wave:
-// (rows per wave) * (chunks per lane per row) <= kSlots.
+// Every GEMV input fits the LDS input vector and every layer phase of a
+// workgroup fits one ring region per memory wave: (rows per wave) * (chunk
+// rows per row) <= kSlots; at most one argmax key per exchange thread.
 bool dec_fits(bool bf16, const Dims& d, int nblocks) {
+  if (nblocks < kGroups || nblocks % kGroups || nblocks > kMaxBlocks) return false;
   const int R = nblocks / kGroups;
   const int VN = bf16 ? 8 : 4;
   const int G = d.NQ / d.NKV;
-  auto slots = [&](int rows_per_block, int K) {
-    const int nch = K / VN;
-    const int cpl = (nch + kWave - 1) / kWave;
-    if (cpl > 8) return 1 << 20;
-    const int cplp = cpl <= 1 ? 1 : cpl <= 2 ? 2 : cpl <= 4 ? 4 : 8;
-    return (rows_per_block + kMemWaves - 1) / kMemWaves * cplp;
+  const int FS = d.F / kGroups;
+  auto fits = [&](int rows_per_block, int K) {
+    if (K > kMaxK || K % VN) return false;
+    const int rows_w = (rows_per_block + kMemWaves - 1) / kMemWaves;
+    return (rows_w << chunk_lg(K, VN)) <= kSlots;
   };
   auto per = [&](int n) { return (n + R - 1) / R; };
-  const int FS = d.F / kGroups;
-  return slots(per((G + 2) * d.D), d.H) <= kSlots && slots(per(d.H), G * d.D) <= kSlots &&
-         slots(2 * per(FS), d.H) <= kSlots && slots(per(d.H), FS) <= kSlots && slots(1, d.H) <= kSlots;
+  return fits(per((G + 2) * d.D), d.H) && fits(per(d.H), G * d.D) && fits(2 * per(FS), d.H) &&
+         fits(per(d.H), FS) && fits(1, d.H);
 }
 
 int dec_split_limit(const Dims& d, int nblocks) {
@@ -1201,9 +1320,9 @@ hipError_t launch_decode(const DecLaunch& a, hipStream_t st) {
   p.R = a.nblocks / kGroups;
   p.nsplit_max = a.nsplit_max;
   p.whole_max = a.whole_max;
-  const Layout lay = layout(d, p.R, a.nsplit_max, a.nblocks);
-  p.lds_x = lay.x; p.lds_xn = lay.xn; p.lds_stage = lay.stage; p.lds_att = lay.att; p.lds_red = lay.red;
-  p.lds_rbuf = lay.rbuf; p.lds_lgb = lay.lgb; p.lds_ring = lay.ring;
+  const Layout lay = layout(a.bf16, d, a.nsplit_max, a.nblocks);
+  p.nhu = lay.nhu;
+  p.lds_stage = lay.stage; p.lds_att = lay.att; p.lds_sbuf = lay.sbuf;
   const void* fn = kernel_for(a.bf16, d);
   if (!fn) return hipErrorInvalidValue;
   void* args[] = {&p};

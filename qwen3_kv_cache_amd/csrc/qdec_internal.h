@@ -102,7 +102,7 @@ struct DecLaunch {
   int nsplit_max, whole_max;
   int* err;                         // device address of a host-visible int
 };
-size_t dec_lds_bytes(const Dims& d, int R, int nsplit_max);
+size_t dec_lds_bytes(bool bf16, const Dims& d, int nblocks, int nsplit_max);
 size_t dec_words(const Dims& d, int nblocks, int nsplit_max, DecOffsets* off);
 unsigned dec_tags_per_step(const Dims& d);
 int dec_split_limit(const Dims& d, int nblocks);

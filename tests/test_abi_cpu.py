@@ -53,8 +53,8 @@ BAD = [
     dict(tied=0), dict(hidden=100), dict(hidden=0), dict(head_dim=48), dict(head_dim=256), dict(n_kv_head=3),
     dict(n_q_head=32, n_kv_head=2), dict(ffn=100), dict(vocab=1), dict(n_layer=0),
     dict(rms_eps=0.0), dict(rope_theta=0.5),
-    # limits of the decode kernel: hidden <= 1024, n_kv_head <= 8, GQA group <= 4, ffn % 64 == 0
-    dict(hidden=2048), dict(n_q_head=16, n_kv_head=16), dict(n_q_head=16, n_kv_head=2), dict(ffn=96),
+    # limits of the decode kernel: hidden <= 1024, n_kv_head <= 8, GQA group <= 4, ffn % 64 == 0, ffn <= 8192
+    dict(hidden=2048), dict(n_q_head=16, n_kv_head=16), dict(n_q_head=16, n_kv_head=2), dict(ffn=96), dict(ffn=8256),
 ]
 
 
