@@ -86,6 +86,13 @@ enum { PH_Q = 0, PH_ATT = 1, PH_O = 2, PH_Z = 3, PH_X = 4, PH_KEY = 5 };
 constexpr int kSlots = 12;
 constexpr int kSlotBytes = kWave * 16;
 constexpr int kMaxK = 1024;  // longest GEMV input: max(hidden, G * D, ffn / 8)
+constexpr int kPtabLds = 1024;  // KV page pointers kept in LDS (positions < 16384)
+#ifndef QDEC_ISSUE_SLEEP
+#define QDEC_ISSUE_SLEEP 0  // s_sleep units between a layer unit's weight loads
+#endif
+#ifndef QDEC_POLL_SLEEP
+#define QDEC_POLL_SLEEP 0  // s_sleep units (64 clocks) between poll rounds
+#endif
 
 __device__ __forceinline__ u64 now() { return __builtin_amdgcn_s_memrealtime(); }
 
@@ -94,13 +101,23 @@ __device__ __forceinline__ u64 now() { return __builtin_amdgcn_s_memrealtime(); 
 // first step of a launch, per workgroup (taken by the first exchange thread).
 constexpr int kTraceN = 512;
 __device__ u64 g_trace[2048 * kTraceN];
-#define TRACE(step, idx)                                                                                 \
-  do {                                                                                                   \
-    if ((step) == 0 && tid == kExBase && (idx) < kTraceN) g_trace[blockIdx.x * kTraceN + (idx)] = now(); \
+__shared__ u64 g_xtr[kTraceN];
+#define TRACEB(step, l, i)                            \
+  do {                                                \
+    if ((l) >= 1 && (l) <= 3) TRACE(step, 464 + ((l) - 1) * 8 + (i)); \
+  } while (0)
+// stamps go to LDS (xtr) and are copied out at the end, so that no store
+// joins the waves' in-order memory counters
+#define TRACE(step, idx)                                                               \
+  do {                                                                                 \
+    if ((step) == 0 && tid == kExBase && (idx) < kTraceN) g_xtr[(idx)] = now(); \
   } while (0)
 #else
 #define TRACE(step, idx) \
   do {                   \
+  } while (0)
+#define TRACEB(step, l, i) \
+  do {                     \
   } while (0)
 #endif
 
@@ -120,6 +137,38 @@ __device__ __forceinline__ u64 get(const u64* p) {
   return __hip_atomic_load(const_cast<u64*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ bool tagged(u64 w, unsigned tag) { return (unsigned)(w >> 32) == tag; }
+
+// Exchanges inside one group (one XCD, whose CUs share an L2) use plain
+// stores, which reach that L2, and non-temporal loads, which read it without
+// allocating in the CU's L1: a shorter round trip than device scope. A
+// reader that ever saw a stale value would only keep polling (tags never
+// repeat), and the wait's time limit turns that into an error.
+__device__ __forceinline__ void put_l(u64* p, float v, unsigned tag) {
+  __hip_atomic_store(p, ((u64)tag << 32) | (u64)__float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// up to four non-temporal 8-byte loads, issued together and awaited together
+__device__ __forceinline__ void get_l4(const u64* a, const u64* b, const u64* c, const u64* d, u64& x, u64& y,
+                                       u64& z, u64& w) {
+  asm volatile(
+      "global_load_dwordx2 %0, %4, off nt\n\t"
+      "global_load_dwordx2 %1, %5, off nt\n\t"
+      "global_load_dwordx2 %2, %6, off nt\n\t"
+      "global_load_dwordx2 %3, %7, off nt\n\t"
+      "s_waitcnt vmcnt(0)"
+      : "=&v"(x), "=&v"(y), "=&v"(z), "=&v"(w)
+      : "v"(a), "v"(b), "v"(c), "v"(d)
+      : "memory");
+}
+
+// Global-address-space views. Pointers read back from LDS (the KV page
+// table) carry no address space, and loads through them would be FLAT
+// operations, which also count against the LDS counter: every LDS wait would
+// then wait for those global loads too.
+typedef __attribute__((address_space(1))) float gfloat;
+typedef __attribute__((address_space(1))) u64 gu64;
+__device__ __forceinline__ u64 get_g(const gu64* p) {
+  return __hip_atomic_load(const_cast<gu64*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ float val(u64 w) { return __uint_as_float((unsigned)w); }
 
 // Cross-lane steps on the VALU (DPP and the gfx950 permlane swaps) instead of
@@ -251,7 +300,7 @@ struct DecParams {
   int nsplit_max;     // attention splits per group
   int whole_max;      // cached positions up to which each rank runs the whole attention
   int nhu;            // LM-head units per memory wave (the largest over waves)
-  int lds_stage, lds_att, lds_sbuf;
+  int lds_stage, lds_att, lds_sbuf, lds_ptab;
 };
 
 // Workgroup-shared control words.
@@ -325,6 +374,7 @@ __device__ __forceinline__ void gather_sum(const u64* W, int P, int n, unsigned 
       for (int q = 0; q < kGroups; ++q)
         if (q < P) done = done && tagged(w[k][q], tag);
     if (done || give_up(t0, ctl, err)) break;
+    if (QDEC_POLL_SLEEP) __builtin_amdgcn_s_sleep(QDEC_POLL_SLEEP);
   }
 #pragma unroll
   for (int k = 0; k < NE; ++k) {
@@ -352,9 +402,31 @@ __device__ __forceinline__ void gather_vec(const u64* W, int n, unsigned tag, fl
 #pragma unroll
     for (int j = 0; j < J; ++j) done = done && tagged(w[j], tag);
     if (done || give_up(t0, ctl, err)) break;
+    if (QDEC_POLL_SLEEP) __builtin_amdgcn_s_sleep(QDEC_POLL_SLEEP);
   }
 #pragma unroll
   for (int j = 0; j < J; ++j)
+    if (et + j * kEx < n) dst[et + j * kEx] = val(w[j]);
+}
+
+// dst[i] = value of W[i] for i = et + j * kEx < n (n <= 4 * kEx), words of
+// this group written with put_l.
+__device__ __forceinline__ void gather_local(const u64* W, int n, unsigned tag, float* dst, int et, Ctl* ctl,
+                                             int* err) {
+  const u64 t0 = now();
+  u64 w[4];
+  const u64* a[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) a[j] = W + min(et + j * kEx, n - 1);
+  while (true) {
+    get_l4(a[0], a[1], a[2], a[3], w[0], w[1], w[2], w[3]);
+    bool done = true;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) done = done && tagged(w[j], tag);
+    if (done || give_up(t0, ctl, err)) break;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
     if (et + j * kEx < n) dst[et + j * kEx] = val(w[j]);
 }
 
@@ -462,7 +534,7 @@ struct Ring {
 // `base`, where ro(q) is lane q of `tab`.
 template <int P>
 __device__ __forceinline__ void issue_unit(Ring& rg, const char* base, int tab, int ns, int lg, int nchm1,
-                                           int lane) {
+                                           int lane, bool paced) {
   char* region = P ? rg.r1 : rg.r0;
   const int jm = (1 << lg) - 1;
 #pragma unroll
@@ -472,6 +544,7 @@ __device__ __forceinline__ void issue_unit(Ring& rg, const char* base, int tab, 
       const int c = min(lane + ((q & jm) << 6), nchm1);
       __builtin_amdgcn_global_load_lds((const void*)(base + ro + c * 16), (lds_void*)(region + q * kSlotBytes), 16,
                                        0, 0);
+      if (QDEC_ISSUE_SLEEP && paced) __builtin_amdgcn_s_sleep(QDEC_ISSUE_SLEEP);
     }
   }
   rg.issued += ns;
@@ -510,9 +583,13 @@ __device__ __forceinline__ void dot_unit(const Ring& rg, const float* xin, float
   reduce12_store(s, dst, lane);
 }
 
-template <int P, typename WT>
-__device__ __forceinline__ void consume_unit(Ring& rg, int lg, const float* xin, float* dst, int lane) {
+template <int P>
+__device__ __forceinline__ void ring_wait(const Ring& rg) {
   wait_vm(rg.issued - (P ? rg.mark1 : rg.mark0));
+}
+
+template <int P, typename WT>
+__device__ __forceinline__ void consume_unit(const Ring& rg, int lg, const float* xin, float* dst, int lane) {
   if (lg == 0) {
     dot_unit<P, 0, WT>(rg, xin, dst, lane);
   } else if (sizeof(WT) == 2 || lg == 1) {
@@ -527,27 +604,41 @@ __device__ __forceinline__ void consume_unit(Ring& rg, int lg, const float* xin,
 // K/V of cached position u for KV head g, DPL floats at dims part*DPL.. ;
 // `fresh` positions were written earlier in this launch by another CU and are
 // read with device-scope loads.
+// Device address of the KV page holding position u (page pointers of the
+// first kPtabLds pages are cached in LDS at launch start).
+__device__ __forceinline__ gfloat* page_of(const DecParams& p, const u64* ptab, int u) {
+  const int pg = u / kPage;
+  u64 a;
+  if (pg < kPtabLds)
+    a = ptab[pg];
+  else  // an atomic global load keeps the two reads from merging into one FLAT load
+    a = get_g((const gu64*)(p.page_table + pg));
+  return (gfloat*)a;
+}
+
 template <int DPL>
-__device__ __forceinline__ void load_kv(const DecParams& p, int l, int g, int u, int part, bool fresh, float* kv,
-                                        float* vv) {
-  const float* page = reinterpret_cast<const float*>(p.page_table[u / kPage]);
+__device__ __forceinline__ void load_kv(const DecParams& p, const u64* ptab, int l, int g, int u, int part, bool fresh,
+                                        float* kv, float* vv) {
+  const gfloat* page = page_of(p, ptab, u);
   Dims dd{p.L, 0, 0, p.NKV, DPL * 8, 0, 0, 0.f};
-  const float* kp = page + page_offset(dd, l, 0, g, u % kPage) + part * DPL;
-  const float* vp = page + page_offset(dd, l, 1, g, u % kPage) + part * DPL;
+  const gfloat* kp = page + page_offset(dd, l, 0, g, u % kPage) + part * DPL;
+  const gfloat* vp = page + page_offset(dd, l, 1, g, u % kPage) + part * DPL;
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(1))) const f32x4 gf32x4;
   if (!fresh) {
 #pragma unroll
     for (int i = 0; i < DPL; i += 4) {
-      const float4 a = *reinterpret_cast<const float4*>(kp + i);
+      const f32x4 a = *reinterpret_cast<gf32x4*>(kp + i);
       kv[i] = a.x; kv[i + 1] = a.y; kv[i + 2] = a.z; kv[i + 3] = a.w;
-      const float4 c = *reinterpret_cast<const float4*>(vp + i);
+      const f32x4 c = *reinterpret_cast<gf32x4*>(vp + i);
       vv[i] = c.x; vv[i + 1] = c.y; vv[i + 2] = c.z; vv[i + 3] = c.w;
     }
   } else {
 #pragma unroll
     for (int i = 0; i < DPL; i += 2) {
-      const u64 a = get(reinterpret_cast<const u64*>(kp + i));
+      const u64 a = get_g(reinterpret_cast<const gu64*>(kp + i));
       kv[i] = __uint_as_float((unsigned)a); kv[i + 1] = __uint_as_float((unsigned)(a >> 32));
-      const u64 c = get(reinterpret_cast<const u64*>(vp + i));
+      const u64 c = get_g(reinterpret_cast<const gu64*>(vp + i));
       vv[i] = __uint_as_float((unsigned)c); vv[i + 1] = __uint_as_float((unsigned)(c >> 32));
     }
   }
@@ -565,11 +656,12 @@ struct Attn {
   static constexpr int kPerIt = kExWaves * 8;  // keys per iteration
   float kv0[DPL], vv0[DPL], kv1[DPL], vv1[DPL];
 
-  __device__ __forceinline__ void prefetch(const DecParams& p, int l, int g, int u0, int n_cached, int ew, int lane) {
+  __device__ __forceinline__ void prefetch(const DecParams& p, const u64* ptab, int l, int g, int u0, int n_cached,
+                                           int ew, int lane) {
     const int slot = lane / 8, part = lane % 8;
     const int k0 = ew * 8 + slot, k1 = k0 + kPerIt;
-    if (k0 < n_cached) load_kv<DPL>(p, l, g, u0 + k0, part, u0 + k0 >= p.pos0, kv0, vv0);
-    if (k1 < n_cached) load_kv<DPL>(p, l, g, u0 + k1, part, u0 + k1 >= p.pos0, kv1, vv1);
+    if (k0 < n_cached) load_kv<DPL>(p, ptab, l, g, u0 + k0, part, u0 + k0 >= p.pos0, kv0, vv0);
+    if (k1 < n_cached) load_kv<DPL>(p, ptab, l, g, u0 + k1, part, u0 + k1 >= p.pos0, kv1, vv1);
   }
 
   __device__ __forceinline__ void step(const float* q_l, const float* k_l, const float* v_l, const float* kv,
@@ -624,9 +716,12 @@ struct Attn {
 
   // q_l: [G][D] (scaled), k_l, v_l: [D] current token; writes wm[ew*G + h],
   // wl[ew*G + h], wo[(ew*G + h)*D + d].
-  __device__ __forceinline__ void partial(const DecParams& p, int l, int g, int u0, int n_cached, bool with_cur,
+  __device__ __forceinline__ void partial(const DecParams& p, const u64* ptab, int l, int g, int u0, int n_cached,
+                                          bool with_cur,
                                           const float* q_l, const float* k_l, const float* v_l, float* wm, float* wl,
-                                          float* wo, int ew, int lane) {
+                                          float* wo, int ew, int lane, int step = 1, int tid = 0) {
+    (void)step;
+    (void)tid;
     const int slot = lane / 8, part = lane % 8;
     float m[G], ls[G], acc[G][DPL];
 #pragma unroll
@@ -639,14 +734,16 @@ struct Attn {
     const int n_keys = n_cached + (with_cur ? 1 : 0);
     for (int base = 0; base < n_keys; base += 2 * kPerIt) {
       const int ka = base + ew * 8 + slot;
-      step(q_l, k_l, v_l, kv0, vv0, ka, n_cached, n_keys, part, m, ls, acc);
+      this->step(q_l, k_l, v_l, kv0, vv0, ka, n_cached, n_keys, part, m, ls, acc);
+      if (base == 0) TRACEB(step, l, 1);
       const int kn0 = ka + 2 * kPerIt;
-      if (kn0 < n_cached) load_kv<DPL>(p, l, g, u0 + kn0, part, u0 + kn0 >= p.pos0, kv0, vv0);
+      if (kn0 < n_cached) load_kv<DPL>(p, ptab, l, g, u0 + kn0, part, u0 + kn0 >= p.pos0, kv0, vv0);
       const int kb = ka + kPerIt;
-      if (base + kPerIt < n_keys) step(q_l, k_l, v_l, kv1, vv1, kb, n_cached, n_keys, part, m, ls, acc);
+      if (base + kPerIt < n_keys) this->step(q_l, k_l, v_l, kv1, vv1, kb, n_cached, n_keys, part, m, ls, acc);
       const int kn1 = kb + 2 * kPerIt;
-      if (kn1 < n_cached) load_kv<DPL>(p, l, g, u0 + kn1, part, u0 + kn1 >= p.pos0, kv1, vv1);
+      if (kn1 < n_cached) load_kv<DPL>(p, ptab, l, g, u0 + kn1, part, u0 + kn1 >= p.pos0, kv1, vv1);
     }
+    TRACEB(step, l, 6);
     // sum the 8 key slots of the wave (same running max within the wave)
 #pragma unroll
     for (int h = 0; h < G; ++h)
@@ -657,6 +754,7 @@ struct Attn {
         v = sum32(sum16(v));
         acc[h][i] = v;
       }
+    TRACEB(step, l, 7);
     if (slot == 0) {
 #pragma unroll
       for (int h = 0; h < G; ++h)
@@ -689,6 +787,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
   float* stage = sm + p.lds_stage;  // split-attention partials of all ranks
   float* att = sm + p.lds_att;      // q_l [G][D] | k_l [D] | v_l [D] | wm | wl | wo
   float* sbuf = sm + p.lds_sbuf;    // per-slot partial dots [wave][unit][kSlots]
+  u64* ptab = reinterpret_cast<u64*>(sm + p.lds_ptab);  // KV page pointers
   float* q_l = att;
   float* k_l = q_l + QD;
   float* v_l = k_l + D;
@@ -726,6 +825,20 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
   if (mem) {
     // ================================================================ memory waves
     const int w = wave;
+#ifdef QDEC_TRACE
+    // memory wave 0's stamps of units 4..15 of the first step, kept in LDS so
+    // that no store disturbs the wave's load counting
+    constexpr int kMTrace = 72;
+    __shared__ u64 mtr[kMTrace];
+#define MTRACE(k, s)                                                                              \
+  do {                                                                                            \
+    if (step == 0 && w == 0 && ml == 0 && (k) >= 4 && (k) < 16) mtr[((k) - 4) * 6 + (s)] = now(); \
+  } while (0)
+#else
+#define MTRACE(k, s) \
+  do {               \
+  } while (0)
+#endif
     Ring rg{ring0 + w * kSlots * kSlotBytes, ring1 + w * kSlots * kSlotBytes, 0, 0, 0};
     // the four layer jobs A, C, D, E: slots issued, chunk rows per row (lg),
     // last chunk, and lane q of tab = byte offset of slot q's row from the matrix base
@@ -767,14 +880,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
         const int cm = t == 0 ? nchm1[0] : t == 1 ? nchm1[1] : t == 2 ? nchm1[2] : nchm1[3];
         const size_t toff = t == 0 ? 0 : t == 1 ? p.off_o : t == 2 ? p.off_gu : p.off_d;
         const char* base = wbase + ((size_t)l * p.layer_elems + toff) * ES;
-        issue_unit<P>(rg, base, tb, n, lg, cm, ml);
+        issue_unit<P>(rg, base, tb, n, lg, cm, ml, true);
       } else {
         const int u = k - nlu;
         const int i0 = u * rpbH;  // first local head row of the unit
         int n = nrwH - i0;
         n = n < 0 ? 0 : (n > rpbH ? rpbH : n);
         const int ro = (h0 + w + kMemWaves * (i0 + (ml >> lgH))) * rowH;
-        issue_unit<P>(rg, ebase, ro, __builtin_amdgcn_readfirstlane(n << lgH), lgH, nchH, ml);
+        issue_unit<P>(rg, ebase, ro, __builtin_amdgcn_readfirstlane(n << lgH), lgH, nchH, ml, false);
       }
     };
     auto unit_lg = [&](int k) __attribute__((always_inline)) {
@@ -791,6 +904,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
       for (int k = 0; k < n_units; ++k) {
         asm volatile("" : "+v"(ml));
         const bool head = k >= nlu;
+        MTRACE(k, 0);
         if (!head || k == nlu) bar();  // input ready
         float* dst = sbuf + (head ? (w * NHU + (k - nlu)) * kSlots : w * kSlots);
         const int lg = unit_lg(k);
@@ -799,19 +913,33 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
           kk -= n_units;
           ++st;
         }
+        MTRACE(k, 1);
         if (g & 1) {
+          ring_wait<1>(rg);
+          MTRACE(k, 2);
           consume_unit<1, WT>(rg, lg, xin, dst, ml);
+          MTRACE(k, 3);
           if (!head) bar();  // partials ready
+          MTRACE(k, 4);
           if (st < p.nsteps) issue(std::integral_constant<int, 1>{}, kk);
         } else {
+          ring_wait<0>(rg);
+          MTRACE(k, 2);
           consume_unit<0, WT>(rg, lg, xin, dst, ml);
+          MTRACE(k, 3);
           if (!head) bar();  // partials ready
+          MTRACE(k, 4);
           if (st < p.nsteps) issue(std::integral_constant<int, 0>{}, kk);
         }
+        MTRACE(k, 5);
         if (head && k == n_units - 1) bar();  // LM-head partials ready
         ++g;
       }
     }
+#ifdef QDEC_TRACE
+    if (w == 0 && ml == 0)
+      for (int i = 0; i < kMTrace; ++i) g_trace[blockIdx.x * kTraceN + 320 + i] = mtr[i];
+#endif
     return;
   }
 
@@ -890,6 +1018,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
   load_in(0);
   load_post(0);
   load_qk(0);
+  {
+    const int np = min((pp->pos0 + pp->nsteps + kPage - 1) / kPage, kPtabLds);
+    for (int i = et; i < np; i += kEx) ptab[i] = (u64)pp->page_table[i];
+  }
   int token = pp->token_dev ? pp->token_dev[0] : pp->token;
   token = token < 0 ? 0 : (token >= pp->V ? pp->V - 1 : token);
   bar();  // start
@@ -917,6 +1049,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
       u0 = su;
       n_cached = se - su;
     }
+    // cached K/V of a layer's first two attention iterations do not depend on
+    // the token: they are loaded one phase ahead, under an exchange wait
+    Attn<D, G> at;
+    if (has_att && att_rank) at.prefetch(p, ptab, 0, X, u0, n_cached, ew, ln);
 
     for (int l = 0; l <= L; ++l) {
       QDEC_OPAQUE();
@@ -940,19 +1076,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
         // ---------------- A
         norm_input(gi);
         pad(H);
-        load_in(l + 1);
-        Attn<D, G> at;
-        // cached K/V of the first two iterations do not depend on this token:
-        // their loads overlap the wait for the group's Q/K/V rows
-        if (att_rank) at.prefetch(p, l, X, u0, n_cached, ew, ln);
+        if (l < 16) TRACE(step, 400 + l * 4 + 0);
         bar();  // input ready
         bar();  // partials ready
         TRACE(step, 1 + l * 10 + 1);
         {
           const float inv = norm_scale();
           const int lg = chunk_lg(H, VN);
-          for (int j = et; j < a1 - a0; j += kEx) put(Lq + a0 + j, inv * row_val(j, lg), tg + PH_Q);
+          for (int j = et; j < a1 - a0; j += kEx) put_l(Lq + a0 + j, inv * row_val(j, lg), tg + PH_Q);
         }
+        TRACEB(step, l, 0);
         // ---------------- B: this wave's head vectors from the group's Q/K/V rows
         QDEC_OPAQUE();
         float va[2], vb[2];
@@ -960,13 +1093,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
           const u64 t0 = now();
           u64 w[2][2];
           const int hl = ln < half ? ln : 0;
+          const int hv0 = min(ew, G + 1), hv1 = min(ew + kExWaves, G + 1);
           while (true) {
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-              const int hv = min(ew + kExWaves * i, G + 1);
-              w[i][0] = get(Lq + hv * D + hl);
-              w[i][1] = get(Lq + hv * D + hl + half);
-            }
+            get_l4(Lq + hv0 * D + hl, Lq + hv0 * D + hl + half, Lq + hv1 * D + hl, Lq + hv1 * D + hl + half,
+                   w[0][0], w[0][1], w[1][0], w[1][1]);
             const bool done = tagged(w[0][0], tg + PH_Q) && tagged(w[0][1], tg + PH_Q) &&
                               tagged(w[1][0], tg + PH_Q) && tagged(w[1][1], tg + PH_Q);
             if (done || give_up(t0, &ctl, pp->err)) break;
@@ -980,7 +1110,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
         TRACE(step, 1 + l * 10 + 2);
         // per-head RMSNorm + RoPE (q heads, k); v copied; rank 0 appends K and V at pos
         {
-          float* page = reinterpret_cast<float*>(pp->page_table[pos / kPage]);
+          gfloat* page = page_of(p, ptab, pos);
           Dims dd{L, 0, 0, NKV, D, 0, 0, 0.f};
 #pragma unroll
           for (int i = 0; i < 2; ++i) {
@@ -1005,7 +1135,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
                 dstv[ln] = a;
                 dstv[ln + half] = c;
                 if (r == 0) {  // write-through; completion awaited before the partials are merged
-                  float* kvp = page + page_offset(dd, l, hv == G ? 0 : 1, X, pos % kPage);
+                  gfloat* kvp = page + page_offset(dd, l, hv == G ? 0 : 1, X, pos % kPage);
                   __hip_atomic_store(kvp + ln, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                   __hip_atomic_store(kvp + ln + half, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
@@ -1013,12 +1143,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
             }
           }
         }
-        if (l + 1 < L) load_qk(l + 1);
+        TRACEB(step, l, 2);
         ex_sync(exgen, ln, &ctl, pp->err);
+        TRACEB(step, l, 3);
         if (att_rank)
-          at.partial(p, l, X, u0, n_cached, whole || r == nsplit - 1, q_l, k_l, v_l, wm, wl, wo, ew, ln);
-        if (r == 0) __builtin_amdgcn_s_waitcnt(0x0F70);  // KV append stores complete
+          at.partial(p, ptab, l, X, u0, n_cached, whole || r == nsplit - 1, q_l, k_l, v_l, wm, wl, wo, ew, ln, step,
+                     tid);
+        TRACEB(step, l, 4);
         ex_sync(exgen, ln, &ctl, pp->err);
+        TRACEB(step, l, 5);
         TRACE(step, 1 + l * 10 + 3);
         // ---------------- C input: o of the G heads, merged over waves (and splits)
         QDEC_OPAQUE();
@@ -1075,6 +1208,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
           }
         }
         pad(QD);
+        // next layer's gains: a wave's loads retire in order, so these are
+        // issued only now, ahead of the O-partial wait that hides them
+        load_in(l + 1);
+        if (l + 1 < L) load_qk(l + 1);
         TRACE(step, 1 + l * 10 + 4);
         bar();  // input ready
         bar();  // partials ready
@@ -1089,11 +1226,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
       // ---------------- D
       QDEC_OPAQUE();
       TRACE(step, 1 + l * 10 + 5);
+      // rank 0's K/V append stores are complete before anything else of this
+      // workgroup is published (a later step reads them from other CUs)
+      if (has_att && r == 0) __builtin_amdgcn_s_waitcnt(0x0F70);
       gather_sum<NE>(Lo, NKV, H, tg + PH_O, x, et, &ctl, pp->err);
       TRACE(step, 1 + l * 10 + 6);
       norm_input(gp);
       pad(H);
       if (l + 1 < L) load_post(l + 1);
+      if (l < 16) TRACE(step, 400 + l * 4 + 1);
       bar();  // input ready
       bar();  // partials ready
       {
@@ -1101,14 +1242,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
         const int lg = chunk_lg(H, VN);
         for (int i = et; i < z1 - z0; i += kEx) {
           const float gt = inv * row_val(2 * i, lg), up = inv * row_val(2 * i + 1, lg);
-          put(Lz + z0 + i, gt / (1.f + expf(-gt)) * up, tg + PH_Z);
+          put_l(Lz + z0 + i, gt / (1.f + expf(-gt)) * up, tg + PH_Z);
         }
       }
       TRACE(step, 1 + l * 10 + 7);
 
       // ---------------- E
       QDEC_OPAQUE();
-      gather_any(Lz, FS, tg + PH_Z, xin, et, &ctl, pp->err);
+      gather_local(Lz, FS, tg + PH_Z, xin, et, &ctl, pp->err);
       pad(FS);
       TRACE(step, 1 + l * 10 + 8);
       bar();  // input ready
@@ -1117,6 +1258,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
         const int lg = chunk_lg(FS, VN);
         for (int j = et; j < e1 - e0; j += kEx) put(Lx + (size_t)X * H + e0 + j, row_val(j, lg), tg + PH_X);
       }
+      if (has_att && att_rank && l + 1 < L) at.prefetch(p, ptab, l + 1, X, u0, n_cached, ew, ln);
       TRACE(step, 1 + l * 10 + 9);
     }
 
@@ -1184,11 +1326,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
       TRACE(step, 302);
     }
   }
+#ifdef QDEC_TRACE
+  if (tid == kExBase)
+    for (int i = 0; i < 320; ++i) g_trace[blockIdx.x * kTraceN + i] = g_xtr[i];
+  if (tid == kExBase)
+    for (int i = 392; i < kTraceN; ++i) g_trace[blockIdx.x * kTraceN + i] = g_xtr[i];
+#endif
 }
 
-// Dynamic LDS layout (floats): stage | att | sbuf
+// Dynamic LDS layout (floats): stage | att | sbuf | ptab (u64)
 struct Layout {
-  int stage, att, sbuf, total, nhu;
+  int stage, att, sbuf, ptab, total, nhu;
 };
 Layout layout(bool bf16, const Dims& d, int nsplit_max, int nb) {
   const int G = d.NQ / d.NKV;
@@ -1204,7 +1352,8 @@ Layout layout(bool bf16, const Dims& d, int nsplit_max, int nb) {
   o.stage = 0;
   o.att = o.stage + ((stage + 3) & ~3);
   o.sbuf = o.att + ((att + 3) & ~3);
-  o.total = o.sbuf + kMemWaves * o.nhu * kSlots;
+  o.ptab = o.sbuf + ((kMemWaves * o.nhu * kSlots + 3) & ~3);
+  o.total = o.ptab + 2 * kPtabLds;
   return o;
 }
 
@@ -1322,7 +1471,7 @@ hipError_t launch_decode(const DecLaunch& a, hipStream_t st) {
   p.whole_max = a.whole_max;
   const Layout lay = layout(a.bf16, d, a.nsplit_max, a.nblocks);
   p.nhu = lay.nhu;
-  p.lds_stage = lay.stage; p.lds_att = lay.att; p.lds_sbuf = lay.sbuf;
+  p.lds_stage = lay.stage; p.lds_att = lay.att; p.lds_sbuf = lay.sbuf; p.lds_ptab = lay.ptab;
   const void* fn = kernel_for(a.bf16, d);
   if (!fn) return hipErrorInvalidValue;
   void* args[] = {&p};
