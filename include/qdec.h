@@ -124,6 +124,9 @@ int qdec_state_create(qdec_model* m, int32_t max_ctx, qdec_state** out);
 void qdec_state_destroy(qdec_state* s);
 
 #define QDEC_PAGE 16
+/* Decode runs at positions below this bound (the decode kernel keeps the
+ * state's KV page table on chip); prefill is bounded by max_ctx only. */
+#define QDEC_DECODE_MAX_POS 16384
 
 /* Prefill (NCNN page section 5; transcribe.cpp LLM decoder table).
  * ids_host: HOST int32[n_tokens] token ids; ids in [audio_begin,
@@ -142,8 +145,9 @@ int qdec_prefill(qdec_state* s, const int32_t* ids_host, int32_t n_tokens, const
 /* One decode step (NCNN page section 5, steps 1-6): embeds `token`
  * (0 <= token < vocab), runs all layers at position pos attending over
  * [0, pos], appends K/V at pos and sets n_past = pos + 1.
- * Requires pos == n_past (else QDEC_E_POS) and pos < max_ctx (else
- * QDEC_E_CAPACITY). logits_dev / argmax_dev as for qdec_prefill. */
+ * Requires pos == n_past (else QDEC_E_POS), pos < max_ctx and
+ * pos < QDEC_DECODE_MAX_POS (else QDEC_E_CAPACITY). logits_dev /
+ * argmax_dev as for qdec_prefill. */
 int qdec_decode_step(qdec_state* s, int32_t token, int32_t pos, float* logits_dev, int32_t* argmax_dev);
 
 /* As qdec_decode_step, with the token read on the device from token_dev
@@ -160,7 +164,7 @@ int qdec_decode_step_dev(qdec_state* s, const int32_t* token_dev, int32_t pos, f
  * host round trip. tokens_dev: DEVICE int32 [n_steps], receives each step's
  * greedy token. logits_dev: DEVICE fp32 [n_steps, vocab] or NULL.
  * Requires pos == n_past (else QDEC_E_POS), 1 <= n_steps <= 4096 and
- * pos + n_steps <= max_ctx (else QDEC_E_CAPACITY). Sets n_past = pos +
+ * pos + n_steps <= min(max_ctx, QDEC_DECODE_MAX_POS) (else QDEC_E_CAPACITY). Sets n_past = pos +
  * n_steps. End-of-sequence handling stays with the caller: every step runs.
  * A *token_dev outside [0, vocab) is clamped into range on the device. */
 int qdec_decode_greedy(qdec_state* s, const int32_t* token_dev, int32_t pos, int32_t n_steps, float* logits_dev,

@@ -303,6 +303,9 @@ int run_decode(qdec_state* s, int token, const int32_t* token_dev, int pos, int 
   hipStream_t st = m->stream;
   if (__atomic_load_n(m->err_host, __ATOMIC_ACQUIRE))
     return fail(QDEC_E_DEVICE, "an earlier decode launch hit its time limit; the model must be recreated");
+  if ((int64_t)pos + nsteps > kDecMaxPos)
+    return fail(QDEC_E_CAPACITY, "decode reaches position %lld; decode supports positions below %d",
+                (long long)pos + nsteps - 1, kDecMaxPos);
   // tags never repeat while stale words could still hold them: before the
   // counter would wrap, every word is cleared and tags restart at 1
   const unsigned need = (unsigned)nsteps * dec_tags_per_step(d);

@@ -86,7 +86,7 @@ enum { PH_Q = 0, PH_ATT = 1, PH_O = 2, PH_Z = 3, PH_X = 4, PH_KEY = 5 };
 constexpr int kSlots = 12;
 constexpr int kSlotBytes = kWave * 16;
 constexpr int kMaxK = 1024;  // longest GEMV input: max(hidden, G * D, ffn / 8)
-constexpr int kPtabLds = 1024;  // KV page pointers kept in LDS (positions < 16384)
+constexpr int kPtabLds = kDecMaxPos / kPage;  // KV page pointers kept in LDS
 #ifndef QDEC_ISSUE_SLEEP
 #define QDEC_ISSUE_SLEEP 0  // s_sleep units between a layer unit's weight loads
 #endif
@@ -102,6 +102,10 @@ __device__ __forceinline__ u64 now() { return __builtin_amdgcn_s_memrealtime(); 
 constexpr int kTraceN = 512;
 __device__ u64 g_trace[2048 * kTraceN];
 __shared__ u64 g_xtr[kTraceN];
+#define TRACEC(step, l, i)                                            \
+  do {                                                                \
+    if ((l) >= 1 && (l) <= 3) TRACE(step, 432 + ((l) - 1) * 8 + (i)); \
+  } while (0)
 #define TRACEB(step, l, i)                            \
   do {                                                \
     if ((l) >= 1 && (l) <= 3) TRACE(step, 464 + ((l) - 1) * 8 + (i)); \
@@ -117,6 +121,9 @@ __shared__ u64 g_xtr[kTraceN];
   do {                   \
   } while (0)
 #define TRACEB(step, l, i) \
+  do {                     \
+  } while (0)
+#define TRACEC(step, l, i) \
   do {                     \
   } while (0)
 #endif
@@ -183,6 +190,7 @@ constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within each 8
 constexpr int kDppMirror = 0x140;     // lane i <-> 15 - i within each 16
 constexpr int kDppXor8 = 0x128;       // row_ror:8, i.e. lane i <-> i ^ 8 within each 16
+constexpr int kDppRor4 = 0x124;       // row_ror:4, lane i reads lane (i + 4) mod 16 of its row
 // permlane32_swap(a, b) exchanges lanes 32-63 of a with lanes 0-31 of b;
 // permlane16_swap(a, b) exchanges the odd 16-lane rows of a with the even rows
 // of b. pair32(a, b): lanes 0-31 hold a[i] + a[i+32], lanes 32-63 b[i-32] + b[i].
@@ -601,165 +609,194 @@ __device__ __forceinline__ void consume_unit(const Ring& rg, int lg, const float
 
 // ---------------------------------------------------------------- attention
 
-// K/V of cached position u for KV head g, DPL floats at dims part*DPL.. ;
-// `fresh` positions were written earlier in this launch by another CU and are
-// read with device-scope loads.
-// Device address of the KV page holding position u (page pointers of the
-// first kPtabLds pages are cached in LDS at launch start).
-__device__ __forceinline__ gfloat* page_of(const DecParams& p, const u64* ptab, int u) {
-  const int pg = u / kPage;
-  u64 a;
-  if (pg < kPtabLds)
-    a = ptab[pg];
-  else  // an atomic global load keeps the two reads from merging into one FLAT load
-    a = get_g((const gu64*)(p.page_table + pg));
-  return (gfloat*)a;
-}
+// Device address of the KV page holding position u. The page pointers are
+// copied to LDS at launch start (a launch covers positions < kPtabLds *
+// kPage); reading them only from LDS keeps K/V loads free of any wait on
+// other global loads.
+__device__ __forceinline__ gfloat* page_of(const u64* ptab, int u) { return (gfloat*)ptab[u / kPage]; }
 
-template <int DPL>
-__device__ __forceinline__ void load_kv(const DecParams& p, const u64* ptab, int l, int g, int u, int part, bool fresh,
-                                        float* kv, float* vv) {
-  const gfloat* page = page_of(p, ptab, u);
-  Dims dd{p.L, 0, 0, p.NKV, DPL * 8, 0, 0, 0.f};
-  const gfloat* kp = page + page_offset(dd, l, 0, g, u % kPage) + part * DPL;
-  const gfloat* vp = page + page_offset(dd, l, 1, g, u % kPage) + part * DPL;
-  typedef float f32x4 __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(1))) const f32x4 gf32x4;
+// N floats (N even) of cached position u, K (which = 0) or V (which = 1) of
+// KV head g, dims [d0, d0 + N). `fresh` positions were written earlier in this
+// launch by another CU and are read with device-scope loads.
+template <int D, int N>
+__device__ __forceinline__ void load_kvrow(const DecParams& p, const u64* ptab, int l, int g, int u, int which, int d0,
+                                           bool fresh, float* out) {
+  const gfloat* page = page_of(ptab, u);
+  Dims dd{p.L, 0, 0, p.NKV, D, 0, 0, 0.f};
+  const gfloat* src = page + page_offset(dd, l, which, g, u % kPage) + d0;
   if (!fresh) {
+    if constexpr (N % 4 == 0) {
+      typedef float f32x4 __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(1))) const f32x4 gf32x4;
 #pragma unroll
-    for (int i = 0; i < DPL; i += 4) {
-      const f32x4 a = *reinterpret_cast<gf32x4*>(kp + i);
-      kv[i] = a.x; kv[i + 1] = a.y; kv[i + 2] = a.z; kv[i + 3] = a.w;
-      const f32x4 c = *reinterpret_cast<gf32x4*>(vp + i);
-      vv[i] = c.x; vv[i + 1] = c.y; vv[i + 2] = c.z; vv[i + 3] = c.w;
+      for (int i = 0; i < N; i += 4) {
+        const f32x4 a = *reinterpret_cast<gf32x4*>(src + i);
+        out[i] = a.x; out[i + 1] = a.y; out[i + 2] = a.z; out[i + 3] = a.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < N; ++i) out[i] = src[i];
     }
   } else {
+    if constexpr (N % 2 == 0) {
 #pragma unroll
-    for (int i = 0; i < DPL; i += 2) {
-      const u64 a = get_g(reinterpret_cast<const gu64*>(kp + i));
-      kv[i] = __uint_as_float((unsigned)a); kv[i + 1] = __uint_as_float((unsigned)(a >> 32));
-      const u64 c = get_g(reinterpret_cast<const gu64*>(vp + i));
-      vv[i] = __uint_as_float((unsigned)c); vv[i + 1] = __uint_as_float((unsigned)(c >> 32));
+      for (int i = 0; i < N; i += 2) {
+        const u64 a = get_g(reinterpret_cast<const gu64*>(src + i));
+        out[i] = __uint_as_float((unsigned)a);
+        out[i + 1] = __uint_as_float((unsigned)(a >> 32));
+      }
+    } else {
+      typedef __attribute__((address_space(1))) unsigned gu32;
+#pragma unroll
+      for (int i = 0; i < N; ++i)
+        out[i] = __uint_as_float(__hip_atomic_load(reinterpret_cast<gu32*>(const_cast<gfloat*>(src + i)),
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     }
   }
 }
 
 // Online-softmax attention of the G query heads of KV head g over the keys
 // [u0, u0 + n_cached) of the cache plus (if with_cur) the current token held
-// in LDS, one exchange wave's share. Lane layout: key slot = lane / 8 (8 keys
-// per wave per iteration), part = lane % 8 owns DPL = D/8 dims. The wave's
-// result per head: running max, sum and unnormalised output in wm, wl, wo.
-// The first two iterations' K/V come from prefetch().
+// in LDS, one exchange wave's share. Keys are taken in blocks of KPB; wave w
+// owns keys [w KPW, (w + 1) KPW) of each block.
+//  - Scores: four lanes per key (lane = 4 slot + part), each holding a quarter
+//    of the dims; a quad reduction gives every lane of the quad the score.
+//  - Output: lanes own output dims (VD per lane) and loop over the wave's
+//    keys with the probabilities broadcast from LDS, so P.V needs no
+//    cross-lane reduction.
+// The wave's result per head: running max, sum and unnormalised output in
+// wm, wl, wo. Block 0's K/V come from prefetch().
 template <int D, int G>
 struct Attn {
-  static constexpr int DPL = D / 8;
-  static constexpr int kPerIt = kExWaves * 8;  // keys per iteration
-  float kv0[DPL], vv0[DPL], kv1[DPL], vv1[DPL];
+  static constexpr int PARTS = 4;              // lanes per key for the scores
+  static constexpr int DPL = D / PARTS;        // score dims per lane
+  static constexpr int KPW = kWave / PARTS;    // keys per wave per block
+  static constexpr int KPB = KPW * kExWaves;   // keys per block
+  static constexpr int VD = D >= kWave ? D / kWave : 1;  // output dims per lane
+  static constexpr int VL = D / VD;            // lanes holding output dims
+  // q and k rows in LDS are padded by 4 floats after each part's DPL dims, so
+  // the four parts of a key, read in the same instruction, sit in different banks
+  static constexpr int QS = D + 4 * PARTS;     // padded row length
+  __host__ __device__ static constexpr int padi(int d) { return d + (d / DPL) * 4; }
+  float kr[DPL];      // K chunk of this lane's key
+  float vr[KPW][VD];  // V of the wave's keys at this lane's dims
+
+  // Every lane loads unconditionally from a valid position (keys past the
+  // cached ones are clamped to the last cached one, or to position 0), so the
+  // loads stay independent of each other; those values are masked later.
+  __device__ __forceinline__ void load_block(const DecParams& p, const u64* ptab, int l, int g, int u0, int b0,
+                                             int n_cached, int ew, int lane) {
+    const int slot = lane / PARTS, part = lane % PARTS;
+    const int last = n_cached > 0 ? u0 + n_cached - 1 : 0;
+    const int uk = min(u0 + b0 + ew * KPW + slot, last);
+    load_kvrow<D, DPL>(p, ptab, l, g, uk, 0, part * DPL, uk >= p.pos0, kr);
+#pragma unroll
+    for (int j = 0; j < KPW; ++j) {
+      const int uj = min(u0 + b0 + ew * KPW + j, last);  // wave-uniform
+      load_kvrow<D, VD>(p, ptab, l, g, uj, 1, (lane % VL) * VD, uj >= p.pos0, vr[j]);
+    }
+  }
 
   __device__ __forceinline__ void prefetch(const DecParams& p, const u64* ptab, int l, int g, int u0, int n_cached,
                                            int ew, int lane) {
-    const int slot = lane / 8, part = lane % 8;
-    const int k0 = ew * 8 + slot, k1 = k0 + kPerIt;
-    if (k0 < n_cached) load_kv<DPL>(p, ptab, l, g, u0 + k0, part, u0 + k0 >= p.pos0, kv0, vv0);
-    if (k1 < n_cached) load_kv<DPL>(p, ptab, l, g, u0 + k1, part, u0 + k1 >= p.pos0, kv1, vv1);
+    load_block(p, ptab, l, g, u0, 0, n_cached, ew, lane);
   }
 
-  __device__ __forceinline__ void step(const float* q_l, const float* k_l, const float* v_l, const float* kv,
-                                       const float* vv, int kidx, int n_cached, int n_keys, int part, float* m,
-                                       float* ls, float (*acc)[DPL]) {
-    const bool valid = kidx < n_keys;
-    float kk[DPL], vvv[DPL];
-    if (kidx >= n_cached && valid) {
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) {
-        kk[i] = k_l[part * DPL + i];
-        vvv[i] = v_l[part * DPL + i];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) {
-        kk[i] = valid ? kv[i] : 0.f;
-        vvv[i] = valid ? vv[i] : 0.f;
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float sc = 0.f;
-#pragma unroll
-      for (int i = 0; i < DPL; i += 4) {
-        const float4 q = *reinterpret_cast<const float4*>(q_l + h * D + part * DPL + i);
-        sc = fmaf(q.x, kk[i], sc);
-        sc = fmaf(q.y, kk[i + 1], sc);
-        sc = fmaf(q.z, kk[i + 2], sc);
-        sc = fmaf(q.w, kk[i + 3], sc);
-      }
-      // sum over the 8 parts of a key (quad steps, then the two quads of the 8)
-      sc += dpp<kDppXor1>(sc);
-      sc += dpp<kDppXor2>(sc);
-      sc += dpp<kDppHalfMirror>(sc);
-      if (!valid) sc = -INFINITY;
-      // max over the 8 keys of the wave (values are uniform within each 8 lanes)
-      float mx = fmaxf(sc, dpp<kDppMirror>(sc));
-      mx = max32(max16(mx));
-      const float mn = fmaxf(m[h], mx);
-      if (mn == -INFINITY) continue;  // nothing valid seen yet by this wave (wave-uniform)
-      const float alpha = expf(m[h] - mn);
-      const float pr = valid ? expf(sc - mn) : 0.f;
-      float ps = pr + dpp<kDppMirror>(pr);
-      ps = sum32(sum16(ps));
-      ls[h] = ls[h] * alpha + ps;
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) acc[h][i] = fmaf(pr, vvv[i], acc[h][i] * alpha);
-      m[h] = mn;
-    }
-  }
-
-  // q_l: [G][D] (scaled), k_l, v_l: [D] current token; writes wm[ew*G + h],
-  // wl[ew*G + h], wo[(ew*G + h)*D + d].
+  // q_l: [G][D] (scaled), k_l, v_l: [D] current token; pw: this wave's
+  // probabilities [G][KPW]; writes wm[ew*G + h], wl[ew*G + h], wo[(ew*G + h)*D + d].
   __device__ __forceinline__ void partial(const DecParams& p, const u64* ptab, int l, int g, int u0, int n_cached,
-                                          bool with_cur,
-                                          const float* q_l, const float* k_l, const float* v_l, float* wm, float* wl,
-                                          float* wo, int ew, int lane, int step = 1, int tid = 0) {
+                                          bool with_cur, const float* q_l, const float* k_l, const float* v_l,
+                                          float* pw, float* wm, float* wl, float* wo, int ew, int lane, int step = 1,
+                                          int tid = 0) {
     (void)step;
     (void)tid;
-    const int slot = lane / 8, part = lane % 8;
-    float m[G], ls[G], acc[G][DPL];
+    const int slot = lane / PARTS, part = lane % PARTS;
+    const int n_keys = n_cached + (with_cur ? 1 : 0);
+    float m[G], ls[G], o[G][VD];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       m[h] = -INFINITY;
       ls[h] = 0.f;
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) acc[h][i] = 0.f;
+      for (int t = 0; t < VD; ++t) o[h][t] = 0.f;
     }
-    const int n_keys = n_cached + (with_cur ? 1 : 0);
-    for (int base = 0; base < n_keys; base += 2 * kPerIt) {
-      const int ka = base + ew * 8 + slot;
-      this->step(q_l, k_l, v_l, kv0, vv0, ka, n_cached, n_keys, part, m, ls, acc);
-      if (base == 0) TRACEB(step, l, 1);
-      const int kn0 = ka + 2 * kPerIt;
-      if (kn0 < n_cached) load_kv<DPL>(p, ptab, l, g, u0 + kn0, part, u0 + kn0 >= p.pos0, kv0, vv0);
-      const int kb = ka + kPerIt;
-      if (base + kPerIt < n_keys) this->step(q_l, k_l, v_l, kv1, vv1, kb, n_cached, n_keys, part, m, ls, acc);
-      const int kn1 = kb + 2 * kPerIt;
-      if (kn1 < n_cached) load_kv<DPL>(p, ptab, l, g, u0 + kn1, part, u0 + kn1 >= p.pos0, kv1, vv1);
-    }
-    TRACEB(step, l, 6);
-    // sum the 8 key slots of the wave (same running max within the wave)
+    for (int b0 = 0; b0 < n_keys; b0 += KPB) {
+      if (b0 > 0) load_block(p, ptab, l, g, u0, b0, n_cached, ew, lane);
+      const int key = b0 + ew * KPW + slot;
+      if (b0 == 0) TRACEB(step, l, 1);
+      float kk[DPL];
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+      for (int i = 0; i < DPL; ++i) kk[i] = key == n_cached ? k_l[part * (DPL + 4) + i] : kr[i];
+      if (b0 == 0) TRACEC(step, l, 1);
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) {
-        float v = acc[h][i];
-        v += dpp<kDppXor8>(v);  // same part of the other key slot in the row
-        v = sum32(sum16(v));
-        acc[h][i] = v;
+      for (int h = 0; h < G; ++h) {
+        if (b0 == 0 && h == 1) TRACEC(step, l, 2);
+        float sc = 0.f;
+#pragma unroll
+        for (int i = 0; i < DPL; i += 4) {
+          const float4 q = *reinterpret_cast<const float4*>(q_l + h * QS + part * (DPL + 4) + i);
+          sc = fmaf(q.x, kk[i], sc);
+          sc = fmaf(q.y, kk[i + 1], sc);
+          sc = fmaf(q.z, kk[i + 2], sc);
+          sc = fmaf(q.w, kk[i + 3], sc);
+        }
+        sc += dpp<kDppXor1>(sc);  // the key's four parts
+        sc += dpp<kDppXor2>(sc);
+        if (key >= n_keys) sc = -INFINITY;
+        if (b0 == 0 && h == 0) TRACEC(step, l, 3);
+        // the wave's keys sit at lanes i, i+4, i+8, i+12 of each 16-lane row
+        float mx = fmaxf(sc, dpp<kDppRor4>(sc));
+        mx = fmaxf(mx, dpp<kDppXor8>(mx));
+        mx = max32(max16(mx));
+        const float mn = fmaxf(m[h], mx);
+        if (mn == -INFINITY) continue;  // no valid key seen yet by this wave (wave-uniform)
+        const float alpha = expf(m[h] - mn);
+        const float pr = key < n_keys ? expf(sc - mn) : 0.f;
+        float ps = pr + dpp<kDppRor4>(pr);
+        ps += dpp<kDppXor8>(ps);
+        ps = sum32(sum16(ps));
+        ls[h] = ls[h] * alpha + ps;
+        m[h] = mn;
+#pragma unroll
+        for (int t = 0; t < VD; ++t) o[h][t] *= alpha;
+        if (part == 0) pw[h * KPW + slot] = pr;
       }
-    TRACEB(step, l, 7);
-    if (slot == 0) {
+      if (b0 == 0) TRACEB(step, l, 6);
+      // P.V: this lane's output dims over the wave's keys of the block; the
+      // probabilities and the current token's V are read once, up front
+      float pv[G][KPW];
 #pragma unroll
       for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int i = 0; i < DPL; ++i) wo[(ew * G + h) * D + part * DPL + i] = acc[h][i];
+        for (int i = 0; i < KPW; i += 4) {
+          const float4 t4 = *reinterpret_cast<const float4*>(pw + h * KPW + i);
+          pv[h][i] = t4.x;
+          pv[h][i + 1] = t4.y;
+          pv[h][i + 2] = t4.z;
+          pv[h][i + 3] = t4.w;
+        }
+      float vcur[VD];
+#pragma unroll
+      for (int t = 0; t < VD; ++t) vcur[t] = v_l[(lane % VL) * VD + t];
+#pragma unroll
+      for (int j = 0; j < KPW; ++j) {
+        const int kj = b0 + ew * KPW + j;  // wave-uniform
+        if (kj >= n_keys) break;
+        float vv[VD];
+#pragma unroll
+        for (int t = 0; t < VD; ++t) vv[t] = kj == n_cached ? vcur[t] : vr[j][t];
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int t = 0; t < VD; ++t) o[h][t] = fmaf(pv[h][j], vv[t], o[h][t]);
+      }
+    }
+    TRACEB(step, l, 7);
+    if (lane < VL) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int t = 0; t < VD; ++t) wo[(ew * G + h) * D + lane * VD + t] = o[h][t];
     }
     if (lane == 0) {
 #pragma unroll
@@ -785,15 +822,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
   __shared__ __attribute__((aligned(16))) char ring1[kMemWaves * kSlots * kSlotBytes];
   __shared__ Ctl ctl;
   float* stage = sm + p.lds_stage;  // split-attention partials of all ranks
-  float* att = sm + p.lds_att;      // q_l [G][D] | k_l [D] | v_l [D] | wm | wl | wo
+  float* att = sm + p.lds_att;      // q_l [G][D] | k_l [D] | v_l [D] | wm | wl | wo | pw
   float* sbuf = sm + p.lds_sbuf;    // per-slot partial dots [wave][unit][kSlots]
   u64* ptab = reinterpret_cast<u64*>(sm + p.lds_ptab);  // KV page pointers
-  float* q_l = att;
-  float* k_l = q_l + QD;
-  float* v_l = k_l + D;
+  constexpr int QS = Attn<D, G>::QS;  // padded q/k row length
+  float* q_l = att;                   // [G][QS]
+  float* k_l = q_l + G * QS;          // [QS]
+  float* v_l = k_l + QS;              // [D]
   float* wm = v_l + D;
   float* wl = wm + kExWaves * G;
   float* wo = wl + kExWaves * G;
+  float* pw = wo + kExWaves * G * D;  // attention probabilities [wave][G][keys per wave]
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -1019,7 +1058,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
   load_post(0);
   load_qk(0);
   {
-    const int np = min((pp->pos0 + pp->nsteps + kPage - 1) / kPage, kPtabLds);
+    const int np = (pp->pos0 + pp->nsteps + kPage - 1) / kPage;  // <= kPtabLds (checked by the host)
     for (int i = et; i < np; i += kEx) ptab[i] = (u64)pp->page_table[i];
   }
   int token = pp->token_dev ? pp->token_dev[0] : pp->token;
@@ -1065,6 +1104,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
         gather_sum<NE>(Lx_prev, kGroups, H, tgp + PH_X, x, et, &ctl, pp->err);
       }
       TRACE(step, 1 + l * 10 + 0);
+#ifdef QDEC_TRACE
+      // shader-clock counter beside the 100 MHz counter (clock-rate check)
+      if (step == 0 && tid == kExBase && (l == 2 || l == 12)) g_xtr[l == 2 ? 504 : 505] = __builtin_amdgcn_s_memtime();
+#endif
       if (l == L) break;
       u64* Lq = pp->ll + pp->o_q + ((size_t)par * NKV + X) * GW;
       u64* La = pp->ll + pp->o_att + ((size_t)par * NKV + X) * R * G * (D + 2);
@@ -1076,7 +1119,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
         // ---------------- A
         norm_input(gi);
         pad(H);
-        if (l < 16) TRACE(step, 400 + l * 4 + 0);
+        if (l < 8) TRACE(step, 400 + l * 4 + 0);
         bar();  // input ready
         bar();  // partials ready
         TRACE(step, 1 + l * 10 + 1);
@@ -1110,8 +1153,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
         TRACE(step, 1 + l * 10 + 2);
         // per-head RMSNorm + RoPE (q heads, k); v copied; rank 0 appends K and V at pos
         {
-          gfloat* page = page_of(p, ptab, pos);
-          Dims dd{L, 0, 0, NKV, D, 0, 0, 0.f};
 #pragma unroll
           for (int i = 0; i < 2; ++i) {
             const int hv = ew + kExWaves * i;
@@ -1128,17 +1169,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
             }
             if (ln < half) {
               if (hv < G) {
-                q_l[hv * D + ln] = a * pp->scale;
-                q_l[hv * D + ln + half] = c * pp->scale;
+                q_l[hv * QS + Attn<D, G>::padi(ln)] = a * pp->scale;
+                q_l[hv * QS + Attn<D, G>::padi(ln + half)] = c * pp->scale;
+              } else if (hv == G) {
+                k_l[Attn<D, G>::padi(ln)] = a;
+                k_l[Attn<D, G>::padi(ln + half)] = c;
               } else {
-                float* dstv = hv == G ? k_l : v_l;
-                dstv[ln] = a;
-                dstv[ln + half] = c;
-                if (r == 0) {  // write-through; completion awaited before the partials are merged
-                  gfloat* kvp = page + page_offset(dd, l, hv == G ? 0 : 1, X, pos % kPage);
-                  __hip_atomic_store(kvp + ln, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                  __hip_atomic_store(kvp + ln + half, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
+                v_l[ln] = a;
+                v_l[ln + half] = c;
               }
             }
           }
@@ -1147,8 +1185,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
         ex_sync(exgen, ln, &ctl, pp->err);
         TRACEB(step, l, 3);
         if (att_rank)
-          at.partial(p, ptab, l, X, u0, n_cached, whole || r == nsplit - 1, q_l, k_l, v_l, wm, wl, wo, ew, ln, step,
-                     tid);
+          at.partial(p, ptab, l, X, u0, n_cached, whole || r == nsplit - 1, q_l, k_l, v_l,
+                     pw + ew * G * Attn<D, G>::KPW, wm, wl, wo, ew, ln, step, tid);
         TRACEB(step, l, 4);
         ex_sync(exgen, ln, &ctl, pp->err);
         TRACEB(step, l, 5);
@@ -1208,6 +1246,20 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
           }
         }
         pad(QD);
+        // rank 0 appends this token's K and V at pos (device scope: other CUs
+        // of the group read them in later steps). Stores count against the
+        // same in-order counter as loads, so they are issued only after the
+        // attention; they complete before this workgroup publishes again.
+        if (r == 0) {
+          gfloat* page = page_of(ptab, pos);
+          Dims dd{L, 0, 0, NKV, D, 0, 0, 0.f};
+          for (int i = et; i < 2 * D; i += kEx) {
+            const int sel = i / D, d = i % D;
+            __hip_atomic_store(page + page_offset(dd, l, sel, X, pos % kPage) + d,
+                               sel ? v_l[d] : k_l[Attn<D, G>::padi(d)],
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
         // next layer's gains: a wave's loads retire in order, so these are
         // issued only now, ahead of the O-partial wait that hides them
         load_in(l + 1);
@@ -1234,7 +1286,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
       norm_input(gp);
       pad(H);
       if (l + 1 < L) load_post(l + 1);
-      if (l < 16) TRACE(step, 400 + l * 4 + 1);
+      if (l < 8) TRACE(step, 400 + l * 4 + 1);
       bar();  // input ready
       bar();  // partials ready
       {
@@ -1343,7 +1395,8 @@ Layout layout(bool bf16, const Dims& d, int nsplit_max, int nb) {
   const int QD = G * d.D;
   const int VN = bf16 ? 8 : 4;
   const int stage = std::max(8, nsplit_max * G * (d.D + 2));
-  const int att = QD + 2 * d.D + 2 * kExWaves * G + kExWaves * G * d.D;
+  const int qs = d.D + 16;  // padded q/k row (4 floats after each quarter)
+  const int att = (G + 1) * qs + d.D + 2 * kExWaves * G + kExWaves * G * d.D + kExWaves * G * (kWave / 4);
   const int hrows = (d.V + nb - 1) / nb;
   const int rows_w = (hrows + kMemWaves - 1) / kMemWaves;
   const int rpb = kSlots >> chunk_lg(d.H, VN);

@@ -13,6 +13,7 @@ constexpr int kPage = QDEC_PAGE;   // positions per KV page
 constexpr int kGuGroup = 8;        // gate/up rows interleaved in groups of 8 in the packed weight
 constexpr int kAttnChunk = 256;    // positions per split in decode attention
 constexpr int kMaxBatch = 16;
+constexpr int kDecMaxPos = QDEC_DECODE_MAX_POS;  // decode positions (KV page pointers held in LDS)
 
 // Model dimensions as the kernels see them.
 struct Dims {
