@@ -724,9 +724,18 @@ struct Attn {
       if (b0 > 0) load_block(p, ptab, l, g, u0, b0, n_cached, ew, lane);
       const int key = b0 + ew * KPW + slot;
       if (b0 == 0) TRACEB(step, l, 1);
+      // the current token's K (LDS) replaces the cached one in its key's lanes:
+      // read for every lane, then selected without branches
+      const bool cur = key == n_cached;
       float kk[DPL];
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) kk[i] = key == n_cached ? k_l[part * (DPL + 4) + i] : kr[i];
+      for (int i = 0; i < DPL; i += 4) {
+        const float4 t4 = *reinterpret_cast<const float4*>(k_l + part * (DPL + 4) + i);
+        kk[i] = cur ? t4.x : kr[i];
+        kk[i + 1] = cur ? t4.y : kr[i + 1];
+        kk[i + 2] = cur ? t4.z : kr[i + 2];
+        kk[i + 3] = cur ? t4.w : kr[i + 3];
+      }
       if (b0 == 0) TRACEC(step, l, 1);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
