@@ -43,6 +43,25 @@ def decode_bytes(shape, ctx_lens) -> float:
     return float(np.mean([w + L * kv_row * p + L * kv_row for p in ctx_lens]))
 
 
+def counter_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
+    or None when the decode kernel's source has changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "decode_kernel_short_traffic.txt")
+    src = os.path.join(ROOT, "qwen3_kv_cache_amd", "csrc", "qdec_decode.hip")
+    try:
+        kv = {}
+        for line in open(path):
+            if ":" in line and not line.startswith((" ", "#")):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+        if kv.get("source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+            return None
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def copy_probe():
     import torch
     n = 1 << 28  # 1 GiB of fp32
@@ -186,8 +205,10 @@ def main():
         "decode_ms_per_token": round(float(dec_ms.mean()) / n, 5),
     }
     if achieved is not None:
+        # counters were taken on the short workload's 64-step launch
+        traffic = counter_traffic() if (w.name == "short" and not a.per_step) else None
         line["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                             "kernel": "decode_kernel (%d steps per launch)" % (1 if a.per_step else n),
                             "bytes_per_unit": round(bytes_tok)}
     if a.cpu_sample > 0:
