@@ -142,6 +142,8 @@ struct qdec_model {
   float* pZ = nullptr;
   void* pA0 = nullptr;  // bf16 hi (or fp32 activations for fp32 weights)
   void* pA1 = nullptr;  // bf16 lo
+  float* pPart = nullptr;  // small-M GEMM chunk partials (prompts of <= 64 tokens)
+  size_t part_cap = 0;
   PagePool pool;
   int live_states = 0;
   // persistent decode
@@ -205,6 +207,9 @@ void free_prefill(qdec_model* m) {
   (void)hipFree(m->pZ);
   (void)hipFree(m->pA0);
   (void)hipFree(m->pA1);
+  (void)hipFree(m->pPart);
+  m->pPart = nullptr;
+  m->part_cap = 0;
   m->p_ids = nullptr;
   m->pX = m->pQKV = m->pAttn = m->pZ = nullptr;
   m->pA0 = m->pA1 = nullptr;
@@ -261,6 +266,12 @@ int ensure_rope(qdec_model* m, int n_pos) {
   return QDEC_OK;
 }
 
+// chunk partials of the small-M GEMM path, largest over the layer GEMMs
+size_t part_floats(const Dims& d, int T) {
+  return std::max(std::max(skinny_partial_floats(T, d.H, d.qkv()), skinny_partial_floats(T, d.NQ * d.D, d.H)),
+                  std::max(skinny_partial_floats(T, d.H, 2 * d.F), skinny_partial_floats(T, d.F, d.H)));
+}
+
 int ensure_prefill(qdec_model* m, int T) {
   if (T <= m->pf_cap) return QDEC_OK;
   HIP_TRY(hipStreamSynchronize(m->stream));
@@ -271,7 +282,8 @@ int ensure_prefill(qdec_model* m, int T) {
   if ((e = dev_alloc(&m->p_ids, T, "prefill ids")) || (e = dev_alloc(&m->pX, (size_t)T * d.H, "prefill X")) ||
       (e = dev_alloc(&m->pQKV, (size_t)T * d.qkv(), "prefill QKV")) ||
       (e = dev_alloc(&m->pAttn, (size_t)T * d.NQ * d.D, "prefill attention")) ||
-      (e = dev_alloc(&m->pZ, (size_t)T * d.F, "prefill FFN"))) {
+      (e = dev_alloc(&m->pZ, (size_t)T * d.F, "prefill FFN")) ||
+      (T <= 64 && (e = dev_alloc(&m->pPart, part_floats(d, T), "GEMM partials")))) {
     free_prefill(m);
     return e;
   }
@@ -283,6 +295,7 @@ int ensure_prefill(qdec_model* m, int T) {
     return fail(QDEC_E_OOM, "cannot allocate prefill activations for %d tokens", T);
   }
   m->pf_cap = T;
+  m->part_cap = T <= 64 ? part_floats(d, T) : 0;
   return QDEC_OK;
 }
 
@@ -361,16 +374,20 @@ int run_prefill(qdec_state* s, int T, const float* audio, int a0, int La, float*
   for (int l = 0; l < d.L; ++l) {
     const LayerW& w = m->layers[l];
     LAUNCH(norm_in(m->pX, d.H, w.in_norm));
-    LAUNCH(launch_gemm(bf, EPI_STORE, m->pA0, m->pA1, T, d.H, w.wqkv, d.qkv(), m->pQKV, d.qkv(), st));
+    LAUNCH(launch_gemm(bf, EPI_STORE, m->pA0, m->pA1, T, d.H, w.wqkv, d.qkv(), m->pQKV, d.qkv(), st, m->pPart,
+                            m->part_cap));
     LAUNCH(launch_qk_rope_append(d, m->pQKV, T, 0, w.q_norm, w.k_norm, m->rope_cos, m->rope_sin, s->pt_dev, l,
                                  st));
     LAUNCH(launch_attn_prefill(d, m->pQKV, T, m->pAttn, st));
     LAUNCH(norm_in(m->pAttn, d.NQ * d.D, nullptr));
-    LAUNCH(launch_gemm(bf, EPI_RESID, m->pA0, m->pA1, T, d.NQ * d.D, w.wo, d.H, m->pX, d.H, st));
+    LAUNCH(launch_gemm(bf, EPI_RESID, m->pA0, m->pA1, T, d.NQ * d.D, w.wo, d.H, m->pX, d.H, st, m->pPart,
+                            m->part_cap));
     LAUNCH(norm_in(m->pX, d.H, w.post_norm));
-    LAUNCH(launch_gemm(bf, EPI_SWIGLU, m->pA0, m->pA1, T, d.H, w.wgu, 2 * d.F, m->pZ, d.F, st));
+    LAUNCH(launch_gemm(bf, EPI_SWIGLU, m->pA0, m->pA1, T, d.H, w.wgu, 2 * d.F, m->pZ, d.F, st, m->pPart,
+                            m->part_cap));
     LAUNCH(norm_in(m->pZ, d.F, nullptr));
-    LAUNCH(launch_gemm(bf, EPI_RESID, m->pA0, m->pA1, T, d.F, w.wd, d.H, m->pX, d.H, st));
+    LAUNCH(launch_gemm(bf, EPI_RESID, m->pA0, m->pA1, T, d.F, w.wd, d.H, m->pX, d.H, st, m->pPart,
+                            m->part_cap));
   }
   LAUNCH(launch_lm_head(d, bf, m->embed, m->pX + (size_t)(T - 1) * d.H, m->final_norm, logits, m->keys, st));
   LAUNCH(launch_argmax_final(m->keys, 1, argmax ? argmax : m->argmax_tmp, st));
