@@ -144,6 +144,28 @@ struct qdec_model {
   void* pA1 = nullptr;  // bf16 lo
   float* pPart = nullptr;  // small-M GEMM chunk partials (prompts of <= 64 tokens)
   size_t part_cap = 0;
+  // batched decode workspace for kMaxBatch rows, allocated on first use
+  bool b_ready = false;
+  float* bX = nullptr;
+  float* bQKV = nullptr;
+  float* bAttn = nullptr;
+  float* bZ = nullptr;
+  void* bA0 = nullptr;
+  void* bA1 = nullptr;
+  float* bPart = nullptr;
+  size_t b_part_cap = 0;
+  float* bLogits = nullptr;  // logits when the caller passes none
+  unsigned long long* bKeys = nullptr;
+  int32_t* bTok = nullptr;   // argmax when the caller passes none
+  float* bAttnPart = nullptr;
+  int b_nsplit_cap = 0;
+  // fused small-M GEMM workspace (up to 64 rows): split-K partials, arrival
+  // counters, RMSNorm sum-of-squares partials
+  unsigned long long* rP = nullptr;
+  size_t rP_words = 0;
+  unsigned rows_tag = 1;  // tag of the next fused GEMM launch
+  unsigned* rCnt = nullptr;
+  float* rSsq = nullptr;
   PagePool pool;
   int live_states = 0;
   // persistent decode
@@ -216,9 +238,26 @@ void free_prefill(qdec_model* m) {
   m->pf_cap = 0;
 }
 
+void free_batch(qdec_model* m) {
+  for (void* p : {(void*)m->bX, (void*)m->bQKV, (void*)m->bAttn, (void*)m->bZ, m->bA0, m->bA1, (void*)m->bPart,
+                  (void*)m->bLogits, (void*)m->bKeys, (void*)m->bTok, (void*)m->bAttnPart})
+    (void)hipFree(p);
+  m->bX = m->bQKV = m->bAttn = m->bZ = m->bPart = m->bLogits = m->bAttnPart = nullptr;
+  m->bA0 = m->bA1 = nullptr;
+  m->bKeys = nullptr;
+  m->bTok = nullptr;
+  m->b_part_cap = 0;
+  m->b_nsplit_cap = 0;
+  m->b_ready = false;
+}
+
 void free_model(qdec_model* m) {
   if (!m) return;
   if (m->stream) (void)hipStreamSynchronize(m->stream);
+  free_batch(m);
+  (void)hipFree(m->rP);
+  (void)hipFree(m->rCnt);
+  (void)hipFree(m->rSsq);
   (void)hipFree(m->final_norm);
   (void)hipFree(m->wbuf);
   (void)hipFree(m->nbuf);
@@ -315,7 +354,7 @@ int run_decode(qdec_state* s, int token, const int32_t* token_dev, int pos, int 
   const Dims& d = m->d;
   hipStream_t st = m->stream;
   if (__atomic_load_n(m->err_host, __ATOMIC_ACQUIRE))
-    return fail(QDEC_E_DEVICE, "an earlier decode launch hit its time limit; the model must be recreated");
+    return fail(QDEC_E_DEVICE, "an earlier launch hit its time limit; the model must be recreated");
   if ((int64_t)pos + nsteps > kDecMaxPos)
     return fail(QDEC_E_CAPACITY, "decode reaches position %lld; decode supports positions below %d",
                 (long long)pos + nsteps - 1, kDecMaxPos);
@@ -360,34 +399,250 @@ int run_decode(qdec_state* s, int token, const int32_t* token_dev, int pos, int 
   return QDEC_OK;
 }
 
+int ensure_batch(qdec_model* m, int nsplit) {
+  const Dims& d = m->d;
+  constexpr int B = kMaxBatch;
+  if (!m->b_ready) {
+    const int kmax = std::max(std::max(d.H, d.NQ * d.D), d.F);
+    const size_t abytes = m->bf16 ? 2 : 4;
+    const size_t part = m->bf16 ? std::max(part_floats(d, B), skinny_partial_floats(B, d.H, d.V)) : 0;
+    int e = 0;
+    if ((e = dev_alloc(&m->bX, (size_t)B * d.H, "batch X")) ||
+        (e = dev_alloc(&m->bQKV, (size_t)B * d.qkv(), "batch QKV")) ||
+        (e = dev_alloc(&m->bAttn, (size_t)B * d.NQ * d.D, "batch attention")) ||
+        (e = dev_alloc(&m->bZ, (size_t)B * d.F, "batch FFN")) || (e = dev_alloc(&m->bPart, part, "batch partials")) ||
+        (e = dev_alloc(&m->bLogits, (size_t)B * d.V, "batch logits")) ||
+        (e = dev_alloc(&m->bKeys, (size_t)B, "batch keys")) || (e = dev_alloc(&m->bTok, (size_t)B, "batch tokens"))) {
+      free_batch(m);
+      return e;
+    }
+    if (hipMalloc(&m->bA0, (size_t)B * kmax * abytes) != hipSuccess ||
+        (m->bf16 && hipMalloc(&m->bA1, (size_t)B * kmax * abytes) != hipSuccess)) {
+      (void)hipGetLastError();
+      free_batch(m);
+      return fail(QDEC_E_OOM, "cannot allocate batch activations");
+    }
+    m->b_part_cap = part;
+    m->b_ready = true;
+  }
+  if (nsplit > m->b_nsplit_cap) {
+    HIP_TRY(hipStreamSynchronize(m->stream));
+    (void)hipFree(m->bAttnPart);
+    m->bAttnPart = nullptr;
+    m->b_nsplit_cap = 0;
+    if (int e = dev_alloc(&m->bAttnPart, (size_t)B * d.NQ * nsplit * (d.D + 2), "batch attention partials"))
+      return e;
+    m->b_nsplit_cap = nsplit;
+  }
+  return QDEC_OK;
+}
+
+// Workspace of the fused small-M GEMMs, sized for 64 rows; counters start at
+// zero and every launch leaves them at zero.
+int ensure_rows(qdec_model* m) {
+  if (m->rP) return QDEC_OK;
+  const Dims& d = m->d;
+  constexpr int R = 64;
+  const int shapes[5][2] = {{d.H, d.qkv()}, {d.NQ * d.D, d.H}, {d.H, 2 * d.F}, {d.F, d.H}, {d.H, d.V}};
+  size_t part = 1;
+  int cnt = 1;
+  for (auto& kn : shapes) {
+    if (!rows_fits(R, kn[0], kn[1])) continue;
+    part = std::max(part, rows_partial_floats(R, kn[0], kn[1]));
+    cnt = std::max(cnt, rows_counters(kn[0], kn[1]));
+  }
+  const size_t nss = (size_t)std::max(1, d.H / 16);
+  int e = 0;
+  if ((e = dev_alloc(&m->rP, part, "GEMM partial tiles")) || (e = dev_alloc(&m->rCnt, (size_t)cnt, "GEMM counters")) ||
+      (e = dev_alloc(&m->rSsq, nss * R, "RMSNorm partials"))) {
+    (void)hipFree(m->rP);
+    (void)hipFree(m->rCnt);
+    (void)hipFree(m->rSsq);
+    m->rP = nullptr;
+    m->rSsq = nullptr;
+    m->rCnt = nullptr;
+    return e;
+  }
+  HIP_TRY(hipMemset(m->rCnt, 0, (size_t)cnt * sizeof(unsigned)));
+  HIP_TRY(hipMemset(m->rP, 0, part * sizeof(unsigned long long)));
+  m->rP_words = part;
+  m->rows_tag = 1;
+  return QDEC_OK;
+}
+
+// Tag for the next fused GEMM launch. Before the counter would wrap, the
+// partial words are cleared (tag 0 is never used), so no stale word can match.
+int next_rows_tag(qdec_model* m, unsigned* tag) {
+  if (m->rows_tag >= 0xFFFFFFF0u) {
+    HIP_TRY(hipMemsetAsync(m->rP, 0, m->rP_words * sizeof(unsigned long long), m->stream));
+    m->rows_tag = 1;
+  }
+  *tag = m->rows_tag++;
+  return QDEC_OK;
+}
+
+int gemm_rows(qdec_model* m, Epi epi, bool norm, RowsGemm& g) {
+  if (int e = next_rows_tag(m, &g.tag)) return e;
+  g.err = m->err_dev;
+  LAUNCH(launch_gemm_rows(epi, norm, g, m->stream));
+  return QDEC_OK;
+}
+
+bool use_rows(const qdec_model* m, int T) {
+  const Dims& d = m->d;
+  return m->bf16 && rows_fits(T, d.H, d.qkv()) && rows_fits(T, d.NQ * d.D, d.H) && rows_fits(T, d.H, 2 * d.F) &&
+         rows_fits(T, d.F, d.H);
+}
+
+// The decoder layers over T <= 64 rows with the fused GEMMs: RMSNorm runs in
+// the prologue of the GEMM that consumes it (from sum-of-squares partials the
+// producer left in rSsq, nss of them per row), residual adds and SwiGLU in the
+// epilogues. Returns the partial count per row of the final X in *nss_out.
+template <typename RopeFn, typename AttnFn>
+int run_layers_rows(qdec_model* m, int T, float* X, float* QKV, float* Attn, float* Z, int nss, RopeFn rope,
+                    AttnFn attn, int* nss_out) {
+  const Dims& d = m->d;
+  hipStream_t st = m->stream;
+  RowsGemm g{};
+  g.M = T;
+  g.eps = d.eps;
+  g.P = m->rP;
+  g.cnt = m->rCnt;
+  const int nss_h = d.H / rows_tile_cols(d.H);
+  for (int l = 0; l < d.L; ++l) {
+    const LayerW& w = m->layers[l];
+    g.A = X, g.lda = d.H, g.ssq = m->rSsq, g.nss = nss, g.gain = w.in_norm;
+    g.W = (const uint16_t*)w.wqkv, g.K = d.H, g.N = d.qkv(), g.C = QKV, g.ldc = d.qkv();
+    if (int e = gemm_rows(m, EPI_STORE, true, g)) return e;
+    LAUNCH(rope(l));
+    LAUNCH(attn(l));
+    g.A = Attn, g.lda = d.NQ * d.D, g.W = (const uint16_t*)w.wo, g.K = d.NQ * d.D, g.N = d.H, g.C = X, g.ldc = d.H;
+    g.ssq_out = m->rSsq;
+    if (int e = gemm_rows(m, EPI_RESID, false, g)) return e;
+    g.A = X, g.lda = d.H, g.ssq = m->rSsq, g.nss = nss_h, g.gain = w.post_norm;
+    g.W = (const uint16_t*)w.wgu, g.K = d.H, g.N = 2 * d.F, g.C = Z, g.ldc = d.F;
+    if (int e = gemm_rows(m, EPI_SWIGLU, true, g)) return e;
+    g.A = Z, g.lda = d.F, g.W = (const uint16_t*)w.wd, g.K = d.F, g.N = d.H, g.C = X, g.ldc = d.H;
+    g.ssq_out = m->rSsq;
+    if (int e = gemm_rows(m, EPI_RESID, false, g)) return e;
+    nss = nss_h;
+  }
+  *nss_out = nss;
+  return QDEC_OK;
+}
+
+// The decoder layers over T activation rows held in X (fp32 [T, H]), one
+// layer after another (transcribe.cpp "Forward map - funasr_nano", table
+// "LLM decoder"). rope(l) applies QK-norm + RoPE and appends K/V of layer l;
+// attn(l) writes the attention output rows into Attn.
+template <typename RopeFn, typename AttnFn>
+int run_layers(qdec_model* m, int T, float* X, float* QKV, float* Attn, float* Z, void* A0, void* A1, float* part,
+               size_t part_cap, RopeFn rope, AttnFn attn) {
+  const Dims& d = m->d;
+  hipStream_t st = m->stream;
+  const bool bf = m->bf16;
+  auto norm_in = [&](const float* src, int K, const float* gain) -> hipError_t {
+    if (bf) return launch_rms_split(src, T, K, gain, d.eps, (uint16_t*)A0, (uint16_t*)A1, st);
+    return launch_rms_apply(src, T, K, gain, d.eps, (float*)A0, st);
+  };
+  for (int l = 0; l < d.L; ++l) {
+    const LayerW& w = m->layers[l];
+    LAUNCH(norm_in(X, d.H, w.in_norm));
+    LAUNCH(launch_gemm(bf, EPI_STORE, A0, A1, T, d.H, w.wqkv, d.qkv(), QKV, d.qkv(), st, part, part_cap));
+    LAUNCH(rope(l));
+    LAUNCH(attn(l));
+    LAUNCH(norm_in(Attn, d.NQ * d.D, nullptr));
+    LAUNCH(launch_gemm(bf, EPI_RESID, A0, A1, T, d.NQ * d.D, w.wo, d.H, X, d.H, st, part, part_cap));
+    LAUNCH(norm_in(X, d.H, w.post_norm));
+    LAUNCH(launch_gemm(bf, EPI_SWIGLU, A0, A1, T, d.H, w.wgu, 2 * d.F, Z, d.F, st, part, part_cap));
+    LAUNCH(norm_in(Z, d.F, nullptr));
+    LAUNCH(launch_gemm(bf, EPI_RESID, A0, A1, T, d.F, w.wd, d.H, X, d.H, st, part, part_cap));
+  }
+  return QDEC_OK;
+}
+
+// One decode step for n states at once: every weight is read once for all n
+// rows; attention runs per row over that state's own pages.
+int run_decode_batch(qdec_state* const* states, int n, const int32_t* tokens, float* logits, int32_t* argmax) {
+  qdec_model* m = states[0]->m;
+  const Dims& d = m->d;
+  hipStream_t st = m->stream;
+  BatchRows rows{};
+  rows.n = n;
+  int longest = 0;
+  for (int i = 0; i < n; ++i) {
+    rows.tok[i] = tokens[i];
+    rows.pos[i] = states[i]->n_past;
+    rows.pt[i] = states[i]->pt_dev;
+    longest = std::max(longest, rows.pos[i] + 1);
+  }
+  const int nsplit = (longest + kAttnChunk - 1) / kAttnChunk;
+  if (int e = ensure_batch(m, nsplit)) return e;
+  if (__atomic_load_n(m->err_host, __ATOMIC_ACQUIRE))
+    return fail(QDEC_E_DEVICE, "an earlier launch hit its time limit; the model must be recreated");
+  const bool fused = use_rows(m, n);
+  if (fused) {
+    if (int e = ensure_rows(m)) return e;
+  }
+  float* lg = logits ? logits : m->bLogits;
+  LAUNCH(launch_reset_keys(m->bKeys, n, st));
+  LAUNCH(launch_embed_rows(d, m->bf16, m->embed, rows, m->bX, fused ? m->rSsq : nullptr, st));
+  auto rope = [&](int l) {
+    const LayerW& w = m->layers[l];
+    return launch_qk_rope_rows(d, m->bQKV, rows, w.q_norm, w.k_norm, m->rope_cos, m->rope_sin, l, st);
+  };
+  auto attn = [&](int l) { return launch_attn_rows(d, m->bQKV, rows, l, nsplit, m->bAttnPart, m->bAttn, st); };
+  if (fused) {
+    int nss = 1;
+    if (int e = run_layers_rows(m, n, m->bX, m->bQKV, m->bAttn, m->bZ, 1, rope, attn, &nss)) return e;
+    if (rows_fits(n, d.H, d.V)) {
+      RowsGemm g{};
+      g.A = m->bX, g.lda = d.H, g.ssq = m->rSsq, g.nss = nss, g.gain = m->final_norm, g.eps = d.eps;
+      g.W = (const uint16_t*)m->embed, g.M = n, g.K = d.H, g.N = d.V, g.P = m->rP, g.cnt = m->rCnt;
+      g.C = logits, g.ldc = d.V, g.keys = m->bKeys;
+      if (int e = gemm_rows(m, EPI_HEAD, true, g)) return e;
+      LAUNCH(launch_argmax_final(m->bKeys, n, argmax ? argmax : m->bTok, st));
+      return QDEC_OK;
+    }
+  } else if (int e = run_layers(m, n, m->bX, m->bQKV, m->bAttn, m->bZ, m->bA0, m->bA1, m->bPart, m->b_part_cap,
+                                rope, attn)) {
+    return e;
+  }
+  if (m->bf16)
+    LAUNCH(launch_rms_split(m->bX, n, d.H, m->final_norm, d.eps, (uint16_t*)m->bA0, (uint16_t*)m->bA1, st));
+  else
+    LAUNCH(launch_rms_apply(m->bX, n, d.H, m->final_norm, d.eps, (float*)m->bA0, st));
+  LAUNCH(launch_gemm(m->bf16, EPI_STORE, m->bA0, m->bA1, n, d.H, m->embed, d.V, lg, d.V, st, m->bPart,
+                     m->b_part_cap));
+  LAUNCH(launch_argmax_rows(lg, n, d.V, m->bKeys, st));
+  LAUNCH(launch_argmax_final(m->bKeys, n, argmax ? argmax : m->bTok, st));
+  return QDEC_OK;
+}
+
 int run_prefill(qdec_state* s, int T, const float* audio, int a0, int La, float* logits, int32_t* argmax) {
   qdec_model* m = s->m;
   const Dims& d = m->d;
   hipStream_t st = m->stream;
   const bool bf = m->bf16;
   LAUNCH(launch_reset_keys(m->keys, 1, st));
-  LAUNCH(launch_embed_prefill(d, bf, m->embed, m->p_ids, T, audio, a0, La, m->pX, st));
-  auto norm_in = [&](const float* X, int K, const float* gain) -> hipError_t {
-    if (bf) return launch_rms_split(X, T, K, gain, d.eps, (uint16_t*)m->pA0, (uint16_t*)m->pA1, st);
-    return launch_rms_apply(X, T, K, gain, d.eps, (float*)m->pA0, st);
-  };
-  for (int l = 0; l < d.L; ++l) {
+  if (__atomic_load_n(m->err_host, __ATOMIC_ACQUIRE))
+    return fail(QDEC_E_DEVICE, "an earlier launch hit its time limit; the model must be recreated");
+  const bool fused = use_rows(m, T);
+  if (fused) {
+    if (int e = ensure_rows(m)) return e;
+  }
+  LAUNCH(launch_embed_prefill(d, bf, m->embed, m->p_ids, T, audio, a0, La, m->pX, fused ? m->rSsq : nullptr, st));
+  auto rope = [&](int l) {
     const LayerW& w = m->layers[l];
-    LAUNCH(norm_in(m->pX, d.H, w.in_norm));
-    LAUNCH(launch_gemm(bf, EPI_STORE, m->pA0, m->pA1, T, d.H, w.wqkv, d.qkv(), m->pQKV, d.qkv(), st, m->pPart,
-                            m->part_cap));
-    LAUNCH(launch_qk_rope_append(d, m->pQKV, T, 0, w.q_norm, w.k_norm, m->rope_cos, m->rope_sin, s->pt_dev, l,
-                                 st));
-    LAUNCH(launch_attn_prefill(d, m->pQKV, T, m->pAttn, st));
-    LAUNCH(norm_in(m->pAttn, d.NQ * d.D, nullptr));
-    LAUNCH(launch_gemm(bf, EPI_RESID, m->pA0, m->pA1, T, d.NQ * d.D, w.wo, d.H, m->pX, d.H, st, m->pPart,
-                            m->part_cap));
-    LAUNCH(norm_in(m->pX, d.H, w.post_norm));
-    LAUNCH(launch_gemm(bf, EPI_SWIGLU, m->pA0, m->pA1, T, d.H, w.wgu, 2 * d.F, m->pZ, d.F, st, m->pPart,
-                            m->part_cap));
-    LAUNCH(norm_in(m->pZ, d.F, nullptr));
-    LAUNCH(launch_gemm(bf, EPI_RESID, m->pA0, m->pA1, T, d.F, w.wd, d.H, m->pX, d.H, st, m->pPart,
-                            m->part_cap));
+    return launch_qk_rope_append(d, m->pQKV, T, 0, w.q_norm, w.k_norm, m->rope_cos, m->rope_sin, s->pt_dev, l, st);
+  };
+  auto attn = [&](int) { return launch_attn_prefill(d, m->pQKV, T, m->pAttn, st); };
+  if (fused) {
+    int nss = 1;
+    if (int e = run_layers_rows(m, T, m->pX, m->pQKV, m->pAttn, m->pZ, 1, rope, attn, &nss)) return e;
+  } else if (int e = run_layers(m, T, m->pX, m->pQKV, m->pAttn, m->pZ, m->pA0, m->pA1, m->pPart, m->part_cap, rope,
+                                attn)) {
+    return e;
   }
   LAUNCH(launch_lm_head(d, bf, m->embed, m->pX + (size_t)(T - 1) * d.H, m->final_norm, logits, m->keys, st));
   LAUNCH(launch_argmax_final(m->keys, 1, argmax ? argmax : m->argmax_tmp, st));
@@ -705,13 +960,8 @@ int qdec_decode_batch(qdec_state* const* states, int32_t n, const int32_t* token
       return fail(QDEC_E_INVALID, "tokens[%d] = %d outside [0, %d)", i, tokens_host[i], m->d.V);
   }
   if (int e = check_outputs(m, n, logits_dev, argmax_dev)) return e;
-  for (int i = 0; i < n; ++i) {
-    qdec_state* s = states[i];
-    if (int e = run_decode(s, tokens_host[i], nullptr, s->n_past, 1,
-                           logits_dev ? logits_dev + (size_t)i * m->d.V : nullptr, argmax_dev ? argmax_dev + i : nullptr))
-      return e;
-    s->n_past += 1;
-  }
+  if (int e = run_decode_batch(states, n, tokens_host, logits_dev, argmax_dev)) return e;
+  for (int i = 0; i < n; ++i) states[i]->n_past += 1;
   return ok();
 }
 

@@ -45,25 +45,70 @@ __host__ __device__ inline size_t page_offset(const Dims& d, int layer, int kv, 
   return ((((size_t)layer * 2 + kv) * d.NKV + head) * kPage + slot) * d.D;
 }
 
-// ---- launchers (qdec_kernels.hip); all enqueue on `st`, return hipError_t
-hipError_t launch_embed_decode(const Dims& d, bool bf16, const void* E, int token, const int32_t* token_dev,
-                               float* x, unsigned long long* key, hipStream_t st);
-hipError_t launch_embed_prefill(const Dims& d, bool bf16, const void* E, const int32_t* ids, int T,
-                                const float* audio, int a0, int La, float* X, hipStream_t st);
+// Rows of a batched decode step, passed by value as a kernel argument: row r
+// is one state fed token tok[r] at position pos[r], its KV page table at
+// pt[r] (device).
+struct BatchRows {
+  int n;
+  int tok[kMaxBatch];
+  int pos[kMaxBatch];
+  const int64_t* pt[kMaxBatch];
+};
 
-enum Epi { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
-hipError_t launch_gemv(bool bf16, Epi epi, const void* W, int R, int K, const float* x, const float* gain,
-                       float eps, float* out, hipStream_t st);
+// ---- launchers (qdec_kernels.hip); all enqueue on `st`, return hipError_t
+// The embed launchers also write each row's sum of squares to ssq[row] when
+// ssq is set (the first layer's RMSNorm partials, one per row).
+hipError_t launch_embed_rows(const Dims& d, bool bf16, const void* E, const BatchRows& rows, float* X, float* ssq,
+                             hipStream_t st);
+hipError_t launch_embed_prefill(const Dims& d, bool bf16, const void* E, const int32_t* ids, int T,
+                                const float* audio, int a0, int La, float* X, float* ssq, hipStream_t st);
+
+enum Epi { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_HEAD = 3 };
+
+// Arguments of the fused small-M GEMM (gemm_rows_kernel): up to 64 fp32
+// activation rows against bf16 weights, optional RMSNorm prologue, split-K
+// reduced in a fixed order, epilogue per Epi.
+struct RowsGemm {
+  const float* A;               // activations [M, lda] (first K columns used)
+  int lda;
+  const float* ssq;             // NORM: per-row sum-of-squares partials [nss][M]
+  int nss;
+  const float* gain;            // NORM: gain [K]
+  float eps;
+  const uint16_t* W;            // [N, K]
+  int M, K, N;
+  int KC;                       // set by the launcher
+  unsigned long long* P;        // split-K partial words (rows_partial_floats of them)
+  unsigned* cnt;                // arrival counters, zero between launches (rows_counters)
+  unsigned tag;                 // nonzero, differs from every tag still held in P
+  int* err;                     // set to 1 if a partial never became visible (host-mapped)
+  float* C;                     // output; SWIGLU: [M, N/2]; HEAD: logits or null
+  int ldc;
+  float* ssq_out;               // RESID: [N / rows_tile_cols(N)][M]
+  unsigned long long* keys;     // HEAD: argmax key per row
+};
+bool rows_fits(int M, int K, int N);
+int rows_tile_cols(int N);
+size_t rows_partial_floats(int M, int K, int N);
+int rows_counters(int K, int N);
+hipError_t launch_gemm_rows(Epi epi, bool norm, const RowsGemm& g, hipStream_t st);
 hipError_t launch_lm_head(const Dims& d, bool bf16, const void* E, const float* x, const float* gain,
                           float* logits, unsigned long long* key, hipStream_t st);
 hipError_t launch_argmax_final(const unsigned long long* key, int n, int32_t* out, hipStream_t st);
 hipError_t launch_reset_keys(unsigned long long* key, int n, hipStream_t st);
+// key[r] = max(key[r], argmax key of logits row r), r < n
+hipError_t launch_argmax_rows(const float* logits, int n, int V, unsigned long long* key, hipStream_t st);
 
 hipError_t launch_qk_rope_append(const Dims& d, float* qkv, int T, int pos0, const float* q_norm,
                                  const float* k_norm, const float* rope_cos, const float* rope_sin,
                                  const int64_t* page_table, int layer, hipStream_t st);
-hipError_t launch_attn_decode(const Dims& d, const float* q, int n, const int64_t* page_table, int layer,
-                              float* partial, float* out, hipStream_t st);
+hipError_t launch_qk_rope_rows(const Dims& d, float* qkv, const BatchRows& rows, const float* q_norm,
+                               const float* k_norm, const float* rope_cos, const float* rope_sin, int layer,
+                               hipStream_t st);
+// partial holds rows.n * NQ * nsplit * (D + 2) floats; nsplit * kAttnChunk
+// must cover the longest row (pos + 1)
+hipError_t launch_attn_rows(const Dims& d, const float* qkv, const BatchRows& rows, int layer, int nsplit,
+                            float* partial, float* out, hipStream_t st);
 hipError_t launch_attn_prefill(const Dims& d, const float* qkv, int T, float* out, hipStream_t st);
 
 hipError_t launch_rms_split(const float* X, int T, int K, const float* gain, float eps, uint16_t* hi,

@@ -1,16 +1,19 @@
-// HIP kernels for the Qwen3 KV-cache decoder on gfx950 (CDNA4, wave64).
+// HIP kernels for the Qwen3 KV-cache decoder on gfx950 (CDNA4, wave64):
+// prefill and batched decode run layer by layer through these kernels; the
+// single-state decode step is the persistent kernel of qdec_decode.hip.
 //
 // Step map (transcribe.cpp "Forward map - funasr_nano", table "LLM decoder";
 // NCNN "Qwen3ASR ncnn多平台移植", section 5):
-//   embed + audio-row override   -> embed_decode_kernel / embed_prefill_kernel
-//   rms_norm + Q/K/V projection  -> gemv_kernel (decode), rms_split + gemm (prefill)
-//   per-head Q/K-RMSNorm + NeoX RoPE + KV append -> qk_rope_append_kernel
-//   causal GQA attention         -> attn_decode_kernel + attn_combine_kernel,
+//   embed + audio-row override   -> embed_prefill_kernel / embed_rows_kernel
+//   rms_norm + Q/K/V projection  -> rms_split + gemm
+//   per-head Q/K-RMSNorm + NeoX RoPE + KV append -> qk_rope_append_kernel / qk_rope_rows_kernel
+//   causal GQA attention         -> attn_rows_kernel + attn_combine_rows_kernel,
 //                                   attn_prefill_kernel
-//   O projection + residual      -> gemv / gemm with the residual epilogue
-//   rms_norm + gate_up + SiLU*up -> gemv / gemm with the SwiGLU epilogue
-//   down projection + residual   -> gemv / gemm with the residual epilogue
-//   final rms_norm + tied head + greedy argmax -> lm_head_kernel + argmax_final_kernel
+//   O projection + residual      -> gemm with the residual epilogue
+//   rms_norm + gate_up + SiLU*up -> gemm with the SwiGLU epilogue
+//   down projection + residual   -> gemm with the residual epilogue
+//   final rms_norm + tied head + greedy argmax -> lm_head_kernel (one row) or gemm +
+//                                   argmax_rows_kernel (batch), then argmax_final_kernel
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -107,121 +110,52 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, int idx) {
 // ------------------------------------------------------------------ embed
 
 template <typename WT>
-__global__ __launch_bounds__(256) void embed_decode_kernel(const WT* __restrict__ E, int H, int V, int token,
-                                                            const int32_t* __restrict__ token_dev,
-                                                            float* __restrict__ x, unsigned long long* key) {
-  int t = token_dev ? token_dev[0] : token;
-  t = t < 0 ? 0 : (t >= V ? V - 1 : t);
-  const WT* row = E + (size_t)t * H;
-  for (int i = threadIdx.x; i < H; i += blockDim.x) x[i] = load_w(row, i);
-  if (threadIdx.x == 0 && key) *key = 0ull;
-}
-
-template <typename WT>
 __global__ __launch_bounds__(256) void embed_prefill_kernel(const WT* __restrict__ E, int H,
                                                              const int32_t* __restrict__ ids,
                                                              const float* __restrict__ audio, int a0, int La,
-                                                             float* __restrict__ X) {
+                                                             float* __restrict__ X, float* __restrict__ ssq) {
+  __shared__ float red[8];
   const int t = blockIdx.x;
   float* out = X + (size_t)t * H;
+  float ss = 0.f;
   if (t >= a0 && t < a0 + La) {
     const float* src = audio + (size_t)(t - a0) * H;
-    for (int i = threadIdx.x; i < H; i += blockDim.x) out[i] = src[i];
+    for (int i = threadIdx.x; i < H; i += blockDim.x) {
+      const float v = src[i];
+      out[i] = v;
+      ss = fmaf(v, v, ss);
+    }
   } else {
     const WT* row = E + (size_t)ids[t] * H;
-    for (int i = threadIdx.x; i < H; i += blockDim.x) out[i] = load_w(row, i);
+    for (int i = threadIdx.x; i < H; i += blockDim.x) {
+      const float v = load_w(row, i);
+      out[i] = v;
+      ss = fmaf(v, v, ss);
+    }
+  }
+  if (ssq) {
+    ss = block_sum(ss, red);
+    if (threadIdx.x == 0) ssq[t] = ss;
   }
 }
 
-// ------------------------------------------------------------------- GEMV
-// y[r] = sum_k W[r, k] * xin[k] for one activation row; xin optionally
-// RMS-normalised with `gain` first. Each wave owns ROWS consecutive rows; each
-// lane reads 16-byte weight chunks c = lane + 64 j. 4 waves per block.
-
-template <typename WT, int ROWS, int KCH, int EPI>
-__global__ __launch_bounds__(256) void gemv_kernel(const WT* __restrict__ W, int R, int K,
-                                                    const float* __restrict__ xin, const float* __restrict__ gain,
-                                                    float eps, float* __restrict__ out) {
-  extern __shared__ float smem[];
-  float* xs = smem;         // K floats
-  float* red = smem + K;    // 64 floats scratch
-  constexpr int VN = Chunk<WT>::N;
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-
-  float inv = 1.f;
-  if (gain) {
-    float ss = 0.f;
-    for (int i = threadIdx.x; i < K; i += blockDim.x) {
-      float v = xin[i];
-      ss = fmaf(v, v, ss);
-    }
+// One row per state of a batched decode step: X[r] = E[tok[r]].
+template <typename WT>
+__global__ __launch_bounds__(256) void embed_rows_kernel(const WT* __restrict__ E, int H, BatchRows rows,
+                                                          float* __restrict__ X, float* __restrict__ ssq) {
+  __shared__ float red[8];
+  const int r = blockIdx.x;
+  const WT* src = E + (size_t)rows.tok[r] * H;
+  float* out = X + (size_t)r * H;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < H; i += blockDim.x) {
+    const float v = load_w(src, i);
+    out[i] = v;
+    ss = fmaf(v, v, ss);
+  }
+  if (ssq) {
     ss = block_sum(ss, red);
-    inv = 1.f / sqrtf(ss / (float)K + eps);
-    for (int i = threadIdx.x; i < K; i += blockDim.x) xs[i] = xin[i] * inv * gain[i];
-  } else {
-    for (int i = threadIdx.x; i < K; i += blockDim.x) xs[i] = xin[i];
-  }
-  __syncthreads();
-
-  const int r0 = (blockIdx.x * 4 + wave) * ROWS;
-  const int nch = K / VN;
-  Chunk<WT> w[KCH][ROWS];
-#pragma unroll
-  for (int j = 0; j < KCH; ++j) {
-    const int c = lane + kWave * j;
-#pragma unroll
-    for (int r = 0; r < ROWS; ++r) {
-      if (c < nch && r0 + r < R) w[j][r].load(W + (size_t)(r0 + r) * K + (size_t)c * VN);
-    }
-  }
-  float acc[ROWS];
-#pragma unroll
-  for (int r = 0; r < ROWS; ++r) acc[r] = 0.f;
-#pragma unroll
-  for (int j = 0; j < KCH; ++j) {
-    const int c = lane + kWave * j;
-    if (c < nch) {
-      float xv[VN];
-#pragma unroll
-      for (int i = 0; i < VN; ++i) xv[i] = xs[c * VN + i];
-#pragma unroll
-      for (int r = 0; r < ROWS; ++r)
-        if (r0 + r < R) acc[r] += w[j][r].dot(xv);
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < ROWS; ++r) acc[r] = wave_sum(acc[r]);
-
-  if (EPI == EPI_SWIGLU) {
-    // block rows = 4 * ROWS = 16 = one interleave group: 8 gate rows then 8 up rows
-    __syncthreads();
-    if (lane < ROWS) {
-      float v = acc[0];
-#pragma unroll
-      for (int r = 1; r < ROWS; ++r)
-        if (lane == r) v = acc[r];
-      red[wave * ROWS + lane] = v;
-    }
-    __syncthreads();
-    if (threadIdx.x < kGuGroup) {
-      const float g = red[threadIdx.x], u = red[kGuGroup + threadIdx.x];
-      const int grp = blockIdx.x;  // one group per block
-      if ((grp + 1) * 2 * kGuGroup <= R) out[grp * kGuGroup + threadIdx.x] = g / (1.f + expf(-g)) * u;
-    }
-  } else {
-    if (lane < ROWS) {
-      float v = acc[0];
-#pragma unroll
-      for (int r = 1; r < ROWS; ++r)
-        if (lane == r) v = acc[r];
-      const int row = r0 + lane;
-      if (row < R) {
-        if (EPI == EPI_RESID)
-          out[row] += v;
-        else
-          out[row] = v;
-      }
-    }
+    if (threadIdx.x == 0) ssq[r] = ss;
   }
 }
 
@@ -297,6 +231,30 @@ __global__ void argmax_final_kernel(const unsigned long long* key, int n, int32_
   if (i < n) out[i] = (int32_t)(0xFFFFFFFFu - (uint32_t)(key[i] & 0xFFFFFFFFull));
 }
 
+// key[r] = max over v of argmax_key(logits[r][v], v); grid (chunks, rows).
+__global__ __launch_bounds__(256) void argmax_rows_kernel(const float* __restrict__ logits, int V,
+                                                           unsigned long long* key) {
+  __shared__ unsigned long long wbest[4];
+  const int r = blockIdx.y;
+  const float* lr = logits + (size_t)r * V;
+  unsigned long long best = 0ull;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < V; i += gridDim.x * blockDim.x) {
+    const unsigned long long k = argmax_key(lr[i], i);
+    best = k > best ? k : best;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const unsigned long long k = __shfl_xor(best, o, kWave);
+    best = k > best ? k : best;
+  }
+  if (threadIdx.x % kWave == 0) wbest[threadIdx.x / kWave] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < (int)(blockDim.x / kWave); ++w) best = wbest[w] > best ? wbest[w] : best;
+    atomicMax(key + r, best);
+  }
+}
+
 __global__ void reset_keys_kernel(unsigned long long* key, int n) {
   const int i = threadIdx.x;
   if (i < n) key[i] = 0ull;
@@ -308,18 +266,15 @@ __global__ void reset_keys_kernel(unsigned long long* key, int n) {
 // half pair (l, l + D/2). Q and K are rewritten in place (post-RoPE); K and V
 // of position pos0 + row go to the paged cache.
 
-__global__ __launch_bounds__(64) void qk_rope_append_kernel(float* __restrict__ qkv, int ld, int pos0, int NQ,
-                                                             int NKV, int D, int L, float eps,
-                                                             const float* __restrict__ q_norm,
-                                                             const float* __restrict__ k_norm,
-                                                             const float* __restrict__ rcos,
-                                                             const float* __restrict__ rsin,
-                                                             const int64_t* __restrict__ page_table, int layer) {
-  const int row = blockIdx.y, head = blockIdx.x, lane = threadIdx.x;
+__device__ __forceinline__ void qk_rope_row(float* __restrict__ qrow, int head, int pos, int NQ, int NKV, int D,
+                                            int L, float eps, const float* __restrict__ q_norm,
+                                            const float* __restrict__ k_norm, const float* __restrict__ rcos,
+                                            const float* __restrict__ rsin, const int64_t* __restrict__ page_table,
+                                            int layer) {
+  const int lane = threadIdx.x;
   const int half = D / 2;
-  const int pos = pos0 + row;
   const bool is_q = head < NQ;
-  float* vec = qkv + (size_t)row * ld + (size_t)head * D;  // q heads then k heads are contiguous
+  float* vec = qrow + (size_t)head * D;  // q heads then k heads are contiguous
   const float* g = is_q ? q_norm : k_norm;
   float a = 0.f, b = 0.f;
   if (lane < half) {
@@ -342,7 +297,7 @@ __global__ __launch_bounds__(64) void qk_rope_append_kernel(float* __restrict__ 
       const int slot = pos % kPage;
       float* kd = page + page_offset(d, layer, 0, kh, slot);
       float* vd = page + page_offset(d, layer, 1, kh, slot);
-      const float* vs = qkv + (size_t)row * ld + (size_t)(NQ + NKV + kh) * D;
+      const float* vs = qrow + (size_t)(NQ + NKV + kh) * D;
       kd[lane] = ra;
       kd[lane + half] = rb;
       vd[lane] = vs[lane];
@@ -351,24 +306,57 @@ __global__ __launch_bounds__(64) void qk_rope_append_kernel(float* __restrict__ 
   }
 }
 
-// ------------------------------------------------------- decode attention
-// Split-K flash decoding over the paged cache. Block = (kv head g, split s),
-// 4 waves. In a wave, lane = 8 * slot + part: 8 keys at a time, each key's
-// head_dim split over 8 lanes (DPL = D / 8 values per lane). All GROUP query
-// heads of the KV head share every K/V load. Output per (q head, split):
-// running max m, denominator l and the unnormalised D-vector.
+// Prompt rows: row t sits at position pos0 + t of one state.
+__global__ __launch_bounds__(64) void qk_rope_append_kernel(float* __restrict__ qkv, int ld, int pos0, int NQ,
+                                                             int NKV, int D, int L, float eps,
+                                                             const float* __restrict__ q_norm,
+                                                             const float* __restrict__ k_norm,
+                                                             const float* __restrict__ rcos,
+                                                             const float* __restrict__ rsin,
+                                                             const int64_t* __restrict__ page_table, int layer) {
+  const int row = blockIdx.y;
+  qk_rope_row(qkv + (size_t)row * ld, blockIdx.x, pos0 + row, NQ, NKV, D, L, eps, q_norm, k_norm, rcos, rsin,
+              page_table, layer);
+}
+
+// Batch rows: row r is its own state at its own position.
+__global__ __launch_bounds__(64) void qk_rope_rows_kernel(float* __restrict__ qkv, int ld, BatchRows rows, int NQ,
+                                                           int NKV, int D, int L, float eps,
+                                                           const float* __restrict__ q_norm,
+                                                           const float* __restrict__ k_norm,
+                                                           const float* __restrict__ rcos,
+                                                           const float* __restrict__ rsin, int layer) {
+  const int row = blockIdx.y;
+  qk_rope_row(qkv + (size_t)row * ld, blockIdx.x, rows.pos[row], NQ, NKV, D, L, eps, q_norm, k_norm, rcos, rsin,
+              rows.pt[row], layer);
+}
+
+// ------------------------------------------------ batched decode attention
+// Split-K flash decoding over the paged cache for the rows of a batched
+// decode step; row r is one state attending over positions [0, pos_r] (its
+// own K/V at pos_r already appended). Block = (kv head g, split s, row r),
+// 4 waves. Blocks are numbered kv head fastest, so with 8 KV heads every
+// block of head g runs on XCD g and rows that share prompt pages (cloned
+// states) read them through one L2. In a wave, lane = 8 * slot + part: 8 keys
+// at a time, each key's head_dim split over 8 lanes (DPL = D / 8 values per
+// lane), the next 8 keys in flight while the current ones are used. All GROUP
+// query heads of the KV head share every K/V load. Output per (row, q head,
+// split): running max m, denominator l and the unnormalised D-vector.
 
 template <int D, int GROUP>
-__global__ __launch_bounds__(256) void attn_decode_kernel(const float* __restrict__ q, int n, int NKV, int L,
-                                                           const int64_t* __restrict__ page_table, int layer,
-                                                           float* __restrict__ partial, int nsplit, float scale) {
+__global__ __launch_bounds__(256) void attn_rows_kernel(const float* __restrict__ qkv, int ld, BatchRows rows,
+                                                         int NKV, int L, int layer, float* __restrict__ partial,
+                                                         int nsplit, float scale) {
   constexpr int DPL = D / 8;
   __shared__ float sm_m[4][GROUP], sm_l[4][GROUP];
   __shared__ float sm_o[4][GROUP][D];
-  const int g = blockIdx.x, s = blockIdx.y;
+  const int g = blockIdx.x, s = blockIdx.y, r = blockIdx.z;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int slot = lane / 8, part = lane % 8;
+  const int n = rows.pos[r] + 1;
+  const int64_t* __restrict__ page_table = rows.pt[r];
   const int u0 = s * kAttnChunk, u1 = min(n, u0 + kAttnChunk);
+  const float* q = qkv + (size_t)r * ld;
   Dims d{L, 0, 0, NKV, D, 0, 0, 0.f};
 
   float qr[GROUP][DPL];
@@ -386,30 +374,34 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const float* __restric
     for (int i = 0; i < DPL; ++i) acc[h][i] = 0.f;
   }
 
-  for (int base = u0 + wave * 8; base < u1; base += 32) {
-    const int u = base + slot;
-    const bool valid = u < u1;
-    float kv[DPL], vv[DPL];
-    if (valid) {
-      const float* page = reinterpret_cast<const float*>(page_table[u / kPage]);
-      const float* kp = page + page_offset(d, layer, 0, g, u % kPage) + part * DPL;
-      const float* vp = page + page_offset(d, layer, 1, g, u % kPage) + part * DPL;
+  // key u clamped into [u0, u1): loads past the end repeat the last key and
+  // are masked out of the softmax
+  auto load = [&](int base, float (&kv)[DPL], float (&vv)[DPL]) {
+    const int u = min(base + slot, u1 - 1);
+    const float* page = reinterpret_cast<const float*>(page_table[u / kPage]);
+    const float* kp = page + page_offset(d, layer, 0, g, u % kPage) + part * DPL;
+    const float* vp = page + page_offset(d, layer, 1, g, u % kPage) + part * DPL;
 #pragma unroll
-      for (int i = 0; i < DPL; i += 4) {
-        const float4 a = *reinterpret_cast<const float4*>(kp + i);
-        kv[i] = a.x; kv[i + 1] = a.y; kv[i + 2] = a.z; kv[i + 3] = a.w;
-        const float4 b = *reinterpret_cast<const float4*>(vp + i);
-        vv[i] = b.x; vv[i + 1] = b.y; vv[i + 2] = b.z; vv[i + 3] = b.w;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) kv[i] = vv[i] = 0.f;
+    for (int i = 0; i < DPL; i += 4) {
+      const float4 a = *reinterpret_cast<const float4*>(kp + i);
+      kv[i] = a.x; kv[i + 1] = a.y; kv[i + 2] = a.z; kv[i + 3] = a.w;
+      const float4 b = *reinterpret_cast<const float4*>(vp + i);
+      vv[i] = b.x; vv[i + 1] = b.y; vv[i + 2] = b.z; vv[i + 3] = b.w;
     }
+  };
+
+  int base = u0 + wave * 8;
+  float kc[DPL], vc[DPL];
+  if (base < u1) load(base, kc, vc);
+  for (; base < u1; base += 32) {
+    float kn[DPL], vn[DPL];
+    load(base + 32, kn, vn);
+    const bool valid = base + slot < u1;
 #pragma unroll
     for (int h = 0; h < GROUP; ++h) {
       float sc = 0.f;
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) sc = fmaf(qr[h][i], kv[i], sc);
+      for (int i = 0; i < DPL; ++i) sc = fmaf(qr[h][i], kc[i], sc);
       sc += __shfl_xor(sc, 1, kWave);
       sc += __shfl_xor(sc, 2, kWave);
       sc += __shfl_xor(sc, 4, kWave);
@@ -425,8 +417,13 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const float* __restric
       ps += __shfl_xor(ps, 32, kWave);
       l[h] = l[h] * alpha + ps;
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) acc[h][i] = fmaf(p, vv[i], acc[h][i] * alpha);
+      for (int i = 0; i < DPL; ++i) acc[h][i] = fmaf(p, vc[i], acc[h][i] * alpha);
       m[h] = mn;
+    }
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) {
+      kc[i] = kn[i];
+      vc[i] = vn[i];
     }
   }
   // sum the 8 key slots (same running max within the wave)
@@ -455,6 +452,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const float* __restric
   }
   __syncthreads();
   // combine the 4 waves; thread t handles (head h, dim i) pairs
+  const int NQ = NKV * GROUP;
   for (int idx = threadIdx.x; idx < GROUP * D; idx += blockDim.x) {
     const int h = idx / D, i = idx % D;
     float M = -INFINITY;
@@ -465,7 +463,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const float* __restric
       o = fmaf(f, sm_o[w][h][i], o);
       lsum = fmaf(f, sm_l[w][h], lsum);
     }
-    float* dst = partial + ((size_t)(g * GROUP + h) * nsplit + s) * (D + 2);
+    float* dst = partial + (((size_t)r * NQ + g * GROUP + h) * nsplit + s) * (D + 2);
     dst[2 + i] = o;
     if (i == 0) {
       dst[0] = M;
@@ -474,11 +472,11 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const float* __restric
   }
 }
 
-// out[h*D + i] = sum_s e^{m_s - M} o_s[i] / sum_s e^{m_s - M} l_s
-__global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ partial, int nsplit, int D,
-                                                            float* __restrict__ out) {
-  const int h = blockIdx.x;
-  const float* p = partial + (size_t)h * nsplit * (D + 2);
+// out[r][h*D + i] = sum_s e^{m_s - M} o_s[i] / sum_s e^{m_s - M} l_s; grid (NQ, rows)
+__global__ __launch_bounds__(128) void attn_combine_rows_kernel(const float* __restrict__ partial, int nsplit,
+                                                                 int D, float* __restrict__ out, int ldo) {
+  const int h = blockIdx.x, r = blockIdx.y, NQ = gridDim.x;
+  const float* p = partial + ((size_t)r * NQ + h) * nsplit * (D + 2);
   float M = -INFINITY;
   for (int s = 0; s < nsplit; ++s) M = fmaxf(M, p[s * (D + 2)]);
   for (int i = threadIdx.x; i < D; i += blockDim.x) {
@@ -489,7 +487,7 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
       o = fmaf(f, p[s * (D + 2) + 2 + i], o);
       l = fmaf(f, p[s * (D + 2) + 1], l);
     }
-    out[(size_t)h * D + i] = o / l;
+    out[(size_t)r * ldo + (size_t)h * D + i] = o / l;
   }
 }
 
@@ -792,6 +790,259 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(const uint16_t* __restr
     }
 }
 
+// Small-M GEMM with fused prologue and epilogue, for up to 64 activation rows
+// (batched decode, short prompts): C[M, N] = op(A)[M, K] . W[N, K]^T.
+// op(A) is A itself or, with NORM, the RMS-normalised rows A * inv * gain,
+// inv = 1 / sqrt(sum(ssq partials of the row) / K + eps); the fp32 values
+// are split into bf16 hi + lo in registers for the MFMAs. Workgroup =
+// (16 NT output columns, K chunk of KC), 4 waves splitting the chunk; the
+// waves' sums meet in LDS. With several chunks, each workgroup stores its
+// partial tile, and the last to arrive at the column tile (arrival counter,
+// reset by that workgroup) adds all partials in chunk order, so the result
+// does not depend on scheduling. Epilogues:
+//   STORE   C = v
+//   RESID   C += v, and ssq_out[tile][row] = sum over the tile's columns of
+//           the new C^2 (the next NORM prologue's partials)
+//   SWIGLU  columns come as 8 gate then 8 up rows per group of 16; output j
+//           of group q is silu(gate) * up at C[row][8q + j]
+//   HEAD    C = v when C is set; keys[row] = max(keys[row], argmax key)
+template <int MT, int NT, bool NORM>
+struct RowsStep {
+  uint4 b[NT];
+  float4 a[MT][2];
+  float4 gv[2];
+  __device__ __forceinline__ void load(const uint16_t* const* wrow, const float* const* arow, const float* gk,
+                                       int k) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) b[j] = *reinterpret_cast<const uint4*>(wrow[j] + k);
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      a[i][0] = *reinterpret_cast<const float4*>(arow[i] + k);
+      a[i][1] = *reinterpret_cast<const float4*>(arow[i] + k + 4);
+    }
+    if (NORM) {
+      gv[0] = *reinterpret_cast<const float4*>(gk + k);
+      gv[1] = *reinterpret_cast<const float4*>(gk + k + 4);
+    }
+  }
+  __device__ __forceinline__ void mma(f32x4_t (&acc)[MT][NT], const float* inv) const {
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      float v[8] = {a[i][0].x, a[i][0].y, a[i][0].z, a[i][0].w, a[i][1].x, a[i][1].y, a[i][1].z, a[i][1].w};
+      if (NORM) {
+        const float g8[8] = {gv[0].x, gv[0].y, gv[0].z, gv[0].w, gv[1].x, gv[1].y, gv[1].z, gv[1].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = v[e] * inv[i] * g8[e];
+      }
+      bf16x8_t hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        hi[e] = (__bf16)v[e];
+        lo[e] = (__bf16)(v[e] - (float)hi[e]);
+      }
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, __builtin_bit_cast(bf16x8_t, b[j]), acc[i][j], 0, 0,
+                                                            0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, __builtin_bit_cast(bf16x8_t, b[j]), acc[i][j], 0, 0,
+                                                            0);
+      }
+    }
+  }
+};
+
+constexpr unsigned long long kRowsWaitTicks = 200000000ull;  // about 0.1 s of s_memtime
+
+template <int MT, int NT, int EPI, bool NORM>
+__global__ __launch_bounds__(256) void gemm_rows_kernel(RowsGemm g) {
+  constexpr int U = 4;                 // k-steps of loads in flight per wave
+  constexpr int S = MT * NT * 4;       // accumulator floats per lane
+  constexpr int TR = MT * 16, TC = NT * 16;
+  __shared__ float red[4][S][kWave];
+  __shared__ float tv[TR][TC + 1];
+  __shared__ int s_last;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int tile = blockIdx.x, c = blockIdx.y, nkc = gridDim.y;
+  const int n0 = tile * TC;
+  const int M = g.M, K = g.K;
+  const int kw = g.KC / 4;
+  const int kb = c * g.KC + wave * kw, ke = min(K, kb + kw);
+  const int r = lane % 16, kq = (lane / 16) * 8;
+
+  const uint16_t* wrow[NT];
+  const float* arow[MT];
+  float inv[MT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) wrow[j] = g.W + (size_t)(n0 + j * 16 + r) * K + kq;
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    // rows past M repeat row M - 1: an MFMA output row depends only on its
+    // own A row, and those rows are never stored
+    const int row = min(i * 16 + r, M - 1);
+    arow[i] = g.A + (size_t)row * g.lda + kq;
+    inv[i] = 1.f;
+    if (NORM) {
+      // the 4 lanes of a row split the partials, then meet by butterfly
+      // (every lane of the row ends with the same sum)
+      float ss = 0.f;
+#pragma unroll 8
+      for (int t = lane / 16; t < g.nss; t += 4) ss += g.ssq[(size_t)t * M + row];
+      ss += __shfl_xor(ss, 16, kWave);
+      ss += __shfl_xor(ss, 32, kWave);
+      inv[i] = 1.f / sqrtf(ss / (float)K + g.eps);
+    }
+  }
+  const float* gk = NORM ? g.gain + kq : nullptr;
+
+  f32x4_t acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  int k = kb;
+  for (; k + 32 * U <= ke; k += 32 * U) {
+    RowsStep<MT, NT, NORM> st[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) st[u].load(wrow, arow, gk, k + 32 * u);
+    // every load of the batch ahead of the first multiply
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) st[u].mma(acc, inv);
+  }
+  for (; k < ke; k += 32) {
+    RowsStep<MT, NT, NORM> st;
+    st.load(wrow, arow, gk, k);
+    st.mma(acc, inv);
+  }
+
+  // the 4 waves' sums, in wave order; thread (wave w, lane l) then owns the
+  // slots s = 4 q + w, s = 4 (i NT + j) + e <-> row 16 i + 4 (l / 16) + e,
+  // column 16 j + l % 16 of the tile
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[wave][(i * NT + j) * 4 + e][lane] = acc[i][j][e];
+  __syncthreads();
+  float v[MT * NT];
+#pragma unroll
+  for (int q = 0; q < MT * NT; ++q) {
+    const int sl = 4 * q + wave;
+    v[q] = ((red[0][sl][lane] + red[1][sl][lane]) + red[2][sl][lane]) + red[3][sl][lane];
+  }
+
+  if (nkc > 1) {
+    // Partials travel as 8-byte words (tag of this launch, value) written and
+    // read at device scope, so a word is either absent or whole, and no cache
+    // flush is needed. The workgroup that brings the tile's counter to nkc
+    // has seen every other workgroup's stores complete before their
+    // increments; it still checks each tag, waiting (bounded) for a word
+    // that is not yet visible.
+    unsigned long long* pt = g.P + (size_t)tile * S * kWave;
+    const size_t cstride = (size_t)gridDim.x * S * kWave;
+    const unsigned long long tag = (unsigned long long)g.tag << 32;
+#pragma unroll
+    for (int q = 0; q < MT * NT; ++q)
+      __hip_atomic_store(pt + c * cstride + (4 * q + wave) * kWave + lane, tag | __float_as_uint(v[q]),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // stores acknowledged before the barrier, so before the increment
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0)
+      s_last = __hip_atomic_fetch_add(g.cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               (unsigned)(nkc - 1);
+    __syncthreads();
+    if (!s_last) return;
+    // all chunks' words requested at once, 8 chunks per round (addresses
+    // clamped to the last chunk, surplus words ignored), then summed in
+    // chunk order
+    const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+    bool late = false;
+    float t[MT * NT];
+#pragma unroll
+    for (int q = 0; q < MT * NT; ++q) t[q] = 0.f;
+    for (int cb = 0; cb < nkc; cb += 8) {
+      unsigned long long w[MT * NT][8];
+#pragma unroll
+      for (int q = 0; q < MT * NT; ++q)
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          w[q][u] = __hip_atomic_load(pt + min(cb + u, nkc - 1) * cstride + (4 * q + wave) * kWave + lane,
+                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int q = 0; q < MT * NT; ++q)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int cc = cb + u;
+          if (cc < nkc) {
+            if (cc == c) {
+              t[q] += v[q];
+            } else {
+              while ((w[q][u] >> 32) != g.tag && !late) {
+                late = __builtin_amdgcn_s_memtime() - t0 > kRowsWaitTicks;
+                w[q][u] = __hip_atomic_load(pt + cc * cstride + (4 * q + wave) * kWave + lane, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+              }
+              t[q] += (w[q][u] >> 32) == g.tag ? __uint_as_float((unsigned)w[q][u]) : __builtin_nanf("");
+            }
+          }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < MT * NT; ++q) v[q] = t[q];
+    if (late) __hip_atomic_store(g.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    if (threadIdx.x == 0) __hip_atomic_store(g.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+#pragma unroll
+  for (int q = 0; q < MT * NT; ++q) {
+    const int sl = 4 * q + wave;
+    const int e = sl % 4, ij = sl / 4, i = ij / NT, j = ij % NT;
+    tv[16 * i + 4 * (lane / 16) + e][16 * j + lane % 16] = v[q];
+  }
+  __syncthreads();
+
+  if (EPI == EPI_SWIGLU) {
+    for (int idx = threadIdx.x; idx < TR * NT * 8; idx += blockDim.x) {
+      const int rt = idx / (NT * 8), o = idx % (NT * 8), j = o / 8, e = o % 8;
+      if (rt < M) g.C[(size_t)rt * g.ldc + (n0 / 16 + j) * 8 + e] = silu_mul(tv[rt][16 * j + e], tv[rt][16 * j + 8 + e]);
+    }
+    return;
+  }
+  if (EPI != EPI_HEAD || g.C) {
+    for (int idx = threadIdx.x; idx < TR * TC; idx += blockDim.x) {
+      const int rt = idx / TC, ct = idx % TC;
+      if (rt < M) {
+        float* dst = g.C + (size_t)rt * g.ldc + n0 + ct;
+        if (EPI == EPI_RESID) {
+          const float x = *dst + tv[rt][ct];
+          *dst = x;
+          tv[rt][ct] = x;
+        } else {
+          *dst = tv[rt][ct];
+        }
+      }
+    }
+  }
+  if (EPI == EPI_RESID) {
+    __syncthreads();
+    if (threadIdx.x < M) {
+      float ss = 0.f;
+      for (int ct = 0; ct < TC; ++ct) ss = fmaf(tv[threadIdx.x][ct], tv[threadIdx.x][ct], ss);
+      g.ssq_out[(size_t)tile * M + threadIdx.x] = ss;
+    }
+  }
+  if (EPI == EPI_HEAD && threadIdx.x < M) {
+    unsigned long long best = 0ull;
+    for (int ct = 0; ct < TC; ++ct) {
+      const unsigned long long kk = argmax_key(tv[threadIdx.x][ct], n0 + ct);
+      best = kk > best ? kk : best;
+    }
+    atomicMax(g.keys + threadIdx.x, best);
+  }
+}
+
 // Sums the nkc chunk partials of gemm_skinny_kernel (chunk order fixed) and
 // applies the epilogue. SwiGLU: columns come in groups of 16 (8 gate rows,
 // then the matching 8 up rows); output j of a row is silu(gate) * up of gate
@@ -892,63 +1143,22 @@ __global__ void to_f32_kernel(const WT* __restrict__ src, size_t n, float* __res
 
 // ================================================================ launchers
 
-hipError_t launch_embed_decode(const Dims& d, bool bf16, const void* E, int token, const int32_t* token_dev,
-                               float* x, unsigned long long* key, hipStream_t st) {
-  if (bf16)
-    embed_decode_kernel<uint16_t><<<1, 256, 0, st>>>((const uint16_t*)E, d.H, d.V, token, token_dev, x, key);
-  else
-    embed_decode_kernel<float><<<1, 256, 0, st>>>((const float*)E, d.H, d.V, token, token_dev, x, key);
-  return hipGetLastError();
-}
-
 hipError_t launch_embed_prefill(const Dims& d, bool bf16, const void* E, const int32_t* ids, int T,
-                                const float* audio, int a0, int La, float* X, hipStream_t st) {
+                                const float* audio, int a0, int La, float* X, float* ssq, hipStream_t st) {
   if (bf16)
-    embed_prefill_kernel<uint16_t><<<T, 256, 0, st>>>((const uint16_t*)E, d.H, ids, audio, a0, La, X);
+    embed_prefill_kernel<uint16_t><<<T, 256, 0, st>>>((const uint16_t*)E, d.H, ids, audio, a0, La, X, ssq);
   else
-    embed_prefill_kernel<float><<<T, 256, 0, st>>>((const float*)E, d.H, ids, audio, a0, La, X);
+    embed_prefill_kernel<float><<<T, 256, 0, st>>>((const float*)E, d.H, ids, audio, a0, La, X, ssq);
   return hipGetLastError();
 }
 
-template <typename WT, int ROWS, int EPI>
-static hipError_t gemv_dispatch(const WT* W, int R, int K, const float* x, const float* gain, float eps, float* out,
-                                hipStream_t st) {
-  constexpr int VN = Chunk<WT>::N;
-  const int kch = (K / VN + kWave - 1) / kWave;
-  const int blocks = (R + 4 * ROWS - 1) / (4 * ROWS);
-  const size_t sh = (size_t)(K + 64) * sizeof(float);
-#define QDEC_GEMV_CASE(KC)                                                                           \
-  case KC:                                                                                           \
-    gemv_kernel<WT, ROWS, KC, EPI><<<blocks, 256, sh, st>>>(W, R, K, x, gain, eps, out);             \
-    break;
-  switch (kch) {
-    QDEC_GEMV_CASE(1)
-    QDEC_GEMV_CASE(2)
-    QDEC_GEMV_CASE(3)
-    QDEC_GEMV_CASE(4)
-    QDEC_GEMV_CASE(5)
-    QDEC_GEMV_CASE(6)
-    QDEC_GEMV_CASE(8)
-    default:
-      return hipErrorInvalidValue;
-  }
-#undef QDEC_GEMV_CASE
+hipError_t launch_embed_rows(const Dims& d, bool bf16, const void* E, const BatchRows& rows, float* X, float* ssq,
+                             hipStream_t st) {
+  if (bf16)
+    embed_rows_kernel<uint16_t><<<rows.n, 256, 0, st>>>((const uint16_t*)E, d.H, rows, X, ssq);
+  else
+    embed_rows_kernel<float><<<rows.n, 256, 0, st>>>((const float*)E, d.H, rows, X, ssq);
   return hipGetLastError();
-}
-
-hipError_t launch_gemv(bool bf16, Epi epi, const void* W, int R, int K, const float* x, const float* gain,
-                       float eps, float* out, hipStream_t st) {
-  // SwiGLU needs 16 rows per block (one gate/up group): 4 waves x 4 rows.
-  if (bf16) {
-    const uint16_t* w = (const uint16_t*)W;
-    if (epi == EPI_STORE) return gemv_dispatch<uint16_t, 4, EPI_STORE>(w, R, K, x, gain, eps, out, st);
-    if (epi == EPI_RESID) return gemv_dispatch<uint16_t, 4, EPI_RESID>(w, R, K, x, gain, eps, out, st);
-    return gemv_dispatch<uint16_t, 4, EPI_SWIGLU>(w, R, K, x, gain, eps, out, st);
-  }
-  const float* w = (const float*)W;
-  if (epi == EPI_STORE) return gemv_dispatch<float, 4, EPI_STORE>(w, R, K, x, gain, eps, out, st);
-  if (epi == EPI_RESID) return gemv_dispatch<float, 4, EPI_RESID>(w, R, K, x, gain, eps, out, st);
-  return gemv_dispatch<float, 4, EPI_SWIGLU>(w, R, K, x, gain, eps, out, st);
 }
 
 hipError_t launch_lm_head(const Dims& d, bool bf16, const void* E, const float* x, const float* gain,
@@ -987,6 +1197,12 @@ hipError_t launch_argmax_final(const unsigned long long* key, int n, int32_t* ou
   return hipGetLastError();
 }
 
+hipError_t launch_argmax_rows(const float* logits, int n, int V, unsigned long long* key, hipStream_t st) {
+  const int chunks = std::max(1, std::min(64, (V + 4095) / 4096));
+  argmax_rows_kernel<<<dim3(chunks, n), 256, 0, st>>>(logits, V, key);
+  return hipGetLastError();
+}
+
 hipError_t launch_reset_keys(unsigned long long* key, int n, hipStream_t st) {
   reset_keys_kernel<<<1, 64, 0, st>>>(key, n);
   return hipGetLastError();
@@ -1001,20 +1217,28 @@ hipError_t launch_qk_rope_append(const Dims& d, float* qkv, int T, int pos0, con
   return hipGetLastError();
 }
 
-hipError_t launch_attn_decode(const Dims& d, const float* q, int n, const int64_t* page_table, int layer,
-                              float* partial, float* out, hipStream_t st) {
-  const int nsplit = (n + kAttnChunk - 1) / kAttnChunk;
+hipError_t launch_qk_rope_rows(const Dims& d, float* qkv, const BatchRows& rows, const float* q_norm,
+                               const float* k_norm, const float* rope_cos, const float* rope_sin, int layer,
+                               hipStream_t st) {
+  dim3 grid(d.NQ + d.NKV, rows.n);
+  qk_rope_rows_kernel<<<grid, 64, 0, st>>>(qkv, d.qkv(), rows, d.NQ, d.NKV, d.D, d.L, d.eps, q_norm, k_norm,
+                                           rope_cos, rope_sin, layer);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_rows(const Dims& d, const float* qkv, const BatchRows& rows, int layer, int nsplit,
+                            float* partial, float* out, hipStream_t st) {
   const int group = d.NQ / d.NKV;
   const float scale = 1.f / sqrtf((float)d.D);
-  dim3 grid(d.NKV, nsplit);
-#define QDEC_ATTN_CASE(DD, GG)                                                                             \
-  if (d.D == DD && group == GG) {                                                                          \
-    attn_decode_kernel<DD, GG><<<grid, 256, 0, st>>>(q, n, d.NKV, d.L, page_table, layer, partial, nsplit, scale); \
+  dim3 grid(d.NKV, nsplit, rows.n);
+#define QDEC_ATTN_CASE(DD, GG)                                                                      \
+  if (d.D == DD && group == GG) {                                                                   \
+    attn_rows_kernel<DD, GG><<<grid, 256, 0, st>>>(qkv, d.qkv(), rows, d.NKV, d.L, layer, partial, nsplit, \
+                                                   scale);                                          \
   } else
   QDEC_ATTN_CASE(128, 2)
   QDEC_ATTN_CASE(128, 1)
   QDEC_ATTN_CASE(128, 4)
-  QDEC_ATTN_CASE(128, 8)
   QDEC_ATTN_CASE(64, 2)
   QDEC_ATTN_CASE(32, 2)
   QDEC_ATTN_CASE(32, 1)
@@ -1023,7 +1247,7 @@ hipError_t launch_attn_decode(const Dims& d, const float* q, int n, const int64_
 #undef QDEC_ATTN_CASE
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  attn_combine_kernel<<<d.NQ, 128, 0, st>>>(partial, nsplit, d.D, out);
+  attn_combine_rows_kernel<<<dim3(d.NQ, rows.n), 128, 0, st>>>(partial, nsplit, d.D, out, d.NQ * d.D);
   return hipGetLastError();
 }
 
@@ -1094,17 +1318,95 @@ void launch_skinny(dim3 grid, const uint16_t* hi, const uint16_t* lo, int M, int
 
 size_t skinny_partial_floats(int M, int K, int N) { return (size_t)skinny_chunks(K, N) * M * N; }
 
+namespace {
+
+struct RowsPlan {
+  int nt, tiles, kc, nkc;
+};
+
+// 32 output columns per workgroup for wide outputs (each A load then feeds
+// two column tiles), 16 otherwise; K chunks (multiples of 128, one k-step of
+// 32 per wave at least) so that about 512 workgroups stream the weights
+RowsPlan rows_plan(int K, int N) {
+  RowsPlan p;
+  p.nt = N % 32 == 0 && N >= 2048 ? 2 : 1;
+  p.tiles = N / (16 * p.nt);
+  const int want = std::max(1, (512 + p.tiles - 1) / p.tiles);
+  p.kc = std::max(128, ((K + want - 1) / want + 127) / 128 * 128);
+  p.nkc = (K + p.kc - 1) / p.kc;
+  return p;
+}
+
+template <int MT, int NT>
+hipError_t rows_dispatch(Epi epi, bool norm, dim3 grid, const RowsGemm& g, hipStream_t st) {
+  if (epi == EPI_STORE && norm)
+    gemm_rows_kernel<MT, NT, EPI_STORE, true><<<grid, 256, 0, st>>>(g);
+  else if (epi == EPI_SWIGLU && norm)
+    gemm_rows_kernel<MT, NT, EPI_SWIGLU, true><<<grid, 256, 0, st>>>(g);
+  else if (epi == EPI_HEAD && norm)
+    gemm_rows_kernel<MT, NT, EPI_HEAD, true><<<grid, 256, 0, st>>>(g);
+  else if (epi == EPI_RESID && !norm)
+    gemm_rows_kernel<MT, NT, EPI_RESID, false><<<grid, 256, 0, st>>>(g);
+  else if (epi == EPI_STORE && !norm)
+    gemm_rows_kernel<MT, NT, EPI_STORE, false><<<grid, 256, 0, st>>>(g);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool rows_fits(int M, int K, int N) { return M >= 1 && M <= 64 && K >= 32 && K % 32 == 0 && N % 16 == 0; }
+
+int rows_tile_cols(int N) { return rows_plan(32, N).nt * 16; }
+
+size_t rows_partial_floats(int M, int K, int N) {
+  const RowsPlan p = rows_plan(K, N);
+  if (p.nkc == 1) return 0;
+  const int mt = (M + 15) / 16;
+  return (size_t)p.nkc * p.tiles * mt * p.nt * 4 * 64;  // 8-byte words
+}
+
+int rows_counters(int K, int N) {
+  const RowsPlan p = rows_plan(K, N);
+  return p.nkc == 1 ? 0 : p.tiles;
+}
+
+hipError_t launch_gemm_rows(Epi epi, bool norm, const RowsGemm& g0, hipStream_t st) {
+  if (!rows_fits(g0.M, g0.K, g0.N)) return hipErrorInvalidValue;
+  const RowsPlan p = rows_plan(g0.K, g0.N);
+  if (p.nkc > 1 && (!g0.P || !g0.cnt)) return hipErrorInvalidValue;
+  RowsGemm g = g0;
+  g.KC = p.kc;
+  const dim3 grid(p.tiles, p.nkc);
+  const int mt = (g.M + 15) / 16;
+#define QDEC_ROWS_CASE(MT)                                                        \
+  if (mt == MT) return p.nt == 2 ? rows_dispatch<MT, 2>(epi, norm, grid, g, st) \
+                                 : rows_dispatch<MT, 1>(epi, norm, grid, g, st);
+  QDEC_ROWS_CASE(1)
+  QDEC_ROWS_CASE(2)
+  QDEC_ROWS_CASE(3)
+  QDEC_ROWS_CASE(4)
+#undef QDEC_ROWS_CASE
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_gemm(bool bf16, Epi epi, const void* A0, const void* A1, int M, int K, const void* W, int N,
                        float* C, int ldc, hipStream_t st, float* part, size_t part_cap) {
-  if (bf16 && M >= 1 && M <= 64 && N % 16 == 0 && K % 32 == 0 && part &&
-      skinny_partial_floats(M, K, N) <= part_cap) {
-    const int nkc = skinny_chunks(K, N), KC = skinny_chunk_len(K, N), nt = skinny_nt(N);
+  const int nkc = skinny_chunks(K, N);
+  // a single chunk of a plain store needs no partials: the GEMM writes C
+  const bool direct = nkc == 1 && epi == EPI_STORE && ldc == N;
+  if (bf16 && M >= 1 && M <= 64 && N % 16 == 0 && K % 32 == 0 &&
+      (direct || (part && skinny_partial_floats(M, K, N) <= part_cap))) {
+    const int KC = skinny_chunk_len(K, N), nt = skinny_nt(N);
     const dim3 grid(N / (16 * nt), nkc);
     const uint16_t *hi = (const uint16_t*)A0, *lo = (const uint16_t*)A1, *w = (const uint16_t*)W;
+    float* P = direct ? C : part;
     if (nt == 2)
-      launch_skinny<2>(grid, hi, lo, M, K, w, N, KC, part, st);
+      launch_skinny<2>(grid, hi, lo, M, K, w, N, KC, P, st);
     else
-      launch_skinny<1>(grid, hi, lo, M, K, w, N, KC, part, st);
+      launch_skinny<1>(grid, hi, lo, M, K, w, N, KC, P, st);
+    if (direct) return hipGetLastError();
     const size_t n_out = (size_t)M * (epi == EPI_SWIGLU ? N / 2 : N);
     const unsigned blocks = (unsigned)((n_out + 255) / 256);
     if (epi == EPI_STORE)

@@ -100,3 +100,64 @@ def test_greedy_multi_step(name):
     # the argmax written is the token fed forward: check logits against the oracle step by step
     worst = check_steps(gpu, got_tokens, ref, fp32=not shape.bf16, label=name)
     print(name, worst)
+
+
+# Batched decode (NCNN page section 5: branches decode from clones of one
+# context): cloned states share the prompt's full pages, each row sits at its
+# own position (branch b first takes b single steps), and the batch steps run
+# through the layer-by-layer batch path. Every row must match the oracle's
+# independent decode of that branch.
+BATCH = {
+    # D=64: rows straddle the 256-position attention split and page ends
+    "d64_g2_b5": (MID["d64_g2"][0], 250, 17, 100, 5, 6),
+    # GQA 4, fp32 weights (vector GEMM path)
+    "d32_g4_f32_b3": (MID["d32_g4_f32"][0], 45, 3, 9, 3, 4),
+    # D=128 (0.6B head geometry), the full batch of 16 rows
+    "d128_g2_b16": (MID["d128_g2"][0], 77, 8, 20, 16, 3),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BATCH))
+def test_decode_batch_rows(name):
+    from qwen3_kv_cache_amd import qdec
+    from .gpu_harness import torch_dev
+    shape, T, a0, La, B, n = BATCH[name]
+    W, ids, audio, a0, _ = mid_workload(shape, 13, T, a0, La, 1)
+    pre = [synth.random_ids(300 + b, b, shape.vocab) for b in range(B)]      # single steps before the batch
+    feed = np.stack([synth.random_ids(400 + b, n, shape.vocab) for b in range(B)])  # [B, n] batch tokens
+    orc = oracle.Qwen3Oracle(oracle.OracleConfig.from_shape(shape), W.f32)
+    st0 = orc.new_state()
+    orc.prefill(st0, ids, audio, a0)
+    ref = np.zeros((n, B, shape.vocab))
+    for b in range(B):
+        sb = st0.clone()
+        for j, tok in enumerate(pre[b]):
+            orc.decode(sb, int(tok), T + j)
+        for s in range(n):
+            ref[s, b] = orc.decode(sb, int(feed[b, s]), T + len(pre[b]) + s)
+    torch, dev = torch_dev()
+    m = device_model(shape, W)
+    try:
+        base = qdec.qdec_state_create(m.handle, T + B + n)
+        audio_d = torch.from_numpy(audio).to(dev)
+        qdec.qdec_prefill(base, ids, T, audio_d.data_ptr(), a0, len(audio), None, None)
+        branches = [qdec.qdec_clone_state(base) for _ in range(B)]
+        qdec.qdec_state_destroy(base)
+        scratch = torch.zeros(shape.vocab, dtype=torch.float32, device=dev)
+        for b in range(B):
+            for j, tok in enumerate(pre[b]):
+                qdec.qdec_decode_step(branches[b], int(tok), T + j, scratch.data_ptr(), None)
+        logits = torch.full((n, B, shape.vocab), float("nan"), dtype=torch.float32, device=dev)
+        amax = torch.full((n, B), -1, dtype=torch.int32, device=dev)
+        print(f"[{name}] batch of {B} rows at positions {T}..{T + B - 1}, {n} steps", flush=True)
+        for s in range(n):
+            qdec.qdec_decode_batch(branches, feed[:, s], logits[s].data_ptr(), amax[s].data_ptr())
+        torch.cuda.synchronize()
+        for b, st in enumerate(branches):
+            assert qdec.qdec_state_pos(st) == T + b + n
+            qdec.qdec_state_destroy(st)
+    finally:
+        m.close()
+    L, A = logits.cpu().numpy(), amax.cpu().numpy()
+    for b in range(B):
+        check_steps(L[:, b], A[:, b], ref[:, b], fp32=not shape.bf16, label=f"{name} row {b}")
