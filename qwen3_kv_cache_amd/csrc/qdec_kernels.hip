@@ -591,6 +591,205 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const float* __restri
   }
 }
 
+// Causal GQA flash attention on the matrix cores, head_dim 128. Block = (64
+// query positions, kv head g), 4 waves; wave w owns positions q0 + 16 w + i
+// (i < 16) of all GROUP query heads of g. Per key tile of KT the block stages
+// K as [key][d] and V transposed as [d][key] in LDS, each as bf16 hi + lo
+// (hi = bf16(x), lo = bf16(x - hi)). Scores are computed transposed,
+// S^T = K Q^T, so that a lane holds the scores of one query (column l % 16)
+// for keys 16 j + 4 (l / 16) + e: that is both where the online softmax needs
+// them (row statistics are per lane, reduced over the 4 lanes of the query)
+// and, once exponentiated, the B operand of O^T = V^T P^T, whose k-slots are
+// taken as keys {4 (l / 16) + e} and {16 + 4 (l / 16) + e} of each 32-key
+// group (the A operand reads V^T at the same keys). Every product is the sum
+// of three bf16 MFMAs (hi hi, hi lo, lo hi), about 16 mantissa bits. Scores
+// are kept in base 2 (Q carries log2(e) / sqrt(D)), so the softmax uses the
+// hardware exp2.
+namespace fa {
+constexpr int D = 128;
+constexpr int QT = 64;          // query positions per block
+constexpr int KT = 32;          // keys per tile
+constexpr int KP = D + 8;       // bf16 pitch of a K row in LDS
+constexpr int VP = KT + 8;      // bf16 pitch of a V^T row in LDS
+constexpr int KB = KT / 16;     // 16-key blocks per tile
+constexpr int KH = KT / 32;     // 32-key groups per tile
+}  // namespace fa
+
+template <int GROUP>
+__global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* __restrict__ qkv, int T, int ld,
+                                                                 int NQ, int NKV, float* __restrict__ out, int ldo,
+                                                                 float qscale) {
+  using namespace fa;
+  __shared__ __bf16 Kh[KT * KP], Kl[KT * KP];
+  __shared__ __bf16 Vh[D * VP], Vl[D * VP];
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const int c16 = lane % 16, gq = lane / 16;
+  const int g = blockIdx.y;
+  // heavier (later) query tiles first
+  const int q0 = (gridDim.x - 1 - blockIdx.x) * QT;
+  const int qp = q0 + 16 * w + c16;           // this lane's query position
+  const int qrow = min(qp, T - 1);
+
+  // Q^T operands (B of S^T = K Q^T): lane supplies Q[query c16][32 s + 8 gq + i]
+  bf16x8_t qh[GROUP][4], ql[GROUP][4];
+#pragma unroll
+  for (int hh = 0; hh < GROUP; ++hh) {
+    const float* qsrc = qkv + (size_t)qrow * ld + (size_t)(g * GROUP + hh) * D + 8 * gq;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const float4 a = *reinterpret_cast<const float4*>(qsrc + 32 * st);
+      const float4 b = *reinterpret_cast<const float4*>(qsrc + 32 * st + 4);
+      const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = v[i] * qscale;
+        const __bf16 h = (__bf16)x;
+        qh[hh][st][i] = h;
+        ql[hh][st][i] = (__bf16)(x - (float)h);
+      }
+    }
+  }
+
+  float m[GROUP], lsum[GROUP];
+  f32x4_t acc[GROUP][D / 16];
+#pragma unroll
+  for (int hh = 0; hh < GROUP; ++hh) {
+    m[hh] = -INFINITY;
+    lsum[hh] = 0.f;
+#pragma unroll
+    for (int b = 0; b < D / 16; ++b) acc[hh][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const size_t koff = (size_t)NQ * D + (size_t)g * D;
+  const size_t voff = (size_t)(NQ + NKV) * D + (size_t)g * D;
+  const int last_key = min(T, q0 + QT) - 1;
+  for (int k0 = 0; k0 <= last_key; k0 += KT) {
+    __syncthreads();
+    {
+      // K: thread -> key t / 8, 16 columns from 16 (t % 8)
+      const int key = threadIdx.x / 8, d0 = 16 * (threadIdx.x % 8);
+      const float* src = qkv + (size_t)min(k0 + key, T - 1) * ld + koff + d0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 a = *reinterpret_cast<const float4*>(src + 4 * i);
+        const float v[4] = {a.x, a.y, a.z, a.w};
+        __bf16 h4[4], l4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          h4[e] = (__bf16)v[e];
+          l4[e] = (__bf16)(v[e] - (float)h4[e]);
+        }
+        *reinterpret_cast<uint2*>(&Kh[key * KP + d0 + 4 * i]) = __builtin_bit_cast(uint2, h4);
+        *reinterpret_cast<uint2*>(&Kl[key * KP + d0 + 4 * i]) = __builtin_bit_cast(uint2, l4);
+      }
+      // V^T: thread -> column d = t % 128, keys 16 (t / 128) + 0..15
+      const int d = threadIdx.x % D, kb = 16 * (threadIdx.x / D);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __bf16 h4[4], l4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = qkv[(size_t)min(k0 + kb + 4 * i + e, T - 1) * ld + voff + d];
+          h4[e] = (__bf16)v;
+          l4[e] = (__bf16)(v - (float)h4[e]);
+        }
+        *reinterpret_cast<uint2*>(&Vh[d * VP + kb + 4 * i]) = __builtin_bit_cast(uint2, h4);
+        *reinterpret_cast<uint2*>(&Vl[d * VP + kb + 4 * i]) = __builtin_bit_cast(uint2, l4);
+      }
+    }
+    __syncthreads();
+
+    // S^T tile: KB key blocks of 16 x this wave's 16 queries, per head
+    f32x4_t sc[GROUP][KB];
+#pragma unroll
+    for (int hh = 0; hh < GROUP; ++hh)
+#pragma unroll
+      for (int j = 0; j < KB; ++j) sc[hh][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KB; ++j)
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const int off = (16 * j + c16) * KP + 32 * st + 8 * gq;
+        const bf16x8_t kh = *reinterpret_cast<const bf16x8_t*>(&Kh[off]);
+        const bf16x8_t kl = *reinterpret_cast<const bf16x8_t*>(&Kl[off]);
+#pragma unroll
+        for (int hh = 0; hh < GROUP; ++hh) {
+          sc[hh][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qh[hh][st], sc[hh][j], 0, 0, 0);
+          sc[hh][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, qh[hh][st], sc[hh][j], 0, 0, 0);
+          sc[hh][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, ql[hh][st], sc[hh][j], 0, 0, 0);
+        }
+      }
+
+    // online softmax per head; P^T operands per 32-key group
+    bf16x8_t ph[GROUP][KH], pl[GROUP][KH];
+#pragma unroll
+    for (int hh = 0; hh < GROUP; ++hh) {
+      float mx = m[hh];
+#pragma unroll
+      for (int j = 0; j < KB; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = k0 + 16 * j + 4 * gq + e;
+          if (key > qp || key >= T) sc[hh][j][e] = -INFINITY;
+          mx = fmaxf(mx, sc[hh][j][e]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      // key 0 is visible to every query, so mx is finite from the first tile on
+      const float alpha = __builtin_amdgcn_exp2f(m[hh] - mx);
+      float ps = 0.f;
+#pragma unroll
+      for (int j = 0; j < KB; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p = __builtin_amdgcn_exp2f(sc[hh][j][e] - mx);
+          ps += p;
+          const __bf16 h = (__bf16)p;
+          ph[hh][j / 2][4 * (j % 2) + e] = h;
+          pl[hh][j / 2][4 * (j % 2) + e] = (__bf16)(p - (float)h);
+        }
+      ps += __shfl_xor(ps, 16, kWave);
+      ps += __shfl_xor(ps, 32, kWave);
+      lsum[hh] = lsum[hh] * alpha + ps;
+      m[hh] = mx;
+#pragma unroll
+      for (int b = 0; b < D / 16; ++b) acc[hh][b] *= alpha;
+    }
+
+    // O^T += V^T P^T: d block b, 32-key group c
+#pragma unroll
+    for (int b = 0; b < D / 16; ++b)
+#pragma unroll
+      for (int c = 0; c < KH; ++c) {
+        const int off = (16 * b + c16) * VP + 32 * c + 4 * gq;
+        const uint2 h0 = *reinterpret_cast<const uint2*>(&Vh[off]);
+        const uint2 h1 = *reinterpret_cast<const uint2*>(&Vh[off + 16]);
+        const uint2 l0 = *reinterpret_cast<const uint2*>(&Vl[off]);
+        const uint2 l1 = *reinterpret_cast<const uint2*>(&Vl[off + 16]);
+        const bf16x8_t vh = __builtin_bit_cast(bf16x8_t, make_uint4(h0.x, h0.y, h1.x, h1.y));
+        const bf16x8_t vl = __builtin_bit_cast(bf16x8_t, make_uint4(l0.x, l0.y, l1.x, l1.y));
+#pragma unroll
+        for (int hh = 0; hh < GROUP; ++hh) {
+          acc[hh][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vh, ph[hh][c], acc[hh][b], 0, 0, 0);
+          acc[hh][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vl, ph[hh][c], acc[hh][b], 0, 0, 0);
+          acc[hh][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vh, pl[hh][c], acc[hh][b], 0, 0, 0);
+        }
+      }
+  }
+
+  if (qp < T) {
+#pragma unroll
+    for (int hh = 0; hh < GROUP; ++hh) {
+      const float il = 1.f / lsum[hh];
+      float* dst = out + (size_t)qp * ldo + (size_t)(g * GROUP + hh) * D + 4 * gq;
+#pragma unroll
+      for (int b = 0; b < D / 16; ++b)
+        *reinterpret_cast<float4*>(dst + 16 * b) =
+            make_float4(acc[hh][b][0] * il, acc[hh][b][1] * il, acc[hh][b][2] * il, acc[hh][b][3] * il);
+    }
+  }
+}
+
 // ------------------------------------------------ prefill activations / GEMM
 // Activations are fp32; the bf16 MFMA consumes them as hi + lo bf16 pairs
 // (hi = bf16(v), lo = bf16(v - hi)), two MFMAs per tile, which keeps about 16
@@ -1254,6 +1453,15 @@ hipError_t launch_attn_rows(const Dims& d, const float* qkv, const BatchRows& ro
 hipError_t launch_attn_prefill(const Dims& d, const float* qkv, int T, float* out, hipStream_t st) {
   const int group = d.NQ / d.NKV;
   const float scale = 1.f / sqrtf((float)d.D);
+  if (d.D == fa::D && (group == 1 || group == 2)) {
+    dim3 grid((T + fa::QT - 1) / fa::QT, d.NKV);
+    const float qs = scale * 1.4426950408889634f;  // scores in base 2
+    if (group == 2)
+      attn_prefill_mfma_kernel<2><<<grid, 256, 0, st>>>(qkv, T, d.qkv(), d.NQ, d.NKV, out, d.NQ * d.D, qs);
+    else
+      attn_prefill_mfma_kernel<1><<<grid, 256, 0, st>>>(qkv, T, d.qkv(), d.NQ, d.NKV, out, d.NQ * d.D, qs);
+    return hipGetLastError();
+  }
 #define QDEC_PATTN_CASE(DD, GG)                                                                      \
   if (d.D == DD && group == GG) {                                                                    \
     dim3 grid((T + 64 / GG - 1) / (64 / GG), d.NKV);                                                \
