@@ -1274,6 +1274,116 @@ __global__ __launch_bounds__(256) void skinny_epilogue_kernel(const float* __res
   }
 }
 
+// Large-M GEMM (prefill): C[M, N] (+)= (Ahi + Alo)[M, K] . W[N, K]^T with
+// 128 x 128 output tiles and K steps of 32 staged in LDS (double buffered:
+// the next step's global loads are in flight while the current one is
+// multiplied). 4 waves in a 2 x 2 arrangement, each 64 x 64 = 4 x 4 MFMA
+// tiles of 16 x 16, two MFMAs (hi, lo) per tile and step. LDS rows are
+// padded to 80 bytes so the 16 rows an MFMA operand read touches fall in
+// distinct banks. Epilogues as in gemm_bf16x2_kernel.
+namespace tg {
+constexpr int BM = 128, BN = 128, BK = 32;
+constexpr int P = BK + 8;  // bf16 pitch of an LDS row
+}  // namespace tg
+
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint16_t* __restrict__ Ahi,
+                                                          const uint16_t* __restrict__ Alo, int M, int K,
+                                                          const uint16_t* __restrict__ W, int N,
+                                                          float* __restrict__ C, int ldc) {
+  using namespace tg;
+  __shared__ uint16_t sAh[2][BM * P], sAl[2][BM * P], sW[2][BN * P];
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const int c16 = lane % 16, gq = lane / 16;
+  const int wm = w / 2, wn = w % 2;
+  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+
+  // staging: 128 rows x 4 chunks of 16 bytes per matrix; thread t moves
+  // chunks t and t + 256 (rows t / 4 and t / 4 + 64, chunk t % 4)
+  const int srow = threadIdx.x / 4, skc = threadIdx.x % 4;
+  const size_t a0 = (size_t)min(m0 + srow, M - 1) * K + 8 * skc;
+  const size_t a1 = (size_t)min(m0 + srow + 64, M - 1) * K + 8 * skc;
+  const size_t w0 = (size_t)(n0 + srow) * K + 8 * skc;
+  const size_t w1 = (size_t)(n0 + srow + 64) * K + 8 * skc;
+  const int l0 = srow * P + 8 * skc, l1 = (srow + 64) * P + 8 * skc;
+  uint4 rh0, rh1, rl0, rl1, rw0, rw1;
+#define QDEC_TG_LOAD(k)                                         \
+  rh0 = *reinterpret_cast<const uint4*>(Ahi + a0 + (k));        \
+  rh1 = *reinterpret_cast<const uint4*>(Ahi + a1 + (k));        \
+  rl0 = *reinterpret_cast<const uint4*>(Alo + a0 + (k));        \
+  rl1 = *reinterpret_cast<const uint4*>(Alo + a1 + (k));        \
+  rw0 = *reinterpret_cast<const uint4*>(W + w0 + (k));          \
+  rw1 = *reinterpret_cast<const uint4*>(W + w1 + (k));
+#define QDEC_TG_STORE(buf)                                      \
+  *reinterpret_cast<uint4*>(&sAh[buf][l0]) = rh0;               \
+  *reinterpret_cast<uint4*>(&sAh[buf][l1]) = rh1;               \
+  *reinterpret_cast<uint4*>(&sAl[buf][l0]) = rl0;               \
+  *reinterpret_cast<uint4*>(&sAl[buf][l1]) = rl1;               \
+  *reinterpret_cast<uint4*>(&sW[buf][l0]) = rw0;                \
+  *reinterpret_cast<uint4*>(&sW[buf][l1]) = rw1;
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = K / BK;
+  QDEC_TG_LOAD(0)
+  QDEC_TG_STORE(0)
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) {
+      QDEC_TG_LOAD((kt + 1) * BK)
+    }
+    bf16x8_t ah[4], al[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int off = (wm * 64 + 16 * i + c16) * P + 8 * gq;
+      ah[i] = *reinterpret_cast<const bf16x8_t*>(&sAh[buf][off]);
+      al[i] = *reinterpret_cast<const bf16x8_t*>(&sAl[buf][off]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      b[j] = *reinterpret_cast<const bf16x8_t*>(&sW[buf][(wn * 64 + 16 * j + c16) * P + 8 * gq]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[i], b[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[i], b[j], acc[i][j], 0, 0, 0);
+      }
+    if (kt + 1 < nk) {
+      QDEC_TG_STORE(buf ^ 1)
+    }
+    __syncthreads();
+  }
+#undef QDEC_TG_LOAD
+#undef QDEC_TG_STORE
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + wn * 64 + 16 * j + c16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = m0 + wm * 64 + 16 * i + 4 * gq + e;
+        const float v = acc[i][j][e];
+        if (EPI == EPI_SWIGLU) {
+          const float u = __shfl_xor(v, 8, kWave);
+          if (c16 < kGuGroup && row < M) C[(size_t)row * ldc + (col / 16) * kGuGroup + c16] = silu_mul(v, u);
+        } else if (row < M) {
+          if (EPI == EPI_RESID)
+            C[(size_t)row * ldc + col] += v;
+          else
+            C[(size_t)row * ldc + col] = v;
+        }
+      }
+    }
+}
+
 // fp32 weights: C[M, N] (+)= A[M, K] . W[N, K]^T on the vector units.
 // Block 16 x 16 threads computes a 32 x 32 tile (2 x 2 per thread); K tiles of
 // 16 staged in LDS. For the SwiGLU epilogue the tile's columns hold whole
@@ -1623,6 +1733,17 @@ hipError_t launch_gemm(bool bf16, Epi epi, const void* A0, const void* A1, int M
       skinny_epilogue_kernel<EPI_RESID><<<blocks, 256, 0, st>>>(part, nkc, M, N, C, ldc);
     else
       skinny_epilogue_kernel<EPI_SWIGLU><<<blocks, 256, 0, st>>>(part, nkc, M, N, C, ldc);
+    return hipGetLastError();
+  }
+  if (bf16 && M > 64 && N % tg::BN == 0 && K % tg::BK == 0) {
+    const dim3 grid(N / tg::BN, (M + tg::BM - 1) / tg::BM);
+    const uint16_t *hi = (const uint16_t*)A0, *lo = (const uint16_t*)A1, *w = (const uint16_t*)W;
+    if (epi == EPI_STORE)
+      gemm_tiled_kernel<EPI_STORE><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc);
+    else if (epi == EPI_RESID)
+      gemm_tiled_kernel<EPI_RESID><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc);
+    else
+      gemm_tiled_kernel<EPI_SWIGLU><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc);
     return hipGetLastError();
   }
   if (bf16) {
