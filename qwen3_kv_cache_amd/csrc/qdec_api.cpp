@@ -157,7 +157,8 @@ struct qdec_model {
   float* bLogits = nullptr;  // logits when the caller passes none
   unsigned long long* bKeys = nullptr;
   int32_t* bTok = nullptr;   // argmax when the caller passes none
-  float* bAttnPart = nullptr;
+  unsigned long long* bAttnPart = nullptr;  // split partial words of batched attention
+  unsigned* bAttnCnt = nullptr;
   int b_nsplit_cap = 0;
   // fused small-M GEMM workspace (up to 64 rows): split-K partials, arrival
   // counters, RMSNorm sum-of-squares partials
@@ -240,9 +241,11 @@ void free_prefill(qdec_model* m) {
 
 void free_batch(qdec_model* m) {
   for (void* p : {(void*)m->bX, (void*)m->bQKV, (void*)m->bAttn, (void*)m->bZ, m->bA0, m->bA1, (void*)m->bPart,
-                  (void*)m->bLogits, (void*)m->bKeys, (void*)m->bTok, (void*)m->bAttnPart})
+                  (void*)m->bLogits, (void*)m->bKeys, (void*)m->bTok, (void*)m->bAttnPart, (void*)m->bAttnCnt})
     (void)hipFree(p);
-  m->bX = m->bQKV = m->bAttn = m->bZ = m->bPart = m->bLogits = m->bAttnPart = nullptr;
+  m->bX = m->bQKV = m->bAttn = m->bZ = m->bPart = m->bLogits = nullptr;
+  m->bAttnPart = nullptr;
+  m->bAttnCnt = nullptr;
   m->bA0 = m->bA1 = nullptr;
   m->bKeys = nullptr;
   m->bTok = nullptr;
@@ -412,7 +415,8 @@ int ensure_batch(qdec_model* m, int nsplit) {
         (e = dev_alloc(&m->bAttn, (size_t)B * d.NQ * d.D, "batch attention")) ||
         (e = dev_alloc(&m->bZ, (size_t)B * d.F, "batch FFN")) || (e = dev_alloc(&m->bPart, part, "batch partials")) ||
         (e = dev_alloc(&m->bLogits, (size_t)B * d.V, "batch logits")) ||
-        (e = dev_alloc(&m->bKeys, (size_t)B, "batch keys")) || (e = dev_alloc(&m->bTok, (size_t)B, "batch tokens"))) {
+        (e = dev_alloc(&m->bKeys, (size_t)B, "batch keys")) || (e = dev_alloc(&m->bTok, (size_t)B, "batch tokens")) ||
+        (e = dev_alloc(&m->bAttnCnt, (size_t)B * d.NKV, "batch attention counters"))) {
       free_batch(m);
       return e;
     }
@@ -422,6 +426,7 @@ int ensure_batch(qdec_model* m, int nsplit) {
       free_batch(m);
       return fail(QDEC_E_OOM, "cannot allocate batch activations");
     }
+    HIP_TRY(hipMemset(m->bAttnCnt, 0, (size_t)B * d.NKV * sizeof(unsigned)));
     m->b_part_cap = part;
     m->b_ready = true;
   }
@@ -430,8 +435,9 @@ int ensure_batch(qdec_model* m, int nsplit) {
     (void)hipFree(m->bAttnPart);
     m->bAttnPart = nullptr;
     m->b_nsplit_cap = 0;
-    if (int e = dev_alloc(&m->bAttnPart, (size_t)B * d.NQ * nsplit * (d.D + 2), "batch attention partials"))
-      return e;
+    const size_t words = (size_t)B * d.NQ * nsplit * (d.D + 2);
+    if (int e = dev_alloc(&m->bAttnPart, words, "batch attention partials")) return e;
+    HIP_TRY(hipMemset(m->bAttnPart, 0, words * sizeof(unsigned long long)));  // tag 0 is never used
     m->b_nsplit_cap = nsplit;
   }
   return QDEC_OK;
@@ -474,7 +480,11 @@ int ensure_rows(qdec_model* m) {
 // partial words are cleared (tag 0 is never used), so no stale word can match.
 int next_rows_tag(qdec_model* m, unsigned* tag) {
   if (m->rows_tag >= 0xFFFFFFF0u) {
-    HIP_TRY(hipMemsetAsync(m->rP, 0, m->rP_words * sizeof(unsigned long long), m->stream));
+    if (m->rP) HIP_TRY(hipMemsetAsync(m->rP, 0, m->rP_words * sizeof(unsigned long long), m->stream));
+    if (m->bAttnPart)
+      HIP_TRY(hipMemsetAsync(m->bAttnPart, 0,
+                             (size_t)kMaxBatch * m->d.NQ * m->b_nsplit_cap * (m->d.D + 2) * sizeof(unsigned long long),
+                             m->stream));
     m->rows_tag = 1;
   }
   *tag = m->rows_tag++;
@@ -514,8 +524,8 @@ int run_layers_rows(qdec_model* m, int T, float* X, float* QKV, float* Attn, flo
     g.A = X, g.lda = d.H, g.ssq = m->rSsq, g.nss = nss, g.gain = w.in_norm;
     g.W = (const uint16_t*)w.wqkv, g.K = d.H, g.N = d.qkv(), g.C = QKV, g.ldc = d.qkv();
     if (int e = gemm_rows(m, EPI_STORE, true, g)) return e;
-    LAUNCH(rope(l));
-    LAUNCH(attn(l));
+    if (int e = rope(l)) return e;
+    if (int e = attn(l)) return e;
     g.A = Attn, g.lda = d.NQ * d.D, g.W = (const uint16_t*)w.wo, g.K = d.NQ * d.D, g.N = d.H, g.C = X, g.ldc = d.H;
     g.ssq_out = m->rSsq;
     if (int e = gemm_rows(m, EPI_RESID, false, g)) return e;
@@ -534,7 +544,7 @@ int run_layers_rows(qdec_model* m, int T, float* X, float* QKV, float* Attn, flo
 // The decoder layers over T activation rows held in X (fp32 [T, H]), one
 // layer after another (transcribe.cpp "Forward map - funasr_nano", table
 // "LLM decoder"). rope(l) applies QK-norm + RoPE and appends K/V of layer l;
-// attn(l) writes the attention output rows into Attn.
+// attn(l) writes the attention output rows into Attn; both return a status.
 template <typename RopeFn, typename AttnFn>
 int run_layers(qdec_model* m, int T, float* X, float* QKV, float* Attn, float* Z, void* A0, void* A1, float* part,
                size_t part_cap, RopeFn rope, AttnFn attn) {
@@ -549,8 +559,8 @@ int run_layers(qdec_model* m, int T, float* X, float* QKV, float* Attn, float* Z
     const LayerW& w = m->layers[l];
     LAUNCH(norm_in(X, d.H, w.in_norm));
     LAUNCH(launch_gemm(bf, EPI_STORE, A0, A1, T, d.H, w.wqkv, d.qkv(), QKV, d.qkv(), st, part, part_cap));
-    LAUNCH(rope(l));
-    LAUNCH(attn(l));
+    if (int e = rope(l)) return e;
+    if (int e = attn(l)) return e;
     LAUNCH(norm_in(Attn, d.NQ * d.D, nullptr));
     LAUNCH(launch_gemm(bf, EPI_RESID, A0, A1, T, d.NQ * d.D, w.wo, d.H, X, d.H, st, part, part_cap));
     LAUNCH(norm_in(X, d.H, w.post_norm));
@@ -587,11 +597,25 @@ int run_decode_batch(qdec_state* const* states, int n, const int32_t* tokens, fl
   float* lg = logits ? logits : m->bLogits;
   LAUNCH(launch_reset_keys(m->bKeys, n, st));
   LAUNCH(launch_embed_rows(d, m->bf16, m->embed, rows, m->bX, fused ? m->rSsq : nullptr, st));
-  auto rope = [&](int l) {
+  auto rope = [](int) { return 0; };  // inside the attention launch
+  auto attn = [&](int l) -> int {
     const LayerW& w = m->layers[l];
-    return launch_qk_rope_rows(d, m->bQKV, rows, w.q_norm, w.k_norm, m->rope_cos, m->rope_sin, l, st);
+    AttnRows a{};
+    a.rows = rows;
+    a.qkv = m->bQKV;
+    a.layer = l;
+    a.q_norm = w.q_norm;
+    a.k_norm = w.k_norm;
+    a.rcos = m->rope_cos;
+    a.rsin = m->rope_sin;
+    a.out = m->bAttn;
+    a.part = m->bAttnPart;
+    a.cnt = m->bAttnCnt;
+    a.err = m->err_dev;
+    if (int e = next_rows_tag(m, &a.tag)) return e;
+    LAUNCH(launch_attn_rows(d, a, nsplit, st));
+    return 0;
   };
-  auto attn = [&](int l) { return launch_attn_rows(d, m->bQKV, rows, l, nsplit, m->bAttnPart, m->bAttn, st); };
   if (fused) {
     int nss = 1;
     if (int e = run_layers_rows(m, n, m->bX, m->bQKV, m->bAttn, m->bZ, 1, rope, attn, &nss)) return e;
@@ -632,11 +656,15 @@ int run_prefill(qdec_state* s, int T, const float* audio, int a0, int La, float*
     if (int e = ensure_rows(m)) return e;
   }
   LAUNCH(launch_embed_prefill(d, bf, m->embed, m->p_ids, T, audio, a0, La, m->pX, fused ? m->rSsq : nullptr, st));
-  auto rope = [&](int l) {
+  auto rope = [&](int l) -> int {
     const LayerW& w = m->layers[l];
-    return launch_qk_rope_append(d, m->pQKV, T, 0, w.q_norm, w.k_norm, m->rope_cos, m->rope_sin, s->pt_dev, l, st);
+    LAUNCH(launch_qk_rope_append(d, m->pQKV, T, 0, w.q_norm, w.k_norm, m->rope_cos, m->rope_sin, s->pt_dev, l, st));
+    return 0;
   };
-  auto attn = [&](int) { return launch_attn_prefill(d, m->pQKV, T, m->pAttn, st); };
+  auto attn = [&](int) -> int {
+    LAUNCH(launch_attn_prefill(d, m->pQKV, T, m->pAttn, st));
+    return 0;
+  };
   if (fused) {
     int nss = 1;
     if (int e = run_layers_rows(m, T, m->pX, m->pQKV, m->pAttn, m->pZ, 1, rope, attn, &nss)) return e;

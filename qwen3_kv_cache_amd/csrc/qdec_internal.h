@@ -11,7 +11,8 @@ namespace qdec {
 
 constexpr int kPage = QDEC_PAGE;   // positions per KV page
 constexpr int kGuGroup = 8;        // gate/up rows interleaved in groups of 8 in the packed weight
-constexpr int kAttnChunk = 256;    // positions per split in decode attention
+constexpr int kAttnChunk = 128;    // positions per split in batched decode attention
+static_assert(kAttnChunk % kPage == 0, "a split covers whole pages");
 constexpr int kMaxBatch = 16;
 constexpr int kDecMaxPos = QDEC_DECODE_MAX_POS;  // decode positions (KV page pointers held in LDS)
 
@@ -102,13 +103,26 @@ hipError_t launch_argmax_rows(const float* logits, int n, int V, unsigned long l
 hipError_t launch_qk_rope_append(const Dims& d, float* qkv, int T, int pos0, const float* q_norm,
                                  const float* k_norm, const float* rope_cos, const float* rope_sin,
                                  const int64_t* page_table, int layer, hipStream_t st);
-hipError_t launch_qk_rope_rows(const Dims& d, float* qkv, const BatchRows& rows, const float* q_norm,
-                               const float* k_norm, const float* rope_cos, const float* rope_sin, int layer,
-                               hipStream_t st);
-// partial holds rows.n * NQ * nsplit * (D + 2) floats; nsplit * kAttnChunk
-// must cover the longest row (pos + 1)
-hipError_t launch_attn_rows(const Dims& d, const float* qkv, const BatchRows& rows, int layer, int nsplit,
-                            float* partial, float* out, hipStream_t st);
+// Batched decode attention for one layer (QK-norm, RoPE and K/V append of
+// the rows' current positions included). The launcher fills L, NKV, ld, eps
+// and qscale.
+struct AttnRows {
+  BatchRows rows;
+  float* qkv;                   // [n, ld] raw Q | K | V rows of the QKV GEMM
+  int ld, L, NKV, layer;
+  const float* q_norm;
+  const float* k_norm;
+  const float* rcos;
+  const float* rsin;
+  float eps, qscale;
+  float* out;                   // [n, NQ * D]
+  unsigned long long* part;     // n * NKV * nsplit * GROUP * (D + 2) words
+  unsigned* cnt;                // n * NKV counters, zero between launches
+  unsigned tag;                 // as RowsGemm::tag
+  int* err;
+};
+// nsplit * kAttnChunk must cover the longest row (pos + 1)
+hipError_t launch_attn_rows(const Dims& d, const AttnRows& a, int nsplit, hipStream_t st);
 hipError_t launch_attn_prefill(const Dims& d, const float* qkv, int T, float* out, hipStream_t st);
 
 hipError_t launch_rms_split(const float* X, int T, int K, const float* gain, float eps, uint16_t* hi,

@@ -6,9 +6,10 @@
 // NCNN "Qwen3ASR ncnn多平台移植", section 5):
 //   embed + audio-row override   -> embed_prefill_kernel / embed_rows_kernel
 //   rms_norm + Q/K/V projection  -> rms_split + gemm
-//   per-head Q/K-RMSNorm + NeoX RoPE + KV append -> qk_rope_append_kernel / qk_rope_rows_kernel
-//   causal GQA attention         -> attn_rows_kernel + attn_combine_rows_kernel,
-//                                   attn_prefill_kernel
+//   per-head Q/K-RMSNorm + NeoX RoPE + KV append -> qk_rope_append_kernel (prefill),
+//                                   the prologue of attn_rows_kernel (batched decode)
+//   causal GQA attention         -> attn_rows_kernel (batched decode),
+//                                   attn_prefill_mfma_kernel / attn_prefill_kernel
 //   O projection + residual      -> gemm with the residual epilogue
 //   rms_norm + gate_up + SiLU*up -> gemm with the SwiGLU epilogue
 //   down projection + residual   -> gemm with the residual epilogue
@@ -319,51 +320,105 @@ __global__ __launch_bounds__(64) void qk_rope_append_kernel(float* __restrict__ 
               page_table, layer);
 }
 
-// Batch rows: row r is its own state at its own position.
-__global__ __launch_bounds__(64) void qk_rope_rows_kernel(float* __restrict__ qkv, int ld, BatchRows rows, int NQ,
-                                                           int NKV, int D, int L, float eps,
-                                                           const float* __restrict__ q_norm,
-                                                           const float* __restrict__ k_norm,
-                                                           const float* __restrict__ rcos,
-                                                           const float* __restrict__ rsin, int layer) {
-  const int row = blockIdx.y;
-  qk_rope_row(qkv + (size_t)row * ld, blockIdx.x, rows.pos[row], NQ, NKV, D, L, eps, q_norm, k_norm, rcos, rsin,
-              rows.pt[row], layer);
-}
-
 // ------------------------------------------------ batched decode attention
-// Split-K flash decoding over the paged cache for the rows of a batched
-// decode step; row r is one state attending over positions [0, pos_r] (its
-// own K/V at pos_r already appended). Block = (kv head g, split s, row r),
-// 4 waves. Blocks are numbered kv head fastest, so with 8 KV heads every
-// block of head g runs on XCD g and rows that share prompt pages (cloned
-// states) read them through one L2. In a wave, lane = 8 * slot + part: 8 keys
-// at a time, each key's head_dim split over 8 lanes (DPL = D / 8 values per
-// lane), the next 8 keys in flight while the current ones are used. All GROUP
-// query heads of the KV head share every K/V load. Output per (row, q head,
-// split): running max m, denominator l and the unnormalised D-vector.
+// One launch per layer for the rows of a batched decode step; row r is one
+// state at position pos_r. Block = (kv head g, split s of kAttnChunk
+// positions, row r), 4 waves; blocks are numbered kv head fastest, so with
+// 8 KV heads every block of head g runs on XCD g and rows that share prompt
+// pages (clones) read them through one L2.
+//  1. Prologue: per-head Q/K-RMSNorm and RoPE at pos_r of the GROUP query
+//     heads and of key head g (one wave per head), into LDS. The block whose
+//     split holds pos_r also appends K/V at pos_r to the row's pages and uses
+//     its LDS copy for that key.
+//  2. Split-K flash decoding over [u0, u1) of the row's pages: lane = 8 slot +
+//     part, 8 keys at a time, head_dim split over 8 lanes, the next 8 keys in
+//     flight while the current ones are used; the GROUP query heads share every
+//     K/V load. Scores are in base 2 (q carries log2(e) / sqrt(D)).
+//  3. Merge: with one split the block writes the output; otherwise each block
+//     publishes (m, l, o) as tagged device-scope words and bumps the (row,
+//     kv head) counter, and the last block to arrive merges all splits in
+//     split order (scheduling-independent), writes the output and resets the
+//     counter.
+constexpr unsigned long long kAttnWaitTicks = 200000000ull;  // about 0.1 s of s_memtime
 
 template <int D, int GROUP>
-__global__ __launch_bounds__(256) void attn_rows_kernel(const float* __restrict__ qkv, int ld, BatchRows rows,
-                                                         int NKV, int L, int layer, float* __restrict__ partial,
-                                                         int nsplit, float scale) {
+__global__ __launch_bounds__(256) void attn_rows_kernel(AttnRows a) {
   constexpr int DPL = D / 8;
+  constexpr int HALF = D / 2;
+  __shared__ float q_l[GROUP][D], k_l[D], v_l[D];
   __shared__ float sm_m[4][GROUP], sm_l[4][GROUP];
   __shared__ float sm_o[4][GROUP][D];
-  const int g = blockIdx.x, s = blockIdx.y, r = blockIdx.z;
+  __shared__ const float* pg[kAttnChunk / kPage];
+  __shared__ int s_last;
+  const int g = blockIdx.x, s = blockIdx.y, r = blockIdx.z, nsplit = gridDim.y;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int slot = lane / 8, part = lane % 8;
-  const int n = rows.pos[r] + 1;
-  const int64_t* __restrict__ page_table = rows.pt[r];
+  const int pos = a.rows.pos[r];
+  const int n = pos + 1;
+  const int64_t* __restrict__ page_table = a.rows.pt[r];
   const int u0 = s * kAttnChunk, u1 = min(n, u0 + kAttnChunk);
-  const float* q = qkv + (size_t)r * ld;
-  Dims d{L, 0, 0, NKV, D, 0, 0, 0.f};
+  const bool has_cur = u0 <= pos && pos < u1;
+  const int NQ = a.NKV * GROUP;
+  Dims d{a.L, 0, NQ, a.NKV, D, 0, 0, 0.f};
+  float* row = a.qkv + (size_t)r * a.ld;
+
+  // the split's page pointers, so that each key load needs no dependent
+  // global load first
+  if (threadIdx.x < kAttnChunk / kPage && u0 < u1)
+    pg[threadIdx.x] = reinterpret_cast<const float*>(page_table[min(u0 / kPage + (int)threadIdx.x, (u1 - 1) / kPage)]);
+
+  // 1. QK-norm + RoPE: items 0..GROUP-1 are the query heads, GROUP the key head
+  for (int it = wave; it <= GROUP; it += 4) {
+    const bool is_q = it < GROUP;
+    const float* src = row + (size_t)(is_q ? g * GROUP + it : NQ + g) * D;
+    const float* gain = is_q ? a.q_norm : a.k_norm;
+    float x0 = 0.f, x1 = 0.f;
+    if (lane < HALF) {
+      x0 = src[lane];
+      x1 = src[lane + HALF];
+    }
+    const float ss = wave_sum(x0 * x0 + x1 * x1);
+    const float inv = 1.f / sqrtf(ss / (float)D + a.eps);
+    if (lane < HALF) {
+      x0 = x0 * inv * gain[lane];
+      x1 = x1 * inv * gain[lane + HALF];
+      const float c = a.rcos[(size_t)pos * HALF + lane], sn = a.rsin[(size_t)pos * HALF + lane];
+      const float r0 = x0 * c - x1 * sn, r1 = x1 * c + x0 * sn;
+      if (is_q) {
+        q_l[it][lane] = r0 * a.qscale;
+        q_l[it][lane + HALF] = r1 * a.qscale;
+      } else {
+        k_l[lane] = r0;
+        k_l[lane + HALF] = r1;
+        const float* vs = row + (size_t)(NQ + a.NKV + g) * D;
+        const float v0 = vs[lane], v1 = vs[lane + HALF];
+        v_l[lane] = v0;
+        v_l[lane + HALF] = v1;
+        if (has_cur) {
+          float* page = reinterpret_cast<float*>(page_table[pos / kPage]);
+          float* kd = page + page_offset(d, a.layer, 0, g, pos % kPage);
+          float* vd = page + page_offset(d, a.layer, 1, g, pos % kPage);
+          kd[lane] = r0;
+          kd[lane + HALF] = r1;
+          vd[lane] = v0;
+          vd[lane + HALF] = v1;
+        }
+      }
+    }
+  }
+  __syncthreads();
 
   float qr[GROUP][DPL];
 #pragma unroll
   for (int h = 0; h < GROUP; ++h)
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) qr[h][i] = q[(size_t)(g * GROUP + h) * D + part * DPL + i] * scale;
+    for (int i = 0; i < DPL; ++i) qr[h][i] = q_l[h][part * DPL + i];
+  float kcur[DPL], vcur[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) {
+    kcur[i] = k_l[part * DPL + i];
+    vcur[i] = v_l[part * DPL + i];
+  }
 
   float m[GROUP], l[GROUP], acc[GROUP][DPL];
 #pragma unroll
@@ -374,19 +429,19 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const float* __restrict_
     for (int i = 0; i < DPL; ++i) acc[h][i] = 0.f;
   }
 
-  // key u clamped into [u0, u1): loads past the end repeat the last key and
-  // are masked out of the softmax
+  // 2. key u clamped into [u0, u1): loads past the end repeat the last key
+  // and are masked out; the key at pos comes from LDS
   auto load = [&](int base, float (&kv)[DPL], float (&vv)[DPL]) {
     const int u = min(base + slot, u1 - 1);
-    const float* page = reinterpret_cast<const float*>(page_table[u / kPage]);
-    const float* kp = page + page_offset(d, layer, 0, g, u % kPage) + part * DPL;
-    const float* vp = page + page_offset(d, layer, 1, g, u % kPage) + part * DPL;
+    const float* page = pg[u / kPage - u0 / kPage];
+    const float* kp = page + page_offset(d, a.layer, 0, g, u % kPage) + part * DPL;
+    const float* vp = page + page_offset(d, a.layer, 1, g, u % kPage) + part * DPL;
 #pragma unroll
     for (int i = 0; i < DPL; i += 4) {
-      const float4 a = *reinterpret_cast<const float4*>(kp + i);
-      kv[i] = a.x; kv[i + 1] = a.y; kv[i + 2] = a.z; kv[i + 3] = a.w;
-      const float4 b = *reinterpret_cast<const float4*>(vp + i);
-      vv[i] = b.x; vv[i + 1] = b.y; vv[i + 2] = b.z; vv[i + 3] = b.w;
+      const float4 x = *reinterpret_cast<const float4*>(kp + i);
+      kv[i] = x.x; kv[i + 1] = x.y; kv[i + 2] = x.z; kv[i + 3] = x.w;
+      const float4 y = *reinterpret_cast<const float4*>(vp + i);
+      vv[i] = y.x; vv[i + 1] = y.y; vv[i + 2] = y.z; vv[i + 3] = y.w;
     }
   };
 
@@ -396,7 +451,14 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const float* __restrict_
   for (; base < u1; base += 32) {
     float kn[DPL], vn[DPL];
     load(base + 32, kn, vn);
-    const bool valid = base + slot < u1;
+    const int u = base + slot;
+    const bool valid = u < u1;
+    const bool cur = u == pos;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) {
+      kc[i] = cur ? kcur[i] : kc[i];
+      vc[i] = cur ? vcur[i] : vc[i];
+    }
 #pragma unroll
     for (int h = 0; h < GROUP; ++h) {
       float sc = 0.f;
@@ -410,8 +472,8 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const float* __restrict_
       mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
       mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
       const float mn = fmaxf(m[h], mx);
-      const float alpha = expf(m[h] - mn);
-      const float p = valid ? expf(sc - mn) : 0.f;
+      const float alpha = __builtin_amdgcn_exp2f(m[h] - mn);
+      const float p = valid ? __builtin_amdgcn_exp2f(sc - mn) : 0.f;
       float ps = p + __shfl_xor(p, 8, kWave);
       ps += __shfl_xor(ps, 16, kWave);
       ps += __shfl_xor(ps, 32, kWave);
@@ -451,44 +513,83 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const float* __restrict_
     }
   }
   __syncthreads();
-  // combine the 4 waves; thread t handles (head h, dim i) pairs
-  const int NQ = NKV * GROUP;
+
+  // 3. the 4 waves' (m, l, o) merged in wave order; thread -> (head, dim)
+  float* out = a.out + (size_t)r * NQ * D + (size_t)g * GROUP * D;
+  const unsigned long long tag = (unsigned long long)a.tag << 32;
+  unsigned long long* words = a.part + ((size_t)r * a.NKV + g) * nsplit * GROUP * (D + 2);
   for (int idx = threadIdx.x; idx < GROUP * D; idx += blockDim.x) {
     const int h = idx / D, i = idx % D;
     float M = -INFINITY;
     for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][h]);
-    float o = 0.f, lsum = 0.f;
+    float o = 0.f, ls = 0.f;
     for (int w = 0; w < 4; ++w) {
-      const float f = (sm_m[w][h] == -INFINITY) ? 0.f : expf(sm_m[w][h] - M);
+      const float f = sm_m[w][h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sm_m[w][h] - M);
       o = fmaf(f, sm_o[w][h][i], o);
-      lsum = fmaf(f, sm_l[w][h], lsum);
+      ls = fmaf(f, sm_l[w][h], ls);
     }
-    float* dst = partial + (((size_t)r * NQ + g * GROUP + h) * nsplit + s) * (D + 2);
-    dst[2 + i] = o;
-    if (i == 0) {
-      dst[0] = M;
-      dst[1] = lsum;
+    if (nsplit == 1) {
+      out[(size_t)h * D + i] = o / ls;
+    } else {
+      unsigned long long* wd = words + ((size_t)s * GROUP + h) * (D + 2);
+      __hip_atomic_store(wd + 2 + i, tag | __float_as_uint(o), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (i == 0) {
+        __hip_atomic_store(wd, tag | __float_as_uint(M), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(wd + 1, tag | __float_as_uint(ls), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   }
-}
-
-// out[r][h*D + i] = sum_s e^{m_s - M} o_s[i] / sum_s e^{m_s - M} l_s; grid (NQ, rows)
-__global__ __launch_bounds__(128) void attn_combine_rows_kernel(const float* __restrict__ partial, int nsplit,
-                                                                 int D, float* __restrict__ out, int ldo) {
-  const int h = blockIdx.x, r = blockIdx.y, NQ = gridDim.x;
-  const float* p = partial + ((size_t)r * NQ + h) * nsplit * (D + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, p[s * (D + 2)]);
-  for (int i = threadIdx.x; i < D; i += blockDim.x) {
-    float o = 0.f, l = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float ms = p[s * (D + 2)];
-      const float f = (ms == -INFINITY) ? 0.f : expf(ms - M);
-      o = fmaf(f, p[s * (D + 2) + 2 + i], o);
-      l = fmaf(f, p[s * (D + 2) + 1], l);
+  if (nsplit == 1) return;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  unsigned* cnt = a.cnt + (size_t)r * a.NKV + g;
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(nsplit - 1);
+  __syncthreads();
+  if (!s_last) return;
+  // every split's (m, l, o_i) requested at once, 8 splits per round
+  // (addresses clamped to the last split, surplus ignored); a word not yet
+  // visible is re-read under a time limit
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  bool late = false;
+  auto value = [&](unsigned long long w, const unsigned long long* p) {
+    while ((w >> 32) != a.tag && !late) {
+      late = __builtin_amdgcn_s_memtime() - t0 > kAttnWaitTicks;
+      w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    out[(size_t)r * ldo + (size_t)h * D + i] = o / l;
+    return (w >> 32) == a.tag ? __uint_as_float((unsigned)w) : __builtin_nanf("");
+  };
+  for (int idx = threadIdx.x; idx < GROUP * D; idx += blockDim.x) {
+    const int h = idx / D, i = idx % D;
+    float M = -INFINITY, o = 0.f, ls = 0.f;
+    for (int sb = 0; sb < nsplit; sb += 8) {
+      unsigned long long wm[8], wl[8], wo[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const unsigned long long* wd = words + ((size_t)min(sb + u, nsplit - 1) * GROUP + h) * (D + 2);
+        wm[u] = __hip_atomic_load(wd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        wl[u] = __hip_atomic_load(wd + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        wo[u] = __hip_atomic_load(wd + 2 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (sb + u < nsplit) {
+          const unsigned long long* wd = words + ((size_t)(sb + u) * GROUP + h) * (D + 2);
+          const float ms = value(wm[u], wd), lv = value(wl[u], wd + 1), ov = value(wo[u], wd + 2 + i);
+          // running merge in split order
+          const float Mn = fmaxf(M, ms);
+          const float fa = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+          const float fb = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - Mn);
+          o = o * fa + ov * fb;
+          ls = ls * fa + lv * fb;
+          M = Mn;
+        }
+      }
+    }
+    out[(size_t)h * D + i] = o / ls;
   }
+  if (late) __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------ prefill attention
@@ -1526,24 +1627,18 @@ hipError_t launch_qk_rope_append(const Dims& d, float* qkv, int T, int pos0, con
   return hipGetLastError();
 }
 
-hipError_t launch_qk_rope_rows(const Dims& d, float* qkv, const BatchRows& rows, const float* q_norm,
-                               const float* k_norm, const float* rope_cos, const float* rope_sin, int layer,
-                               hipStream_t st) {
-  dim3 grid(d.NQ + d.NKV, rows.n);
-  qk_rope_rows_kernel<<<grid, 64, 0, st>>>(qkv, d.qkv(), rows, d.NQ, d.NKV, d.D, d.L, d.eps, q_norm, k_norm,
-                                           rope_cos, rope_sin, layer);
-  return hipGetLastError();
-}
-
-hipError_t launch_attn_rows(const Dims& d, const float* qkv, const BatchRows& rows, int layer, int nsplit,
-                            float* partial, float* out, hipStream_t st) {
+hipError_t launch_attn_rows(const Dims& d, const AttnRows& args, int nsplit, hipStream_t st) {
   const int group = d.NQ / d.NKV;
-  const float scale = 1.f / sqrtf((float)d.D);
-  dim3 grid(d.NKV, nsplit, rows.n);
-#define QDEC_ATTN_CASE(DD, GG)                                                                      \
-  if (d.D == DD && group == GG) {                                                                   \
-    attn_rows_kernel<DD, GG><<<grid, 256, 0, st>>>(qkv, d.qkv(), rows, d.NKV, d.L, layer, partial, nsplit, \
-                                                   scale);                                          \
+  AttnRows a = args;
+  a.L = d.L;
+  a.NKV = d.NKV;
+  a.ld = d.qkv();
+  a.eps = d.eps;
+  a.qscale = 1.4426950408889634f / sqrtf((float)d.D);  // scores in base 2
+  dim3 grid(d.NKV, nsplit, a.rows.n);
+#define QDEC_ATTN_CASE(DD, GG)                                    \
+  if (d.D == DD && group == GG) {                                 \
+    attn_rows_kernel<DD, GG><<<grid, 256, 0, st>>>(a);            \
   } else
   QDEC_ATTN_CASE(128, 2)
   QDEC_ATTN_CASE(128, 1)
@@ -1554,9 +1649,6 @@ hipError_t launch_attn_rows(const Dims& d, const float* qkv, const BatchRows& ro
   QDEC_ATTN_CASE(32, 4)
   return hipErrorInvalidValue;
 #undef QDEC_ATTN_CASE
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  attn_combine_rows_kernel<<<dim3(d.NQ, rows.n), 128, 0, st>>>(partial, nsplit, d.D, out, d.NQ * d.D);
   return hipGetLastError();
 }
 
