@@ -10,6 +10,11 @@ multi-step launch (qdec_decode_greedy); --per-step launches once per token.
 Inputs and weights are resident in HBM before timing; states are created
 before the timed region.
 
+The default run also reports, under "other_workloads", the rest of the
+metric with the same weights and fewer repetitions: B=16 batched decode of
+16 clones of a 512-token prefill (branch16), and the 1024- and 8192-token
+prompts (long, prefill8k). --no-others skips them.
+
 Usage: python bench.py [--steps K] [--warmup W] [--workload short|long|prefill8k|branch16]
        python bench.py --copy-probe   (plain copy kernel for counter calibration)
 """
@@ -100,6 +105,67 @@ def cpu_baseline(w, W, n_decode_sample: int):
                       f"({w.prompt_len / t_pre:.1f} prefill tok/s) then {n_decode_sample} greedy decode steps, B=1"}
 
 
+def measure(w, model, steps, warmup, per_step=False):
+    """Prefill of the workload's prompt then its decode (greedy in one launch
+    for B=1; B=16 clones of the prefilled state stepping through
+    qdec_decode_batch), `warmup` untimed and `steps` timed repetitions.
+    Returns per-repetition prefill and decode milliseconds (HIP events on the
+    library's stream) and the wall time of the timed repetitions."""
+    import torch
+
+    import synth
+    from qwen3_kv_cache_amd import qdec
+
+    dev = torch.device("cuda:0")
+    ids, audio, a0 = synth.make_prompt(w)
+    audio_d = torch.from_numpy(audio).to(dev)
+    B = w.n_branch
+    n = w.n_decode
+    toks = torch.zeros((n + 1, B), dtype=torch.int32, device=dev)
+    streams = np.stack([synth.branch_stream(w, b) for b in range(B)]) if B > 1 else None
+    total = warmup + steps
+    states = [qdec.qdec_state_create(model.handle, w.max_ctx) for _ in range(total)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(total)]
+    torch.cuda.synchronize()
+
+    def one_step(i):
+        st = states[i]
+        e0, e1, e2 = ev[i]
+        e0.record()
+        qdec.qdec_prefill(st, ids, len(ids), audio_d.data_ptr(), a0, len(audio), None, toks[0].data_ptr())
+        e1.record()
+        if B == 1:
+            if per_step:
+                for s in range(n):
+                    qdec.qdec_decode_step_dev(st, toks[s].data_ptr(), w.prompt_len + s, None, toks[s + 1].data_ptr())
+            else:
+                qdec.qdec_decode_greedy(st, toks[0].data_ptr(), w.prompt_len, n, None, toks[1].data_ptr())
+        else:
+            br = [qdec.qdec_clone_state(st) for _ in range(B)]
+            for s in range(n):
+                qdec.qdec_decode_batch(br, streams[:, s], None, toks[s + 1].data_ptr())
+            e2.record()
+            torch.cuda.synchronize()
+            for b in br:
+                qdec.qdec_state_destroy(b)
+            return
+        e2.record()
+
+    for i in range(warmup):
+        one_step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(warmup, total):
+        one_step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(warmup, total)])
+    dec_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(warmup, total)])
+    for st in states:
+        qdec.qdec_state_destroy(st)
+    return pre_ms, dec_ms, wall
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,6 +174,8 @@ def main():
     ap.add_argument("--workload", default="short")
     ap.add_argument("--cpu-sample", type=int, default=24, help="oracle decode steps for the CPU baseline (0 = skip)")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the other workloads the default run also reports (B=16, long and 8k prompts)")
     ap.add_argument("--per-step", action="store_true",
                     help="decode with one launch per token (qdec_decode_step_dev) instead of one launch for all steps")
     a = ap.parse_args()
@@ -129,55 +197,8 @@ def main():
     dev = torch.device("cuda:0")
     W = synth.make_weights(w.shape, w.weight_seed)
     model = Model(w.shape, W.bits if w.shape.bf16 else W.f32, bf16=w.shape.bf16)
-    ids, audio, a0 = synth.make_prompt(w)
-    audio_d = torch.from_numpy(audio).to(dev)
-    V = w.shape.vocab
-    B = w.n_branch
-    n = w.n_decode
-    logits = torch.zeros((B, V), dtype=torch.float32, device=dev)
-    toks = torch.zeros((n + 1, B), dtype=torch.int32, device=dev)
-    streams = np.stack([synth.branch_stream(w, b) for b in range(B)]) if B > 1 else None
-    total = a.warmup + a.steps
-    states = [qdec.qdec_state_create(model.handle, w.max_ctx) for _ in range(total)]
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(total)]
-    torch.cuda.synchronize()
-
-    def one_step(i):
-        st = states[i]
-        e0, e1, e2 = ev[i]
-        e0.record()
-        qdec.qdec_prefill(st, ids, len(ids), audio_d.data_ptr(), a0, len(audio), None, toks[0].data_ptr())
-        e1.record()
-        if B == 1:
-            if a.per_step:
-                for s in range(n):
-                    qdec.qdec_decode_step_dev(st, toks[s].data_ptr(), w.prompt_len + s, None, toks[s + 1].data_ptr())
-            else:
-                qdec.qdec_decode_greedy(st, toks[0].data_ptr(), w.prompt_len, n, None, toks[1].data_ptr())
-        else:
-            br = [qdec.qdec_clone_state(st) for _ in range(B)]
-            for s in range(n):
-                qdec.qdec_decode_batch(br, streams[:, s], None, toks[s + 1].data_ptr())
-            e2.record()
-            torch.cuda.synchronize()
-            for b in br:
-                qdec.qdec_state_destroy(b)
-            return
-        e2.record()
-
-    for i in range(a.warmup):
-        one_step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(a.warmup, total):
-        one_step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    pre_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(a.warmup, total)])
-    dec_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(a.warmup, total)])
-    for st in states:
-        qdec.qdec_state_destroy(st)
-
+    pre_ms, dec_ms, wall = measure(w, model, a.steps, a.warmup, a.per_step)
+    n, B = w.n_decode, w.n_branch
     decode_tok_s = n * B * a.steps / (dec_ms.sum() / 1e3)
     prefill_tok_s = w.prompt_len * a.steps / (pre_ms.sum() / 1e3)
     ctx = [w.prompt_len + s + 1 for s in range(n)]
@@ -211,6 +232,19 @@ def main():
                             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                             "kernel": "decode_kernel (%d steps per launch)" % (1 if a.per_step else n),
                             "bytes_per_unit": round(bytes_tok)}
+    if a.workload == "short" and not a.no_others:
+        # the rest of the metric (B=16 decode, prefill of long prompts), same
+        # weights, fewer repetitions
+        others = {}
+        for name in ("branch16", "long", "prefill8k"):
+            wo = synth.WORKLOADS[name]
+            assert wo.shape == w.shape and wo.weight_seed == w.weight_seed, name
+            p_ms, d_ms, _ = measure(wo, model, 2, 1)
+            others[name] = {"decode_tok_s": round(wo.n_decode * wo.n_branch * len(d_ms) / (d_ms.sum() / 1e3), 1),
+                            "batch": wo.n_branch, "prompt_len": wo.prompt_len, "decode_steps": wo.n_decode,
+                            "prefill_tok_s": round(wo.prompt_len * len(p_ms) / (p_ms.sum() / 1e3), 1),
+                            "prefill_ms": round(float(p_ms.mean()), 3)}
+        line["other_workloads"] = others
     if a.cpu_sample > 0:
         line["cpu_baseline"] = cpu_baseline(w, W, a.cpu_sample)
     model.close()
