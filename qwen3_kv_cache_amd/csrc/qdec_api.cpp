@@ -142,8 +142,6 @@ struct qdec_model {
   float* pZ = nullptr;
   void* pA0 = nullptr;  // bf16 hi (or fp32 activations for fp32 weights)
   void* pA1 = nullptr;  // bf16 lo
-  float* pPart = nullptr;  // small-M GEMM chunk partials (prompts of <= 64 tokens)
-  size_t part_cap = 0;
   // batched decode workspace for kMaxBatch rows, allocated on first use
   bool b_ready = false;
   float* bX = nullptr;
@@ -152,8 +150,6 @@ struct qdec_model {
   float* bZ = nullptr;
   void* bA0 = nullptr;
   void* bA1 = nullptr;
-  float* bPart = nullptr;
-  size_t b_part_cap = 0;
   float* bLogits = nullptr;  // logits when the caller passes none
   unsigned long long* bKeys = nullptr;
   int32_t* bTok = nullptr;   // argmax when the caller passes none
@@ -230,9 +226,6 @@ void free_prefill(qdec_model* m) {
   (void)hipFree(m->pZ);
   (void)hipFree(m->pA0);
   (void)hipFree(m->pA1);
-  (void)hipFree(m->pPart);
-  m->pPart = nullptr;
-  m->part_cap = 0;
   m->p_ids = nullptr;
   m->pX = m->pQKV = m->pAttn = m->pZ = nullptr;
   m->pA0 = m->pA1 = nullptr;
@@ -240,16 +233,15 @@ void free_prefill(qdec_model* m) {
 }
 
 void free_batch(qdec_model* m) {
-  for (void* p : {(void*)m->bX, (void*)m->bQKV, (void*)m->bAttn, (void*)m->bZ, m->bA0, m->bA1, (void*)m->bPart,
+  for (void* p : {(void*)m->bX, (void*)m->bQKV, (void*)m->bAttn, (void*)m->bZ, m->bA0, m->bA1,
                   (void*)m->bLogits, (void*)m->bKeys, (void*)m->bTok, (void*)m->bAttnPart, (void*)m->bAttnCnt})
     (void)hipFree(p);
-  m->bX = m->bQKV = m->bAttn = m->bZ = m->bPart = m->bLogits = nullptr;
+  m->bX = m->bQKV = m->bAttn = m->bZ = m->bLogits = nullptr;
   m->bAttnPart = nullptr;
   m->bAttnCnt = nullptr;
   m->bA0 = m->bA1 = nullptr;
   m->bKeys = nullptr;
   m->bTok = nullptr;
-  m->b_part_cap = 0;
   m->b_nsplit_cap = 0;
   m->b_ready = false;
 }
@@ -308,12 +300,6 @@ int ensure_rope(qdec_model* m, int n_pos) {
   return QDEC_OK;
 }
 
-// chunk partials of the small-M GEMM path, largest over the layer GEMMs
-size_t part_floats(const Dims& d, int T) {
-  return std::max(std::max(skinny_partial_floats(T, d.H, d.qkv()), skinny_partial_floats(T, d.NQ * d.D, d.H)),
-                  std::max(skinny_partial_floats(T, d.H, 2 * d.F), skinny_partial_floats(T, d.F, d.H)));
-}
-
 int ensure_prefill(qdec_model* m, int T) {
   if (T <= m->pf_cap) return QDEC_OK;
   HIP_TRY(hipStreamSynchronize(m->stream));
@@ -324,8 +310,7 @@ int ensure_prefill(qdec_model* m, int T) {
   if ((e = dev_alloc(&m->p_ids, T, "prefill ids")) || (e = dev_alloc(&m->pX, (size_t)T * d.H, "prefill X")) ||
       (e = dev_alloc(&m->pQKV, (size_t)T * d.qkv(), "prefill QKV")) ||
       (e = dev_alloc(&m->pAttn, (size_t)T * d.NQ * d.D, "prefill attention")) ||
-      (e = dev_alloc(&m->pZ, (size_t)T * d.F, "prefill FFN")) ||
-      (T <= 64 && (e = dev_alloc(&m->pPart, part_floats(d, T), "GEMM partials")))) {
+      (e = dev_alloc(&m->pZ, (size_t)T * d.F, "prefill FFN"))) {
     free_prefill(m);
     return e;
   }
@@ -337,7 +322,6 @@ int ensure_prefill(qdec_model* m, int T) {
     return fail(QDEC_E_OOM, "cannot allocate prefill activations for %d tokens", T);
   }
   m->pf_cap = T;
-  m->part_cap = T <= 64 ? part_floats(d, T) : 0;
   return QDEC_OK;
 }
 
@@ -408,12 +392,11 @@ int ensure_batch(qdec_model* m, int nsplit) {
   if (!m->b_ready) {
     const int kmax = std::max(std::max(d.H, d.NQ * d.D), d.F);
     const size_t abytes = m->bf16 ? 2 : 4;
-    const size_t part = m->bf16 ? std::max(part_floats(d, B), skinny_partial_floats(B, d.H, d.V)) : 0;
     int e = 0;
     if ((e = dev_alloc(&m->bX, (size_t)B * d.H, "batch X")) ||
         (e = dev_alloc(&m->bQKV, (size_t)B * d.qkv(), "batch QKV")) ||
         (e = dev_alloc(&m->bAttn, (size_t)B * d.NQ * d.D, "batch attention")) ||
-        (e = dev_alloc(&m->bZ, (size_t)B * d.F, "batch FFN")) || (e = dev_alloc(&m->bPart, part, "batch partials")) ||
+        (e = dev_alloc(&m->bZ, (size_t)B * d.F, "batch FFN")) ||
         (e = dev_alloc(&m->bLogits, (size_t)B * d.V, "batch logits")) ||
         (e = dev_alloc(&m->bKeys, (size_t)B, "batch keys")) || (e = dev_alloc(&m->bTok, (size_t)B, "batch tokens")) ||
         (e = dev_alloc(&m->bAttnCnt, (size_t)B * d.NKV, "batch attention counters"))) {
@@ -427,7 +410,6 @@ int ensure_batch(qdec_model* m, int nsplit) {
       return fail(QDEC_E_OOM, "cannot allocate batch activations");
     }
     HIP_TRY(hipMemset(m->bAttnCnt, 0, (size_t)B * d.NKV * sizeof(unsigned)));
-    m->b_part_cap = part;
     m->b_ready = true;
   }
   if (nsplit > m->b_nsplit_cap) {
@@ -546,8 +528,8 @@ int run_layers_rows(qdec_model* m, int T, float* X, float* QKV, float* Attn, flo
 // "LLM decoder"). rope(l) applies QK-norm + RoPE and appends K/V of layer l;
 // attn(l) writes the attention output rows into Attn; both return a status.
 template <typename RopeFn, typename AttnFn>
-int run_layers(qdec_model* m, int T, float* X, float* QKV, float* Attn, float* Z, void* A0, void* A1, float* part,
-               size_t part_cap, RopeFn rope, AttnFn attn) {
+int run_layers(qdec_model* m, int T, float* X, float* QKV, float* Attn, float* Z, void* A0, void* A1, RopeFn rope,
+               AttnFn attn) {
   const Dims& d = m->d;
   hipStream_t st = m->stream;
   const bool bf = m->bf16;
@@ -558,15 +540,15 @@ int run_layers(qdec_model* m, int T, float* X, float* QKV, float* Attn, float* Z
   for (int l = 0; l < d.L; ++l) {
     const LayerW& w = m->layers[l];
     LAUNCH(norm_in(X, d.H, w.in_norm));
-    LAUNCH(launch_gemm(bf, EPI_STORE, A0, A1, T, d.H, w.wqkv, d.qkv(), QKV, d.qkv(), st, part, part_cap));
+    LAUNCH(launch_gemm(bf, EPI_STORE, A0, A1, T, d.H, w.wqkv, d.qkv(), QKV, d.qkv(), st));
     if (int e = rope(l)) return e;
     if (int e = attn(l)) return e;
     LAUNCH(norm_in(Attn, d.NQ * d.D, nullptr));
-    LAUNCH(launch_gemm(bf, EPI_RESID, A0, A1, T, d.NQ * d.D, w.wo, d.H, X, d.H, st, part, part_cap));
+    LAUNCH(launch_gemm(bf, EPI_RESID, A0, A1, T, d.NQ * d.D, w.wo, d.H, X, d.H, st));
     LAUNCH(norm_in(X, d.H, w.post_norm));
-    LAUNCH(launch_gemm(bf, EPI_SWIGLU, A0, A1, T, d.H, w.wgu, 2 * d.F, Z, d.F, st, part, part_cap));
+    LAUNCH(launch_gemm(bf, EPI_SWIGLU, A0, A1, T, d.H, w.wgu, 2 * d.F, Z, d.F, st));
     LAUNCH(norm_in(Z, d.F, nullptr));
-    LAUNCH(launch_gemm(bf, EPI_RESID, A0, A1, T, d.F, w.wd, d.H, X, d.H, st, part, part_cap));
+    LAUNCH(launch_gemm(bf, EPI_RESID, A0, A1, T, d.F, w.wd, d.H, X, d.H, st));
   }
   return QDEC_OK;
 }
@@ -628,16 +610,14 @@ int run_decode_batch(qdec_state* const* states, int n, const int32_t* tokens, fl
       LAUNCH(launch_argmax_final(m->bKeys, n, argmax ? argmax : m->bTok, st));
       return QDEC_OK;
     }
-  } else if (int e = run_layers(m, n, m->bX, m->bQKV, m->bAttn, m->bZ, m->bA0, m->bA1, m->bPart, m->b_part_cap,
-                                rope, attn)) {
+  } else if (int e = run_layers(m, n, m->bX, m->bQKV, m->bAttn, m->bZ, m->bA0, m->bA1, rope, attn)) {
     return e;
   }
   if (m->bf16)
     LAUNCH(launch_rms_split(m->bX, n, d.H, m->final_norm, d.eps, (uint16_t*)m->bA0, (uint16_t*)m->bA1, st));
   else
     LAUNCH(launch_rms_apply(m->bX, n, d.H, m->final_norm, d.eps, (float*)m->bA0, st));
-  LAUNCH(launch_gemm(m->bf16, EPI_STORE, m->bA0, m->bA1, n, d.H, m->embed, d.V, lg, d.V, st, m->bPart,
-                     m->b_part_cap));
+  LAUNCH(launch_gemm(m->bf16, EPI_STORE, m->bA0, m->bA1, n, d.H, m->embed, d.V, lg, d.V, st));
   LAUNCH(launch_argmax_rows(lg, n, d.V, m->bKeys, st));
   LAUNCH(launch_argmax_final(m->bKeys, n, argmax ? argmax : m->bTok, st));
   return QDEC_OK;
@@ -668,8 +648,7 @@ int run_prefill(qdec_state* s, int T, const float* audio, int a0, int La, float*
   if (fused) {
     int nss = 1;
     if (int e = run_layers_rows(m, T, m->pX, m->pQKV, m->pAttn, m->pZ, 1, rope, attn, &nss)) return e;
-  } else if (int e = run_layers(m, T, m->pX, m->pQKV, m->pAttn, m->pZ, m->pA0, m->pA1, m->pPart, m->part_cap, rope,
-                                attn)) {
+  } else if (int e = run_layers(m, T, m->pX, m->pQKV, m->pAttn, m->pZ, m->pA0, m->pA1, rope, attn)) {
     return e;
   }
   LAUNCH(launch_lm_head(d, bf, m->embed, m->pX + (size_t)(T - 1) * d.H, m->final_norm, logits, m->keys, st));

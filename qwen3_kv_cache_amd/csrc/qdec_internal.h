@@ -129,11 +129,10 @@ hipError_t launch_rms_split(const float* X, int T, int K, const float* gain, flo
                             uint16_t* lo, hipStream_t st);
 hipError_t launch_rms_apply(const float* X, int T, int K, const float* gain, float eps, float* out,
                             hipStream_t st);
-// M <= 64 with bf16 weights takes the small-M path when `part` holds at
-// least skinny_partial_floats(M, K, N) floats (chunk partials).
+// C[M, N] (+)= A[M, K] . W[N, K]^T with a bf16 hi/lo split A (bf16 weights)
+// or fp32 A (fp32 weights); the tiled MFMA kernel for M > 64.
 hipError_t launch_gemm(bool bf16, Epi epi, const void* A0, const void* A1, int M, int K, const void* W, int N,
-                       float* C, int ldc, hipStream_t st, float* part = nullptr, size_t part_cap = 0);
-size_t skinny_partial_floats(int M, int K, int N);
+                       float* C, int ldc, hipStream_t st);
 hipError_t launch_to_f32(const void* src, bool bf16, size_t n, float* dst, hipStream_t st);
 
 // ---- persistent decode (qdec_decode.hip)

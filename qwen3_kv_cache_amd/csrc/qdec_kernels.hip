@@ -1000,96 +1000,6 @@ __global__ __launch_bounds__(256) void gemm_bf16x2_kernel(const uint16_t* __rest
     }
 }
 
-// Small-M GEMM (M <= 64, prefill of short prompts and batched decode):
-// C[M, N] (+)= (Ahi + Alo)[M, K] . W[N, K]^T. A launch of (N / (16 NT)) x nkc
-// single-wave workgroups: wave (n, c) streams its 16 NT weight rows over K
-// chunk c once and multiplies them with every row of A (small, L2-resident)
-// in MT tiles of 16 rows. Enough waves are in flight to stream the weights at
-// HBM rate even for M = 1. Chunk partials go to P[c][M][N];
-// skinny_epilogue_kernel sums them in a fixed order and applies the
-// epilogue, so results do not depend on scheduling. Rows of A past M are
-// clamped to row M - 1: an MFMA output row depends only on its own A row, and
-// those rows are never stored.
-template <int MT, int NT>
-struct SkinnyStep {
-  uint4 b[NT], ah[MT], al[MT];
-  __device__ __forceinline__ void load(const uint16_t* const* wrow, const uint16_t* const* hrow,
-                                       const uint16_t* const* lrow, int k) {
-#pragma unroll
-    for (int j = 0; j < NT; ++j) b[j] = *reinterpret_cast<const uint4*>(wrow[j] + k);
-#pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      ah[i] = *reinterpret_cast<const uint4*>(hrow[i] + k);
-      al[i] = *reinterpret_cast<const uint4*>(lrow[i] + k);
-    }
-  }
-  __device__ __forceinline__ void mma(f32x4_t (&acc)[MT][NT]) const {
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ah[i]),
-                                                            __builtin_bit_cast(bf16x8_t, b[j]), acc[i][j], 0, 0, 0);
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, al[i]),
-                                                            __builtin_bit_cast(bf16x8_t, b[j]), acc[i][j], 0, 0, 0);
-      }
-  }
-};
-
-template <int MT, int NT>
-__global__ __launch_bounds__(64) void gemm_skinny_kernel(const uint16_t* __restrict__ Ahi,
-                                                          const uint16_t* __restrict__ Alo, int M, int K,
-                                                          const uint16_t* __restrict__ W, int N, int KC,
-                                                          float* __restrict__ P) {
-  constexpr int U = 4;  // k-steps of loads in flight
-  const int lane = threadIdx.x;
-  const int n0 = blockIdx.x * 16 * NT;
-  const int c = blockIdx.y;
-  const int kb = c * KC, ke = min(K, kb + KC);
-  const int r = lane % 16, kq = (lane / 16) * 8;
-  const uint16_t *wrow[NT], *hrow[MT], *lrow[MT];
-#pragma unroll
-  for (int j = 0; j < NT; ++j) wrow[j] = W + (size_t)(n0 + j * 16 + r) * K + kq;
-#pragma unroll
-  for (int i = 0; i < MT; ++i) {
-    const size_t row = (size_t)min(i * 16 + r, M - 1);
-    hrow[i] = Ahi + row * K + kq;
-    lrow[i] = Alo + row * K + kq;
-  }
-  f32x4_t acc[MT][NT];
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int j = 0; j < NT; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  int k = kb;
-  for (; k + 32 * U <= ke; k += 32 * U) {
-    SkinnyStep<MT, NT> st[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) st[u].load(wrow, hrow, lrow, k + 32 * u);
-    // keep every load of the batch ahead of the first multiply: the default
-    // schedule interleaves them and waits on each load in turn
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int u = 0; u < U; ++u) st[u].mma(acc);
-  }
-  for (; k < ke; k += 32) {
-    SkinnyStep<MT, NT> st;
-    st.load(wrow, hrow, lrow, k);
-    st.mma(acc);
-  }
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = i * 16 + 4 * (lane / 16) + e;
-      if (row < M) {
-        float* out = P + ((size_t)c * M + row) * N + n0 + r;
-#pragma unroll
-        for (int j = 0; j < NT; ++j) out[j * 16] = acc[i][j][e];
-      }
-    }
-}
-
 // Small-M GEMM with fused prologue and epilogue, for up to 64 activation rows
 // (batched decode, short prompts): C[M, N] = op(A)[M, K] . W[N, K]^T.
 // op(A) is A itself or, with NORM, the RMS-normalised rows A * inv * gain,
@@ -1340,38 +1250,6 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(RowsGemm g) {
       best = kk > best ? kk : best;
     }
     atomicMax(g.keys + threadIdx.x, best);
-  }
-}
-
-// Sums the nkc chunk partials of gemm_skinny_kernel (chunk order fixed) and
-// applies the epilogue. SwiGLU: columns come in groups of 16 (8 gate rows,
-// then the matching 8 up rows); output j of a row is silu(gate) * up of gate
-// column (j / 8) * 16 + j % 8.
-template <int EPI>
-__global__ __launch_bounds__(256) void skinny_epilogue_kernel(const float* __restrict__ P, int nkc, int M, int N,
-                                                              float* __restrict__ C, int ldc) {
-  const int n_out = EPI == EPI_SWIGLU ? N / 2 : N;
-  const size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
-  if (idx >= (size_t)M * n_out) return;
-  const int row = (int)(idx / n_out), j = (int)(idx % n_out);
-  const size_t stride = (size_t)M * N;
-  if (EPI == EPI_SWIGLU) {
-    const int gc = (j / kGuGroup) * 2 * kGuGroup + j % kGuGroup;
-    const float* pg = P + (size_t)row * N + gc;
-    float g = 0.f, u = 0.f;
-    for (int c = 0; c < nkc; ++c) {
-      g += pg[c * stride];
-      u += pg[c * stride + kGuGroup];
-    }
-    C[(size_t)row * ldc + j] = silu_mul(g, u);
-  } else {
-    const float* pp = P + (size_t)row * N + j;
-    float v = 0.f;
-    for (int c = 0; c < nkc; ++c) v += pp[c * stride];
-    if (EPI == EPI_RESID)
-      C[(size_t)row * ldc + j] += v;
-    else
-      C[(size_t)row * ldc + j] = v;
   }
 }
 
@@ -1694,39 +1572,6 @@ hipError_t launch_rms_apply(const float* X, int T, int K, const float* gain, flo
   return hipGetLastError();
 }
 
-namespace {
-
-int skinny_nt(int N) { return N % 32 == 0 ? 2 : 1; }
-
-// K chunks per column tile: about 2048 waves in flight, chunks of at least
-// 128 columns of K (a multiple of 32)
-int skinny_chunk_len(int K, int N) {
-  const int tiles = N / (16 * skinny_nt(N));
-  const int nkc = std::max(1, std::min(K / 128, (2048 + tiles - 1) / tiles));
-  return ((K + nkc - 1) / nkc + 31) / 32 * 32;
-}
-
-int skinny_chunks(int K, int N) {
-  const int kc = skinny_chunk_len(K, N);
-  return (K + kc - 1) / kc;
-}
-
-template <int NT>
-void launch_skinny(dim3 grid, const uint16_t* hi, const uint16_t* lo, int M, int K, const uint16_t* w, int N,
-                   int KC, float* part, hipStream_t st) {
-  if (M <= 16)
-    gemm_skinny_kernel<1, NT><<<grid, 64, 0, st>>>(hi, lo, M, K, w, N, KC, part);
-  else if (M <= 32)
-    gemm_skinny_kernel<2, NT><<<grid, 64, 0, st>>>(hi, lo, M, K, w, N, KC, part);
-  else if (M <= 48)
-    gemm_skinny_kernel<3, NT><<<grid, 64, 0, st>>>(hi, lo, M, K, w, N, KC, part);
-  else
-    gemm_skinny_kernel<4, NT><<<grid, 64, 0, st>>>(hi, lo, M, K, w, N, KC, part);
-}
-
-}  // namespace
-
-size_t skinny_partial_floats(int M, int K, int N) { return (size_t)skinny_chunks(K, N) * M * N; }
 
 namespace {
 
@@ -1802,31 +1647,7 @@ hipError_t launch_gemm_rows(Epi epi, bool norm, const RowsGemm& g0, hipStream_t 
 }
 
 hipError_t launch_gemm(bool bf16, Epi epi, const void* A0, const void* A1, int M, int K, const void* W, int N,
-                       float* C, int ldc, hipStream_t st, float* part, size_t part_cap) {
-  const int nkc = skinny_chunks(K, N);
-  // a single chunk of a plain store needs no partials: the GEMM writes C
-  const bool direct = nkc == 1 && epi == EPI_STORE && ldc == N;
-  if (bf16 && M >= 1 && M <= 64 && N % 16 == 0 && K % 32 == 0 &&
-      (direct || (part && skinny_partial_floats(M, K, N) <= part_cap))) {
-    const int KC = skinny_chunk_len(K, N), nt = skinny_nt(N);
-    const dim3 grid(N / (16 * nt), nkc);
-    const uint16_t *hi = (const uint16_t*)A0, *lo = (const uint16_t*)A1, *w = (const uint16_t*)W;
-    float* P = direct ? C : part;
-    if (nt == 2)
-      launch_skinny<2>(grid, hi, lo, M, K, w, N, KC, P, st);
-    else
-      launch_skinny<1>(grid, hi, lo, M, K, w, N, KC, P, st);
-    if (direct) return hipGetLastError();
-    const size_t n_out = (size_t)M * (epi == EPI_SWIGLU ? N / 2 : N);
-    const unsigned blocks = (unsigned)((n_out + 255) / 256);
-    if (epi == EPI_STORE)
-      skinny_epilogue_kernel<EPI_STORE><<<blocks, 256, 0, st>>>(part, nkc, M, N, C, ldc);
-    else if (epi == EPI_RESID)
-      skinny_epilogue_kernel<EPI_RESID><<<blocks, 256, 0, st>>>(part, nkc, M, N, C, ldc);
-    else
-      skinny_epilogue_kernel<EPI_SWIGLU><<<blocks, 256, 0, st>>>(part, nkc, M, N, C, ldc);
-    return hipGetLastError();
-  }
+                       float* C, int ldc, hipStream_t st) {
   if (bf16 && M > 64 && N % tg::BN == 0 && K % tg::BK == 0) {
     const dim3 grid(N / tg::BN, (M + tg::BM - 1) / tg::BM);
     const uint16_t *hi = (const uint16_t*)A0, *lo = (const uint16_t*)A1, *w = (const uint16_t*)W;

@@ -114,6 +114,9 @@ BATCH = {
     "d32_g4_f32_b3": (MID["d32_g4_f32"][0], 45, 3, 9, 3, 4),
     # D=128 (0.6B head geometry), the full batch of 16 rows
     "d128_g2_b16": (MID["d128_g2"][0], 77, 8, 20, 16, 3),
+    # 300-token prompt: 8 clones whose first 18 pages are shared, attention
+    # over three 128-position splits (the last one partial)
+    "d128_g2_b8_shared": (MID["d128_g2"][0], 300, 8, 20, 8, 4),
 }
 
 
