@@ -437,7 +437,7 @@ int ensure_rows(qdec_model* m) {
   for (auto& kn : shapes) {
     if (!rows_fits(R, kn[0], kn[1])) continue;
     part = std::max(part, rows_partial_floats(R, kn[0], kn[1]));
-    cnt = std::max(cnt, rows_counters(kn[0], kn[1]));
+    cnt = std::max(cnt, rows_counters(R, kn[0], kn[1]));
   }
   const size_t nss = (size_t)std::max(1, d.H / 16);
   int e = 0;

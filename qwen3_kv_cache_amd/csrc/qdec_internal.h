@@ -91,7 +91,7 @@ struct RowsGemm {
 bool rows_fits(int M, int K, int N);
 int rows_tile_cols(int N);
 size_t rows_partial_floats(int M, int K, int N);
-int rows_counters(int K, int N);
+int rows_counters(int M, int K, int N);
 hipError_t launch_gemm_rows(Epi epi, bool norm, const RowsGemm& g, hipStream_t st);
 hipError_t launch_lm_head(const Dims& d, bool bf16, const void* E, const float* x, const float* gain,
                           float* logits, unsigned long long* key, hipStream_t st);

@@ -1073,7 +1073,7 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(RowsGemm g) {
   __shared__ int s_last;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int tile = blockIdx.x, c = blockIdx.y, nkc = gridDim.y;
-  const int n0 = tile * TC;
+  const int n0 = tile * TC, m0 = blockIdx.z * TR;  // output tile: rows m0 + [0, TR), columns n0 + [0, TC)
   const int M = g.M, K = g.K;
   const int kw = g.KC / 4;
   const int kb = c * g.KC + wave * kw, ke = min(K, kb + kw);
@@ -1088,7 +1088,7 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(RowsGemm g) {
   for (int i = 0; i < MT; ++i) {
     // rows past M repeat row M - 1: an MFMA output row depends only on its
     // own A row, and those rows are never stored
-    const int row = min(i * 16 + r, M - 1);
+    const int row = min(m0 + i * 16 + r, M - 1);
     arow[i] = g.A + (size_t)row * g.lda + kq;
     inv[i] = 1.f;
     if (NORM) {
@@ -1149,8 +1149,9 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(RowsGemm g) {
     // has seen every other workgroup's stores complete before their
     // increments; it still checks each tag, waiting (bounded) for a word
     // that is not yet visible.
-    unsigned long long* pt = g.P + (size_t)tile * S * kWave;
-    const size_t cstride = (size_t)gridDim.x * S * kWave;
+    const int ot = blockIdx.z * gridDim.x + tile;  // output tile index
+    unsigned long long* pt = g.P + (size_t)ot * S * kWave;
+    const size_t cstride = (size_t)gridDim.x * gridDim.z * S * kWave;
     const unsigned long long tag = (unsigned long long)g.tag << 32;
 #pragma unroll
     for (int q = 0; q < MT * NT; ++q)
@@ -1160,7 +1161,7 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(RowsGemm g) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (threadIdx.x == 0)
-      s_last = __hip_atomic_fetch_add(g.cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+      s_last = __hip_atomic_fetch_add(g.cnt + ot, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                (unsigned)(nkc - 1);
     __syncthreads();
     if (!s_last) return;
@@ -1202,7 +1203,7 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(RowsGemm g) {
 #pragma unroll
     for (int q = 0; q < MT * NT; ++q) v[q] = t[q];
     if (late) __hip_atomic_store(g.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    if (threadIdx.x == 0) __hip_atomic_store(g.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) __hip_atomic_store(g.cnt + ot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
 #pragma unroll
@@ -1216,15 +1217,16 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(RowsGemm g) {
   if (EPI == EPI_SWIGLU) {
     for (int idx = threadIdx.x; idx < TR * NT * 8; idx += blockDim.x) {
       const int rt = idx / (NT * 8), o = idx % (NT * 8), j = o / 8, e = o % 8;
-      if (rt < M) g.C[(size_t)rt * g.ldc + (n0 / 16 + j) * 8 + e] = silu_mul(tv[rt][16 * j + e], tv[rt][16 * j + 8 + e]);
+      if (m0 + rt < M)
+        g.C[(size_t)(m0 + rt) * g.ldc + (n0 / 16 + j) * 8 + e] = silu_mul(tv[rt][16 * j + e], tv[rt][16 * j + 8 + e]);
     }
     return;
   }
   if (EPI != EPI_HEAD || g.C) {
     for (int idx = threadIdx.x; idx < TR * TC; idx += blockDim.x) {
       const int rt = idx / TC, ct = idx % TC;
-      if (rt < M) {
-        float* dst = g.C + (size_t)rt * g.ldc + n0 + ct;
+      if (m0 + rt < M) {
+        float* dst = g.C + (size_t)(m0 + rt) * g.ldc + n0 + ct;
         if (EPI == EPI_RESID) {
           const float x = *dst + tv[rt][ct];
           *dst = x;
@@ -1237,19 +1239,19 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(RowsGemm g) {
   }
   if (EPI == EPI_RESID) {
     __syncthreads();
-    if (threadIdx.x < M) {
+    if (threadIdx.x < TR && m0 + (int)threadIdx.x < M) {
       float ss = 0.f;
       for (int ct = 0; ct < TC; ++ct) ss = fmaf(tv[threadIdx.x][ct], tv[threadIdx.x][ct], ss);
-      g.ssq_out[(size_t)tile * M + threadIdx.x] = ss;
+      g.ssq_out[(size_t)tile * M + m0 + threadIdx.x] = ss;
     }
   }
-  if (EPI == EPI_HEAD && threadIdx.x < M) {
+  if (EPI == EPI_HEAD && threadIdx.x < TR && m0 + (int)threadIdx.x < M) {
     unsigned long long best = 0ull;
     for (int ct = 0; ct < TC; ++ct) {
       const unsigned long long kk = argmax_key(tv[threadIdx.x][ct], n0 + ct);
       best = kk > best ? kk : best;
     }
-    atomicMax(g.keys + threadIdx.x, best);
+    atomicMax(g.keys + m0 + threadIdx.x, best);
   }
 }
 
@@ -1618,13 +1620,12 @@ int rows_tile_cols(int N) { return rows_plan(32, N).nt * 16; }
 size_t rows_partial_floats(int M, int K, int N) {
   const RowsPlan p = rows_plan(K, N);
   if (p.nkc == 1) return 0;
-  const int mt = (M + 15) / 16;
-  return (size_t)p.nkc * p.tiles * mt * p.nt * 4 * 64;  // 8-byte words
+  return (size_t)p.nkc * p.tiles * ((M + 15) / 16) * p.nt * 4 * 64;  // 8-byte words
 }
 
-int rows_counters(int K, int N) {
+int rows_counters(int M, int K, int N) {
   const RowsPlan p = rows_plan(K, N);
-  return p.nkc == 1 ? 0 : p.tiles;
+  return p.nkc == 1 ? 0 : p.tiles * ((M + 15) / 16);
 }
 
 hipError_t launch_gemm_rows(Epi epi, bool norm, const RowsGemm& g0, hipStream_t st) {
@@ -1633,17 +1634,10 @@ hipError_t launch_gemm_rows(Epi epi, bool norm, const RowsGemm& g0, hipStream_t 
   if (p.nkc > 1 && (!g0.P || !g0.cnt)) return hipErrorInvalidValue;
   RowsGemm g = g0;
   g.KC = p.kc;
-  const dim3 grid(p.tiles, p.nkc);
-  const int mt = (g.M + 15) / 16;
-#define QDEC_ROWS_CASE(MT)                                                        \
-  if (mt == MT) return p.nt == 2 ? rows_dispatch<MT, 2>(epi, norm, grid, g, st) \
-                                 : rows_dispatch<MT, 1>(epi, norm, grid, g, st);
-  QDEC_ROWS_CASE(1)
-  QDEC_ROWS_CASE(2)
-  QDEC_ROWS_CASE(3)
-  QDEC_ROWS_CASE(4)
-#undef QDEC_ROWS_CASE
-  return hipErrorInvalidValue;
+  // one 16-row tile per workgroup: rows past 16 take more workgroups (their
+  // weight tiles are read again, mostly from the XCD's L2), not more registers
+  const dim3 grid(p.tiles, p.nkc, (g.M + 15) / 16);
+  return p.nt == 2 ? rows_dispatch<1, 2>(epi, norm, grid, g, st) : rows_dispatch<1, 1>(epi, norm, grid, g, st);
 }
 
 hipError_t launch_gemm(bool bf16, Epi epi, const void* A0, const void* A1, int M, int K, const void* W, int N,
