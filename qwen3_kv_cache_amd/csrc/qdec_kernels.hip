@@ -1582,13 +1582,16 @@ struct RowsPlan {
 };
 
 // 32 output columns per workgroup for wide outputs (each A load then feeds
-// two column tiles), 16 otherwise; K chunks (multiples of 128, one k-step of
-// 32 per wave at least) so that about 512 workgroups stream the weights
+// two column tiles), 16 otherwise; K is split into chunks (multiples of 128,
+// one k-step of 32 per wave at least) only until there are 128 column-tile x
+// chunk workgroups per row tile: the split-K exchange costs more than the
+// extra weight parallelism gains beyond that (measured on batched decode and
+// 48-token prompts)
 RowsPlan rows_plan(int K, int N) {
   RowsPlan p;
   p.nt = N % 32 == 0 && N >= 2048 ? 2 : 1;
   p.tiles = N / (16 * p.nt);
-  const int want = std::max(1, (512 + p.tiles - 1) / p.tiles);
+  const int want = std::max(1, (128 + p.tiles - 1) / p.tiles);
   p.kc = std::max(128, ((K + want - 1) / want + 127) / 128 * 128);
   p.nkc = (K + p.kc - 1) / p.kc;
   return p;
