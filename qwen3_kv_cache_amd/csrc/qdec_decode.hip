@@ -295,7 +295,7 @@ struct DecParams {
   const float* rope_sin;
   const int64_t* page_table;
   int L, H, NQ, NKV, F, V;
-  float eps, scale;
+  float eps, scale;  // scale: log2(e) / sqrt(head_dim), scores in base 2
   int pos0, nsteps, token;
   const int32_t* token_dev;
   float* logits;        // [nsteps, V] or null
@@ -665,7 +665,8 @@ __device__ __forceinline__ void load_kvrow(const DecParams& p, const u64* ptab, 
 //    keys with the probabilities broadcast from LDS, so P.V needs no
 //    cross-lane reduction.
 // The wave's result per head: running max, sum and unnormalised output in
-// wm, wl, wo. Block 0's K/V come from prefetch().
+// wm, wl, wo. Block 0's K/V come from prefetch(). Scores are in base 2 (q
+// carries log2(e) / sqrt(D)), so the softmax uses the hardware exp2.
 template <int D, int G>
 struct Attn {
   static constexpr int PARTS = 4;              // lanes per key for the scores
@@ -759,8 +760,8 @@ struct Attn {
         mx = max32(max16(mx));
         const float mn = fmaxf(m[h], mx);
         if (mn == -INFINITY) continue;  // no valid key seen yet by this wave (wave-uniform)
-        const float alpha = expf(m[h] - mn);
-        const float pr = key < n_keys ? expf(sc - mn) : 0.f;
+        const float alpha = __builtin_amdgcn_exp2f(m[h] - mn);
+        const float pr = key < n_keys ? __builtin_amdgcn_exp2f(sc - mn) : 0.f;
         float ps = pr + dpp<kDppRor4>(pr);
         ps += dpp<kDppXor8>(ps);
         ps = sum32(sum16(ps));
@@ -1212,7 +1213,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
 #pragma unroll
             for (int w2 = 0; w2 < kExWaves; ++w2) {
               const float mw = wm[w2 * G + h];
-              const float f = (mw == -INFINITY) ? 0.f : expf(mw - M);
+              const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
               lt = fmaf(f, wl[w2 * G + h], lt);
               o = fmaf(f, wo[(w2 * G + h) * D + d], o);
             }
@@ -1231,7 +1232,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
 #pragma unroll
                 for (int w2 = 0; w2 < kExWaves; ++w2) {
                   const float mw = wm[w2 * G + h];
-                  const float f = (mw == -INFINITY) ? 0.f : expf(mw - M);
+                  const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
                   v = fmaf(f, e == 1 ? wl[w2 * G + h] : wo[(w2 * G + h) * D + (e - 2)], v);
                 }
               }
@@ -1247,7 +1248,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
             float o = 0.f, lt = 0.f;
             for (int s = 0; s < nsplit; ++s) {
               const float* ps = stage + (s * G + h) * (D + 2);
-              const float f = (ps[0] == -INFINITY) ? 0.f : expf(ps[0] - M);
+              const float f = (ps[0] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ps[0] - M);
               o = fmaf(f, ps[2 + d], o);
               lt = fmaf(f, ps[1], lt);
             }
@@ -1517,7 +1518,8 @@ hipError_t launch_decode(const DecLaunch& a, hipStream_t st) {
   p.page_table = a.page_table;
   p.L = d.L; p.H = d.H; p.NQ = d.NQ; p.NKV = d.NKV; p.F = d.F; p.V = d.V;
   p.eps = d.eps;
-  p.scale = 1.f / sqrtf((float)d.D);
+  // scores in base 2: q carries log2(e) / sqrt(D), the softmax uses exp2
+  p.scale = 1.4426950408889634f / sqrtf((float)d.D);
   p.pos0 = a.pos;
   p.nsteps = a.nsteps;
   p.token = a.token;
