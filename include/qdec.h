@@ -186,6 +186,43 @@ int qdec_decode_batch(qdec_state* const* states, int32_t n, const int32_t* token
  * be destroyed first. */
 int qdec_clone_state(const qdec_state* src, qdec_state** dst);
 
+/* Sampling options after the LM head (NCNN page section 1: greedy,
+ * temperature, top-k, top-p and repetition penalty; section 6: greedy is the
+ * default, the others serve non-deterministic generation). */
+typedef struct {
+  float temperature;         /* 0: greedy (lowest index of the maximum); > 0: sample */
+  int32_t top_k;             /* 1 .. QDEC_SAMPLE_TOP_K_MAX when temperature > 0 */
+  float top_p;               /* (0, 1]; 1 keeps the whole top-k */
+  float repetition_penalty;  /* > 0; 1 is off */
+} qdec_sampling;
+
+#define QDEC_SAMPLE_TOP_K_MAX 128
+
+/* Pick one token per row of logits (e.g. from qdec_decode_step or
+ * qdec_decode_batch), in this order: every distinct id of the row's history
+ * has its logit z divided by repetition_penalty if z > 0, else multiplied by
+ * it; greedy when temperature is 0; otherwise z / temperature, candidates
+ * ordered by (value descending, index ascending), the first top_k kept,
+ * softmax over them, the shortest prefix whose mass reaches top_p kept, and
+ * the first candidate whose cumulative mass exceeds uniforms_host[r] times the
+ * kept mass is the token. The page gives no formulas; this is the common
+ * reading. Values and divisions in float32, the softmax and sums in float64.
+ *   logits_dev:    DEVICE fp32 [n_rows, vocab] (borrowed, not modified)
+ *   n_rows:        1 .. 16
+ *   history_dev:   DEVICE int32 [n_rows, history_len] token ids (ids outside
+ *                  [0, vocab) are ignored, e.g. -1 padding); NULL if
+ *                  history_len is 0
+ *   uniforms_host: HOST fp32 [n_rows], each in [0, 1), supplied by the caller
+ *                  (the library draws no random numbers)
+ *   tokens_dev:    DEVICE int32 [n_rows], receives the picks
+ * Work is enqueued on the model's stream. Errors: QDEC_E_INVALID for bad
+ * arguments (top_k outside 1 .. QDEC_SAMPLE_TOP_K_MAX or above vocab with
+ * temperature > 0, top_p outside (0, 1], a penalty <= 0, a uniform outside
+ * [0, 1), non-finite values), QDEC_E_DEVICE for HIP errors. Non-finite
+ * logits give an unspecified token. */
+int qdec_sample(qdec_model* m, const float* logits_dev, int32_t n_rows, const qdec_sampling* params,
+                const int32_t* history_dev, int32_t history_len, const float* uniforms_host, int32_t* tokens_dev);
+
 /* n_past of the state (-1 for NULL). */
 int32_t qdec_state_pos(const qdec_state* s);
 

@@ -52,11 +52,12 @@ def penalize(logits: np.ndarray, history: Sequence[int], rho: float) -> np.ndarr
 
 def candidates(z: np.ndarray, top_k: int) -> np.ndarray:
     """Step 4: indices ordered by (value descending, index ascending), the
-    first top_k of them (all when top_k is 0)."""
-    order = sorted(range(z.size), key=lambda i: (-float(z[i]), i))
+    first top_k of them (all when top_k is 0). numpy's stable lexsort: the
+    last key (-value) is the primary one, the index breaks ties."""
+    order = np.lexsort((np.arange(z.size), -z.astype(np.float64)))
     if top_k > 0:
         order = order[:top_k]
-    return np.array(order, dtype=np.int64)
+    return order.astype(np.int64)
 
 
 def kept_distribution(logits: np.ndarray, params: SamplingParams, history: Sequence[int] = ()):

@@ -163,6 +163,9 @@ struct qdec_model {
   unsigned rows_tag = 1;  // tag of the next fused GEMM launch
   unsigned* rCnt = nullptr;
   float* rSsq = nullptr;
+  // sampling workspace: two candidate-key buffers
+  unsigned long long* sBuf0 = nullptr;
+  unsigned long long* sBuf1 = nullptr;
   PagePool pool;
   int live_states = 0;
   // persistent decode
@@ -253,6 +256,8 @@ void free_model(qdec_model* m) {
   (void)hipFree(m->rP);
   (void)hipFree(m->rCnt);
   (void)hipFree(m->rSsq);
+  (void)hipFree(m->sBuf0);
+  (void)hipFree(m->sBuf1);
   (void)hipFree(m->final_norm);
   (void)hipFree(m->wbuf);
   (void)hipFree(m->nbuf);
@@ -969,6 +974,46 @@ int qdec_decode_batch(qdec_state* const* states, int32_t n, const int32_t* token
   if (int e = check_outputs(m, n, logits_dev, argmax_dev)) return e;
   if (int e = run_decode_batch(states, n, tokens_host, logits_dev, argmax_dev)) return e;
   for (int i = 0; i < n; ++i) states[i]->n_past += 1;
+  return ok();
+}
+
+int qdec_sample(qdec_model* m, const float* logits_dev, int32_t n_rows, const qdec_sampling* params,
+                const int32_t* history_dev, int32_t history_len, const float* uniforms_host, int32_t* tokens_dev) {
+  if (!m || !params || !uniforms_host) return fail(QDEC_E_INVALID, "model, params or uniforms_host is NULL");
+  const Dims& d = m->d;
+  if (n_rows < 1 || n_rows > kMaxBatch) return fail(QDEC_E_INVALID, "n_rows %d outside [1, %d]", n_rows, kMaxBatch);
+  const qdec_sampling& p = *params;
+  if (!(p.temperature >= 0.f) || !std::isfinite(p.temperature))
+    return fail(QDEC_E_INVALID, "temperature must be finite and >= 0");
+  if (p.temperature > 0.f && (p.top_k < 1 || p.top_k > QDEC_SAMPLE_TOP_K_MAX || p.top_k > d.V))
+    return fail(QDEC_E_INVALID, "top_k %d outside [1, %d]", p.top_k, std::min(QDEC_SAMPLE_TOP_K_MAX, d.V));
+  if (!(p.top_p > 0.f && p.top_p <= 1.f)) return fail(QDEC_E_INVALID, "top_p must lie in (0, 1]");
+  if (!(p.repetition_penalty > 0.f) || !std::isfinite(p.repetition_penalty))
+    return fail(QDEC_E_INVALID, "repetition_penalty must be finite and > 0");
+  if (history_len < 0 || (history_len > 0 && !history_dev))
+    return fail(QDEC_E_INVALID, "history_len %d with history_dev %p", history_len, (const void*)history_dev);
+  SampleUniforms u{};
+  for (int r = 0; r < n_rows; ++r) {
+    if (!(uniforms_host[r] >= 0.f && uniforms_host[r] < 1.f))
+      return fail(QDEC_E_INVALID, "uniforms_host[%d] outside [0, 1)", r);
+    u.u[r] = uniforms_host[r];
+  }
+  if (int e = check_dev(logits_dev, (size_t)n_rows * d.V * sizeof(float), "logits_dev")) return e;
+  if (int e = check_dev(tokens_dev, (size_t)n_rows * sizeof(int32_t), "tokens_dev")) return e;
+  if (history_len > 0) {
+    if (int e = check_dev(history_dev, (size_t)n_rows * history_len * sizeof(int32_t), "history_dev")) return e;
+  }
+  if (!m->sBuf0) {
+    const size_t words = sample_buffer_words(d.V);
+    if (int e = dev_alloc(&m->sBuf0, words, "sampling buffer")) return e;
+    if (int e = dev_alloc(&m->sBuf1, words, "sampling buffer")) {
+      (void)hipFree(m->sBuf0);
+      m->sBuf0 = nullptr;
+      return e;
+    }
+  }
+  LAUNCH(launch_sample(logits_dev, n_rows, d.V, history_dev, history_len, p.repetition_penalty, p.temperature,
+                       p.top_k, p.top_p, u, m->sBuf0, m->sBuf1, tokens_dev, m->stream));
   return ok();
 }
 

@@ -135,6 +135,19 @@ hipError_t launch_gemm(bool bf16, Epi epi, const void* A0, const void* A1, int M
                        float* C, int ldc, hipStream_t st);
 hipError_t launch_to_f32(const void* src, bool bf16, size_t n, float* dst, hipStream_t st);
 
+// ---- sampling after the LM head (qdec_kernels.hip)
+constexpr int kSampleKMax = 128;  // largest top-k
+struct SampleUniforms {
+  float u[kMaxBatch];
+};
+// tok[r] for rows r < n of logits [n, V]; hist [n, nh] ids (outside [0, V)
+// ignored); temp 0 = greedy (penalty still applied); buf0/buf1 hold
+// sample_buffer_words(V) words each.
+hipError_t launch_sample(const float* logits, int n, int V, const int32_t* hist, int nh, float rho, float temp,
+                         int top_k, float top_p, const SampleUniforms& u, unsigned long long* buf0,
+                         unsigned long long* buf1, int32_t* tok, hipStream_t st);
+size_t sample_buffer_words(int V);
+
 // ---- persistent decode (qdec_decode.hip)
 // Word offsets of the exchange regions inside the model's word buffer.
 struct DecOffsets {

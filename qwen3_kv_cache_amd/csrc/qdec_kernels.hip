@@ -1429,6 +1429,147 @@ __global__ void to_f32_kernel(const WT* __restrict__ src, size_t n, float* __res
     dst[i] = load_w(src, i);
 }
 
+// ------------------------------------------------------------------ sampling
+// Sampling after the LM head (NCNN "Qwen3ASR ncnn多平台移植", section 1: greedy,
+// temperature, top-k, top-p, repetition penalty; section 6: greedy default).
+// Order: penalty on the row's history ids, temperature, candidates by (value
+// descending, index ascending), top-k, softmax, top-p prefix, inverse CDF at
+// the caller's uniform. A candidate travels as one 64-bit key: the
+// order-preserving bits of its float32 value above 0xFFFFFFFF - index, so a
+// descending sort of keys is exactly that candidate order.
+
+constexpr int kSampleChunk = 2048;  // keys sorted per block
+
+__device__ __forceinline__ unsigned long long cand_key(float v, int idx) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)o << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)idx);
+}
+__device__ __forceinline__ float cand_value(unsigned long long k) {
+  const uint32_t o = (uint32_t)(k >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+__device__ __forceinline__ int cand_index(unsigned long long k) {
+  return (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
+}
+
+// Descending bitonic sort of N keys in LDS by the whole block.
+template <int N>
+__device__ void bitonic_desc(unsigned long long* a) {
+  for (int k = 2; k <= N; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < N; i += blockDim.x) {
+        const int p = i ^ j;
+        if (p > i) {
+          const unsigned long long x = a[i], y = a[p];
+          // runs alternate direction so that each k-run ends up descending
+          const bool swap = ((i & k) == 0) ? (x < y) : (x > y);
+          if (swap) {
+            a[i] = y;
+            a[p] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+}
+
+// One level of top-k: block (chunk c, row r) sorts kSampleChunk keys and
+// writes its first k. Level 0 (RAW) builds the keys from row r's logits: the
+// repetition penalty on the row's history ids, then the temperature (inv_t =
+// 0 skips it: greedy). Later levels read the previous level's keys.
+template <bool RAW>
+__global__ __launch_bounds__(256) void topk_level_kernel(const float* __restrict__ logits, int V,
+                                                          const unsigned long long* __restrict__ in, int n_in,
+                                                          const int32_t* __restrict__ hist, int nh, float rho,
+                                                          float temp, int k, unsigned long long* __restrict__ out) {
+  __shared__ unsigned long long key[kSampleChunk];
+  const int c = blockIdx.x, r = blockIdx.y;
+  const int base = c * kSampleChunk;
+  const int n = RAW ? V : n_in;
+  for (int i = threadIdx.x; i < kSampleChunk; i += blockDim.x) {
+    const int e = base + i;
+    unsigned long long kk = 0ull;  // below every real key
+    if (e < n) {
+      if (RAW) {
+        float z = logits[(size_t)r * V + e];
+        if (temp > 0.f) z = z / temp;
+        kk = cand_key(z, e);
+      } else {
+        kk = in[(size_t)r * n_in + e];
+      }
+    }
+    key[i] = kk;
+  }
+  if (RAW && nh > 0) {
+    __syncthreads();
+    // a history id in this chunk: recompute its value from the logit with the
+    // penalty (duplicates write the same key)
+    for (int t = threadIdx.x; t < nh; t += blockDim.x) {
+      const int id = hist[(size_t)r * nh + t];
+      if (id >= base && id < base + kSampleChunk && id < V) {
+        float z = logits[(size_t)r * V + id];
+        z = z > 0.f ? z / rho : z * rho;
+        if (temp > 0.f) z = z / temp;
+        key[id - base] = cand_key(z, id);
+      }
+    }
+  }
+  __syncthreads();
+  bitonic_desc<kSampleChunk>(key);
+  const int nc = gridDim.x;
+  for (int j = threadIdx.x; j < k; j += blockDim.x) out[((size_t)r * nc + c) * k + j] = key[j];
+}
+
+// The pick from row r's k candidates (sorted, keys), one wave: float64
+// softmax over the candidates, top-p prefix, inverse CDF at u[r].
+__global__ __launch_bounds__(64) void sample_pick_kernel(const unsigned long long* __restrict__ cand, int k,
+                                                          float top_p, SampleUniforms u, int32_t* __restrict__ tok) {
+  const int r = blockIdx.x, lane = threadIdx.x;
+  const unsigned long long* c = cand + (size_t)r * k;
+  const double z0 = (double)cand_value(c[0]);
+  // lane holds candidates 2 lane and 2 lane + 1
+  double e[2], cum[2];
+  double run = 0.0;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = 2 * lane + h;
+    e[h] = i < k ? exp((double)cand_value(c[i]) - z0) : 0.0;
+  }
+  // inclusive scan of the lane pairs, then of the lanes
+  double s = e[0] + e[1];
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double t = __shfl_up(s, o, kWave);
+    if (lane >= o) s += t;
+  }
+  run = s - (e[0] + e[1]);
+  cum[0] = run + e[0];
+  cum[1] = cum[0] + e[1];
+  const double total = __shfl(s, 63, kWave);
+  // top-p: n = 1 + the number of leading candidates whose mass stays below top_p
+  int n = k;
+  if (top_p < 1.f) {
+    const double lim = (double)top_p * total;
+    const int below = (2 * lane < k && cum[0] < lim ? 1 : 0) + (2 * lane + 1 < k && cum[1] < lim ? 1 : 0);
+    int cnt = below;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o, kWave);
+    n = min(k, cnt + 1);
+  }
+  const double mass = __shfl(n - 1 < 2 * lane + 2 ? cum[(n - 1) & 1] : 0.0, (n - 1) / 2, kWave);
+  const double target = (double)u.u[r] * mass;
+  // first candidate i < n with cum[i] > target
+  int first = n - 1;
+  int mine = 1 << 30;
+  if (2 * lane < n && cum[0] > target) mine = 2 * lane;
+  else if (2 * lane + 1 < n && cum[1] > target) mine = 2 * lane + 1;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mine = min(mine, __shfl_xor(mine, o, kWave));
+  if (mine < n) first = mine;
+  if (lane == 0) tok[r] = cand_index(c[first]);
+}
+
 }  // namespace
 
 // ================================================================ launchers
@@ -1677,6 +1818,32 @@ hipError_t launch_gemm(bool bf16, Epi epi, const void* A0, const void* A1, int M
       gemm_f32_kernel<EPI_SWIGLU><<<grid, 256, 0, st>>>(a, M, K, w, N, C, ldc);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_sample(const float* logits, int n, int V, const int32_t* hist, int nh, float rho, float temp,
+                         int top_k, float top_p, const SampleUniforms& u, unsigned long long* buf0,
+                         unsigned long long* buf1, int32_t* tok, hipStream_t st) {
+  const int k = temp > 0.f ? top_k : 1;
+  if (k < 1 || k > kSampleKMax || n < 1 || n > kMaxBatch) return hipErrorInvalidValue;
+  int nc = (V + kSampleChunk - 1) / kSampleChunk;
+  topk_level_kernel<true><<<dim3(nc, n), 256, 0, st>>>(logits, V, nullptr, 0, hist, nh, rho, temp, k, buf0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  unsigned long long* cur = buf0;
+  unsigned long long* nxt = buf1;
+  while (nc > 1) {
+    const int n_in = nc * k;
+    nc = (n_in + kSampleChunk - 1) / kSampleChunk;
+    topk_level_kernel<false><<<dim3(nc, n), 256, 0, st>>>(nullptr, 0, cur, n_in, nullptr, 0, 1.f, 0.f, k, nxt);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    std::swap(cur, nxt);
+  }
+  sample_pick_kernel<<<n, 64, 0, st>>>(cur, k, temp > 0.f ? top_p : 1.f, u, tok);
+  return hipGetLastError();
+}
+
+size_t sample_buffer_words(int V) {
+  return (size_t)kMaxBatch * ((V + kSampleChunk - 1) / kSampleChunk) * kSampleKMax;
 }
 
 hipError_t launch_to_f32(const void* src, bool bf16, size_t n, float* dst, hipStream_t st) {

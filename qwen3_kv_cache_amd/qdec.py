@@ -33,8 +33,10 @@ QDEC_PAGE = 16
  QDEC_W_POST_NORM, QDEC_W_GATE, QDEC_W_UP, QDEC_W_DOWN, QDEC_W_PER_LAYER) = range(12)
 
 EXPORTS = ("qdec_create", "qdec_destroy", "qdec_state_create", "qdec_state_destroy", "qdec_prefill",
-           "qdec_decode_step", "qdec_decode_step_dev", "qdec_decode_greedy", "qdec_decode_batch", "qdec_clone_state",
-           "qdec_state_pos", "qdec_last_error")
+           "qdec_decode_step", "qdec_decode_step_dev", "qdec_decode_greedy", "qdec_decode_batch", "qdec_sample",
+           "qdec_clone_state", "qdec_state_pos", "qdec_last_error")
+
+QDEC_SAMPLE_TOP_K_MAX = 128
 
 
 class QdecError(RuntimeError):
@@ -53,6 +55,11 @@ class qdec_config(ctypes.Structure):
 class qdec_weights(ctypes.Structure):
     _fields_ = [("embed", ctypes.c_void_p), ("final_norm", ctypes.c_void_p),
                 ("layer", ctypes.POINTER(ctypes.c_void_p))]
+
+
+class qdec_sampling(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_float), ("top_k", ctypes.c_int32), ("top_p", ctypes.c_float),
+                ("repetition_penalty", ctypes.c_float)]
 
 
 _lib = None
@@ -86,6 +93,8 @@ def lib() -> ctypes.CDLL:
         "qdec_decode_step_dev": (ctypes.c_int, [vp, vp, i32, vp, vp]),
         "qdec_decode_greedy": (ctypes.c_int, [vp, vp, i32, i32, vp, vp]),
         "qdec_decode_batch": (ctypes.c_int, [ctypes.POINTER(vp), i32, ctypes.POINTER(i32), vp, vp]),
+        "qdec_sample": (ctypes.c_int, [vp, vp, i32, ctypes.POINTER(qdec_sampling), vp, i32,
+                                       ctypes.POINTER(ctypes.c_float), vp]),
         "qdec_clone_state": (ctypes.c_int, [vp, ctypes.POINTER(vp)]),
         "qdec_state_pos": (i32, [vp]),
         "qdec_last_error": (ctypes.c_char_p, []),
@@ -162,6 +171,16 @@ def qdec_decode_batch(states: Sequence[int], tokens_host, logits_dev=None, argma
         raise ValueError("tokens_host shorter than the batch")
     _check(lib().qdec_decode_batch(arr, n, toks.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                                    _ptr(logits_dev), _ptr(argmax_dev)))
+
+
+def qdec_sample(model: int, logits_dev, n_rows: int, temperature: float, top_k: int, top_p: float,
+                repetition_penalty: float, history_dev, history_len: int, uniforms_host, tokens_dev) -> None:
+    p = qdec_sampling(float(temperature), int(top_k), float(top_p), float(repetition_penalty))
+    u = np.ascontiguousarray(uniforms_host, dtype=np.float32)
+    if u.size < n_rows:
+        raise ValueError("uniforms_host shorter than n_rows")
+    _check(lib().qdec_sample(_ptr(model), _ptr(logits_dev), int(n_rows), ctypes.byref(p), _ptr(history_dev),
+                             int(history_len), u.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), _ptr(tokens_dev)))
 
 
 def qdec_clone_state(src: int) -> int:

@@ -102,6 +102,12 @@ def test_null_handles_are_rejected():
     assert e.value.code == qdec.QDEC_E_INVALID
 
 
+def test_sample_rejects_without_model():
+    with pytest.raises(qdec.QdecError) as e:
+        qdec.qdec_sample(0, None, 1, 1.0, 10, 1.0, 1.0, None, 0, [0.5], None)
+    assert e.value.code == qdec.QDEC_E_INVALID
+
+
 def test_batch_size_limit():
     with pytest.raises(qdec.QdecError) as e:
         qdec.qdec_decode_batch([1] * 17, [0] * 17)
