@@ -13,7 +13,8 @@ before the timed region.
 The default run also reports, under "other_workloads", the rest of the
 metric with the same weights and fewer repetitions: B=16 batched decode of
 16 clones of a 512-token prefill (branch16), and the 1024- and 8192-token
-prompts (long, prefill8k). --no-others skips them.
+prompts (long, prefill8k); and under "sampling" the time of one sampling
+step (qdec_sample) over 1 and 16 rows of logits. --no-others skips them.
 
 Usage: python bench.py [--steps K] [--warmup W] [--workload short|long|prefill8k|branch16]
        python bench.py --copy-probe   (plain copy kernel for counter calibration)
@@ -166,6 +167,39 @@ def measure(w, model, steps, warmup, per_step=False):
     return pre_ms, dec_ms, wall
 
 
+def measure_sampling(model, V, calls=50):
+    """qdec_sample on 1 and 16 rows of seeded N(0, 3^2) logits (temperature
+    0.8, top-k 50, top-p 0.95, repetition penalty 1.1 over 64 history ids):
+    mean microseconds per call, HIP events on the library's stream."""
+    import torch
+
+    from qwen3_kv_cache_amd import qdec
+
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(7)
+    out = {"temperature": 0.8, "top_k": 50, "top_p": 0.95, "repetition_penalty": 1.1, "history": 64}
+    for n in (1, 16):
+        z = torch.from_numpy((3.0 * rng.standard_normal((n, V))).astype(np.float32)).to(dev)
+        h = torch.from_numpy(rng.integers(0, V, size=(n, 64)).astype(np.int32)).to(dev)
+        tok = torch.zeros(n, dtype=torch.int32, device=dev)
+        u = rng.random(n).astype(np.float32)
+
+        def call():
+            qdec.qdec_sample(model.handle, z.data_ptr(), n, 0.8, 50, 0.95, 1.1, h.data_ptr(), 64, u, tok.data_ptr())
+
+        for _ in range(3):
+            call()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(calls):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        out[f"rows{n}_us"] = round(e0.elapsed_time(e1) * 1e3 / calls, 2)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -245,6 +279,7 @@ def main():
                             "prefill_tok_s": round(wo.prompt_len * len(p_ms) / (p_ms.sum() / 1e3), 1),
                             "prefill_ms": round(float(p_ms.mean()), 3)}
         line["other_workloads"] = others
+        line["sampling"] = measure_sampling(model, w.shape.vocab)
     if a.cpu_sample > 0:
         line["cpu_baseline"] = cpu_baseline(w, W, a.cpu_sample)
     model.close()

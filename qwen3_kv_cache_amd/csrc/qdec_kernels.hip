@@ -1438,7 +1438,7 @@ __global__ void to_f32_kernel(const WT* __restrict__ src, size_t n, float* __res
 // order-preserving bits of its float32 value above 0xFFFFFFFF - index, so a
 // descending sort of keys is exactly that candidate order.
 
-constexpr int kSampleChunk = 2048;  // keys sorted per block
+constexpr int kSampleChunk = 1024;  // keys sorted per block
 
 __device__ __forceinline__ unsigned long long cand_key(float v, int idx) {
   const uint32_t u = __float_as_uint(v);
@@ -1453,22 +1453,21 @@ __device__ __forceinline__ int cand_index(unsigned long long k) {
   return (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
 }
 
-// Descending bitonic sort of N keys in LDS by the whole block.
+// Descending bitonic sort of N keys in LDS by the whole block: each stage
+// visits its N / 2 compare-exchange pairs (i, i + j), i with bit j clear, so
+// no thread idles.
 template <int N>
 __device__ void bitonic_desc(unsigned long long* a) {
   for (int k = 2; k <= N; k <<= 1)
     for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < N; i += blockDim.x) {
-        const int p = i ^ j;
-        if (p > i) {
-          const unsigned long long x = a[i], y = a[p];
-          // runs alternate direction so that each k-run ends up descending
-          const bool swap = ((i & k) == 0) ? (x < y) : (x > y);
-          if (swap) {
-            a[i] = y;
-            a[p] = x;
-          }
-        }
+      for (int t = threadIdx.x; t < N / 2; t += blockDim.x) {
+        const int i = ((t & ~(j - 1)) << 1) | (t & (j - 1));
+        const int p = i + j;
+        const unsigned long long x = a[i], y = a[p];
+        // runs alternate direction so that each k-run ends up descending
+        const bool swap = ((i & k) == 0) ? (x < y) : (x > y);
+        a[i] = swap ? y : x;
+        a[p] = swap ? x : y;
       }
       __syncthreads();
     }
@@ -1479,7 +1478,7 @@ __device__ void bitonic_desc(unsigned long long* a) {
 // repetition penalty on the row's history ids, then the temperature (inv_t =
 // 0 skips it: greedy). Later levels read the previous level's keys.
 template <bool RAW>
-__global__ __launch_bounds__(256) void topk_level_kernel(const float* __restrict__ logits, int V,
+__global__ __launch_bounds__(512) void topk_level_kernel(const float* __restrict__ logits, int V,
                                                           const unsigned long long* __restrict__ in, int n_in,
                                                           const int32_t* __restrict__ hist, int nh, float rho,
                                                           float temp, int k, unsigned long long* __restrict__ out) {
@@ -1826,7 +1825,7 @@ hipError_t launch_sample(const float* logits, int n, int V, const int32_t* hist,
   const int k = temp > 0.f ? top_k : 1;
   if (k < 1 || k > kSampleKMax || n < 1 || n > kMaxBatch) return hipErrorInvalidValue;
   int nc = (V + kSampleChunk - 1) / kSampleChunk;
-  topk_level_kernel<true><<<dim3(nc, n), 256, 0, st>>>(logits, V, nullptr, 0, hist, nh, rho, temp, k, buf0);
+  topk_level_kernel<true><<<dim3(nc, n), 512, 0, st>>>(logits, V, nullptr, 0, hist, nh, rho, temp, k, buf0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   unsigned long long* cur = buf0;
@@ -1834,7 +1833,7 @@ hipError_t launch_sample(const float* logits, int n, int V, const int32_t* hist,
   while (nc > 1) {
     const int n_in = nc * k;
     nc = (n_in + kSampleChunk - 1) / kSampleChunk;
-    topk_level_kernel<false><<<dim3(nc, n), 256, 0, st>>>(nullptr, 0, cur, n_in, nullptr, 0, 1.f, 0.f, k, nxt);
+    topk_level_kernel<false><<<dim3(nc, n), 512, 0, st>>>(nullptr, 0, cur, n_in, nullptr, 0, 1.f, 0.f, k, nxt);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     std::swap(cur, nxt);
   }
