@@ -836,14 +836,24 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
         }
       mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
       mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      // key 0 is visible to every query, so mx is finite from the first tile on
-      const float alpha = __builtin_amdgcn_exp2f(m[hh] - mx);
+      // The exponent base m moves only when a score passes it by more than 8
+      // (a factor of 256 in the probabilities): the normalised result is the
+      // same for any base, and most tiles then skip rescaling the output
+      // accumulators. Key 0 is visible to every query, so the first tile sets
+      // a finite base (m starts at -inf, where alpha is 0).
+      if (mx > m[hh] + 8.f) {
+        const float alpha = __builtin_amdgcn_exp2f(m[hh] - mx);
+        lsum[hh] *= alpha;
+#pragma unroll
+        for (int b = 0; b < D / 16; ++b) acc[hh][b] *= alpha;
+        m[hh] = mx;
+      }
       float ps = 0.f;
 #pragma unroll
       for (int j = 0; j < KB; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p = __builtin_amdgcn_exp2f(sc[hh][j][e] - mx);
+          const float p = __builtin_amdgcn_exp2f(sc[hh][j][e] - m[hh]);
           ps += p;
           const __bf16 h = (__bf16)p;
           ph[hh][j / 2][4 * (j % 2) + e] = h;
@@ -851,10 +861,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
         }
       ps += __shfl_xor(ps, 16, kWave);
       ps += __shfl_xor(ps, 32, kWave);
-      lsum[hh] = lsum[hh] * alpha + ps;
-      m[hh] = mx;
-#pragma unroll
-      for (int b = 0; b < D / 16; ++b) acc[hh][b] *= alpha;
+      lsum[hh] += ps;
     }
 
     // O^T += V^T P^T: d block b, 32-key group c
