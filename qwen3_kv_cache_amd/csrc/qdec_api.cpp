@@ -139,6 +139,7 @@ struct qdec_model {
   float* pX = nullptr;
   float* pQKV = nullptr;
   float* pAttn = nullptr;
+  uint16_t* pKV[4] = {nullptr, nullptr, nullptr, nullptr};  // converted K / V^T for the matrix-core attention
   float* pZ = nullptr;
   void* pA0 = nullptr;  // bf16 hi (or fp32 activations for fp32 weights)
   void* pA1 = nullptr;  // bf16 lo
@@ -226,6 +227,10 @@ void free_prefill(qdec_model* m) {
   (void)hipFree(m->pX);
   (void)hipFree(m->pQKV);
   (void)hipFree(m->pAttn);
+  for (uint16_t*& p : m->pKV) {
+    (void)hipFree(p);
+    p = nullptr;
+  }
   (void)hipFree(m->pZ);
   (void)hipFree(m->pA0);
   (void)hipFree(m->pA1);
@@ -315,6 +320,11 @@ int ensure_prefill(qdec_model* m, int T) {
   if ((e = dev_alloc(&m->p_ids, T, "prefill ids")) || (e = dev_alloc(&m->pX, (size_t)T * d.H, "prefill X")) ||
       (e = dev_alloc(&m->pQKV, (size_t)T * d.qkv(), "prefill QKV")) ||
       (e = dev_alloc(&m->pAttn, (size_t)T * d.NQ * d.D, "prefill attention")) ||
+      (attn_prefill_uses_split(d) &&
+       ((e = dev_alloc(&m->pKV[0], (size_t)d.NKV * T * d.D, "prefill K")) ||
+        (e = dev_alloc(&m->pKV[1], (size_t)d.NKV * T * d.D, "prefill K")) ||
+        (e = dev_alloc(&m->pKV[2], (size_t)d.NKV * d.D * kv_split_pad(T), "prefill V")) ||
+        (e = dev_alloc(&m->pKV[3], (size_t)d.NKV * d.D * kv_split_pad(T), "prefill V")))) ||
       (e = dev_alloc(&m->pZ, (size_t)T * d.F, "prefill FFN"))) {
     free_prefill(m);
     return e;
@@ -647,7 +657,7 @@ int run_prefill(qdec_state* s, int T, const float* audio, int a0, int La, float*
     return 0;
   };
   auto attn = [&](int) -> int {
-    LAUNCH(launch_attn_prefill(d, m->pQKV, T, m->pAttn, st));
+    LAUNCH(launch_attn_prefill(d, m->pQKV, T, m->pAttn, m->pKV, st));
     return 0;
   };
   if (fused) {

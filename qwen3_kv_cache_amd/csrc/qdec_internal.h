@@ -123,7 +123,14 @@ struct AttnRows {
 };
 // nsplit * kAttnChunk must cover the longest row (pos + 1)
 hipError_t launch_attn_rows(const Dims& d, const AttnRows& a, int nsplit, hipStream_t st);
-hipError_t launch_attn_prefill(const Dims& d, const float* qkv, int T, float* out, hipStream_t st);
+// Causal prefill attention over QKV rows [T, qkv()]. For head_dim 128 with
+// GQA 1 or 2 (attn_prefill_uses_split) K and V are first converted into
+// kv[0..3] = K hi, K lo ([NKV][T][128] bf16 each) and V^T hi, lo
+// ([NKV][128][kv_split_pad(T)] bf16 each); otherwise kv is unused.
+bool attn_prefill_uses_split(const Dims& d);
+int kv_split_pad(int T);
+hipError_t launch_attn_prefill(const Dims& d, const float* qkv, int T, float* out, uint16_t* const kv[4],
+                               hipStream_t st);
 
 hipError_t launch_rms_split(const float* X, int T, int K, const float* gain, float eps, uint16_t* hi,
                             uint16_t* lo, hipStream_t st);

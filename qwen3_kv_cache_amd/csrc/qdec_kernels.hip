@@ -706,6 +706,60 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const float* __restri
 // of three bf16 MFMAs (hi hi, hi lo, lo hi), about 16 mantissa bits. Scores
 // are kept in base 2 (Q carries log2(e) / sqrt(D)), so the softmax uses the
 // hardware exp2.
+// K and V of one KV head for the matrix-core attention, converted once per
+// layer: kh / kl [g][t][128] bf16 hi / lo of the rotated keys, vth / vtl
+// [g][128][Tp] bf16 hi / lo of the values transposed (columns t >= T repeat
+// row T - 1, so every staged tile is finite). Block = (64 tokens, head g).
+__global__ __launch_bounds__(256) void kv_split_kernel(const float* __restrict__ qkv, int T, int ld, int NQ,
+                                                        int NKV, uint16_t* __restrict__ kh,
+                                                        uint16_t* __restrict__ kl, uint16_t* __restrict__ vth,
+                                                        uint16_t* __restrict__ vtl, int Tp) {
+  constexpr int D = 128, TT = 64;
+  __shared__ float vs[D][TT + 1];
+  const int g = blockIdx.y, t0 = blockIdx.x * TT;
+  const float* kbase = qkv + (size_t)(NQ + g) * D;
+  const float* vbase = qkv + (size_t)(NQ + NKV + g) * D;
+#pragma unroll
+  for (int i = 0; i < TT * D / 4 / 256; ++i) {
+    const int c = threadIdx.x + 256 * i, tl = c / (D / 4), d0 = 4 * (c % (D / 4));
+    const int t = min(t0 + tl, T - 1);
+    const float4 k = *reinterpret_cast<const float4*>(kbase + (size_t)t * ld + d0);
+    const float4 v = *reinterpret_cast<const float4*>(vbase + (size_t)t * ld + d0);
+    vs[d0][tl] = v.x;
+    vs[d0 + 1][tl] = v.y;
+    vs[d0 + 2][tl] = v.z;
+    vs[d0 + 3][tl] = v.w;
+    if (t0 + tl < T) {
+      const float kk[4] = {k.x, k.y, k.z, k.w};
+      __bf16 h4[4], l4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        h4[e] = (__bf16)kk[e];
+        l4[e] = (__bf16)(kk[e] - (float)h4[e]);
+      }
+      const size_t o = ((size_t)g * T + t0 + tl) * D + d0;
+      *reinterpret_cast<uint2*>(kh + o) = __builtin_bit_cast(uint2, h4);
+      *reinterpret_cast<uint2*>(kl + o) = __builtin_bit_cast(uint2, l4);
+    }
+  }
+  __syncthreads();
+  // V^T: thread -> column d, 4 consecutive tokens
+#pragma unroll
+  for (int i = 0; i < TT * D / 4 / 256; ++i) {
+    const int c = threadIdx.x + 256 * i, d = c / (TT / 4), tq = 4 * (c % (TT / 4));
+    __bf16 h4[4], l4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float v = vs[d][tq + e];
+      h4[e] = (__bf16)v;
+      l4[e] = (__bf16)(v - (float)h4[e]);
+    }
+    const size_t o = ((size_t)g * D + d) * Tp + t0 + tq;
+    *reinterpret_cast<uint2*>(vth + o) = __builtin_bit_cast(uint2, h4);
+    *reinterpret_cast<uint2*>(vtl + o) = __builtin_bit_cast(uint2, l4);
+  }
+}
+
 namespace fa {
 constexpr int D = 128;
 constexpr int QT = 64;          // query positions per block
@@ -718,8 +772,11 @@ constexpr int KH = KT / 32;     // 32-key groups per tile
 
 template <int GROUP>
 __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* __restrict__ qkv, int T, int ld,
-                                                                 int NQ, int NKV, float* __restrict__ out, int ldo,
-                                                                 float qscale) {
+                                                                 const uint16_t* __restrict__ khs,
+                                                                 const uint16_t* __restrict__ kls,
+                                                                 const uint16_t* __restrict__ vths,
+                                                                 const uint16_t* __restrict__ vtls, int Tp,
+                                                                 float* __restrict__ out, int ldo, float qscale) {
   using namespace fa;
   __shared__ __bf16 Kh[KT * KP], Kl[KT * KP];
   __shared__ __bf16 Vh[D * VP], Vl[D * VP];
@@ -761,42 +818,28 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
     for (int b = 0; b < D / 16; ++b) acc[hh][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  const size_t koff = (size_t)NQ * D + (size_t)g * D;
-  const size_t voff = (size_t)(NQ + NKV) * D + (size_t)g * D;
+  const uint16_t* kh_g = khs + (size_t)g * T * D;
+  const uint16_t* kl_g = kls + (size_t)g * T * D;
+  const uint16_t* vh_g = vths + (size_t)g * D * Tp;
+  const uint16_t* vl_g = vtls + (size_t)g * D * Tp;
   const int last_key = min(T, q0 + QT) - 1;
   for (int k0 = 0; k0 <= last_key; k0 += KT) {
     __syncthreads();
-    {
-      // K: thread -> key t / 8, 16 columns from 16 (t % 8)
-      const int key = threadIdx.x / 8, d0 = 16 * (threadIdx.x % 8);
-      const float* src = qkv + (size_t)min(k0 + key, T - 1) * ld + koff + d0;
+    // copies of the converted tiles: K rows of 16-byte chunks (key c / 16,
+    // columns 8 (c % 16)), V^T rows (column d = c / 4, keys 8 (c % 4))
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 a = *reinterpret_cast<const float4*>(src + 4 * i);
-        const float v[4] = {a.x, a.y, a.z, a.w};
-        __bf16 h4[4], l4[4];
+    for (int i = 0; i < KT * D / 8 / 256; ++i) {
+      const int c = threadIdx.x + 256 * i, key = c / (D / 8), d0 = 8 * (c % (D / 8));
+      const size_t o = (size_t)min(k0 + key, T - 1) * D + d0;
+      *reinterpret_cast<uint4*>(&Kh[key * KP + d0]) = *reinterpret_cast<const uint4*>(kh_g + o);
+      *reinterpret_cast<uint4*>(&Kl[key * KP + d0]) = *reinterpret_cast<const uint4*>(kl_g + o);
+    }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          h4[e] = (__bf16)v[e];
-          l4[e] = (__bf16)(v[e] - (float)h4[e]);
-        }
-        *reinterpret_cast<uint2*>(&Kh[key * KP + d0 + 4 * i]) = __builtin_bit_cast(uint2, h4);
-        *reinterpret_cast<uint2*>(&Kl[key * KP + d0 + 4 * i]) = __builtin_bit_cast(uint2, l4);
-      }
-      // V^T: thread -> column d = t % 128, keys 16 (t / 128) + 0..15
-      const int d = threadIdx.x % D, kb = 16 * (threadIdx.x / D);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        __bf16 h4[4], l4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float v = qkv[(size_t)min(k0 + kb + 4 * i + e, T - 1) * ld + voff + d];
-          h4[e] = (__bf16)v;
-          l4[e] = (__bf16)(v - (float)h4[e]);
-        }
-        *reinterpret_cast<uint2*>(&Vh[d * VP + kb + 4 * i]) = __builtin_bit_cast(uint2, h4);
-        *reinterpret_cast<uint2*>(&Vl[d * VP + kb + 4 * i]) = __builtin_bit_cast(uint2, l4);
-      }
+    for (int i = 0; i < D * KT / 8 / 256; ++i) {
+      const int c = threadIdx.x + 256 * i, d = c / (KT / 8), kq = 8 * (c % (KT / 8));
+      const size_t o = (size_t)d * Tp + k0 + kq;
+      *reinterpret_cast<uint4*>(&Vh[d * VP + kq]) = *reinterpret_cast<const uint4*>(vh_g + o);
+      *reinterpret_cast<uint4*>(&Vl[d * VP + kq]) = *reinterpret_cast<const uint4*>(vl_g + o);
     }
     __syncthreads();
 
@@ -1679,16 +1722,31 @@ hipError_t launch_attn_rows(const Dims& d, const AttnRows& args, int nsplit, hip
   return hipGetLastError();
 }
 
-hipError_t launch_attn_prefill(const Dims& d, const float* qkv, int T, float* out, hipStream_t st) {
+int kv_split_pad(int T) { return (T + 63) / 64 * 64; }
+
+bool attn_prefill_uses_split(const Dims& d) {
+  const int group = d.NQ / d.NKV;
+  return d.D == fa::D && (group == 1 || group == 2);
+}
+
+hipError_t launch_attn_prefill(const Dims& d, const float* qkv, int T, float* out, uint16_t* const kv[4],
+                               hipStream_t st) {
   const int group = d.NQ / d.NKV;
   const float scale = 1.f / sqrtf((float)d.D);
-  if (d.D == fa::D && (group == 1 || group == 2)) {
+  if (attn_prefill_uses_split(d)) {
+    const int Tp = kv_split_pad(T);
+    kv_split_kernel<<<dim3(Tp / 64, d.NKV), 256, 0, st>>>(qkv, T, d.qkv(), d.NQ, d.NKV, kv[0], kv[1], kv[2], kv[3],
+                                                          Tp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     dim3 grid((T + fa::QT - 1) / fa::QT, d.NKV);
     const float qs = scale * 1.4426950408889634f;  // scores in base 2
     if (group == 2)
-      attn_prefill_mfma_kernel<2><<<grid, 256, 0, st>>>(qkv, T, d.qkv(), d.NQ, d.NKV, out, d.NQ * d.D, qs);
+      attn_prefill_mfma_kernel<2><<<grid, 256, 0, st>>>(qkv, T, d.qkv(), kv[0], kv[1], kv[2], kv[3], Tp, out,
+                                                        d.NQ * d.D, qs);
     else
-      attn_prefill_mfma_kernel<1><<<grid, 256, 0, st>>>(qkv, T, d.qkv(), d.NQ, d.NKV, out, d.NQ * d.D, qs);
+      attn_prefill_mfma_kernel<1><<<grid, 256, 0, st>>>(qkv, T, d.qkv(), kv[0], kv[1], kv[2], kv[3], Tp, out,
+                                                        d.NQ * d.D, qs);
     return hipGetLastError();
   }
 #define QDEC_PATTN_CASE(DD, GG)                                                                      \
