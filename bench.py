@@ -33,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 METRIC = "decode tok/s (B=1,B=16) + prefill tok/s, Qwen3-0.6B bf16; % HBM peak"
 
 
@@ -49,12 +50,21 @@ def decode_bytes(shape, ctx_lens) -> float:
     return float(np.mean([w + L * kv_row * p + L * kv_row for p in ctx_lens]))
 
 
-def counter_traffic():
-    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
-    or None when the decode kernel's source has changed since it was taken."""
+def prefill_flops(shape, T: int) -> float:
+    """Useful FLOPs of a T-token prefill, each counted once: 2 per weight per
+    row for the layer projections, 4 D per (query head, attended key) pair for
+    QK and PV with causal masking, and the LM head on the last row."""
+    H, L, D, NQ, NKV, F = shape.hidden, shape.n_layer, shape.head_dim, shape.n_q_head, shape.n_kv_head, shape.ffn
+    layer_w = H * (NQ + 2 * NKV) * D + NQ * D * H + 3 * F * H
+    return 2.0 * L * layer_w * T + L * 4.0 * NQ * D * T * (T + 1) / 2 + 2.0 * shape.vocab * H
+
+
+def read_profile_values(name: str, source: str):
+    """The key: value lines of a committed profile summary, or None when the
+    named source file has changed since the counters were taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "decode_kernel_short_traffic.txt")
-    src = os.path.join(ROOT, "qwen3_kv_cache_amd", "csrc", "qdec_decode.hip")
+    path = os.path.join(ROOT, "profiles", name)
+    src = os.path.join(ROOT, "qwen3_kv_cache_amd", "csrc", source)
     try:
         kv = {}
         for line in open(path):
@@ -63,8 +73,36 @@ def counter_traffic():
                 kv[k.strip()] = v.strip()
         if kv.get("source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
             return None
-        return int(float(kv["hbm_bytes_per_launch"]))
-    except (OSError, KeyError, ValueError):
+        return kv
+    except OSError:
+        return None
+
+
+def prefill_mfma(shape, T: int, ms: float, workload: str):
+    """MFMA roofline of the prefill: useful FLOP/s against the dense bf16
+    peak, with the counter-measured MFMA busy share of the prefill kernels
+    when a matching summary is committed (taken at T = 8192)."""
+    f = prefill_flops(shape, T)
+    tf = f / (ms / 1e3) / 1e12
+    out = {"bound": "mfma", "useful_flops": f, "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+           "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "counters": None}
+    kv = read_profile_values("prefill_mfma_counters_8k.txt", "qdec_kernels.hip") if workload == "prefill8k" else None
+    if kv is not None:
+        try:
+            out["counters"] = {"mfma_busy_pct_prefill_kernels": float(kv["mfma_busy_pct_prefill_kernels"]),
+                               "mfma_flops_issued_per_prefill": float(kv["mfma_flops_issued_per_prefill"])}
+        except (KeyError, ValueError):
+            pass
+    return out
+
+
+def counter_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
+    or None when the decode kernel's source has changed since it was taken."""
+    kv = read_profile_values("decode_kernel_short_traffic.txt", "qdec_decode.hip")
+    try:
+        return int(float(kv["hbm_bytes_per_launch"])) if kv is not None else None
+    except (KeyError, ValueError):
         return None
 
 
@@ -258,6 +296,7 @@ def main():
         "prefill_tok_s": round(prefill_tok_s, 1),
         "prefill_ms": round(float(pre_ms.mean()), 4),
         "decode_ms_per_token": round(float(dec_ms.mean()) / n, 5),
+        "prefill_mfma": prefill_mfma(w.shape, w.prompt_len, float(pre_ms.mean()), w.name),
     }
     if achieved is not None:
         # counters were taken on the short workload's 64-step launch
@@ -277,7 +316,8 @@ def main():
             others[name] = {"decode_tok_s": round(wo.n_decode * wo.n_branch * len(d_ms) / (d_ms.sum() / 1e3), 1),
                             "batch": wo.n_branch, "prompt_len": wo.prompt_len, "decode_steps": wo.n_decode,
                             "prefill_tok_s": round(wo.prompt_len * len(p_ms) / (p_ms.sum() / 1e3), 1),
-                            "prefill_ms": round(float(p_ms.mean()), 3)}
+                            "prefill_ms": round(float(p_ms.mean()), 3),
+                            "prefill_mfma": prefill_mfma(wo.shape, wo.prompt_len, float(p_ms.mean()), name)}
         line["other_workloads"] = others
         line["sampling"] = measure_sampling(model, w.shape.vocab)
     if a.cpu_sample > 0:
