@@ -522,7 +522,7 @@ int run_layers_rows(qdec_model* m, int T, float* X, float* QKV, float* Attn, flo
     g.W = (const uint16_t*)w.wqkv, g.K = d.H, g.N = d.qkv(), g.C = QKV, g.ldc = d.qkv();
     if (int e = gemm_rows(m, EPI_STORE, true, g)) return e;
     if (int e = rope(l)) return e;
-    if (int e = attn(l)) return e;
+    if (int e = attn(l, nullptr, nullptr)) return e;
     g.A = Attn, g.lda = d.NQ * d.D, g.W = (const uint16_t*)w.wo, g.K = d.NQ * d.D, g.N = d.H, g.C = X, g.ldc = d.H;
     g.ssq_out = m->rSsq;
     if (int e = gemm_rows(m, EPI_RESID, false, g)) return e;
@@ -541,10 +541,15 @@ int run_layers_rows(qdec_model* m, int T, float* X, float* QKV, float* Attn, flo
 // The decoder layers over T activation rows held in X (fp32 [T, H]), one
 // layer after another (transcribe.cpp "Forward map - funasr_nano", table
 // "LLM decoder"). rope(l) applies QK-norm + RoPE and appends K/V of layer l;
-// attn(l) writes the attention output rows into Attn; both return a status.
+// attn(l, hi, lo) writes the attention output rows into Attn (fp32), or, when
+// hi is set, as their bf16 hi/lo split into hi and lo (attn_split says whether
+// it can); both return a status.
+// With bf16 weights on the tiled GEMM, the attention and the SwiGLU GEMM write
+// the next GEMM's hi/lo operand themselves (the same bits the split pass would
+// make); Z's fp32 buffer then holds Z hi and Z lo.
 template <typename RopeFn, typename AttnFn>
 int run_layers(qdec_model* m, int T, float* X, float* QKV, float* Attn, float* Z, void* A0, void* A1, RopeFn rope,
-               AttnFn attn) {
+               AttnFn attn, bool attn_split) {
   const Dims& d = m->d;
   hipStream_t st = m->stream;
   const bool bf = m->bf16;
@@ -552,18 +557,32 @@ int run_layers(qdec_model* m, int T, float* X, float* QKV, float* Attn, float* Z
     if (bf) return launch_rms_split(src, T, K, gain, d.eps, (uint16_t*)A0, (uint16_t*)A1, st);
     return launch_rms_apply(src, T, K, gain, d.eps, (float*)A0, st);
   };
+  const bool fuse_o = attn_split && gemm_tiled_fits(bf, T, d.NQ * d.D, d.H);
+  const bool fuse_z = gemm_tiled_fits(bf, T, d.H, 2 * d.F) && gemm_tiled_fits(bf, T, d.F, d.H);
+  uint16_t* zhi = (uint16_t*)Z;
+  uint16_t* zlo = zhi + (size_t)T * d.F;
   for (int l = 0; l < d.L; ++l) {
     const LayerW& w = m->layers[l];
     LAUNCH(norm_in(X, d.H, w.in_norm));
     LAUNCH(launch_gemm(bf, EPI_STORE, A0, A1, T, d.H, w.wqkv, d.qkv(), QKV, d.qkv(), st));
     if (int e = rope(l)) return e;
-    if (int e = attn(l)) return e;
-    LAUNCH(norm_in(Attn, d.NQ * d.D, nullptr));
+    if (fuse_o) {
+      if (int e = attn(l, (uint16_t*)A0, (uint16_t*)A1)) return e;
+    } else {
+      if (int e = attn(l, nullptr, nullptr)) return e;
+      LAUNCH(norm_in(Attn, d.NQ * d.D, nullptr));
+    }
     LAUNCH(launch_gemm(bf, EPI_RESID, A0, A1, T, d.NQ * d.D, w.wo, d.H, X, d.H, st));
     LAUNCH(norm_in(X, d.H, w.post_norm));
-    LAUNCH(launch_gemm(bf, EPI_SWIGLU, A0, A1, T, d.H, w.wgu, 2 * d.F, Z, d.F, st));
-    LAUNCH(norm_in(Z, d.F, nullptr));
-    LAUNCH(launch_gemm(bf, EPI_RESID, A0, A1, T, d.F, w.wd, d.H, X, d.H, st));
+    if (fuse_z) {
+      LAUNCH(launch_gemm_swiglu_split((const uint16_t*)A0, (const uint16_t*)A1, T, d.H, (const uint16_t*)w.wgu,
+                                      2 * d.F, zhi, zlo, d.F, st));
+      LAUNCH(launch_gemm(bf, EPI_RESID, zhi, zlo, T, d.F, w.wd, d.H, X, d.H, st));
+    } else {
+      LAUNCH(launch_gemm(bf, EPI_SWIGLU, A0, A1, T, d.H, w.wgu, 2 * d.F, Z, d.F, st));
+      LAUNCH(norm_in(Z, d.F, nullptr));
+      LAUNCH(launch_gemm(bf, EPI_RESID, A0, A1, T, d.F, w.wd, d.H, X, d.H, st));
+    }
   }
   return QDEC_OK;
 }
@@ -595,7 +614,7 @@ int run_decode_batch(qdec_state* const* states, int n, const int32_t* tokens, fl
   LAUNCH(launch_reset_keys(m->bKeys, n, st));
   LAUNCH(launch_embed_rows(d, m->bf16, m->embed, rows, m->bX, fused ? m->rSsq : nullptr, st));
   auto rope = [](int) { return 0; };  // inside the attention launch
-  auto attn = [&](int l) -> int {
+  auto attn = [&](int l, uint16_t*, uint16_t*) -> int {  // fp32 output only
     const LayerW& w = m->layers[l];
     AttnRows a{};
     a.rows = rows;
@@ -625,7 +644,7 @@ int run_decode_batch(qdec_state* const* states, int n, const int32_t* tokens, fl
       LAUNCH(launch_argmax_final(m->bKeys, n, argmax ? argmax : m->bTok, st));
       return QDEC_OK;
     }
-  } else if (int e = run_layers(m, n, m->bX, m->bQKV, m->bAttn, m->bZ, m->bA0, m->bA1, rope, attn)) {
+  } else if (int e = run_layers(m, n, m->bX, m->bQKV, m->bAttn, m->bZ, m->bA0, m->bA1, rope, attn, false)) {
     return e;
   }
   if (m->bf16)
@@ -656,14 +675,15 @@ int run_prefill(qdec_state* s, int T, const float* audio, int a0, int La, float*
     LAUNCH(launch_qk_rope_append(d, m->pQKV, T, 0, w.q_norm, w.k_norm, m->rope_cos, m->rope_sin, s->pt_dev, l, st));
     return 0;
   };
-  auto attn = [&](int) -> int {
-    LAUNCH(launch_attn_prefill(d, m->pQKV, T, m->pAttn, m->pKV, st));
+  auto attn = [&](int, uint16_t* hi, uint16_t* lo) -> int {
+    LAUNCH(launch_attn_prefill(d, m->pQKV, T, m->pAttn, m->pKV, st, hi, lo));
     return 0;
   };
   if (fused) {
     int nss = 1;
     if (int e = run_layers_rows(m, T, m->pX, m->pQKV, m->pAttn, m->pZ, 1, rope, attn, &nss)) return e;
-  } else if (int e = run_layers(m, T, m->pX, m->pQKV, m->pAttn, m->pZ, m->pA0, m->pA1, rope, attn)) {
+  } else if (int e = run_layers(m, T, m->pX, m->pQKV, m->pAttn, m->pZ, m->pA0, m->pA1, rope, attn,
+                                attn_prefill_uses_split(d))) {
     return e;
   }
   LAUNCH(launch_lm_head(d, bf, m->embed, m->pX + (size_t)(T - 1) * d.H, m->final_norm, logits, m->keys, st));

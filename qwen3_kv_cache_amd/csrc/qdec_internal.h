@@ -64,7 +64,9 @@ hipError_t launch_embed_rows(const Dims& d, bool bf16, const void* E, const Batc
 hipError_t launch_embed_prefill(const Dims& d, bool bf16, const void* E, const int32_t* ids, int T,
                                 const float* audio, int a0, int La, float* X, float* ssq, hipStream_t st);
 
-enum Epi { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_HEAD = 3 };
+// EPI_SWIGLU_SPLIT (tiled GEMM only): the SwiGLU output written as bf16 hi
+// and lo, the next GEMM's operand, instead of fp32
+enum Epi { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_HEAD = 3, EPI_SWIGLU_SPLIT = 4 };
 
 // Arguments of the fused small-M GEMM (gemm_rows_kernel): up to 64 fp32
 // activation rows against bf16 weights, optional RMSNorm prologue, split-K
@@ -126,11 +128,13 @@ hipError_t launch_attn_rows(const Dims& d, const AttnRows& a, int nsplit, hipStr
 // Causal prefill attention over QKV rows [T, qkv()]. For head_dim 128 with
 // GQA 1 or 2 (attn_prefill_uses_split) K and V are first converted into
 // kv[0..3] = K hi, K lo ([NKV][T][128] bf16 each) and V^T hi, lo
-// ([NKV][128][kv_split_pad(T)] bf16 each); otherwise kv is unused.
+// ([NKV][128][kv_split_pad(T)] bf16 each); otherwise kv is unused. The
+// output is fp32 [T][NQ D] in out, or, with out_hi and out_lo (only where
+// attn_prefill_uses_split), its bf16 hi and lo split in those two arrays.
 bool attn_prefill_uses_split(const Dims& d);
 int kv_split_pad(int T);
 hipError_t launch_attn_prefill(const Dims& d, const float* qkv, int T, float* out, uint16_t* const kv[4],
-                               hipStream_t st);
+                               hipStream_t st, uint16_t* out_hi = nullptr, uint16_t* out_lo = nullptr);
 
 hipError_t launch_rms_split(const float* X, int T, int K, const float* gain, float eps, uint16_t* hi,
                             uint16_t* lo, hipStream_t st);
@@ -140,6 +144,13 @@ hipError_t launch_rms_apply(const float* X, int T, int K, const float* gain, flo
 // or fp32 A (fp32 weights); the tiled MFMA kernel for M > 64.
 hipError_t launch_gemm(bool bf16, Epi epi, const void* A0, const void* A1, int M, int K, const void* W, int N,
                        float* C, int ldc, hipStream_t st);
+// Whether launch_gemm takes the tiled MFMA kernel for this shape.
+bool gemm_tiled_fits(bool bf16, int M, int K, int N);
+// The SwiGLU GEMM on the tiled kernel, its output Z[M, N / 2] (row pitch ldz)
+// written as bf16 hi and lo (the down projection's operand); shapes that
+// gemm_tiled_fits rejects return hipErrorInvalidValue.
+hipError_t launch_gemm_swiglu_split(const uint16_t* A0, const uint16_t* A1, int M, int K, const uint16_t* W, int N,
+                                    uint16_t* zhi, uint16_t* zlo, int ldz, hipStream_t st);
 hipError_t launch_to_f32(const void* src, bool bf16, size_t n, float* dst, hipStream_t st);
 
 // ---- sampling after the LM head (qdec_kernels.hip)

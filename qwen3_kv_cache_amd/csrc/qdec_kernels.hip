@@ -776,7 +776,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
                                                                  const uint16_t* __restrict__ kls,
                                                                  const uint16_t* __restrict__ vths,
                                                                  const uint16_t* __restrict__ vtls, int Tp,
-                                                                 float* __restrict__ out, int ldo, float qscale) {
+                                                                 float* __restrict__ out, int ldo, float qscale,
+                                                                 uint16_t* __restrict__ ohi,
+                                                                 uint16_t* __restrict__ olo) {
   using namespace fa;
   __shared__ __bf16 Kh[KT * KP], Kl[KT * KP];
   __shared__ __bf16 Vh[D * VP], Vl[D * VP];
@@ -932,11 +934,26 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
 #pragma unroll
     for (int hh = 0; hh < GROUP; ++hh) {
       const float il = 1.f / lsum[hh];
-      float* dst = out + (size_t)qp * ldo + (size_t)(g * GROUP + hh) * D + 4 * gq;
+      const size_t o = (size_t)qp * ldo + (size_t)(g * GROUP + hh) * D + 4 * gq;
 #pragma unroll
-      for (int b = 0; b < D / 16; ++b)
-        *reinterpret_cast<float4*>(dst + 16 * b) =
-            make_float4(acc[hh][b][0] * il, acc[hh][b][1] * il, acc[hh][b][2] * il, acc[hh][b][3] * il);
+      for (int b = 0; b < D / 16; ++b) {
+        const float v[4] = {acc[hh][b][0] * il, acc[hh][b][1] * il, acc[hh][b][2] * il, acc[hh][b][3] * il};
+        if (ohi) {
+          // the O projection's operand directly: bf16 hi = bf16(v), lo = bf16(v - hi)
+          // of the rounded fp32 v (no contraction into the product above)
+#pragma clang fp contract(off)
+          uint16_t h[4], l[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            h[e] = f32_to_bf16_rne(v[e]);
+            l[e] = f32_to_bf16_rne(v[e] - bf16_to_f32(h[e]));
+          }
+          *reinterpret_cast<uint2*>(ohi + o + 16 * b) = make_uint2(h[0] | ((unsigned)h[1] << 16), h[2] | ((unsigned)h[3] << 16));
+          *reinterpret_cast<uint2*>(olo + o + 16 * b) = make_uint2(l[0] | ((unsigned)l[1] << 16), l[2] | ((unsigned)l[3] << 16));
+        } else {
+          *reinterpret_cast<float4*>(out + o + 16 * b) = make_float4(v[0], v[1], v[2], v[3]);
+        }
+      }
     }
   }
 }
@@ -1321,7 +1338,9 @@ template <int EPI>
 __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint16_t* __restrict__ Ahi,
                                                           const uint16_t* __restrict__ Alo, int M, int K,
                                                           const uint16_t* __restrict__ W, int N,
-                                                          float* __restrict__ C, int ldc) {
+                                                          float* __restrict__ C, int ldc,
+                                                          uint16_t* __restrict__ Zhi,
+                                                          uint16_t* __restrict__ Zlo) {
   using namespace tg;
   __shared__ uint16_t sAh[2][BM * P], sAl[2][BM * P], sW[2][BN * P];
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
@@ -1402,9 +1421,22 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint16_t* __restr
       for (int e = 0; e < 4; ++e) {
         const int row = m0 + wm * 64 + 16 * i + 4 * gq + e;
         const float v = acc[i][j][e];
-        if (EPI == EPI_SWIGLU) {
+        if (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SPLIT) {
           const float u = __shfl_xor(v, 8, kWave);
-          if (c16 < kGuGroup && row < M) C[(size_t)row * ldc + (col / 16) * kGuGroup + c16] = silu_mul(v, u);
+          if (c16 < kGuGroup && row < M) {
+            const size_t o = (size_t)row * ldc + (col / 16) * kGuGroup + c16;
+            const float z = silu_mul(v, u);
+            if (EPI == EPI_SWIGLU) {
+              C[o] = z;
+            } else {
+              // the down projection's operand directly: bf16 hi and lo of the
+              // rounded fp32 z (no contraction into the product above)
+#pragma clang fp contract(off)
+              const uint16_t h = f32_to_bf16_rne(z);
+              Zhi[o] = h;
+              Zlo[o] = f32_to_bf16_rne(z - bf16_to_f32(h));
+            }
+          }
         } else if (row < M) {
           if (EPI == EPI_RESID)
             C[(size_t)row * ldc + col] += v;
@@ -1730,8 +1762,9 @@ bool attn_prefill_uses_split(const Dims& d) {
 }
 
 hipError_t launch_attn_prefill(const Dims& d, const float* qkv, int T, float* out, uint16_t* const kv[4],
-                               hipStream_t st) {
+                               hipStream_t st, uint16_t* out_hi, uint16_t* out_lo) {
   const int group = d.NQ / d.NKV;
+  if ((out_hi != nullptr) != (out_lo != nullptr) || (out_hi && !attn_prefill_uses_split(d))) return hipErrorInvalidValue;
   const float scale = 1.f / sqrtf((float)d.D);
   if (attn_prefill_uses_split(d)) {
     const int Tp = kv_split_pad(T);
@@ -1743,10 +1776,10 @@ hipError_t launch_attn_prefill(const Dims& d, const float* qkv, int T, float* ou
     const float qs = scale * 1.4426950408889634f;  // scores in base 2
     if (group == 2)
       attn_prefill_mfma_kernel<2><<<grid, 256, 0, st>>>(qkv, T, d.qkv(), kv[0], kv[1], kv[2], kv[3], Tp, out,
-                                                        d.NQ * d.D, qs);
+                                                        d.NQ * d.D, qs, out_hi, out_lo);
     else
       attn_prefill_mfma_kernel<1><<<grid, 256, 0, st>>>(qkv, T, d.qkv(), kv[0], kv[1], kv[2], kv[3], Tp, out,
-                                                        d.NQ * d.D, qs);
+                                                        d.NQ * d.D, qs, out_hi, out_lo);
     return hipGetLastError();
   }
 #define QDEC_PATTN_CASE(DD, GG)                                                                      \
@@ -1848,17 +1881,27 @@ hipError_t launch_gemm_rows(Epi epi, bool norm, const RowsGemm& g0, hipStream_t 
   return p.nt == 2 ? rows_dispatch<1, 2>(epi, norm, grid, g, st) : rows_dispatch<1, 1>(epi, norm, grid, g, st);
 }
 
+bool gemm_tiled_fits(bool bf16, int M, int K, int N) { return bf16 && M > 64 && N % tg::BN == 0 && K % tg::BK == 0; }
+
+hipError_t launch_gemm_swiglu_split(const uint16_t* A0, const uint16_t* A1, int M, int K, const uint16_t* W, int N,
+                                    uint16_t* zhi, uint16_t* zlo, int ldz, hipStream_t st) {
+  if (!gemm_tiled_fits(true, M, K, N)) return hipErrorInvalidValue;
+  const dim3 grid(N / tg::BN, (M + tg::BM - 1) / tg::BM);
+  gemm_tiled_kernel<EPI_SWIGLU_SPLIT><<<grid, 256, 0, st>>>(A0, A1, M, K, W, N, nullptr, ldz, zhi, zlo);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(bool bf16, Epi epi, const void* A0, const void* A1, int M, int K, const void* W, int N,
                        float* C, int ldc, hipStream_t st) {
-  if (bf16 && M > 64 && N % tg::BN == 0 && K % tg::BK == 0) {
+  if (gemm_tiled_fits(bf16, M, K, N)) {
     const dim3 grid(N / tg::BN, (M + tg::BM - 1) / tg::BM);
     const uint16_t *hi = (const uint16_t*)A0, *lo = (const uint16_t*)A1, *w = (const uint16_t*)W;
     if (epi == EPI_STORE)
-      gemm_tiled_kernel<EPI_STORE><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc);
+      gemm_tiled_kernel<EPI_STORE><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc, nullptr, nullptr);
     else if (epi == EPI_RESID)
-      gemm_tiled_kernel<EPI_RESID><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc);
+      gemm_tiled_kernel<EPI_RESID><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc, nullptr, nullptr);
     else
-      gemm_tiled_kernel<EPI_SWIGLU><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc);
+      gemm_tiled_kernel<EPI_SWIGLU><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc, nullptr, nullptr);
     return hipGetLastError();
   }
   if (bf16) {
