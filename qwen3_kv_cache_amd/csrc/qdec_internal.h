@@ -128,7 +128,8 @@ hipError_t launch_attn_rows(const Dims& d, const AttnRows& a, int nsplit, hipStr
 // Causal prefill attention over QKV rows [T, qkv()]. For head_dim 128 with
 // GQA 1 or 2 (attn_prefill_uses_split) K and V are first converted into
 // kv[0..3] = K hi, K lo ([NKV][T][128] bf16 each) and V^T hi, lo
-// ([NKV][128][kv_split_pad(T)] bf16 each); otherwise kv is unused. The
+// ([NKV][128][kv_split_pad(T)] bf16 each, keys permuted within each 32-key
+// group to the attention's operand order); otherwise kv is unused. The
 // output is fp32 [T][NQ D] in out, or, with out_hi and out_lo (only where
 // attn_prefill_uses_split), its bf16 hi and lo split in those two arrays.
 bool attn_prefill_uses_split(const Dims& d);

@@ -709,7 +709,11 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const float* __restri
 // K and V of one KV head for the matrix-core attention, converted once per
 // layer: kh / kl [g][t][128] bf16 hi / lo of the rotated keys, vth / vtl
 // [g][128][Tp] bf16 hi / lo of the values transposed (columns t >= T repeat
-// row T - 1, so every staged tile is finite). Block = (64 tokens, head g).
+// row T - 1, so every staged tile is finite). Within each 32-key group the
+// V^T columns are stored in the order the P^T operand takes its k-slots:
+// keys 4 q + e and 16 + 4 q + e (e = 0..3) at slots 8 q + e and 8 q + 4 + e,
+// so a lane's A operand of O^T = V^T P^T is one 16-byte LDS read. Block =
+// (64 tokens, head g).
 __global__ __launch_bounds__(256) void kv_split_kernel(const float* __restrict__ qkv, int T, int ld, int NQ,
                                                         int NKV, uint16_t* __restrict__ kh,
                                                         uint16_t* __restrict__ kl, uint16_t* __restrict__ vth,
@@ -754,7 +758,9 @@ __global__ __launch_bounds__(256) void kv_split_kernel(const float* __restrict__
       h4[e] = (__bf16)v;
       l4[e] = (__bf16)(v - (float)h4[e]);
     }
-    const size_t o = ((size_t)g * D + d) * Tp + t0 + tq;
+    // key quad qi of its 32-key group goes to slot 8 qi (qi < 4) or 8 (qi - 4) + 4
+    const int qi = (tq % 32) / 4;
+    const size_t o = ((size_t)g * D + d) * Tp + t0 + (tq - tq % 32) + (qi < 4 ? 8 * qi : 8 * (qi - 4) + 4);
     *reinterpret_cast<uint2*>(vth + o) = __builtin_bit_cast(uint2, h4);
     *reinterpret_cast<uint2*>(vtl + o) = __builtin_bit_cast(uint2, l4);
   }
@@ -914,13 +920,10 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
     for (int b = 0; b < D / 16; ++b)
 #pragma unroll
       for (int c = 0; c < KH; ++c) {
-        const int off = (16 * b + c16) * VP + 32 * c + 4 * gq;
-        const uint2 h0 = *reinterpret_cast<const uint2*>(&Vh[off]);
-        const uint2 h1 = *reinterpret_cast<const uint2*>(&Vh[off + 16]);
-        const uint2 l0 = *reinterpret_cast<const uint2*>(&Vl[off]);
-        const uint2 l1 = *reinterpret_cast<const uint2*>(&Vl[off + 16]);
-        const bf16x8_t vh = __builtin_bit_cast(bf16x8_t, make_uint4(h0.x, h0.y, h1.x, h1.y));
-        const bf16x8_t vl = __builtin_bit_cast(bf16x8_t, make_uint4(l0.x, l0.y, l1.x, l1.y));
+        // keys 4 gq + e and 16 + 4 gq + e of the group sit together at 8 gq
+        const int off = (16 * b + c16) * VP + 32 * c + 8 * gq;
+        const bf16x8_t vh = *reinterpret_cast<const bf16x8_t*>(&Vh[off]);
+        const bf16x8_t vl = *reinterpret_cast<const bf16x8_t*>(&Vl[off]);
 #pragma unroll
         for (int hh = 0; hh < GROUP; ++hh) {
           acc[hh][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vh, ph[hh][c], acc[hh][b], 0, 0, 0);
