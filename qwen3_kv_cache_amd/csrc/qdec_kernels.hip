@@ -1345,6 +1345,7 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(RowsGemm g) {
 // distinct banks. Epilogues as in gemm_bf16x2_kernel.
 namespace tg {
 constexpr int BM = 128, BN = 128, BK = 32;
+constexpr size_t kTiledWSliceBytes = size_t(3) << 20;  // W bytes per XCD column group
 constexpr int P = BK + 8;  // bf16 pitch of an LDS row
 }  // namespace tg
 
@@ -1360,7 +1361,24 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint16_t* __restr
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   const int c16 = lane % 16, gq = lane / 16;
   const int wm = w / 2, wn = w % 2;
-  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+  // Workgroup i runs on XCD i % 8. The tiles are dealt so that each XCD owns
+  // one of gc column groups and one of 8 / gc row groups, gc the smallest
+  // power of two that keeps its W slice within kTiledWSliceBytes (so the slice
+  // stays in the XCD's L2 while the XCD sweeps its row tiles, column fastest).
+  // Launch order alone would give every XCD a column slice of every row tile,
+  // so all eight L2s would read all of A.
+  int tile = blockIdx.x + blockIdx.y * gridDim.x;
+  {
+    const size_t wbytes = (size_t)N * K * 2;
+    int gc = 1;
+    while (gc < 8 && (wbytes > (size_t)gc * kTiledWSliceBytes || gridDim.y % (8 / gc) != 0)) gc *= 2;
+    if (gridDim.x % gc == 0 && gridDim.y % (8 / gc) == 0) {
+      const int x = tile % 8, j = tile / 8;
+      const int cw = gridDim.x / gc, rh = gridDim.y / (8 / gc);
+      tile = ((x / gc) * rh + j / cw) * gridDim.x + (x % gc) * cw + j % cw;
+    }
+  }
+  const int n0 = (tile % gridDim.x) * BN, m0 = (tile / gridDim.x) * BM;
 
   // staging: 128 rows x 4 chunks of 16 bytes per matrix; thread t moves
   // chunks t and t + 256 (rows t / 4 and t / 4 + 64, chunk t % 4)
