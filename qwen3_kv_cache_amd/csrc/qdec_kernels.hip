@@ -1340,13 +1340,18 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(RowsGemm g) {
 // 128 x 128 output tiles and K steps of 32 staged in LDS (double buffered:
 // the next step's global loads are in flight while the current one is
 // multiplied). 4 waves in a 2 x 2 arrangement, each 64 x 64 = 4 x 4 MFMA
-// tiles of 16 x 16, two MFMAs (hi, lo) per tile and step. LDS rows are
-// padded to 80 bytes so the 16 rows an MFMA operand read touches fall in
-// distinct banks. Epilogues as in gemm_bf16x2_kernel.
+// tiles of 16 x 16, two MFMAs (hi, lo) per tile and step. LDS rows are 64
+// bytes with XOR-swizzled 16-byte chunks (tg_sw). Epilogues as in
+// gemm_bf16x2_kernel.
 namespace tg {
 constexpr int BM = 128, BN = 128, BK = 32;
 constexpr size_t kTiledWSliceBytes = size_t(3) << 20;  // W bytes per XCD column group
-constexpr int P = BK + 8;  // bf16 pitch of an LDS row
+constexpr int P = BK;  // bf16 pitch of an LDS row (chunks XOR-swizzled)
+// 16-byte chunk c of LDS row r sits at chunk c ^ ((r / 4) % 4): the 16 rows
+// an MFMA operand read touches (one chunk each) then fall in distinct banks
+// without padding, which keeps the double-buffered tiles at 48 KB (three
+// workgroups per CU)
+__device__ __forceinline__ int tg_sw(int r, int c) { return r * P + 8 * (c ^ ((r >> 2) & 3)); }
 }  // namespace tg
 
 template <int EPI>
@@ -1387,7 +1392,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint16_t* __restr
   const size_t a1 = (size_t)min(m0 + srow + 64, M - 1) * K + 8 * skc;
   const size_t w0 = (size_t)(n0 + srow) * K + 8 * skc;
   const size_t w1 = (size_t)(n0 + srow + 64) * K + 8 * skc;
-  const int l0 = srow * P + 8 * skc, l1 = (srow + 64) * P + 8 * skc;
+  const int l0 = tg_sw(srow, skc), l1 = tg_sw(srow + 64, skc);
   uint4 rh0, rh1, rl0, rl1, rw0, rw1;
 #define QDEC_TG_LOAD(k)                                         \
   rh0 = *reinterpret_cast<const uint4*>(Ahi + a0 + (k));        \
@@ -1422,13 +1427,13 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint16_t* __restr
     bf16x8_t ah[4], al[4], b[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int off = (wm * 64 + 16 * i + c16) * P + 8 * gq;
+      const int off = tg_sw(wm * 64 + 16 * i + c16, gq);
       ah[i] = *reinterpret_cast<const bf16x8_t*>(&sAh[buf][off]);
       al[i] = *reinterpret_cast<const bf16x8_t*>(&sAl[buf][off]);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      b[j] = *reinterpret_cast<const bf16x8_t*>(&sW[buf][(wn * 64 + 16 * j + c16) * P + 8 * gq]);
+      b[j] = *reinterpret_cast<const bf16x8_t*>(&sW[buf][tg_sw(wn * 64 + 16 * j + c16, gq)]);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
