@@ -78,6 +78,8 @@ WORKLOADS: Dict[str, Workload] = {
     "branch16": Workload("branch16", QWEN3_0P6B, 2, 4, 512, 8, 128, 128, n_branch=16),
     # 0.6B: 8192-token prompt, 6000 audio rows, 64 steps
     "prefill8k": Workload("prefill8k", QWEN3_0P6B, 2, 5, 8192, 8, 6000, 64),
+    # 0.6B: 3001-token prompt (ragged against every tile size), 2000 audio rows, 16 steps
+    "ragged3k": Workload("ragged3k", QWEN3_0P6B, 2, 6, 3001, 8, 2000, 16),
 }
 
 

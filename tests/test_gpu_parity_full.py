@@ -110,6 +110,13 @@ def test_prefill8k_teacher_forced():
     run_teacher_forced("prefill8k")
 
 
+def test_ragged3k_teacher_forced():
+    # 3001 tokens: a partial last tile for every prefill kernel (query tiles of
+    # 64, GEMM tiles of 128, K/V padding to 64), the XCD head placement of the
+    # attention (47 query tiles) and the column/row-group deal of the GEMMs
+    run_teacher_forced("ragged3k")
+
+
 def test_branch16_clone_decode():
     from qwen3_kv_cache_amd import qdec
     torch, dev = torch_dev()
