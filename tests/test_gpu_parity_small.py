@@ -24,6 +24,9 @@ MID = {
     # MHA (group 1), D=128, one layer, prompt of one token
     "d128_g1_T1": (synth.custom_shape(hidden=256, n_layer=1, n_q_head=4, n_kv_head=4, head_dim=128, ffn=512,
                                       vocab=1000, bf16=True), 1, 0, 0, 20),
+    # a prompt made only of audio rows (span [0, T)): no id is read
+    "d64_g2_allaudio": (synth.custom_shape(hidden=256, n_layer=2, n_q_head=4, n_kv_head=2, head_dim=64, ffn=768,
+                                           vocab=5003, bf16=True), 40, 0, 40, 6),
 }
 
 
