@@ -180,6 +180,54 @@ def branch_stream(w: Workload, b: int, n: Optional[int] = None) -> np.ndarray:
     return _rng(w.prompt_seed, 10 + b).integers(0, w.shape.vocab, size=n).astype(np.int32)
 
 
+@dataclasses.dataclass(frozen=True)
+class AdaptorShape:
+    """Sizes of the audio adaptor (linear1, linear2, pre-norm blocks)."""
+    enc_dim: int = 512
+    mid_dim: int = 2048
+    dim: int = 1024
+    ffn_dim: int = 256
+    n_block: int = 2
+    n_head: int = 8
+
+
+def adaptor_params(a: AdaptorShape) -> List[tuple]:
+    """(name, shape, kind) in draw order; kind "w" matrix [out, in], "b" bias,
+    "g" LayerNorm gain."""
+    D, F = a.dim, a.ffn_dim
+    out = [("linear1.w", (a.mid_dim, a.enc_dim), "w"), ("linear1.b", (a.mid_dim,), "b"),
+           ("linear2.w", (D, a.mid_dim), "w"), ("linear2.b", (D,), "b")]
+    for i in range(a.n_block):
+        p = f"blocks.{i}."
+        out += [(p + "norm1.g", (D,), "g"), (p + "norm1.b", (D,), "b")]
+        for t in ("q", "k", "v", "o"):
+            out += [(p + t + ".w", (D, D), "w"), (p + t + ".b", (D,), "b")]
+        out += [(p + "norm2.g", (D,), "g"), (p + "norm2.b", (D,), "b"),
+                (p + "fc1.w", (F, D), "w"), (p + "fc1.b", (F,), "b"),
+                (p + "fc2.w", (D, F), "w"), (p + "fc2.b", (D,), "b")]
+    return out
+
+
+def make_adaptor_weights(a: AdaptorShape, seed_id: int):
+    """Adaptor parameters from stream 3, in adaptor_params order: matrices and
+    biases 0.02 N(0,1), gains 1 + 0.02 N(0,1), rounded to bf16. Returns
+    (float32 values, bf16 bit patterns), both keyed by name."""
+    rng = _rng(seed_id, 3)
+    scale = np.float32(0.02)
+    f32: Dict[str, np.ndarray] = {}
+    bits: Dict[str, np.ndarray] = {}
+    for name, shp, kind in adaptor_params(a):
+        z = rng.standard_normal(shp, dtype=np.float32)
+        w = (np.float32(1.0) + scale * z) if kind == "g" else (scale * z)
+        bits[name], f32[name] = _round_bf16(w.astype(np.float32, copy=False))
+    return f32, bits
+
+
+def encoder_frames(seed_id: int, n: int, width: int) -> np.ndarray:
+    """Encoder output frames float32[n, width], N(0,1), stream 4."""
+    return _rng(seed_id, 4).standard_normal((n, width), dtype=np.float32)
+
+
 def random_ids(seed: int, n: int, vocab: int) -> np.ndarray:
     return _rng(1000 + seed, 1).integers(0, vocab, size=n).astype(np.int32)
 
