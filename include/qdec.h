@@ -223,6 +223,73 @@ typedef struct {
 int qdec_sample(qdec_model* m, const float* logits_dev, int32_t n_rows, const qdec_sampling* params,
                 const int32_t* history_dev, int32_t history_len, const float* uniforms_host, int32_t* tokens_dev);
 
+/* ---------------------------------------------------------------- adaptor
+ * The audio adaptor that makes the rows qdec_prefill takes as audio_dev
+ * (transcribe.cpp "Forward map - funasr_nano", section "Adaptor", stage table
+ * and its list of deviations from the encoder block): encoder frames
+ * [T, enc_dim] -> linear1 + bias -> ReLU -> linear2 + bias -> n_block blocks,
+ * each  x += O(MHA(LN1(x)))  with biased Q/K/V/O projections and every frame
+ * attending to every frame (scale 1/sqrt(dim / n_head)), then
+ * x += fc2(ReLU(fc1(LN2(x))))  with biases. LN(x) = (x - mean) /
+ * sqrt(var + ln_eps) * g + b over the row, population variance. The caller
+ * keeps the first rows it needs as the prompt's audio span. Weights bf16;
+ * activations, norms and softmax fp32. The head count is not on the page:
+ * it is a parameter (8 heads of 128 for the 1024-wide adaptor). */
+typedef struct {
+  int32_t enc_dim;  /* linear1 input, a multiple of 32 */
+  int32_t mid_dim;  /* linear1 output, a multiple of 128 */
+  int32_t dim;      /* linear2 output and block width, n_head * 128 */
+  int32_t ffn_dim;  /* block FFN width, a multiple of 128 */
+  int32_t n_block;  /* 1 .. 8 */
+  int32_t n_head;   /* heads of 128 */
+  float ln_eps;     /* > 0 (1e-12 on the page) */
+  int32_t weight_dtype; /* QDEC_BF16 */
+} qdec_adaptor_config;
+
+/* Per block, QDEC_AB_PER_BLOCK device pointers in this order; matrices
+ * [out, in] row-major, vectors [out]. */
+enum {
+  QDEC_AB_NORM1_G = 0, QDEC_AB_NORM1_B, QDEC_AB_Q_W, QDEC_AB_Q_B, QDEC_AB_K_W, QDEC_AB_K_B, QDEC_AB_V_W,
+  QDEC_AB_V_B, QDEC_AB_O_W, QDEC_AB_O_B, QDEC_AB_NORM2_G, QDEC_AB_NORM2_B, QDEC_AB_FC1_W, QDEC_AB_FC1_B,
+  QDEC_AB_FC2_W, QDEC_AB_FC2_B, QDEC_AB_PER_BLOCK
+};
+
+/* Device pointers, all bf16: linear1_w [mid_dim, enc_dim], linear1_b
+ * [mid_dim], linear2_w [dim, mid_dim], linear2_b [dim]; block: HOST array of
+ * n_block * QDEC_AB_PER_BLOCK device pointers, block-major (q/k/v/o [dim,
+ * dim], fc1 [ffn_dim, dim], fc2 [dim, ffn_dim]). Ownership: the matrices
+ * linear1_w, linear2_w, o, fc1 and fc2 are borrowed and must stay valid until
+ * qdec_adaptor_destroy; q/k/v are packed into one [3 dim, dim] copy, and
+ * every bias and norm vector is copied (as fp32), so those may be freed. */
+typedef struct {
+  const void* linear1_w;
+  const void* linear1_b;
+  const void* linear2_w;
+  const void* linear2_b;
+  const void* const* block;
+} qdec_adaptor_weights;
+
+typedef struct qdec_adaptor qdec_adaptor;
+
+/* Validate (QDEC_E_INVALID), copy and pack on `hip_stream`; the stream is
+ * synchronised before return. */
+int qdec_adaptor_create(const qdec_adaptor_config* cfg, const qdec_adaptor_weights* w, void* hip_stream,
+                        qdec_adaptor** out);
+
+/* Adaptor rows for n_frames encoder frames.
+ *   frames_dev: DEVICE fp32 [n_frames, enc_dim] (borrowed, not modified)
+ *   n_frames:   >= 1
+ *   out_dev:    DEVICE fp32 [n_frames, dim], receives the rows (it also
+ *               holds the residual stream while the blocks run)
+ * Scratch for the largest n_frames seen so far is kept (allocated on first
+ * use, QDEC_E_OOM if that fails). Work is enqueued on the adaptor's stream;
+ * outputs are valid once it is synchronised. Errors: QDEC_E_INVALID for NULL
+ * or undersized buffers, QDEC_E_DEVICE for HIP errors. */
+int qdec_adaptor_run(qdec_adaptor* a, const float* frames_dev, int32_t n_frames, float* out_dev);
+
+/* Free the adaptor (synchronises its stream). NULL is a no-op. */
+void qdec_adaptor_destroy(qdec_adaptor* a);
+
 /* n_past of the state (-1 for NULL). */
 int32_t qdec_state_pos(const qdec_state* s);
 

@@ -1092,3 +1092,218 @@ int qdec_clone_state(const qdec_state* src, qdec_state** dst) {
 }
 
 }  // extern "C"
+
+// ================================================================= adaptor
+// The audio adaptor (transcribe.cpp "Forward map - funasr_nano", section
+// "Adaptor"): linear1 + ReLU, linear2, then pre-norm blocks of biased MHA with
+// every frame attending to every frame, and a ReLU FFN. All on the prefill
+// kernels: bf16 hi/lo split operands, the tiled (or small-M) MFMA GEMMs with
+// bias / ReLU / residual epilogues, LayerNorm written as the next GEMM's
+// operand, and the matrix-core attention without the causal mask.
+
+struct qdec_adaptor {
+  qdec_adaptor_config c{};
+  hipStream_t stream = nullptr;
+  const uint16_t* w1 = nullptr;
+  const uint16_t* w2 = nullptr;
+  float* b1 = nullptr;
+  float* b2 = nullptr;
+  struct Block {
+    uint16_t* wqkv = nullptr;  // [3 dim, dim]: q rows, k rows, v rows
+    const uint16_t *wo = nullptr, *fc1 = nullptr, *fc2 = nullptr;
+    float *bqkv = nullptr, *bo = nullptr, *n1g = nullptr, *n1b = nullptr, *n2g = nullptr, *n2b = nullptr;
+    float *bf1 = nullptr, *bf2 = nullptr;
+  };
+  std::vector<Block> blocks;
+  float* vecs = nullptr;  // every bias and norm vector, fp32
+  // scratch for up to `cap` frames
+  int cap = 0;
+  uint16_t* A0 = nullptr;  // bf16 hi of the current GEMM operand
+  uint16_t* A1 = nullptr;  // bf16 lo
+  float* H = nullptr;      // linear1 / fc1 output
+  float* QKV = nullptr;
+  uint16_t* kv[4] = {nullptr, nullptr, nullptr, nullptr};
+};
+
+namespace {
+
+Dims adaptor_dims(const qdec_adaptor_config& c) {
+  return Dims{1, c.dim, c.n_head, c.n_head, c.dim / c.n_head, 0, 0, 0.f};
+}
+
+void free_adaptor_scratch(qdec_adaptor* a) {
+  for (void* p : {(void*)a->A0, (void*)a->A1, (void*)a->H, (void*)a->QKV, (void*)a->kv[0], (void*)a->kv[1],
+                  (void*)a->kv[2], (void*)a->kv[3]})
+    if (p) (void)hipFree(p);
+  a->A0 = a->A1 = nullptr;
+  a->H = a->QKV = nullptr;
+  for (auto& k : a->kv) k = nullptr;
+  a->cap = 0;
+}
+
+void free_adaptor(qdec_adaptor* a) {
+  if (!a) return;
+  (void)hipStreamSynchronize(a->stream);
+  free_adaptor_scratch(a);
+  for (auto& b : a->blocks)
+    if (b.wqkv) (void)hipFree(b.wqkv);
+  if (a->vecs) (void)hipFree(a->vecs);
+  delete a;
+}
+
+int ensure_adaptor(qdec_adaptor* a, int T) {
+  if (T <= a->cap) return QDEC_OK;
+  free_adaptor_scratch(a);
+  const qdec_adaptor_config& c = a->c;
+  const size_t wide = (size_t)std::max(std::max(c.enc_dim, c.mid_dim), std::max(c.dim, c.ffn_dim));
+  const size_t Tp = (size_t)kv_split_pad(T);
+  int e;
+  if ((e = dev_alloc(&a->A0, (size_t)T * wide, "adaptor operand")) ||
+      (e = dev_alloc(&a->A1, (size_t)T * wide, "adaptor operand")) ||
+      (e = dev_alloc(&a->H, (size_t)T * std::max(c.mid_dim, c.ffn_dim), "adaptor hidden")) ||
+      (e = dev_alloc(&a->QKV, (size_t)T * 3 * c.dim, "adaptor qkv")) ||
+      (e = dev_alloc(&a->kv[0], (size_t)T * c.dim, "adaptor K")) ||
+      (e = dev_alloc(&a->kv[1], (size_t)T * c.dim, "adaptor K")) ||
+      (e = dev_alloc(&a->kv[2], Tp * c.dim, "adaptor V")) || (e = dev_alloc(&a->kv[3], Tp * c.dim, "adaptor V"))) {
+    free_adaptor_scratch(a);
+    return e;
+  }
+  a->cap = T;
+  return QDEC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qdec_adaptor_create(const qdec_adaptor_config* cfg, const qdec_adaptor_weights* w, void* hip_stream,
+                        qdec_adaptor** out) {
+  if (!out) return fail(QDEC_E_INVALID, "out is NULL");
+  *out = nullptr;
+  if (!cfg) return fail(QDEC_E_INVALID, "config is NULL");
+  const qdec_adaptor_config& c = *cfg;
+  if (c.weight_dtype != QDEC_BF16) return fail(QDEC_E_INVALID, "the adaptor takes bf16 weights");
+  if (c.enc_dim < 32 || c.enc_dim % 32 || c.mid_dim < 128 || c.mid_dim % 128 || c.ffn_dim < 128 ||
+      c.ffn_dim % 128)
+    return fail(QDEC_E_INVALID, "enc_dim %d (multiple of 32), mid_dim %d and ffn_dim %d (multiples of 128)",
+                c.enc_dim, c.mid_dim, c.ffn_dim);
+  if (c.n_head < 1 || c.n_head > 64 || c.dim != c.n_head * 128)
+    return fail(QDEC_E_INVALID, "dim %d must be n_head (%d) * 128", c.dim, c.n_head);
+  if (c.n_block < 1 || c.n_block > 8) return fail(QDEC_E_INVALID, "n_block %d outside 1 .. 8", c.n_block);
+  if (!(c.ln_eps > 0.f) || !std::isfinite(c.ln_eps)) return fail(QDEC_E_INVALID, "ln_eps must be > 0");
+  if (!w || !w->linear1_w || !w->linear1_b || !w->linear2_w || !w->linear2_b || !w->block)
+    return fail(QDEC_E_INVALID, "adaptor weights incomplete");
+  const size_t D = c.dim, F = c.ffn_dim;
+  if (int e = check_dev(w->linear1_w, (size_t)c.mid_dim * c.enc_dim * 2, "linear1_w")) return e;
+  if (int e = check_dev(w->linear1_b, (size_t)c.mid_dim * 2, "linear1_b")) return e;
+  if (int e = check_dev(w->linear2_w, D * c.mid_dim * 2, "linear2_w")) return e;
+  if (int e = check_dev(w->linear2_b, D * 2, "linear2_b")) return e;
+  for (int b = 0; b < c.n_block; ++b) {
+    const void* const* t = w->block + (size_t)b * QDEC_AB_PER_BLOCK;
+    for (int i = 0; i < QDEC_AB_PER_BLOCK; ++i) {
+      const bool mat = i == QDEC_AB_Q_W || i == QDEC_AB_K_W || i == QDEC_AB_V_W || i == QDEC_AB_O_W ||
+                       i == QDEC_AB_FC1_W || i == QDEC_AB_FC2_W;
+      const size_t n = i == QDEC_AB_FC1_W || i == QDEC_AB_FC2_W ? F * D : mat ? D * D : i == QDEC_AB_FC1_B ? F : D;
+      char what[48];
+      snprintf(what, sizeof what, "block %d tensor %d", b, i);
+      if (int e = check_dev(t[i], n * 2, what)) return e;
+    }
+  }
+  qdec_adaptor* a = new (std::nothrow) qdec_adaptor();
+  if (!a) return fail(QDEC_E_OOM, "host allocation failed");
+  a->c = c;
+  a->stream = (hipStream_t)hip_stream;
+  a->w1 = (const uint16_t*)w->linear1_w;
+  a->w2 = (const uint16_t*)w->linear2_w;
+  const size_t per_block = 9 * D + F;
+  const size_t nvec = (size_t)c.mid_dim + D + (size_t)c.n_block * per_block;
+  if (int e = dev_alloc(&a->vecs, nvec, "adaptor vectors")) {
+    free_adaptor(a);
+    return e;
+  }
+  hipStream_t st = a->stream;
+  auto fail_dev = [&](const char* what, hipError_t he) {
+    const int r = fail(QDEC_E_DEVICE, "%s: %s", what, hipGetErrorString(he));
+    free_adaptor(a);
+    return r;
+  };
+  hipError_t he;
+  float* v = a->vecs;
+  a->b1 = v;
+  v += c.mid_dim;
+  a->b2 = v;
+  v += D;
+  if ((he = launch_to_f32(w->linear1_b, true, c.mid_dim, a->b1, st))) return fail_dev("linear1_b", he);
+  if ((he = launch_to_f32(w->linear2_b, true, D, a->b2, st))) return fail_dev("linear2_b", he);
+  a->blocks.resize(c.n_block);
+  for (int b = 0; b < c.n_block; ++b) {
+    const void* const* t = w->block + (size_t)b * QDEC_AB_PER_BLOCK;
+    qdec_adaptor::Block& k = a->blocks[b];
+    if (int e = dev_alloc(&k.wqkv, 3 * D * D, "adaptor wqkv")) {
+      free_adaptor(a);
+      return e;
+    }
+    const size_t mb = D * D * 2;
+    if ((he = hipMemcpyAsync(k.wqkv, t[QDEC_AB_Q_W], mb, hipMemcpyDeviceToDevice, st)) ||
+        (he = hipMemcpyAsync(k.wqkv + D * D, t[QDEC_AB_K_W], mb, hipMemcpyDeviceToDevice, st)) ||
+        (he = hipMemcpyAsync(k.wqkv + 2 * D * D, t[QDEC_AB_V_W], mb, hipMemcpyDeviceToDevice, st)))
+      return fail_dev("pack wqkv", he);
+    k.wo = (const uint16_t*)t[QDEC_AB_O_W];
+    k.fc1 = (const uint16_t*)t[QDEC_AB_FC1_W];
+    k.fc2 = (const uint16_t*)t[QDEC_AB_FC2_W];
+    k.bqkv = v;
+    k.bo = v + 3 * D;
+    k.n1g = v + 4 * D;
+    k.n1b = v + 5 * D;
+    k.n2g = v + 6 * D;
+    k.n2b = v + 7 * D;
+    k.bf2 = v + 8 * D;
+    k.bf1 = v + 9 * D;
+    v += per_block;
+    const struct {
+      int idx;
+      float* dst;
+      size_t n;
+    } vecs[] = {{QDEC_AB_Q_B, k.bqkv, D}, {QDEC_AB_K_B, k.bqkv + D, D}, {QDEC_AB_V_B, k.bqkv + 2 * D, D},
+                {QDEC_AB_O_B, k.bo, D},   {QDEC_AB_NORM1_G, k.n1g, D},  {QDEC_AB_NORM1_B, k.n1b, D},
+                {QDEC_AB_NORM2_G, k.n2g, D}, {QDEC_AB_NORM2_B, k.n2b, D}, {QDEC_AB_FC2_B, k.bf2, D},
+                {QDEC_AB_FC1_B, k.bf1, F}};
+    for (const auto& x : vecs)
+      if ((he = launch_to_f32(t[x.idx], true, x.n, x.dst, st))) return fail_dev("adaptor vector", he);
+  }
+  if ((he = hipStreamSynchronize(st))) return fail_dev("adaptor packing", he);
+  *out = a;
+  return ok();
+}
+
+int qdec_adaptor_run(qdec_adaptor* a, const float* frames_dev, int32_t n_frames, float* out_dev) {
+  if (!a) return fail(QDEC_E_INVALID, "adaptor is NULL");
+  if (n_frames < 1) return fail(QDEC_E_INVALID, "n_frames %d < 1", n_frames);
+  const qdec_adaptor_config& c = a->c;
+  const int T = n_frames, D = c.dim, F = c.ffn_dim;
+  if (int e = check_dev(frames_dev, (size_t)T * c.enc_dim * sizeof(float), "frames_dev")) return e;
+  if (int e = check_dev(out_dev, (size_t)T * D * sizeof(float), "out_dev")) return e;
+  if (int e = ensure_adaptor(a, T)) return e;
+  hipStream_t st = a->stream;
+  uint16_t *A0 = a->A0, *A1 = a->A1;
+  const Dims ad = adaptor_dims(c);
+  LAUNCH(launch_rms_split(frames_dev, T, c.enc_dim, nullptr, 0.f, A0, A1, st));
+  LAUNCH(launch_gemm(true, EPI_RELU, A0, A1, T, c.enc_dim, a->w1, c.mid_dim, a->H, c.mid_dim, st, a->b1));
+  LAUNCH(launch_rms_split(a->H, T, c.mid_dim, nullptr, 0.f, A0, A1, st));
+  LAUNCH(launch_gemm(true, EPI_STORE, A0, A1, T, c.mid_dim, a->w2, D, out_dev, D, st, a->b2));
+  for (const qdec_adaptor::Block& k : a->blocks) {
+    LAUNCH(launch_ln_split(out_dev, T, D, k.n1g, k.n1b, c.ln_eps, A0, A1, st));
+    LAUNCH(launch_gemm(true, EPI_STORE, A0, A1, T, D, k.wqkv, 3 * D, a->QKV, 3 * D, st, k.bqkv));
+    LAUNCH(launch_attn_prefill(ad, a->QKV, T, nullptr, a->kv, st, A0, A1, false));
+    LAUNCH(launch_gemm(true, EPI_RESID, A0, A1, T, D, k.wo, D, out_dev, D, st, k.bo));
+    LAUNCH(launch_ln_split(out_dev, T, D, k.n2g, k.n2b, c.ln_eps, A0, A1, st));
+    LAUNCH(launch_gemm(true, EPI_RELU, A0, A1, T, D, k.fc1, F, a->H, F, st, k.bf1));
+    LAUNCH(launch_rms_split(a->H, T, F, nullptr, 0.f, A0, A1, st));
+    LAUNCH(launch_gemm(true, EPI_RESID, A0, A1, T, F, k.fc2, D, out_dev, D, st, k.bf2));
+  }
+  return ok();
+}
+
+void qdec_adaptor_destroy(qdec_adaptor* a) { free_adaptor(a); }
+
+}  // extern "C"

@@ -66,7 +66,8 @@ hipError_t launch_embed_prefill(const Dims& d, bool bf16, const void* E, const i
 
 // EPI_SWIGLU_SPLIT (tiled GEMM only): the SwiGLU output written as bf16 hi
 // and lo, the next GEMM's operand, instead of fp32
-enum Epi { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_HEAD = 3, EPI_SWIGLU_SPLIT = 4 };
+// EPI_RELU (bf16 GEMMs): C = max(v + bias, 0)
+enum Epi { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_HEAD = 3, EPI_SWIGLU_SPLIT = 4, EPI_RELU = 5 };
 
 // Arguments of the fused small-M GEMM (gemm_rows_kernel): up to 64 fp32
 // activation rows against bf16 weights, optional RMSNorm prologue, split-K
@@ -134,17 +135,24 @@ hipError_t launch_attn_rows(const Dims& d, const AttnRows& a, int nsplit, hipStr
 // attn_prefill_uses_split), its bf16 hi and lo split in those two arrays.
 bool attn_prefill_uses_split(const Dims& d);
 int kv_split_pad(int T);
+// causal = false (only where attn_prefill_uses_split): every query sees every key.
 hipError_t launch_attn_prefill(const Dims& d, const float* qkv, int T, float* out, uint16_t* const kv[4],
-                               hipStream_t st, uint16_t* out_hi = nullptr, uint16_t* out_lo = nullptr);
+                               hipStream_t st, uint16_t* out_hi = nullptr, uint16_t* out_lo = nullptr,
+                               bool causal = true);
 
 hipError_t launch_rms_split(const float* X, int T, int K, const float* gain, float eps, uint16_t* hi,
                             uint16_t* lo, hipStream_t st);
+// LayerNorm (population variance, gain and bias) of T rows of K, as bf16 hi/lo.
+hipError_t launch_ln_split(const float* X, int T, int K, const float* gain, const float* bias, float eps,
+                           uint16_t* hi, uint16_t* lo, hipStream_t st);
 hipError_t launch_rms_apply(const float* X, int T, int K, const float* gain, float eps, float* out,
                             hipStream_t st);
 // C[M, N] (+)= A[M, K] . W[N, K]^T with a bf16 hi/lo split A (bf16 weights)
 // or fp32 A (fp32 weights); the tiled MFMA kernel for M > 64.
+// bias (fp32 [N], bf16 weights only) is added to each output before the
+// epilogue (STORE, RESID, RELU); nullptr for none.
 hipError_t launch_gemm(bool bf16, Epi epi, const void* A0, const void* A1, int M, int K, const void* W, int N,
-                       float* C, int ldc, hipStream_t st);
+                       float* C, int ldc, hipStream_t st, const float* bias = nullptr);
 // Whether launch_gemm takes the tiled MFMA kernel for this shape.
 bool gemm_tiled_fits(bool bf16, int M, int K, int N);
 // The SwiGLU GEMM on the tiled kernel, its output Z[M, N / 2] (row pitch ldz)

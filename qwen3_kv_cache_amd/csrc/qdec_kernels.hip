@@ -784,7 +784,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
                                                                  const uint16_t* __restrict__ vtls, int Tp,
                                                                  float* __restrict__ out, int ldo, float qscale,
                                                                  uint16_t* __restrict__ ohi,
-                                                                 uint16_t* __restrict__ olo) {
+                                                                 uint16_t* __restrict__ olo, int causal) {
   using namespace fa;
   __shared__ __bf16 Kh[KT * KP], Kl[KT * KP];
   __shared__ __bf16 Vh[D * VP], Vl[D * VP];
@@ -841,7 +841,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
   const uint16_t* kl_g = kls + (size_t)g * T * D;
   const uint16_t* vh_g = vths + (size_t)g * D * Tp;
   const uint16_t* vl_g = vtls + (size_t)g * D * Tp;
-  const int last_key = min(T, q0 + QT) - 1;
+  // causal: keys up to the block's last query; otherwise every key
+  const int last_key = causal ? min(T, q0 + QT) - 1 : T - 1;
+  const int qlim = causal ? qp : T - 1;  // this lane's last visible key
   for (int k0 = 0; k0 <= last_key; k0 += KT) {
     __syncthreads();
     // copies of the converted tiles: K rows of 16-byte chunks (key c / 16,
@@ -893,7 +895,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int key = k0 + 16 * j + 4 * gq + e;
-          if (key > qp || key >= T) sc[hh][j][e] = -INFINITY;
+          if (key > qlim || key >= T) sc[hh][j][e] = -INFINITY;
           mx = fmaxf(mx, sc[hh][j][e]);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
@@ -998,6 +1000,32 @@ __global__ __launch_bounds__(256) void rms_split_kernel(const float* __restrict_
   }
 }
 
+// LayerNorm of each row (mean and population variance over K, gain and bias)
+// written as the next GEMM's bf16 hi/lo operand. Block = one row.
+__global__ __launch_bounds__(256) void ln_split_kernel(const float* __restrict__ X, int K,
+                                                        const float* __restrict__ gain, const float* __restrict__ bias,
+                                                        float eps, uint16_t* __restrict__ hi,
+                                                        uint16_t* __restrict__ lo) {
+  __shared__ float red[8];
+  const int t = blockIdx.x;
+  const float* x = X + (size_t)t * K;
+  float s = 0.f;
+  for (int i = threadIdx.x; i < K; i += blockDim.x) s += x[i];
+  const float mean = block_sum(s, red) / (float)K;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < K; i += blockDim.x) {
+    const float c = x[i] - mean;
+    ss = fmaf(c, c, ss);
+  }
+  const float inv = 1.f / sqrtf(block_sum(ss, red) / (float)K + eps);
+  for (int i = threadIdx.x; i < K; i += blockDim.x) {
+    const float v = (x[i] - mean) * inv * gain[i] + bias[i];
+    const uint16_t h = f32_to_bf16_rne(v);
+    hi[(size_t)t * K + i] = h;
+    lo[(size_t)t * K + i] = f32_to_bf16_rne(v - bf16_to_f32(h));
+  }
+}
+
 __global__ __launch_bounds__(256) void rms_apply_kernel(const float* __restrict__ X, int K,
                                                          const float* __restrict__ gain, float eps,
                                                          float* __restrict__ out) {
@@ -1024,7 +1052,8 @@ template <int EPI>
 __global__ __launch_bounds__(256) void gemm_bf16x2_kernel(const uint16_t* __restrict__ Ahi,
                                                            const uint16_t* __restrict__ Alo, int M, int K,
                                                            const uint16_t* __restrict__ W, int N,
-                                                           float* __restrict__ C, int ldc) {
+                                                           float* __restrict__ C, int ldc,
+                                                           const float* __restrict__ bias) {
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int m0 = blockIdx.y * 64 + (wave / 2) * 32;
   const int n0 = blockIdx.x * 64 + (wave % 2) * 32;
@@ -1066,14 +1095,17 @@ __global__ __launch_bounds__(256) void gemm_bf16x2_kernel(const uint16_t* __rest
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = m0 + i * 16 + 4 * (lane / 16) + e;
-        const float v = acc[i][j][e];
+        float v = acc[i][j][e];
         if (EPI == EPI_SWIGLU) {
           const float u = __shfl_xor(v, 8, kWave);
           if ((lane % 16) < kGuGroup && row < M && col < N)
             C[(size_t)row * ldc + (col / 16) * kGuGroup + (lane % 8)] = silu_mul(v, u);
         } else if (row < M && col < N) {
+          if (bias) v += bias[col];
           if (EPI == EPI_RESID)
             C[(size_t)row * ldc + col] += v;
+          else if (EPI == EPI_RELU)
+            C[(size_t)row * ldc + col] = fmaxf(v, 0.f);
           else
             C[(size_t)row * ldc + col] = v;
         }
@@ -1360,7 +1392,8 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint16_t* __restr
                                                           const uint16_t* __restrict__ W, int N,
                                                           float* __restrict__ C, int ldc,
                                                           uint16_t* __restrict__ Zhi,
-                                                          uint16_t* __restrict__ Zlo) {
+                                                          uint16_t* __restrict__ Zlo,
+                                                          const float* __restrict__ bias) {
   using namespace tg;
   __shared__ uint16_t sAh[2][BM * P], sAl[2][BM * P], sW[2][BN * P];
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
@@ -1475,10 +1508,13 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint16_t* __restr
             }
           }
         } else if (row < M) {
+          const float vb = bias ? v + bias[col] : v;
           if (EPI == EPI_RESID)
-            C[(size_t)row * ldc + col] += v;
+            C[(size_t)row * ldc + col] += vb;
+          else if (EPI == EPI_RELU)
+            C[(size_t)row * ldc + col] = fmaxf(vb, 0.f);
           else
-            C[(size_t)row * ldc + col] = v;
+            C[(size_t)row * ldc + col] = vb;
         }
       }
     }
@@ -1799,9 +1835,10 @@ bool attn_prefill_uses_split(const Dims& d) {
 }
 
 hipError_t launch_attn_prefill(const Dims& d, const float* qkv, int T, float* out, uint16_t* const kv[4],
-                               hipStream_t st, uint16_t* out_hi, uint16_t* out_lo) {
+                               hipStream_t st, uint16_t* out_hi, uint16_t* out_lo, bool causal) {
   const int group = d.NQ / d.NKV;
-  if ((out_hi != nullptr) != (out_lo != nullptr) || (out_hi && !attn_prefill_uses_split(d))) return hipErrorInvalidValue;
+  if ((out_hi != nullptr) != (out_lo != nullptr) || ((out_hi || !causal) && !attn_prefill_uses_split(d)))
+    return hipErrorInvalidValue;
   const float scale = 1.f / sqrtf((float)d.D);
   if (attn_prefill_uses_split(d)) {
     const int Tp = kv_split_pad(T);
@@ -1813,10 +1850,10 @@ hipError_t launch_attn_prefill(const Dims& d, const float* qkv, int T, float* ou
     const float qs = scale * 1.4426950408889634f;  // scores in base 2
     if (group == 2)
       attn_prefill_mfma_kernel<2><<<grid, 256, 0, st>>>(qkv, T, d.qkv(), kv[0], kv[1], kv[2], kv[3], Tp, out,
-                                                        d.NQ * d.D, qs, out_hi, out_lo);
+                                                        d.NQ * d.D, qs, out_hi, out_lo, causal ? 1 : 0);
     else
       attn_prefill_mfma_kernel<1><<<grid, 256, 0, st>>>(qkv, T, d.qkv(), kv[0], kv[1], kv[2], kv[3], Tp, out,
-                                                        d.NQ * d.D, qs, out_hi, out_lo);
+                                                        d.NQ * d.D, qs, out_hi, out_lo, causal ? 1 : 0);
     return hipGetLastError();
   }
 #define QDEC_PATTN_CASE(DD, GG)                                                                      \
@@ -1834,6 +1871,12 @@ hipError_t launch_attn_prefill(const Dims& d, const float* qkv, int T, float* ou
   QDEC_PATTN_CASE(32, 4)
   return hipErrorInvalidValue;
 #undef QDEC_PATTN_CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_ln_split(const float* X, int T, int K, const float* gain, const float* bias, float eps,
+                           uint16_t* hi, uint16_t* lo, hipStream_t st) {
+  ln_split_kernel<<<T, 256, 0, st>>>(X, K, gain, bias, eps, hi, lo);
   return hipGetLastError();
 }
 
@@ -1924,21 +1967,24 @@ hipError_t launch_gemm_swiglu_split(const uint16_t* A0, const uint16_t* A1, int 
                                     uint16_t* zhi, uint16_t* zlo, int ldz, hipStream_t st) {
   if (!gemm_tiled_fits(true, M, K, N)) return hipErrorInvalidValue;
   const dim3 grid(N / tg::BN, (M + tg::BM - 1) / tg::BM);
-  gemm_tiled_kernel<EPI_SWIGLU_SPLIT><<<grid, 256, 0, st>>>(A0, A1, M, K, W, N, nullptr, ldz, zhi, zlo);
+  gemm_tiled_kernel<EPI_SWIGLU_SPLIT><<<grid, 256, 0, st>>>(A0, A1, M, K, W, N, nullptr, ldz, zhi, zlo, nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(bool bf16, Epi epi, const void* A0, const void* A1, int M, int K, const void* W, int N,
-                       float* C, int ldc, hipStream_t st) {
+                       float* C, int ldc, hipStream_t st, const float* bias) {
+  if ((bias || epi == EPI_RELU) && (!bf16 || epi == EPI_SWIGLU)) return hipErrorInvalidValue;
   if (gemm_tiled_fits(bf16, M, K, N)) {
     const dim3 grid(N / tg::BN, (M + tg::BM - 1) / tg::BM);
     const uint16_t *hi = (const uint16_t*)A0, *lo = (const uint16_t*)A1, *w = (const uint16_t*)W;
     if (epi == EPI_STORE)
-      gemm_tiled_kernel<EPI_STORE><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc, nullptr, nullptr);
+      gemm_tiled_kernel<EPI_STORE><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc, nullptr, nullptr, bias);
     else if (epi == EPI_RESID)
-      gemm_tiled_kernel<EPI_RESID><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc, nullptr, nullptr);
+      gemm_tiled_kernel<EPI_RESID><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc, nullptr, nullptr, bias);
+    else if (epi == EPI_RELU)
+      gemm_tiled_kernel<EPI_RELU><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc, nullptr, nullptr, bias);
     else
-      gemm_tiled_kernel<EPI_SWIGLU><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc, nullptr, nullptr);
+      gemm_tiled_kernel<EPI_SWIGLU><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc, nullptr, nullptr, nullptr);
     return hipGetLastError();
   }
   if (bf16) {
@@ -1946,11 +1992,13 @@ hipError_t launch_gemm(bool bf16, Epi epi, const void* A0, const void* A1, int M
     dim3 grid((N + 63) / 64, (M + 63) / 64);
     const uint16_t *hi = (const uint16_t*)A0, *lo = (const uint16_t*)A1, *w = (const uint16_t*)W;
     if (epi == EPI_STORE)
-      gemm_bf16x2_kernel<EPI_STORE><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc);
+      gemm_bf16x2_kernel<EPI_STORE><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc, bias);
     else if (epi == EPI_RESID)
-      gemm_bf16x2_kernel<EPI_RESID><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc);
+      gemm_bf16x2_kernel<EPI_RESID><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc, bias);
+    else if (epi == EPI_RELU)
+      gemm_bf16x2_kernel<EPI_RELU><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc, bias);
     else
-      gemm_bf16x2_kernel<EPI_SWIGLU><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc);
+      gemm_bf16x2_kernel<EPI_SWIGLU><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc, nullptr);
   } else {
     dim3 grid((N + 31) / 32, (M + 31) / 32);
     const float *a = (const float*)A0, *w = (const float*)W;

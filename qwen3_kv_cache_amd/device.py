@@ -59,3 +59,47 @@ class Model:
             self.close()
         except Exception:
             pass
+
+
+class Adaptor:
+    """The audio adaptor on the GPU: ``bits`` maps the parameter names
+    ("linear1.w", "linear1.b", "linear2.w", "linear2.b", "blocks.{i}.<t>" for
+    t in qdec.ADAPTOR_BLOCK_TENSORS) to bf16 bit patterns (uint16)."""
+
+    def __init__(self, shape, bits: Dict[str, np.ndarray], ln_eps: float = 1e-12, device: str = "cuda:0"):
+        torch = _torch()
+        self.shape = shape
+        self.device = torch.device(device)
+        self.tensors = {name: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(self.device)
+                        for name, a in bits.items()}
+        blocks = [self.tensors[f"blocks.{i}.{t}"].data_ptr() for i in range(shape.n_block)
+                  for t in qdec.ADAPTOR_BLOCK_TENSORS]
+        self._block_arr = (qdec.ctypes.c_void_p * len(blocks))(*blocks)
+        w = qdec.qdec_adaptor_weights(self.tensors["linear1.w"].data_ptr(), self.tensors["linear1.b"].data_ptr(),
+                                      self.tensors["linear2.w"].data_ptr(), self.tensors["linear2.b"].data_ptr(),
+                                      qdec.ctypes.cast(self._block_arr, qdec.ctypes.POINTER(qdec.ctypes.c_void_p)))
+        self.cfg = qdec.qdec_adaptor_config(shape.enc_dim, shape.mid_dim, shape.dim, shape.ffn_dim, shape.n_block,
+                                            shape.n_head, ln_eps, qdec.QDEC_BF16)
+        self.stream = torch.cuda.current_stream(self.device).cuda_stream
+        self.handle = qdec.qdec_adaptor_create(self.cfg, w, self.stream)
+        torch.cuda.synchronize(self.device)
+
+    def run(self, frames, out=None):
+        """frames: fp32 device tensor [T, enc_dim]; returns [T, dim] fp32."""
+        torch = _torch()
+        T = frames.shape[0]
+        if out is None:
+            out = torch.empty((T, self.shape.dim), dtype=torch.float32, device=self.device)
+        qdec.qdec_adaptor_run(self.handle, frames.data_ptr(), T, out.data_ptr())
+        return out
+
+    def close(self) -> None:
+        if self.handle:
+            qdec.qdec_adaptor_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

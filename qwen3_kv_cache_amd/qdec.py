@@ -34,7 +34,8 @@ QDEC_PAGE = 16
 
 EXPORTS = ("qdec_create", "qdec_destroy", "qdec_state_create", "qdec_state_destroy", "qdec_prefill",
            "qdec_decode_step", "qdec_decode_step_dev", "qdec_decode_greedy", "qdec_decode_batch", "qdec_sample",
-           "qdec_clone_state", "qdec_state_pos", "qdec_last_error")
+           "qdec_clone_state", "qdec_state_pos", "qdec_last_error", "qdec_adaptor_create", "qdec_adaptor_run",
+           "qdec_adaptor_destroy")
 
 QDEC_SAMPLE_TOP_K_MAX = 128
 
@@ -55,6 +56,22 @@ class qdec_config(ctypes.Structure):
 class qdec_weights(ctypes.Structure):
     _fields_ = [("embed", ctypes.c_void_p), ("final_norm", ctypes.c_void_p),
                 ("layer", ctypes.POINTER(ctypes.c_void_p))]
+
+
+class qdec_adaptor_config(ctypes.Structure):
+    _fields_ = [("enc_dim", ctypes.c_int32), ("mid_dim", ctypes.c_int32), ("dim", ctypes.c_int32),
+                ("ffn_dim", ctypes.c_int32), ("n_block", ctypes.c_int32), ("n_head", ctypes.c_int32),
+                ("ln_eps", ctypes.c_float), ("weight_dtype", ctypes.c_int32)]
+
+
+class qdec_adaptor_weights(ctypes.Structure):
+    _fields_ = [("linear1_w", ctypes.c_void_p), ("linear1_b", ctypes.c_void_p), ("linear2_w", ctypes.c_void_p),
+                ("linear2_b", ctypes.c_void_p), ("block", ctypes.POINTER(ctypes.c_void_p))]
+
+
+# per-block tensor order of qdec_adaptor_weights.block
+ADAPTOR_BLOCK_TENSORS = ("norm1.g", "norm1.b", "q.w", "q.b", "k.w", "k.b", "v.w", "v.b", "o.w", "o.b",
+                         "norm2.g", "norm2.b", "fc1.w", "fc1.b", "fc2.w", "fc2.b")
 
 
 class qdec_sampling(ctypes.Structure):
@@ -98,6 +115,10 @@ def lib() -> ctypes.CDLL:
         "qdec_clone_state": (ctypes.c_int, [vp, ctypes.POINTER(vp)]),
         "qdec_state_pos": (i32, [vp]),
         "qdec_last_error": (ctypes.c_char_p, []),
+        "qdec_adaptor_create": (ctypes.c_int, [ctypes.POINTER(qdec_adaptor_config),
+                                               ctypes.POINTER(qdec_adaptor_weights), vp, ctypes.POINTER(vp)]),
+        "qdec_adaptor_run": (ctypes.c_int, [vp, vp, i32, vp]),
+        "qdec_adaptor_destroy": (None, [vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -187,6 +208,20 @@ def qdec_clone_state(src: int) -> int:
     out = ctypes.c_void_p()
     _check(lib().qdec_clone_state(_ptr(src), ctypes.byref(out)))
     return out.value
+
+
+def qdec_adaptor_create(cfg: qdec_adaptor_config, weights: qdec_adaptor_weights, stream: int = 0) -> int:
+    out = ctypes.c_void_p()
+    _check(lib().qdec_adaptor_create(ctypes.byref(cfg), ctypes.byref(weights), _ptr(stream), ctypes.byref(out)))
+    return out.value
+
+
+def qdec_adaptor_run(adaptor: int, frames_dev, n_frames: int, out_dev) -> None:
+    _check(lib().qdec_adaptor_run(_ptr(adaptor), _ptr(frames_dev), int(n_frames), _ptr(out_dev)))
+
+
+def qdec_adaptor_destroy(adaptor: int) -> None:
+    lib().qdec_adaptor_destroy(_ptr(adaptor))
 
 
 def qdec_state_pos(state: int) -> int:

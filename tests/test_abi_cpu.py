@@ -112,3 +112,32 @@ def test_batch_size_limit():
     with pytest.raises(qdec.QdecError) as e:
         qdec.qdec_decode_batch([1] * 17, [0] * 17)
     assert e.value.code == qdec.QDEC_E_INVALID
+
+
+def adaptor_cfg(**kw):
+    base = dict(enc_dim=512, mid_dim=2048, dim=1024, ffn_dim=256, n_block=2, n_head=8, ln_eps=1e-12,
+                weight_dtype=qdec.QDEC_BF16)
+    base.update(kw)
+    return qdec.qdec_adaptor_config(**base)
+
+
+ADAPTOR_BAD = [dict(weight_dtype=qdec.QDEC_F32), dict(enc_dim=100), dict(mid_dim=2000), dict(ffn_dim=200),
+               dict(dim=1000), dict(n_head=4), dict(n_block=0), dict(n_block=9), dict(ln_eps=0.0)]
+
+
+@pytest.mark.parametrize("kw", ADAPTOR_BAD, ids=[str(k) for k in ADAPTOR_BAD])
+def test_adaptor_create_rejects_bad_config(kw):
+    w = qdec.qdec_adaptor_weights(0, 0, 0, 0, None)
+    with pytest.raises(qdec.QdecError) as e:
+        qdec.qdec_adaptor_create(adaptor_cfg(**kw), w, 0)
+    assert e.value.code == qdec.QDEC_E_INVALID
+
+
+def test_adaptor_null_arguments():
+    with pytest.raises(qdec.QdecError) as e:
+        qdec.qdec_adaptor_create(adaptor_cfg(), qdec.qdec_adaptor_weights(0, 0, 0, 0, None), 0)
+    assert e.value.code == qdec.QDEC_E_INVALID  # weights incomplete
+    with pytest.raises(qdec.QdecError) as e:
+        qdec.qdec_adaptor_run(0, 0, 4, 0)
+    assert e.value.code == qdec.QDEC_E_INVALID
+    qdec.qdec_adaptor_destroy(0)  # NULL is a no-op
