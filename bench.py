@@ -13,8 +13,10 @@ before the timed region.
 The default run also reports, under "other_workloads", the rest of the
 metric with the same weights and fewer repetitions: B=16 batched decode of
 16 clones of a 512-token prefill (branch16), and the 1024- and 8192-token
-prompts (long, prefill8k); and under "sampling" the time of one sampling
-step (qdec_sample) over 1 and 16 rows of logits. --no-others skips them.
+prompts (long, prefill8k); under "sampling" the time of one sampling step
+(qdec_sample) over 1 and 16 rows of logits; and under "adaptor" the audio
+adaptor that makes the audio rows (qdec_adaptor_run) at 183 and 6000 encoder
+frames. --no-others skips them.
 
 Usage: python bench.py [--steps K] [--warmup W] [--workload short|long|prefill8k|branch16]
        python bench.py --copy-probe   (plain copy kernel for counter calibration)
@@ -93,6 +95,47 @@ def prefill_mfma(shape, T: int, ms: float, workload: str):
                                "mfma_flops_issued_per_prefill": float(kv["mfma_flops_issued_per_prefill"])}
         except (KeyError, ValueError):
             pass
+    return out
+
+
+def adaptor_flops(a, T: int) -> float:
+    """Useful FLOPs of the audio adaptor over T frames: 2 per weight per frame
+    for every linear, and 4 dim per (frame, frame) pair per block for QK and PV."""
+    lin = a.enc_dim * a.mid_dim + a.mid_dim * a.dim
+    blk = 4 * a.dim * a.dim + 2 * a.dim * a.ffn_dim
+    return 2.0 * T * lin + a.n_block * (2.0 * T * blk + 4.0 * T * T * a.dim)
+
+
+def measure_adaptor(frames=(183, 6000), reps=5):
+    """Time qdec_adaptor_run (seeded bf16 weights of the 512/2048/1024/256
+    adaptor, 2 blocks, 8 heads) on N(0,1) frames, inputs resident on the GPU."""
+    import torch
+
+    import synth
+    from qwen3_kv_cache_amd.device import Adaptor
+    shape = synth.AdaptorShape()
+    _, bits = synth.make_adaptor_weights(shape, 1)
+    a = Adaptor(shape, bits)
+    out = {}
+    try:
+        for T in frames:
+            x = torch.from_numpy(synth.encoder_frames(1, T, shape.enc_dim)).cuda()
+            y = torch.empty((T, shape.dim), dtype=torch.float32, device="cuda")
+            a.run(x, y)
+            torch.cuda.synchronize()
+            st = torch.cuda.current_stream()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            for _ in range(reps):
+                a.run(x, y)
+            e1.record(st)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            tf = adaptor_flops(shape, T) / (ms / 1e3) / 1e12
+            out[f"T{T}"] = {"ms": round(ms, 4), "frames_per_s": round(T / (ms / 1e3), 1),
+                            "useful_tflops": round(tf, 1), "frac_bf16_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+    finally:
+        a.close()
     return out
 
 
@@ -320,6 +363,7 @@ def main():
                             "prefill_mfma": prefill_mfma(wo.shape, wo.prompt_len, float(p_ms.mean()), name)}
         line["other_workloads"] = others
         line["sampling"] = measure_sampling(model, w.shape.vocab)
+        line["adaptor"] = measure_adaptor()
     if a.cpu_sample > 0:
         line["cpu_baseline"] = cpu_baseline(w, W, a.cpu_sample)
     model.close()

@@ -39,3 +39,15 @@ def test_prefill_flops_qwen3_shape():
     s = SimpleNamespace(hidden=1024, n_layer=28, head_dim=128, n_q_head=16, n_kv_head=8, ffn=3072, vocab=151936)
     assert bench.prefill_flops(s, 1) == 2 * 440_401_920 + 28 * 4 * 16 * 128 + 2 * 151936 * 1024
     assert abs(bench.prefill_flops(s, 8192) - 1.4913e13) / 1.4913e13 < 1e-4
+
+
+def test_adaptor_flops_counted():
+    a = SimpleNamespace(enc_dim=16, mid_dim=32, dim=24, ffn_dim=8, n_block=2)
+    for T in (1, 5):
+        macs = T * (16 * 32 + 32 * 24)
+        for _b in range(2):
+            macs += T * (4 * 24 * 24 + 24 * 8 + 8 * 24)
+            for _t in range(T):
+                for _u in range(T):
+                    macs += 2 * 24  # one q.k and one p.v per (head dim) summed over heads
+        assert bench.adaptor_flops(a, T) == 2 * macs
