@@ -20,6 +20,7 @@ frames. --no-others skips them.
 
 Usage: python bench.py [--steps K] [--warmup W] [--workload short|long|prefill8k|branch16]
        python bench.py --copy-probe   (plain copy kernel for counter calibration)
+       python bench.py --adaptor-only (the audio adaptor alone)
 """
 from __future__ import annotations
 
@@ -289,6 +290,8 @@ def main():
     ap.add_argument("--workload", default="short")
     ap.add_argument("--cpu-sample", type=int, default=24, help="oracle decode steps for the CPU baseline (0 = skip)")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--adaptor-only", action="store_true",
+                    help="time only the audio adaptor (qdec_adaptor_run) and print its JSON")
     ap.add_argument("--no-others", action="store_true",
                     help="skip the other workloads the default run also reports (B=16, long and 8k prompts)")
     ap.add_argument("--per-step", action="store_true",
@@ -300,6 +303,9 @@ def main():
         sys.exit(2)
     if a.copy_probe:
         copy_probe()
+        return
+    if a.adaptor_only:
+        print(json.dumps({"adaptor": measure_adaptor()}), flush=True)
         return
 
     import torch
