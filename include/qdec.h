@@ -280,7 +280,8 @@ int qdec_adaptor_create(const qdec_adaptor_config* cfg, const qdec_adaptor_weigh
  *   frames_dev: DEVICE fp32 [n_frames, enc_dim] (borrowed, not modified)
  *   n_frames:   >= 1
  *   out_dev:    DEVICE fp32 [n_frames, dim], receives the rows (it also
- *               holds the residual stream while the blocks run)
+ *               holds the residual stream while the blocks run, so it must
+ *               not overlap frames_dev: QDEC_E_INVALID)
  * Scratch for the largest n_frames seen so far is kept (allocated on first
  * use, QDEC_E_OOM if that fails). Work is enqueued on the adaptor's stream;
  * outputs are valid once it is synchronised. Errors: QDEC_E_INVALID for NULL

@@ -1283,6 +1283,11 @@ int qdec_adaptor_run(qdec_adaptor* a, const float* frames_dev, int32_t n_frames,
   const int T = n_frames, D = c.dim, F = c.ffn_dim;
   if (int e = check_dev(frames_dev, (size_t)T * c.enc_dim * sizeof(float), "frames_dev")) return e;
   if (int e = check_dev(out_dev, (size_t)T * D * sizeof(float), "out_dev")) return e;
+  {
+    const char *f0 = (const char*)frames_dev, *f1 = f0 + (size_t)T * c.enc_dim * sizeof(float);
+    const char *o0 = (const char*)out_dev, *o1 = o0 + (size_t)T * D * sizeof(float);
+    if (f0 < o1 && o0 < f1) return fail(QDEC_E_INVALID, "out_dev overlaps frames_dev");
+  }
   if (int e = ensure_adaptor(a, T)) return e;
   hipStream_t st = a->stream;
   uint16_t *A0 = a->A0, *A1 = a->A1;
