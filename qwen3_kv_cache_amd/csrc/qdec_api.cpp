@@ -544,9 +544,10 @@ int run_layers_rows(qdec_model* m, int T, float* X, float* QKV, float* Attn, flo
 // attn(l, hi, lo) writes the attention output rows into Attn (fp32), or, when
 // hi is set, as their bf16 hi/lo split into hi and lo (attn_split says whether
 // it can); both return a status.
-// With bf16 weights on the tiled GEMM, the attention and the SwiGLU GEMM write
-// the next GEMM's hi/lo operand themselves (the same bits the split pass would
-// make); Z's fp32 buffer then holds Z hi and Z lo.
+// With bf16 weights the attention writes the O projection's hi/lo operand
+// itself, and on the tiled GEMM so does the SwiGLU GEMM for the down
+// projection (the same bits the split pass would make); Z's fp32 buffer then
+// holds Z hi and Z lo.
 template <typename RopeFn, typename AttnFn>
 int run_layers(qdec_model* m, int T, float* X, float* QKV, float* Attn, float* Z, void* A0, void* A1, RopeFn rope,
                AttnFn attn, bool attn_split) {
@@ -557,7 +558,7 @@ int run_layers(qdec_model* m, int T, float* X, float* QKV, float* Attn, float* Z
     if (bf) return launch_rms_split(src, T, K, gain, d.eps, (uint16_t*)A0, (uint16_t*)A1, st);
     return launch_rms_apply(src, T, K, gain, d.eps, (float*)A0, st);
   };
-  const bool fuse_o = attn_split && gemm_tiled_fits(bf, T, d.NQ * d.D, d.H);
+  const bool fuse_o = attn_split && bf;  // both bf16 GEMMs read the same hi/lo operand
   const bool fuse_z = gemm_tiled_fits(bf, T, d.H, 2 * d.F) && gemm_tiled_fits(bf, T, d.F, d.H);
   uint16_t* zhi = (uint16_t*)Z;
   uint16_t* zlo = zhi + (size_t)T * d.F;

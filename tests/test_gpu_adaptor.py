@@ -95,3 +95,21 @@ def test_adaptor_rows_drive_the_decoder():
     print(f"[adaptor->decoder] logits max abs {err:.3g} cos {cos:.7f}", flush=True)
     assert err <= 5e-2 and cos >= 0.9999, (err, cos)
     assert tok == oracle.pick_token(ref)
+
+
+def test_adaptor_rejects_overlapping_output():
+    from qwen3_kv_cache_amd import qdec
+    from qwen3_kv_cache_amd.device import Adaptor
+    torch, dev = torch_dev()
+    _, bits = synth.make_adaptor_weights(SMALL, 27)
+    a = Adaptor(SMALL, bits)
+    try:
+        buf = torch.zeros((8, max(SMALL.enc_dim, SMALL.dim)), dtype=torch.float32, device=dev)
+        with pytest.raises(qdec.QdecError) as e:
+            qdec.qdec_adaptor_run(a.handle, buf.data_ptr(), 4, buf.data_ptr() + 4 * SMALL.enc_dim)
+        assert e.value.code == qdec.QDEC_E_INVALID
+        with pytest.raises(qdec.QdecError) as e:
+            qdec.qdec_adaptor_run(a.handle, buf.data_ptr(), 0, buf.data_ptr())
+        assert e.value.code == qdec.QDEC_E_INVALID
+    finally:
+        a.close()
