@@ -1000,6 +1000,51 @@ __global__ __launch_bounds__(256) void rms_split_kernel(const float* __restrict_
   }
 }
 
+// The same for rows of K % 4 == 0, K <= 4 * 256 * R: each thread keeps its
+// float4 chunks c = tid + 256 r in registers, so the row is read once, and
+// writes 8-byte hi / lo groups.
+template <int R>
+__global__ __launch_bounds__(256) void rms_split_vec_kernel(const float* __restrict__ X, int K,
+                                                             const float* __restrict__ gain, float eps,
+                                                             uint16_t* __restrict__ hi, uint16_t* __restrict__ lo) {
+  __shared__ float red[8];
+  const int t = blockIdx.x, nc = K / 4;
+  const float4* x = reinterpret_cast<const float4*>(X + (size_t)t * K);
+  float4 v[R];
+  float ss = 0.f;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int c = threadIdx.x + 256 * r;
+    v[r] = c < nc ? x[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+    ss = fmaf(v[r].x, v[r].x, fmaf(v[r].y, v[r].y, fmaf(v[r].z, v[r].z, fmaf(v[r].w, v[r].w, ss))));
+  }
+  float inv = 1.f;
+  if (gain) inv = 1.f / sqrtf(block_sum(ss, red) / (float)K + eps);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int c = threadIdx.x + 256 * r;
+    if (c < nc) {
+      float e[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+      if (gain) {
+        const float4 g = reinterpret_cast<const float4*>(gain)[c];
+        e[0] = e[0] * inv * g.x;
+        e[1] = e[1] * inv * g.y;
+        e[2] = e[2] * inv * g.z;
+        e[3] = e[3] * inv * g.w;
+      }
+      uint16_t h[4], l[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        h[k] = f32_to_bf16_rne(e[k]);
+        l[k] = f32_to_bf16_rne(e[k] - bf16_to_f32(h[k]));
+      }
+      const size_t o = (size_t)t * K + 4 * c;
+      *reinterpret_cast<uint2*>(hi + o) = make_uint2(h[0] | ((unsigned)h[1] << 16), h[2] | ((unsigned)h[3] << 16));
+      *reinterpret_cast<uint2*>(lo + o) = make_uint2(l[0] | ((unsigned)l[1] << 16), l[2] | ((unsigned)l[3] << 16));
+    }
+  }
+}
+
 // LayerNorm of each row (mean and population variance over K, gain and bias)
 // written as the next GEMM's bf16 hi/lo operand. Block = one row.
 __global__ __launch_bounds__(256) void ln_split_kernel(const float* __restrict__ X, int K,
@@ -1882,7 +1927,12 @@ hipError_t launch_ln_split(const float* X, int T, int K, const float* gain, cons
 
 hipError_t launch_rms_split(const float* X, int T, int K, const float* gain, float eps, uint16_t* hi,
                             uint16_t* lo, hipStream_t st) {
-  rms_split_kernel<<<T, 256, 0, st>>>(X, K, gain, eps, hi, lo);
+  if (K % 4 == 0 && K <= 1024)
+    rms_split_vec_kernel<1><<<T, 256, 0, st>>>(X, K, gain, eps, hi, lo);
+  else if (K % 4 == 0 && K <= 4096)
+    rms_split_vec_kernel<4><<<T, 256, 0, st>>>(X, K, gain, eps, hi, lo);
+  else
+    rms_split_kernel<<<T, 256, 0, st>>>(X, K, gain, eps, hi, lo);
   return hipGetLastError();
 }
 
