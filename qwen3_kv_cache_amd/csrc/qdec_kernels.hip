@@ -307,6 +307,68 @@ __device__ __forceinline__ void qk_rope_row(float* __restrict__ qrow, int head, 
   }
 }
 
+// Several heads per wave for head_dim D (32, 64 or 128): LPH = D / 8 lanes
+// per head, lane j of a head owning the float4 groups [4 j, 4 j + 4) and
+// [D/2 + 4 j, D/2 + 4 j + 4) (rotate-half partners), so one wave covers
+// 64 / LPH heads of a row with 16-byte accesses. Same arithmetic per element
+// as qk_rope_row; the sum of squares is reduced over the head's LPH lanes.
+template <int D>
+__global__ __launch_bounds__(256) void qk_rope_append_vec_kernel(float* __restrict__ qkv, int ld, int pos0, int NQ,
+                                                                  int NKV, int L, float eps,
+                                                                  const float* __restrict__ q_norm,
+                                                                  const float* __restrict__ k_norm,
+                                                                  const float* __restrict__ rcos,
+                                                                  const float* __restrict__ rsin,
+                                                                  const int64_t* __restrict__ page_table, int layer) {
+  constexpr int HALF = D / 2, LPH = D / 8, HPW = kWave / LPH;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int row = blockIdx.y, j = lane % LPH;
+  const int head = (blockIdx.x * 4 + wave) * HPW + lane / LPH;
+  const bool live = head < NQ + NKV;
+  const int hd = live ? head : NQ + NKV - 1;  // idle lanes mirror a real head, store nothing
+  const int pos = pos0 + row;
+  const bool is_q = hd < NQ;
+  float* rowp = qkv + (size_t)row * ld;
+  float* vec = rowp + (size_t)hd * D;
+  const float* g = is_q ? q_norm : k_norm;
+  float4 a = *reinterpret_cast<const float4*>(vec + 4 * j);
+  float4 b = *reinterpret_cast<const float4*>(vec + HALF + 4 * j);
+  float ss = a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w + b.x * b.x + b.y * b.y + b.z * b.z + b.w * b.w;
+#pragma unroll
+  for (int o = 1; o < LPH; o <<= 1) ss += __shfl_xor(ss, o, kWave);
+  const float inv = 1.f / sqrtf(ss / (float)D + eps);
+  const float4 ga = *reinterpret_cast<const float4*>(g + 4 * j);
+  const float4 gb = *reinterpret_cast<const float4*>(g + HALF + 4 * j);
+  const float4 c = *reinterpret_cast<const float4*>(rcos + (size_t)pos * HALF + 4 * j);
+  const float4 sn = *reinterpret_cast<const float4*>(rsin + (size_t)pos * HALF + 4 * j);
+  float av[4] = {a.x * inv * ga.x, a.y * inv * ga.y, a.z * inv * ga.z, a.w * inv * ga.w};
+  float bv[4] = {b.x * inv * gb.x, b.y * inv * gb.y, b.z * inv * gb.z, b.w * inv * gb.w};
+  const float cv[4] = {c.x, c.y, c.z, c.w}, sv[4] = {sn.x, sn.y, sn.z, sn.w};
+  float ra[4], rb[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    ra[e] = av[e] * cv[e] - bv[e] * sv[e];
+    rb[e] = bv[e] * cv[e] + av[e] * sv[e];
+  }
+  if (!live) return;
+  const float4 ra4 = make_float4(ra[0], ra[1], ra[2], ra[3]), rb4 = make_float4(rb[0], rb[1], rb[2], rb[3]);
+  *reinterpret_cast<float4*>(vec + 4 * j) = ra4;
+  *reinterpret_cast<float4*>(vec + HALF + 4 * j) = rb4;
+  if (!is_q) {
+    const int kh = hd - NQ;
+    Dims d{L, 0, NQ, NKV, D, 0, 0, 0.f};
+    float* page = reinterpret_cast<float*>(page_table[pos / kPage]);
+    const int slot = pos % kPage;
+    float* kd = page + page_offset(d, layer, 0, kh, slot);
+    float* vd = page + page_offset(d, layer, 1, kh, slot);
+    const float* vs = rowp + (size_t)(NQ + NKV + kh) * D;
+    *reinterpret_cast<float4*>(kd + 4 * j) = ra4;
+    *reinterpret_cast<float4*>(kd + HALF + 4 * j) = rb4;
+    *reinterpret_cast<float4*>(vd + 4 * j) = *reinterpret_cast<const float4*>(vs + 4 * j);
+    *reinterpret_cast<float4*>(vd + HALF + 4 * j) = *reinterpret_cast<const float4*>(vs + HALF + 4 * j);
+  }
+}
+
 // Prompt rows: row t sits at position pos0 + t of one state.
 __global__ __launch_bounds__(64) void qk_rope_append_kernel(float* __restrict__ qkv, int ld, int pos0, int NQ,
                                                              int NKV, int D, int L, float eps,
@@ -1841,6 +1903,21 @@ hipError_t launch_reset_keys(unsigned long long* key, int n, hipStream_t st) {
 hipError_t launch_qk_rope_append(const Dims& d, float* qkv, int T, int pos0, const float* q_norm,
                                  const float* k_norm, const float* rope_cos, const float* rope_sin,
                                  const int64_t* page_table, int layer, hipStream_t st) {
+  if (d.D == 128 || d.D == 64 || d.D == 32) {
+    const int hpb = 4 * (kWave / (d.D / 8));  // heads per 256-thread block
+    const dim3 grid((d.NQ + d.NKV + hpb - 1) / hpb, T);
+#define QDEC_ROPE_VEC(DD)                                                                                 \
+  qk_rope_append_vec_kernel<DD><<<grid, 256, 0, st>>>(qkv, d.qkv(), pos0, d.NQ, d.NKV, d.L, d.eps, q_norm, k_norm, \
+                                                      rope_cos, rope_sin, page_table, layer)
+    if (d.D == 128)
+      QDEC_ROPE_VEC(128);
+    else if (d.D == 64)
+      QDEC_ROPE_VEC(64);
+    else
+      QDEC_ROPE_VEC(32);
+#undef QDEC_ROPE_VEC
+    return hipGetLastError();
+  }
   dim3 grid(d.NQ + d.NKV, T);
   qk_rope_append_kernel<<<grid, 64, 0, st>>>(qkv, d.qkv(), pos0, d.NQ, d.NKV, d.D, d.L, d.eps, q_norm, k_norm,
                                              rope_cos, rope_sin, page_table, layer);
