@@ -53,6 +53,35 @@ def decode_bytes(shape, ctx_lens) -> float:
     return float(np.mean([w + L * kv_row * p + L * kv_row for p in ctx_lens]))
 
 
+def batch_decode_bytes(shape, prefix: int, B: int, s: int):
+    """Algorithmic HBM bytes of batched decode step s (0-based) of B branches
+    cloned from a prefix of `prefix` positions: (unique, per sequence).
+    Unique: every weight once, the shared prefix K/V once, each branch's own
+    s + 1 positions, the B new K/V rows and embedding rows. Per sequence:
+    each branch reading the whole history, as B separate decodes would."""
+    H, L = shape.hidden, shape.n_layer
+    kv_row = 2 * shape.n_kv_head * shape.head_dim * 4
+    w = decode_bytes(shape, [0]) - L * kv_row - H * 2  # weights, norms and head only
+    unique = w + L * kv_row * (prefix + B * (s + 1)) + B * L * kv_row + B * H * 2
+    per_seq = w + B * L * kv_row * (prefix + s + 1) + B * L * kv_row + B * H * 2
+    return float(unique), float(per_seq)
+
+
+def decode_roofline(shape, wl, dec_ms_mean: float):
+    """Achieved GB/s of a workload's decode from the byte model above."""
+    n, B = wl.n_decode, wl.n_branch
+    t_step = dec_ms_mean / 1e3 / n
+    if B == 1:
+        b = decode_bytes(shape, [wl.prompt_len + s + 1 for s in range(n)])
+        return {"bytes_per_step": round(b), "achieved": round(b / t_step / 1e9, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(b / t_step / 1e9 / HBM_PEAK_GBS, 4)}
+    u = np.mean([batch_decode_bytes(shape, wl.prompt_len, B, s)[0] for s in range(n)])
+    q = np.mean([batch_decode_bytes(shape, wl.prompt_len, B, s)[1] for s in range(n)])
+    return {"bytes_per_step_unique": round(u), "bytes_per_step_per_sequence": round(q),
+            "achieved_unique": round(u / t_step / 1e9, 1), "achieved_per_sequence": round(q / t_step / 1e9, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac_unique": round(u / t_step / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def prefill_flops(shape, T: int) -> float:
     """Useful FLOPs of a T-token prefill, each counted once: 2 per weight per
     row for the layer projections, 4 D per (query head, attended key) pair for
@@ -208,23 +237,27 @@ def measure(w, model, steps, warmup, per_step=False):
     streams = np.stack([synth.branch_stream(w, b) for b in range(B)]) if B > 1 else None
     total = warmup + steps
     states = [qdec.qdec_state_create(model.handle, w.max_ctx) for _ in range(total)]
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(total)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(total)]
     torch.cuda.synchronize()
 
     def one_step(i):
         st = states[i]
-        e0, e1, e2 = ev[i]
+        e0, e1, e1d, e2 = ev[i]
         e0.record()
         qdec.qdec_prefill(st, ids, len(ids), audio_d.data_ptr(), a0, len(audio), None, toks[0].data_ptr())
         e1.record()
         if B == 1:
+            e1d.record()
             if per_step:
                 for s in range(n):
                     qdec.qdec_decode_step_dev(st, toks[s].data_ptr(), w.prompt_len + s, None, toks[s + 1].data_ptr())
             else:
                 qdec.qdec_decode_greedy(st, toks[0].data_ptr(), w.prompt_len, n, None, toks[1].data_ptr())
         else:
+            # the clones (host work and a page-table upload each) stay outside
+            # the timed decode
             br = [qdec.qdec_clone_state(st) for _ in range(B)]
+            e1d.record()
             for s in range(n):
                 qdec.qdec_decode_batch(br, streams[:, s], None, toks[s + 1].data_ptr())
             e2.record()
@@ -243,7 +276,7 @@ def measure(w, model, steps, warmup, per_step=False):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     pre_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(warmup, total)])
-    dec_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(warmup, total)])
+    dec_ms = np.array([ev[i][2].elapsed_time(ev[i][3]) for i in range(warmup, total)])
     for st in states:
         qdec.qdec_state_destroy(st)
     return pre_ms, dec_ms, wall
@@ -366,7 +399,8 @@ def main():
                             "batch": wo.n_branch, "prompt_len": wo.prompt_len, "decode_steps": wo.n_decode,
                             "prefill_tok_s": round(wo.prompt_len * len(p_ms) / (p_ms.sum() / 1e3), 1),
                             "prefill_ms": round(float(p_ms.mean()), 3),
-                            "prefill_mfma": prefill_mfma(wo.shape, wo.prompt_len, float(p_ms.mean()), name)}
+                            "prefill_mfma": prefill_mfma(wo.shape, wo.prompt_len, float(p_ms.mean()), name),
+                            "decode_roofline": decode_roofline(wo.shape, wo, float(d_ms.mean()))}
         line["other_workloads"] = others
         line["sampling"] = measure_sampling(model, w.shape.vocab)
         line["adaptor"] = measure_adaptor()

@@ -51,3 +51,18 @@ def test_adaptor_flops_counted():
                 for _u in range(T):
                     macs += 2 * 24  # one q.k and one p.v per (head dim) summed over heads
         assert bench.adaptor_flops(a, T) == 2 * macs
+
+
+def test_batch_decode_bytes_survey_figures():
+    # the step byte model quoted for 16 clones of a 512-token prefix:
+    # about 1.31e9 unique bytes at the first step and 1.78e9 at step 128
+    s = SimpleNamespace(hidden=1024, n_layer=28, head_dim=128, n_q_head=16, n_kv_head=8, ffn=3072, vocab=151936)
+    u0, q0 = bench.batch_decode_bytes(s, 512, 16, 0)
+    u128, q128 = bench.batch_decode_bytes(s, 512, 16, 128)
+    assert abs(u0 / 1.31e9 - 1) < 0.01 and abs(u128 / 1.78e9 - 1) < 0.01
+    # per sequence every branch re-reads the prefix: 3.07e9 .. 3.54e9 over the run
+    assert abs(q0 / 3.07e9 - 1) < 0.01 and abs(q128 / 3.54e9 - 1) < 0.01
+    # one branch: unique == per sequence == the single-sequence model at the same context
+    u, q = bench.batch_decode_bytes(s, 512, 1, 10)
+    assert u == q
+    assert abs(u - bench.decode_bytes(s, [523])) < 1.0
