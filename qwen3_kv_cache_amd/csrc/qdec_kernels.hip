@@ -838,7 +838,11 @@ constexpr int KB = KT / 16;     // 16-key blocks per tile
 constexpr int KH = KT / 32;     // 32-key groups per tile
 }  // namespace fa
 
-template <int GROUP>
+// GROUP query heads share each KV head; QS query blocks of 16 per wave (GROUP
+// x QS "virtual heads" v: head g GROUP + v % GROUP, queries 16 (w QS + v / GROUP)
+// + [0, 16) of the block). With one query head per KV head, two query blocks
+// per wave let every K/V fragment read from LDS feed twice the MFMAs.
+template <int GROUP, int QS>
 __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* __restrict__ qkv, int T, int ld,
                                                                  const uint16_t* __restrict__ khs,
                                                                  const uint16_t* __restrict__ kls,
@@ -848,6 +852,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
                                                                  uint16_t* __restrict__ ohi,
                                                                  uint16_t* __restrict__ olo, int causal) {
   using namespace fa;
+  constexpr int VH = GROUP * QS, QTB = 64 * QS;  // virtual heads per wave, queries per block
   __shared__ __bf16 Kh[KT * KP], Kl[KT * KP];
   __shared__ __bf16 Vh[D * VP], Vl[D * VP];
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
@@ -865,15 +870,16 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
     qb = j % gridDim.x;
   }
   // heavier (later) query tiles first
-  const int q0 = (gridDim.x - 1 - qb) * QT;
-  const int qp = q0 + 16 * w + c16;           // this lane's query position
-  const int qrow = min(qp, T - 1);
+  const int q0 = (gridDim.x - 1 - qb) * QTB;
+  int qpv[VH];  // this lane's query position per virtual head
+#pragma unroll
+  for (int v = 0; v < VH; ++v) qpv[v] = q0 + 16 * (w * QS + v / GROUP) + c16;
 
   // Q^T operands (B of S^T = K Q^T): lane supplies Q[query c16][32 s + 8 gq + i]
-  bf16x8_t qh[GROUP][4], ql[GROUP][4];
+  bf16x8_t qh[VH][4], ql[VH][4];
 #pragma unroll
-  for (int hh = 0; hh < GROUP; ++hh) {
-    const float* qsrc = qkv + (size_t)qrow * ld + (size_t)(g * GROUP + hh) * D + 8 * gq;
+  for (int hh = 0; hh < VH; ++hh) {
+    const float* qsrc = qkv + (size_t)min(qpv[hh], T - 1) * ld + (size_t)(g * GROUP + hh % GROUP) * D + 8 * gq;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const float4 a = *reinterpret_cast<const float4*>(qsrc + 32 * st);
@@ -889,10 +895,10 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
     }
   }
 
-  float m[GROUP], lsum[GROUP];
-  f32x4_t acc[GROUP][D / 16];
+  float m[VH], lsum[VH];
+  f32x4_t acc[VH][D / 16];
 #pragma unroll
-  for (int hh = 0; hh < GROUP; ++hh) {
+  for (int hh = 0; hh < VH; ++hh) {
     m[hh] = -INFINITY;
     lsum[hh] = 0.f;
 #pragma unroll
@@ -904,8 +910,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
   const uint16_t* vh_g = vths + (size_t)g * D * Tp;
   const uint16_t* vl_g = vtls + (size_t)g * D * Tp;
   // causal: keys up to the block's last query; otherwise every key
-  const int last_key = causal ? min(T, q0 + QT) - 1 : T - 1;
-  const int qlim = causal ? qp : T - 1;  // this lane's last visible key
+  const int last_key = causal ? min(T, q0 + QTB) - 1 : T - 1;
   for (int k0 = 0; k0 <= last_key; k0 += KT) {
     __syncthreads();
     // copies of the converted tiles: K rows of 16-byte chunks (key c / 16,
@@ -927,9 +932,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
     __syncthreads();
 
     // S^T tile: KB key blocks of 16 x this wave's 16 queries, per head
-    f32x4_t sc[GROUP][KB];
+    f32x4_t sc[VH][KB];
 #pragma unroll
-    for (int hh = 0; hh < GROUP; ++hh)
+    for (int hh = 0; hh < VH; ++hh)
 #pragma unroll
       for (int j = 0; j < KB; ++j) sc[hh][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -940,7 +945,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
         const bf16x8_t kh = *reinterpret_cast<const bf16x8_t*>(&Kh[off]);
         const bf16x8_t kl = *reinterpret_cast<const bf16x8_t*>(&Kl[off]);
 #pragma unroll
-        for (int hh = 0; hh < GROUP; ++hh) {
+        for (int hh = 0; hh < VH; ++hh) {
           sc[hh][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qh[hh][st], sc[hh][j], 0, 0, 0);
           sc[hh][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, qh[hh][st], sc[hh][j], 0, 0, 0);
           sc[hh][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, ql[hh][st], sc[hh][j], 0, 0, 0);
@@ -948,9 +953,10 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
       }
 
     // online softmax per head; P^T operands per 32-key group
-    bf16x8_t ph[GROUP][KH], pl[GROUP][KH];
+    bf16x8_t ph[VH][KH], pl[VH][KH];
 #pragma unroll
-    for (int hh = 0; hh < GROUP; ++hh) {
+    for (int hh = 0; hh < VH; ++hh) {
+      const int qlim = causal ? qpv[hh] : T - 1;  // this lane's last visible key
       float mx = m[hh];
 #pragma unroll
       for (int j = 0; j < KB; ++j)
@@ -1000,7 +1006,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
         const bf16x8_t vh = *reinterpret_cast<const bf16x8_t*>(&Vh[off]);
         const bf16x8_t vl = *reinterpret_cast<const bf16x8_t*>(&Vl[off]);
 #pragma unroll
-        for (int hh = 0; hh < GROUP; ++hh) {
+        for (int hh = 0; hh < VH; ++hh) {
           acc[hh][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vh, ph[hh][c], acc[hh][b], 0, 0, 0);
           acc[hh][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vl, ph[hh][c], acc[hh][b], 0, 0, 0);
           acc[hh][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vh, pl[hh][c], acc[hh][b], 0, 0, 0);
@@ -1008,11 +1014,11 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
       }
   }
 
-  if (qp < T) {
 #pragma unroll
-    for (int hh = 0; hh < GROUP; ++hh) {
+  for (int hh = 0; hh < VH; ++hh) {
+    if (qpv[hh] < T) {
       const float il = 1.f / lsum[hh];
-      const size_t o = (size_t)qp * ldo + (size_t)(g * GROUP + hh) * D + 4 * gq;
+      const size_t o = (size_t)qpv[hh] * ldo + (size_t)(g * GROUP + hh % GROUP) * D + 4 * gq;
 #pragma unroll
       for (int b = 0; b < D / 16; ++b) {
         const float v[4] = {acc[hh][b][0] * il, acc[hh][b][1] * il, acc[hh][b][2] * il, acc[hh][b][3] * il};
@@ -1968,13 +1974,21 @@ hipError_t launch_attn_prefill(const Dims& d, const float* qkv, int T, float* ou
                                                           Tp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    dim3 grid((T + fa::QT - 1) / fa::QT, d.NKV);
     const float qs = scale * 1.4426950408889634f;  // scores in base 2
-    if (group == 2)
-      attn_prefill_mfma_kernel<2><<<grid, 256, 0, st>>>(qkv, T, d.qkv(), kv[0], kv[1], kv[2], kv[3], Tp, out,
+    // one query head per KV head and a long input: two 16-query blocks per
+    // wave, 128 per block (6000 frames of the adaptor: 2.11 -> 1.99 ms; below
+    // 1024 positions the halved block count costs more than it saves)
+    const bool two = group == 1 && T >= 1024;
+    const int qtb = two ? 2 * fa::QT : fa::QT;
+    dim3 grid((T + qtb - 1) / qtb, d.NKV);
+    if (group == 1 && !two)
+      attn_prefill_mfma_kernel<1, 1><<<grid, 256, 0, st>>>(qkv, T, d.qkv(), kv[0], kv[1], kv[2], kv[3], Tp, out,
+                                                           d.NQ * d.D, qs, out_hi, out_lo, causal ? 1 : 0);
+    else if (group == 2)
+      attn_prefill_mfma_kernel<2, 1><<<grid, 256, 0, st>>>(qkv, T, d.qkv(), kv[0], kv[1], kv[2], kv[3], Tp, out,
                                                         d.NQ * d.D, qs, out_hi, out_lo, causal ? 1 : 0);
     else
-      attn_prefill_mfma_kernel<1><<<grid, 256, 0, st>>>(qkv, T, d.qkv(), kv[0], kv[1], kv[2], kv[3], Tp, out,
+      attn_prefill_mfma_kernel<1, 2><<<grid, 256, 0, st>>>(qkv, T, d.qkv(), kv[0], kv[1], kv[2], kv[3], Tp, out,
                                                         d.NQ * d.D, qs, out_hi, out_lo, causal ? 1 : 0);
     return hipGetLastError();
   }
