@@ -80,6 +80,9 @@ WORKLOADS: Dict[str, Workload] = {
     "prefill8k": Workload("prefill8k", QWEN3_0P6B, 2, 5, 8192, 8, 6000, 64),
     # 0.6B: 3001-token prompt (ragged against every tile size), 2000 audio rows, 16 steps
     "ragged3k": Workload("ragged3k", QWEN3_0P6B, 2, 6, 3001, 8, 2000, 16),
+    # tiny fp32 decoder at the decode kernel's position limit: a 16381-token
+    # prompt, then greedy steps at positions 16381, 16382 and 16383 (the last)
+    "tiny_maxpos": Workload("tiny_maxpos", TINY, 1, 7, 16381, 8, 8, 3),
 }
 
 

@@ -171,3 +171,48 @@ def test_decode_batch_rows(name):
     L, A = logits.cpu().numpy(), amax.cpu().numpy()
     for b in range(B):
         check_steps(L[:, b], A[:, b], ref[:, b], fp32=not shape.bf16, label=f"{name} row {b}")
+
+
+def test_decode_at_the_position_limit():
+    """The tiny fp32 decoder prefilled with 16381 tokens, then teacher-forced
+    decode steps at positions 16381, 16382 and 16383 (the last one the decode
+    kernel's in-LDS page table covers, QDEC_DECODE_MAX_POS - 1), against the
+    oracle's stored logits (tests/golden/teacher_tiny_maxpos.npz, written by
+    make_teacher.py; every vocabulary entry is stored): fp32 bar 1e-4 and the
+    same argmax. The next position is rejected with QDEC_E_CAPACITY."""
+    import os
+
+    from qwen3_kv_cache_amd import qdec
+    from .gpu_harness import torch_dev
+    w = synth.WORKLOADS["tiny_maxpos"]
+    z = np.load(os.path.join(os.path.dirname(__file__), "golden", "teacher_tiny_maxpos.npz"))
+    assert w.prompt_len + w.n_decode == 16384  # QDEC_DECODE_MAX_POS in include/qdec.h
+    V = w.shape.vocab
+    assert np.array_equal(z["sample_idx"], np.arange(V))
+    W = synth.make_weights(w.shape, w.weight_seed)
+    ids, audio, a0 = synth.make_prompt(w)
+    T = len(ids)
+    torch, dev = torch_dev()
+    m = device_model(w.shape, W)
+    st = qdec.qdec_state_create(m.handle, w.max_ctx)
+    try:
+        lg = torch.full((w.n_decode + 1, V), float("nan"), dtype=torch.float32, device=dev)
+        am = torch.full((w.n_decode + 1,), -1, dtype=torch.int32, device=dev)
+        audio_d = torch.from_numpy(audio).to(dev)
+        print(f"[maxpos] prefill {T} tokens", flush=True)
+        qdec.qdec_prefill(st, ids, T, audio_d.data_ptr(), a0, len(audio), lg[0].data_ptr(), am[0].data_ptr())
+        for s in range(w.n_decode):
+            qdec.qdec_decode_step(st, int(z["tokens"][s]), T + s, lg[s + 1].data_ptr(), am[s + 1].data_ptr())
+        with pytest.raises(qdec.QdecError) as e:
+            qdec.qdec_decode_step(st, int(z["tokens"][w.n_decode]), T + w.n_decode)
+        assert e.value.code == qdec.QDEC_E_CAPACITY
+        torch.cuda.synchronize()
+        got = lg.cpu().numpy()
+        amax = am.cpu().numpy()
+    finally:
+        qdec.qdec_state_destroy(st)
+        m.close()
+    err = float(np.max(np.abs(got - z["sample_vals"])))
+    print(f"[maxpos] positions {T}..{T + w.n_decode - 1}: max abs {err:.3g}", flush=True)
+    assert err <= 1e-4, err
+    assert list(amax) == list(z["tokens"])
