@@ -284,8 +284,9 @@ int qdec_adaptor_create(const qdec_adaptor_config* cfg, const qdec_adaptor_weigh
  *               not overlap frames_dev: QDEC_E_INVALID)
  * Scratch for the largest n_frames seen so far is kept (allocated on first
  * use, QDEC_E_OOM if that fails). Work is enqueued on the adaptor's stream;
- * outputs are valid once it is synchronised. Errors: QDEC_E_INVALID for NULL
- * or undersized buffers, QDEC_E_DEVICE for HIP errors. */
+ * outputs are valid once it is synchronised. Calls on one adaptor are not
+ * thread-safe (they share its scratch). Errors: QDEC_E_INVALID for NULL or
+ * undersized buffers, QDEC_E_DEVICE for HIP errors. */
 int qdec_adaptor_run(qdec_adaptor* a, const float* frames_dev, int32_t n_frames, float* out_dev);
 
 /* Free the adaptor (synchronises its stream). NULL is a no-op. */
