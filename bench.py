@@ -315,6 +315,122 @@ def measure_sampling(model, V, calls=50):
     return out
 
 
+# Stamp slots of the diagnostic decode build (first decode step of a launch,
+# first exchange thread of each workgroup): slot 1 + 10 l + i is boundary i of
+# layer l, 1 + 10 L is the final residual, 300-302 close the LM head and the
+# argmax exchange.
+TRACE_PHASES = ("A  input norm + QKV dot", "E1 q/k/v rows exchange (group)", "B  QK-norm, RoPE, attention",
+                "M  attention merge (+ split exchange)", "C  O dot + publish", "E3 O partials exchange (chip)",
+                "D  post norm + gate/up dot + SwiGLU", "E4 z exchange (group)", "E  down dot + publish",
+                "E5 down partials exchange (chip)")
+
+
+def decode_trace(w, model, n_steps: int = 8):
+    """Per-phase time of one decode step from the diagnostic library's
+    realtime-counter stamps (100 MHz): median and 90th percentile over
+    workgroups and layers 1 .. L-2 of each phase, plus the LM head."""
+    import ctypes
+
+    import torch
+
+    import synth
+    from qwen3_kv_cache_amd import qdec
+
+    L = w.shape.n_layer
+    dev = torch.device("cuda:0")
+    ids, audio, a0 = synth.make_prompt(w)
+    audio_d = torch.from_numpy(audio).to(dev)
+    toks = torch.zeros(n_steps + 1, dtype=torch.int32, device=dev)
+    for rep in range(2):  # the second launch is the one read back
+        st = qdec.qdec_state_create(model.handle, w.max_ctx)
+        qdec.qdec_prefill(st, ids, len(ids), audio_d.data_ptr(), a0, len(audio), None, toks[0].data_ptr())
+        qdec.qdec_decode_greedy(st, toks[0].data_ptr(), w.prompt_len, n_steps, None, toks[1].data_ptr())
+        torch.cuda.synchronize()
+        qdec.qdec_state_destroy(st)
+    nb = torch.cuda.get_device_properties(0).multi_processor_count
+    n = nb * 512
+    buf = (ctypes.c_ulonglong * n)()
+    if qdec.lib().qdec_debug_trace(buf, n) != 0:
+        raise RuntimeError("qdec_debug_trace failed")
+    t = np.frombuffer(buf, dtype=np.uint64).reshape(nb, 512).astype(np.int64)
+    us = 0.01  # one realtime tick = 10 ns
+    rows = {}
+    for i, name in enumerate(TRACE_PHASES):
+        d = []
+        for l in range(1, L - 1):
+            a = t[:, 1 + 10 * l + i]
+            b = t[:, 1 + 10 * (l + 1)] if i == 9 else t[:, 1 + 10 * l + i + 1]
+            d.append((b - a) * us)
+        d = np.concatenate(d)
+        rows[name] = {"median_us": round(float(np.median(d)), 3), "p90_us": round(float(np.percentile(d, 90)), 3)}
+    layer = np.concatenate([(t[:, 1 + 10 * (l + 1)] - t[:, 1 + 10 * l]) * us for l in range(1, L - 1)])
+    head = (t[:, 300] - t[:, 1 + 10 * L]) * us
+    key = (t[:, 302] - t[:, 300]) * us
+    step = (t[:, 302] - t[:, 0]) * us
+    # Exchanges: the realtime counter is chip-wide, so a consumer's completion
+    # can be set against its producers' publish stamps: "skew" is how long the
+    # consumer waited for the last producer, "latency" the time from the last
+    # publish to the consumer seeing every word.
+    grp = np.arange(nb) % 8
+
+    def xch(pub_i, done_i, nxt, local):
+        lat, skew = [], []
+        for l in range(1, L - 1):
+            pub = t[:, 1 + 10 * l + pub_i]
+            done = t[:, 1 + 10 * (l + nxt) + done_i]
+            last = np.array([pub[grp == g].max() for g in range(8)])[grp] if local else np.full(nb, pub.max())
+            lat.append((done - last) * us)
+            skew.append((last - pub) * us)
+        lat, skew = np.concatenate(lat), np.concatenate(skew)
+        return {"latency_after_last_publish_us": round(float(np.median(lat)), 3),
+                "wait_for_last_producer_us": round(float(np.median(skew)), 3)}
+    exchanges = {"E3 O partials (chip)": xch(5, 6, 0, False), "E4 z (group)": xch(7, 8, 0, True),
+                 "E5 down partials (chip)": xch(9, 0, 1, False)}
+    # inside the FFN phases (layers 1 .. 7): D = input norm | bars + dot | SwiGLU + publish,
+    # E = bars + dot | publish + attention prefetch
+    sub = {}
+    for name, a_i, b_i in (("D norm_input", 6, 401), ("D bars+dot", 401, 402), ("D swiglu+publish", 402, 7),
+                           ("E bars+dot", 8, 403), ("E publish+prefetch", 403, 9)):
+        d = []
+        for l in range(1, 8):
+            ia = 1 + 10 * l + a_i if a_i < 10 else 400 + l * 4 + (a_i - 400)
+            ib = 1 + 10 * l + b_i if b_i < 10 else 400 + l * 4 + (b_i - 400)
+            d.append((t[:, ib] - t[:, ia]) * us)
+        sub[name] = round(float(np.median(np.concatenate(d))), 3)
+    out = {"phases": rows, "exchanges": exchanges, "ffn_detail_us": sub, "layer_us_median": round(float(np.median(layer)), 3),
+           "head_dot_us_median": round(float(np.median(head)), 3),
+           "argmax_exchange_us_median": round(float(np.median(key)), 3),
+           "step_us_median": round(float(np.median(step)), 3), "workgroups": nb,
+           "workload": w.name, "context": w.prompt_len}
+    # attention stages of layers 1 .. 3 (slots 464 + 8 (l - 1) + i): A publish
+    # done, block 0 started, QK-norm + RoPE done, exchange-wave sync, partial
+    # done, second sync; and block 0's scores done, end of the partial
+    att = {}
+    for name, i0, i1 in (("qkv gather", None, 0), ("qk-norm+rope", 0, 2), ("sync1", 2, 3), ("partial", 3, 4),
+                         ("sync2", 4, 5), ("partial: to scores", 1, 6), ("partial: scores..end", 6, 7),
+                         ("block0: key select", 1, 101), ("block0: head0 scores", 101, 103),
+                         ("block0: head0 softmax..head1 start", 103, 102), ("block0: head1..softmax end", 102, 6)):
+        d = []
+        for l in range(1, 4):
+            def slot(i):  # 0..7: attention stages; 101..103: block-0 details
+                return 432 + 8 * (l - 1) + (i - 100) if i >= 100 else 464 + 8 * (l - 1) + i
+            b = t[:, slot(i1)]
+            a = t[:, 1 + 10 * l + 1] if i0 is None else t[:, slot(i0)]
+            d.append((b - a) * us)
+        att[name] = round(float(np.median(np.concatenate(d))), 3)
+    # memory wave 0 of each workgroup: units 4 .. 15 of the step (6 stamps each:
+    # start, input ready, ring filled, dot done, partials ready, next issued)
+    m = t[:, 320:392].reshape(nb, 12, 6)
+    out["memory_wave"] = {k: round(float(np.median((m[:, :, j + 1] - m[:, :, j]) * us)), 3) for j, k in
+                          enumerate(("wait input", "ring wait", "dot", "wait partials barrier", "issue"))}
+    out["memory_wave_by_unit"] = {
+        u: {k: round(float(np.median((m[:, ui::4, j + 1] - m[:, ui::4, j]) * us)), 3) for j, k in
+            enumerate(("wait input", "ring wait", "dot", "wait partials barrier", "issue"))}
+        for ui, u in enumerate(("A qkv", "C o", "D gate/up", "E down"))}
+    out["attention_detail_us"] = att
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -327,6 +443,9 @@ def main():
                     help="time only the audio adaptor (qdec_adaptor_run) and print its JSON")
     ap.add_argument("--no-others", action="store_true",
                     help="skip the other workloads the default run also reports (B=16, long and 8k prompts)")
+    ap.add_argument("--trace", action="store_true",
+                    help="per-phase time of a decode step from the diagnostic build libqdec_trace.so "
+                         "(python -m qwen3_kv_cache_amd.build --trace)")
     ap.add_argument("--per-step", action="store_true",
                     help="decode with one launch per token (qdec_decode_step_dev) instead of one launch for all steps")
     a = ap.parse_args()
@@ -347,10 +466,24 @@ def main():
     from qwen3_kv_cache_amd import qdec
     from qwen3_kv_cache_amd.device import Model
 
+    if a.trace:
+        from qwen3_kv_cache_amd.build import TRACE_LIB
+        qdec.use_library(TRACE_LIB)
     w = synth.WORKLOADS[a.workload]
     dev = torch.device("cuda:0")
     W = synth.make_weights(w.shape, w.weight_seed)
     model = Model(w.shape, W.bits if w.shape.bf16 else W.f32, bf16=w.shape.bf16)
+    if a.trace:
+        res = decode_trace(w, model)
+        model.close()
+        for k, v in res["phases"].items():
+            print(f"{k:42s} median {v['median_us']:7.3f} us   p90 {v['p90_us']:7.3f} us", flush=True)
+        for k, v in res["exchanges"].items():
+            print(f"{k:42s} latency {v['latency_after_last_publish_us']:7.3f} us   "
+                  f"producer skew {v['wait_for_last_producer_us']:7.3f} us", flush=True)
+        print(json.dumps(res["ffn_detail_us"]), flush=True)
+        print(json.dumps({"decode_trace": res}), flush=True)
+        return
     pre_ms, dec_ms, wall = measure(w, model, a.steps, a.warmup, a.per_step)
     n, B = w.n_decode, w.n_branch
     decode_tok_s = n * B * a.steps / (dec_ms.sum() / 1e3)

@@ -27,10 +27,18 @@
  * Calls are not thread-safe for one model; states of one model share its
  * scratch memory and must be used from one host thread at a time.
  *
- * Errors: every int-returning call returns one of the QDEC_* codes below. On
- * error nothing is enqueued and the state is unchanged; qdec_last_error()
- * returns a description (thread-local, valid until the next call on the same
- * thread).
+ * Errors: every int-returning call returns one of the QDEC_* codes below, and
+ * qdec_last_error() returns a description (thread-local, valid until the next
+ * call on the same thread). Argument, lifecycle and capacity errors
+ * (QDEC_E_INVALID, _POS, _CAPACITY, _STATE) and allocation failures
+ * (QDEC_E_OOM) are found before anything is enqueued and leave the state
+ * unchanged. QDEC_E_DEVICE from a failed HIP launch may leave the call's
+ * earlier launches enqueued (the state's KV pages may then hold partial
+ * writes) while the state's position stays unchanged. Device-side waits in
+ * the decode and fused GEMM kernels have a time limit; when one expires the
+ * kernel still runs to the end, its outputs are invalid, qdec_model_status()
+ * reports QDEC_E_DEVICE once the stream has been synchronised, and every
+ * later compute call on the model fails with QDEC_E_DEVICE.
  */
 #ifndef QDEC_H
 #define QDEC_H
@@ -110,7 +118,13 @@ typedef struct qdec_state qdec_state;
 
 /* Validate the config and weights, pack the weights on `hip_stream` (a
  * hipStream_t; NULL = the null stream) and build the RoPE tables. The stream
- * is synchronised before return. */
+ * is synchronised before return.
+ * The decode kernel exchanges some values only between the workgroups that
+ * share one XCD, through that XCD's L2; qdec_create checks with a probe launch
+ * that the device places those workgroups together and otherwise exchanges
+ * them at device scope. Setting the environment variable
+ * QDEC_EXCHANGE_SCOPE=device before qdec_create forces the device-scope form
+ * (same results, slower). */
 int qdec_create(const qdec_config* cfg, const qdec_weights* w, void* hip_stream, qdec_model** out);
 
 /* Free the model. Returns QDEC_E_STATE (and frees nothing) while states of
@@ -138,7 +152,10 @@ void qdec_state_destroy(qdec_state* s);
  * audio_begin + audio_len <= n_tokens.
  * Writes the K/V of positions [0, n_tokens) and sets n_past = n_tokens.
  * logits_dev: DEVICE fp32 [vocab] last-position logits, or NULL.
- * argmax_dev: DEVICE int32 greedy token of the last position, or NULL. */
+ * argmax_dev: DEVICE int32 greedy token of the last position, or NULL.
+ * Asynchronous: the ids are copied at call time (ids_host may be reused on
+ * return); audio_dev must stay valid and outputs are valid once the model's
+ * stream has been synchronised. */
 int qdec_prefill(qdec_state* s, const int32_t* ids_host, int32_t n_tokens, const float* audio_dev,
                  int32_t audio_begin, int32_t audio_len, float* logits_dev, int32_t* argmax_dev);
 
@@ -294,6 +311,13 @@ void qdec_adaptor_destroy(qdec_adaptor* a);
 
 /* n_past of the state (-1 for NULL). */
 int32_t qdec_state_pos(const qdec_state* s);
+
+/* QDEC_OK, or QDEC_E_DEVICE if a device-side wait of any launch on this model
+ * has hit its time limit (the outputs of that launch and of later ones are
+ * invalid and the model must be recreated). Call it after synchronising the
+ * model's stream to confirm the outputs of asynchronous calls; QDEC_E_INVALID
+ * for NULL. */
+int qdec_model_status(const qdec_model* m);
 
 /* Description of the last error on this thread ("" if none). */
 const char* qdec_last_error(void);

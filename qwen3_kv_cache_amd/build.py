@@ -6,6 +6,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqdec.so")
+# diagnostic variant: the decode kernel records realtime-counter stamps at its
+# phase boundaries (read back with qdec_debug_trace); never the product library
+TRACE_LIB = os.path.join(HERE, "libqdec_trace.so")
 SOURCES = ["qdec_api.cpp", "qdec_kernels.hip", "qdec_decode.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -33,5 +36,11 @@ def build(verbose: bool = False, out: str = LIB, extra=()) -> str:
     return out
 
 
+def build_trace(verbose: bool = False) -> str:
+    return build(verbose, TRACE_LIB, ("-DQDEC_TRACE",))
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    if "--trace" in sys.argv[1:]:
+        print(build_trace(verbose=True))

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -179,6 +180,14 @@ struct qdec_model {
   unsigned tag_next = 1;  // next unused exchange tag (0 marks a cleared word)
   int* err_host = nullptr;
   int* err_dev = nullptr;
+  bool dec_local = false;  // decode kernel's group-local words at workgroup scope
+  // pinned host staging for asynchronous uploads (prompt ids, page tables):
+  // a buffer is rewritten only after the event of its last copy has completed
+  struct Staging {
+    void* host = nullptr;
+    size_t cap = 0;
+    hipEvent_t ev = nullptr;
+  } st_ids, st_pt;
   size_t layer_elems = 0, off_o = 0, off_gu = 0, off_d = 0;
   int norm_elems = 0;
 };
@@ -273,6 +282,10 @@ void free_model(qdec_model* m) {
   free_prefill(m);
   (void)hipFree(m->ll);
   if (m->err_host) (void)hipHostFree(m->err_host);
+  for (qdec_model::Staging* g : {&m->st_ids, &m->st_pt}) {
+    if (g->host) (void)hipHostFree(g->host);
+    if (g->ev) (void)hipEventDestroy(g->ev);
+  }
   for (void* c : m->pool.chunks) (void)hipFree(c);
   delete m;
 }
@@ -396,6 +409,7 @@ int run_decode(qdec_state* s, int token, const int32_t* token_dev, int pos, int 
   a.nsplit_max = m->nsplit_max;
   a.whole_max = m->whole_max;
   a.err = m->err_dev;
+  a.local = m->dec_local;
   LAUNCH(launch_decode(a, st));
   m->tag_next += need;
   return QDEC_OK;
@@ -664,8 +678,6 @@ int run_prefill(qdec_state* s, int T, const float* audio, int a0, int La, float*
   hipStream_t st = m->stream;
   const bool bf = m->bf16;
   LAUNCH(launch_reset_keys(m->keys, 1, st));
-  if (__atomic_load_n(m->err_host, __ATOMIC_ACQUIRE))
-    return fail(QDEC_E_DEVICE, "an earlier launch hit its time limit; the model must be recreated");
   const bool fused = use_rows(m, T);
   if (fused) {
     if (int e = ensure_rows(m)) return e;
@@ -708,11 +720,59 @@ int release_state_pages(qdec_state* s) {
   return QDEC_OK;
 }
 
+// Copies `bytes` from `src` to device `dst` on the model's stream through a
+// pinned staging buffer, so the call returns without waiting for the copy.
+// The buffer is reused only after its previous copy has completed.
+int staged_upload(qdec_model* m, qdec_model::Staging& g, void* dst, const void* src, size_t bytes) {
+  if (g.ev) HIP_TRY(hipEventSynchronize(g.ev));
+  if (bytes > g.cap) {
+    if (g.host) (void)hipHostFree(g.host);
+    g.host = nullptr;
+    g.cap = 0;
+    const size_t cap = std::max<size_t>(bytes, 4096);
+    if (hipHostMalloc(&g.host, cap, hipHostMallocDefault) != hipSuccess) {
+      (void)hipGetLastError();
+      g.host = nullptr;
+      return fail(QDEC_E_OOM, "cannot allocate %zu bytes of pinned staging memory", cap);
+    }
+    g.cap = cap;
+  }
+  if (!g.ev) HIP_TRY(hipEventCreateWithFlags(&g.ev, hipEventDisableTiming));
+  memcpy(g.host, src, bytes);
+  HIP_TRY(hipMemcpyAsync(dst, g.host, bytes, hipMemcpyHostToDevice, m->stream));
+  HIP_TRY(hipEventRecord(g.ev, m->stream));
+  return QDEC_OK;
+}
+
 int upload_page_table(qdec_state* s) {
   std::vector<int64_t> pt(s->pages.size());
   for (size_t i = 0; i < pt.size(); ++i) pt[i] = (int64_t)(intptr_t)s->pages[i];
-  HIP_TRY(hipMemcpyAsync(s->pt_dev, pt.data(), pt.size() * sizeof(int64_t), hipMemcpyHostToDevice, s->m->stream));
-  HIP_TRY(hipStreamSynchronize(s->m->stream));
+  return staged_upload(s->m, s->m->st_pt, s->pt_dev, pt.data(), pt.size() * sizeof(int64_t));
+}
+
+// The decode kernel's group-local exchange words (plain stores, non-temporal
+// loads served by one XCD's L2) are correct only if every workgroup of group x
+// (workgroups b with b % 8 == x) runs on one XCD. A probe launch of the decode
+// kernel's shape records each workgroup's XCD; if some group spans two XCDs,
+// or QDEC_EXCHANGE_SCOPE=device is set in the environment, those words use
+// device scope instead (slower, placement-independent).
+int check_placement(qdec_model* m) {
+  m->dec_local = false;
+  const char* env = getenv("QDEC_EXCHANGE_SCOPE");
+  if (env && strcmp(env, "device") == 0) return QDEC_OK;
+  const int nb = m->dec_blocks;
+  int* d = nullptr;
+  if (int e = dev_alloc(&d, (size_t)nb, "placement probe")) return e;
+  std::vector<int> h(nb, -1);
+  hipError_t he = launch_xcc_probe(m->bf16, m->d, d, nb, m->dec_lds, m->stream);
+  if (he == hipSuccess) he = hipMemcpyAsync(h.data(), d, nb * sizeof(int), hipMemcpyDeviceToHost, m->stream);
+  if (he == hipSuccess) he = hipStreamSynchronize(m->stream);
+  (void)hipFree(d);
+  if (he != hipSuccess) return fail(QDEC_E_DEVICE, "placement probe: %s", hipGetErrorString(he));
+  bool same = true;
+  constexpr int kGroupCount = 8;  // decode groups (one per XCD)
+  for (int b = kGroupCount; b < nb; ++b) same = same && h[b] == h[b % kGroupCount];
+  m->dec_local = same;
   return QDEC_OK;
 }
 
@@ -852,6 +912,10 @@ int qdec_create(const qdec_config* cfg, const qdec_weights* w, void* hip_stream,
       return e;
     }
     if ((he = launch_clear_words(m->ll, m->ll_words, st))) return fail_dev("exchange init", he);
+    if ((e = check_placement(m))) {
+      free_model(m);
+      return e;
+    }
     if ((he = hipHostMalloc((void**)&m->err_host, sizeof(int), hipHostMallocMapped))) {
       m->err_host = nullptr;
       return fail_dev("error flag", he);
@@ -914,6 +978,13 @@ void qdec_state_destroy(qdec_state* s) {
 
 int32_t qdec_state_pos(const qdec_state* s) { return s ? s->n_past : -1; }
 
+int qdec_model_status(const qdec_model* m) {
+  if (!m) return fail(QDEC_E_INVALID, "model is NULL");
+  if (__atomic_load_n(m->err_host, __ATOMIC_ACQUIRE))
+    return fail(QDEC_E_DEVICE, "a device-side wait hit its time limit; outputs since then are invalid");
+  return ok();
+}
+
 int qdec_prefill(qdec_state* s, const int32_t* ids_host, int32_t n_tokens, const float* audio_dev,
                  int32_t audio_begin, int32_t audio_len, float* logits_dev, int32_t* argmax_dev) {
   if (!s) return fail(QDEC_E_INVALID, "state is NULL");
@@ -935,13 +1006,13 @@ int qdec_prefill(qdec_state* s, const int32_t* ids_host, int32_t n_tokens, const
       return fail(QDEC_E_INVALID, "ids[%d] = %d outside [0, %d)", t, ids_host[t], m->d.V);
   }
   if (int e = check_outputs(m, 1, logits_dev, argmax_dev)) return e;
+  if (__atomic_load_n(m->err_host, __ATOMIC_ACQUIRE))
+    return fail(QDEC_E_DEVICE, "an earlier launch hit its time limit; the model must be recreated");
   if (int e = ensure_prefill(m, n_tokens)) return e;
   std::vector<int32_t> ids(ids_host, ids_host + n_tokens);
   for (int t = audio_begin; t < audio_begin + audio_len; ++t) ids[t] = 0;  // never read
-  HIP_TRY(hipMemcpyAsync(m->p_ids, ids.data(), n_tokens * sizeof(int32_t), hipMemcpyHostToDevice, m->stream));
+  if (int e = staged_upload(m, m->st_ids, m->p_ids, ids.data(), n_tokens * sizeof(int32_t))) return e;
   if (int e = run_prefill(s, n_tokens, audio_dev, audio_begin, audio_len, logits_dev, argmax_dev)) return e;
-  // the host copy source must outlive the async copy
-  HIP_TRY(hipStreamSynchronize(m->stream));
   s->n_past = n_tokens;
   return ok();
 }

@@ -77,7 +77,7 @@ constexpr int kGroups = 8;                // XCDs
 constexpr int kMaxBlocks = kEx;           // one argmax key per exchange thread
 constexpr u64 kWaitTicks = 200000000ull;  // 2 s of the 100 MHz realtime counter
 constexpr int kTagSlots = 8;              // tags per (step, layer)
-enum { PH_Q = 0, PH_ATT = 1, PH_O = 2, PH_Z = 3, PH_X = 4, PH_KEY = 5 };
+enum { PH_Q = 0, PH_ATT = 1, PH_O = 2, PH_Z = 3, PH_X = 4, PH_KEY = 5, PH_OS = 6, PH_XS = 7 };
 
 // Weight staging. Each memory wave owns an LDS ring of two regions of kSlots
 // slots; a slot holds one 16-byte chunk per lane (1 KB). A unit (one phase's
@@ -87,12 +87,6 @@ constexpr int kSlots = 12;
 constexpr int kSlotBytes = kWave * 16;
 constexpr int kMaxK = 1024;  // longest GEMV input: max(hidden, G * D, ffn / 8)
 constexpr int kPtabLds = kDecMaxPos / kPage;  // KV page pointers kept in LDS
-#ifndef QDEC_ISSUE_SLEEP
-#define QDEC_ISSUE_SLEEP 0  // s_sleep units between a layer unit's weight loads
-#endif
-#ifndef QDEC_POLL_SLEEP
-#define QDEC_POLL_SLEEP 0  // s_sleep units (64 clocks) between poll rounds
-#endif
 
 __device__ __forceinline__ u64 now() { return __builtin_amdgcn_s_memrealtime(); }
 
@@ -145,26 +139,39 @@ __device__ __forceinline__ u64 get(const u64* p) {
 }
 __device__ __forceinline__ bool tagged(u64 w, unsigned tag) { return (unsigned)(w >> 32) == tag; }
 
-// Exchanges inside one group (one XCD, whose CUs share an L2) use plain
-// stores, which reach that L2, and non-temporal loads, which read it without
-// allocating in the CU's L1: a shorter round trip than device scope. A
-// reader that ever saw a stale value would only keep polling (tags never
-// repeat), and the wait's time limit turns that into an error.
-__device__ __forceinline__ void put_l(u64* p, float v, unsigned tag) {
-  __hip_atomic_store(p, ((u64)tag << 32) | (u64)__float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+// Exchanges inside one group use plain stores, which reach the XCD's L2, and
+// non-temporal loads, which read that L2 without allocating in the CU's L1: a
+// shorter round trip than device scope. This needs every workgroup of a group
+// on one XCD; the host checks the placement once per model (a probe launch
+// records each workgroup's XCC id) and otherwise sets `local` to 0, and these
+// words then use device scope like the chip-wide ones. A reader that ever saw
+// a stale value would only keep polling (tags never repeat), and the wait's
+// time limit turns that into an error.
+__device__ __forceinline__ void put_l(u64* p, float v, unsigned tag, bool local) {
+  if (local)
+    __hip_atomic_store(p, ((u64)tag << 32) | (u64)__float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  else
+    put(p, v, tag);
 }
-// up to four non-temporal 8-byte loads, issued together and awaited together
+// up to four group-local 8-byte loads, issued together and awaited together
 __device__ __forceinline__ void get_l4(const u64* a, const u64* b, const u64* c, const u64* d, u64& x, u64& y,
-                                       u64& z, u64& w) {
-  asm volatile(
-      "global_load_dwordx2 %0, %4, off nt\n\t"
-      "global_load_dwordx2 %1, %5, off nt\n\t"
-      "global_load_dwordx2 %2, %6, off nt\n\t"
-      "global_load_dwordx2 %3, %7, off nt\n\t"
-      "s_waitcnt vmcnt(0)"
-      : "=&v"(x), "=&v"(y), "=&v"(z), "=&v"(w)
-      : "v"(a), "v"(b), "v"(c), "v"(d)
-      : "memory");
+                                       u64& z, u64& w, bool local) {
+  if (local) {
+    asm volatile(
+        "global_load_dwordx2 %0, %4, off nt\n\t"
+        "global_load_dwordx2 %1, %5, off nt\n\t"
+        "global_load_dwordx2 %2, %6, off nt\n\t"
+        "global_load_dwordx2 %3, %7, off nt\n\t"
+        "s_waitcnt vmcnt(0)"
+        : "=&v"(x), "=&v"(y), "=&v"(z), "=&v"(w)
+        : "v"(a), "v"(b), "v"(c), "v"(d)
+        : "memory");
+  } else {
+    x = get(a);
+    y = get(b);
+    z = get(c);
+    w = get(d);
+  }
 }
 
 // Global-address-space views. Pointers read back from LDS (the KV page
@@ -177,6 +184,14 @@ __device__ __forceinline__ u64 get_g(const gu64* p) {
   return __hip_atomic_load(const_cast<gu64*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ float val(u64 w) { return __uint_as_float((unsigned)w); }
+// A wave-uniform 64-bit value moved to scalar registers. readfirstlane returns
+// a signed int: each half is widened through unsigned, so the low half is not
+// sign-extended into the high one.
+__device__ __forceinline__ u64 uniform64(u64 v) {
+  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)v);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(v >> 32));
+  return ((u64)hi << 32) | (u64)lo;
+}
 
 // Cross-lane steps on the VALU (DPP and the gfx950 permlane swaps) instead of
 // LDS-routed shuffles. dpp(v, ctrl) returns the value of the lane selected by
@@ -301,9 +316,10 @@ struct DecParams {
   float* logits;        // [nsteps, V] or null
   int32_t* tokens_out;  // [nsteps]
   u64* ll;
-  size_t o_q, o_att, o_o, o_z, o_x, o_key;
+  size_t o_q, o_att, o_o, o_z, o_x, o_key, o_os, o_xs;
   unsigned tag0;
   int* err;
+  int local;          // 1: group-local words use workgroup scope (placement checked), 0: device scope
   int R;              // ranks per group
   int nsplit_max;     // attention splits per group
   int whole_max;      // cached positions up to which each rank runs the whole attention
@@ -356,44 +372,59 @@ __device__ __forceinline__ bool give_up(u64 t0, Ctl* ctl, int* err) {
   return false;
 }
 
-// x[k] += sum_{q < P} W[q * n + e] for e = et + k * kEx < n (P <= 8), in that order.
+// Chip-wide sum of partial vectors in two levels: x[k] += sum_{q < P}
+// W[q * n + e] for e = et + k * kEx < n, in part order, with the same result
+// in every workgroup.
+//  1. This workgroup owns elements [e0, e1) (the same range in every group).
+//     The thread holding element e of that range polls its P partial words
+//     (device scope: they come from every XCD), adds them to its residual
+//     value in part order and publishes the sum as a group-local word of S.
+//  2. Every thread then collects the sums of its elements from the owners of
+//     its own group (S, served by the XCD's L2).
+// A workgroup thus reads 8 bytes per owned element and partial across the
+// chip instead of every partial of every element.
 template <int NE>
-__device__ __forceinline__ void gather_sum(const u64* W, int P, int n, unsigned tag, float (&x)[NE], int et,
-                                           Ctl* ctl, int* err) {
-  const u64 t0 = now();
-  u64 w[NE][kGroups];
-  // a wave-uniform base per part plus one 32-bit byte offset per element
-  unsigned eo[NE];
-#pragma unroll
-  for (int k = 0; k < NE; ++k) eo[k] = (unsigned)min(et + k * kEx, n - 1) * 8u;
-  while (true) {
-#pragma unroll
-    for (int q = 0; q < kGroups; ++q) {
-      if (q < P) {
-        const char* wq = (const char*)(W + (size_t)q * n);
-#pragma unroll
-        for (int k = 0; k < NE; ++k) w[k][q] = get((const u64*)(wq + eo[k]));
-      }
-    }
-    bool done = true;
-#pragma unroll
-    for (int k = 0; k < NE; ++k)
-#pragma unroll
-      for (int q = 0; q < kGroups; ++q)
-        if (q < P) done = done && tagged(w[k][q], tag);
-    if (done || give_up(t0, ctl, err)) break;
-    if (QDEC_POLL_SLEEP) __builtin_amdgcn_s_sleep(QDEC_POLL_SLEEP);
-  }
+__device__ __forceinline__ void reduce2(const u64* W, int P, int n, int e0, int e1, unsigned tag1, u64* S,
+                                        unsigned tag2, float (&x)[NE], int et, Ctl* ctl, int* err, bool local) {
+  static_assert(NE <= 4, "stage 2 collects up to four elements per thread");
 #pragma unroll
   for (int k = 0; k < NE; ++k) {
-    if (et + k * kEx < n) {
+    const int e = et + k * kEx;
+    if (e >= e0 && e < e1 && e < n) {
+      const u64 t0 = now();
+      u64 w[kGroups];
+      while (true) {
+#pragma unroll
+        for (int q = 0; q < kGroups; ++q)
+          if (q < P) w[q] = get(W + (size_t)q * n + e);
+        bool done = true;
+#pragma unroll
+        for (int q = 0; q < kGroups; ++q)
+          if (q < P) done = done && tagged(w[q], tag1);
+        if (done || give_up(t0, ctl, err)) break;
+      }
       float s = x[k];
 #pragma unroll
       for (int q = 0; q < kGroups; ++q)
-        if (q < P) s += val(w[k][q]);
-      x[k] = s;
+        if (q < P) s += val(w[q]);
+      put_l(S + e, s, tag2, local);
     }
   }
+  const u64 t0 = now();
+  u64 w[4];
+  const u64* a[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) a[k] = S + min(et + k * kEx, n - 1);
+  while (true) {
+    get_l4(a[0], a[1], a[2], a[3], w[0], w[1], w[2], w[3], local);
+    bool done = true;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) done = done && tagged(w[k], tag2);
+    if (done || give_up(t0, ctl, err)) break;
+  }
+#pragma unroll
+  for (int k = 0; k < NE; ++k)
+    if (et + k * kEx < n) x[k] = val(w[k]);
 }
 
 // dst[i] = value of W[i] for i = et + j * kEx < n (n <= J * kEx).
@@ -410,7 +441,6 @@ __device__ __forceinline__ void gather_vec(const u64* W, int n, unsigned tag, fl
 #pragma unroll
     for (int j = 0; j < J; ++j) done = done && tagged(w[j], tag);
     if (done || give_up(t0, ctl, err)) break;
-    if (QDEC_POLL_SLEEP) __builtin_amdgcn_s_sleep(QDEC_POLL_SLEEP);
   }
 #pragma unroll
   for (int j = 0; j < J; ++j)
@@ -420,14 +450,14 @@ __device__ __forceinline__ void gather_vec(const u64* W, int n, unsigned tag, fl
 // dst[i] = value of W[i] for i = et + j * kEx < n (n <= 4 * kEx), words of
 // this group written with put_l.
 __device__ __forceinline__ void gather_local(const u64* W, int n, unsigned tag, float* dst, int et, Ctl* ctl,
-                                             int* err) {
+                                             int* err, bool local) {
   const u64 t0 = now();
   u64 w[4];
   const u64* a[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) a[j] = W + min(et + j * kEx, n - 1);
   while (true) {
-    get_l4(a[0], a[1], a[2], a[3], w[0], w[1], w[2], w[3]);
+    get_l4(a[0], a[1], a[2], a[3], w[0], w[1], w[2], w[3], local);
     bool done = true;
 #pragma unroll
     for (int j = 0; j < 4; ++j) done = done && tagged(w[j], tag);
@@ -552,7 +582,6 @@ __device__ __forceinline__ void issue_unit(Ring& rg, const char* base, int tab, 
       const int c = min(lane + ((q & jm) << 6), nchm1);
       __builtin_amdgcn_global_load_lds((const void*)(base + ro + c * 16), (lds_void*)(region + q * kSlotBytes), 16,
                                        0, 0);
-      if (QDEC_ISSUE_SLEEP && paced) __builtin_amdgcn_s_sleep(QDEC_ISSUE_SLEEP);
     }
   }
   rg.issued += ns;
@@ -615,46 +644,6 @@ __device__ __forceinline__ void consume_unit(const Ring& rg, int lg, const float
 // other global loads.
 __device__ __forceinline__ gfloat* page_of(const u64* ptab, int u) { return (gfloat*)ptab[u / kPage]; }
 
-// N floats (N even) of cached position u, K (which = 0) or V (which = 1) of
-// KV head g, dims [d0, d0 + N). `fresh` positions were written earlier in this
-// launch by another CU and are read with device-scope loads.
-template <int D, int N>
-__device__ __forceinline__ void load_kvrow(const DecParams& p, const u64* ptab, int l, int g, int u, int which, int d0,
-                                           bool fresh, float* out) {
-  const gfloat* page = page_of(ptab, u);
-  Dims dd{p.L, 0, 0, p.NKV, D, 0, 0, 0.f};
-  const gfloat* src = page + page_offset(dd, l, which, g, u % kPage) + d0;
-  if (!fresh) {
-    if constexpr (N % 4 == 0) {
-      typedef float f32x4 __attribute__((ext_vector_type(4)));
-      typedef __attribute__((address_space(1))) const f32x4 gf32x4;
-#pragma unroll
-      for (int i = 0; i < N; i += 4) {
-        const f32x4 a = *reinterpret_cast<gf32x4*>(src + i);
-        out[i] = a.x; out[i + 1] = a.y; out[i + 2] = a.z; out[i + 3] = a.w;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < N; ++i) out[i] = src[i];
-    }
-  } else {
-    if constexpr (N % 2 == 0) {
-#pragma unroll
-      for (int i = 0; i < N; i += 2) {
-        const u64 a = get_g(reinterpret_cast<const gu64*>(src + i));
-        out[i] = __uint_as_float((unsigned)a);
-        out[i + 1] = __uint_as_float((unsigned)(a >> 32));
-      }
-    } else {
-      typedef __attribute__((address_space(1))) unsigned gu32;
-#pragma unroll
-      for (int i = 0; i < N; ++i)
-        out[i] = __uint_as_float(__hip_atomic_load(reinterpret_cast<gu32*>(const_cast<gfloat*>(src + i)),
-                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    }
-  }
-}
-
 // Online-softmax attention of the G query heads of KV head g over the keys
 // [u0, u0 + n_cached) of the cache plus (if with_cur) the current token held
 // in LDS, one exchange wave's share. Keys are taken in blocks of KPB; wave w
@@ -675,26 +664,75 @@ struct Attn {
   static constexpr int KPB = KPW * kExWaves;   // keys per block
   static constexpr int VD = D >= kWave ? D / kWave : 1;  // output dims per lane
   static constexpr int VL = D / VD;            // lanes holding output dims
-  // q and k rows in LDS are padded by 4 floats after each part's DPL dims, so
-  // the four parts of a key, read in the same instruction, sit in different banks
+  // Lane `part` of a key holds the 4-dim chunks part, part + PARTS, part +
+  // 2 PARTS, ... of that key, so the four lanes of a key read 64 contiguous
+  // bytes per load. q and k rows in LDS keep each part's DPL dims together in
+  // that order, padded by 4 floats after each part, so the four parts of a
+  // key, read in the same instruction, sit in different banks.
   static constexpr int QS = D + 4 * PARTS;     // padded row length
-  __host__ __device__ static constexpr int padi(int d) { return d + (d / DPL) * 4; }
+  __host__ __device__ static constexpr int padi(int d) {
+    return (d / 4 % PARTS) * (DPL + 4) + (d / 4 / PARTS) * 4 + d % 4;
+  }
+  // offset from a key's first dim of register element i (of DPL) of lane `part`
+  __host__ __device__ static constexpr int kdim(int part, int i) { return (part + PARTS * (i / 4)) * 4 + i % 4; }
   float kr[DPL];      // K chunk of this lane's key
   float vr[KPW][VD];  // V of the wave's keys at this lane's dims
 
-  // Every lane loads unconditionally from a valid position (keys past the
-  // cached ones are clamped to the last cached one, or to position 0), so the
-  // loads stay independent of each other; those values are masked later.
+  // A wave's KPW keys of a block start on a page boundary (splits and blocks
+  // are page aligned and KPW == kPage), so they are the slots of one KV page:
+  // one wave-uniform page pointer and fixed offsets address every load. Slots
+  // past the last cached key hold values of later (or never written)
+  // positions of that page; they are masked out of the scores and skipped in
+  // P.V. A wave whose keys all lie past the last cached one reads the last
+  // cached key's page. Pages holding positions written earlier in this launch
+  // (by rank 0 of the group) are read with device-scope loads.
   __device__ __forceinline__ void load_block(const DecParams& p, const u64* ptab, int l, int g, int u0, int b0,
                                              int n_cached, int ew, int lane) {
+    static_assert(KPW == kPage, "a wave's keys of a block are one page");
     const int slot = lane / PARTS, part = lane % PARTS;
     const int last = n_cached > 0 ? u0 + n_cached - 1 : 0;
-    const int uk = min(u0 + b0 + ew * KPW + slot, last);
-    load_kvrow<D, DPL>(p, ptab, l, g, uk, 0, part * DPL, uk >= p.pos0, kr);
+    const int kb = u0 + b0 + ew * KPW;  // first key of the wave, a multiple of kPage
+    const gfloat* page = (const gfloat*)uniform64(ptab[min(kb, last) / kPage]);
+    const size_t lk = ((size_t)(l * 2) * p.NKV + g) * kPage * D;  // layer l, K, head g, slot 0
+    const size_t lv = lk + (size_t)p.NKV * kPage * D;              // V of the same head
+    const gfloat* ks = page + lk + slot * D;
+    const gfloat* vs = page + lv + (lane % VL) * VD;
+    if (kb + KPW - 1 < p.pos0) {  // wave-uniform: every slot written before this launch
+      typedef float f32x4 __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(1))) const f32x4 gf32x4;
 #pragma unroll
-    for (int j = 0; j < KPW; ++j) {
-      const int uj = min(u0 + b0 + ew * KPW + j, last);  // wave-uniform
-      load_kvrow<D, VD>(p, ptab, l, g, uj, 1, (lane % VL) * VD, uj >= p.pos0, vr[j]);
+      for (int i = 0; i < DPL; i += 4) {
+        const f32x4 a = *reinterpret_cast<gf32x4*>(ks + kdim(part, i));
+        kr[i] = a.x; kr[i + 1] = a.y; kr[i + 2] = a.z; kr[i + 3] = a.w;
+      }
+#pragma unroll
+      for (int j = 0; j < KPW; ++j)
+#pragma unroll
+        for (int t = 0; t < VD; ++t) vr[j][t] = vs[j * D + t];
+    } else {
+#pragma unroll
+      for (int i = 0; i < DPL; i += 2) {
+        const u64 a = get_g(reinterpret_cast<const gu64*>(ks + kdim(part, i)));
+        kr[i] = __uint_as_float((unsigned)a);
+        kr[i + 1] = __uint_as_float((unsigned)(a >> 32));
+      }
+#pragma unroll
+      for (int j = 0; j < KPW; ++j) {
+        if constexpr (VD % 2 == 0) {
+#pragma unroll
+          for (int t = 0; t < VD; t += 2) {
+            const u64 a = get_g(reinterpret_cast<const gu64*>(vs + j * D + t));
+            vr[j][t] = __uint_as_float((unsigned)a);
+            vr[j][t + 1] = __uint_as_float((unsigned)(a >> 32));
+          }
+        } else {
+          typedef __attribute__((address_space(1))) unsigned gu32;
+#pragma unroll
+          for (int t = 0; t < VD; ++t)
+            vr[j][t] = __uint_as_float(__hip_atomic_load(reinterpret_cast<gu32*>(const_cast<gfloat*>(vs + j * D + t)),
+                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        }
+      }
     }
   }
 
@@ -725,31 +763,39 @@ struct Attn {
       if (b0 > 0) load_block(p, ptab, l, g, u0, b0, n_cached, ew, lane);
       const int key = b0 + ew * KPW + slot;
       if (b0 == 0) TRACEB(step, l, 1);
-      // the current token's K (LDS) replaces the cached one in its key's lanes:
-      // read for every lane, then selected without branches
-      const bool cur = key == n_cached;
-      float kk[DPL];
+      // the current token's K (LDS) replaces the cached one in the four lanes
+      // of its key: read straight into their K registers
+      if (key == n_cached) {
 #pragma unroll
-      for (int i = 0; i < DPL; i += 4) {
-        const float4 t4 = *reinterpret_cast<const float4*>(k_l + part * (DPL + 4) + i);
-        kk[i] = cur ? t4.x : kr[i];
-        kk[i + 1] = cur ? t4.y : kr[i + 1];
-        kk[i + 2] = cur ? t4.z : kr[i + 2];
-        kk[i + 3] = cur ? t4.w : kr[i + 3];
+        for (int i = 0; i < DPL; i += 4) {
+          const float4 t4 = *reinterpret_cast<const float4*>(k_l + part * (DPL + 4) + i);
+          kr[i] = t4.x;
+          kr[i + 1] = t4.y;
+          kr[i + 2] = t4.z;
+          kr[i + 3] = t4.w;
+        }
       }
       if (b0 == 0) TRACEC(step, l, 1);
+      // every head's partial score in one pass over the key chunk (each head's
+      // products are summed in dimension order)
+      float scs[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) scs[h] = 0.f;
+#pragma unroll
+      for (int i = 0; i < DPL; i += 4) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float4 q = *reinterpret_cast<const float4*>(q_l + h * QS + part * (DPL + 4) + i);
+          scs[h] = fmaf(q.x, kr[i], scs[h]);
+          scs[h] = fmaf(q.y, kr[i + 1], scs[h]);
+          scs[h] = fmaf(q.z, kr[i + 2], scs[h]);
+          scs[h] = fmaf(q.w, kr[i + 3], scs[h]);
+        }
+      }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         if (b0 == 0 && h == 1) TRACEC(step, l, 2);
-        float sc = 0.f;
-#pragma unroll
-        for (int i = 0; i < DPL; i += 4) {
-          const float4 q = *reinterpret_cast<const float4*>(q_l + h * QS + part * (DPL + 4) + i);
-          sc = fmaf(q.x, kk[i], sc);
-          sc = fmaf(q.y, kk[i + 1], sc);
-          sc = fmaf(q.z, kk[i + 2], sc);
-          sc = fmaf(q.w, kk[i + 3], sc);
-        }
+        float sc = scs[h];
         sc += dpp<kDppXor1>(sc);  // the key's four parts
         sc += dpp<kDppXor2>(sc);
         if (key >= n_keys) sc = -INFINITY;
@@ -822,7 +868,7 @@ struct Attn {
 
 template <typename WT, int D, int G, int NE>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
-  extern __shared__ float sm[];
+  extern __shared__ __attribute__((aligned(16))) float sm[];  // 16-byte aligned: float4 rows live here
   constexpr int QD = G * D, GW = (G + 2) * D;
   constexpr int VN = 16 / sizeof(WT);
   constexpr int ES = sizeof(WT);
@@ -1088,15 +1134,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
     TRACE(step, 0);
     // attention mode for this step
     const bool whole = n_hist <= pp->whole_max;
-    int nsplit = 1;
-    if (!whole) nsplit = min(pp->nsplit_max, (n_hist + pp->whole_max - 1) / pp->whole_max);
+    int nsplit = 1, per = n_hist;
+    if (!whole) {
+      // splits of whole pages; nsplit recounted so that none is empty
+      nsplit = min(pp->nsplit_max, (n_hist + pp->whole_max - 1) / pp->whole_max);
+      per = ((n_hist + nsplit - 1) / nsplit + kPage - 1) / kPage * kPage;
+      nsplit = (n_hist + per - 1) / per;
+    }
     const bool att_rank = whole || r < nsplit;
     int u0 = 0, n_cached = n_hist;
     if (!whole) {
-      int su, se;
-      split(n_hist, nsplit, r, su, se);
-      u0 = su;
-      n_cached = se - su;
+      u0 = min(n_hist, r * per);
+      n_cached = min(n_hist, u0 + per) - u0;
     }
     // cached K/V of a layer's first two attention iterations do not depend on
     // the token: they are loaded one phase ahead, under an exchange wait
@@ -1111,7 +1160,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
       const unsigned tgp = tg - kTagSlots;  // layer l-1 of this step
       if (l > 0) {
         const u64* Lx_prev = pp->ll + pp->o_x + (size_t)ppar * kGroups * H;
-        gather_sum<NE>(Lx_prev, kGroups, H, tgp + PH_X, x, et, &ctl, pp->err);
+        u64* Lxs_prev = pp->ll + pp->o_xs + ((size_t)ppar * kGroups + X) * H;
+        reduce2<NE>(Lx_prev, kGroups, H, e0, e1, tgp + PH_X, Lxs_prev, tgp + PH_XS, x, et, &ctl, pp->err, pp->local);
       }
       TRACE(step, 1 + l * 10 + 0);
 #ifdef QDEC_TRACE
@@ -1136,7 +1186,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
         {
           const float inv = norm_scale();
           const int lg = chunk_lg(H, VN);
-          for (int j = et; j < a1 - a0; j += kEx) put_l(Lq + a0 + j, inv * row_val(j, lg), tg + PH_Q);
+          for (int j = et; j < a1 - a0; j += kEx) put_l(Lq + a0 + j, inv * row_val(j, lg), tg + PH_Q, pp->local);
         }
         TRACEB(step, l, 0);
         // ---------------- B: this wave's head vectors from the group's Q/K/V rows
@@ -1149,7 +1199,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
           const int hv0 = min(ew, G + 1), hv1 = min(ew + kExWaves, G + 1);
           while (true) {
             get_l4(Lq + hv0 * D + hl, Lq + hv0 * D + hl + half, Lq + hv1 * D + hl, Lq + hv1 * D + hl + half,
-                   w[0][0], w[0][1], w[1][0], w[1][1]);
+                   w[0][0], w[0][1], w[1][0], w[1][1], pp->local);
             const bool done = tagged(w[0][0], tg + PH_Q) && tagged(w[0][1], tg + PH_Q) &&
                               tagged(w[1][0], tg + PH_Q) && tagged(w[1][1], tg + PH_Q);
             if (done || give_up(t0, &ctl, pp->err)) break;
@@ -1291,7 +1341,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
       // rank 0's K/V append stores are complete before anything else of this
       // workgroup is published (a later step reads them from other CUs)
       if (has_att && r == 0) __builtin_amdgcn_s_waitcnt(0x0F70);
-      gather_sum<NE>(Lo, NKV, H, tg + PH_O, x, et, &ctl, pp->err);
+      {
+        u64* Los = pp->ll + pp->o_os + ((size_t)par * kGroups + X) * H;
+        reduce2<NE>(Lo, NKV, H, c0, c1, tg + PH_O, Los, tg + PH_OS, x, et, &ctl, pp->err, pp->local);
+      }
       TRACE(step, 1 + l * 10 + 6);
       norm_input(gp);
       pad(H);
@@ -1299,23 +1352,25 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
       if (l < 8) TRACE(step, 400 + l * 4 + 1);
       bar();  // input ready
       bar();  // partials ready
+      if (l < 8) TRACE(step, 400 + l * 4 + 2);
       {
         const float inv = norm_scale();
         const int lg = chunk_lg(H, VN);
         for (int i = et; i < z1 - z0; i += kEx) {
           const float gt = inv * row_val(2 * i, lg), up = inv * row_val(2 * i + 1, lg);
-          put_l(Lz + z0 + i, gt / (1.f + expf(-gt)) * up, tg + PH_Z);
+          put_l(Lz + z0 + i, gt / (1.f + expf(-gt)) * up, tg + PH_Z, pp->local);
         }
       }
       TRACE(step, 1 + l * 10 + 7);
 
       // ---------------- E
       QDEC_OPAQUE();
-      gather_local(Lz, FS, tg + PH_Z, xin, et, &ctl, pp->err);
+      gather_local(Lz, FS, tg + PH_Z, xin, et, &ctl, pp->err, pp->local);
       pad(FS);
       TRACE(step, 1 + l * 10 + 8);
       bar();  // input ready
       bar();  // partials ready
+      if (l < 8) TRACE(step, 400 + l * 4 + 3);
       {
         const int lg = chunk_lg(FS, VN);
         for (int j = et; j < e1 - e0; j += kEx) put(Lx + (size_t)X * H + e0 + j, row_val(j, lg), tg + PH_X);
@@ -1463,6 +1518,8 @@ size_t dec_words(const Dims& d, int nb, int nsplit_max, DecOffsets* off) {
   off->z = o; o += 2 * (size_t)kGroups * (d.F / kGroups);
   off->x = o; o += 2 * (size_t)kGroups * d.H;
   off->key = o; o += 2 * 2 * (size_t)nb;
+  off->os = o; o += 2 * (size_t)kGroups * d.H;
+  off->xs = o; o += 2 * (size_t)kGroups * d.H;
   return o;
 }
 
@@ -1528,8 +1585,10 @@ hipError_t launch_decode(const DecLaunch& a, hipStream_t st) {
   p.tokens_out = a.tokens_out;
   p.ll = a.ll;
   p.o_q = a.off.q; p.o_att = a.off.att; p.o_o = a.off.o; p.o_z = a.off.z; p.o_x = a.off.x; p.o_key = a.off.key;
+  p.o_os = a.off.os; p.o_xs = a.off.xs;
   p.tag0 = a.tag0;
   p.err = a.err;
+  p.local = a.local ? 1 : 0;
   p.R = a.nblocks / kGroups;
   p.nsplit_max = a.nsplit_max;
   p.whole_max = a.whole_max;
@@ -1548,6 +1607,32 @@ extern "C" int qdec_debug_trace(unsigned long long* host, int n) {
                                   hipMemcpyDeviceToHost);
 }
 #endif
+
+// Placement probe: thread 0 of each workgroup records the id of the XCD it
+// runs on (hardware register XCC_ID, low 4 bits). Launched with the decode
+// kernel's grid, block and LDS size, so the dispatcher places it the same way.
+__global__ __launch_bounds__(kThreads) void xcc_probe_kernel(int* out) {
+  extern __shared__ float probe_lds[];
+  if (threadIdx.x == 0) {
+    probe_lds[0] = 0.f;
+    out[blockIdx.x] = (int)(__builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11)) & 0xF);
+  }
+}
+
+hipError_t launch_xcc_probe(bool bf16, const Dims& d, int* out_dev, int nblocks, size_t lds_bytes, hipStream_t st) {
+  // the probe asks for the decode kernel's whole LDS (static + dynamic), so
+  // one workgroup fits per CU as in a decode launch
+  const void* fn = kernel_for(bf16, d);
+  if (!fn) return hipErrorInvalidValue;
+  hipFuncAttributes attr{};
+  hipError_t e = hipFuncGetAttributes(&attr, fn);
+  if (e != hipSuccess) return e;
+  const size_t total = attr.sharedSizeBytes + lds_bytes;
+  e = hipFuncSetAttribute((const void*)xcc_probe_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)total);
+  if (e != hipSuccess) return e;
+  xcc_probe_kernel<<<nblocks, kThreads, total, st>>>(out_dev);
+  return hipGetLastError();
+}
 
 // Fill kernel for the exchange words (used when tags are about to wrap).
 __global__ void clear_words_kernel(u64* w, size_t n) {

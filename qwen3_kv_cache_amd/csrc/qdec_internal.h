@@ -178,7 +178,7 @@ size_t sample_buffer_words(int V);
 // ---- persistent decode (qdec_decode.hip)
 // Word offsets of the exchange regions inside the model's word buffer.
 struct DecOffsets {
-  size_t q, att, o, z, x, key;
+  size_t q, att, o, z, x, key, os, xs;
 };
 struct DecLaunch {
   Dims d;
@@ -203,6 +203,7 @@ struct DecLaunch {
   unsigned tag0;
   int nsplit_max, whole_max;
   int* err;                         // device address of a host-visible int
+  bool local;                       // group-local words at workgroup scope (placement checked)
 };
 size_t dec_lds_bytes(bool bf16, const Dims& d, int nblocks, int nsplit_max);
 size_t dec_words(const Dims& d, int nblocks, int nsplit_max, DecOffsets* off);
@@ -212,5 +213,8 @@ bool dec_fits(bool bf16, const Dims& d, int nblocks);
 hipError_t dec_prepare(bool bf16, const Dims& d, size_t lds, int* blocks_per_cu);
 hipError_t launch_decode(const DecLaunch& a, hipStream_t st);
 hipError_t launch_clear_words(unsigned long long* w, size_t n, hipStream_t st);
+// Records in out_dev[b] the XCD that workgroup b runs on, for a launch of the
+// decode kernel's shape (nblocks x 512 threads, its static LDS plus lds_bytes).
+hipError_t launch_xcc_probe(bool bf16, const Dims& d, int* out_dev, int nblocks, size_t lds_bytes, hipStream_t st);
 
 }  // namespace qdec

@@ -34,8 +34,8 @@ QDEC_PAGE = 16
 
 EXPORTS = ("qdec_create", "qdec_destroy", "qdec_state_create", "qdec_state_destroy", "qdec_prefill",
            "qdec_decode_step", "qdec_decode_step_dev", "qdec_decode_greedy", "qdec_decode_batch", "qdec_sample",
-           "qdec_clone_state", "qdec_state_pos", "qdec_last_error", "qdec_adaptor_create", "qdec_adaptor_run",
-           "qdec_adaptor_destroy")
+           "qdec_clone_state", "qdec_state_pos", "qdec_model_status", "qdec_last_error", "qdec_adaptor_create",
+           "qdec_adaptor_run", "qdec_adaptor_destroy")
 
 QDEC_SAMPLE_TOP_K_MAX = 128
 
@@ -82,6 +82,15 @@ class qdec_sampling(ctypes.Structure):
 _lib = None
 
 
+def use_library(path: str) -> None:
+    """Load the library from `path` instead of libqdec.so (the diagnostic
+    build libqdec_trace.so); must run before the first call."""
+    global LIB_PATH
+    if _lib is not None:
+        raise RuntimeError("the qdec library is already loaded")
+    LIB_PATH = path
+
+
 def lib() -> ctypes.CDLL:
     """Load libqdec.so (raises if it has not been built)."""
     global _lib
@@ -114,6 +123,7 @@ def lib() -> ctypes.CDLL:
                                        ctypes.POINTER(ctypes.c_float), vp]),
         "qdec_clone_state": (ctypes.c_int, [vp, ctypes.POINTER(vp)]),
         "qdec_state_pos": (i32, [vp]),
+        "qdec_model_status": (ctypes.c_int, [vp]),
         "qdec_last_error": (ctypes.c_char_p, []),
         "qdec_adaptor_create": (ctypes.c_int, [ctypes.POINTER(qdec_adaptor_config),
                                                ctypes.POINTER(qdec_adaptor_weights), vp, ctypes.POINTER(vp)]),
@@ -123,6 +133,9 @@ def lib() -> ctypes.CDLL:
     for name, (res, args) in sig.items():
         f = getattr(L, name)
         f.restype, f.argtypes = res, args
+    if hasattr(L, "qdec_debug_trace"):  # diagnostic build only
+        L.qdec_debug_trace.restype = ctypes.c_int
+        L.qdec_debug_trace.argtypes = [ctypes.POINTER(ctypes.c_ulonglong), ctypes.c_int]
     _lib = L
     return L
 
@@ -226,6 +239,12 @@ def qdec_adaptor_destroy(adaptor: int) -> None:
 
 def qdec_state_pos(state: int) -> int:
     return lib().qdec_state_pos(_ptr(state))
+
+
+def qdec_model_status(model: int) -> None:
+    """Raises QdecError(QDEC_E_DEVICE) if a device-side wait on this model has
+    hit its time limit (check after synchronising the stream)."""
+    _check(lib().qdec_model_status(_ptr(model)))
 
 
 # ---------------------------------------------------------------- helpers

@@ -11,3 +11,9 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: CPU test that takes more than a few seconds")
+
+
+def pytest_sessionfinish(session, exitstatus):
+    # the per-step parity metrics the GPU tests recorded (nothing on a CPU-only run)
+    from tests import gpu_harness
+    gpu_harness.write_report()

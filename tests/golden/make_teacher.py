@@ -9,9 +9,11 @@ vector (step 0 = prefill, step s = the step that consumed token s-1):
   * values at a fixed seeded sample of vocabulary indices plus the oracle's
     top-k indices and values,
   * top-1/top-2 margin (float32 domain) and the full-vector L2 norm,
-  * the full float32 logits of the first and last step.
+  * the full float32 logits at several steps spread over the run (greedy
+    workloads: 9 steps from the prefill logit to the last step; branch
+    workloads: the prefill and branch 0's last step).
 
-Usage: python tests/golden/make_teacher.py short long prefill8k branch16
+Usage: python tests/golden/make_teacher.py prefill8k ragged3k branch16
 """
 import argparse
 import os
@@ -43,19 +45,27 @@ def summarize(logits: np.ndarray, sample_idx: np.ndarray, k: int):
     }
 
 
-def run_greedy(w, model, n_sample=1024, k=32):
+def run_greedy(w, model, n_sample=8192, k=32, n_full=9):
     ids, audio, a0 = synth.make_prompt(w)
-    sample_idx = np.sort(np.random.default_rng(SAMPLE_SEED).choice(w.shape.vocab, n_sample, replace=False))
+    if n_sample >= w.shape.vocab:  # small vocabularies: every entry
+        sample_idx = np.arange(w.shape.vocab)
+    else:
+        sample_idx = np.sort(np.random.default_rng(SAMPLE_SEED).choice(w.shape.vocab, n_sample, replace=False))
+    full_steps = np.unique(np.round(np.linspace(0, w.n_decode, n_full)).astype(np.int32))
+    full = []
     st = model.new_state()
     t0 = time.perf_counter()
     lg = model.prefill(st, ids, audio, a0)
     t_prefill = time.perf_counter() - t0
     rows = [summarize(lg, sample_idx, k)]
+    full.append(lg.astype(np.float32))
     full_first = lg.astype(np.float32)
     t0 = time.perf_counter()
     for s in range(w.n_decode):
         lg = model.decode(st, rows[-1]["token"], w.prompt_len + s)
         rows.append(summarize(lg, sample_idx, k))
+        if s + 1 in full_steps:
+            full.append(lg.astype(np.float32))
         print(f"  step {s + 1}/{w.n_decode} token {rows[-1]['token']} margin {rows[-1]['margin']:.4g}", flush=True)
     t_decode = time.perf_counter() - t0
     return dict(
@@ -68,6 +78,8 @@ def run_greedy(w, model, n_sample=1024, k=32):
         norm=np.array([r["norm"] for r in rows]),
         full_first=full_first,
         full_last=lg.astype(np.float32),
+        full_steps=full_steps,
+        full_vals=np.stack(full),
         oracle_prefill_s=np.float64(t_prefill),
         oracle_decode_s=np.float64(t_decode),
     )
