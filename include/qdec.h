@@ -240,6 +240,20 @@ typedef struct {
 int qdec_sample(qdec_model* m, const float* logits_dev, int32_t n_rows, const qdec_sampling* params,
                 const int32_t* history_dev, int32_t history_len, const float* uniforms_host, int32_t* tokens_dev);
 
+/* qdec_sample without any allocation, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Same arguments, checks and picks as qdec_sample. Its
+ * scratch (the candidate-key buffers) is a fixed 4.9 MB array that the library
+ * holds on each GPU it runs on until the process ends; its device address is
+ * looked up at qdec_create. That array holds vocabularies of at most
+ * QDEC_SAMPLE_NOALLOC_MAX_VOCAB entries (QDEC_E_INVALID for a larger model).
+ * All calls on one GPU share the array: calls that overlap on one GPU (for
+ * example on two streams) race; calls in sequence on one stream do not. */
+#define QDEC_SAMPLE_NOALLOC_MAX_VOCAB 153600
+int qdec_sample_noalloc(qdec_model* m, const float* logits_dev, int32_t n_rows, const qdec_sampling* params,
+                        const int32_t* history_dev, int32_t history_len, const float* uniforms_host,
+                        int32_t* tokens_dev);
+
 /* ---------------------------------------------------------------- adaptor
  * The audio adaptor that makes the rows qdec_prefill takes as audio_dev
  * (transcribe.cpp "Forward map - funasr_nano", section "Adaptor", stage table

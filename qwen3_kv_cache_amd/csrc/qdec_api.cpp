@@ -168,6 +168,9 @@ struct qdec_model {
   // sampling workspace: two candidate-key buffers
   unsigned long long* sBuf0 = nullptr;
   unsigned long long* sBuf1 = nullptr;
+  // the same for qdec_sample_noalloc: the device's fixed scratch array
+  unsigned long long* sStatic0 = nullptr;
+  unsigned long long* sStatic1 = nullptr;
   PagePool pool;
   int live_states = 0;
   // persistent decode
@@ -916,6 +919,8 @@ int qdec_create(const qdec_config* cfg, const qdec_weights* w, void* hip_stream,
       free_model(m);
       return e;
     }
+    // the fixed sampling scratch of this device (qdec_sample_noalloc)
+    if ((he = sample_static_scratch(&m->sStatic0, &m->sStatic1))) return fail_dev("sampling scratch address", he);
     if ((he = hipHostMalloc((void**)&m->err_host, sizeof(int), hipHostMallocMapped))) {
       m->err_host = nullptr;
       return fail_dev("error flag", he);
@@ -1079,8 +1084,14 @@ int qdec_decode_batch(qdec_state* const* states, int32_t n, const int32_t* token
   return ok();
 }
 
-int qdec_sample(qdec_model* m, const float* logits_dev, int32_t n_rows, const qdec_sampling* params,
-                const int32_t* history_dev, int32_t history_len, const float* uniforms_host, int32_t* tokens_dev) {
+}  // extern "C"
+
+namespace {
+
+// Checks the arguments of a sampling call (both entry points) and fills u.
+int sample_args(qdec_model* m, const float* logits_dev, int32_t n_rows, const qdec_sampling* params,
+                const int32_t* history_dev, int32_t history_len, const float* uniforms_host, int32_t* tokens_dev,
+                SampleUniforms* u) {
   if (!m || !params || !uniforms_host) return fail(QDEC_E_INVALID, "model, params or uniforms_host is NULL");
   const Dims& d = m->d;
   if (n_rows < 1 || n_rows > kMaxBatch) return fail(QDEC_E_INVALID, "n_rows %d outside [1, %d]", n_rows, kMaxBatch);
@@ -1094,17 +1105,30 @@ int qdec_sample(qdec_model* m, const float* logits_dev, int32_t n_rows, const qd
     return fail(QDEC_E_INVALID, "repetition_penalty must be finite and > 0");
   if (history_len < 0 || (history_len > 0 && !history_dev))
     return fail(QDEC_E_INVALID, "history_len %d with history_dev %p", history_len, (const void*)history_dev);
-  SampleUniforms u{};
   for (int r = 0; r < n_rows; ++r) {
     if (!(uniforms_host[r] >= 0.f && uniforms_host[r] < 1.f))
       return fail(QDEC_E_INVALID, "uniforms_host[%d] outside [0, 1)", r);
-    u.u[r] = uniforms_host[r];
+    u->u[r] = uniforms_host[r];
   }
   if (int e = check_dev(logits_dev, (size_t)n_rows * d.V * sizeof(float), "logits_dev")) return e;
   if (int e = check_dev(tokens_dev, (size_t)n_rows * sizeof(int32_t), "tokens_dev")) return e;
   if (history_len > 0) {
     if (int e = check_dev(history_dev, (size_t)n_rows * history_len * sizeof(int32_t), "history_dev")) return e;
   }
+  return QDEC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qdec_sample(qdec_model* m, const float* logits_dev, int32_t n_rows, const qdec_sampling* params,
+                const int32_t* history_dev, int32_t history_len, const float* uniforms_host, int32_t* tokens_dev) {
+  SampleUniforms u{};
+  if (int e = sample_args(m, logits_dev, n_rows, params, history_dev, history_len, uniforms_host, tokens_dev, &u))
+    return e;
+  const Dims& d = m->d;
+  const qdec_sampling& p = *params;
   if (!m->sBuf0) {
     const size_t words = sample_buffer_words(d.V);
     if (int e = dev_alloc(&m->sBuf0, words, "sampling buffer")) return e;
@@ -1116,6 +1140,25 @@ int qdec_sample(qdec_model* m, const float* logits_dev, int32_t n_rows, const qd
   }
   LAUNCH(launch_sample(logits_dev, n_rows, d.V, history_dev, history_len, p.repetition_penalty, p.temperature,
                        p.top_k, p.top_p, u, m->sBuf0, m->sBuf1, tokens_dev, m->stream));
+  return ok();
+}
+
+int qdec_sample_noalloc(qdec_model* m, const float* logits_dev, int32_t n_rows, const qdec_sampling* params,
+                        const int32_t* history_dev, int32_t history_len, const float* uniforms_host,
+                        int32_t* tokens_dev) {
+  SampleUniforms u{};
+  if (int e = sample_args(m, logits_dev, n_rows, params, history_dev, history_len, uniforms_host, tokens_dev, &u))
+    return e;
+  const Dims& d = m->d;
+  if (d.V > sample_static_max_vocab())
+    return fail(QDEC_E_INVALID, "vocab %d exceeds the %d entries the fixed sampling scratch holds", d.V,
+                sample_static_max_vocab());
+  const qdec_sampling& p = *params;
+  // the device's fixed scratch (address resolved at qdec_create); every
+  // buffer word a level reads was written by the level before it, so nothing
+  // needs clearing
+  LAUNCH(launch_sample(logits_dev, n_rows, d.V, history_dev, history_len, p.repetition_penalty, p.temperature,
+                       p.top_k, p.top_p, u, m->sStatic0, m->sStatic1, tokens_dev, m->stream));
   return ok();
 }
 

@@ -174,6 +174,11 @@ hipError_t launch_sample(const float* logits, int n, int V, const int32_t* hist,
                          int top_k, float top_p, const SampleUniforms& u, unsigned long long* buf0,
                          unsigned long long* buf1, int32_t* tok, hipStream_t st);
 size_t sample_buffer_words(int V);
+// The fixed scratch of the allocation-free sampling entry point: both buffers
+// on the current device (its address resolved once per device), and the
+// largest vocabulary they hold.
+hipError_t sample_static_scratch(unsigned long long** buf0, unsigned long long** buf1);
+int sample_static_max_vocab();
 
 // ---- persistent decode (qdec_decode.hip)
 // Word offsets of the exchange regions inside the model's word buffer.

@@ -17,6 +17,8 @@
 //                                   argmax_rows_kernel (batch), then argmax_final_kernel
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include <algorithm>
 #include <cfloat>
 #include <cmath>
@@ -2184,6 +2186,38 @@ hipError_t launch_sample(const float* logits, int n, int V, const int32_t* hist,
 
 size_t sample_buffer_words(int V) {
   return (size_t)kMaxBatch * ((V + kSampleChunk - 1) / kSampleChunk) * kSampleKMax;
+}
+
+// Fixed scratch of qdec_sample_noalloc: the two candidate-key buffers of
+// launch_sample for up to kMaxBatch rows of a vocabulary of at most
+// kSampleStaticChunks * kSampleChunk entries (2 x 2.4 MB). Each GPU holds its
+// own copy for the life of the process. In host code `scratch` is only a
+// stand-in for the symbol: its device address comes from hipGetSymbolAddress,
+// once per device.
+constexpr int kSampleStaticChunks = 150;
+constexpr size_t kSampleStaticWords = (size_t)kMaxBatch * kSampleStaticChunks * kSampleKMax;
+__device__ __align__(256) unsigned long long scratch[2 * kSampleStaticWords];
+
+int sample_static_max_vocab() { return kSampleStaticChunks * kSampleChunk; }
+
+hipError_t sample_static_scratch(unsigned long long** buf0, unsigned long long** buf1) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *buf0 = (unsigned long long*)addr[dev];
+  *buf1 = *buf0 + kSampleStaticWords;
+  return hipSuccess;
 }
 
 hipError_t launch_to_f32(const void* src, bool bf16, size_t n, float* dst, hipStream_t st) {

@@ -34,10 +34,12 @@ QDEC_PAGE = 16
 
 EXPORTS = ("qdec_create", "qdec_destroy", "qdec_state_create", "qdec_state_destroy", "qdec_prefill",
            "qdec_decode_step", "qdec_decode_step_dev", "qdec_decode_greedy", "qdec_decode_batch", "qdec_sample",
+           "qdec_sample_noalloc",
            "qdec_clone_state", "qdec_state_pos", "qdec_model_status", "qdec_last_error", "qdec_adaptor_create",
            "qdec_adaptor_run", "qdec_adaptor_destroy")
 
 QDEC_SAMPLE_TOP_K_MAX = 128
+QDEC_SAMPLE_NOALLOC_MAX_VOCAB = 153600
 
 
 class QdecError(RuntimeError):
@@ -121,6 +123,8 @@ def lib() -> ctypes.CDLL:
         "qdec_decode_batch": (ctypes.c_int, [ctypes.POINTER(vp), i32, ctypes.POINTER(i32), vp, vp]),
         "qdec_sample": (ctypes.c_int, [vp, vp, i32, ctypes.POINTER(qdec_sampling), vp, i32,
                                        ctypes.POINTER(ctypes.c_float), vp]),
+        "qdec_sample_noalloc": (ctypes.c_int, [vp, vp, i32, ctypes.POINTER(qdec_sampling), vp, i32,
+                                               ctypes.POINTER(ctypes.c_float), vp]),
         "qdec_clone_state": (ctypes.c_int, [vp, ctypes.POINTER(vp)]),
         "qdec_state_pos": (i32, [vp]),
         "qdec_model_status": (ctypes.c_int, [vp]),
@@ -215,6 +219,17 @@ def qdec_sample(model: int, logits_dev, n_rows: int, temperature: float, top_k: 
         raise ValueError("uniforms_host shorter than n_rows")
     _check(lib().qdec_sample(_ptr(model), _ptr(logits_dev), int(n_rows), ctypes.byref(p), _ptr(history_dev),
                              int(history_len), u.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), _ptr(tokens_dev)))
+
+
+def qdec_sample_noalloc(model: int, logits_dev, n_rows: int, temperature: float, top_k: int, top_p: float,
+                        repetition_penalty: float, history_dev, history_len: int, uniforms_host, tokens_dev) -> None:
+    p = qdec_sampling(float(temperature), int(top_k), float(top_p), float(repetition_penalty))
+    u = np.ascontiguousarray(uniforms_host, dtype=np.float32)
+    if u.size < n_rows:
+        raise ValueError("uniforms_host shorter than n_rows")
+    _check(lib().qdec_sample_noalloc(_ptr(model), _ptr(logits_dev), int(n_rows), ctypes.byref(p),
+                                     _ptr(history_dev), int(history_len),
+                                     u.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), _ptr(tokens_dev)))
 
 
 def qdec_clone_state(src: int) -> int:
