@@ -190,30 +190,53 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "launches": 5}))
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, W, n_decode_sample: int):
-    """The float64 oracle on the host: prefill of the same prompt and a bounded
-    number of greedy decode steps; returns decode tok/s and prefill tok/s."""
+    """The oracle in float32 (the plain fp32 CPU reference of the decoder) on
+    the host: prefill of the same prompt and a bounded number of greedy decode
+    steps, with the BLAS thread pool set to the cores this process may run on.
+    Returns decode tok/s, with prefill tok/s and the host described in
+    `sample`."""
     import oracle
     import synth
+    cores = len(os.sched_getaffinity(0))
+    limit = None
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
+        limit = threadpool_limits(limits=cores, user_api="blas")
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [cores])
     except Exception:
-        threads = len(os.sched_getaffinity(0))
-    orc = oracle.Qwen3Oracle(oracle.OracleConfig.from_shape(w.shape), W.f32)
-    ids, audio, a0 = synth.make_prompt(w)
-    st = orc.new_state()
-    t0 = time.perf_counter()
-    lg = orc.prefill(st, ids, audio, a0)
-    t_pre = time.perf_counter() - t0
-    tok = oracle.pick_token(lg)
-    t0 = time.perf_counter()
-    for s in range(n_decode_sample):
-        lg = orc.decode(st, tok, w.prompt_len + s)
+        threads = cores
+    try:
+        orc = oracle.Qwen3Oracle(oracle.OracleConfig.from_shape(w.shape), W.f32, dtype=np.float32)
+        ids, audio, a0 = synth.make_prompt(w)
+        st = orc.new_state()
+        t0 = time.perf_counter()
+        lg = orc.prefill(st, ids, audio, a0)
+        t_pre = time.perf_counter() - t0
         tok = oracle.pick_token(lg)
-    t_dec = time.perf_counter() - t0
-    return {"value": n_decode_sample / t_dec, "unit": "decode tok/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"float64 numpy oracle: prefill of the {w.prompt_len}-token prompt "
+        t0 = time.perf_counter()
+        for s in range(n_decode_sample):
+            lg = orc.decode(st, tok, w.prompt_len + s)
+            tok = oracle.pick_token(lg)
+        t_dec = time.perf_counter() - t0
+    finally:
+        if limit is not None:
+            limit.restore_original_limits()
+    return {"value": round(n_decode_sample / t_dec, 2), "unit": "decode tok/s", "cores": int(threads), "kind": "oracle",
+            "dtype": "f32", "prefill_tok_s": round(w.prompt_len / t_pre, 1),
+            "host": {"cpu_model": cpu_model(), "affinity_cores": cores, "blas_threads": int(threads),
+                     "OPENBLAS_NUM_THREADS": os.environ.get("OPENBLAS_NUM_THREADS")},
+            "sample": f"float32 numpy oracle: prefill of the {w.prompt_len}-token prompt "
                       f"({w.prompt_len / t_pre:.1f} prefill tok/s) then {n_decode_sample} greedy decode steps, B=1"}
 
 
@@ -282,10 +305,11 @@ def measure(w, model, steps, warmup, per_step=False):
     return pre_ms, dec_ms, wall
 
 
-def measure_sampling(model, V, calls=50):
+def measure_sampling(model, V, calls=20, groups=7):
     """qdec_sample on 1 and 16 rows of seeded N(0, 3^2) logits (temperature
     0.8, top-k 50, top-p 0.95, repetition penalty 1.1 over 64 history ids):
-    mean microseconds per call, HIP events on the library's stream."""
+    microseconds per call as the median of `groups` timed groups of `calls`
+    calls each (HIP events on the library's stream), with every group's value."""
     import torch
 
     from qwen3_kv_cache_amd import qdec
@@ -304,14 +328,18 @@ def measure_sampling(model, V, calls=50):
 
         for _ in range(3):
             call()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        e0.record()
-        for _ in range(calls):
-            call()
-        e1.record()
-        torch.cuda.synchronize()
-        out[f"rows{n}_us"] = round(e0.elapsed_time(e1) * 1e3 / calls, 2)
+        per = []
+        for _ in range(groups):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(calls):
+                call()
+            e1.record()
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) * 1e3 / calls)
+        out[f"rows{n}_us"] = round(float(np.median(per)), 2)
+        out[f"rows{n}_us_groups"] = [round(x, 2) for x in per]
     return out
 
 
@@ -437,7 +465,8 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="short")
-    ap.add_argument("--cpu-sample", type=int, default=24, help="oracle decode steps for the CPU baseline (0 = skip)")
+    ap.add_argument("--cpu-sample", type=int, default=64,
+                    help="greedy decode steps the CPU oracle runs for the baseline (0 = skip)")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--adaptor-only", action="store_true",
                     help="time only the audio adaptor (qdec_adaptor_run) and print its JSON")

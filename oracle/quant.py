@@ -7,8 +7,9 @@ for the same greedy transcript as the F16 weights; it does not define the
 format. Reading (listed in the design doc), the common block format:
   * a row of an [out, in] matrix is cut into blocks of 32 consecutive inputs;
   * per block, d = max|w| / 127 in float32, stored rounded to float16;
-  * q = w / d with that float32 d, rounded half away from zero, |q| <= 127
-    (q = 0 and d = 0 for an all-zero block);
+  * q = w / d: one IEEE float32 division by that float32 d (not a product
+    with a rounded reciprocal), then rounded half away from zero, evaluated
+    exactly (float64), |q| <= 127 (q = 0 and d = 0 for an all-zero block);
   * the decoder uses w' = q * float32(fp16 d), exact in float32 (8-bit by
     11-bit significands), so a quantized model is the float oracle fed w'.
 """
@@ -28,11 +29,10 @@ def quantize(w: np.ndarray):
     blocks = w.reshape(out, n // BLOCK, BLOCK)
     amax = np.abs(blocks).max(axis=2)
     d = (amax / np.float32(127.0)).astype(np.float32)
-    inv = np.zeros_like(d)
-    nz = d > 0
-    inv[nz] = np.float32(1.0) / d[nz]
-    x = blocks * inv[:, :, None]
-    q = np.sign(x) * np.floor(np.abs(x) + np.float32(0.5))  # half away from zero
+    safe = np.where(d > 0, d, np.float32(1.0)).astype(np.float32)
+    x = (blocks / safe[:, :, None]).astype(np.float32)  # float32 division, one rounding
+    x = np.where(d[:, :, None] > 0, x, np.float32(0.0)).astype(np.float64)
+    q = np.sign(x) * np.floor(np.abs(x) + 0.5)  # half away from zero, exact for float32 x
     q = np.clip(q, -127, 127).astype(np.int8)
     return q.reshape(out, n), d.astype(np.float16)
 

@@ -62,6 +62,67 @@ def test_requantizing_dequantized_weights_is_a_fixed_point():
     np.testing.assert_array_equal(q2, q)
 
 
+def _block(amax_bits, w_bits):
+    """One block whose largest magnitude and second entry are the given float32 bit patterns."""
+    w = np.zeros((1, BLOCK), np.float32)
+    w[0, 0] = np.uint32(amax_bits).view(np.float32)
+    w[0, 1] = np.uint32(w_bits).view(np.float32)
+    return w
+
+
+def test_rounding_is_of_the_float32_quotient():
+    # Blocks where w / d (one float32 division) and w * (1 / d) (a rounded
+    # reciprocal, then a product) land on opposite sides of a half-integer, so
+    # the two readings give different codes. The reading taken is w / d.
+    # amax 0.0445032, w 0.0022777228: w / d = 6.4999995 -> 6 (w * (1/d) = 6.5 -> 7)
+    q, _ = quantize(_block(1026967805, 991249881))
+    assert q[0, 1] == 6
+    # amax 0.014388194, w 0.00062311074: w / d = 5.5 -> 6 (w * (1/d) = 5.4999995 -> 5)
+    q, _ = quantize(_block(1013693558, 975394881))
+    assert q[0, 1] == 6
+    q, _ = quantize(-_block(1013693558, 975394881))
+    assert q[0, 1] == -6  # half away from zero on both sides
+
+
+def test_rounding_below_one_half():
+    # amax 127 gives d = 1 exactly, so q = round(w). The float32 just below 0.5
+    # rounds to 0: adding 0.5 to it in float32 would round up to 1.0.
+    w = np.zeros((1, BLOCK), np.float32)
+    w[0, :8] = [127.0, np.nextafter(np.float32(0.5), np.float32(0)), 0.5, -0.5, 1.5, -2.5, 126.5, -126.49999]
+    q, d = quantize(w)
+    assert float(d[0, 0]) == 1.0
+    assert q[0, :8].tolist() == [127, 0, 1, -1, 2, -3, 127, -126]
+
+
 def test_width_must_be_whole_blocks():
     with pytest.raises(ValueError):
         quantize(np.zeros((2, 40), np.float32))
+
+
+def test_pins_catch_planted_rounding_mistakes():
+    # the two readings the pins above separate, planted in a copy of the
+    # oracle's source: each must fail its pin
+    import inspect
+
+    import oracle.quant as qmod
+    src = inspect.getsource(qmod)
+    planted = {
+        "reciprocal product": ("x = (blocks / safe[:, :, None]).astype(np.float32)",
+                               "x = (blocks * (np.float32(1.0) / safe)[:, :, None]).astype(np.float32)",
+                               test_rounding_is_of_the_float32_quotient),
+        "float32 half add": ("q = np.sign(x) * np.floor(np.abs(x) + 0.5)",
+                             "x = x.astype(np.float32); q = np.sign(x) * np.floor(np.abs(x) + np.float32(0.5))",
+                             test_rounding_below_one_half),
+    }
+    global quantize
+    original = quantize
+    try:
+        for name, (old, new, pin) in planted.items():
+            assert old in src, name
+            ns = {}
+            exec(compile(src.replace(old, new), f"<planted {name}>", "exec"), ns)
+            quantize = ns["quantize"]
+            with pytest.raises(AssertionError):
+                pin()
+    finally:
+        quantize = original
