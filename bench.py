@@ -459,6 +459,71 @@ def decode_trace(w, model, n_steps: int = 8):
     return out
 
 
+def _csv_rows(directory: str, suffix: str):
+    import csv
+    import glob
+    paths = sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True))
+    if not paths:
+        raise SystemExit(f"no *{suffix} under {directory}")
+    return list(csv.DictReader(open(paths[0])))
+
+
+def profile_summary(kind: str, directory: str, bench_log: str = None, copy_dir: str = None) -> str:
+    """Text summary of rocprofv3 output for profiles/: `stats` reads the
+    kernel-trace statistics (time per kernel); `traffic` reads the FETCH_SIZE
+    and WRITE_SIZE counter runs of the decode kernel (directory holds both)
+    and of the 1 GiB copy probe (copy_dir), and converts the counters to HBM
+    bytes per launch with the copy's known bytes as the scale."""
+    import hashlib
+    src = os.path.join(ROOT, "qwen3_kv_cache_amd", "csrc")
+    shas = {f: hashlib.sha256(open(os.path.join(src, f), "rb").read()).hexdigest()
+            for f in ("qdec_decode.hip", "qdec_kernels.hip")}
+    out = []
+    if kind == "stats":
+        rows = _csv_rows(directory, "kernel_stats.csv")
+        out.append(f"{'kernel':66s} {'calls':>6s} {'total_us':>11s} {'avg_us':>10s} {'pct':>6s}")
+        for r in rows:
+            name = r["Name"].replace("void ", "").replace("qdec::(anonymous namespace)::", "")[:64]
+            out.append(f"{name:66s} {int(r['Calls']):6d} {float(r['TotalDurationNs']) / 1e3:11.1f} "
+                       f"{float(r['AverageNs']) / 1e3:10.2f} {float(r['Percentage']):6.2f}")
+        dec = [r for r in rows if "decode_kernel" in r["Name"]]
+        if dec:
+            avg = float(dec[0]["AverageNs"]) / 1e3
+            out.append("")
+            out.append(f"decode_kernel_avg_us_per_launch: {avg:.2f}")
+        if bench_log:
+            line = [ln for ln in open(bench_log) if ln.startswith("{")]
+            if line:
+                b = json.loads(line[-1])
+                n = b["config"]["decode_steps"]
+                out.append(f"decode_us_per_token_from_profile: {avg / n:.2f}" if dec else "")
+                out.append(f"bench line of the same run (under the profiler): decode {b['value']} tok/s, "
+                           f"roofline {b['roofline']['achieved']} GB/s = {100 * b['roofline']['frac']:.1f}% of 8 TB/s")
+    else:
+        def per_dispatch(d, counter, kernel):
+            rows = [r for r in _csv_rows(d, "counter_collection.csv") if r["Counter_Name"] == counter and kernel in r["Kernel_Name"]]
+            vals = [float(r["Counter_Value"]) for r in rows]
+            return (sum(vals) / len(vals), len(vals)) if vals else (float("nan"), 0)
+        f_dec, nf = per_dispatch(os.path.join(directory, "fetch"), "FETCH_SIZE", "decode_kernel")
+        w_dec, nw = per_dispatch(os.path.join(directory, "write"), "WRITE_SIZE", "decode_kernel")
+        f_cp, _ = per_dispatch(os.path.join(copy_dir, "fetch"), "FETCH_SIZE", "copyBuffer")
+        w_cp, _ = per_dispatch(os.path.join(copy_dir, "write"), "WRITE_SIZE", "copyBuffer")
+        gib_kib = (1 << 30) / 1024
+        fs, ws = gib_kib / f_cp, gib_kib / w_cp
+        hbm = (f_dec * fs + w_dec * ws) * 1024
+        import synth
+        w = synth.WORKLOADS["short"]
+        alg = decode_bytes(w.shape, [w.prompt_len + s + 1 for s in range(w.n_decode)]) * w.n_decode
+        out += [f"source_sha256: {shas['qdec_decode.hip']}", f"fetch_kib_per_dispatch: {f_dec:.1f}",
+                f"write_kib_per_dispatch: {w_dec:.1f}", f"copy_fetch_kib: {f_cp:.1f}", f"copy_write_kib: {w_cp:.1f}",
+                f"fetch_scale: {fs:.4f}", f"write_scale: {ws:.4f}", f"hbm_bytes_per_launch: {hbm:.0f}",
+                f"algorithmic_bytes_per_launch: {alg:.0f}", "",
+                f"Traffic / algorithmic bytes = {hbm / alg:.4f} (dispatches averaged: {nf} fetch, {nw} write)."]
+    out.append("")
+    out.append("Source sha256 (qwen3_kv_cache_amd/csrc): " + "; ".join(f"{k} {v}" for k, v in shas.items()))
+    return "\n".join(out)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -477,7 +542,15 @@ def main():
                          "(python -m qwen3_kv_cache_amd.build --trace)")
     ap.add_argument("--per-step", action="store_true",
                     help="decode with one launch per token (qdec_decode_step_dev) instead of one launch for all steps")
+    ap.add_argument("--profile-summary", choices=("stats", "traffic"),
+                    help="print the profiles/ summary of rocprofv3 output under --profile-dir (no GPU use)")
+    ap.add_argument("--profile-dir")
+    ap.add_argument("--copy-dir", help="counter runs of --copy-probe (traffic summaries)")
+    ap.add_argument("--bench-log", help="bench output of the profiled run (stats summaries)")
     a = ap.parse_args()
+    if a.profile_summary:
+        print(profile_summary(a.profile_summary, a.profile_dir, a.bench_log, a.copy_dir))
+        return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {a.gpus}); the decoder is single-GPU by design.",
               file=sys.stderr)

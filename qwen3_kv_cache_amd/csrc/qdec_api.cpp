@@ -883,7 +883,7 @@ int qdec_create(const qdec_config* cfg, const qdec_weights* w, void* hip_stream,
   m->off_gu = n_qkv + n_o;
   m->off_d = n_qkv + n_o + n_gu;
   m->norm_elems = (int)norms_per_layer;
-  // persistent decode: one workgroup per CU, all resident (cooperative launch)
+  // persistent decode: one workgroup per CU, all resident at once (one per CU by LDS)
   {
     int dev = 0;
     hipDeviceProp_t prop;

@@ -1,4 +1,4 @@
-// Persistent decode for gfx950: one cooperative launch runs one or more
+// Persistent decode for gfx950: one launch of one workgroup per CU runs one or more
 // greedy decode steps of one sequence (NCNN "Qwen3ASR ncnn多平台移植", section
 // 5, steps 1-6): embed the token, the Qwen3 blocks (transcribe.cpp "Forward map
 // - funasr_nano", LLM decoder table) and the tied LM head with a greedy argmax
@@ -316,7 +316,7 @@ struct DecParams {
   float* logits;        // [nsteps, V] or null
   int32_t* tokens_out;  // [nsteps]
   u64* ll;
-  size_t o_q, o_att, o_o, o_z, o_x, o_key, o_os, o_xs;
+  size_t o_q, o_att, o_o, o_z, o_x, o_key, o_os, o_xs, o_att2;
   unsigned tag0;
   int* err;
   int local;          // 1: group-local words use workgroup scope (placement checked), 0: device scope
@@ -427,26 +427,6 @@ __device__ __forceinline__ void reduce2(const u64* W, int P, int n, int e0, int 
     if (et + k * kEx < n) x[k] = val(w[k]);
 }
 
-// dst[i] = value of W[i] for i = et + j * kEx < n (n <= J * kEx).
-template <int J>
-__device__ __forceinline__ void gather_vec(const u64* W, int n, unsigned tag, float* dst, int et, Ctl* ctl,
-                                           int* err) {
-  const u64 t0 = now();
-  u64 w[J];
-  const unsigned last = (unsigned)(n - 1) * 8u;
-  while (true) {
-#pragma unroll
-    for (int j = 0; j < J; ++j) w[j] = get((const u64*)((const char*)W + min((unsigned)(et + j * kEx) * 8u, last)));
-    bool done = true;
-#pragma unroll
-    for (int j = 0; j < J; ++j) done = done && tagged(w[j], tag);
-    if (done || give_up(t0, ctl, err)) break;
-  }
-#pragma unroll
-  for (int j = 0; j < J; ++j)
-    if (et + j * kEx < n) dst[et + j * kEx] = val(w[j]);
-}
-
 // dst[i] = value of W[i] for i = et + j * kEx < n (n <= 4 * kEx), words of
 // this group written with put_l.
 __device__ __forceinline__ void gather_local(const u64* W, int n, unsigned tag, float* dst, int et, Ctl* ctl,
@@ -468,12 +448,6 @@ __device__ __forceinline__ void gather_local(const u64* W, int n, unsigned tag, 
     if (et + j * kEx < n) dst[et + j * kEx] = val(w[j]);
 }
 
-__device__ __forceinline__ void gather_any(const u64* W, int n, unsigned tag, float* dst, int et, Ctl* ctl, int* err) {
-  if (n <= 4 * kEx)
-    gather_vec<4>(W, n, tag, dst, et, ctl, err);
-  else
-    gather_vec<32>(W, n, tag, dst, et, ctl, err);
-}
 
 // Barrier of the four exchange waves (the memory waves do not take part):
 // each wave adds one arrival to an LDS counter and waits for the generation's
@@ -1286,24 +1260,47 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
                   v = fmaf(f, e == 1 ? wl[w2 * G + h] : wo[(w2 * G + h) * D + (e - 2)], v);
                 }
               }
-              put(La + (size_t)r * G * (D + 2) + idx, v, tg + PH_ATT);
+              put_l(La + (size_t)r * G * (D + 2) + idx, v, tg + PH_ATT, pp->local);
             }
           }
-          gather_any(La, nsplit * G * (D + 2), tg + PH_ATT, stage, et, &ctl, pp->err);
+          // Merge in two light stages instead of every rank reading every
+          // split's partials: rank r merges outputs [j0, j0 + per) of the
+          // G * D, reading only their (m, l, o) words of each split, and
+          // publishes them; every rank then collects the merged vector.
+          const int mper = (QD + R - 1) / R, j0 = min(QD, r * mper), jn = min(mper, QD - j0);
+          float* m2 = stage;                  // [split][mper]
+          float* l2 = m2 + nsplit * mper;
+          float* o2 = l2 + nsplit * mper;
+          for (int t = et; t < nsplit * mper; t += kEx) {
+            const int sp = t / mper, jj = t % mper, j = min(j0 + jj, QD - 1);
+            const u64* base = La + (size_t)sp * G * (D + 2) + (j / D) * (D + 2);
+            const u64 t0 = now();
+            u64 wv[4];
+            while (true) {
+              get_l4(base, base + 1, base + 2 + j % D, base + 2 + j % D, wv[0], wv[1], wv[2], wv[3], pp->local);
+              if ((tagged(wv[0], tg + PH_ATT) && tagged(wv[1], tg + PH_ATT) && tagged(wv[2], tg + PH_ATT)) ||
+                  give_up(t0, &ctl, pp->err))
+                break;
+            }
+            m2[t] = val(wv[0]);
+            l2[t] = val(wv[1]);
+            o2[t] = val(wv[2]);
+          }
           ex_sync(exgen, ln, &ctl, pp->err);
-          for (int idx = et; idx < QD; idx += kEx) {
-            const int h = idx / D, d = idx % D;
+          u64* Lm = pp->ll + pp->o_att2 + ((size_t)par * NKV + X) * QD;
+          for (int jj = et; jj < jn; jj += kEx) {
             float M = -INFINITY;
-            for (int s = 0; s < nsplit; ++s) M = fmaxf(M, stage[(s * G + h) * (D + 2)]);
+            for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, m2[sp * mper + jj]);
             float o = 0.f, lt = 0.f;
-            for (int s = 0; s < nsplit; ++s) {
-              const float* ps = stage + (s * G + h) * (D + 2);
-              const float f = (ps[0] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ps[0] - M);
-              o = fmaf(f, ps[2 + d], o);
-              lt = fmaf(f, ps[1], lt);
+            for (int sp = 0; sp < nsplit; ++sp) {
+              const float ms = m2[sp * mper + jj];
+              const float f = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+              o = fmaf(f, o2[sp * mper + jj], o);
+              lt = fmaf(f, l2[sp * mper + jj], lt);
             }
-            xin[idx] = o / lt;
+            put_l(Lm + j0 + jj, o / lt, tg + PH_ATT, pp->local);
           }
+          gather_local(Lm, QD, tg + PH_ATT, xin, et, &ctl, pp->err, pp->local);
         }
         pad(QD);
         // rank 0 appends this token's K and V at pos (device scope: other CUs
@@ -1369,13 +1366,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
       pad(FS);
       TRACE(step, 1 + l * 10 + 8);
       bar();  // input ready
+      // cached K/V of the next layer's first attention block do not depend on
+      // the token: their loads are issued while the memory waves run the down
+      // dot, so issuing them costs the exchange waves no time on the chain
+      if (has_att && att_rank && l + 1 < L) at.prefetch(p, ptab, l + 1, X, u0, n_cached, ew, ln);
       bar();  // partials ready
       if (l < 8) TRACE(step, 400 + l * 4 + 3);
       {
         const int lg = chunk_lg(FS, VN);
         for (int j = et; j < e1 - e0; j += kEx) put(Lx + (size_t)X * H + e0 + j, row_val(j, lg), tg + PH_X);
       }
-      if (has_att && att_rank && l + 1 < L) at.prefetch(p, ptab, l + 1, X, u0, n_cached, ew, ln);
       TRACE(step, 1 + l * 10 + 9);
     }
 
@@ -1459,7 +1459,8 @@ Layout layout(bool bf16, const Dims& d, int nsplit_max, int nb) {
   const int G = d.NQ / d.NKV;
   const int QD = G * d.D;
   const int VN = bf16 ? 8 : 4;
-  const int stage = std::max(8, nsplit_max * G * (d.D + 2));
+  const int per = (G * d.D + nb / kGroups - 1) / (nb / kGroups);  // merged outputs per rank
+  const int stage = std::max(8, 3 * nsplit_max * per);            // split merge: (m, l, o) per split
   const int qs = d.D + 16;  // padded q/k row (4 floats after each quarter)
   const int att = (G + 1) * qs + d.D + 2 * kExWaves * G + kExWaves * G * d.D + kExWaves * G * (kWave / 4);
   const int hrows = (d.V + nb - 1) / nb;
@@ -1520,6 +1521,7 @@ size_t dec_words(const Dims& d, int nb, int nsplit_max, DecOffsets* off) {
   off->key = o; o += 2 * 2 * (size_t)nb;
   off->os = o; o += 2 * (size_t)kGroups * d.H;
   off->xs = o; o += 2 * (size_t)kGroups * d.H;
+  off->att2 = o; o += 2 * (size_t)d.NKV * G * d.D;
   return o;
 }
 
@@ -1545,9 +1547,9 @@ bool dec_fits(bool bf16, const Dims& d, int nblocks) {
 }
 
 int dec_split_limit(const Dims& d, int nblocks) {
-  const int G = d.NQ / d.NKV;
-  // the partial words of all splits must fit one gather (32 words per exchange thread)
-  return std::max(1, std::min(nblocks / kGroups, 32 * kEx / (G * (d.D + 2))));
+  (void)d;
+  // every rank of a group may take a split (the partial words hold R splits)
+  return std::max(1, nblocks / kGroups);
 }
 
 hipError_t dec_prepare(bool bf16, const Dims& d, size_t lds, int* blocks_per_cu) {
@@ -1585,7 +1587,7 @@ hipError_t launch_decode(const DecLaunch& a, hipStream_t st) {
   p.tokens_out = a.tokens_out;
   p.ll = a.ll;
   p.o_q = a.off.q; p.o_att = a.off.att; p.o_o = a.off.o; p.o_z = a.off.z; p.o_x = a.off.x; p.o_key = a.off.key;
-  p.o_os = a.off.os; p.o_xs = a.off.xs;
+  p.o_os = a.off.os; p.o_xs = a.off.xs; p.o_att2 = a.off.att2;
   p.tag0 = a.tag0;
   p.err = a.err;
   p.local = a.local ? 1 : 0;
@@ -1598,7 +1600,13 @@ hipError_t launch_decode(const DecLaunch& a, hipStream_t st) {
   const void* fn = kernel_for(a.bf16, d);
   if (!fn) return hipErrorInvalidValue;
   void* args[] = {&p};
-  return hipLaunchCooperativeKernel(fn, dim3(a.nblocks), dim3(kThreads), args, (unsigned)a.lds_bytes, st);
+  // A plain launch: one workgroup per CU (the LDS footprint allows no more),
+  // as many workgroups as CUs, so on a device this process has to itself all
+  // of them are resident at once. Residency is not assumed for safety: every
+  // cross-CU wait has a time limit, so a workgroup that could not start would
+  // make the launch report QDEC_E_DEVICE rather than hang. (A cooperative
+  // launch costs about 17 us more per call.)
+  return hipLaunchKernel(fn, dim3(a.nblocks), dim3(kThreads), args, (unsigned)a.lds_bytes, st);
 }
 
 #ifdef QDEC_TRACE

@@ -183,7 +183,7 @@ int sample_static_max_vocab();
 // ---- persistent decode (qdec_decode.hip)
 // Word offsets of the exchange regions inside the model's word buffer.
 struct DecOffsets {
-  size_t q, att, o, z, x, key, os, xs;
+  size_t q, att, o, z, x, key, os, xs, att2;
 };
 struct DecLaunch {
   Dims d;
