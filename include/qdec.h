@@ -17,8 +17,8 @@
  *    append K/V, full-vocabulary logits, greedy pick; the context holding the
  *    KV cache and position can be cloned to branch from one prefill.
  *
- * Arithmetic: weights bf16 (or fp32), activations, norms, softmax, logits and
- * the KV cache fp32. RMSNorm is x / sqrt(mean(x^2) + eps) * g. Attention
+ * Arithmetic: weights bf16, fp32 or block-int8 (QDEC_Q8_0), activations,
+ * norms, softmax, logits and the KV cache fp32. RMSNorm is x / sqrt(mean(x^2) + eps) * g. Attention
  * scale is 1/sqrt(head_dim); query head h reads KV head h / (n_q / n_kv).
  * The greedy token is the lowest index among the maximal fp32 logits.
  *
@@ -57,9 +57,22 @@ extern "C" {
 #define QDEC_E_OOM (-5)      /* device allocation failed */
 #define QDEC_E_DEVICE (-6)   /* a HIP runtime error */
 
-/* Weight storage types. */
+/* Weight storage types.
+ * QDEC_Q8_0 (audio.cpp "Fun-ASR-Nano Native Runtime Implementation Plan",
+ * Task 8, which ships Q8_0 weight packages; the page names the type but not
+ * its bytes, read here as the common block format): every matrix (WQ, WK, WV,
+ * WO, W_GATE, W_UP, W_DOWN and the embedding) is row-major and each row is
+ * cut into blocks of 32 consecutive inputs, stored in row order as 34 bytes
+ * per block: an IEEE fp16 scale d (little-endian), then 32 int8 codes q. The
+ * weight is exactly q * d. The norm gains are fp32. With QDEC_Q8_0 the
+ * computation is the same as with fp32 weights equal to q * d: the prefill
+ * and batched paths run on that exact dequantization, the single-sequence
+ * decode kernel streams the int8 codes and scales (each 32-input partial
+ * dot scaled by its block's d). Requires ffn to be a multiple of 256 (each
+ * of the 8 slices of W_DOWN's inputs is whole blocks). */
 #define QDEC_F32 0
 #define QDEC_BF16 1
+#define QDEC_Q8_0 2
 
 /* Per-layer tensors, in the order of the qdec_weights.layer table. Linear
  * weights are row-major [out, in]; norm gains are vectors.
@@ -91,7 +104,7 @@ enum {
  * multiple of 64 and <= 8192; n_q_head * head_dim <= 8192; vocab >= 2;
  * rms_eps > 0; rope_theta > 1; each layer's rows per CU fit the decode
  * kernel's LDS staging (true for the Qwen3-0.6B shape on 256 CUs);
- * weight_dtype QDEC_F32 or QDEC_BF16; tied == 1 (the LM head is the token
+ * weight_dtype QDEC_F32, QDEC_BF16 or QDEC_Q8_0; tied == 1 (the LM head is the token
  * embedding table, audio.cpp plan Task 1 Step 3 rejects untied embeddings). */
 typedef struct {
   int32_t n_layer, hidden, n_q_head, n_kv_head, head_dim, ffn, vocab;
@@ -100,13 +113,15 @@ typedef struct {
   int32_t tied;
 } qdec_config;
 
-/* Device pointers to the weights, all of the config's weight_dtype.
+/* Device pointers to the weights, all of the config's weight_dtype (for
+ * QDEC_Q8_0: the matrices as Q8_0 blocks, the norm gains fp32).
  * embed [vocab, hidden] (also the tied LM head), final_norm [hidden].
  * layer: HOST array of n_layer * QDEC_W_PER_LAYER device pointers, layer-major
  * (layer[i * QDEC_W_PER_LAYER + QDEC_W_Q] is layer i's WQ).
  * Ownership: qdec_create copies the per-layer tensors and final_norm into its
- * own packed layout, so those may be freed afterwards; embed is borrowed and
- * must stay valid until qdec_destroy. */
+ * own packed layout, so those may be freed afterwards; with QDEC_F32 and
+ * QDEC_BF16 embed is borrowed and must stay valid until qdec_destroy, with
+ * QDEC_Q8_0 it is unpacked into the library's own copies as well. */
 typedef struct {
   const void* embed;
   const void* final_norm;

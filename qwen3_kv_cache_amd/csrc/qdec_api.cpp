@@ -122,7 +122,17 @@ int dev_alloc(T** p, size_t n, const char* what) {
 struct qdec_model {
   qdec_config cfg{};
   Dims d{};
-  bool bf16 = true;
+  bool bf16 = true;  // bf16 weights in wbuf / embed (else fp32)
+  int wt = QDEC_BF16;  // the config's weight_dtype
+  // QDEC_Q8_0: wbuf and embed hold the exactly dequantized fp32 weights (the
+  // prefill and batched paths); the decode kernel streams int8 codes and the
+  // segmented fp16 scales below
+  int8_t* q_codes = nullptr;
+  uint16_t* q_scales = nullptr;
+  int8_t* q_embed = nullptr;
+  uint16_t* q_escale = nullptr;
+  float* embed_own = nullptr;
+  size_t layer_sbytes = 0, soff_o = 0, soff_gu = 0, soff_d = 0;
   hipStream_t stream = nullptr;
   const void* embed = nullptr;
   float* final_norm = nullptr;
@@ -228,8 +238,10 @@ int validate_config(const qdec_config* c) {
   if (!(c->rms_eps > 0.f) || !std::isfinite(c->rms_eps)) return fail(QDEC_E_INVALID, "rms_eps must be > 0");
   if (!(c->rope_theta > 1.f) || !std::isfinite(c->rope_theta))
     return fail(QDEC_E_INVALID, "rope_theta must be > 1");
-  if (c->weight_dtype != QDEC_F32 && c->weight_dtype != QDEC_BF16)
+  if (c->weight_dtype != QDEC_F32 && c->weight_dtype != QDEC_BF16 && c->weight_dtype != QDEC_Q8_0)
     return fail(QDEC_E_INVALID, "weight_dtype %d unknown", c->weight_dtype);
+  if (c->weight_dtype == QDEC_Q8_0 && c->ffn % (8 * kQ8Block))
+    return fail(QDEC_E_INVALID, "Q8_0 weights need ffn %d to be a multiple of %d", c->ffn, 8 * kQ8Block);
   if (c->tied != 1) return fail(QDEC_E_INVALID, "untied LM head is not supported (tied must be 1)");
   return QDEC_OK;
 }
@@ -277,6 +289,11 @@ void free_model(qdec_model* m) {
   (void)hipFree(m->sBuf1);
   (void)hipFree(m->final_norm);
   (void)hipFree(m->wbuf);
+  (void)hipFree(m->q_codes);
+  (void)hipFree(m->q_scales);
+  (void)hipFree(m->q_embed);
+  (void)hipFree(m->q_escale);
+  (void)hipFree(m->embed_own);
   (void)hipFree(m->nbuf);
   (void)hipFree(m->rope_cos);
   (void)hipFree(m->rope_sin);
@@ -385,17 +402,24 @@ int run_decode(qdec_state* s, int token, const int32_t* token_dev, int pos, int 
   }
   DecLaunch a{};
   a.d = d;
-  a.bf16 = m->bf16;
+  a.wt = m->wt;
   a.nblocks = m->dec_blocks;
   a.lds_bytes = m->dec_lds;
-  a.wbuf = m->wbuf;
+  const bool q8 = m->wt == QDEC_Q8_0;
+  a.wbuf = q8 ? (const void*)m->q_codes : m->wbuf;
   a.layer_elems = m->layer_elems;
   a.off_o = m->off_o;
   a.off_gu = m->off_gu;
   a.off_d = m->off_d;
   a.nbuf = m->nbuf;
   a.norm_elems = m->norm_elems;
-  a.embed = m->embed;
+  a.embed = q8 ? (const void*)m->q_embed : m->embed;
+  a.wscale = m->q_scales;
+  a.layer_sbytes = m->layer_sbytes;
+  a.soff_o = m->soff_o;
+  a.soff_gu = m->soff_gu;
+  a.soff_d = m->soff_d;
+  a.escale = m->q_escale;
   a.final_norm = m->final_norm;
   a.rope_cos = m->rope_cos;
   a.rope_sin = m->rope_sin;
@@ -767,7 +791,7 @@ int check_placement(qdec_model* m) {
   int* d = nullptr;
   if (int e = dev_alloc(&d, (size_t)nb, "placement probe")) return e;
   std::vector<int> h(nb, -1);
-  hipError_t he = launch_xcc_probe(m->bf16, m->d, d, nb, m->dec_lds, m->stream);
+  hipError_t he = launch_xcc_probe(m->wt, m->d, d, nb, m->dec_lds, m->stream);
   if (he == hipSuccess) he = hipMemcpyAsync(h.data(), d, nb * sizeof(int), hipMemcpyDeviceToHost, m->stream);
   if (he == hipSuccess) he = hipStreamSynchronize(m->stream);
   (void)hipFree(d);
@@ -794,18 +818,24 @@ int qdec_create(const qdec_config* cfg, const qdec_weights* w, void* hip_stream,
   if (!w || !w->embed || !w->final_norm || !w->layer) return fail(QDEC_E_INVALID, "weights incomplete");
   const qdec_config& c = *cfg;
   Dims d{c.n_layer, c.hidden, c.n_q_head, c.n_kv_head, c.head_dim, c.ffn, c.vocab, c.rms_eps};
+  const bool q8 = c.weight_dtype == QDEC_Q8_0;
+  // element size of every tensor (of the norm gains only, for Q8_0: fp32)
   const size_t es = c.weight_dtype == QDEC_BF16 ? 2 : 4;
   const size_t shp[QDEC_W_PER_LAYER] = {
       (size_t)d.H, (size_t)d.NQ * d.D * d.H, (size_t)d.NKV * d.D * d.H, (size_t)d.NKV * d.D * d.H,
       (size_t)d.D, (size_t)d.D, (size_t)d.H * d.NQ * d.D, (size_t)d.H, (size_t)d.F * d.H, (size_t)d.F * d.H,
       (size_t)d.H * d.F};
-  if (int e = check_dev(w->embed, (size_t)d.V * d.H * es, "embed")) return e;
+  const bool is_matrix[QDEC_W_PER_LAYER] = {false, true, true, true, false, false, true, false, true, true, true};
+  // bytes of a matrix of n weights: Q8_0 blocks, or n elements
+  auto mat_bytes = [&](size_t n) { return q8 ? n / kQ8Block * kQ8BlockBytes : n * es; };
+  if (int e = check_dev(w->embed, mat_bytes((size_t)d.V * d.H), "embed")) return e;
   if (int e = check_dev(w->final_norm, (size_t)d.H * es, "final_norm")) return e;
   for (int l = 0; l < d.L; ++l)
     for (int t = 0; t < QDEC_W_PER_LAYER; ++t) {
       char what[64];
       snprintf(what, sizeof what, "layer %d tensor %d", l, t);
-      if (int e = check_dev(w->layer[l * QDEC_W_PER_LAYER + t], shp[t] * es, what)) return e;
+      const size_t nb = is_matrix[t] ? mat_bytes(shp[t]) : shp[t] * es;
+      if (int e = check_dev(w->layer[l * QDEC_W_PER_LAYER + t], nb, what)) return e;
     }
 
   qdec_model* m = new (std::nothrow) qdec_model();
@@ -813,6 +843,7 @@ int qdec_create(const qdec_config* cfg, const qdec_weights* w, void* hip_stream,
   m->cfg = c;
   m->d = d;
   m->bf16 = c.weight_dtype == QDEC_BF16;
+  m->wt = c.weight_dtype;
   m->stream = (hipStream_t)hip_stream;
   m->embed = w->embed;
   m->pool.page_bytes = page_floats(d) * sizeof(float);
@@ -843,6 +874,31 @@ int qdec_create(const qdec_config* cfg, const qdec_weights* w, void* hip_stream,
   hipError_t he;
   char* wb = (char*)m->wbuf;
   m->layers.resize(d.L);
+  if (q8) {
+    // int8 codes in the packed row order, their segmented scales, and the
+    // embedding as codes, scales and its exact fp32 dequantization
+    const int QD = d.NQ / d.NKV * d.D, FS = d.F / 8;
+    const size_t spH = q8_seg_bytes(d.H), spQD = q8_seg_bytes(QD), spFS = q8_seg_bytes(FS);
+    m->soff_o = (size_t)d.qkv() * spH;
+    m->soff_gu = m->soff_o + (size_t)d.H * d.NKV * spQD;
+    m->soff_d = m->soff_gu + (size_t)2 * d.F * spH;
+    m->layer_sbytes = m->soff_d + (size_t)d.H * 8 * spFS;
+    const size_t sbytes = m->layer_sbytes * d.L + kQ8ScalePad, esbytes = (size_t)d.V * spH + kQ8ScalePad;
+    if ((e = dev_alloc(&m->q_codes, per_layer * d.L, "int8 weight codes")) ||
+        (e = dev_alloc(&m->q_scales, sbytes / 2, "weight scales")) ||
+        (e = dev_alloc(&m->q_embed, (size_t)d.V * d.H, "int8 embedding codes")) ||
+        (e = dev_alloc(&m->q_escale, esbytes / 2, "embedding scales")) ||
+        (e = dev_alloc(&m->embed_own, (size_t)d.V * d.H, "dequantized embedding"))) {
+      free_model(m);
+      return e;
+    }
+    m->embed = m->embed_own;
+    // padding between and after segments reads as zero scales
+    if ((he = hipMemsetAsync(m->q_scales, 0, sbytes, st)) || (he = hipMemsetAsync(m->q_escale, 0, esbytes, st)))
+      return fail_dev("scale init", he);
+    if ((he = launch_q8_unpack(w->embed, d.V, d.H, d.H, 0, -1, m->q_embed, m->q_escale, m->embed_own, st)))
+      return fail_dev("unpack embed", he);
+  }
   for (int l = 0; l < d.L; ++l) {
     const void* const* t = w->layer + (size_t)l * QDEC_W_PER_LAYER;
     char* base = wb + per_layer * es * l;
@@ -850,27 +906,49 @@ int qdec_create(const qdec_config* cfg, const qdec_weights* w, void* hip_stream,
     char* o = qkv + n_qkv * es;
     char* gu = o + n_o * es;
     char* dn = gu + n_gu * es;
-    const size_t row = (size_t)d.H * es;
-    size_t off = 0;
-    if ((he = hipMemcpyAsync(qkv + off, t[QDEC_W_Q], shp[QDEC_W_Q] * es, hipMemcpyDeviceToDevice, st)))
-      return fail_dev("pack wq", he);
-    off += shp[QDEC_W_Q] * es;
-    if ((he = hipMemcpyAsync(qkv + off, t[QDEC_W_K], shp[QDEC_W_K] * es, hipMemcpyDeviceToDevice, st)))
-      return fail_dev("pack wk", he);
-    off += shp[QDEC_W_K] * es;
-    if ((he = hipMemcpyAsync(qkv + off, t[QDEC_W_V], shp[QDEC_W_V] * es, hipMemcpyDeviceToDevice, st)))
-      return fail_dev("pack wv", he);
-    if ((he = hipMemcpyAsync(o, t[QDEC_W_O], n_o * es, hipMemcpyDeviceToDevice, st))) return fail_dev("pack wo", he);
-    // gate/up interleaved in groups of kGuGroup rows
-    const size_t grp = (size_t)kGuGroup * row;
-    if ((he = hipMemcpy2DAsync(gu, 2 * grp, t[QDEC_W_GATE], grp, grp, d.F / kGuGroup, hipMemcpyDeviceToDevice, st)))
-      return fail_dev("pack gate", he);
-    if ((he = hipMemcpy2DAsync(gu + grp, 2 * grp, t[QDEC_W_UP], grp, grp, d.F / kGuGroup, hipMemcpyDeviceToDevice,
-                               st)))
-      return fail_dev("pack up", he);
-    if ((he = hipMemcpyAsync(dn, t[QDEC_W_DOWN], n_d * es, hipMemcpyDeviceToDevice, st)))
-      return fail_dev("pack down", he);
     float* nb = m->nbuf + norms_per_layer * l;
+    if (q8) {
+      int8_t* cb = m->q_codes + per_layer * l;
+      uint16_t* sb = m->q_scales + m->layer_sbytes * l / 2;
+      float* fb = (float*)base;
+      const int QD = d.NQ / d.NKV * d.D;
+      struct Part {
+        int t, rows, K, kseg, row0, gu_half;
+        size_t off, soff;
+      };
+      const Part parts[] = {{QDEC_W_Q, d.NQ * d.D, d.H, d.H, 0, -1, 0, 0},
+                            {QDEC_W_K, d.NKV * d.D, d.H, d.H, d.NQ * d.D, -1, 0, 0},
+                            {QDEC_W_V, d.NKV * d.D, d.H, d.H, (d.NQ + d.NKV) * d.D, -1, 0, 0},
+                            {QDEC_W_O, d.H, d.NQ * d.D, QD, 0, -1, n_qkv, m->soff_o},
+                            {QDEC_W_GATE, d.F, d.H, d.H, 0, 0, n_qkv + n_o, m->soff_gu},
+                            {QDEC_W_UP, d.F, d.H, d.H, 0, 1, n_qkv + n_o, m->soff_gu},
+                            {QDEC_W_DOWN, d.H, d.F, d.F / 8, 0, -1, n_qkv + n_o + n_gu, m->soff_d}};
+      for (const Part& pt : parts)
+        if ((he = launch_q8_unpack(t[pt.t], pt.rows, pt.K, pt.kseg, pt.row0, pt.gu_half, cb + pt.off,
+                                   sb + pt.soff / 2, fb + pt.off, st)))
+          return fail_dev("unpack weights", he);
+    } else {
+      const size_t row = (size_t)d.H * es;
+      size_t off = 0;
+      if ((he = hipMemcpyAsync(qkv + off, t[QDEC_W_Q], shp[QDEC_W_Q] * es, hipMemcpyDeviceToDevice, st)))
+        return fail_dev("pack wq", he);
+      off += shp[QDEC_W_Q] * es;
+      if ((he = hipMemcpyAsync(qkv + off, t[QDEC_W_K], shp[QDEC_W_K] * es, hipMemcpyDeviceToDevice, st)))
+        return fail_dev("pack wk", he);
+      off += shp[QDEC_W_K] * es;
+      if ((he = hipMemcpyAsync(qkv + off, t[QDEC_W_V], shp[QDEC_W_V] * es, hipMemcpyDeviceToDevice, st)))
+        return fail_dev("pack wv", he);
+      if ((he = hipMemcpyAsync(o, t[QDEC_W_O], n_o * es, hipMemcpyDeviceToDevice, st))) return fail_dev("pack wo", he);
+      // gate/up interleaved in groups of kGuGroup rows
+      const size_t grp = (size_t)kGuGroup * row;
+      if ((he = hipMemcpy2DAsync(gu, 2 * grp, t[QDEC_W_GATE], grp, grp, d.F / kGuGroup, hipMemcpyDeviceToDevice, st)))
+        return fail_dev("pack gate", he);
+      if ((he = hipMemcpy2DAsync(gu + grp, 2 * grp, t[QDEC_W_UP], grp, grp, d.F / kGuGroup, hipMemcpyDeviceToDevice,
+                                 st)))
+        return fail_dev("pack up", he);
+      if ((he = hipMemcpyAsync(dn, t[QDEC_W_DOWN], n_d * es, hipMemcpyDeviceToDevice, st)))
+        return fail_dev("pack down", he);
+    }
     if ((he = launch_to_f32(t[QDEC_W_IN_NORM], m->bf16, d.H, nb, st))) return fail_dev("in_norm", he);
     if ((he = launch_to_f32(t[QDEC_W_POST_NORM], m->bf16, d.H, nb + d.H, st))) return fail_dev("post_norm", he);
     if ((he = launch_to_f32(t[QDEC_W_Q_NORM], m->bf16, d.D, nb + 2 * d.H, st))) return fail_dev("q_norm", he);
@@ -893,7 +971,7 @@ int qdec_create(const qdec_config* cfg, const qdec_weights* w, void* hip_stream,
       free_model(m);
       return fail(QDEC_E_INVALID, "decode needs a multiple of 8 compute units (device has %d)", m->dec_blocks);
     }
-    if (!dec_fits(m->bf16, d, m->dec_blocks)) {
+    if (!dec_fits(m->wt, d, m->dec_blocks)) {
       free_model(m);
       return fail(QDEC_E_INVALID, "shape too large for the decode kernel's LDS staging on %d CUs", m->dec_blocks);
     }
@@ -901,9 +979,9 @@ int qdec_create(const qdec_config* cfg, const qdec_weights* w, void* hip_stream,
     m->whole_max = 64;
     // dynamic LDS; the kernel's static weight rings (96 KB) already keep the
     // runtime from placing two workgroups on one CU
-    m->dec_lds = dec_lds_bytes(m->bf16, d, m->dec_blocks, m->nsplit_max);
+    m->dec_lds = dec_lds_bytes(m->wt, d, m->dec_blocks, m->nsplit_max);
     int occ = 0;
-    if ((he = dec_prepare(m->bf16, d, m->dec_lds, &occ))) return fail_dev("decode kernel setup", he);
+    if ((he = dec_prepare(m->wt, d, m->dec_lds, &occ))) return fail_dev("decode kernel setup", he);
     if (occ != 1) {
       free_model(m);
       return fail(QDEC_E_INVALID, "decode kernel must fit exactly one workgroup per CU (got %d, LDS %zu bytes)", occ,

@@ -305,6 +305,9 @@ struct DecParams {
   const float* nbuf;  // per layer: in_norm[H], post_norm[H], q_norm[D], k_norm[D]
   int norm_elems;
   const void* embed;
+  const void* wscale;  // int8 weights: segmented fp16 scales, layer l at wscale + l * layer_sbytes
+  size_t layer_sbytes, soff_o, soff_gu, soff_d;
+  const void* escale;  // int8 weights: scales of the embedding rows
   const float* final_norm;
   const float* rope_cos;
   const float* rope_sin;
@@ -490,6 +493,32 @@ __device__ __forceinline__ float dot_chunk<float>(const u32x4& raw, const float*
   s = fmaf(__uint_as_float(raw.z), x[2], s);
   return fmaf(__uint_as_float(raw.w), x[3], s);
 }
+// 16 int8 codes (little-endian bytes of raw.x .. raw.w) times x[0..15]; each
+// code converts exactly, so only the sum rounds
+__device__ __forceinline__ float code(unsigned w, int byte) { return (float)((int)(w << (24 - 8 * byte)) >> 24); }
+template <>
+__device__ __forceinline__ float dot_chunk<int8_t>(const u32x4& raw, const float* x) {
+  float s = code(raw.x, 0) * x[0];
+  s = fmaf(code(raw.x, 1), x[1], s);
+  s = fmaf(code(raw.x, 2), x[2], s);
+  s = fmaf(code(raw.x, 3), x[3], s);
+  s = fmaf(code(raw.y, 0), x[4], s);
+  s = fmaf(code(raw.y, 1), x[5], s);
+  s = fmaf(code(raw.y, 2), x[6], s);
+  s = fmaf(code(raw.y, 3), x[7], s);
+  s = fmaf(code(raw.z, 0), x[8], s);
+  s = fmaf(code(raw.z, 1), x[9], s);
+  s = fmaf(code(raw.z, 2), x[10], s);
+  s = fmaf(code(raw.z, 3), x[11], s);
+  s = fmaf(code(raw.w, 0), x[12], s);
+  s = fmaf(code(raw.w, 1), x[13], s);
+  s = fmaf(code(raw.w, 2), x[14], s);
+  return fmaf(code(raw.w, 3), x[15], s);
+}
+// an IEEE half given by its bits, widened exactly
+__device__ __forceinline__ float half_bits(unsigned short b) { return (float)__builtin_bit_cast(_Float16, b); }
+template <typename WT>
+constexpr bool kIsQ8 = std::is_same<WT, int8_t>::value;
 
 // Rows of one phase for this workgroup. Local row j of the job maps to a
 // physical row of a row-major matrix (row stride ld elements); the dot covers
@@ -539,14 +568,18 @@ struct Ring {
   char* r1;
   int issued;        // loads issued by this wave
   int mark0, mark1;  // `issued` right after the unit of each region was issued
+  char* s0;          // int8 weights: the block scales of the unit in region 0 / 1,
+  char* s1;          // 64 bytes per slot (the 32 fp16 scales of the slot's row)
 };
 
 // Issue one unit into region P: slot q (q < ns) holds chunk c = lane + 64 (q & (2^lg - 1))
 // (clamped to the row's last chunk) of the row starting ro(q) bytes after
-// `base`, where ro(q) is lane q of `tab`.
-template <int P>
+// `base`, where ro(q) is lane q of `tab`. Int8 weights (Q8) add one load of
+// the unit's scales: lane 4 q + i (q < ns) brings the 16 bytes at sbase + soff,
+// the i-th quarter of slot q's 64 scale bytes.
+template <int P, bool Q8>
 __device__ __forceinline__ void issue_unit(Ring& rg, const char* base, int tab, int ns, int lg, int nchm1,
-                                           int lane, bool paced) {
+                                           int lane, const char* sbase, int soff) {
   char* region = P ? rg.r1 : rg.r0;
   const int jm = (1 << lg) - 1;
 #pragma unroll
@@ -557,6 +590,11 @@ __device__ __forceinline__ void issue_unit(Ring& rg, const char* base, int tab, 
       __builtin_amdgcn_global_load_lds((const void*)(base + ro + c * 16), (lds_void*)(region + q * kSlotBytes), 16,
                                        0, 0);
     }
+  }
+  if (Q8 && ns > 0) {
+    if (lane < 4 * ns)
+      __builtin_amdgcn_global_load_lds((const void*)(sbase + soff), (lds_void*)(P ? rg.s1 : rg.s0), 16, 0, 0);
+    ++ns;
   }
   rg.issued += ns;
   if (P)
@@ -591,6 +629,14 @@ __device__ __forceinline__ void dot_unit(const Ring& rg, const float* xin, float
   float s[kSlots];
 #pragma unroll
   for (int q = 0; q < kSlots; ++q) s[q] = dot_chunk<WT>(raw[q], xr[q & (CPL - 1)]);
+  if constexpr (kIsQ8<WT>) {
+    // one chunk row per row (LG 0): lane l holds codes [16 l, 16 l + 16),
+    // block l / 2 of the slot's row
+    static_assert(LG == 0, "int8 rows of up to 1024 inputs fill one chunk row");
+    const unsigned short* sc = reinterpret_cast<const unsigned short*>(P ? rg.s1 : rg.s0) + (lane >> 1);
+#pragma unroll
+    for (int q = 0; q < kSlots; ++q) s[q] *= half_bits(sc[q * 32]);
+  }
   reduce12_store(s, dst, lane);
 }
 
@@ -601,7 +647,9 @@ __device__ __forceinline__ void ring_wait(const Ring& rg) {
 
 template <int P, typename WT>
 __device__ __forceinline__ void consume_unit(const Ring& rg, int lg, const float* xin, float* dst, int lane) {
-  if (lg == 0) {
+  if constexpr (kIsQ8<WT>) {
+    dot_unit<P, 0, WT>(rg, xin, dst, lane);
+  } else if (lg == 0) {
     dot_unit<P, 0, WT>(rg, xin, dst, lane);
   } else if (sizeof(WT) == 2 || lg == 1) {
     dot_unit<P, 1, WT>(rg, xin, dst, lane);
@@ -846,10 +894,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
   constexpr int QD = G * D, GW = (G + 2) * D;
   constexpr int VN = 16 / sizeof(WT);
   constexpr int ES = sizeof(WT);
+  constexpr bool Q8 = kIsQ8<WT>;
+  constexpr int kScaleRegion = Q8 ? kSlots * 64 : 16;  // per memory wave
   // GEMV input of the current phase (x * g, o_x or z_x), zero past its length
   __shared__ __attribute__((aligned(16))) float xin[kMaxK];
   __shared__ __attribute__((aligned(16))) char ring0[kMemWaves * kSlots * kSlotBytes];
   __shared__ __attribute__((aligned(16))) char ring1[kMemWaves * kSlots * kSlotBytes];
+  __shared__ __attribute__((aligned(16))) char sring0[kMemWaves * kScaleRegion];
+  __shared__ __attribute__((aligned(16))) char sring1[kMemWaves * kScaleRegion];
   __shared__ Ctl ctl;
   float* stage = sm + p.lds_stage;  // split-attention partials of all ranks
   float* att = sm + p.lds_att;      // q_l [G][D] | k_l [D] | v_l [D] | wm | wl | wo | pw
@@ -908,12 +960,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
   do {               \
   } while (0)
 #endif
-    Ring rg{ring0 + w * kSlots * kSlotBytes, ring1 + w * kSlots * kSlotBytes, 0, 0, 0};
+    Ring rg{ring0 + w * kSlots * kSlotBytes, ring1 + w * kSlots * kSlotBytes, 0, 0, 0,
+            sring0 + w * kScaleRegion, sring1 + w * kScaleRegion};
     // the four layer jobs A, C, D, E: slots issued, chunk rows per row (lg),
     // last chunk, and lane q of tab = byte offset of slot q's row from the matrix base
     const Job jobs[4] = {Job{H, 0, H, a1 - a0, 1, a0}, Job{NQ * D, X * QD, QD, c1 - c0, 0, c0},
                          Job{H, 0, H, 2 * (z1 - z0), 2, X * FS + z0}, Job{F, X * FS, FS, e1 - e0, 0, e0}};
-    int tab[4], ns[4], lgs[4], nchm1[4];
+    // int8 weights: lane 4 q + i of stab = byte offset (from the job's scale
+    // base) of the i-th 16 bytes of slot q's row segment of scales
+    int tab[4], ns[4], lgs[4], nchm1[4], stab[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const Job& jb = jobs[t];
@@ -928,11 +983,21 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
         ro = (jb.phys(j, QD, D, NQ * D, NKV * D, X) * jb.ld + jb.col0) * ES;
       }
       tab[t] = ro;
+      int so = 0;
+      if (Q8 && lane < 4 * nrw) {
+        const int j = w + kMemWaves * (lane >> 2);
+        const int ph = jb.phys(j, QD, D, NQ * D, NKV * D, X);
+        so = (ph * (jb.ld / jb.K) + jb.col0 / jb.K) * q8_seg_bytes(jb.K) + 16 * (lane & 3);
+      }
+      stab[t] = so;
     }
     const int nrwH = (h1 - h0) > w ? ((h1 - h0) - w + kMemWaves - 1) / kMemWaves : 0;
     const int n_units = nlu + NHU;
     const char* wbase = (const char*)p.wbuf;
     const char* ebase = (const char*)p.embed;
+    const char* wsbase = (const char*)p.wscale;
+    const char* esbase = (const char*)p.escale;
+    const int spH = q8_seg_bytes(H);
     const int rowH = H * ES;
     const int nchH = H / VN - 1;
     int ml = lane;  // made opaque per unit, like the exchange waves' indices
@@ -949,14 +1014,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
         const int cm = t == 0 ? nchm1[0] : t == 1 ? nchm1[1] : t == 2 ? nchm1[2] : nchm1[3];
         const size_t toff = t == 0 ? 0 : t == 1 ? p.off_o : t == 2 ? p.off_gu : p.off_d;
         const char* base = wbase + ((size_t)l * p.layer_elems + toff) * ES;
-        issue_unit<P>(rg, base, tb, n, lg, cm, ml, true);
+        const int so = t == 0 ? stab[0] : t == 1 ? stab[1] : t == 2 ? stab[2] : stab[3];
+        const size_t stoff = t == 0 ? 0 : t == 1 ? p.soff_o : t == 2 ? p.soff_gu : p.soff_d;
+        issue_unit<P, Q8>(rg, base, tb, n, lg, cm, ml, wsbase + (size_t)l * p.layer_sbytes + stoff, so);
       } else {
         const int u = k - nlu;
         const int i0 = u * rpbH;  // first local head row of the unit
         int n = nrwH - i0;
         n = n < 0 ? 0 : (n > rpbH ? rpbH : n);
         const int ro = (h0 + w + kMemWaves * (i0 + (ml >> lgH))) * rowH;
-        issue_unit<P>(rg, ebase, ro, __builtin_amdgcn_readfirstlane(n << lgH), lgH, nchH, ml, false);
+        // int8: one chunk row per head row, so scale lane 4 q + i serves row q
+        const int so = Q8 ? (h0 + w + kMemWaves * (i0 + (ml >> 2))) * spH + 16 * (ml & 3) : 0;
+        issue_unit<P, Q8>(rg, ebase, ro, __builtin_amdgcn_readfirstlane(n << lgH), lgH, nchH, ml, esbase, so);
       }
     };
     auto unit_lg = [&](int k) __attribute__((always_inline)) {
@@ -1103,8 +1172,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
       rc = pp->rope_cos[(size_t)pos * half + ln];
       rs = pp->rope_sin[(size_t)pos * half + ln];
     }
+    if constexpr (Q8) {
+      const int8_t* ec = (const int8_t*)pp->embed + (size_t)token * H;
+      const unsigned short* es = (const unsigned short*)((const char*)pp->escale + (size_t)token * q8_seg_bytes(H));
 #pragma unroll
-    for (int k = 0; k < NE; ++k) x[k] = wload((const WT*)pp->embed, (size_t)token * H + min(et + k * kEx, H - 1));
+      for (int k = 0; k < NE; ++k) {
+        const int e = min(et + k * kEx, H - 1);
+        x[k] = (float)ec[e] * half_bits(es[e / kQ8Block]);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < NE; ++k) x[k] = wload((const WT*)pp->embed, (size_t)token * H + min(et + k * kEx, H - 1));
+    }
     TRACE(step, 0);
     // attention mode for this step
     const bool whole = n_hist <= pp->whole_max;
@@ -1455,10 +1534,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
 struct Layout {
   int stage, att, sbuf, ptab, total, nhu;
 };
-Layout layout(bool bf16, const Dims& d, int nsplit_max, int nb) {
+// inputs per 16-byte chunk for a weight kind (QDEC_F32, QDEC_BF16, QDEC_Q8_0)
+int chunk_elems(int wt) { return wt == QDEC_BF16 ? 8 : wt == QDEC_Q8_0 ? 16 : 4; }
+
+Layout layout(int wt, const Dims& d, int nsplit_max, int nb) {
   const int G = d.NQ / d.NKV;
   const int QD = G * d.D;
-  const int VN = bf16 ? 8 : 4;
+  const int VN = chunk_elems(wt);
   const int per = (G * d.D + nb / kGroups - 1) / (nb / kGroups);  // merged outputs per rank
   const int stage = std::max(8, 3 * nsplit_max * per);            // split merge: (m, l, o) per split
   const int qs = d.D + 16;  // padded q/k row (4 floats after each quarter)
@@ -1476,7 +1558,7 @@ Layout layout(bool bf16, const Dims& d, int nsplit_max, int nb) {
   return o;
 }
 
-const void* kernel_for(bool bf16, const Dims& d) {
+const void* kernel_for(int wt, const Dims& d) {
   const int G = d.NQ / d.NKV;
   const int NE = (d.H + kEx - 1) / kEx;
 #define QDEC_DEC_CASE(WT, DD, GG, EE) \
@@ -1491,8 +1573,10 @@ const void* kernel_for(bool bf16, const Dims& d) {
   QDEC_DEC_CASE(WT, 32, 1, 4)     \
   QDEC_DEC_CASE(WT, 32, 2, 4)     \
   QDEC_DEC_CASE(WT, 32, 4, 4)
-  if (bf16) {
+  if (wt == QDEC_BF16) {
     QDEC_DEC_ALL(uint16_t)
+  } else if (wt == QDEC_Q8_0) {
+    QDEC_DEC_ALL(int8_t)
   } else {
     QDEC_DEC_ALL(float)
   }
@@ -1503,8 +1587,8 @@ const void* kernel_for(bool bf16, const Dims& d) {
 
 }  // namespace
 
-size_t dec_lds_bytes(bool bf16, const Dims& d, int nblocks, int nsplit_max) {
-  return (size_t)layout(bf16, d, nsplit_max, nblocks).total * sizeof(float);
+size_t dec_lds_bytes(int wt, const Dims& d, int nblocks, int nsplit_max) {
+  return (size_t)layout(wt, d, nsplit_max, nblocks).total * sizeof(float);
 }
 
 size_t dec_words(const Dims& d, int nb, int nsplit_max, DecOffsets* off) {
@@ -1529,15 +1613,17 @@ unsigned dec_tags_per_step(const Dims& d) { return (unsigned)((d.L + 1) * kTagSl
 
 // Every GEMV input fits the LDS input vector and every layer phase of a
 // workgroup fits one ring region per memory wave: (rows per wave) * (chunk
-// rows per row) <= kSlots; at most one argmax key per exchange thread.
-bool dec_fits(bool bf16, const Dims& d, int nblocks) {
+// rows per row) <= kSlots; at most one argmax key per exchange thread. Int8
+// weights also need every dot's input length to be whole scale blocks.
+bool dec_fits(int wt, const Dims& d, int nblocks) {
   if (nblocks < kGroups || nblocks % kGroups || nblocks > kMaxBlocks) return false;
   const int R = nblocks / kGroups;
-  const int VN = bf16 ? 8 : 4;
+  const int VN = chunk_elems(wt);
   const int G = d.NQ / d.NKV;
   const int FS = d.F / kGroups;
   auto fits = [&](int rows_per_block, int K) {
     if (K > kMaxK || K % VN) return false;
+    if (wt == QDEC_Q8_0 && K % kQ8Block) return false;
     const int rows_w = (rows_per_block + kMemWaves - 1) / kMemWaves;
     return (rows_w << chunk_lg(K, VN)) <= kSlots;
   };
@@ -1552,8 +1638,8 @@ int dec_split_limit(const Dims& d, int nblocks) {
   return std::max(1, nblocks / kGroups);
 }
 
-hipError_t dec_prepare(bool bf16, const Dims& d, size_t lds, int* blocks_per_cu) {
-  const void* fn = kernel_for(bf16, d);
+hipError_t dec_prepare(int wt, const Dims& d, size_t lds, int* blocks_per_cu) {
+  const void* fn = kernel_for(wt, d);
   if (!fn) return hipErrorInvalidValue;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -1571,6 +1657,12 @@ hipError_t launch_decode(const DecLaunch& a, hipStream_t st) {
   p.nbuf = a.nbuf;
   p.norm_elems = a.norm_elems;
   p.embed = a.embed;
+  p.wscale = a.wscale;
+  p.layer_sbytes = a.layer_sbytes;
+  p.soff_o = a.soff_o;
+  p.soff_gu = a.soff_gu;
+  p.soff_d = a.soff_d;
+  p.escale = a.escale;
   p.final_norm = a.final_norm;
   p.rope_cos = a.rope_cos;
   p.rope_sin = a.rope_sin;
@@ -1594,10 +1686,10 @@ hipError_t launch_decode(const DecLaunch& a, hipStream_t st) {
   p.R = a.nblocks / kGroups;
   p.nsplit_max = a.nsplit_max;
   p.whole_max = a.whole_max;
-  const Layout lay = layout(a.bf16, d, a.nsplit_max, a.nblocks);
+  const Layout lay = layout(a.wt, d, a.nsplit_max, a.nblocks);
   p.nhu = lay.nhu;
   p.lds_stage = lay.stage; p.lds_att = lay.att; p.lds_sbuf = lay.sbuf; p.lds_ptab = lay.ptab;
-  const void* fn = kernel_for(a.bf16, d);
+  const void* fn = kernel_for(a.wt, d);
   if (!fn) return hipErrorInvalidValue;
   void* args[] = {&p};
   // A plain launch: one workgroup per CU (the LDS footprint allows no more),
@@ -1627,10 +1719,10 @@ __global__ __launch_bounds__(kThreads) void xcc_probe_kernel(int* out) {
   }
 }
 
-hipError_t launch_xcc_probe(bool bf16, const Dims& d, int* out_dev, int nblocks, size_t lds_bytes, hipStream_t st) {
+hipError_t launch_xcc_probe(int wt, const Dims& d, int* out_dev, int nblocks, size_t lds_bytes, hipStream_t st) {
   // the probe asks for the decode kernel's whole LDS (static + dynamic), so
   // one workgroup fits per CU as in a decode launch
-  const void* fn = kernel_for(bf16, d);
+  const void* fn = kernel_for(wt, d);
   if (!fn) return hipErrorInvalidValue;
   hipFuncAttributes attr{};
   hipError_t e = hipFuncGetAttributes(&attr, fn);

@@ -162,6 +162,28 @@ hipError_t launch_gemm_swiglu_split(const uint16_t* A0, const uint16_t* A1, int 
                                     uint16_t* zhi, uint16_t* zlo, int ldz, hipStream_t st);
 hipError_t launch_to_f32(const void* src, bool bf16, size_t n, float* dst, hipStream_t st);
 
+// ---- block-int8 (Q8_0) weights
+// A Q8_0 matrix [rows, K] arrives as rows of K / 32 blocks of kQ8BlockBytes:
+// an fp16 scale d, then 32 int8 codes q; the weight is q * d. The decode
+// kernel reads the codes as int8 rows and the scales from a separate array
+// in which each row is cut into segments of kseg inputs (the column slice one
+// workgroup's dot covers), each segment's kseg / 32 fp16 scales padded to
+// q8_seg_bytes(kseg) bytes so that every segment starts 16-byte aligned.
+constexpr int kQ8Block = 32;
+constexpr int kQ8BlockBytes = 34;
+__host__ __device__ constexpr int q8_seg_bytes(int kseg) { return ((kseg / kQ8Block) * 2 + 15) & ~15; }
+// Bytes past the last segment that the decode kernel's 64-byte scale loads
+// may read (zero-filled).
+constexpr int kQ8ScalePad = 64;
+// Unpack rows [0, rows) of a Q8_0 matrix with K inputs per row: source row r
+// goes to destination row dst_row(r) = row0 + r, or with gu_half >= 0 to the
+// gate/up interleaved row (r / kGuGroup) * 2 kGuGroup + gu_half * kGuGroup +
+// r % kGuGroup. Codes to codes[dst_row * K ...], the exact q * d to
+// deq[dst_row * K ...] (fp32), scales to the segmented layout at
+// scales + (dst_row * (K / kseg) + b / (kseg / 32)) * q8_seg_bytes(kseg).
+hipError_t launch_q8_unpack(const void* src, int rows, int K, int kseg, int row0, int gu_half, int8_t* codes,
+                            uint16_t* scales, float* deq, hipStream_t st);
+
 // ---- sampling after the LM head (qdec_kernels.hip)
 constexpr int kSampleKMax = 128;  // largest top-k
 struct SampleUniforms {
@@ -185,9 +207,11 @@ int sample_static_max_vocab();
 struct DecOffsets {
   size_t q, att, o, z, x, key, os, xs, att2;
 };
+// Weight kinds of the decode kernel: the qdec_config weight_dtype codes
+// (QDEC_F32, QDEC_BF16, QDEC_Q8_0).
 struct DecLaunch {
   Dims d;
-  bool bf16;
+  int wt;
   int nblocks;                      // one workgroup per CU, a multiple of 8
   size_t lds_bytes;
   const void* wbuf;                 // packed layer weights, layer l at wbuf + l * layer_elems
@@ -195,6 +219,12 @@ struct DecLaunch {
   const float* nbuf;                // fp32 norm gains, layer l at nbuf + l * norm_elems
   int norm_elems;
   const void* embed;
+  // QDEC_Q8_0: wbuf and embed hold int8 codes; the fp16 scales of layer l
+  // start at wscale + l * layer_sbytes (jobs at soff_o, soff_gu, soff_d), the
+  // embedding's at escale
+  const void* wscale;
+  size_t layer_sbytes, soff_o, soff_gu, soff_d;
+  const void* escale;
   const float* final_norm;
   const float* rope_cos;
   const float* rope_sin;
@@ -210,16 +240,16 @@ struct DecLaunch {
   int* err;                         // device address of a host-visible int
   bool local;                       // group-local words at workgroup scope (placement checked)
 };
-size_t dec_lds_bytes(bool bf16, const Dims& d, int nblocks, int nsplit_max);
+size_t dec_lds_bytes(int wt, const Dims& d, int nblocks, int nsplit_max);
 size_t dec_words(const Dims& d, int nblocks, int nsplit_max, DecOffsets* off);
 unsigned dec_tags_per_step(const Dims& d);
 int dec_split_limit(const Dims& d, int nblocks);
-bool dec_fits(bool bf16, const Dims& d, int nblocks);
-hipError_t dec_prepare(bool bf16, const Dims& d, size_t lds, int* blocks_per_cu);
+bool dec_fits(int wt, const Dims& d, int nblocks);
+hipError_t dec_prepare(int wt, const Dims& d, size_t lds, int* blocks_per_cu);
 hipError_t launch_decode(const DecLaunch& a, hipStream_t st);
 hipError_t launch_clear_words(unsigned long long* w, size_t n, hipStream_t st);
 // Records in out_dev[b] the XCD that workgroup b runs on, for a launch of the
 // decode kernel's shape (nblocks x 512 threads, its static LDS plus lds_bytes).
-hipError_t launch_xcc_probe(bool bf16, const Dims& d, int* out_dev, int nblocks, size_t lds_bytes, hipStream_t st);
+hipError_t launch_xcc_probe(int wt, const Dims& d, int* out_dev, int nblocks, size_t lds_bytes, hipStream_t st);
 
 }  // namespace qdec

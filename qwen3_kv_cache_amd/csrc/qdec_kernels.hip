@@ -2229,4 +2229,38 @@ hipError_t launch_to_f32(const void* src, bool bf16, size_t n, float* dst, hipSt
   return hipGetLastError();
 }
 
+// One thread per Q8_0 block: 34 source bytes (fp16 scale, 32 int8 codes) read
+// bytewise, since blocks sit at 2-byte alignment only.
+__global__ void q8_unpack_kernel(const uint8_t* src, int rows, int K, int kseg, int row0, int gu_half,
+                                 int8_t* codes, uint16_t* scales, float* deq) {
+  const int nbk = K / kQ8Block, bps = kseg / kQ8Block, nseg = K / kseg, sp = q8_seg_bytes(kseg);
+  const size_t total = (size_t)rows * nbk;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const int r = (int)(i / nbk), b = (int)(i % nbk);
+    const uint8_t* blk = src + i * kQ8BlockBytes;
+    const unsigned short dbits = (unsigned short)(blk[0] | (blk[1] << 8));
+    const float d = (float)__builtin_bit_cast(_Float16, dbits);
+    const int dr = gu_half < 0 ? row0 + r : (r / kGuGroup) * 2 * kGuGroup + gu_half * kGuGroup + r % kGuGroup;
+    int8_t* c = codes + (size_t)dr * K + (size_t)b * kQ8Block;
+    float* w = deq + (size_t)dr * K + (size_t)b * kQ8Block;
+    for (int j = 0; j < kQ8Block; ++j) {
+      const int8_t q = (int8_t)blk[2 + j];
+      c[j] = q;
+      w[j] = (float)q * d;  // exact: 8 by 11 significant bits
+    }
+    const size_t so = ((size_t)dr * nseg + b / bps) * sp;
+    scales[so / 2 + b % bps] = dbits;
+  }
+}
+
+hipError_t launch_q8_unpack(const void* src, int rows, int K, int kseg, int row0, int gu_half, int8_t* codes,
+                            uint16_t* scales, float* deq, hipStream_t st) {
+  if (rows <= 0 || K <= 0 || K % kQ8Block || kseg <= 0 || kseg % kQ8Block || K % kseg) return hipErrorInvalidValue;
+  if (gu_half >= 0 && rows % kGuGroup) return hipErrorInvalidValue;
+  const size_t total = (size_t)rows * (K / kQ8Block);
+  const int blocks = (int)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
+  q8_unpack_kernel<<<blocks, 256, 0, st>>>((const uint8_t*)src, rows, K, kseg, row0, gu_half, codes, scales, deq);
+  return hipGetLastError();
+}
+
 }  // namespace qdec

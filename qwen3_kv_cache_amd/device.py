@@ -3,7 +3,9 @@
 ``Model`` uploads a weight mapping to the GPU with torch and creates a qdec
 model on the current torch stream. The mapping uses the names "embed",
 "final_norm" and "L{i}.{in_norm,wq,wk,wv,q_norm,k_norm,wo,post_norm,w_gate,
-w_up,w_down}"; bf16 weights are given as uint16 bit patterns.
+w_up,w_down}"; bf16 weights are given as uint16 bit patterns. With q8=True
+the matrices and the embedding are uint8 arrays of Q8_0 blocks (one row of
+in / 32 blocks of 34 bytes per matrix row) and the norm gains float32.
 """
 from __future__ import annotations
 
@@ -14,6 +16,7 @@ import numpy as np
 from . import qdec
 
 LAYER_TENSORS = ("in_norm", "wq", "wk", "wv", "q_norm", "k_norm", "wo", "post_norm", "w_gate", "w_up", "w_down")
+NORM_TENSORS = ("in_norm", "q_norm", "k_norm", "post_norm", "final_norm")
 
 
 def _torch():
@@ -24,14 +27,19 @@ def _torch():
 
 
 class Model:
-    def __init__(self, shape, arrays: Dict[str, np.ndarray], bf16: bool, device: str = "cuda:0"):
+    def __init__(self, shape, arrays: Dict[str, np.ndarray], bf16: bool, device: str = "cuda:0", q8: bool = False):
         torch = _torch()
         self.shape = shape
         self.device = torch.device(device)
-        self.bf16 = bf16
+        self.bf16 = bf16 and not q8
+        self.q8 = q8
         self.tensors = {}
         for name, a in arrays.items():
-            if bf16:
+            if q8:
+                is_norm = name.split(".")[-1] in NORM_TENSORS
+                a = np.ascontiguousarray(a, dtype=np.float32 if is_norm else np.uint8)
+                t = torch.from_numpy(a).to(self.device)
+            elif bf16:
                 t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(self.device).view(torch.bfloat16)
             else:
                 t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(self.device)
@@ -39,13 +47,15 @@ class Model:
         layer_ptrs = [[self.tensors[f"L{i}.{t}"].data_ptr() for t in LAYER_TENSORS] for i in range(shape.n_layer)]
         self.table = qdec.WeightTable(self.tensors["embed"].data_ptr(), self.tensors["final_norm"].data_ptr(),
                                       layer_ptrs)
+        dtype = qdec.QDEC_Q8_0 if q8 else (qdec.QDEC_BF16 if bf16 else qdec.QDEC_F32)
         self.cfg = qdec.make_config(shape.hidden, shape.n_layer, shape.n_q_head, shape.n_kv_head, shape.head_dim,
-                                    shape.ffn, shape.vocab, shape.rms_eps, shape.rope_theta, bf16=bf16)
+                                    shape.ffn, shape.vocab, shape.rms_eps, shape.rope_theta, weight_dtype=dtype)
         self.stream = torch.cuda.current_stream(self.device).cuda_stream
         self.handle = qdec.qdec_create(self.cfg, self.table.c, self.stream)
-        # packed copies now live inside the library; keep only the tied embedding
+        # packed copies now live inside the library; keep only a borrowed
+        # embedding (Q8_0 embeddings are unpacked into the library's copies)
         for name in list(self.tensors):
-            if name != "embed":
+            if name != "embed" or q8:
                 del self.tensors[name]
         torch.cuda.synchronize(self.device)
 

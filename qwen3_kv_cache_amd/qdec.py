@@ -27,6 +27,7 @@ QDEC_E_DEVICE = -6
 
 QDEC_F32 = 0
 QDEC_BF16 = 1
+QDEC_Q8_0 = 2
 QDEC_PAGE = 16
 
 (QDEC_W_IN_NORM, QDEC_W_Q, QDEC_W_K, QDEC_W_V, QDEC_W_Q_NORM, QDEC_W_K_NORM, QDEC_W_O,
@@ -265,9 +266,12 @@ def qdec_model_status(model: int) -> None:
 # ---------------------------------------------------------------- helpers
 
 def make_config(hidden, n_layer, n_q_head, n_kv_head, head_dim, ffn, vocab, rms_eps=1e-6, rope_theta=1e6,
-                bf16=True, tied=1) -> qdec_config:
+                bf16=True, tied=1, weight_dtype=None) -> qdec_config:
+    """weight_dtype (QDEC_F32, QDEC_BF16, QDEC_Q8_0) overrides `bf16` when given."""
+    if weight_dtype is None:
+        weight_dtype = QDEC_BF16 if bf16 else QDEC_F32
     return qdec_config(n_layer, hidden, n_q_head, n_kv_head, head_dim, ffn, vocab, rms_eps, rope_theta,
-                       QDEC_BF16 if bf16 else QDEC_F32, tied)
+                       weight_dtype, tied)
 
 
 class WeightTable:

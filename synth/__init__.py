@@ -241,3 +241,81 @@ def random_rows(seed: int, n: int, width: int) -> np.ndarray:
 
 def custom_shape(**kw) -> ModelShape:
     return dataclasses.replace(TINY, **kw)
+
+
+# ------------------------------------------------------------------ Q8_0
+
+# The matrices a Q8_0 weight set stores as blocks (norm gains and the tied
+# embedding stay bf16).
+Q8_MATRICES = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
+Q8_BLOCK = 32          # inputs per block
+Q8_BLOCK_BYTES = 34    # fp16 scale, then 32 int8 codes
+
+
+class Q8Weights:
+    """A Q8_0 weight set. ``codes[name]`` int8 [out, in] and ``scales[name]``
+    float16 [out, in / 32] for the embedding ("embed") and the seven matrices
+    of each layer, ``blocks[name]`` the same data as bytes, one row of in / 32
+    blocks of 34 bytes each (the block's fp16 scale, then its 32 codes);
+    ``base`` is the weight set of the same seed whose norm gains (float32
+    values) the Q8_0 set shares."""
+
+    def __init__(self, base: Weights, codes, scales, blocks):
+        self.shape = base.shape
+        self.base = base
+        self.codes = codes
+        self.scales = scales
+        self.blocks = blocks
+
+    def abi_arrays(self) -> Dict[str, np.ndarray]:
+        """The mapping the C ABI takes for Q8_0: blocks for the matrices and
+        the embedding, float32 norm gains."""
+        out = dict(self.blocks)
+        for name in self.base.names():
+            if name not in out:
+                out[name] = self.base.f32[name]
+        return out
+
+
+def pack_q8_blocks(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Byte layout of Q8_0 rows: block b of a row is scales[:, b] (fp16, little
+    endian) followed by codes[:, 32 b : 32 b + 32]."""
+    out, n = codes.shape
+    nb = n // Q8_BLOCK
+    blk = np.empty((out, nb, Q8_BLOCK_BYTES), np.uint8)
+    blk[:, :, :2] = np.ascontiguousarray(scales.astype("<f2")).view(np.uint8).reshape(out, nb, 2)
+    blk[:, :, 2:] = codes.reshape(out, nb, Q8_BLOCK).view(np.uint8)
+    return blk.reshape(out, nb * Q8_BLOCK_BYTES)
+
+
+_Q8_CACHE: Dict[tuple, Q8Weights] = {}
+
+
+def make_q8_weights(shape: ModelShape, seed_id: int) -> Q8Weights:
+    """Draw a Q8_0 weight set (stream 5): for the embedding, then each layer's
+    matrices in order, codes
+    clip(rint(8 N(0, 1)), -127, 127) (a bell with standard deviation about 8),
+    1% of them replaced by uniform codes over [-127, 127] so that every code
+    value occurs, and per-block fp16 scales 0.002 U(0.8, 1.2), so the weights
+    q d have a standard deviation near 0.022, like the bf16 sets' 0.02. No
+    quantizer is involved: codes and scales are the drawn data."""
+    key = (shape, seed_id)
+    if key in _Q8_CACHE:
+        return _Q8_CACHE[key]
+    base = make_weights(shape, seed_id)
+    rng = _rng(seed_id, 5)
+    shp = layer_shapes(shape)
+    order = [("embed", (shape.vocab, shape.hidden))]
+    order += [(f"L{i}.{t}", shp[t]) for i in range(shape.n_layer) for t in Q8_MATRICES]
+    codes, scales, blocks = {}, {}, {}
+    for name, (out, n) in order:
+        g = rng.standard_normal((out, n), dtype=np.float32)
+        q = np.clip(np.rint(np.float32(8.0) * g), -127, 127).astype(np.int8)
+        wide = np.flatnonzero(rng.random((out, n), dtype=np.float32) < np.float32(0.01))
+        q.reshape(-1)[wide] = rng.integers(-127, 128, size=wide.size).astype(np.int8)
+        d = (np.float32(0.002) * rng.uniform(0.8, 1.2, size=(out, n // Q8_BLOCK))).astype(np.float16)
+        codes[name], scales[name] = q, d
+        blocks[name] = pack_q8_blocks(q, d)
+    out_w = Q8Weights(base, codes, scales, blocks)
+    _Q8_CACHE[key] = out_w
+    return out_w

@@ -68,6 +68,23 @@ def test_create_rejects_bad_config(kw):
     assert qdec.qdec_last_error()
 
 
+def test_create_rejects_q8_with_ffn_not_whole_blocks():
+    # Q8_0 weights: each of the down projection's 8 input slices must be whole
+    # 32-input blocks, so ffn must be a multiple of 256 (384 is not)
+    cfg = good_cfg(ffn=384)
+    cfg.weight_dtype = qdec.QDEC_Q8_0
+    table = qdec.WeightTable(0, 0, [[0] * qdec.QDEC_W_PER_LAYER] * 2)
+    with pytest.raises(qdec.QdecError) as e:
+        qdec.qdec_create(cfg, table.c, 0)
+    assert e.value.code == qdec.QDEC_E_INVALID and "Q8_0" in qdec.qdec_last_error()
+    # with ffn 512 the config passes and the null weights are what is rejected
+    cfg = good_cfg(ffn=512)
+    cfg.weight_dtype = qdec.QDEC_Q8_0
+    with pytest.raises(qdec.QdecError) as e:
+        qdec.qdec_create(cfg, table.c, 0)
+    assert e.value.code == qdec.QDEC_E_INVALID and "weights" in qdec.qdec_last_error()
+
+
 def test_create_rejects_bad_dtype_and_null_weights():
     cfg = good_cfg()
     cfg.weight_dtype = 7

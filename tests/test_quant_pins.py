@@ -126,3 +126,41 @@ def test_pins_catch_planted_rounding_mistakes():
                 pin()
     finally:
         quantize = original
+
+
+def test_block_bytes_hand_example():
+    # one row of two blocks: d = 1.0 (fp16 0x3C00) over codes 0..31, then
+    # d = -0.5 (fp16 0xB800) over codes -1, -128 + 1, 127, 0, ...; bytes are
+    # the scale little-endian, then the codes as two's complement bytes
+    import synth
+    q = np.zeros((1, 2 * BLOCK), np.int8)
+    q[0, :BLOCK] = np.arange(BLOCK)
+    q[0, BLOCK:BLOCK + 3] = [-1, -127, 127]
+    d = np.array([[1.0, -0.5]], np.float16)
+    b = synth.pack_q8_blocks(q, d)
+    assert b.dtype == np.uint8 and b.shape == (1, 2 * synth.Q8_BLOCK_BYTES)
+    assert b[0, :2].tolist() == [0x00, 0x3C]
+    assert b[0, 2:34].tolist() == list(range(BLOCK))
+    assert b[0, 34:36].tolist() == [0x00, 0xB8]
+    assert b[0, 36:39].tolist() == [0xFF, 0x81, 0x7F]
+    assert np.all(b[0, 39:] == 0)
+
+
+def test_blocks_parse_back_and_dequantize_to_the_product():
+    # reading the bytes back (scale, then codes, per 34-byte block) recovers
+    # the codes and scales, and the oracle's weights are q * d elementwise
+    import synth
+    Q = synth.make_q8_weights(synth.custom_shape(hidden=128, n_layer=1, n_q_head=2, n_kv_head=1, head_dim=64,
+                                                 ffn=256, vocab=50), 3)
+    for name in ("embed", "L0.wo", "L0.w_down"):
+        q, d, b = Q.codes[name], Q.scales[name], Q.blocks[name]
+        out, n = q.shape
+        blk = b.reshape(out, n // BLOCK, 34)
+        d_back = blk[:, :, :2].copy().view("<f2").reshape(out, n // BLOCK)
+        q_back = blk[:, :, 2:].copy().view(np.int8).reshape(out, n)
+        np.testing.assert_array_equal(d_back, d)
+        np.testing.assert_array_equal(q_back, q)
+        w = dequantize(q_back, d_back)
+        for r, c in [(0, 0), (out - 1, n - 1), (out // 2, 37)]:
+            assert w[r, c] == np.float32(q[r, c]) * np.float32(d[r, c // BLOCK])
+    assert all(float(Q.scales[k].min()) > 0 for k in Q.scales)
