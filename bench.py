@@ -12,8 +12,9 @@ before the timed region.
 
 The default run also reports, under "other_workloads", the rest of the
 metric with the same weights and fewer repetitions: B=16 batched decode of
-16 clones of a 512-token prefill (branch16), and the 1024- and 8192-token
-prompts (long, prefill8k); under "sampling" the time of one sampling step
+16 clones of a 512-token prefill (branch16), the 1024- and 8192-token
+prompts (long, prefill8k), and the default workload on Q8_0 weights of the
+same shape (short_q8_0); under "sampling" the time of one sampling step
 (qdec_sample) over 1 and 16 rows of logits; and under "adaptor" the audio
 adaptor that makes the audio rows (qdec_adaptor_run) at 183 and 6000 encoder
 frames. --no-others skips them.
@@ -50,6 +51,20 @@ def decode_bytes(shape, ctx_lens) -> float:
     head = shape.vocab * H * 2
     kv_row = 2 * shape.n_kv_head * D * 4
     w = L * (layer_w + norms) + head + H * 2
+    return float(np.mean([w + L * kv_row * p + L * kv_row for p in ctx_lens]))
+
+
+def decode_bytes_q8(shape, ctx_lens) -> float:
+    """The same byte model for Q8_0 weights: every matrix weight (layers and
+    the tied head) at 34/32 bytes, its int8 code and its share of the block's
+    fp16 scale; fp32 norm gains; the embedding row as Q8_0 blocks."""
+    H, L, D = shape.hidden, shape.n_layer, shape.head_dim
+    q8 = 34.0 / 32.0
+    layer_w = (shape.n_q_head * D * H + 2 * shape.n_kv_head * D * H + H * shape.n_q_head * D + 3 * shape.ffn * H) * q8
+    norms = (2 * H + 2 * D) * 4
+    head = shape.vocab * H * q8
+    kv_row = 2 * shape.n_kv_head * D * 4
+    w = L * (layer_w + norms) + head + H * q8
     return float(np.mean([w + L * kv_row * p + L * kv_row for p in ctx_lens]))
 
 
@@ -540,6 +555,8 @@ def main():
     ap.add_argument("--trace", action="store_true",
                     help="per-phase time of a decode step from the diagnostic build libqdec_trace.so "
                          "(python -m qwen3_kv_cache_amd.build --trace)")
+    ap.add_argument("--q8", action="store_true",
+                    help="the main measurement on Q8_0 weights (int8 codes, fp16 block scales) of the same shape")
     ap.add_argument("--per-step", action="store_true",
                     help="decode with one launch per token (qdec_decode_step_dev) instead of one launch for all steps")
     ap.add_argument("--profile-summary", choices=("stats", "traffic"),
@@ -574,7 +591,10 @@ def main():
     w = synth.WORKLOADS[a.workload]
     dev = torch.device("cuda:0")
     W = synth.make_weights(w.shape, w.weight_seed)
-    model = Model(w.shape, W.bits if w.shape.bf16 else W.f32, bf16=w.shape.bf16)
+    if a.q8:
+        model = Model(w.shape, synth.make_q8_weights(w.shape, w.weight_seed).abi_arrays(), bf16=False, q8=True)
+    else:
+        model = Model(w.shape, W.bits if w.shape.bf16 else W.f32, bf16=w.shape.bf16)
     if a.trace:
         res = decode_trace(w, model)
         model.close()
@@ -591,7 +611,7 @@ def main():
     decode_tok_s = n * B * a.steps / (dec_ms.sum() / 1e3)
     prefill_tok_s = w.prompt_len * a.steps / (pre_ms.sum() / 1e3)
     ctx = [w.prompt_len + s + 1 for s in range(n)]
-    bytes_tok = decode_bytes(w.shape, ctx)
+    bytes_tok = (decode_bytes_q8 if a.q8 else decode_bytes)(w.shape, ctx)
     per_tok_s = dec_ms.mean() / 1e3 / n
     achieved = bytes_tok / per_tok_s / 1e9 if B == 1 else None
     line = {
@@ -605,7 +625,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 weights, fp32 activations/KV",
+        "dtype": ("Q8_0 weights (int8 codes, fp16 block scales)" if a.q8 else "bf16 weights")
+                 + ", fp32 activations/KV",
         "data": "synthetic (seeded random-init weights of the Qwen3-0.6B shape, uniform ids, N(0,1) audio rows)",
         "config": {"workload": f"{w.name}: Qwen3-0.6B shape, {w.prompt_len}-token prompt with {w.audio_len} audio rows, "
                                f"prefill then {n} greedy decode steps" + (f" x {B} cloned branches" if B > 1 else ", B=1"),
@@ -617,12 +638,12 @@ def main():
     }
     if achieved is not None:
         # counters were taken on the short workload's 64-step launch
-        traffic = counter_traffic() if (w.name == "short" and not a.per_step) else None
+        traffic = counter_traffic() if (w.name == "short" and not a.per_step and not a.q8) else None
         line["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                             "kernel": "decode_kernel (%d steps per launch)" % (1 if a.per_step else n),
                             "bytes_per_unit": round(bytes_tok)}
-    if a.workload == "short" and not a.no_others:
+    if a.workload == "short" and not a.no_others and not a.q8:
         # the rest of the metric (B=16 decode, prefill of long prompts), same
         # weights, fewer repetitions
         others = {}
@@ -636,10 +657,26 @@ def main():
                             "prefill_ms": round(float(p_ms.mean()), 3),
                             "prefill_mfma": prefill_mfma(wo.shape, wo.prompt_len, float(p_ms.mean()), name),
                             "decode_roofline": decode_roofline(wo.shape, wo, float(d_ms.mean()))}
+        # the short workload on Q8_0 weights of the same shape and seed: the
+        # decode kernel streams int8 codes and fp16 scales; prefill runs on the
+        # exactly dequantized fp32 weights
+        Q = synth.make_q8_weights(w.shape, w.weight_seed)
+        m8 = Model(w.shape, Q.abi_arrays(), bf16=False, q8=True)
+        p_ms, d_ms, _ = measure(w, m8, 3, 1)
+        m8.close()
+        t_tok = float(d_ms.mean()) / 1e3 / n
+        b8 = decode_bytes_q8(w.shape, ctx)
+        others["short_q8_0"] = {"decode_tok_s": round(n * len(d_ms) / (d_ms.sum() / 1e3), 1), "batch": 1,
+                                "prompt_len": w.prompt_len, "decode_steps": n,
+                                "decode_ms_per_token": round(t_tok * 1e3, 5),
+                                "prefill_tok_s": round(w.prompt_len * len(p_ms) / (p_ms.sum() / 1e3), 1),
+                                "decode_roofline": {"bytes_per_step": round(b8), "achieved": round(b8 / t_tok / 1e9, 1),
+                                                    "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                                    "frac": round(b8 / t_tok / 1e9 / HBM_PEAK_GBS, 4)}}
         line["other_workloads"] = others
         line["sampling"] = measure_sampling(model, w.shape.vocab)
         line["adaptor"] = measure_adaptor()
-    if a.cpu_sample > 0:
+    if a.cpu_sample > 0 and not a.q8:
         line["cpu_baseline"] = cpu_baseline(w, W, a.cpu_sample)
     model.close()
     print(json.dumps(line), flush=True)

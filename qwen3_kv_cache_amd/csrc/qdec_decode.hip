@@ -86,6 +86,7 @@ enum { PH_Q = 0, PH_ATT = 1, PH_O = 2, PH_Z = 3, PH_X = 4, PH_KEY = 5, PH_OS = 6
 constexpr int kSlots = 12;
 constexpr int kSlotBytes = kWave * 16;
 constexpr int kMaxK = 1024;  // longest GEMV input: max(hidden, G * D, ffn / 8)
+constexpr int kLayerRes = 4 * kSlots;  // row totals of one layer unit (up to 4 packed rows per slot)
 constexpr int kPtabLds = kDecMaxPos / kPage;  // KV page pointers kept in LDS
 
 __device__ __forceinline__ u64 now() { return __builtin_amdgcn_s_memrealtime(); }
@@ -270,6 +271,79 @@ __device__ __forceinline__ void reduce12_store(const float (&s)[kSlots], float* 
   }
 }
 
+// Four and eight 64-lane sums, the same steps as the first slots of
+// reduce12_store: slot q's total goes to dst[q].
+__device__ __forceinline__ void reduce8_store(const float (&s)[8], float* dst, int lane) {
+  const float p0 = pair32(s[0], s[1]), p1 = pair32(s[2], s[3]);
+  const float p2 = pair32(s[4], s[5]), p3 = pair32(s[6], s[7]);
+  const float q01 = pair16(p0, p1), q23 = pair16(p2, p3);
+  const float t = q01 + dpp<kDppXor8>(q01), u = q23 + dpp<kDppXor8>(q23);
+  float r8 = (lane & 8) ? u : t;
+  r8 += dpp<kDppXor1>(r8);
+  r8 += dpp<kDppXor2>(r8);
+  r8 += dpp<kDppHalfMirror>(r8);
+  if ((lane & 7) == 0) {
+    const int g = lane >> 3;
+    dst[((g & 1) << 2) | (((g >> 1) & 1) << 1) | (g >> 2)] = r8;
+  }
+}
+__device__ __forceinline__ void reduce4_store(const float (&s)[4], float* dst, int lane) {
+  const float p0 = pair32(s[0], s[1]), p1 = pair32(s[2], s[3]);
+  float r = pair16(p0, p1);  // 16-lane rows: slots 0, 2, 1, 3
+  r += dpp<kDppXor1>(r);
+  r += dpp<kDppXor2>(r);
+  r += dpp<kDppHalfMirror>(r);
+  r += dpp<kDppMirror>(r);
+  if ((lane & 15) == 0) {
+    const int w = lane >> 4;
+    dst[((w & 1) << 1) | (w >> 1)] = r;
+  }
+}
+// Sums over the 8-lane groups of two registers a and b whose 16-lane rows
+// each hold partials of one result, a's row R in lanes 8 R' .. with the sum
+// of lanes i and i ^ 8 taken first: lane group G = lane / 8 ends with the
+// total of row G / 2 of a (G even) or of b (G odd); lane 8 G writes it to
+// dst[idx(G)].
+template <typename Idx>
+__device__ __forceinline__ void reduce_rows2(float a, float b, float* dst, int lane, Idx idx) {
+  const float t = a + dpp<kDppXor8>(a), u = b + dpp<kDppXor8>(b);
+  float r = (lane & 8) ? u : t;
+  r += dpp<kDppXor1>(r);
+  r += dpp<kDppXor2>(r);
+  r += dpp<kDppHalfMirror>(r);
+  if ((lane & 7) == 0) dst[idx(lane >> 3)] = r;
+}
+// Slot sums for NS slots of one unit. PK = 0: one row per slot, dst[q].
+// PK = 1: lanes 0-31 and 32-63 of slot q are rows 2q and 2q + 1. PK = 2: the
+// 16-lane rows of slot q are rows 4q .. 4q + 3. Row i's total goes to dst[i].
+template <int PK, int NS>
+__device__ __forceinline__ void reduce_store(const float (&s)[NS], float* dst, int lane) {
+  if constexpr (PK == 0) {
+    if constexpr (NS == 12) {
+      reduce12_store(s, dst, lane);
+    } else if constexpr (NS == 8) {
+      reduce8_store(s, dst, lane);
+    } else {
+      reduce4_store(s, dst, lane);
+    }
+  } else if constexpr (PK == 1) {
+    // v_k = pair16(s[2k], s[2k+1]): 16-lane rows hold slot 2k row 0, slot
+    // 2k+1 row 0, slot 2k row 1, slot 2k+1 row 1 (each half-summed)
+#pragma unroll
+    for (int m = 0; m < NS / 4; ++m) {
+      const float v0 = pair16(s[4 * m], s[4 * m + 1]), v1 = pair16(s[4 * m + 2], s[4 * m + 3]);
+      reduce_rows2(v0, v1, dst, lane, [m](int G) {
+        const int R = G >> 1, slot = 4 * m + 2 * (G & 1) + (R & 1);
+        return 2 * slot + (R >> 1);
+      });
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < NS / 2; ++m)
+      reduce_rows2(s[2 * m], s[2 * m + 1], dst, lane, [m](int G) { return 4 * (2 * m + (G & 1)) + (G >> 1); });
+  }
+}
+
 __device__ __forceinline__ u64 argmax_key(float v, int idx) {
   uint32_t u = __float_as_uint(v);
   uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -297,6 +371,13 @@ __host__ __device__ __forceinline__ int chunk_lg(int k, int vn) {
   const int nch = k / vn;
   const int cpl = (nch + kWave - 1) / kWave;
   return cpl <= 1 ? 0 : cpl <= 2 ? 1 : cpl <= 4 ? 2 : 3;
+}
+// log2 of the rows packed per slot for rows of k elements (chunks of vn)
+// whose consecutive rows sit a fixed stride apart: as many as fit 64 lanes
+// whole, at most 4
+__host__ __device__ __forceinline__ int pack_lg(int k, int vn) {
+  const int nch = k / vn;
+  return nch <= 16 ? 2 : nch <= 32 ? 1 : 0;
 }
 
 struct DecParams {
@@ -572,21 +653,32 @@ struct Ring {
   char* s1;          // 64 bytes per slot (the 32 fp16 scales of the slot's row)
 };
 
+// Rows of a unit packed into one slot when they are short: with pk > 0 a
+// slot holds 2^pk consecutive rows of the unit (rows `rstride` bytes apart),
+// lane l serving row l >> (6 - pk) and its chunk l & (2^(6 - pk) - 1); rows
+// past the unit's nrw repeat its last row.
+struct Pack {
+  int pk, nrw, rstride;
+};
+
 // Issue one unit into region P: slot q (q < ns) holds chunk c = lane + 64 (q & (2^lg - 1))
 // (clamped to the row's last chunk) of the row starting ro(q) bytes after
-// `base`, where ro(q) is lane q of `tab`. Int8 weights (Q8) add one load of
-// the unit's scales: lane 4 q + i (q < ns) brings the 16 bytes at sbase + soff,
-// the i-th quarter of slot q's 64 scale bytes.
+// `base`, where ro(q) is lane q of `tab` (packed: of the slot's first row).
+// Int8 weights (Q8) add one load of the unit's scales: lane 4 q + i (q < ns)
+// brings the 16 bytes at sbase + soff, the i-th quarter of slot q's 64
+// scale bytes.
 template <int P, bool Q8>
 __device__ __forceinline__ void issue_unit(Ring& rg, const char* base, int tab, int ns, int lg, int nchm1,
-                                           int lane, const char* sbase, int soff) {
+                                           int lane, const char* sbase, int soff, Pack pkd) {
   char* region = P ? rg.r1 : rg.r0;
   const int jm = (1 << lg) - 1;
+  const int gl = pkd.pk ? lane >> (6 - pkd.pk) : 0;
+  const int cl = pkd.pk ? lane & ((kWave >> pkd.pk) - 1) : lane;
 #pragma unroll
   for (int q = 0; q < kSlots; ++q) {
     if (q < ns) {
-      const int ro = __builtin_amdgcn_readlane(tab, q);
-      const int c = min(lane + ((q & jm) << 6), nchm1);
+      const int ro = __builtin_amdgcn_readlane(tab, q) + min(gl, max(pkd.nrw - 1 - (q << pkd.pk), 0)) * pkd.rstride;
+      const int c = min(cl + ((q & jm) << 6), nchm1);
       __builtin_amdgcn_global_load_lds((const void*)(base + ro + c * 16), (lds_void*)(region + q * kSlotBytes), 16,
                                        0, 0);
     }
@@ -607,37 +699,41 @@ __device__ __forceinline__ void issue_unit(Ring& rg, const char* base, int tab, 
 // the unit's count hold stale data whose results nobody reads): slot q's
 // chunk times this lane's input chunk (q & (2^LG - 1)), summed over the wave.
 // The input must be zero past the GEMV's length up to 64 * VN * 2^LG.
-template <int P, int LG, typename WT>
+template <int P, int LG, int PK, int NS, typename WT>
 __device__ __forceinline__ void dot_unit(const Ring& rg, const float* xin, float* dst, int lane) {
   constexpr int VN = 16 / sizeof(WT);
   constexpr int CPL = 1 << LG;
+  static_assert(PK == 0 || LG == 0, "packed rows are one chunk row long");
   const char* region = P ? rg.r1 : rg.r0;
+  const int xl = PK ? lane & ((kWave >> PK) - 1) : lane;  // this lane's input chunk
   float xr[CPL][VN];
 #pragma unroll
   for (int jj = 0; jj < CPL; ++jj)
 #pragma unroll
     for (int e = 0; e < VN; e += 4) {
-      const float4 t = *reinterpret_cast<const float4*>(xin + (lane + kWave * jj) * VN + e);
+      const float4 t = *reinterpret_cast<const float4*>(xin + (xl + kWave * jj) * VN + e);
       xr[jj][e] = t.x;
       xr[jj][e + 1] = t.y;
       xr[jj][e + 2] = t.z;
       xr[jj][e + 3] = t.w;
     }
-  u32x4 raw[kSlots];
+  u32x4 raw[NS];
 #pragma unroll
-  for (int q = 0; q < kSlots; ++q) raw[q] = *reinterpret_cast<const u32x4*>(region + q * kSlotBytes + lane * 16);
-  float s[kSlots];
+  for (int q = 0; q < NS; ++q) raw[q] = *reinterpret_cast<const u32x4*>(region + q * kSlotBytes + lane * 16);
+  float s[NS];
 #pragma unroll
-  for (int q = 0; q < kSlots; ++q) s[q] = dot_chunk<WT>(raw[q], xr[q & (CPL - 1)]);
+  for (int q = 0; q < NS; ++q) s[q] = dot_chunk<WT>(raw[q], xr[q & (CPL - 1)]);
   if constexpr (kIsQ8<WT>) {
-    // one chunk row per row (LG 0): lane l holds codes [16 l, 16 l + 16),
-    // block l / 2 of the slot's row
+    // one chunk row per row (LG 0): lane l holds the codes of block l / 2 of
+    // its row's 32 (its packed row's 64 / 2^PK bytes of scales start at
+    // 64 / 2^PK times the row's index in the slot, so the lane's scale sits
+    // at 2 (l / 2) for every PK)
     static_assert(LG == 0, "int8 rows of up to 1024 inputs fill one chunk row");
     const unsigned short* sc = reinterpret_cast<const unsigned short*>(P ? rg.s1 : rg.s0) + (lane >> 1);
 #pragma unroll
-    for (int q = 0; q < kSlots; ++q) s[q] *= half_bits(sc[q * 32]);
+    for (int q = 0; q < NS; ++q) s[q] *= half_bits(sc[q * 32]);
   }
-  reduce12_store(s, dst, lane);
+  reduce_store<PK, NS>(s, dst, lane);
 }
 
 template <int P>
@@ -645,16 +741,32 @@ __device__ __forceinline__ void ring_wait(const Ring& rg) {
   wait_vm(rg.issued - (P ? rg.mark1 : rg.mark0));
 }
 
+// Only the slots a unit fills are summed: ns rounded up to 4, 8 or 12.
+template <int P, int LG, int PK, typename WT>
+__device__ __forceinline__ void consume_ns(const Ring& rg, int ns, const float* xin, float* dst, int lane) {
+  if (ns <= 4)
+    dot_unit<P, LG, PK, 4, WT>(rg, xin, dst, lane);
+  else if (ns <= 8)
+    dot_unit<P, LG, PK, 8, WT>(rg, xin, dst, lane);
+  else
+    dot_unit<P, LG, PK, 12, WT>(rg, xin, dst, lane);
+}
 template <int P, typename WT>
-__device__ __forceinline__ void consume_unit(const Ring& rg, int lg, const float* xin, float* dst, int lane) {
-  if constexpr (kIsQ8<WT>) {
-    dot_unit<P, 0, WT>(rg, xin, dst, lane);
-  } else if (lg == 0) {
-    dot_unit<P, 0, WT>(rg, xin, dst, lane);
-  } else if (sizeof(WT) == 2 || lg == 1) {
-    dot_unit<P, 1, WT>(rg, xin, dst, lane);
+__device__ __forceinline__ void consume_unit(const Ring& rg, int lg, int pk, int ns, const float* xin, float* dst,
+                                             int lane) {
+  if (pk == 2) {
+    consume_ns<P, 0, 2, WT>(rg, ns, xin, dst, lane);
+  } else if (pk == 1) {
+    consume_ns<P, 0, 1, WT>(rg, ns, xin, dst, lane);
+  } else if constexpr (kIsQ8<WT>) {
+    consume_ns<P, 0, 0, WT>(rg, ns, xin, dst, lane);
   } else {
-    dot_unit<P, (sizeof(WT) == 2 ? 1 : 2), WT>(rg, xin, dst, lane);
+    if (lg == 0)
+      consume_ns<P, 0, 0, WT>(rg, ns, xin, dst, lane);
+    else if (sizeof(WT) == 2 || lg == 1)
+      consume_ns<P, 1, 0, WT>(rg, ns, xin, dst, lane);
+    else
+      consume_ns<P, (sizeof(WT) == 2 ? 1 : 2), 0, WT>(rg, ns, xin, dst, lane);
   }
 }
 
@@ -966,28 +1078,36 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
     // last chunk, and lane q of tab = byte offset of slot q's row from the matrix base
     const Job jobs[4] = {Job{H, 0, H, a1 - a0, 1, a0}, Job{NQ * D, X * QD, QD, c1 - c0, 0, c0},
                          Job{H, 0, H, 2 * (z1 - z0), 2, X * FS + z0}, Job{F, X * FS, FS, e1 - e0, 0, e0}};
-    // int8 weights: lane 4 q + i of stab = byte offset (from the job's scale
-    // base) of the i-th 16 bytes of slot q's row segment of scales
-    int tab[4], ns[4], lgs[4], nchm1[4], stab[4];
+    // Short rows of the linear jobs (C, E) are packed 2^pk to a slot. Lane q
+    // of tab = byte offset of slot q's (first) row. Int8 weights: lane 4 q + i
+    // of stab = byte offset (from the job's scale base) of the i-th 16 bytes
+    // of slot q's 64 scale bytes (2^pk row segments of 64 / 2^pk bytes).
+    int tab[4], ns[4], lgs[4], nchm1[4], stab[4], pkl[4], nrws[4], rstr[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const Job& jb = jobs[t];
       const int lg = chunk_lg(jb.K, VN);
+      const int pk = (jb.kind == 0 && lg == 0) ? pack_lg(jb.K, VN) : 0;
       const int nrw = jb.nrows > w ? (jb.nrows - w + kMemWaves - 1) / kMemWaves : 0;
+      const int nsl = pk ? (nrw + (1 << pk) - 1) >> pk : nrw << lg;
       lgs[t] = lg;
-      ns[t] = __builtin_amdgcn_readfirstlane(nrw << lg);
+      ns[t] = __builtin_amdgcn_readfirstlane(nsl);
       nchm1[t] = jb.K / VN - 1;
+      pkl[t] = pk;
+      nrws[t] = nrw;
+      rstr[t] = kMemWaves * jb.ld * ES;
       int ro = 0;
-      if (lane < (nrw << lg)) {
-        const int j = w + kMemWaves * (lane >> lg);
+      if (lane < nsl) {
+        const int j = w + kMemWaves * (pk ? lane << pk : lane >> lg);
         ro = (jb.phys(j, QD, D, NQ * D, NKV * D, X) * jb.ld + jb.col0) * ES;
       }
       tab[t] = ro;
       int so = 0;
-      if (Q8 && lane < 4 * nrw) {
-        const int j = w + kMemWaves * (lane >> 2);
-        const int ph = jb.phys(j, QD, D, NQ * D, NKV * D, X);
-        so = (ph * (jb.ld / jb.K) + jb.col0 / jb.K) * q8_seg_bytes(jb.K) + 16 * (lane & 3);
+      if (Q8 && lane < 4 * nsl) {
+        const int q = lane >> 2, i = lane & 3;
+        const int row = min((q << pk) + ((i << pk) >> 2), nrw - 1);
+        const int ph = jb.phys(w + kMemWaves * row, QD, D, NQ * D, NKV * D, X);
+        so = (ph * (jb.ld / jb.K) + jb.col0 / jb.K) * q8_seg_bytes(jb.K) + ((16 * i) & ((64 >> pk) - 1));
       }
       stab[t] = so;
     }
@@ -1016,7 +1136,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
         const char* base = wbase + ((size_t)l * p.layer_elems + toff) * ES;
         const int so = t == 0 ? stab[0] : t == 1 ? stab[1] : t == 2 ? stab[2] : stab[3];
         const size_t stoff = t == 0 ? 0 : t == 1 ? p.soff_o : t == 2 ? p.soff_gu : p.soff_d;
-        issue_unit<P, Q8>(rg, base, tb, n, lg, cm, ml, wsbase + (size_t)l * p.layer_sbytes + stoff, so);
+        const Pack pkd{t == 0 ? pkl[0] : t == 1 ? pkl[1] : t == 2 ? pkl[2] : pkl[3],
+                       t == 0 ? nrws[0] : t == 1 ? nrws[1] : t == 2 ? nrws[2] : nrws[3],
+                       t == 0 ? rstr[0] : t == 1 ? rstr[1] : t == 2 ? rstr[2] : rstr[3]};
+        issue_unit<P, Q8>(rg, base, tb, n, lg, cm, ml, wsbase + (size_t)l * p.layer_sbytes + stoff, so, pkd);
       } else {
         const int u = k - nlu;
         const int i0 = u * rpbH;  // first local head row of the unit
@@ -1025,13 +1148,29 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
         const int ro = (h0 + w + kMemWaves * (i0 + (ml >> lgH))) * rowH;
         // int8: one chunk row per head row, so scale lane 4 q + i serves row q
         const int so = Q8 ? (h0 + w + kMemWaves * (i0 + (ml >> 2))) * spH + 16 * (ml & 3) : 0;
-        issue_unit<P, Q8>(rg, ebase, ro, __builtin_amdgcn_readfirstlane(n << lgH), lgH, nchH, ml, esbase, so);
+        issue_unit<P, Q8>(rg, ebase, ro, __builtin_amdgcn_readfirstlane(n << lgH), lgH, nchH, ml, esbase, so,
+                          Pack{0, 0, 0});
       }
     };
+    // chunk rows per row, rows per slot and slots of unit k
     auto unit_lg = [&](int k) __attribute__((always_inline)) {
       if (k >= nlu) return lgH;
       const int t = k % per_layer + (has_att ? 0 : 2);
       return t == 0 ? lgs[0] : t == 1 ? lgs[1] : t == 2 ? lgs[2] : lgs[3];
+    };
+    auto unit_pk = [&](int k) __attribute__((always_inline)) {
+      if (k >= nlu) return 0;
+      const int t = k % per_layer + (has_att ? 0 : 2);
+      return t == 0 ? pkl[0] : t == 1 ? pkl[1] : t == 2 ? pkl[2] : pkl[3];
+    };
+    auto unit_ns = [&](int k) __attribute__((always_inline)) {
+      if (k >= nlu) {
+        const int i0 = (k - nlu) * rpbH;
+        const int n = nrwH - i0;
+        return (n < 0 ? 0 : (n > rpbH ? rpbH : n)) << lgH;
+      }
+      const int t = k % per_layer + (has_att ? 0 : 2);
+      return t == 0 ? ns[0] : t == 1 ? ns[1] : t == 2 ? ns[2] : ns[3];
     };
 
     if (p.nsteps > 0) issue(std::integral_constant<int, 0>{}, 0);
@@ -1044,8 +1183,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
         const bool head = k >= nlu;
         MTRACE(k, 0);
         if (!head || k == nlu) bar();  // input ready
-        float* dst = sbuf + (head ? (w * NHU + (k - nlu)) * kSlots : w * kSlots);
-        const int lg = unit_lg(k);
+        float* dst = sbuf + (head ? (w * NHU + (k - nlu)) * kSlots : w * kLayerRes);
+        const int lg = unit_lg(k), pku = unit_pk(k), nsu = __builtin_amdgcn_readfirstlane(unit_ns(k));
         int kk = k + 2, st = step;
         if (kk >= n_units) {
           kk -= n_units;
@@ -1055,7 +1194,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
         if (g & 1) {
           ring_wait<1>(rg);
           MTRACE(k, 2);
-          consume_unit<1, WT>(rg, lg, xin, dst, ml);
+          consume_unit<1, WT>(rg, lg, pku, nsu, xin, dst, ml);
           MTRACE(k, 3);
           if (!head) bar();  // partials ready
           MTRACE(k, 4);
@@ -1063,7 +1202,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
         } else {
           ring_wait<0>(rg);
           MTRACE(k, 2);
-          consume_unit<0, WT>(rg, lg, xin, dst, ml);
+          consume_unit<0, WT>(rg, lg, pku, nsu, xin, dst, ml);
           MTRACE(k, 3);
           if (!head) bar();  // partials ready
           MTRACE(k, 4);
@@ -1145,9 +1284,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
     for (int i = n + et; i < end; i += kEx) xin[i] = 0.f;
   };
   // combined dot of local row j of a layer unit with 2^lg chunk rows per row
+  // (packed units have lg 0: row i's total is entry i)
   auto row_val = [&](int j, int lg) __attribute__((always_inline)) {
     const int w = j & (kMemWaves - 1), i = j >> 2;
-    const float* s = sbuf + w * kSlots + (i << lg);
+    const float* s = sbuf + w * kLayerRes + (i << lg);
     float v = s[0];
     for (int jj = 1; jj < (1 << lg); ++jj) v += s[jj];
     return v;
@@ -1553,7 +1693,7 @@ Layout layout(int wt, const Dims& d, int nsplit_max, int nb) {
   o.stage = 0;
   o.att = o.stage + ((stage + 3) & ~3);
   o.sbuf = o.att + ((att + 3) & ~3);
-  o.ptab = o.sbuf + ((kMemWaves * o.nhu * kSlots + 3) & ~3);
+  o.ptab = o.sbuf + ((std::max(kMemWaves * o.nhu * kSlots, kMemWaves * kLayerRes) + 3) & ~3);
   o.total = o.ptab + 2 * kPtabLds;
   return o;
 }
@@ -1621,15 +1761,18 @@ bool dec_fits(int wt, const Dims& d, int nblocks) {
   const int VN = chunk_elems(wt);
   const int G = d.NQ / d.NKV;
   const int FS = d.F / kGroups;
-  auto fits = [&](int rows_per_block, int K) {
+  // packable: consecutive rows a fixed stride apart (the linear jobs C, E)
+  auto fits = [&](int rows_per_block, int K, bool packable) {
     if (K > kMaxK || K % VN) return false;
     if (wt == QDEC_Q8_0 && K % kQ8Block) return false;
     const int rows_w = (rows_per_block + kMemWaves - 1) / kMemWaves;
-    return (rows_w << chunk_lg(K, VN)) <= kSlots;
+    const int lg = chunk_lg(K, VN);
+    const int pk = (packable && lg == 0) ? pack_lg(K, VN) : 0;
+    return (pk ? (rows_w + (1 << pk) - 1) >> pk : rows_w << lg) <= kSlots;
   };
   auto per = [&](int n) { return (n + R - 1) / R; };
-  return fits(per((G + 2) * d.D), d.H) && fits(per(d.H), G * d.D) && fits(2 * per(FS), d.H) &&
-         fits(per(d.H), FS) && fits(1, d.H);
+  return fits(per((G + 2) * d.D), d.H, false) && fits(per(d.H), G * d.D, true) && fits(2 * per(FS), d.H, false) &&
+         fits(per(d.H), FS, true) && fits(1, d.H, false);
 }
 
 int dec_split_limit(const Dims& d, int nblocks) {
