@@ -226,6 +226,87 @@ def make_adaptor_weights(a: AdaptorShape, seed_id: int):
     return f32, bits
 
 
+@dataclasses.dataclass(frozen=True)
+class EncoderShape:
+    """Sizes of the SAN-M speech encoder (stem, main blocks, tp blocks)."""
+    in_dim: int = 560
+    dim: int = 512
+    n_head: int = 4
+    ffn_dim: int = 2048
+    kernel: int = 11
+    n_main: int = 49
+    n_tp: int = 20
+
+    def block_names(self) -> List[str]:
+        return (["encoders0.0."] + [f"encoders.{i}." for i in range(self.n_main)]
+                + [f"tp_encoders.{i}." for i in range(self.n_tp)])
+
+
+def encoder_params(e: EncoderShape) -> List[tuple]:
+    """(name, shape, kind) in draw order; kind "w" matrix [out, in], "b" bias,
+    "g" LayerNorm gain, "f" FSMN taps [dim, kernel]."""
+    D, F = e.dim, e.ffn_dim
+    out = []
+    for b, p in enumerate(e.block_names()):
+        n_in = e.in_dim if b == 0 else D
+        out += [(p + "norm1.g", (n_in,), "g"), (p + "norm1.b", (n_in,), "b")]
+        for t in ("q", "k", "v"):
+            out += [(p + t + ".w", (D, n_in), "w"), (p + t + ".b", (D,), "b")]
+        out += [(p + "fsmn.w", (D, e.kernel), "f"), (p + "o.w", (D, D), "w"), (p + "o.b", (D,), "b"),
+                (p + "norm2.g", (D,), "g"), (p + "norm2.b", (D,), "b"),
+                (p + "ffn1.w", (F, D), "w"), (p + "ffn1.b", (F,), "b"),
+                (p + "ffn2.w", (D, F), "w"), (p + "ffn2.b", (D,), "b")]
+    out += [("after_norm.g", (D,), "g"), ("after_norm.b", (D,), "b"),
+            ("tp_norm.g", (D,), "g"), ("tp_norm.b", (D,), "b")]
+    return out
+
+
+def make_encoder_weights(e: EncoderShape, seed_id: int):
+    """Encoder parameters from stream 6, in encoder_params order: matrices and
+    biases 0.02 N(0,1), gains 1 + 0.02 N(0,1), FSMN taps 0.1 N(0,1), rounded
+    to bf16. Returns (float32 values, bf16 bit patterns), keyed by name."""
+    rng = _rng(seed_id, 6)
+    f32: Dict[str, np.ndarray] = {}
+    bits: Dict[str, np.ndarray] = {}
+    for name, shp, kind in encoder_params(e):
+        z = rng.standard_normal(shp, dtype=np.float32)
+        if kind == "g":
+            w = np.float32(1.0) + np.float32(0.02) * z
+        else:
+            w = (np.float32(0.1) if kind == "f" else np.float32(0.02)) * z
+        bits[name], f32[name] = _round_bf16(w.astype(np.float32, copy=False))
+    return f32, bits
+
+
+SAMPLE_RATE = 16000
+
+
+def pcm(kind: str, n: int, seed_id: int = 0) -> np.ndarray:
+    """Synthetic 16 kHz PCM float32[n] at 16-bit sample scale: "silence";
+    "impulse" (one sample of 10000 at n // 2); "sine440" (amplitude 8000);
+    "voiced" (stream 7): a harmonic tone whose pitch glides between 100 and
+    250 Hz, five harmonics with 1/h amplitudes, a 4 Hz syllable envelope and
+    white noise, peak about 10000 -- a speech-like spectrum, not speech."""
+    t = np.arange(n, dtype=np.float64) / SAMPLE_RATE
+    if kind == "silence":
+        x = np.zeros(n)
+    elif kind == "impulse":
+        x = np.zeros(n)
+        x[n // 2] = 10000.0
+    elif kind == "sine440":
+        x = 8000.0 * np.sin(2 * np.pi * 440.0 * t)
+    elif kind == "voiced":
+        rng = _rng(seed_id, 7)
+        f0 = 175.0 + 75.0 * np.sin(2 * np.pi * rng.uniform(0.3, 0.8) * t + rng.uniform(0, 2 * np.pi))
+        phase = 2 * np.pi * np.cumsum(f0) / SAMPLE_RATE
+        x = sum(np.sin(h * phase) / h for h in range(1, 6))
+        x *= 0.55 + 0.45 * np.sin(2 * np.pi * 4.0 * t + rng.uniform(0, 2 * np.pi))
+        x = 4000.0 * x + 300.0 * rng.standard_normal(n)
+    else:
+        raise ValueError(kind)
+    return x.astype(np.float32)
+
+
 def encoder_frames(seed_id: int, n: int, width: int) -> np.ndarray:
     """Encoder output frames float32[n, width], N(0,1), stream 4."""
     return _rng(seed_id, 4).standard_normal((n, width), dtype=np.float32)
@@ -245,8 +326,8 @@ def custom_shape(**kw) -> ModelShape:
 
 # ------------------------------------------------------------------ Q8_0
 
-# The matrices a Q8_0 weight set stores as blocks (norm gains and the tied
-# embedding stay bf16).
+# The matrices a Q8_0 weight set stores as blocks, besides the embedding
+# (the norm gains stay float).
 Q8_MATRICES = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
 Q8_BLOCK = 32          # inputs per block
 Q8_BLOCK_BYTES = 34    # fp16 scale, then 32 int8 codes
