@@ -338,6 +338,103 @@ int qdec_adaptor_run(qdec_adaptor* a, const float* frames_dev, int32_t n_frames,
 /* Free the adaptor (synchronises its stream). NULL is a no-op. */
 void qdec_adaptor_destroy(qdec_adaptor* a);
 
+/* ------------------------------------------------- frontend and encoder
+ * 16 kHz PCM -> log-mel filterbank -> LFR rows -> SAN-M encoder frames, the
+ * input of the adaptor.
+ * Frontend (audio.cpp "Fun-ASR-Nano Native Runtime Implementation Plan",
+ * Task 2 Step 4; transcribe.cpp "Forward map - funasr_nano", table
+ * "Frontend"): frames of 400 samples every 160 (whole frames only:
+ * T = 1 + (n - 400) / 160); per frame the mean is subtracted, pre-emphasis
+ * y[i] = x[i] - 0.97 x[i-1] (y[0] = 0.03 x[0]), Hamming window
+ * 0.54 - 0.46 cos(2 pi i / 399), |FFT_512|^2 of bins 0 .. 255, 80 triangle
+ * filters on the HTK mel scale 1127 ln(1 + f / 700) with edges equally
+ * spaced from 20 to 8000 Hz, natural log floored at the float32 epsilon.
+ * LFR row r (ceil(T / lfr_n) rows) stacks frames
+ * clamp(r lfr_n + j - (lfr_m - 1) / 2, 0, T - 1), j < lfr_m. No CMVN.
+ * Encoder (same plan, Tasks 3-4; the map's "Encoder" table): x = LFR rows *
+ * sqrt(dim) + PE (PE[t, 2i] = sin(t / 10000^(2i/W)), PE[t, 2i+1] = cos, W =
+ * the row width); then 1 + n_main + n_tp SAN-M blocks, each
+ *   h = LN1(x); q, k, v = h Wq + bq, h Wk + bk, h Wv + bv;
+ *   y = MHA(q, k, v) Wo + bo + v + fsmn(v)   (every frame sees every frame,
+ *       scale 1/sqrt(128); fsmn = per-channel conv over time with K taps,
+ *       zero padding (K-1)/2 each side, no bias);
+ *   x = x + y (the first block, the 560 -> dim stem: x = y);
+ *   x = x + W2 ReLU(W1 LN2(x) + b1) + b2,
+ * with LN = after_norm applied after block n_main and LN = tp_norm after the
+ * last; LN(x) = (x - mean) / sqrt(var + ln_eps) g + b, population variance.
+ * Frontend in float64, encoder weights bf16 with fp32 activations. Head
+ * count, FFN width and FSMN taps are not given by the pages for the real
+ * encoder: parameters (4 heads, 2048, 11 in the workloads). */
+typedef struct {
+  int32_t n_mels;       /* 80 */
+  int32_t lfr_m;        /* frames per LFR row, odd, 1 .. 15 (7) */
+  int32_t lfr_n;        /* LFR stride in frames, 1 .. 15 (6) */
+  int32_t dim;          /* n_head * 128 */
+  int32_t n_head;
+  int32_t ffn_dim;      /* a multiple of 128 */
+  int32_t fsmn_kernel;  /* odd, 1 .. 31 */
+  int32_t n_main;       /* residual blocks after the stem, 0 .. 127 (49) */
+  int32_t n_tp;         /* blocks after after_norm, 0 .. 127 (20) */
+  float ln_eps;         /* > 0 (1e-12) */
+  int32_t weight_dtype; /* QDEC_BF16 */
+} qdec_encoder_config;
+
+/* Per block, QDEC_EB_PER_BLOCK device pointers in this order; matrices
+ * [out, in] row-major, vectors [out]; the stem's norm1 and q/k/v take
+ * in = n_mels * lfr_m inputs, every other block in = dim. FSMN taps
+ * [dim, fsmn_kernel]. */
+enum {
+  QDEC_EB_NORM1_G = 0, QDEC_EB_NORM1_B, QDEC_EB_Q_W, QDEC_EB_Q_B, QDEC_EB_K_W, QDEC_EB_K_B, QDEC_EB_V_W,
+  QDEC_EB_V_B, QDEC_EB_FSMN_W, QDEC_EB_O_W, QDEC_EB_O_B, QDEC_EB_NORM2_G, QDEC_EB_NORM2_B, QDEC_EB_FFN1_W,
+  QDEC_EB_FFN1_B, QDEC_EB_FFN2_W, QDEC_EB_FFN2_B, QDEC_EB_PER_BLOCK
+};
+
+/* Device pointers, all bf16: block: HOST array of (1 + n_main + n_tp) *
+ * QDEC_EB_PER_BLOCK device pointers, block-major in run order (stem, main
+ * blocks, tp blocks); after_norm and tp_norm gains and biases [dim].
+ * Ownership: o, ffn1 and ffn2 are borrowed and must stay valid until
+ * qdec_encoder_destroy; q/k/v are packed into one [3 dim, in] copy (the
+ * stem's columns padded to a multiple of 32), taps and vectors are copied as
+ * fp32, so those may be freed. */
+typedef struct {
+  const void* const* block;
+  const void* after_norm_g;
+  const void* after_norm_b;
+  const void* tp_norm_g;
+  const void* tp_norm_b;
+} qdec_encoder_weights;
+
+typedef struct qdec_encoder qdec_encoder;
+
+/* Validate (QDEC_E_INVALID), copy, pack and build the frontend tables on
+ * `hip_stream`; the stream is synchronised before return. */
+int qdec_encoder_create(const qdec_encoder_config* cfg, const qdec_encoder_weights* w, void* hip_stream,
+                        qdec_encoder** out);
+
+/* LFR rows for n_samples of PCM: ceil(T / lfr_n), T = 1 + (n_samples - 400)
+ * / 160 whole frames; 0 below 400 samples or for a NULL encoder. */
+int32_t qdec_encoder_rows(const qdec_encoder* e, int64_t n_samples);
+
+/* Frontend only: lfr_dev DEVICE fp32 [rows, n_mels * lfr_m] receives the LFR
+ * rows of pcm_dev (DEVICE fp32 [n_samples], at least 400 samples, else
+ * QDEC_E_INVALID). */
+int qdec_frontend_run(qdec_encoder* e, const float* pcm_dev, int64_t n_samples, float* lfr_dev);
+
+/* Encoder only: out_dev DEVICE fp32 [n_rows, dim] receives the encoder
+ * frames (tp_norm's output) of lfr_dev (DEVICE fp32 [n_rows, n_mels *
+ * lfr_m], n_rows >= 1, not modified). */
+int qdec_encoder_forward(qdec_encoder* e, const float* lfr_dev, int32_t n_rows, float* out_dev);
+
+/* Both: out_dev DEVICE fp32 [qdec_encoder_rows(e, n_samples), dim]. */
+int qdec_encoder_run(qdec_encoder* e, const float* pcm_dev, int64_t n_samples, float* out_dev);
+
+/* Scratch for the longest input seen so far is kept (QDEC_E_OOM if it cannot
+ * grow). Work is enqueued on the encoder's stream; calls on one encoder are
+ * not thread-safe. Errors: QDEC_E_INVALID for NULL or undersized buffers,
+ * QDEC_E_DEVICE for HIP errors. Free with qdec_encoder_destroy (synchronises
+ * its stream; NULL is a no-op). */
+void qdec_encoder_destroy(qdec_encoder* e);
+
 /* n_past of the state (-1 for NULL). */
 int32_t qdec_state_pos(const qdec_state* s);
 

@@ -9,7 +9,7 @@ LIB = os.path.join(HERE, "libqdec.so")
 # diagnostic variant: the decode kernel records realtime-counter stamps at its
 # phase boundaries (read back with qdec_debug_trace); never the product library
 TRACE_LIB = os.path.join(HERE, "libqdec_trace.so")
-SOURCES = ["qdec_api.cpp", "qdec_kernels.hip", "qdec_decode.hip"]
+SOURCES = ["qdec_api.cpp", "qdec_kernels.hip", "qdec_decode.hip", "qdec_encoder.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -550,7 +550,6 @@ template <typename RopeFn, typename AttnFn>
 int run_layers_rows(qdec_model* m, int T, float* X, float* QKV, float* Attn, float* Z, int nss, RopeFn rope,
                     AttnFn attn, int* nss_out) {
   const Dims& d = m->d;
-  hipStream_t st = m->stream;
   RowsGemm g{};
   g.M = T;
   g.eps = d.eps;
@@ -1503,5 +1502,349 @@ int qdec_adaptor_run(qdec_adaptor* a, const float* frames_dev, int32_t n_frames,
 }
 
 void qdec_adaptor_destroy(qdec_adaptor* a) { free_adaptor(a); }
+
+}  // extern "C"
+
+// ================================================================= encoder
+// The audio frontend and the SAN-M speech encoder (audio.cpp "Fun-ASR-Nano
+// Native Runtime Implementation Plan", Tasks 2-4; transcribe.cpp "Forward map
+// - funasr_nano", tables "Frontend" and "Encoder"). The frontend kernels run
+// in float64; the 70 blocks reuse the prefill kernels: LayerNorm written as a
+// bf16 hi/lo operand, the MFMA GEMMs with bias / ReLU / residual epilogues,
+// the matrix-core attention without the causal mask, plus the FSMN kernel
+// that adds v + conv(v) into the residual stream ahead of the O projection's
+// residual epilogue.
+
+struct qdec_encoder {
+  qdec_encoder_config c{};
+  hipStream_t stream = nullptr;
+  int in_dim = 0, in_pad = 0;  // LFR row width and the stem's GEMM operand pitch (multiple of 32)
+  struct Block {
+    uint16_t* wqkv = nullptr;  // [3 dim, in_pad] (owned): q rows, k rows, v rows
+    const uint16_t *wo = nullptr, *ffn1 = nullptr, *ffn2 = nullptr;
+    float *bqkv = nullptr, *bo = nullptr, *n1g = nullptr, *n1b = nullptr, *n2g = nullptr, *n2b = nullptr;
+    float *bf1 = nullptr, *bf2 = nullptr, *taps = nullptr;
+  };
+  std::vector<Block> blocks;
+  float* vecs = nullptr;  // biases, norm vectors and FSMN taps, fp32
+  float *an_g = nullptr, *an_b = nullptr, *tn_g = nullptr, *tn_b = nullptr;
+  double* tab = nullptr;  // frontend tables and the PE frequencies, fp64
+  int* mel_range = nullptr;
+  const double* inv_freq = nullptr;
+  FrontTables ft{};
+  // scratch for up to cap_rows LFR rows (cap_rows * lfr_n + lfr_m frames)
+  int cap_rows = 0;
+  float* fb = nullptr;
+  float* x0 = nullptr;
+  float* X = nullptr;
+  float* QKV = nullptr;
+  float* H = nullptr;
+  uint16_t* A0 = nullptr;
+  uint16_t* A1 = nullptr;
+  uint16_t* kv[4] = {nullptr, nullptr, nullptr, nullptr};
+};
+
+namespace {
+
+void free_encoder_scratch(qdec_encoder* e) {
+  for (void* p : {(void*)e->fb, (void*)e->x0, (void*)e->X, (void*)e->QKV, (void*)e->H, (void*)e->A0, (void*)e->A1,
+                  (void*)e->kv[0], (void*)e->kv[1], (void*)e->kv[2], (void*)e->kv[3]})
+    if (p) (void)hipFree(p);
+  e->fb = e->x0 = e->X = e->QKV = e->H = nullptr;
+  e->A0 = e->A1 = nullptr;
+  for (auto& k : e->kv) k = nullptr;
+  e->cap_rows = 0;
+}
+
+void free_encoder(qdec_encoder* e) {
+  if (!e) return;
+  (void)hipStreamSynchronize(e->stream);
+  free_encoder_scratch(e);
+  for (auto& b : e->blocks)
+    if (b.wqkv) (void)hipFree(b.wqkv);
+  for (void* p : {(void*)e->vecs, (void*)e->tab, (void*)e->mel_range})
+    if (p) (void)hipFree(p);
+  delete e;
+}
+
+int ensure_encoder(qdec_encoder* e, int rows) {
+  if (rows <= e->cap_rows) return QDEC_OK;
+  free_encoder_scratch(e);
+  const qdec_encoder_config& c = e->c;
+  const size_t R = (size_t)rows, frames = R * c.lfr_n + c.lfr_m;
+  const size_t wide = (size_t)std::max(std::max(e->in_pad, c.dim), c.ffn_dim);
+  const size_t Tp = (size_t)kv_split_pad(rows);
+  int r;
+  if ((r = dev_alloc(&e->fb, frames * kMels, "fbank frames")) ||
+      (r = dev_alloc(&e->x0, R * e->in_dim, "encoder input rows")) ||
+      (r = dev_alloc(&e->X, R * c.dim, "encoder residual stream")) ||
+      (r = dev_alloc(&e->QKV, R * 3 * c.dim, "encoder qkv")) || (r = dev_alloc(&e->H, R * c.ffn_dim, "encoder ffn")) ||
+      (r = dev_alloc(&e->A0, R * wide, "encoder operand")) || (r = dev_alloc(&e->A1, R * wide, "encoder operand")) ||
+      (r = dev_alloc(&e->kv[0], R * c.dim, "encoder K")) || (r = dev_alloc(&e->kv[1], R * c.dim, "encoder K")) ||
+      (r = dev_alloc(&e->kv[2], Tp * c.dim, "encoder V")) || (r = dev_alloc(&e->kv[3], Tp * c.dim, "encoder V"))) {
+    free_encoder_scratch(e);
+    return r;
+  }
+  e->cap_rows = rows;
+  return QDEC_OK;
+}
+
+int frames_of(int64_t n) { return n < kFrameLen ? 0 : (int)(1 + (n - kFrameLen) / kFrameShift); }
+
+// The encoder blocks over the rows in e->x0, result into out.
+int encoder_blocks(qdec_encoder* e, int T, float* out) {
+  const qdec_encoder_config& c = e->c;
+  const int D = c.dim, F = c.ffn_dim;
+  hipStream_t st = e->stream;
+  uint16_t *A0 = e->A0, *A1 = e->A1;
+  const Dims ad{1, D, c.n_head, c.n_head, 128, 0, 0, 0.f};
+  for (size_t b = 0; b < e->blocks.size(); ++b) {
+    const qdec_encoder::Block& k = e->blocks[b];
+    const bool stem = b == 0;
+    if (stem)
+      LAUNCH(launch_ln_split(e->x0, T, e->in_dim, k.n1g, k.n1b, c.ln_eps, A0, A1, st, e->in_pad));
+    else
+      LAUNCH(launch_ln_split(e->X, T, D, k.n1g, k.n1b, c.ln_eps, A0, A1, st));
+    LAUNCH(launch_gemm(true, EPI_STORE, A0, A1, T, stem ? e->in_pad : D, k.wqkv, 3 * D, e->QKV, 3 * D, st, k.bqkv));
+    LAUNCH(launch_attn_prefill(ad, e->QKV, T, nullptr, e->kv, st, A0, A1, false));
+    LAUNCH(launch_fsmn(e->QKV, 3 * D, T, D, c.fsmn_kernel, k.taps, !stem, e->X, st));
+    LAUNCH(launch_gemm(true, EPI_RESID, A0, A1, T, D, k.wo, D, e->X, D, st, k.bo));
+    LAUNCH(launch_ln_split(e->X, T, D, k.n2g, k.n2b, c.ln_eps, A0, A1, st));
+    LAUNCH(launch_gemm(true, EPI_RELU, A0, A1, T, D, k.ffn1, F, e->H, F, st, k.bf1));
+    LAUNCH(launch_rms_split(e->H, T, F, nullptr, 0.f, A0, A1, st));
+    LAUNCH(launch_gemm(true, EPI_RESID, A0, A1, T, F, k.ffn2, D, e->X, D, st, k.bf2));
+    if ((int)b == c.n_main) LAUNCH(launch_ln_apply(e->X, T, D, e->an_g, e->an_b, c.ln_eps, e->X, st));
+  }
+  LAUNCH(launch_ln_apply(e->X, T, D, e->tn_g, e->tn_b, c.ln_eps, out, st));
+  return QDEC_OK;
+}
+
+// Frontend of n samples: fbank frames into e->fb, then the LFR rows into
+// lfr (optional) and the encoder input rows into e->x0 (when x0 is set).
+int run_frontend(qdec_encoder* e, const float* pcm, int64_t n, float* lfr, bool x0) {
+  const qdec_encoder_config& c = e->c;
+  const int frames = frames_of(n), rows = (frames + c.lfr_n - 1) / c.lfr_n;
+  LAUNCH(launch_fbank(pcm, frames, e->ft, e->fb, e->stream));
+  LAUNCH(launch_lfr_embed(e->fb, frames, kMels, c.lfr_m, c.lfr_n, sqrtf((float)c.dim), e->inv_freq, lfr,
+                          x0 ? e->x0 : nullptr, rows, e->stream));
+  return QDEC_OK;
+}
+
+int check_pcm(qdec_encoder* e, const float* pcm, int64_t n, int* rows) {
+  if (!e) return fail(QDEC_E_INVALID, "encoder is NULL");
+  if (n < kFrameLen) return fail(QDEC_E_INVALID, "%lld samples: at least %d are needed", (long long)n, kFrameLen);
+  const int64_t frames = 1 + (n - kFrameLen) / kFrameShift;
+  if (frames > (int64_t)e->c.lfr_n * 65536) return fail(QDEC_E_INVALID, "input longer than 65536 LFR rows");
+  if (int r = check_dev(pcm, (size_t)n * sizeof(float), "pcm_dev")) return r;
+  *rows = (int)((frames + e->c.lfr_n - 1) / e->c.lfr_n);
+  return ensure_encoder(e, *rows);
+}
+
+}  // namespace
+
+extern "C" {
+
+int qdec_encoder_create(const qdec_encoder_config* cfg, const qdec_encoder_weights* w, void* hip_stream,
+                        qdec_encoder** out) {
+  if (!out) return fail(QDEC_E_INVALID, "out is NULL");
+  *out = nullptr;
+  if (!cfg) return fail(QDEC_E_INVALID, "config is NULL");
+  const qdec_encoder_config& c = *cfg;
+  if (c.weight_dtype != QDEC_BF16) return fail(QDEC_E_INVALID, "the encoder takes bf16 weights");
+  if (c.n_mels != kMels) return fail(QDEC_E_INVALID, "n_mels %d: the frontend computes %d", c.n_mels, kMels);
+  if (c.lfr_m < 1 || c.lfr_m > 15 || c.lfr_m % 2 == 0 || c.lfr_n < 1 || c.lfr_n > 15)
+    return fail(QDEC_E_INVALID, "lfr_m %d (odd, 1 .. 15) or lfr_n %d (1 .. 15)", c.lfr_m, c.lfr_n);
+  if (c.n_head < 1 || c.n_head > 16 || c.dim != c.n_head * 128)
+    return fail(QDEC_E_INVALID, "dim %d must be n_head (%d) * 128", c.dim, c.n_head);
+  if (c.ffn_dim < 128 || c.ffn_dim > 8192 || c.ffn_dim % 128)
+    return fail(QDEC_E_INVALID, "ffn_dim %d must be a multiple of 128 in [128, 8192]", c.ffn_dim);
+  if (c.fsmn_kernel < 1 || c.fsmn_kernel > 31 || c.fsmn_kernel % 2 == 0)
+    return fail(QDEC_E_INVALID, "fsmn_kernel %d must be odd in [1, 31]", c.fsmn_kernel);
+  if (c.n_main < 0 || c.n_main > 127 || c.n_tp < 0 || c.n_tp > 127)
+    return fail(QDEC_E_INVALID, "n_main %d / n_tp %d outside 0 .. 127", c.n_main, c.n_tp);
+  if (!(c.ln_eps > 0.f) || !std::isfinite(c.ln_eps)) return fail(QDEC_E_INVALID, "ln_eps must be > 0");
+  if (!w || !w->block || !w->after_norm_g || !w->after_norm_b || !w->tp_norm_g || !w->tp_norm_b)
+    return fail(QDEC_E_INVALID, "encoder weights incomplete");
+  const int nb = 1 + c.n_main + c.n_tp;
+  const size_t D = c.dim, F = c.ffn_dim, K = c.fsmn_kernel, W = (size_t)kMels * c.lfr_m;
+  for (int b = 0; b < nb; ++b) {
+    const void* const* t = w->block + (size_t)b * QDEC_EB_PER_BLOCK;
+    const size_t in = b == 0 ? W : D;
+    const size_t n[QDEC_EB_PER_BLOCK] = {in, in, D * in, D, D * in, D, D * in, D, D * K, D * D, D, D, D, F * D, F,
+                                         D * F, D};
+    for (int i = 0; i < QDEC_EB_PER_BLOCK; ++i) {
+      char what[48];
+      snprintf(what, sizeof what, "block %d tensor %d", b, i);
+      if (int r = check_dev(t[i], n[i] * 2, what)) return r;
+    }
+  }
+  for (const void* p : {w->after_norm_g, w->after_norm_b, w->tp_norm_g, w->tp_norm_b})
+    if (int r = check_dev(p, D * 2, "final norm vector")) return r;
+
+  qdec_encoder* e = new (std::nothrow) qdec_encoder();
+  if (!e) return fail(QDEC_E_OOM, "host allocation failed");
+  e->c = c;
+  e->stream = (hipStream_t)hip_stream;
+  e->in_dim = (int)W;
+  e->in_pad = (int)((W + 31) / 32 * 32);
+  hipStream_t st = e->stream;
+  auto fail_dev = [&](const char* what, hipError_t he) {
+    const int r = fail(QDEC_E_DEVICE, "%s: %s", what, hipGetErrorString(he));
+    free_encoder(e);
+    return r;
+  };
+  // fp32 vectors: per block 2 norm1 (in wide), qkv, o, 2 norm2, ffn biases, taps
+  const size_t per_block = 2 * std::max(W, D) + 3 * D + D + 2 * D + F + D + D * K;
+  const size_t nvec = (size_t)nb * per_block + 4 * D;
+  if (int r = dev_alloc(&e->vecs, nvec, "encoder vectors")) {
+    free_encoder(e);
+    return r;
+  }
+  hipError_t he;
+  float* v = e->vecs;
+  e->blocks.resize(nb);
+  for (int b = 0; b < nb; ++b) {
+    const void* const* t = w->block + (size_t)b * QDEC_EB_PER_BLOCK;
+    qdec_encoder::Block& k = e->blocks[b];
+    const size_t in = b == 0 ? W : D, pitch = b == 0 ? (size_t)e->in_pad : D;
+    if (int r = dev_alloc(&k.wqkv, 3 * D * pitch, "encoder wqkv")) {
+      free_encoder(e);
+      return r;
+    }
+    if ((he = hipMemsetAsync(k.wqkv, 0, 3 * D * pitch * 2, st))) return fail_dev("clear wqkv", he);
+    const int srcs[3] = {QDEC_EB_Q_W, QDEC_EB_K_W, QDEC_EB_V_W};
+    for (int j = 0; j < 3; ++j)
+      if ((he = hipMemcpy2DAsync(k.wqkv + j * D * pitch, pitch * 2, t[srcs[j]], in * 2, in * 2, D,
+                                 hipMemcpyDeviceToDevice, st)))
+        return fail_dev("pack wqkv", he);
+    k.wo = (const uint16_t*)t[QDEC_EB_O_W];
+    k.ffn1 = (const uint16_t*)t[QDEC_EB_FFN1_W];
+    k.ffn2 = (const uint16_t*)t[QDEC_EB_FFN2_W];
+    k.n1g = v;
+    k.n1b = v + in;
+    v += 2 * std::max(W, D);
+    k.bqkv = v;
+    k.bo = v + 3 * D;
+    k.n2g = v + 4 * D;
+    k.n2b = v + 5 * D;
+    k.bf2 = v + 6 * D;
+    k.bf1 = v + 7 * D;
+    k.taps = v + 7 * D + F;
+    v += 3 * D + D + 2 * D + D + F + D * K;
+    const struct {
+      int idx;
+      float* dst;
+      size_t n;
+    } vecs[] = {{QDEC_EB_NORM1_G, k.n1g, in}, {QDEC_EB_NORM1_B, k.n1b, in},  {QDEC_EB_Q_B, k.bqkv, D},
+                {QDEC_EB_K_B, k.bqkv + D, D}, {QDEC_EB_V_B, k.bqkv + 2 * D, D}, {QDEC_EB_O_B, k.bo, D},
+                {QDEC_EB_NORM2_G, k.n2g, D},  {QDEC_EB_NORM2_B, k.n2b, D},   {QDEC_EB_FFN2_B, k.bf2, D},
+                {QDEC_EB_FFN1_B, k.bf1, F},   {QDEC_EB_FSMN_W, k.taps, D * K}};
+    for (const auto& x : vecs)
+      if ((he = launch_to_f32(t[x.idx], true, x.n, x.dst, st))) return fail_dev("encoder vector", he);
+  }
+  e->an_g = v;
+  e->an_b = v + D;
+  e->tn_g = v + 2 * D;
+  e->tn_b = v + 3 * D;
+  if ((he = launch_to_f32(w->after_norm_g, true, D, e->an_g, st)) ||
+      (he = launch_to_f32(w->after_norm_b, true, D, e->an_b, st)) ||
+      (he = launch_to_f32(w->tp_norm_g, true, D, e->tn_g, st)) ||
+      (he = launch_to_f32(w->tp_norm_b, true, D, e->tn_b, st)))
+    return fail_dev("final norms", he);
+
+  // frontend tables, computed here in double: Hamming window, FFT twiddles,
+  // the mel triangles (HTK mel 1127 ln(1 + f / 700), 82 edges equally spaced
+  // in mel from 20 Hz to 8000 Hz, bins at 31.25 Hz) and the PE frequencies
+  constexpr int kBins = 256;
+  const size_t n_tab = kFrameLen + 2 * kBins + (size_t)kMels * kBins + W / 2;
+  std::vector<double> h(n_tab, 0.0);
+  std::vector<int> range(2 * kMels, 0);
+  double* hw = h.data();
+  double* htr = hw + kFrameLen;
+  double* hti = htr + kBins;
+  double* hm = hti + kBins;
+  double* hf = hm + (size_t)kMels * kBins;
+  const double pi = 3.14159265358979323846;
+  for (int i = 0; i < kFrameLen; ++i) hw[i] = 0.54 - 0.46 * std::cos(2.0 * pi * i / (kFrameLen - 1));
+  for (int k = 0; k < kBins; ++k) {
+    htr[k] = std::cos(2.0 * pi * k / (2 * kBins));
+    hti[k] = -std::sin(2.0 * pi * k / (2 * kBins));
+  }
+  auto to_mel = [](double f) { return 1127.0 * std::log(1.0 + f / 700.0); };
+  const double m_lo = to_mel(20.0), m_hi = to_mel(8000.0), step = (m_hi - m_lo) / (kMels + 1);
+  for (int j = 0; j < kMels; ++j) {
+    const double left = m_lo + j * step, centre = m_lo + (j + 1) * step, right = m_lo + (j + 2) * step;
+    int lo = kBins, hi = 0;
+    for (int k = 0; k < kBins; ++k) {
+      const double m = to_mel(k * 16000.0 / (2 * kBins));
+      double wgt = 0.0;
+      if (m > left && m < right) wgt = m <= centre ? (m - left) / (centre - left) : (right - m) / (right - centre);
+      hm[(size_t)j * kBins + k] = wgt;
+      if (wgt != 0.0) {
+        lo = std::min(lo, k);
+        hi = k + 1;
+      }
+    }
+    range[j] = lo < hi ? lo : 0;
+    range[kMels + j] = lo < hi ? hi : 0;
+  }
+  for (size_t i = 0; i < W / 2; ++i) hf[i] = 1.0 / std::pow(10000.0, 2.0 * (double)i / (double)W);
+  if (int r = dev_alloc(&e->tab, n_tab, "frontend tables")) {
+    free_encoder(e);
+    return r;
+  }
+  if (int r = dev_alloc(&e->mel_range, 2 * kMels, "mel ranges")) {
+    free_encoder(e);
+    return r;
+  }
+  if ((he = hipMemcpyAsync(e->tab, h.data(), n_tab * sizeof(double), hipMemcpyHostToDevice, st)) ||
+      (he = hipMemcpyAsync(e->mel_range, range.data(), range.size() * sizeof(int), hipMemcpyHostToDevice, st)))
+    return fail_dev("frontend tables", he);
+  e->ft = FrontTables{e->tab, e->tab + kFrameLen, e->tab + kFrameLen + kBins, e->tab + kFrameLen + 2 * kBins,
+                      e->mel_range, e->mel_range + kMels};
+  e->inv_freq = e->tab + kFrameLen + 2 * kBins + (size_t)kMels * kBins;
+  // the host vectors are read by the copies above: wait before they go
+  if ((he = hipStreamSynchronize(st))) return fail_dev("encoder packing", he);
+  *out = e;
+  return ok();
+}
+
+int32_t qdec_encoder_rows(const qdec_encoder* e, int64_t n_samples) {
+  if (!e) return 0;
+  const int f = frames_of(n_samples);
+  return (f + e->c.lfr_n - 1) / e->c.lfr_n;
+}
+
+int qdec_frontend_run(qdec_encoder* e, const float* pcm_dev, int64_t n_samples, float* lfr_dev) {
+  int rows = 0;
+  if (int r = check_pcm(e, pcm_dev, n_samples, &rows)) return r;
+  if (int r = check_dev(lfr_dev, (size_t)rows * e->in_dim * sizeof(float), "lfr_dev")) return r;
+  if (int r = run_frontend(e, pcm_dev, n_samples, lfr_dev, false)) return r;
+  return ok();
+}
+
+int qdec_encoder_forward(qdec_encoder* e, const float* lfr_dev, int32_t n_rows, float* out_dev) {
+  if (!e) return fail(QDEC_E_INVALID, "encoder is NULL");
+  if (n_rows < 1 || n_rows > 65536) return fail(QDEC_E_INVALID, "n_rows %d outside 1 .. 65536", n_rows);
+  if (int r = check_dev(lfr_dev, (size_t)n_rows * e->in_dim * sizeof(float), "lfr_dev")) return r;
+  if (int r = check_dev(out_dev, (size_t)n_rows * e->c.dim * sizeof(float), "out_dev")) return r;
+  if (int r = ensure_encoder(e, n_rows)) return r;
+  // the rows themselves as one-frame LFR rows: x0 = rows * sqrt(dim) + PE
+  LAUNCH(launch_lfr_embed(lfr_dev, n_rows, e->in_dim, 1, 1, sqrtf((float)e->c.dim), e->inv_freq, nullptr, e->x0,
+                          n_rows, e->stream));
+  if (int r = encoder_blocks(e, n_rows, out_dev)) return r;
+  return ok();
+}
+
+int qdec_encoder_run(qdec_encoder* e, const float* pcm_dev, int64_t n_samples, float* out_dev) {
+  int rows = 0;
+  if (int r = check_pcm(e, pcm_dev, n_samples, &rows)) return r;
+  if (int r = check_dev(out_dev, (size_t)rows * e->c.dim * sizeof(float), "out_dev")) return r;
+  if (int r = run_frontend(e, pcm_dev, n_samples, nullptr, true)) return r;
+  if (int r = encoder_blocks(e, rows, out_dev)) return r;
+  return ok();
+}
+
+void qdec_encoder_destroy(qdec_encoder* e) { free_encoder(e); }
 
 }  // extern "C"

@@ -1679,7 +1679,6 @@ int chunk_elems(int wt) { return wt == QDEC_BF16 ? 8 : wt == QDEC_Q8_0 ? 16 : 4;
 
 Layout layout(int wt, const Dims& d, int nsplit_max, int nb) {
   const int G = d.NQ / d.NKV;
-  const int QD = G * d.D;
   const int VN = chunk_elems(wt);
   const int per = (G * d.D + nb / kGroups - 1) / (nb / kGroups);  // merged outputs per rank
   const int stage = std::max(8, 3 * nsplit_max * per);            // split merge: (m, l, o) per split

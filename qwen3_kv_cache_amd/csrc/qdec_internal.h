@@ -142,9 +142,10 @@ hipError_t launch_attn_prefill(const Dims& d, const float* qkv, int T, float* ou
 
 hipError_t launch_rms_split(const float* X, int T, int K, const float* gain, float eps, uint16_t* hi,
                             uint16_t* lo, hipStream_t st);
-// LayerNorm (population variance, gain and bias) of T rows of K, as bf16 hi/lo.
+// LayerNorm (population variance, gain and bias) of T rows of K, as bf16 hi/lo
+// rows of pitch ldo >= K (0: K) whose columns K .. ldo are zero.
 hipError_t launch_ln_split(const float* X, int T, int K, const float* gain, const float* bias, float eps,
-                           uint16_t* hi, uint16_t* lo, hipStream_t st);
+                           uint16_t* hi, uint16_t* lo, hipStream_t st, int ldo = 0);
 hipError_t launch_rms_apply(const float* X, int T, int K, const float* gain, float eps, float* out,
                             hipStream_t st);
 // C[M, N] (+)= A[M, K] . W[N, K]^T with a bf16 hi/lo split A (bf16 weights)
@@ -201,6 +202,38 @@ size_t sample_buffer_words(int V);
 // largest vocabulary they hold.
 hipError_t sample_static_scratch(unsigned long long** buf0, unsigned long long** buf1);
 int sample_static_max_vocab();
+
+// ---- audio frontend and SAN-M encoder glue (qdec_encoder.hip)
+constexpr int kFrameLen = 400;    // 25 ms at 16 kHz
+constexpr int kFrameShift = 160;  // 10 ms
+constexpr int kMels = 80;
+constexpr double kPreemph = 0.97;
+// Float64 tables of the frontend, built on the host: the Hamming window
+// [400], FFT twiddles exp(-2 pi i k / 512) for k < 256, and the mel
+// triangle weights [80][256] with each filter's nonzero bin range [lo, hi).
+struct FrontTables {
+  const double* window;
+  const double* tw_re;
+  const double* tw_im;
+  const double* mel_w;
+  const int* mel_lo;
+  const int* mel_hi;
+};
+// out[f, 0 .. 80) = log mel energies of frame f, f < n_frames (frame f
+// starts at pcm + 160 f; the caller guarantees 400 samples)
+hipError_t launch_fbank(const float* pcm, int n_frames, const FrontTables& tb, float* out, hipStream_t st);
+// LFR rows [rows, n_mels m] of T frames (lfr, optional) and the encoder input
+// rows * scale + sinusoidal positions (x0, optional); inv_freq [n_mels m / 2]
+hipError_t launch_lfr_embed(const float* fb, int T, int n_mels, int m, int n, float scale, const double* inv_freq,
+                            float* lfr, float* x0, int rows, hipStream_t st);
+// out (+)= v + depthwise conv of v over time (v = qkv[:, 2 dim : 3 dim], row
+// pitch ld; taps w [dim, K], K odd, zero padding)
+hipError_t launch_fsmn(const float* qkv, int ld, int T, int dim, int K, const float* w, bool accumulate, float* out,
+                       hipStream_t st);
+// LayerNorm (population variance, gain and bias) of T rows of K into fp32;
+// out may be X
+hipError_t launch_ln_apply(const float* X, int T, int K, const float* gain, const float* bias, float eps, float* out,
+                           hipStream_t st);
 
 // ---- persistent decode (qdec_decode.hip)
 // Word offsets of the exchange regions inside the model's word buffer.

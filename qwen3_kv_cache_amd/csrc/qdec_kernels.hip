@@ -1120,7 +1120,7 @@ __global__ __launch_bounds__(256) void rms_split_vec_kernel(const float* __restr
 __global__ __launch_bounds__(256) void ln_split_kernel(const float* __restrict__ X, int K,
                                                         const float* __restrict__ gain, const float* __restrict__ bias,
                                                         float eps, uint16_t* __restrict__ hi,
-                                                        uint16_t* __restrict__ lo) {
+                                                        uint16_t* __restrict__ lo, int ldo) {
   __shared__ float red[8];
   const int t = blockIdx.x;
   const float* x = X + (size_t)t * K;
@@ -1136,8 +1136,12 @@ __global__ __launch_bounds__(256) void ln_split_kernel(const float* __restrict__
   for (int i = threadIdx.x; i < K; i += blockDim.x) {
     const float v = (x[i] - mean) * inv * gain[i] + bias[i];
     const uint16_t h = f32_to_bf16_rne(v);
-    hi[(size_t)t * K + i] = h;
-    lo[(size_t)t * K + i] = f32_to_bf16_rne(v - bf16_to_f32(h));
+    hi[(size_t)t * ldo + i] = h;
+    lo[(size_t)t * ldo + i] = f32_to_bf16_rne(v - bf16_to_f32(h));
+  }
+  for (int i = K + threadIdx.x; i < ldo; i += blockDim.x) {
+    hi[(size_t)t * ldo + i] = 0;
+    lo[(size_t)t * ldo + i] = 0;
   }
 }
 
@@ -2013,8 +2017,10 @@ hipError_t launch_attn_prefill(const Dims& d, const float* qkv, int T, float* ou
 }
 
 hipError_t launch_ln_split(const float* X, int T, int K, const float* gain, const float* bias, float eps,
-                           uint16_t* hi, uint16_t* lo, hipStream_t st) {
-  ln_split_kernel<<<T, 256, 0, st>>>(X, K, gain, bias, eps, hi, lo);
+                           uint16_t* hi, uint16_t* lo, hipStream_t st, int ldo) {
+  if (ldo == 0) ldo = K;
+  if (ldo < K) return hipErrorInvalidValue;
+  ln_split_kernel<<<T, 256, 0, st>>>(X, K, gain, bias, eps, hi, lo, ldo);
   return hipGetLastError();
 }
 

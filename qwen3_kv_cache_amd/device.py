@@ -113,3 +113,71 @@ class Adaptor:
             self.close()
         except Exception:
             pass
+
+
+class Encoder:
+    """The audio frontend and SAN-M encoder on the GPU: ``bits`` maps the
+    parameter names ("{block}<t>" for each block prefix of
+    shape.block_names() and t in qdec.ENCODER_BLOCK_TENSORS, "after_norm.g",
+    "after_norm.b", "tp_norm.g", "tp_norm.b") to bf16 bit patterns (uint16)."""
+
+    def __init__(self, shape, bits: Dict[str, np.ndarray], ln_eps: float = 1e-12, n_mels: int = 80,
+                 lfr_m: int = 7, lfr_n: int = 6, device: str = "cuda:0"):
+        torch = _torch()
+        self.shape = shape
+        self.device = torch.device(device)
+        self.tensors = {name: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(self.device)
+                        for name, a in bits.items()}
+        blocks = [self.tensors[pre + t].data_ptr() for pre in shape.block_names()
+                  for t in qdec.ENCODER_BLOCK_TENSORS]
+        self._block_arr = (qdec.ctypes.c_void_p * len(blocks))(*blocks)
+        w = qdec.qdec_encoder_weights(qdec.ctypes.cast(self._block_arr, qdec.ctypes.POINTER(qdec.ctypes.c_void_p)),
+                                      self.tensors["after_norm.g"].data_ptr(), self.tensors["after_norm.b"].data_ptr(),
+                                      self.tensors["tp_norm.g"].data_ptr(), self.tensors["tp_norm.b"].data_ptr())
+        self.cfg = qdec.qdec_encoder_config(n_mels, lfr_m, lfr_n, shape.dim, shape.n_head, shape.ffn_dim,
+                                            shape.kernel, shape.n_main, shape.n_tp, ln_eps, qdec.QDEC_BF16)
+        self.in_dim = n_mels * lfr_m
+        self.stream = torch.cuda.current_stream(self.device).cuda_stream
+        self.handle = qdec.qdec_encoder_create(self.cfg, w, self.stream)
+        # q/k/v, taps and vectors are copied; o, ffn1 and ffn2 stay borrowed
+        keep = ("o.w", "ffn1.w", "ffn2.w")
+        for name in list(self.tensors):
+            if not name.endswith(keep):
+                del self.tensors[name]
+        torch.cuda.synchronize(self.device)
+
+    def rows(self, n_samples: int) -> int:
+        return qdec.qdec_encoder_rows(self.handle, n_samples)
+
+    def frontend(self, pcm):
+        """pcm: fp32 device tensor [n]; returns the LFR rows [rows, 560] fp32."""
+        torch = _torch()
+        out = torch.empty((self.rows(pcm.shape[0]), self.in_dim), dtype=torch.float32, device=self.device)
+        qdec.qdec_frontend_run(self.handle, pcm.data_ptr(), pcm.shape[0], out.data_ptr())
+        return out
+
+    def forward(self, lfr):
+        """lfr: fp32 device tensor [rows, 560]; returns the encoder frames [rows, dim]."""
+        torch = _torch()
+        out = torch.empty((lfr.shape[0], self.shape.dim), dtype=torch.float32, device=self.device)
+        qdec.qdec_encoder_forward(self.handle, lfr.data_ptr(), lfr.shape[0], out.data_ptr())
+        return out
+
+    def run(self, pcm, out=None):
+        """pcm: fp32 device tensor [n]; returns the encoder frames [rows, dim]."""
+        torch = _torch()
+        if out is None:
+            out = torch.empty((self.rows(pcm.shape[0]), self.shape.dim), dtype=torch.float32, device=self.device)
+        qdec.qdec_encoder_run(self.handle, pcm.data_ptr(), pcm.shape[0], out.data_ptr())
+        return out
+
+    def close(self) -> None:
+        if self.handle:
+            qdec.qdec_encoder_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -37,7 +37,8 @@ EXPORTS = ("qdec_create", "qdec_destroy", "qdec_state_create", "qdec_state_destr
            "qdec_decode_step", "qdec_decode_step_dev", "qdec_decode_greedy", "qdec_decode_batch", "qdec_sample",
            "qdec_sample_noalloc",
            "qdec_clone_state", "qdec_state_pos", "qdec_model_status", "qdec_last_error", "qdec_adaptor_create",
-           "qdec_adaptor_run", "qdec_adaptor_destroy")
+           "qdec_adaptor_run", "qdec_adaptor_destroy", "qdec_encoder_create", "qdec_encoder_rows",
+           "qdec_frontend_run", "qdec_encoder_forward", "qdec_encoder_run", "qdec_encoder_destroy")
 
 QDEC_SAMPLE_TOP_K_MAX = 128
 QDEC_SAMPLE_NOALLOC_MAX_VOCAB = 153600
@@ -75,6 +76,23 @@ class qdec_adaptor_weights(ctypes.Structure):
 # per-block tensor order of qdec_adaptor_weights.block
 ADAPTOR_BLOCK_TENSORS = ("norm1.g", "norm1.b", "q.w", "q.b", "k.w", "k.b", "v.w", "v.b", "o.w", "o.b",
                          "norm2.g", "norm2.b", "fc1.w", "fc1.b", "fc2.w", "fc2.b")
+
+
+class qdec_encoder_config(ctypes.Structure):
+    _fields_ = [("n_mels", ctypes.c_int32), ("lfr_m", ctypes.c_int32), ("lfr_n", ctypes.c_int32),
+                ("dim", ctypes.c_int32), ("n_head", ctypes.c_int32), ("ffn_dim", ctypes.c_int32),
+                ("fsmn_kernel", ctypes.c_int32), ("n_main", ctypes.c_int32), ("n_tp", ctypes.c_int32),
+                ("ln_eps", ctypes.c_float), ("weight_dtype", ctypes.c_int32)]
+
+
+class qdec_encoder_weights(ctypes.Structure):
+    _fields_ = [("block", ctypes.POINTER(ctypes.c_void_p)), ("after_norm_g", ctypes.c_void_p),
+                ("after_norm_b", ctypes.c_void_p), ("tp_norm_g", ctypes.c_void_p), ("tp_norm_b", ctypes.c_void_p)]
+
+
+# per-block tensor order of qdec_encoder_weights.block
+ENCODER_BLOCK_TENSORS = ("norm1.g", "norm1.b", "q.w", "q.b", "k.w", "k.b", "v.w", "v.b", "fsmn.w", "o.w", "o.b",
+                         "norm2.g", "norm2.b", "ffn1.w", "ffn1.b", "ffn2.w", "ffn2.b")
 
 
 class qdec_sampling(ctypes.Structure):
@@ -134,6 +152,13 @@ def lib() -> ctypes.CDLL:
                                                ctypes.POINTER(qdec_adaptor_weights), vp, ctypes.POINTER(vp)]),
         "qdec_adaptor_run": (ctypes.c_int, [vp, vp, i32, vp]),
         "qdec_adaptor_destroy": (None, [vp]),
+        "qdec_encoder_create": (ctypes.c_int, [ctypes.POINTER(qdec_encoder_config),
+                                               ctypes.POINTER(qdec_encoder_weights), vp, ctypes.POINTER(vp)]),
+        "qdec_encoder_rows": (i32, [vp, ctypes.c_int64]),
+        "qdec_frontend_run": (ctypes.c_int, [vp, vp, ctypes.c_int64, vp]),
+        "qdec_encoder_forward": (ctypes.c_int, [vp, vp, i32, vp]),
+        "qdec_encoder_run": (ctypes.c_int, [vp, vp, ctypes.c_int64, vp]),
+        "qdec_encoder_destroy": (None, [vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -251,6 +276,32 @@ def qdec_adaptor_run(adaptor: int, frames_dev, n_frames: int, out_dev) -> None:
 
 def qdec_adaptor_destroy(adaptor: int) -> None:
     lib().qdec_adaptor_destroy(_ptr(adaptor))
+
+
+def qdec_encoder_create(cfg: qdec_encoder_config, weights: qdec_encoder_weights, stream: int = 0) -> int:
+    out = ctypes.c_void_p()
+    _check(lib().qdec_encoder_create(ctypes.byref(cfg), ctypes.byref(weights), _ptr(stream), ctypes.byref(out)))
+    return out.value
+
+
+def qdec_encoder_rows(encoder: int, n_samples: int) -> int:
+    return lib().qdec_encoder_rows(_ptr(encoder), int(n_samples))
+
+
+def qdec_frontend_run(encoder: int, pcm_dev, n_samples: int, lfr_dev) -> None:
+    _check(lib().qdec_frontend_run(_ptr(encoder), _ptr(pcm_dev), int(n_samples), _ptr(lfr_dev)))
+
+
+def qdec_encoder_forward(encoder: int, lfr_dev, n_rows: int, out_dev) -> None:
+    _check(lib().qdec_encoder_forward(_ptr(encoder), _ptr(lfr_dev), int(n_rows), _ptr(out_dev)))
+
+
+def qdec_encoder_run(encoder: int, pcm_dev, n_samples: int, out_dev) -> None:
+    _check(lib().qdec_encoder_run(_ptr(encoder), _ptr(pcm_dev), int(n_samples), _ptr(out_dev)))
+
+
+def qdec_encoder_destroy(encoder: int) -> None:
+    lib().qdec_encoder_destroy(_ptr(encoder))
 
 
 def qdec_state_pos(state: int) -> int:

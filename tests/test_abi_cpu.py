@@ -158,3 +158,36 @@ def test_adaptor_null_arguments():
         qdec.qdec_adaptor_run(0, 0, 4, 0)
     assert e.value.code == qdec.QDEC_E_INVALID
     qdec.qdec_adaptor_destroy(0)  # NULL is a no-op
+
+
+def encoder_cfg(**kw):
+    base = dict(n_mels=80, lfr_m=7, lfr_n=6, dim=512, n_head=4, ffn_dim=2048, fsmn_kernel=11, n_main=49, n_tp=20,
+                ln_eps=1e-12, weight_dtype=qdec.QDEC_BF16)
+    base.update(kw)
+    return qdec.qdec_encoder_config(**base)
+
+
+ENCODER_BAD = [dict(weight_dtype=qdec.QDEC_F32), dict(n_mels=64), dict(lfr_m=6), dict(lfr_m=17), dict(lfr_n=0),
+               dict(dim=500), dict(n_head=3), dict(ffn_dim=1000), dict(fsmn_kernel=10), dict(fsmn_kernel=33),
+               dict(n_main=-1), dict(n_tp=128), dict(ln_eps=0.0)]
+
+
+@pytest.mark.parametrize("kw", ENCODER_BAD, ids=[str(k) for k in ENCODER_BAD])
+def test_encoder_create_rejects_bad_config(kw):
+    w = qdec.qdec_encoder_weights(None, 0, 0, 0, 0)
+    with pytest.raises(qdec.QdecError) as e:
+        qdec.qdec_encoder_create(encoder_cfg(**kw), w, 0)
+    assert e.value.code == qdec.QDEC_E_INVALID
+
+
+def test_encoder_null_arguments_and_row_count():
+    with pytest.raises(qdec.QdecError) as e:
+        qdec.qdec_encoder_create(encoder_cfg(), qdec.qdec_encoder_weights(None, 0, 0, 0, 0), 0)
+    assert e.value.code == qdec.QDEC_E_INVALID and "weights" in qdec.qdec_last_error()
+    for call in (lambda: qdec.qdec_encoder_run(0, 0, 16000, 0), lambda: qdec.qdec_frontend_run(0, 0, 16000, 0),
+                 lambda: qdec.qdec_encoder_forward(0, 0, 4, 0)):
+        with pytest.raises(qdec.QdecError) as e:
+            call()
+        assert e.value.code == qdec.QDEC_E_INVALID
+    assert qdec.qdec_encoder_rows(0, 16000) == 0  # NULL encoder
+    qdec.qdec_encoder_destroy(0)  # NULL is a no-op
