@@ -15,13 +15,15 @@ metric with the same weights and fewer repetitions: B=16 batched decode of
 16 clones of a 512-token prefill (branch16), the 1024- and 8192-token
 prompts (long, prefill8k), and the default workload on Q8_0 weights of the
 same shape (short_q8_0); under "sampling" the time of one sampling step
-(qdec_sample) over 1 and 16 rows of logits; and under "adaptor" the audio
+(qdec_sample) over 1 and 16 rows of logits; under "adaptor" the audio
 adaptor that makes the audio rows (qdec_adaptor_run) at 183 and 6000 encoder
-frames. --no-others skips them.
+frames; and under "encoder" the frontend + SAN-M encoder (qdec_encoder_run)
+on 11 s and 60 s of 16 kHz audio. --no-others skips them.
 
 Usage: python bench.py [--steps K] [--warmup W] [--workload short|long|prefill8k|branch16]
        python bench.py --copy-probe   (plain copy kernel for counter calibration)
        python bench.py --adaptor-only (the audio adaptor alone)
+       python bench.py --encoder-only (the frontend + encoder alone)
 """
 from __future__ import annotations
 
@@ -181,6 +183,60 @@ def measure_adaptor(frames=(183, 6000), reps=5):
                             "useful_tflops": round(tf, 1), "frac_bf16_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
     finally:
         a.close()
+    return out
+
+
+def encoder_flops(e, T: int) -> float:
+    """Useful FLOPs of the SAN-M encoder over T LFR rows: 2 per weight per row
+    for every projection (the stem's q/k/v take 560 inputs), 4 dim per (row,
+    row) pair per block for QK and PV, 2 K dim per row per block for the FSMN."""
+    D, F, nb = e.dim, e.ffn_dim, 1 + e.n_main + e.n_tp
+    per_block = 3 * D * D + D * D + 2 * D * F
+    lin = nb * per_block + 3 * D * (e.in_dim - D)
+    return 2.0 * T * lin + nb * (4.0 * T * T * D + 2.0 * e.kernel * T * D)
+
+
+def measure_encoder(seconds=(11.0, 60.0), reps=3):
+    """Time qdec_encoder_run (frontend + 70 SAN-M blocks, seeded bf16 weights
+    of the 512-wide encoder) on speech-like 16 kHz PCM resident on the GPU,
+    and the frontend alone (qdec_frontend_run); 11 s of audio is the 183
+    LFR rows the adaptor receives in the pages' example."""
+    import torch
+
+    import synth
+    from qwen3_kv_cache_amd.device import Encoder
+    shape = synth.EncoderShape()
+    _, bits = synth.make_encoder_weights(shape, 1)
+    enc = Encoder(shape, bits)
+    out = {}
+    try:
+        for sec in seconds:
+            n = int(sec * 16000)
+            x = torch.from_numpy(synth.pcm("voiced", n, 1)).cuda()
+            T = enc.rows(n)
+            y = torch.empty((T, shape.dim), dtype=torch.float32, device="cuda")
+            lfr = enc.frontend(x)
+            enc.run(x, y)
+            torch.cuda.synchronize()
+            st = torch.cuda.current_stream()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            ev[0].record(st)
+            for _ in range(reps):
+                enc.run(x, y)
+            ev[1].record(st)
+            for _ in range(reps):
+                enc.frontend(x)
+            ev[2].record(st)
+            torch.cuda.synchronize()
+            ms = ev[0].elapsed_time(ev[1]) / reps
+            fe_ms = ev[1].elapsed_time(ev[2]) / reps
+            tf = encoder_flops(shape, T) / (ms / 1e3) / 1e12
+            out[f"{sec:g}s"] = {"rows": T, "ms": round(ms, 3), "frontend_ms": round(fe_ms, 4),
+                                "audio_s_per_s": round(sec / (ms / 1e3), 1), "useful_tflops": round(tf, 1),
+                                "frac_bf16_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+            del lfr
+    finally:
+        enc.close()
     return out
 
 
@@ -492,7 +548,7 @@ def profile_summary(kind: str, directory: str, bench_log: str = None, copy_dir: 
     import hashlib
     src = os.path.join(ROOT, "qwen3_kv_cache_amd", "csrc")
     shas = {f: hashlib.sha256(open(os.path.join(src, f), "rb").read()).hexdigest()
-            for f in ("qdec_decode.hip", "qdec_kernels.hip")}
+            for f in ("qdec_decode.hip", "qdec_kernels.hip", "qdec_encoder.hip")}
     out = []
     if kind == "stats":
         rows = _csv_rows(directory, "kernel_stats.csv")
@@ -510,10 +566,15 @@ def profile_summary(kind: str, directory: str, bench_log: str = None, copy_dir: 
             line = [ln for ln in open(bench_log) if ln.startswith("{")]
             if line:
                 b = json.loads(line[-1])
-                n = b["config"]["decode_steps"]
-                out.append(f"decode_us_per_token_from_profile: {avg / n:.2f}" if dec else "")
-                out.append(f"bench line of the same run (under the profiler): decode {b['value']} tok/s, "
-                           f"roofline {b['roofline']['achieved']} GB/s = {100 * b['roofline']['frac']:.1f}% of 8 TB/s")
+                if "config" in b:
+                    n = b["config"]["decode_steps"]
+                    out.append(f"decode_us_per_token_from_profile: {avg / n:.2f}" if dec else "")
+                    out.append(f"bench line of the same run (under the profiler): decode {b['value']} tok/s, "
+                               f"roofline {b['roofline']['achieved']} GB/s = {100 * b['roofline']['frac']:.1f}% "
+                               "of 8 TB/s")
+                else:
+                    out.append("")
+                    out.append("bench line of the same run (under the profiler): " + json.dumps(b))
     else:
         def per_dispatch(d, counter, kernel):
             rows = [r for r in _csv_rows(d, "counter_collection.csv") if r["Counter_Name"] == counter and kernel in r["Kernel_Name"]]
@@ -550,6 +611,8 @@ def main():
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--adaptor-only", action="store_true",
                     help="time only the audio adaptor (qdec_adaptor_run) and print its JSON")
+    ap.add_argument("--encoder-only", action="store_true",
+                    help="time only the frontend + SAN-M encoder (qdec_encoder_run) and print its JSON")
     ap.add_argument("--no-others", action="store_true",
                     help="skip the other workloads the default run also reports (B=16, long and 8k prompts)")
     ap.add_argument("--trace", action="store_true",
@@ -577,6 +640,9 @@ def main():
         return
     if a.adaptor_only:
         print(json.dumps({"adaptor": measure_adaptor()}), flush=True)
+        return
+    if a.encoder_only:
+        print(json.dumps({"encoder": measure_encoder()}), flush=True)
         return
 
     import torch
@@ -676,6 +742,7 @@ def main():
         line["other_workloads"] = others
         line["sampling"] = measure_sampling(model, w.shape.vocab)
         line["adaptor"] = measure_adaptor()
+        line["encoder"] = measure_encoder()
     if a.cpu_sample > 0 and not a.q8:
         line["cpu_baseline"] = cpu_baseline(w, W, a.cpu_sample)
     model.close()
