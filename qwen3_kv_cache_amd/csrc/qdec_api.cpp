@@ -117,6 +117,20 @@ int dev_alloc(T** p, size_t n, const char* what) {
   return QDEC_OK;
 }
 
+// A split-K workspace for the tiled GEMM (kSplitKFloats fp32 partials).
+struct SplitKBuf {
+  SplitK sk{nullptr, 0};
+};
+int alloc_splitk(SplitKBuf* b) {
+  if (int e = dev_alloc(&b->sk.P, kSplitKFloats, "split-K partials")) return e;
+  b->sk.floats = kSplitKFloats;
+  return QDEC_OK;
+}
+void free_splitk(SplitKBuf* b) {
+  (void)hipFree(b->sk.P);
+  b->sk.P = nullptr;
+}
+
 }  // namespace
 
 struct qdec_model {
@@ -203,6 +217,7 @@ struct qdec_model {
   } st_ids, st_pt;
   size_t layer_elems = 0, off_o = 0, off_gu = 0, off_d = 0;
   int norm_elems = 0;
+  SplitKBuf split;  // the prefill GEMMs' split-K workspace
 };
 
 struct qdec_state {
@@ -301,6 +316,7 @@ void free_model(qdec_model* m) {
   (void)hipFree(m->argmax_tmp);
   free_prefill(m);
   (void)hipFree(m->ll);
+  free_splitk(&m->split);
   if (m->err_host) (void)hipHostFree(m->err_host);
   for (qdec_model::Staging* g : {&m->st_ids, &m->st_pt}) {
     if (g->host) (void)hipHostFree(g->host);
@@ -599,13 +615,14 @@ int run_layers(qdec_model* m, int T, float* X, float* QKV, float* Attn, float* Z
     return launch_rms_apply(src, T, K, gain, d.eps, (float*)A0, st);
   };
   const bool fuse_o = attn_split && bf;  // both bf16 GEMMs read the same hi/lo operand
+  SplitK* sk = &m->split.sk;
   const bool fuse_z = gemm_tiled_fits(bf, T, d.H, 2 * d.F);  // the split epilogue is the tiled kernel's
   uint16_t* zhi = (uint16_t*)Z;
   uint16_t* zlo = zhi + (size_t)T * d.F;
   for (int l = 0; l < d.L; ++l) {
     const LayerW& w = m->layers[l];
     LAUNCH(norm_in(X, d.H, w.in_norm));
-    LAUNCH(launch_gemm(bf, EPI_STORE, A0, A1, T, d.H, w.wqkv, d.qkv(), QKV, d.qkv(), st));
+    LAUNCH(launch_gemm(bf, EPI_STORE, A0, A1, T, d.H, w.wqkv, d.qkv(), QKV, d.qkv(), st, nullptr, sk));
     if (int e = rope(l)) return e;
     if (fuse_o) {
       if (int e = attn(l, (uint16_t*)A0, (uint16_t*)A1)) return e;
@@ -613,16 +630,16 @@ int run_layers(qdec_model* m, int T, float* X, float* QKV, float* Attn, float* Z
       if (int e = attn(l, nullptr, nullptr)) return e;
       LAUNCH(norm_in(Attn, d.NQ * d.D, nullptr));
     }
-    LAUNCH(launch_gemm(bf, EPI_RESID, A0, A1, T, d.NQ * d.D, w.wo, d.H, X, d.H, st));
+    LAUNCH(launch_gemm(bf, EPI_RESID, A0, A1, T, d.NQ * d.D, w.wo, d.H, X, d.H, st, nullptr, sk));
     LAUNCH(norm_in(X, d.H, w.post_norm));
     if (fuse_z) {
       LAUNCH(launch_gemm_swiglu_split((const uint16_t*)A0, (const uint16_t*)A1, T, d.H, (const uint16_t*)w.wgu,
                                       2 * d.F, zhi, zlo, d.F, st));
-      LAUNCH(launch_gemm(bf, EPI_RESID, zhi, zlo, T, d.F, w.wd, d.H, X, d.H, st));
+      LAUNCH(launch_gemm(bf, EPI_RESID, zhi, zlo, T, d.F, w.wd, d.H, X, d.H, st, nullptr, sk));
     } else {
-      LAUNCH(launch_gemm(bf, EPI_SWIGLU, A0, A1, T, d.H, w.wgu, 2 * d.F, Z, d.F, st));
+      LAUNCH(launch_gemm(bf, EPI_SWIGLU, A0, A1, T, d.H, w.wgu, 2 * d.F, Z, d.F, st, nullptr, sk));
       LAUNCH(norm_in(Z, d.F, nullptr));
-      LAUNCH(launch_gemm(bf, EPI_RESID, A0, A1, T, d.F, w.wd, d.H, X, d.H, st));
+      LAUNCH(launch_gemm(bf, EPI_RESID, A0, A1, T, d.F, w.wd, d.H, X, d.H, st, nullptr, sk));
     }
   }
   return QDEC_OK;
@@ -1004,6 +1021,10 @@ int qdec_create(const qdec_config* cfg, const qdec_weights* w, void* hip_stream,
     }
     *m->err_host = 0;
     if ((he = hipHostGetDevicePointer((void**)&m->err_dev, m->err_host, 0))) return fail_dev("error flag map", he);
+    if ((e = alloc_splitk(&m->split))) {
+      free_model(m);
+      return e;
+    }
   }
   if ((he = hipStreamSynchronize(st))) return fail_dev("weight packing", he);
   if ((e = ensure_rope(m, 4096))) {
@@ -1308,6 +1329,7 @@ struct qdec_adaptor {
   };
   std::vector<Block> blocks;
   float* vecs = nullptr;  // every bias and norm vector, fp32
+  SplitKBuf split;        // split-K workspace of the GEMMs
   // scratch for up to `cap` frames
   int cap = 0;
   uint16_t* A0 = nullptr;  // bf16 hi of the current GEMM operand
@@ -1340,6 +1362,7 @@ void free_adaptor(qdec_adaptor* a) {
   for (auto& b : a->blocks)
     if (b.wqkv) (void)hipFree(b.wqkv);
   if (a->vecs) (void)hipFree(a->vecs);
+  free_splitk(&a->split);
   delete a;
 }
 
@@ -1414,6 +1437,10 @@ int qdec_adaptor_create(const qdec_adaptor_config* cfg, const qdec_adaptor_weigh
     return e;
   }
   hipStream_t st = a->stream;
+  if (int e = alloc_splitk(&a->split)) {
+    free_adaptor(a);
+    return e;
+  }
   auto fail_dev = [&](const char* what, hipError_t he) {
     const int r = fail(QDEC_E_DEVICE, "%s: %s", what, hipGetErrorString(he));
     free_adaptor(a);
@@ -1485,18 +1512,19 @@ int qdec_adaptor_run(qdec_adaptor* a, const float* frames_dev, int32_t n_frames,
   uint16_t *A0 = a->A0, *A1 = a->A1;
   const Dims ad = adaptor_dims(c);
   LAUNCH(launch_rms_split(frames_dev, T, c.enc_dim, nullptr, 0.f, A0, A1, st));
-  LAUNCH(launch_gemm(true, EPI_RELU, A0, A1, T, c.enc_dim, a->w1, c.mid_dim, a->H, c.mid_dim, st, a->b1));
+  SplitK* sk = &a->split.sk;
+  LAUNCH(launch_gemm(true, EPI_RELU, A0, A1, T, c.enc_dim, a->w1, c.mid_dim, a->H, c.mid_dim, st, a->b1, sk));
   LAUNCH(launch_rms_split(a->H, T, c.mid_dim, nullptr, 0.f, A0, A1, st));
-  LAUNCH(launch_gemm(true, EPI_STORE, A0, A1, T, c.mid_dim, a->w2, D, out_dev, D, st, a->b2));
+  LAUNCH(launch_gemm(true, EPI_STORE, A0, A1, T, c.mid_dim, a->w2, D, out_dev, D, st, a->b2, sk));
   for (const qdec_adaptor::Block& k : a->blocks) {
     LAUNCH(launch_ln_split(out_dev, T, D, k.n1g, k.n1b, c.ln_eps, A0, A1, st));
-    LAUNCH(launch_gemm(true, EPI_STORE, A0, A1, T, D, k.wqkv, 3 * D, a->QKV, 3 * D, st, k.bqkv));
+    LAUNCH(launch_gemm(true, EPI_STORE, A0, A1, T, D, k.wqkv, 3 * D, a->QKV, 3 * D, st, k.bqkv, sk));
     LAUNCH(launch_attn_prefill(ad, a->QKV, T, nullptr, a->kv, st, A0, A1, false));
-    LAUNCH(launch_gemm(true, EPI_RESID, A0, A1, T, D, k.wo, D, out_dev, D, st, k.bo));
+    LAUNCH(launch_gemm(true, EPI_RESID, A0, A1, T, D, k.wo, D, out_dev, D, st, k.bo, sk));
     LAUNCH(launch_ln_split(out_dev, T, D, k.n2g, k.n2b, c.ln_eps, A0, A1, st));
-    LAUNCH(launch_gemm(true, EPI_RELU, A0, A1, T, D, k.fc1, F, a->H, F, st, k.bf1));
+    LAUNCH(launch_gemm(true, EPI_RELU, A0, A1, T, D, k.fc1, F, a->H, F, st, k.bf1, sk));
     LAUNCH(launch_rms_split(a->H, T, F, nullptr, 0.f, A0, A1, st));
-    LAUNCH(launch_gemm(true, EPI_RESID, A0, A1, T, F, k.fc2, D, out_dev, D, st, k.bf2));
+    LAUNCH(launch_gemm(true, EPI_RESID, A0, A1, T, F, k.fc2, D, out_dev, D, st, k.bf2, sk));
   }
   return ok();
 }
@@ -1532,6 +1560,7 @@ struct qdec_encoder {
   int* mel_range = nullptr;
   const double* inv_freq = nullptr;
   FrontTables ft{};
+  SplitKBuf split;  // split-K workspace of the GEMMs
   // scratch for up to cap_rows LFR rows (cap_rows * lfr_n + lfr_m frames)
   int cap_rows = 0;
   float* fb = nullptr;
@@ -1564,6 +1593,7 @@ void free_encoder(qdec_encoder* e) {
     if (b.wqkv) (void)hipFree(b.wqkv);
   for (void* p : {(void*)e->vecs, (void*)e->tab, (void*)e->mel_range})
     if (p) (void)hipFree(p);
+  free_splitk(&e->split);
   delete e;
 }
 
@@ -1598,6 +1628,7 @@ int encoder_blocks(qdec_encoder* e, int T, float* out) {
   hipStream_t st = e->stream;
   uint16_t *A0 = e->A0, *A1 = e->A1;
   const Dims ad{1, D, c.n_head, c.n_head, 128, 0, 0, 0.f};
+  SplitK* sk = &e->split.sk;
   for (size_t b = 0; b < e->blocks.size(); ++b) {
     const qdec_encoder::Block& k = e->blocks[b];
     const bool stem = b == 0;
@@ -1605,14 +1636,15 @@ int encoder_blocks(qdec_encoder* e, int T, float* out) {
       LAUNCH(launch_ln_split(e->x0, T, e->in_dim, k.n1g, k.n1b, c.ln_eps, A0, A1, st, e->in_pad));
     else
       LAUNCH(launch_ln_split(e->X, T, D, k.n1g, k.n1b, c.ln_eps, A0, A1, st));
-    LAUNCH(launch_gemm(true, EPI_STORE, A0, A1, T, stem ? e->in_pad : D, k.wqkv, 3 * D, e->QKV, 3 * D, st, k.bqkv));
+    LAUNCH(launch_gemm(true, EPI_STORE, A0, A1, T, stem ? e->in_pad : D, k.wqkv, 3 * D, e->QKV, 3 * D, st, k.bqkv,
+                       sk));
     LAUNCH(launch_attn_prefill(ad, e->QKV, T, nullptr, e->kv, st, A0, A1, false));
     LAUNCH(launch_fsmn(e->QKV, 3 * D, T, D, c.fsmn_kernel, k.taps, !stem, e->X, st));
-    LAUNCH(launch_gemm(true, EPI_RESID, A0, A1, T, D, k.wo, D, e->X, D, st, k.bo));
+    LAUNCH(launch_gemm(true, EPI_RESID, A0, A1, T, D, k.wo, D, e->X, D, st, k.bo, sk));
     LAUNCH(launch_ln_split(e->X, T, D, k.n2g, k.n2b, c.ln_eps, A0, A1, st));
-    LAUNCH(launch_gemm(true, EPI_RELU, A0, A1, T, D, k.ffn1, F, e->H, F, st, k.bf1));
+    LAUNCH(launch_gemm(true, EPI_RELU, A0, A1, T, D, k.ffn1, F, e->H, F, st, k.bf1, sk));
     LAUNCH(launch_rms_split(e->H, T, F, nullptr, 0.f, A0, A1, st));
-    LAUNCH(launch_gemm(true, EPI_RESID, A0, A1, T, F, k.ffn2, D, e->X, D, st, k.bf2));
+    LAUNCH(launch_gemm(true, EPI_RESID, A0, A1, T, F, k.ffn2, D, e->X, D, st, k.bf2, sk));
     if ((int)b == c.n_main) LAUNCH(launch_ln_apply(e->X, T, D, e->an_g, e->an_b, c.ln_eps, e->X, st));
   }
   LAUNCH(launch_ln_apply(e->X, T, D, e->tn_g, e->tn_b, c.ln_eps, out, st));
@@ -1697,6 +1729,10 @@ int qdec_encoder_create(const qdec_encoder_config* cfg, const qdec_encoder_weigh
   const size_t per_block = 2 * std::max(W, D) + 3 * D + D + 2 * D + F + D + D * K;
   const size_t nvec = (size_t)nb * per_block + 4 * D;
   if (int r = dev_alloc(&e->vecs, nvec, "encoder vectors")) {
+    free_encoder(e);
+    return r;
+  }
+  if (int r = alloc_splitk(&e->split)) {
     free_encoder(e);
     return r;
   }

@@ -148,17 +148,27 @@ hipError_t launch_ln_split(const float* X, int T, int K, const float* gain, cons
                            uint16_t* hi, uint16_t* lo, hipStream_t st, int ldo = 0);
 hipError_t launch_rms_apply(const float* X, int T, int K, const float* gain, float eps, float* out,
                             hipStream_t st);
+// Workspace of the tiled GEMM's split-K (one per model, adaptor or encoder;
+// launches that share one must run on one stream): fp32 partials of C, one
+// [M, N] slab per split.
+struct SplitK {
+  float* P;
+  size_t floats;
+};
+constexpr size_t kSplitKFloats = (size_t)16 << 20;  // 64 MB
 // C[M, N] (+)= A[M, K] . W[N, K]^T with a bf16 hi/lo split A (bf16 weights)
-// or fp32 A (fp32 weights); the tiled MFMA kernel for M > 64.
+// or fp32 A (fp32 weights); the tiled MFMA kernel for M > 64 (with sk, also
+// below 128 tiles, splitting K).
 // bias (fp32 [N], bf16 weights only) is added to each output before the
 // epilogue (STORE, RESID, RELU); nullptr for none.
 hipError_t launch_gemm(bool bf16, Epi epi, const void* A0, const void* A1, int M, int K, const void* W, int N,
-                       float* C, int ldc, hipStream_t st, const float* bias = nullptr);
-// Whether launch_gemm takes the tiled MFMA kernel for this shape.
+                       float* C, int ldc, hipStream_t st, const float* bias = nullptr, SplitK* sk = nullptr);
+// Whether launch_gemm takes the tiled MFMA kernel for this shape without a
+// split-K workspace.
 bool gemm_tiled_fits(bool bf16, int M, int K, int N);
 // The SwiGLU GEMM on the tiled kernel, its output Z[M, N / 2] (row pitch ldz)
-// written as bf16 hi and lo (the down projection's operand); shapes that
-// gemm_tiled_fits rejects return hipErrorInvalidValue.
+// written as bf16 hi and lo (the down projection's operand); shapes the
+// tiled kernel cannot take return hipErrorInvalidValue.
 hipError_t launch_gemm_swiglu_split(const uint16_t* A0, const uint16_t* A1, int M, int K, const uint16_t* W, int N,
                                     uint16_t* zhi, uint16_t* zlo, int ldz, hipStream_t st);
 hipError_t launch_to_f32(const void* src, bool bf16, size_t n, float* dst, hipStream_t st);

@@ -1505,6 +1505,15 @@ constexpr int P = BK;  // bf16 pitch of an LDS row (chunks XOR-swizzled)
 __device__ __forceinline__ int tg_sw(int r, int c) { return r * P + 8 * (c ^ ((r >> 2) & 3)); }
 }  // namespace tg
 
+// Split-K of the tiled GEMM (grid z = split): split z covers K steps
+// [z kc, (z + 1) kc) / BK and stores its fp32 partial of C to
+// P[z][row][col]; splitk_reduce_kernel then sums the splits in order and
+// applies the epilogue (the kernel boundary makes every partial visible).
+struct TiledSplit {
+  float* P;  // splits * M * N floats (null: no split)
+  int kc;    // K per split (a multiple of BK)
+};
+
 template <int EPI>
 __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint16_t* __restrict__ Ahi,
                                                           const uint16_t* __restrict__ Alo, int M, int K,
@@ -1512,7 +1521,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint16_t* __restr
                                                           float* __restrict__ C, int ldc,
                                                           uint16_t* __restrict__ Zhi,
                                                           uint16_t* __restrict__ Zlo,
-                                                          const float* __restrict__ bias) {
+                                                          const float* __restrict__ bias, TiledSplit sp) {
   using namespace tg;
   __shared__ uint16_t sAh[2][BM * P], sAl[2][BM * P], sW[2][BN * P];
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
@@ -1567,12 +1576,13 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint16_t* __restr
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = K / BK;
-  QDEC_TG_LOAD(0)
+  const int S = gridDim.z, kz = blockIdx.z;
+  const int kbeg = kz * (sp.kc / BK), nk = min(K / BK, kbeg + sp.kc / BK);
+  QDEC_TG_LOAD(kbeg * BK)
   QDEC_TG_STORE(0)
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
+  for (int kt = kbeg; kt < nk; ++kt) {
+    const int buf = (kt - kbeg) & 1;
     if (kt + 1 < nk) {
       QDEC_TG_LOAD((kt + 1) * BK)
     }
@@ -1600,6 +1610,22 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint16_t* __restr
   }
 #undef QDEC_TG_LOAD
 #undef QDEC_TG_STORE
+
+  if (S > 1) {
+    float* pz = sp.P + (size_t)kz * M * N;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = n0 + wn * 64 + 16 * j + c16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = m0 + wm * 64 + 16 * i + 4 * gq + e;
+          if (row < M) pz[(size_t)row * N + col] = acc[i][j][e];
+        }
+      }
+    return;
+  }
 
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -1637,6 +1663,50 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint16_t* __restr
         }
       }
     }
+}
+
+// Sum of the S split partials P[z][row][col] in split order, plus bias, into
+// C by the epilogue (STORE, RESID or RELU); 4 columns per thread.
+template <int EPI>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ P, int S, int M, int N,
+                                                            float* __restrict__ C, int ldc,
+                                                            const float* __restrict__ bias) {
+  const size_t i4 = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t n4 = (size_t)M * N / 4;
+  if (i4 >= n4) return;
+  const size_t i = i4 * 4;
+  const int row = (int)(i / N), col = (int)(i % N);
+  float4 v = *reinterpret_cast<const float4*>(P + i);
+  for (int z = 1; z < S; ++z) {
+    const float4 t = *reinterpret_cast<const float4*>(P + (size_t)z * M * N + i);
+    v.x += t.x;
+    v.y += t.y;
+    v.z += t.z;
+    v.w += t.w;
+  }
+  if (bias) {
+    v.x += bias[col];
+    v.y += bias[col + 1];
+    v.z += bias[col + 2];
+    v.w += bias[col + 3];
+  }
+  float* c = C + (size_t)row * ldc + col;
+  if (EPI == EPI_RESID) {
+    c[0] += v.x;
+    c[1] += v.y;
+    c[2] += v.z;
+    c[3] += v.w;
+  } else if (EPI == EPI_RELU) {
+    c[0] = fmaxf(v.x, 0.f);
+    c[1] = fmaxf(v.y, 0.f);
+    c[2] = fmaxf(v.z, 0.f);
+    c[3] = fmaxf(v.w, 0.f);
+  } else {
+    c[0] = v.x;
+    c[1] = v.y;
+    c[2] = v.z;
+    c[3] = v.w;
+  }
 }
 
 // fp32 weights: C[M, N] (+)= A[M, K] . W[N, K]^T on the vector units.
@@ -2119,28 +2189,75 @@ bool gemm_tiled_fits(bool bf16, int M, int K, int N) {
   return bf16 && M > 64 && N % tg::BN == 0 && K % tg::BK == 0 && (N / tg::BN) * ((M + tg::BM - 1) / tg::BM) >= 128;
 }
 
+namespace {
+
+// The tiled kernel's plan for a shape: splits (1: none) and K per split.
+// Below 128 tiles a workspace lets the K range split until about 256
+// workgroups run (at most 8 splits, at least four K steps each), for the
+// epilogues the reduction kernel applies (STORE, RESID, RELU).
+struct TiledPlan {
+  bool ok;
+  int S, kc;
+};
+TiledPlan tiled_plan(bool bf16, Epi epi, int M, int K, int N, const SplitK* sk) {
+  TiledPlan p{false, 1, K};
+  if (!bf16 || M <= 64 || N % tg::BN || K % tg::BK) return p;
+  const int tiles = (N / tg::BN) * ((M + tg::BM - 1) / tg::BM), nk = K / tg::BK;
+  if (tiles >= 128) {
+    p.ok = true;
+    return p;
+  }
+  if (!sk || (epi != EPI_STORE && epi != EPI_RESID && epi != EPI_RELU)) return p;
+  const int S = std::min(std::min(8, (256 + tiles - 1) / tiles), nk / 4);
+  if (S < 2 || (size_t)S * M * N > sk->floats) return p;
+  const int steps = (nk + S - 1) / S;
+  p.ok = true;
+  p.kc = steps * tg::BK;
+  p.S = (nk + steps - 1) / steps;
+  return p;
+}
+
+}  // namespace
+
 hipError_t launch_gemm_swiglu_split(const uint16_t* A0, const uint16_t* A1, int M, int K, const uint16_t* W, int N,
                                     uint16_t* zhi, uint16_t* zlo, int ldz, hipStream_t st) {
   if (!gemm_tiled_fits(true, M, K, N)) return hipErrorInvalidValue;
   const dim3 grid(N / tg::BN, (M + tg::BM - 1) / tg::BM);
-  gemm_tiled_kernel<EPI_SWIGLU_SPLIT><<<grid, 256, 0, st>>>(A0, A1, M, K, W, N, nullptr, ldz, zhi, zlo, nullptr);
+  gemm_tiled_kernel<EPI_SWIGLU_SPLIT><<<grid, 256, 0, st>>>(A0, A1, M, K, W, N, nullptr, ldz, zhi, zlo, nullptr,
+                                                            TiledSplit{nullptr, K});
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(bool bf16, Epi epi, const void* A0, const void* A1, int M, int K, const void* W, int N,
-                       float* C, int ldc, hipStream_t st, const float* bias) {
+                       float* C, int ldc, hipStream_t st, const float* bias, SplitK* sk) {
   if ((bias || epi == EPI_RELU) && (!bf16 || epi == EPI_SWIGLU)) return hipErrorInvalidValue;
-  if (gemm_tiled_fits(bf16, M, K, N)) {
-    const dim3 grid(N / tg::BN, (M + tg::BM - 1) / tg::BM);
+  const TiledPlan p = tiled_plan(bf16, epi, M, K, N, sk);
+  if (p.ok) {
+    const dim3 grid(N / tg::BN, (M + tg::BM - 1) / tg::BM, p.S);
     const uint16_t *hi = (const uint16_t*)A0, *lo = (const uint16_t*)A1, *w = (const uint16_t*)W;
+    const TiledSplit t{p.S > 1 ? sk->P : nullptr, p.kc};
+    if (p.S > 1) {
+      // partials first (no epilogue), then the ordered sum with the epilogue
+      gemm_tiled_kernel<EPI_STORE><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, nullptr, N, nullptr, nullptr, nullptr, t);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const unsigned blocks = (unsigned)(((size_t)M * N / 4 + 255) / 256);
+      if (epi == EPI_RESID)
+        splitk_reduce_kernel<EPI_RESID><<<blocks, 256, 0, st>>>(sk->P, p.S, M, N, C, ldc, bias);
+      else if (epi == EPI_RELU)
+        splitk_reduce_kernel<EPI_RELU><<<blocks, 256, 0, st>>>(sk->P, p.S, M, N, C, ldc, bias);
+      else
+        splitk_reduce_kernel<EPI_STORE><<<blocks, 256, 0, st>>>(sk->P, p.S, M, N, C, ldc, bias);
+      return hipGetLastError();
+    }
     if (epi == EPI_STORE)
-      gemm_tiled_kernel<EPI_STORE><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc, nullptr, nullptr, bias);
+      gemm_tiled_kernel<EPI_STORE><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc, nullptr, nullptr, bias, t);
     else if (epi == EPI_RESID)
-      gemm_tiled_kernel<EPI_RESID><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc, nullptr, nullptr, bias);
+      gemm_tiled_kernel<EPI_RESID><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc, nullptr, nullptr, bias, t);
     else if (epi == EPI_RELU)
-      gemm_tiled_kernel<EPI_RELU><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc, nullptr, nullptr, bias);
+      gemm_tiled_kernel<EPI_RELU><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc, nullptr, nullptr, bias, t);
     else
-      gemm_tiled_kernel<EPI_SWIGLU><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc, nullptr, nullptr, nullptr);
+      gemm_tiled_kernel<EPI_SWIGLU><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc, nullptr, nullptr, nullptr, t);
     return hipGetLastError();
   }
   if (bf16) {
