@@ -732,7 +732,7 @@ int run_prefill(qdec_state* s, int T, const float* audio, int a0, int La, float*
     return 0;
   };
   auto attn = [&](int, uint16_t* hi, uint16_t* lo) -> int {
-    LAUNCH(launch_attn_prefill(d, m->pQKV, T, m->pAttn, m->pKV, st, hi, lo));
+    LAUNCH(launch_attn_prefill(d, m->pQKV, T, m->pAttn, m->pKV, st, hi, lo, true, &m->split.sk));
     return 0;
   };
   if (fused) {
@@ -1519,7 +1519,7 @@ int qdec_adaptor_run(qdec_adaptor* a, const float* frames_dev, int32_t n_frames,
   for (const qdec_adaptor::Block& k : a->blocks) {
     LAUNCH(launch_ln_split(out_dev, T, D, k.n1g, k.n1b, c.ln_eps, A0, A1, st));
     LAUNCH(launch_gemm(true, EPI_STORE, A0, A1, T, D, k.wqkv, 3 * D, a->QKV, 3 * D, st, k.bqkv, sk));
-    LAUNCH(launch_attn_prefill(ad, a->QKV, T, nullptr, a->kv, st, A0, A1, false));
+    LAUNCH(launch_attn_prefill(ad, a->QKV, T, nullptr, a->kv, st, A0, A1, false, sk));
     LAUNCH(launch_gemm(true, EPI_RESID, A0, A1, T, D, k.wo, D, out_dev, D, st, k.bo, sk));
     LAUNCH(launch_ln_split(out_dev, T, D, k.n2g, k.n2b, c.ln_eps, A0, A1, st));
     LAUNCH(launch_gemm(true, EPI_RELU, A0, A1, T, D, k.fc1, F, a->H, F, st, k.bf1, sk));
@@ -1638,7 +1638,7 @@ int encoder_blocks(qdec_encoder* e, int T, float* out) {
       LAUNCH(launch_ln_split(e->X, T, D, k.n1g, k.n1b, c.ln_eps, A0, A1, st));
     LAUNCH(launch_gemm(true, EPI_STORE, A0, A1, T, stem ? e->in_pad : D, k.wqkv, 3 * D, e->QKV, 3 * D, st, k.bqkv,
                        sk));
-    LAUNCH(launch_attn_prefill(ad, e->QKV, T, nullptr, e->kv, st, A0, A1, false));
+    LAUNCH(launch_attn_prefill(ad, e->QKV, T, nullptr, e->kv, st, A0, A1, false, sk));
     LAUNCH(launch_fsmn(e->QKV, 3 * D, T, D, c.fsmn_kernel, k.taps, !stem, e->X, st));
     LAUNCH(launch_gemm(true, EPI_RESID, A0, A1, T, D, k.wo, D, e->X, D, st, k.bo, sk));
     LAUNCH(launch_ln_split(e->X, T, D, k.n2g, k.n2b, c.ln_eps, A0, A1, st));

@@ -136,9 +136,12 @@ hipError_t launch_attn_rows(const Dims& d, const AttnRows& a, int nsplit, hipStr
 bool attn_prefill_uses_split(const Dims& d);
 int kv_split_pad(int T);
 // causal = false (only where attn_prefill_uses_split): every query sees every key.
+// With a split-K workspace (sk) and few query blocks, each block's key range
+// is split and the partials merged by a second kernel.
+struct SplitK;
 hipError_t launch_attn_prefill(const Dims& d, const float* qkv, int T, float* out, uint16_t* const kv[4],
                                hipStream_t st, uint16_t* out_hi = nullptr, uint16_t* out_lo = nullptr,
-                               bool causal = true);
+                               bool causal = true, SplitK* sk = nullptr);
 
 hipError_t launch_rms_split(const float* X, int T, int K, const float* gain, float eps, uint16_t* hi,
                             uint16_t* lo, hipStream_t st);

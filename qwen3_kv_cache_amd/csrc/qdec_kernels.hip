@@ -852,7 +852,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
                                                                  const uint16_t* __restrict__ vtls, int Tp,
                                                                  float* __restrict__ out, int ldo, float qscale,
                                                                  uint16_t* __restrict__ ohi,
-                                                                 uint16_t* __restrict__ olo, int causal) {
+                                                                 uint16_t* __restrict__ olo, int causal,
+                                                                 float* __restrict__ part) {
   using namespace fa;
   constexpr int VH = GROUP * QS, QTB = 64 * QS;  // virtual heads per wave, queries per block
   __shared__ __bf16 Kh[KT * KP], Kl[KT * KP];
@@ -911,9 +912,13 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
   const uint16_t* kl_g = kls + (size_t)g * T * D;
   const uint16_t* vh_g = vths + (size_t)g * D * Tp;
   const uint16_t* vl_g = vtls + (size_t)g * D * Tp;
-  // causal: keys up to the block's last query; otherwise every key
+  // causal: keys up to the block's last query; otherwise every key. With
+  // gridDim.z = S > 1 the block's key tiles split into S contiguous ranges,
+  // range blockIdx.z here; its unnormalised partial goes to `part`.
   const int last_key = causal ? min(T, q0 + QTB) - 1 : T - 1;
-  for (int k0 = 0; k0 <= last_key; k0 += KT) {
+  const int S = gridDim.z, ntile = last_key / KT + 1, per = (ntile + S - 1) / S;
+  const int kt_end = min(ntile, ((int)blockIdx.z + 1) * per);
+  for (int k0 = blockIdx.z * per * KT; k0 < kt_end * KT; k0 += KT) {
     __syncthreads();
     // copies of the converted tiles: K rows of 16-byte chunks (key c / 16,
     // columns 8 (c % 16)), V^T rows (column d = c / 4, keys 8 (c % 4))
@@ -987,7 +992,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
       for (int j = 0; j < KB; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p = __builtin_amdgcn_exp2f(sc[hh][j][e] - m[hh]);
+          // a masked key counts 0 even while the base is still -inf (a key
+          // range that starts past this query sees no visible key)
+          const float p = sc[hh][j][e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[hh][j][e] - m[hh]);
           ps += p;
           const __bf16 h = (__bf16)p;
           ph[hh][j / 2][4 * (j % 2) + e] = h;
@@ -1016,6 +1023,27 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
       }
   }
 
+  if (S > 1) {
+    // partial of split z: o (unnormalised), the exponent base m and the sum l
+    // per (query, head), records of D + 4 floats (16-byte aligned) at
+    // part[((z T + q) NQ + h) (D + 4)] (NQ = ldo / D)
+    const int nq = ldo / D;
+#pragma unroll
+    for (int hh = 0; hh < VH; ++hh) {
+      if (qpv[hh] < T) {
+        float* pp = part + (((size_t)blockIdx.z * T + qpv[hh]) * nq + g * GROUP + hh % GROUP) * (D + 4);
+#pragma unroll
+        for (int b = 0; b < D / 16; ++b)
+          *reinterpret_cast<float4*>(pp + 16 * b + 4 * gq) =
+              make_float4(acc[hh][b][0], acc[hh][b][1], acc[hh][b][2], acc[hh][b][3]);
+        if (gq == 0) {
+          pp[D] = m[hh];
+          pp[D + 1] = lsum[hh];
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int hh = 0; hh < VH; ++hh) {
     if (qpv[hh] < T) {
@@ -1041,6 +1069,38 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
         }
       }
     }
+  }
+}
+
+// Merge of S key-range partials of the prefill attention: for query q and
+// head h, with bases m_z and sums l_z, o = sum_z 2^(m_z - M) o_z /
+// sum_z 2^(m_z - M) l_z, M = max_z m_z, in split order; written as fp32
+// (out) or as the O projection's bf16 hi / lo operand. One workgroup of D
+// threads per (query, head); a split that saw no key has m = -inf, l = 0.
+__global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict__ part, int S, int T, int nq,
+                                                         float* __restrict__ out, uint16_t* __restrict__ ohi,
+                                                         uint16_t* __restrict__ olo) {
+  constexpr int D = fa::D;
+  const int q = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+  float mx = -INFINITY;
+  for (int z = 0; z < S; ++z) mx = fmaxf(mx, part[(((size_t)z * T + q) * nq + h) * (D + 4) + D]);
+  float o = 0.f, l = 0.f;
+  for (int z = 0; z < S; ++z) {
+    const float* pp = part + (((size_t)z * T + q) * nq + h) * (D + 4);
+    const float mz = pp[D];
+    const float wz = mz == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mz - mx);
+    o = fmaf(wz, pp[d], o);
+    l = fmaf(wz, pp[D + 1], l);
+  }
+  const float v = o / l;
+  const size_t idx = (size_t)q * nq * D + (size_t)h * D + d;
+  if (ohi) {
+#pragma clang fp contract(off)
+    const uint16_t hb = f32_to_bf16_rne(v);
+    ohi[idx] = hb;
+    olo[idx] = f32_to_bf16_rne(v - bf16_to_f32(hb));
+  } else {
+    out[idx] = v;
   }
 }
 
@@ -2039,7 +2099,7 @@ bool attn_prefill_uses_split(const Dims& d) {
 }
 
 hipError_t launch_attn_prefill(const Dims& d, const float* qkv, int T, float* out, uint16_t* const kv[4],
-                               hipStream_t st, uint16_t* out_hi, uint16_t* out_lo, bool causal) {
+                               hipStream_t st, uint16_t* out_hi, uint16_t* out_lo, bool causal, SplitK* sk) {
   const int group = d.NQ / d.NKV;
   if ((out_hi != nullptr) != (out_lo != nullptr) || ((out_hi || !causal) && !attn_prefill_uses_split(d)))
     return hipErrorInvalidValue;
@@ -2056,16 +2116,30 @@ hipError_t launch_attn_prefill(const Dims& d, const float* qkv, int T, float* ou
     // 1024 positions the halved block count costs more than it saves)
     const bool two = group == 1 && T >= 1024;
     const int qtb = two ? 2 * fa::QT : fa::QT;
-    dim3 grid((T + qtb - 1) / qtb, d.NKV);
+    const int nqb = (T + qtb - 1) / qtb, ntile = (T + fa::KT - 1) / fa::KT;
+    // few blocks: split every block's key tiles until about 256 workgroups
+    // run (at most 8 ranges of at least two tiles), partials merged after
+    int S = 1;
+    if (sk && nqb * d.NKV < 128) {
+      S = std::min(std::min(8, (256 + nqb * d.NKV - 1) / (nqb * d.NKV)), ntile / 2);
+      if (S < 2 || (size_t)S * T * d.NQ * (fa::D + 4) > sk->floats) S = 1;
+    }
+    float* part = S > 1 ? sk->P : nullptr;
+    dim3 grid(nqb, d.NKV, S);
     if (group == 1 && !two)
       attn_prefill_mfma_kernel<1, 1><<<grid, 256, 0, st>>>(qkv, T, d.qkv(), kv[0], kv[1], kv[2], kv[3], Tp, out,
-                                                           d.NQ * d.D, qs, out_hi, out_lo, causal ? 1 : 0);
+                                                           d.NQ * d.D, qs, out_hi, out_lo, causal ? 1 : 0, part);
     else if (group == 2)
       attn_prefill_mfma_kernel<2, 1><<<grid, 256, 0, st>>>(qkv, T, d.qkv(), kv[0], kv[1], kv[2], kv[3], Tp, out,
-                                                        d.NQ * d.D, qs, out_hi, out_lo, causal ? 1 : 0);
+                                                        d.NQ * d.D, qs, out_hi, out_lo, causal ? 1 : 0, part);
     else
       attn_prefill_mfma_kernel<1, 2><<<grid, 256, 0, st>>>(qkv, T, d.qkv(), kv[0], kv[1], kv[2], kv[3], Tp, out,
-                                                        d.NQ * d.D, qs, out_hi, out_lo, causal ? 1 : 0);
+                                                        d.NQ * d.D, qs, out_hi, out_lo, causal ? 1 : 0, part);
+    if (S > 1) {
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      attn_merge_kernel<<<dim3(T, d.NQ), fa::D, 0, st>>>(part, S, T, d.NQ, out, out_hi, out_lo);
+    }
     return hipGetLastError();
   }
 #define QDEC_PATTN_CASE(DD, GG)                                                                      \
