@@ -10,18 +10,27 @@
 // attention and its slice of the O projection stay inside one XCD. The FFN is
 // split by z slices, one per group, and the down projection is split along the
 // same slices. A layer then needs two exchanges that span the whole chip (O
-// partials and down partials, both summed by every CU in a fixed order so all
-// copies of the residual stream are bit-identical) and two or three inside a
-// group. Correctness never depends on the placement, only speed: every
-// cross-CU word uses device scope.
+// partials and down partials, summed in two levels: the 8 groups' partials
+// of an element by its owner rank, republished inside each group, always in
+// the same order, so all copies of the residual stream are bit-identical)
+// and two or three inside a group.
 //
 // Exchange. A phase publishes each output as an 8-byte word: fp32 value in the
-// low half, a tag unique to (launch, step, layer, phase) in the high half,
-// stored and loaded as device-scope relaxed atomics. A consumer polls until
-// every word it needs carries the expected tag. Regions are double-buffered by
-// layer parity. Every wait has a time limit; on expiry the workgroup raises a
-// host-visible error flag and stops waiting for the rest of the launch, so
-// every workgroup still runs to the end and the launch always drains.
+// low half, a tag unique to (launch, step, layer, phase) in the high half. A
+// consumer polls until every word it needs carries the expected tag. Words
+// that cross XCDs are device-scope relaxed atomics. Words that stay inside a
+// group are plain stores read with non-temporal loads, served by the XCD's
+// L2; that is correct only while the group's workgroups share one XCD, which
+// the host checks with a probe launch at model creation, falling back to
+// device scope for those words too (`local` = 0) when the placement differs.
+// Regions are double-buffered by layer parity. Every wait has a time limit;
+// on expiry the workgroup raises a host-visible error flag and stops waiting
+// for the rest of the launch, so every workgroup still runs to the end and
+// the launch always drains.
+//
+// Weights: bf16 or fp32 rows, or int8 codes (QDEC_Q8_0) whose fp16 block
+// scales ride along in one extra load per weight unit; each 16-code chunk's
+// partial dot is scaled by its block's scale before the lane reduction.
 //
 // Two roles per workgroup. A wave's vector-memory counter retires loads in
 // issue order, so a load needed now cannot complete before an earlier
