@@ -566,15 +566,59 @@ def profile_summary(kind: str, directory: str, bench_log: str = None, copy_dir: 
             line = [ln for ln in open(bench_log) if ln.startswith("{")]
             if line:
                 b = json.loads(line[-1])
-                if "config" in b:
+                if "config" in b and "roofline" in b:
                     n = b["config"]["decode_steps"]
                     out.append(f"decode_us_per_token_from_profile: {avg / n:.2f}" if dec else "")
                     out.append(f"bench line of the same run (under the profiler): decode {b['value']} tok/s, "
                                f"roofline {b['roofline']['achieved']} GB/s = {100 * b['roofline']['frac']:.1f}% "
                                "of 8 TB/s")
+                elif "config" in b:
+                    out.append("")
+                    out.append(f"bench line of the same run (under the profiler): {b['value']} {b['unit']}, "
+                               f"prefill {b['prefill_ms']} ms")
                 else:
                     out.append("")
                     out.append("bench line of the same run (under the profiler): " + json.dumps(b))
+    elif kind == "mfma":
+        # two counter runs of the prefill8k bench (one warm-up and one timed
+        # prefill each): MfmaUtil under <dir>/util, SQ_INSTS_VALU_MFMA_MOPS_BF16
+        # under <dir>/mops; the prefill kernels are every dispatch except the
+        # decode kernel, copies and set-up
+        def rows_of(d, counter):
+            return [r for r in _csv_rows(d, "counter_collection.csv") if r["Counter_Name"] == counter]
+        skip = ("decode_kernel", "__amd_rocclr", "clear_words", "to_f32", "q8_unpack", "xcc_probe")
+        util = [r for r in rows_of(os.path.join(directory, "util"), "MfmaUtil") if not any(k in r["Kernel_Name"] for k in skip)]
+        mops = [r for r in rows_of(os.path.join(directory, "mops"), "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+                if not any(k in r["Kernel_Name"] for k in skip)]
+        short = lambda n: n.replace("void ", "").replace("qdec::(anonymous namespace)::", "").split("(")[0][:40]
+        per = {}
+        for r in util:
+            k = short(r["Kernel_Name"])
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            e = per.setdefault(k, {"n": 0, "us": 0.0, "busy": 0.0, "mops": 0.0})
+            e["n"] += 1
+            e["us"] += dur
+            e["busy"] += float(r["Counter_Value"]) * dur
+        for r in mops:
+            per.setdefault(short(r["Kernel_Name"]), {"n": 0, "us": 0.0, "busy": 0.0, "mops": 0.0})["mops"] += float(
+                r["Counter_Value"])
+        n_prefill = 2
+        out.append(f"{'kernel':40s} {'dispatches':>10s} {'avg_us':>9s} {'MfmaUtil%':>10s} {'issued_TFLOP':>13s}")
+        for k, e in sorted(per.items(), key=lambda kv: -kv[1]["us"]):
+            if not e["n"]:
+                continue
+            out.append(f"{k:40s} {e['n']:10d} {e['us'] / e['n']:9.2f} {e['busy'] / max(e['us'], 1e-9):10.2f} "
+                       f"{e['mops'] * 512 / 1e12:13.3f}")
+        tot_us = sum(e["us"] for e in per.values())
+        busy = sum(e["busy"] for e in per.values()) / max(tot_us, 1e-9)
+        issued = sum(e["mops"] for e in per.values()) * 512 / n_prefill
+        import synth
+        useful = prefill_flops(synth.QWEN3_0P6B, 8192)
+        out += ["", "Values below are machine-readable by bench.py (key: value).",
+                f"source_sha256: {shas['qdec_kernels.hip']}", f"mfma_busy_pct_prefill_kernels: {busy:.2f}",
+                f"mfma_flops_issued_per_prefill: {issued:.4e}", f"useful_flops_per_prefill: {useful:.4e}", "",
+                f"Issued / useful MFMA FLOPs = {issued / useful:.3f}. Time-weighted MfmaUtil over the prefill kernels "
+                f"= {busy:.2f}%."]
     else:
         def per_dispatch(d, counter, kernel):
             rows = [r for r in _csv_rows(d, "counter_collection.csv") if r["Counter_Name"] == counter and kernel in r["Kernel_Name"]]
@@ -622,7 +666,7 @@ def main():
                     help="the main measurement on Q8_0 weights (int8 codes, fp16 block scales) of the same shape")
     ap.add_argument("--per-step", action="store_true",
                     help="decode with one launch per token (qdec_decode_step_dev) instead of one launch for all steps")
-    ap.add_argument("--profile-summary", choices=("stats", "traffic"),
+    ap.add_argument("--profile-summary", choices=("stats", "traffic", "mfma"),
                     help="print the profiles/ summary of rocprofv3 output under --profile-dir (no GPU use)")
     ap.add_argument("--profile-dir")
     ap.add_argument("--copy-dir", help="counter runs of --copy-probe (traffic summaries)")
