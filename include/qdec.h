@@ -39,6 +39,13 @@
  * kernel still runs to the end, its outputs are invalid, qdec_model_status()
  * reports QDEC_E_DEVICE once the stream has been synchronised, and every
  * later compute call on the model fails with QDEC_E_DEVICE.
+ *
+ * Device memory: the library's own allocations (packed weights, KV pages,
+ * scratch) can be capped for tests with the environment variable
+ * QDEC_DEVICE_LIMIT_BYTES, a decimal byte count read at each allocation: an
+ * allocation that would take the library's live device bytes past it fails
+ * with QDEC_E_OOM as if HBM were full. Memory the caller passes in is not
+ * counted. Decode steps after prefill allocate nothing.
  */
 #ifndef QDEC_H
 #define QDEC_H

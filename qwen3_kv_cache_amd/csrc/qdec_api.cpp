@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <unordered_map>
@@ -36,6 +37,53 @@ int fail(int code, const char* fmt, ...) {
 int ok() {
   g_err.clear();
   return QDEC_OK;
+}
+
+// Every device allocation of the library goes through dmalloc / dfree, which
+// keep the number of live bytes. The environment variable
+// QDEC_DEVICE_LIMIT_BYTES, read at each allocation, caps that number: an
+// allocation that would pass it fails as hipMalloc does when HBM is full, so a
+// test can reach every QDEC_E_OOM path on a GPU with memory to spare.
+std::mutex g_mem_mu;
+std::unordered_map<void*, size_t> g_mem_live;
+size_t g_mem_bytes = 0;
+
+hipError_t dmalloc_bytes(void** p, size_t bytes) {
+  *p = nullptr;
+  std::lock_guard<std::mutex> lock(g_mem_mu);
+  if (const char* lim = getenv("QDEC_DEVICE_LIMIT_BYTES")) {
+    char* end = nullptr;
+    const unsigned long long cap = strtoull(lim, &end, 10);
+    if (end != lim && *end == '\0' && (bytes > cap || g_mem_bytes > cap - bytes)) return hipErrorOutOfMemory;
+  }
+  const hipError_t e = hipMalloc(p, bytes);
+  if (e != hipSuccess) {
+    *p = nullptr;
+    return e;
+  }
+  if (*p) {
+    g_mem_live[*p] = bytes;
+    g_mem_bytes += bytes;
+  }
+  return hipSuccess;
+}
+
+template <typename T>
+hipError_t dmalloc(T** p, size_t bytes) {
+  return dmalloc_bytes((void**)p, bytes);
+}
+
+hipError_t dfree(void* p) {
+  if (!p) return hipSuccess;
+  {
+    std::lock_guard<std::mutex> lock(g_mem_mu);
+    auto it = g_mem_live.find(p);
+    if (it != g_mem_live.end()) {
+      g_mem_bytes -= it->second;
+      g_mem_live.erase(it);
+    }
+  }
+  return hipFree(p);
 }
 
 #define HIP_TRY(expr)                                                                       \
@@ -80,7 +128,7 @@ struct PagePool {
     const int want = n - (int)free_pages.size();
     const int npages = want < 32 ? 32 : want;
     void* p = nullptr;
-    if (hipMalloc(&p, (size_t)npages * page_bytes) != hipSuccess) {
+    if (dmalloc(&p, (size_t)npages * page_bytes) != hipSuccess) {
       (void)hipGetLastError();
       return fail(QDEC_E_OOM, "KV pool: cannot allocate %d pages of %zu bytes", npages, page_bytes);
     }
@@ -109,7 +157,7 @@ template <typename T>
 int dev_alloc(T** p, size_t n, const char* what) {
   *p = nullptr;
   if (n == 0) return QDEC_OK;
-  if (hipMalloc((void**)p, n * sizeof(T)) != hipSuccess) {
+  if (dmalloc((void**)p, n * sizeof(T)) != hipSuccess) {
     (void)hipGetLastError();
     *p = nullptr;
     return fail(QDEC_E_OOM, "cannot allocate %s (%zu bytes)", what, n * sizeof(T));
@@ -127,7 +175,7 @@ int alloc_splitk(SplitKBuf* b) {
   return QDEC_OK;
 }
 void free_splitk(SplitKBuf* b) {
-  (void)hipFree(b->sk.P);
+  (void)dfree(b->sk.P);
   b->sk.P = nullptr;
 }
 
@@ -262,17 +310,17 @@ int validate_config(const qdec_config* c) {
 }
 
 void free_prefill(qdec_model* m) {
-  (void)hipFree(m->p_ids);
-  (void)hipFree(m->pX);
-  (void)hipFree(m->pQKV);
-  (void)hipFree(m->pAttn);
+  (void)dfree(m->p_ids);
+  (void)dfree(m->pX);
+  (void)dfree(m->pQKV);
+  (void)dfree(m->pAttn);
   for (uint16_t*& p : m->pKV) {
-    (void)hipFree(p);
+    (void)dfree(p);
     p = nullptr;
   }
-  (void)hipFree(m->pZ);
-  (void)hipFree(m->pA0);
-  (void)hipFree(m->pA1);
+  (void)dfree(m->pZ);
+  (void)dfree(m->pA0);
+  (void)dfree(m->pA1);
   m->p_ids = nullptr;
   m->pX = m->pQKV = m->pAttn = m->pZ = nullptr;
   m->pA0 = m->pA1 = nullptr;
@@ -282,7 +330,7 @@ void free_prefill(qdec_model* m) {
 void free_batch(qdec_model* m) {
   for (void* p : {(void*)m->bX, (void*)m->bQKV, (void*)m->bAttn, (void*)m->bZ, m->bA0, m->bA1,
                   (void*)m->bLogits, (void*)m->bKeys, (void*)m->bTok, (void*)m->bAttnPart, (void*)m->bAttnCnt})
-    (void)hipFree(p);
+    (void)dfree(p);
   m->bX = m->bQKV = m->bAttn = m->bZ = m->bLogits = nullptr;
   m->bAttnPart = nullptr;
   m->bAttnCnt = nullptr;
@@ -297,32 +345,32 @@ void free_model(qdec_model* m) {
   if (!m) return;
   if (m->stream) (void)hipStreamSynchronize(m->stream);
   free_batch(m);
-  (void)hipFree(m->rP);
-  (void)hipFree(m->rCnt);
-  (void)hipFree(m->rSsq);
-  (void)hipFree(m->sBuf0);
-  (void)hipFree(m->sBuf1);
-  (void)hipFree(m->final_norm);
-  (void)hipFree(m->wbuf);
-  (void)hipFree(m->q_codes);
-  (void)hipFree(m->q_scales);
-  (void)hipFree(m->q_embed);
-  (void)hipFree(m->q_escale);
-  (void)hipFree(m->embed_own);
-  (void)hipFree(m->nbuf);
-  (void)hipFree(m->rope_cos);
-  (void)hipFree(m->rope_sin);
-  (void)hipFree(m->keys);
-  (void)hipFree(m->argmax_tmp);
+  (void)dfree(m->rP);
+  (void)dfree(m->rCnt);
+  (void)dfree(m->rSsq);
+  (void)dfree(m->sBuf0);
+  (void)dfree(m->sBuf1);
+  (void)dfree(m->final_norm);
+  (void)dfree(m->wbuf);
+  (void)dfree(m->q_codes);
+  (void)dfree(m->q_scales);
+  (void)dfree(m->q_embed);
+  (void)dfree(m->q_escale);
+  (void)dfree(m->embed_own);
+  (void)dfree(m->nbuf);
+  (void)dfree(m->rope_cos);
+  (void)dfree(m->rope_sin);
+  (void)dfree(m->keys);
+  (void)dfree(m->argmax_tmp);
   free_prefill(m);
-  (void)hipFree(m->ll);
+  (void)dfree(m->ll);
   free_splitk(&m->split);
   if (m->err_host) (void)hipHostFree(m->err_host);
   for (qdec_model::Staging* g : {&m->st_ids, &m->st_pt}) {
     if (g->host) (void)hipHostFree(g->host);
     if (g->ev) (void)hipEventDestroy(g->ev);
   }
-  for (void* c : m->pool.chunks) (void)hipFree(c);
+  for (void* c : m->pool.chunks) (void)dfree(c);
   delete m;
 }
 
@@ -344,15 +392,15 @@ int ensure_rope(qdec_model* m, int n_pos) {
   float *dc = nullptr, *ds = nullptr;
   if (int e = dev_alloc(&dc, c.size(), "RoPE table")) return e;
   if (int e = dev_alloc(&ds, s.size(), "RoPE table")) {
-    (void)hipFree(dc);
+    (void)dfree(dc);
     return e;
   }
   HIP_TRY(hipMemcpy(dc, c.data(), c.size() * sizeof(float), hipMemcpyHostToDevice));
   HIP_TRY(hipMemcpy(ds, s.data(), s.size() * sizeof(float), hipMemcpyHostToDevice));
   // older tables may still be read by queued work
   HIP_TRY(hipStreamSynchronize(m->stream));
-  (void)hipFree(m->rope_cos);
-  (void)hipFree(m->rope_sin);
+  (void)dfree(m->rope_cos);
+  (void)dfree(m->rope_sin);
   m->rope_cos = dc;
   m->rope_sin = ds;
   m->rope_cap = cap;
@@ -379,8 +427,8 @@ int ensure_prefill(qdec_model* m, int T) {
     return e;
   }
   const size_t abytes = m->bf16 ? 2 : 4;
-  if (hipMalloc(&m->pA0, (size_t)T * kmax * abytes) != hipSuccess ||
-      (m->bf16 && hipMalloc(&m->pA1, (size_t)T * kmax * abytes) != hipSuccess)) {
+  if (dmalloc(&m->pA0, (size_t)T * kmax * abytes) != hipSuccess ||
+      (m->bf16 && dmalloc(&m->pA1, (size_t)T * kmax * abytes) != hipSuccess)) {
     (void)hipGetLastError();
     free_prefill(m);
     return fail(QDEC_E_OOM, "cannot allocate prefill activations for %d tokens", T);
@@ -475,8 +523,8 @@ int ensure_batch(qdec_model* m, int nsplit) {
       free_batch(m);
       return e;
     }
-    if (hipMalloc(&m->bA0, (size_t)B * kmax * abytes) != hipSuccess ||
-        (m->bf16 && hipMalloc(&m->bA1, (size_t)B * kmax * abytes) != hipSuccess)) {
+    if (dmalloc(&m->bA0, (size_t)B * kmax * abytes) != hipSuccess ||
+        (m->bf16 && dmalloc(&m->bA1, (size_t)B * kmax * abytes) != hipSuccess)) {
       (void)hipGetLastError();
       free_batch(m);
       return fail(QDEC_E_OOM, "cannot allocate batch activations");
@@ -486,7 +534,7 @@ int ensure_batch(qdec_model* m, int nsplit) {
   }
   if (nsplit > m->b_nsplit_cap) {
     HIP_TRY(hipStreamSynchronize(m->stream));
-    (void)hipFree(m->bAttnPart);
+    (void)dfree(m->bAttnPart);
     m->bAttnPart = nullptr;
     m->b_nsplit_cap = 0;
     const size_t words = (size_t)B * d.NQ * nsplit * (d.D + 2);
@@ -515,9 +563,9 @@ int ensure_rows(qdec_model* m) {
   int e = 0;
   if ((e = dev_alloc(&m->rP, part, "GEMM partial tiles")) || (e = dev_alloc(&m->rCnt, (size_t)cnt, "GEMM counters")) ||
       (e = dev_alloc(&m->rSsq, nss * R, "RMSNorm partials"))) {
-    (void)hipFree(m->rP);
-    (void)hipFree(m->rCnt);
-    (void)hipFree(m->rSsq);
+    (void)dfree(m->rP);
+    (void)dfree(m->rCnt);
+    (void)dfree(m->rSsq);
     m->rP = nullptr;
     m->rSsq = nullptr;
     m->rCnt = nullptr;
@@ -720,11 +768,10 @@ int run_prefill(qdec_state* s, int T, const float* audio, int a0, int La, float*
   const Dims& d = m->d;
   hipStream_t st = m->stream;
   const bool bf = m->bf16;
-  LAUNCH(launch_reset_keys(m->keys, 1, st));
+  // the fused path's workspace exists already (qdec_prefill allocates it
+  // before anything is enqueued)
   const bool fused = use_rows(m, T);
-  if (fused) {
-    if (int e = ensure_rows(m)) return e;
-  }
+  LAUNCH(launch_reset_keys(m->keys, 1, st));
   LAUNCH(launch_embed_prefill(d, bf, m->embed, m->p_ids, T, audio, a0, La, m->pX, fused ? m->rSsq : nullptr, st));
   auto rope = [&](int l) -> int {
     const LayerW& w = m->layers[l];
@@ -810,7 +857,7 @@ int check_placement(qdec_model* m) {
   hipError_t he = launch_xcc_probe(m->wt, m->d, d, nb, m->dec_lds, m->stream);
   if (he == hipSuccess) he = hipMemcpyAsync(h.data(), d, nb * sizeof(int), hipMemcpyDeviceToHost, m->stream);
   if (he == hipSuccess) he = hipStreamSynchronize(m->stream);
-  (void)hipFree(d);
+  (void)dfree(d);
   if (he != hipSuccess) return fail(QDEC_E_DEVICE, "placement probe: %s", hipGetErrorString(he));
   bool same = true;
   constexpr int kGroupCount = 8;  // decode groups (one per XCD)
@@ -870,7 +917,7 @@ int qdec_create(const qdec_config* cfg, const qdec_weights* w, void* hip_stream,
   const size_t per_layer = n_qkv + n_o + n_gu + n_d;
   const size_t norms_per_layer = 2 * (size_t)d.H + 2 * (size_t)d.D;
   int e = 0;
-  if (hipMalloc(&m->wbuf, per_layer * es * d.L) != hipSuccess) {
+  if (dmalloc(&m->wbuf, per_layer * es * d.L) != hipSuccess) {
     (void)hipGetLastError();
     m->wbuf = nullptr;
     free_model(m);
@@ -1061,7 +1108,7 @@ int qdec_state_create(qdec_model* m, int32_t max_ctx, qdec_state** out) {
   for (int i = 0; i < npages; ++i) s->pages.push_back(m->pool.take());
   if (int e = upload_page_table(s)) {
     release_state_pages(s);
-    (void)hipFree(s->pt_dev);
+    (void)dfree(s->pt_dev);
     delete s;
     return e;
   }
@@ -1074,7 +1121,7 @@ void qdec_state_destroy(qdec_state* s) {
   if (!s) return;
   (void)hipStreamSynchronize(s->m->stream);
   release_state_pages(s);
-  (void)hipFree(s->pt_dev);
+  (void)dfree(s->pt_dev);
   --s->m->live_states;
   delete s;
 }
@@ -1112,6 +1159,9 @@ int qdec_prefill(qdec_state* s, const int32_t* ids_host, int32_t n_tokens, const
   if (__atomic_load_n(m->err_host, __ATOMIC_ACQUIRE))
     return fail(QDEC_E_DEVICE, "an earlier launch hit its time limit; the model must be recreated");
   if (int e = ensure_prefill(m, n_tokens)) return e;
+  if (use_rows(m, n_tokens)) {
+    if (int e = ensure_rows(m)) return e;
+  }
   std::vector<int32_t> ids(ids_host, ids_host + n_tokens);
   for (int t = audio_begin; t < audio_begin + audio_len; ++t) ids[t] = 0;  // never read
   if (int e = staged_upload(m, m->st_ids, m->p_ids, ids.data(), n_tokens * sizeof(int32_t))) return e;
@@ -1231,7 +1281,7 @@ int qdec_sample(qdec_model* m, const float* logits_dev, int32_t n_rows, const qd
     const size_t words = sample_buffer_words(d.V);
     if (int e = dev_alloc(&m->sBuf0, words, "sampling buffer")) return e;
     if (int e = dev_alloc(&m->sBuf1, words, "sampling buffer")) {
-      (void)hipFree(m->sBuf0);
+      (void)dfree(m->sBuf0);
       m->sBuf0 = nullptr;
       return e;
     }
@@ -1288,14 +1338,14 @@ int qdec_clone_state(const qdec_state* src, qdec_state** dst) {
         hipSuccess) {
       (void)hipGetLastError();
       release_state_pages(s);
-      (void)hipFree(s->pt_dev);
+      (void)dfree(s->pt_dev);
       delete s;
       return fail(QDEC_E_DEVICE, "tail page copy failed");
     }
   }
   if (int e = upload_page_table(s)) {
     release_state_pages(s);
-    (void)hipFree(s->pt_dev);
+    (void)dfree(s->pt_dev);
     delete s;
     return e;
   }
@@ -1348,7 +1398,7 @@ Dims adaptor_dims(const qdec_adaptor_config& c) {
 void free_adaptor_scratch(qdec_adaptor* a) {
   for (void* p : {(void*)a->A0, (void*)a->A1, (void*)a->H, (void*)a->QKV, (void*)a->kv[0], (void*)a->kv[1],
                   (void*)a->kv[2], (void*)a->kv[3]})
-    if (p) (void)hipFree(p);
+    if (p) (void)dfree(p);
   a->A0 = a->A1 = nullptr;
   a->H = a->QKV = nullptr;
   for (auto& k : a->kv) k = nullptr;
@@ -1360,8 +1410,8 @@ void free_adaptor(qdec_adaptor* a) {
   (void)hipStreamSynchronize(a->stream);
   free_adaptor_scratch(a);
   for (auto& b : a->blocks)
-    if (b.wqkv) (void)hipFree(b.wqkv);
-  if (a->vecs) (void)hipFree(a->vecs);
+    if (b.wqkv) (void)dfree(b.wqkv);
+  if (a->vecs) (void)dfree(a->vecs);
   free_splitk(&a->split);
   delete a;
 }
@@ -1578,7 +1628,7 @@ namespace {
 void free_encoder_scratch(qdec_encoder* e) {
   for (void* p : {(void*)e->fb, (void*)e->x0, (void*)e->X, (void*)e->QKV, (void*)e->H, (void*)e->A0, (void*)e->A1,
                   (void*)e->kv[0], (void*)e->kv[1], (void*)e->kv[2], (void*)e->kv[3]})
-    if (p) (void)hipFree(p);
+    if (p) (void)dfree(p);
   e->fb = e->x0 = e->X = e->QKV = e->H = nullptr;
   e->A0 = e->A1 = nullptr;
   for (auto& k : e->kv) k = nullptr;
@@ -1590,9 +1640,9 @@ void free_encoder(qdec_encoder* e) {
   (void)hipStreamSynchronize(e->stream);
   free_encoder_scratch(e);
   for (auto& b : e->blocks)
-    if (b.wqkv) (void)hipFree(b.wqkv);
+    if (b.wqkv) (void)dfree(b.wqkv);
   for (void* p : {(void*)e->vecs, (void*)e->tab, (void*)e->mel_range})
-    if (p) (void)hipFree(p);
+    if (p) (void)dfree(p);
   free_splitk(&e->split);
   delete e;
 }
