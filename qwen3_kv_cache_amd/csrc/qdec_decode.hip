@@ -42,7 +42,10 @@
 // Q/K-norm + RoPE, attention, SiLU and the argmax. The roles meet at exactly
 // two workgroup barriers per weight unit: "input ready" and "partials ready".
 // The exchange waves synchronise among themselves through an LDS counter, so
-// the memory waves never wait on exchange-internal steps.
+// the memory waves never wait on exchange-internal steps; the one exception is
+// that a memory wave issues its next prefetch only after the exchange waves
+// have issued the stores that publish the unit it just reduced (those stores
+// would otherwise queue behind the prefetch).
 //
 // RMSNorm folding: the memory waves dot the weights with x * g (gain applied,
 // not yet scaled) and the exchange waves multiply each combined row by
@@ -424,6 +427,7 @@ struct DecParams {
 struct Ctl {
   int abort;                 // a wait of this workgroup timed out: skip all later waits
   int exbar;                 // arrivals at exchange-wave barriers
+  int pub;                   // publishes issued (one arrival per exchange wave and weight unit)
   float red[kExWaves];       // per exchange wave: sum of squares of its residual elements
   u64 best[2][kExWaves];     // per exchange wave: argmax keys
 };
@@ -463,6 +467,23 @@ __device__ __forceinline__ bool give_up(u64 t0, Ctl* ctl, int* err) {
     return true;
   }
   return false;
+}
+
+// Publish before prefetch. A CU's vector-memory requests drain roughly in
+// the order they were issued, so words published just after a memory wave's
+// prefetch burst reach L2 only once that burst has drained. Each exchange
+// wave counts the publish of a weight unit's results in LDS right after
+// issuing its stores; a memory wave issues the loads of a later unit only
+// once that count covers the unit it has just reduced.
+__device__ __forceinline__ void published(int lane, Ctl* ctl) {
+  if (lane == 0) __hip_atomic_fetch_add(&ctl->pub, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void wait_published(int target, Ctl* ctl, int* err) {
+  const u64 t0 = now();
+  while (__hip_atomic_load(&ctl->pub, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
+    if (give_up(t0, ctl, err)) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
 }
 
 // Chip-wide sum of partial vectors in two levels: x[k] += sum_{q < P}
@@ -1062,6 +1083,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
   if (tid == 0) {
     ctl.abort = 0;
     ctl.exbar = 0;
+    ctl.pub = 0;
   }
 
   if (mem) {
@@ -1186,6 +1208,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
     if (p.nsteps > 0 && n_units > 1) issue(std::integral_constant<int, 1>{}, 1);
     bar();  // start
     int g = 0;        // units consumed so far (ring parity)
+    int pubw = 0;     // publishes to wait for before the next issue
     for (int step = 0; step < p.nsteps; ++step) {
       for (int k = 0; k < n_units; ++k) {
         asm volatile("" : "+v"(ml));
@@ -1205,7 +1228,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
           MTRACE(k, 2);
           consume_unit<1, WT>(rg, lg, pku, nsu, xin, dst, ml);
           MTRACE(k, 3);
-          if (!head) bar();  // partials ready
+          if (!head) {
+            bar();  // partials ready
+            pubw += kExWaves;
+            wait_published(pubw, &ctl, p.err);
+          }
           MTRACE(k, 4);
           if (st < p.nsteps) issue(std::integral_constant<int, 1>{}, kk);
         } else {
@@ -1213,7 +1240,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
           MTRACE(k, 2);
           consume_unit<0, WT>(rg, lg, pku, nsu, xin, dst, ml);
           MTRACE(k, 3);
-          if (!head) bar();  // partials ready
+          if (!head) {
+            bar();  // partials ready
+            pubw += kExWaves;
+            wait_published(pubw, &ctl, p.err);
+          }
           MTRACE(k, 4);
           if (st < p.nsteps) issue(std::integral_constant<int, 0>{}, kk);
         }
@@ -1230,6 +1261,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
   }
 
   // ================================================================== exchange waves
+  // Raised issue priority: on the SIMDs they share with the memory waves, the
+  // exchange waves' instructions (the latency-bound chain) are issued first.
+  __builtin_amdgcn_s_setprio(2);
   // Per-thread indices and the parameter block are made opaque at the top of
   // every layer: keeps address arithmetic from being hoisted out of the loops
   // and pinned in registers for the whole launch.
@@ -1390,6 +1424,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
           const int lg = chunk_lg(H, VN);
           for (int j = et; j < a1 - a0; j += kEx) put_l(Lq + a0 + j, inv * row_val(j, lg), tg + PH_Q, pp->local);
         }
+        published(ln, &ctl);
         TRACEB(step, l, 0);
         // ---------------- B: this wave's head vectors from the group's Q/K/V rows
         QDEC_OPAQUE();
@@ -1556,6 +1591,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
           const int lg = chunk_lg(QD, VN);
           for (int j = et; j < c1 - c0; j += kEx) put(Lo + (size_t)X * H + c0 + j, row_val(j, lg), tg + PH_O);
         }
+        published(ln, &ctl);
       } else {
         load_in(l + 1);
       }
@@ -1586,6 +1622,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
           put_l(Lz + z0 + i, gt / (1.f + expf(-gt)) * up, tg + PH_Z, pp->local);
         }
       }
+      published(ln, &ctl);
       TRACE(step, 1 + l * 10 + 7);
 
       // ---------------- E
@@ -1604,6 +1641,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecParams p) {
         const int lg = chunk_lg(FS, VN);
         for (int j = et; j < e1 - e0; j += kEx) put(Lx + (size_t)X * H + e0 + j, row_val(j, lg), tg + PH_X);
       }
+      published(ln, &ctl);
       TRACE(step, 1 + l * 10 + 9);
     }
 
