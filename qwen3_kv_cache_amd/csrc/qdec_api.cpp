@@ -773,12 +773,22 @@ int run_prefill(qdec_state* s, int T, const float* audio, int a0, int La, float*
   const bool fused = use_rows(m, T);
   LAUNCH(launch_reset_keys(m->keys, 1, st));
   LAUNCH(launch_embed_prefill(d, bf, m->embed, m->p_ids, T, audio, a0, La, m->pX, fused ? m->rSsq : nullptr, st));
+  // short prompts on the fused path: Q/K norm, RoPE, K/V append and the
+  // attention in one launch per layer
+  const bool small = fused && attn_small_fits(d, T);
   auto rope = [&](int l) -> int {
+    if (small) return 0;  // inside the attention launch
     const LayerW& w = m->layers[l];
     LAUNCH(launch_qk_rope_append(d, m->pQKV, T, 0, w.q_norm, w.k_norm, m->rope_cos, m->rope_sin, s->pt_dev, l, st));
     return 0;
   };
-  auto attn = [&](int, uint16_t* hi, uint16_t* lo) -> int {
+  auto attn = [&](int l, uint16_t* hi, uint16_t* lo) -> int {
+    if (small) {
+      const LayerW& w = m->layers[l];
+      LAUNCH(launch_attn_small(d, m->pQKV, T, w.q_norm, w.k_norm, m->rope_cos, m->rope_sin, s->pt_dev, l, m->pAttn,
+                               st));
+      return 0;
+    }
     LAUNCH(launch_attn_prefill(d, m->pQKV, T, m->pAttn, m->pKV, st, hi, lo, true, &m->split.sk));
     return 0;
   };

@@ -106,6 +106,14 @@ hipError_t launch_argmax_rows(const float* logits, int n, int V, unsigned long l
 hipError_t launch_qk_rope_append(const Dims& d, float* qkv, int T, int pos0, const float* q_norm,
                                  const float* k_norm, const float* rope_cos, const float* rope_sin,
                                  const int64_t* page_table, int layer, hipStream_t st);
+// Short prompts (T <= kSmallT): per-head Q/K-RMSNorm, RoPE, the K/V append
+// of positions [0, T) and causal attention in one launch; out is fp32
+// [T][NQ D]. qkv is only read.
+constexpr int kSmallT = 64;
+bool attn_small_fits(const Dims& d, int T);
+hipError_t launch_attn_small(const Dims& d, const float* qkv, int T, const float* q_norm, const float* k_norm,
+                             const float* rope_cos, const float* rope_sin, const int64_t* page_table, int layer,
+                             float* out, hipStream_t st);
 // Batched decode attention for one layer (QK-norm, RoPE and K/V append of
 // the rows' current positions included). The launcher fills L, NKV, ld, eps
 // and qscale.

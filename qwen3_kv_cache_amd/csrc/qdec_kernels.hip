@@ -384,6 +384,148 @@ __global__ __launch_bounds__(64) void qk_rope_append_kernel(float* __restrict__ 
               page_table, layer);
 }
 
+// ------------------------------------------------ short prompts: fused attention
+// Causal prefill attention for prompts of at most kSmallT positions, with
+// the per-head Q/K-RMSNorm, RoPE and the K/V append of the same layer
+// folded in (one launch instead of three). Block = (KV head g, block of 8
+// query rows [q0, q1)), 8 waves. Every thread owns one rotation pair (i,
+// i + D / 2) of one row per pass; a pass's loads are all issued before any
+// is used, and a row's sum of squares is reduced over its D / 2 lanes. The
+// block prepares the keys [0, q1) in LDS (keys of earlier blocks are
+// recomputed, not exchanged) and appends K/V of its own rows [q0, q1) to the
+// state's pages. Each (query row, query head of the group) is then one
+// wave's item: scores with one lane per key, the softmax in base 2 (q
+// carries log2(e) / sqrt(D)), and the output with each lane holding D / 64
+// dimensions. All in fp32.
+template <int HALF>
+__device__ __forceinline__ float pair_sum(float v) {
+#pragma unroll
+  for (int o = 1; o < HALF; o <<= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+template <int D, int GROUP>
+__global__ __launch_bounds__(512) void attn_small_kernel(const float* __restrict__ qkv, int T, int NQ, int NKV,
+                                                          int L, float eps, float qscale,
+                                                          const float* __restrict__ q_norm,
+                                                          const float* __restrict__ k_norm,
+                                                          const float* __restrict__ rcos,
+                                                          const float* __restrict__ rsin,
+                                                          const int64_t* __restrict__ page_table, int layer,
+                                                          float* __restrict__ out) {
+  constexpr int HALF = D / 2, QB = 8, KP = D + 1;  // K rows padded: lane-per-key reads hit distinct banks
+  constexpr int NW = 8, RPP = 512 / HALF;          // waves; rows per pass
+  constexpr int DPL = (D + kWave - 1) / kWave;     // output dimensions per lane
+  constexpr int KPASS = (kSmallT + RPP - 1) / RPP;
+  __shared__ float kl[kSmallT * KP];
+  __shared__ float vl[kSmallT * D];
+  __shared__ float ql[QB * GROUP * D];
+  __shared__ float pl[NW][kSmallT];
+  const int g = blockIdx.x, q0 = blockIdx.y * QB, q1 = min(T, q0 + QB);
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int pi = threadIdx.x % HALF, pr = threadIdx.x / HALF;  // this thread's pair and row within a pass
+  const int ld = (NQ + 2 * NKV) * D;
+  Dims d{L, 0, NQ, NKV, D, 0, 0, 0.f};
+  const float gk0 = k_norm[pi], gk1 = k_norm[pi + HALF];
+
+  // keys and values [0, q1)
+  {
+    float k0[KPASS], k1[KPASS], v0[KPASS], v1[KPASS], c[KPASS], sn[KPASS];
+#pragma unroll
+    for (int ps = 0; ps < KPASS; ++ps) {
+      const int t = min(ps * RPP + pr, q1 - 1);  // rows past q1 repeat the last one, stored nowhere
+      const float* row = qkv + (size_t)t * ld;
+      k0[ps] = row[(size_t)(NQ + g) * D + pi];
+      k1[ps] = row[(size_t)(NQ + g) * D + pi + HALF];
+      v0[ps] = row[(size_t)(NQ + NKV + g) * D + pi];
+      v1[ps] = row[(size_t)(NQ + NKV + g) * D + pi + HALF];
+      c[ps] = rcos[(size_t)t * HALF + pi];
+      sn[ps] = rsin[(size_t)t * HALF + pi];
+    }
+#pragma unroll
+    for (int ps = 0; ps < KPASS; ++ps) {
+      const int t = ps * RPP + pr;
+      const float inv = 1.f / sqrtf(pair_sum<HALF>(k0[ps] * k0[ps] + k1[ps] * k1[ps]) / (float)D + eps);
+      const float x0 = k0[ps] * inv * gk0, x1 = k1[ps] * inv * gk1;
+      const float r0 = x0 * c[ps] - x1 * sn[ps], r1 = x1 * c[ps] + x0 * sn[ps];
+      if (t < q1) {
+        kl[t * KP + pi] = r0;
+        kl[t * KP + pi + HALF] = r1;
+        vl[t * D + pi] = v0[ps];
+        vl[t * D + pi + HALF] = v1[ps];
+        if (t >= q0) {
+          float* page = reinterpret_cast<float*>(page_table[t / kPage]);
+          float* kd = page + page_offset(d, layer, 0, g, t % kPage);
+          float* vd = page + page_offset(d, layer, 1, g, t % kPage);
+          kd[pi] = r0;
+          kd[pi + HALF] = r1;
+          vd[pi] = v0[ps];
+          vd[pi + HALF] = v1[ps];
+        }
+      }
+    }
+  }
+  // the group's query heads of rows [q0, q1), scaled for base-2 scores
+  {
+    constexpr int QPASS = (QB * GROUP + RPP - 1) / RPP;
+    const float gq0 = q_norm[pi], gq1 = q_norm[pi + HALF];
+    float a0[QPASS], a1[QPASS], c[QPASS], sn[QPASS];
+#pragma unroll
+    for (int ps = 0; ps < QPASS; ++ps) {
+      const int it = min(ps * RPP + pr, (q1 - q0) * GROUP - 1);
+      const int t = q0 + it / GROUP, hh = it % GROUP;
+      const float* src = qkv + (size_t)t * ld + (size_t)(g * GROUP + hh) * D;
+      a0[ps] = src[pi];
+      a1[ps] = src[pi + HALF];
+      c[ps] = rcos[(size_t)t * HALF + pi];
+      sn[ps] = rsin[(size_t)t * HALF + pi];
+    }
+#pragma unroll
+    for (int ps = 0; ps < QPASS; ++ps) {
+      const int it = ps * RPP + pr;
+      const float inv = 1.f / sqrtf(pair_sum<HALF>(a0[ps] * a0[ps] + a1[ps] * a1[ps]) / (float)D + eps);
+      const float x0 = a0[ps] * inv * gq0, x1 = a1[ps] * inv * gq1;
+      if (it < (q1 - q0) * GROUP) {
+        ql[it * D + pi] = (x0 * c[ps] - x1 * sn[ps]) * qscale;
+        ql[it * D + pi + HALF] = (x1 * c[ps] + x0 * sn[ps]) * qscale;
+      }
+    }
+  }
+  __syncthreads();
+
+  for (int it = wave; it < (q1 - q0) * GROUP; it += NW) {
+    const int t = q0 + it / GROUP, hh = it % GROUP;
+    const float* q = ql + it * D;
+    // scores: lane u <-> key u (keys past t masked)
+    float sc = -INFINITY;
+    if (lane <= t) {
+      float a = 0.f;
+#pragma unroll 16
+      for (int e = 0; e < D; ++e) a = fmaf(q[e], kl[lane * KP + e], a);
+      sc = a;
+    }
+    const float mx = wave_max(sc);
+    const float pv = lane <= t ? __builtin_amdgcn_exp2f(sc - mx) : 0.f;
+    const float ls = wave_sum(pv);
+    pl[wave][lane] = pv;
+    __builtin_amdgcn_wave_barrier();
+    float o[DPL];
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) o[k] = 0.f;
+    for (int u = 0; u <= t; ++u) {
+      const float pu = pl[wave][u];
+#pragma unroll
+      for (int k = 0; k < DPL; ++k)
+        if (lane + k * kWave < D) o[k] = fmaf(pu, vl[u * D + lane + k * kWave], o[k]);
+    }
+    float* dst = out + (size_t)t * NQ * D + (size_t)(g * GROUP + hh) * D;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k)
+      if (lane + k * kWave < D) dst[lane + k * kWave] = o[k] / ls;
+    __builtin_amdgcn_wave_barrier();  // pl is rewritten by this wave's next item
+  }
+}
+
 // ------------------------------------------------ batched decode attention
 // One launch per layer for the rows of a batched decode step; row r is one
 // state at position pos_r. Block = (kv head g, split s of kAttnChunk
@@ -2064,6 +2206,37 @@ hipError_t launch_qk_rope_append(const Dims& d, float* qkv, int T, int pos0, con
   qk_rope_append_kernel<<<grid, 64, 0, st>>>(qkv, d.qkv(), pos0, d.NQ, d.NKV, d.D, d.L, d.eps, q_norm, k_norm,
                                              rope_cos, rope_sin, page_table, layer);
   return hipGetLastError();
+}
+
+bool attn_small_fits(const Dims& d, int T) {
+  const int group = d.NQ / d.NKV;
+  return T >= 1 && T <= kSmallT && (d.D == 32 || d.D == 64 || d.D == 128) && (group == 1 || group == 2 || group == 4);
+}
+
+hipError_t launch_attn_small(const Dims& d, const float* qkv, int T, const float* q_norm, const float* k_norm,
+                             const float* rope_cos, const float* rope_sin, const int64_t* page_table, int layer,
+                             float* out, hipStream_t st) {
+  if (!attn_small_fits(d, T)) return hipErrorInvalidValue;
+  const int group = d.NQ / d.NKV;
+  const float qscale = 1.4426950408889634f / sqrtf((float)d.D);  // scores in base 2
+  const dim3 grid(d.NKV, (T + 7) / 8);
+#define QDEC_SMALL_CASE(DD, GG)                                                                             \
+  if (d.D == DD && group == GG) {                                                                           \
+    attn_small_kernel<DD, GG><<<grid, 512, 0, st>>>(qkv, T, d.NQ, d.NKV, d.L, d.eps, qscale, q_norm, k_norm, \
+                                                    rope_cos, rope_sin, page_table, layer, out);            \
+    return hipGetLastError();                                                                               \
+  }
+  QDEC_SMALL_CASE(128, 1)
+  QDEC_SMALL_CASE(128, 2)
+  QDEC_SMALL_CASE(128, 4)
+  QDEC_SMALL_CASE(64, 1)
+  QDEC_SMALL_CASE(64, 2)
+  QDEC_SMALL_CASE(64, 4)
+  QDEC_SMALL_CASE(32, 1)
+  QDEC_SMALL_CASE(32, 2)
+  QDEC_SMALL_CASE(32, 4)
+#undef QDEC_SMALL_CASE
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_attn_rows(const Dims& d, const AttnRows& args, int nsplit, hipStream_t st) {

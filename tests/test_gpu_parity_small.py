@@ -31,6 +31,13 @@ MID = {
     # a prompt made only of audio rows (span [0, T)): no id is read
     "d64_g2_allaudio": (synth.custom_shape(hidden=256, n_layer=2, n_q_head=4, n_kv_head=2, head_dim=64, ffn=768,
                                            vocab=5003, bf16=True), 40, 0, 40, 6),
+    # short prompts take the fused attention launch (QK-norm, RoPE, append and
+    # attention together, T <= 64): GQA 4 with a ragged third 16-query block,
+    # and D=32 at exactly 64 positions
+    "d64_g4_T33": (synth.custom_shape(hidden=256, n_layer=2, n_q_head=8, n_kv_head=2, head_dim=64, ffn=768,
+                                      vocab=1000, bf16=True), 33, 5, 10, 6),
+    "d32_g4_T64": (synth.custom_shape(hidden=128, n_layer=2, n_q_head=8, n_kv_head=2, head_dim=32, ffn=384,
+                                      vocab=777, bf16=True), 64, 20, 12, 6),
 }
 
 
