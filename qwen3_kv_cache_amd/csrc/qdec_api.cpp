@@ -554,10 +554,13 @@ int ensure_rows(qdec_model* m) {
   const int shapes[5][2] = {{d.H, d.qkv()}, {d.NQ * d.D, d.H}, {d.H, 2 * d.F}, {d.F, d.H}, {d.H, d.V}};
   size_t part = 1;
   int cnt = 1;
+  // the split depends on the row count: the largest need over 1 .. R rows
   for (auto& kn : shapes) {
-    if (!rows_fits(R, kn[0], kn[1])) continue;
-    part = std::max(part, rows_partial_floats(R, kn[0], kn[1]));
-    cnt = std::max(cnt, rows_counters(R, kn[0], kn[1]));
+    for (int M = 1; M <= R; ++M) {
+      if (!rows_fits(M, kn[0], kn[1])) continue;
+      part = std::max(part, rows_partial_floats(M, kn[0], kn[1]));
+      cnt = std::max(cnt, rows_counters(M, kn[0], kn[1]));
+    }
   }
   const size_t nss = (size_t)std::max(1, d.H / 16);
   int e = 0;

@@ -2369,15 +2369,16 @@ struct RowsPlan {
 
 // 32 output columns per workgroup for wide outputs (each A load then feeds
 // two column tiles), 16 otherwise; K is split into chunks (multiples of 128,
-// one k-step of 32 per wave at least) only until there are 128 column-tile x
-// chunk workgroups per row tile: the split-K exchange costs more than the
-// extra weight parallelism gains beyond that (measured on batched decode and
-// 48-token prompts)
-RowsPlan rows_plan(int K, int N) {
+// one k-step of 32 per wave at least) only until the launch has 128
+// workgroups, counting every 16-row tile: the split-K exchange costs more
+// than the extra weight parallelism gains beyond that (measured on batched
+// decode and 48-token prompts, where 48 rows already give three tiles)
+RowsPlan rows_plan(int K, int N, int M) {
   RowsPlan p;
   p.nt = N % 32 == 0 && N >= 2048 ? 2 : 1;
   p.tiles = N / (16 * p.nt);
-  const int want = std::max(1, (128 + p.tiles - 1) / p.tiles);
+  const int rt = (M + 15) / 16;
+  const int want = std::max(1, (128 + p.tiles * rt - 1) / (p.tiles * rt));
   p.kc = std::max(128, ((K + want - 1) / want + 127) / 128 * 128);
   p.nkc = (K + p.kc - 1) / p.kc;
   return p;
@@ -2404,22 +2405,22 @@ hipError_t rows_dispatch(Epi epi, bool norm, dim3 grid, const RowsGemm& g, hipSt
 
 bool rows_fits(int M, int K, int N) { return M >= 1 && M <= 64 && K >= 32 && K % 32 == 0 && N % 16 == 0; }
 
-int rows_tile_cols(int N) { return rows_plan(32, N).nt * 16; }
+int rows_tile_cols(int N) { return rows_plan(32, N, 16).nt * 16; }
 
 size_t rows_partial_floats(int M, int K, int N) {
-  const RowsPlan p = rows_plan(K, N);
+  const RowsPlan p = rows_plan(K, N, M);
   if (p.nkc == 1) return 0;
   return (size_t)p.nkc * p.tiles * ((M + 15) / 16) * p.nt * 4 * 64;  // 8-byte words
 }
 
 int rows_counters(int M, int K, int N) {
-  const RowsPlan p = rows_plan(K, N);
+  const RowsPlan p = rows_plan(K, N, M);
   return p.nkc == 1 ? 0 : p.tiles * ((M + 15) / 16);
 }
 
 hipError_t launch_gemm_rows(Epi epi, bool norm, const RowsGemm& g0, hipStream_t st) {
   if (!rows_fits(g0.M, g0.K, g0.N)) return hipErrorInvalidValue;
-  const RowsPlan p = rows_plan(g0.K, g0.N);
+  const RowsPlan p = rows_plan(g0.K, g0.N, g0.M);
   if (p.nkc > 1 && (!g0.P || !g0.cnt)) return hipErrorInvalidValue;
   RowsGemm g = g0;
   g.KC = p.kc;
