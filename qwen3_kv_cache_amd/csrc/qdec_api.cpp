@@ -598,6 +598,7 @@ int next_rows_tag(qdec_model* m, unsigned* tag) {
 
 int gemm_rows(qdec_model* m, Epi epi, bool norm, RowsGemm& g) {
   if (int e = next_rows_tag(m, &g.tag)) return e;
+  g.wf32 = m->bf16 ? 0 : 1;
   g.err = m->err_dev;
   LAUNCH(launch_gemm_rows(epi, norm, g, m->stream));
   return QDEC_OK;
@@ -605,7 +606,7 @@ int gemm_rows(qdec_model* m, Epi epi, bool norm, RowsGemm& g) {
 
 bool use_rows(const qdec_model* m, int T) {
   const Dims& d = m->d;
-  return m->bf16 && rows_fits(T, d.H, d.qkv()) && rows_fits(T, d.NQ * d.D, d.H) && rows_fits(T, d.H, 2 * d.F) &&
+  return rows_fits(T, d.H, d.qkv()) && rows_fits(T, d.NQ * d.D, d.H) && rows_fits(T, d.H, 2 * d.F) &&
          rows_fits(T, d.F, d.H);
 }
 
@@ -626,17 +627,17 @@ int run_layers_rows(qdec_model* m, int T, float* X, float* QKV, float* Attn, flo
   for (int l = 0; l < d.L; ++l) {
     const LayerW& w = m->layers[l];
     g.A = X, g.lda = d.H, g.ssq = m->rSsq, g.nss = nss, g.gain = w.in_norm;
-    g.W = (const uint16_t*)w.wqkv, g.K = d.H, g.N = d.qkv(), g.C = QKV, g.ldc = d.qkv();
+    g.W = w.wqkv, g.K = d.H, g.N = d.qkv(), g.C = QKV, g.ldc = d.qkv();
     if (int e = gemm_rows(m, EPI_STORE, true, g)) return e;
     if (int e = rope(l)) return e;
     if (int e = attn(l, nullptr, nullptr)) return e;
-    g.A = Attn, g.lda = d.NQ * d.D, g.W = (const uint16_t*)w.wo, g.K = d.NQ * d.D, g.N = d.H, g.C = X, g.ldc = d.H;
+    g.A = Attn, g.lda = d.NQ * d.D, g.W = w.wo, g.K = d.NQ * d.D, g.N = d.H, g.C = X, g.ldc = d.H;
     g.ssq_out = m->rSsq;
     if (int e = gemm_rows(m, EPI_RESID, false, g)) return e;
     g.A = X, g.lda = d.H, g.ssq = m->rSsq, g.nss = nss_h, g.gain = w.post_norm;
-    g.W = (const uint16_t*)w.wgu, g.K = d.H, g.N = 2 * d.F, g.C = Z, g.ldc = d.F;
+    g.W = w.wgu, g.K = d.H, g.N = 2 * d.F, g.C = Z, g.ldc = d.F;
     if (int e = gemm_rows(m, EPI_SWIGLU, true, g)) return e;
-    g.A = Z, g.lda = d.F, g.W = (const uint16_t*)w.wd, g.K = d.F, g.N = d.H, g.C = X, g.ldc = d.H;
+    g.A = Z, g.lda = d.F, g.W = w.wd, g.K = d.F, g.N = d.H, g.C = X, g.ldc = d.H;
     g.ssq_out = m->rSsq;
     if (int e = gemm_rows(m, EPI_RESID, false, g)) return e;
     nss = nss_h;
@@ -747,7 +748,7 @@ int run_decode_batch(qdec_state* const* states, int n, const int32_t* tokens, fl
     if (rows_fits(n, d.H, d.V)) {
       RowsGemm g{};
       g.A = m->bX, g.lda = d.H, g.ssq = m->rSsq, g.nss = nss, g.gain = m->final_norm, g.eps = d.eps;
-      g.W = (const uint16_t*)m->embed, g.M = n, g.K = d.H, g.N = d.V, g.P = m->rP, g.cnt = m->rCnt;
+      g.W = m->embed, g.M = n, g.K = d.H, g.N = d.V, g.P = m->rP, g.cnt = m->rCnt;
       g.C = logits, g.ldc = d.V, g.keys = m->bKeys;
       if (int e = gemm_rows(m, EPI_HEAD, true, g)) return e;
       LAUNCH(launch_argmax_final(m->bKeys, n, argmax ? argmax : m->bTok, st));

@@ -79,7 +79,8 @@ struct RowsGemm {
   int nss;
   const float* gain;            // NORM: gain [K]
   float eps;
-  const uint16_t* W;            // [N, K]
+  const void* W;                // [N, K], bf16 (fp32 when wf32)
+  int wf32;
   int M, K, N;
   int KC;                       // set by the launcher
   unsigned long long* P;        // split-K partial words (rows_partial_floats of them)

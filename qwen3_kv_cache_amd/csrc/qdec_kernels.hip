@@ -22,6 +22,7 @@
 #include <algorithm>
 #include <cfloat>
 #include <cmath>
+#include <type_traits>
 
 #include "qdec_internal.h"
 
@@ -1437,8 +1438,12 @@ __global__ __launch_bounds__(256) void gemm_bf16x2_kernel(const uint16_t* __rest
 // Small-M GEMM with fused prologue and epilogue, for up to 64 activation rows
 // (batched decode, short prompts): C[M, N] = op(A)[M, K] . W[N, K]^T.
 // op(A) is A itself or, with NORM, the RMS-normalised rows A * inv * gain,
-// inv = 1 / sqrt(sum(ssq partials of the row) / K + eps); the fp32 values
-// are split into bf16 hi + lo in registers for the MFMAs. Workgroup =
+// inv = 1 / sqrt(sum(ssq partials of the row) / K + eps); with bf16 weights
+// the fp32 values are split into bf16 hi + lo in registers for the MFMAs,
+// with fp32 weights (fp32 models, the dequantized copies of Q8_0 models)
+// they go unsplit to the fp32 MFMA: a lane's 8 consecutive k of its A row and
+// of its W row feed 8 16x16x4 products, product e taking element e, so each
+// covers k = e, 8 + e, 16 + e, 24 + e of the 32-wide step. Workgroup =
 // (16 NT output columns, K chunk of KC), 4 waves splitting the chunk; the
 // waves' sums meet in LDS. With several chunks, each workgroup stores its
 // partial tile, and the last to arrive at the column tile (arrival counter,
@@ -1450,15 +1455,18 @@ __global__ __launch_bounds__(256) void gemm_bf16x2_kernel(const uint16_t* __rest
 //   SWIGLU  columns come as 8 gate then 8 up rows per group of 16; output j
 //           of group q is silu(gate) * up at C[row][8q + j]
 //   HEAD    C = v when C is set; keys[row] = max(keys[row], argmax key)
-template <int MT, int NT, bool NORM>
+template <int MT, int NT, bool NORM, typename WT>
 struct RowsStep {
-  uint4 b[NT];
+  static constexpr bool F32 = std::is_same<WT, float>::value;
+  static constexpr int WB = F32 ? 2 : 1;  // 16-byte loads per lane of a W row's 8 k
+  uint4 b[NT][WB];
   float4 a[MT][2];
   float4 gv[2];
-  __device__ __forceinline__ void load(const uint16_t* const* wrow, const float* const* arow, const float* gk,
-                                       int k) {
+  __device__ __forceinline__ void load(const WT* const* wrow, const float* const* arow, const float* gk, int k) {
 #pragma unroll
-    for (int j = 0; j < NT; ++j) b[j] = *reinterpret_cast<const uint4*>(wrow[j] + k);
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int h = 0; h < WB; ++h) b[j][h] = *reinterpret_cast<const uint4*>(wrow[j] + k + 4 * h);
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
       a[i][0] = *reinterpret_cast<const float4*>(arow[i] + k);
@@ -1478,6 +1486,17 @@ struct RowsStep {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = v[e] * inv[i] * g8[e];
       }
+      if constexpr (F32) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          const float w8[8] = {__uint_as_float(b[j][0].x), __uint_as_float(b[j][0].y), __uint_as_float(b[j][0].z),
+                               __uint_as_float(b[j][0].w), __uint_as_float(b[j][1].x), __uint_as_float(b[j][1].y),
+                               __uint_as_float(b[j][1].z), __uint_as_float(b[j][1].w)};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(v[e], w8[e], acc[i][j], 0, 0, 0);
+        }
+        continue;
+      }
       bf16x8_t hi, lo;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -1486,10 +1505,10 @@ struct RowsStep {
       }
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, __builtin_bit_cast(bf16x8_t, b[j]), acc[i][j], 0, 0,
-                                                            0);
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, __builtin_bit_cast(bf16x8_t, b[j]), acc[i][j], 0, 0,
-                                                            0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, __builtin_bit_cast(bf16x8_t, b[j][0]), acc[i][j], 0,
+                                                            0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, __builtin_bit_cast(bf16x8_t, b[j][0]), acc[i][j], 0,
+                                                            0, 0);
       }
     }
   }
@@ -1497,7 +1516,7 @@ struct RowsStep {
 
 constexpr unsigned long long kRowsWaitTicks = 200000000ull;  // about 0.1 s of s_memtime
 
-template <int MT, int NT, int EPI, bool NORM>
+template <int MT, int NT, int EPI, bool NORM, typename WT>
 __global__ __launch_bounds__(256) void gemm_rows_kernel(RowsGemm g) {
   constexpr int U = 4;                 // k-steps of loads in flight per wave
   constexpr int S = MT * NT * 4;       // accumulator floats per lane
@@ -1513,11 +1532,11 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(RowsGemm g) {
   const int kb = c * g.KC + wave * kw, ke = min(K, kb + kw);
   const int r = lane % 16, kq = (lane / 16) * 8;
 
-  const uint16_t* wrow[NT];
+  const WT* wrow[NT];
   const float* arow[MT];
   float inv[MT];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) wrow[j] = g.W + (size_t)(n0 + j * 16 + r) * K + kq;
+  for (int j = 0; j < NT; ++j) wrow[j] = (const WT*)g.W + (size_t)(n0 + j * 16 + r) * K + kq;
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
     // rows past M repeat row M - 1: an MFMA output row depends only on its
@@ -1545,7 +1564,7 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(RowsGemm g) {
     for (int j = 0; j < NT; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   int k = kb;
   for (; k + 32 * U <= ke; k += 32 * U) {
-    RowsStep<MT, NT, NORM> st[U];
+    RowsStep<MT, NT, NORM, WT> st[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) st[u].load(wrow, arow, gk, k + 32 * u);
     // every load of the batch ahead of the first multiply
@@ -1554,7 +1573,7 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(RowsGemm g) {
     for (int u = 0; u < U; ++u) st[u].mma(acc, inv);
   }
   for (; k < ke; k += 32) {
-    RowsStep<MT, NT, NORM> st;
+    RowsStep<MT, NT, NORM, WT> st;
     st.load(wrow, arow, gk, k);
     st.mma(acc, inv);
   }
@@ -2384,18 +2403,18 @@ RowsPlan rows_plan(int K, int N, int M) {
   return p;
 }
 
-template <int MT, int NT>
+template <int MT, int NT, typename WT>
 hipError_t rows_dispatch(Epi epi, bool norm, dim3 grid, const RowsGemm& g, hipStream_t st) {
   if (epi == EPI_STORE && norm)
-    gemm_rows_kernel<MT, NT, EPI_STORE, true><<<grid, 256, 0, st>>>(g);
+    gemm_rows_kernel<MT, NT, EPI_STORE, true, WT><<<grid, 256, 0, st>>>(g);
   else if (epi == EPI_SWIGLU && norm)
-    gemm_rows_kernel<MT, NT, EPI_SWIGLU, true><<<grid, 256, 0, st>>>(g);
+    gemm_rows_kernel<MT, NT, EPI_SWIGLU, true, WT><<<grid, 256, 0, st>>>(g);
   else if (epi == EPI_HEAD && norm)
-    gemm_rows_kernel<MT, NT, EPI_HEAD, true><<<grid, 256, 0, st>>>(g);
+    gemm_rows_kernel<MT, NT, EPI_HEAD, true, WT><<<grid, 256, 0, st>>>(g);
   else if (epi == EPI_RESID && !norm)
-    gemm_rows_kernel<MT, NT, EPI_RESID, false><<<grid, 256, 0, st>>>(g);
+    gemm_rows_kernel<MT, NT, EPI_RESID, false, WT><<<grid, 256, 0, st>>>(g);
   else if (epi == EPI_STORE && !norm)
-    gemm_rows_kernel<MT, NT, EPI_STORE, false><<<grid, 256, 0, st>>>(g);
+    gemm_rows_kernel<MT, NT, EPI_STORE, false, WT><<<grid, 256, 0, st>>>(g);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -2427,7 +2446,11 @@ hipError_t launch_gemm_rows(Epi epi, bool norm, const RowsGemm& g0, hipStream_t 
   // one 16-row tile per workgroup: rows past 16 take more workgroups (their
   // weight tiles are read again, mostly from the XCD's L2), not more registers
   const dim3 grid(p.tiles, p.nkc, (g.M + 15) / 16);
-  return p.nt == 2 ? rows_dispatch<1, 2>(epi, norm, grid, g, st) : rows_dispatch<1, 1>(epi, norm, grid, g, st);
+  if (g.wf32)
+    return p.nt == 2 ? rows_dispatch<1, 2, float>(epi, norm, grid, g, st)
+                     : rows_dispatch<1, 1, float>(epi, norm, grid, g, st);
+  return p.nt == 2 ? rows_dispatch<1, 2, uint16_t>(epi, norm, grid, g, st)
+                   : rows_dispatch<1, 1, uint16_t>(epi, norm, grid, g, st);
 }
 
 // The tiled kernel needs M > 64 and whole column tiles, and is taken only with
