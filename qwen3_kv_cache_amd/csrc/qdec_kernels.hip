@@ -999,8 +999,10 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
                                                                  float* __restrict__ part) {
   using namespace fa;
   constexpr int VH = GROUP * QS, QTB = 64 * QS;  // virtual heads per wave, queries per block
-  __shared__ __bf16 Kh[KT * KP], Kl[KT * KP];
-  __shared__ __bf16 Vh[D * VP], Vl[D * VP];
+  // two tile buffers: the next tile's global loads are in flight while the
+  // current one is multiplied, one barrier per tile
+  __shared__ __bf16 Kh[2][KT * KP], Kl[2][KT * KP];
+  __shared__ __bf16 Vh[2][D * VP], Vl[2][D * VP];
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   const int c16 = lane % 16, gq = lane / 16;
   // Workgroup i runs on XCD i % 8. With a multiple of 8 KV heads and long
@@ -1061,25 +1063,48 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
   const int last_key = causal ? min(T, q0 + QTB) - 1 : T - 1;
   const int S = gridDim.z, ntile = last_key / KT + 1, per = (ntile + S - 1) / S;
   const int kt_end = min(ntile, ((int)blockIdx.z + 1) * per);
-  for (int k0 = blockIdx.z * per * KT; k0 < kt_end * KT; k0 += KT) {
-    __syncthreads();
-    // copies of the converted tiles: K rows of 16-byte chunks (key c / 16,
-    // columns 8 (c % 16)), V^T rows (column d = c / 4, keys 8 (c % 4))
-#pragma unroll
-    for (int i = 0; i < KT * D / 8 / 256; ++i) {
-      const int c = threadIdx.x + 256 * i, key = c / (D / 8), d0 = 8 * (c % (D / 8));
-      const size_t o = (size_t)min(k0 + key, T - 1) * D + d0;
-      *reinterpret_cast<uint4*>(&Kh[key * KP + d0]) = *reinterpret_cast<const uint4*>(kh_g + o);
-      *reinterpret_cast<uint4*>(&Kl[key * KP + d0]) = *reinterpret_cast<const uint4*>(kl_g + o);
-    }
-#pragma unroll
-    for (int i = 0; i < D * KT / 8 / 256; ++i) {
-      const int c = threadIdx.x + 256 * i, d = c / (KT / 8), kq = 8 * (c % (KT / 8));
-      const size_t o = (size_t)d * Tp + k0 + kq;
-      *reinterpret_cast<uint4*>(&Vh[d * VP + kq]) = *reinterpret_cast<const uint4*>(vh_g + o);
-      *reinterpret_cast<uint4*>(&Vl[d * VP + kq]) = *reinterpret_cast<const uint4*>(vl_g + o);
-    }
-    __syncthreads();
+  // copies of the converted tiles: K rows of 16-byte chunks (key c / 16,
+  // columns 8 (c % 16)), V^T rows (column d = c / 4, keys 8 (c % 4)); thread
+  // t moves chunks c = t and t + 256 of each of the four arrays
+  static_assert(KT * D / 8 == 512, "two chunks per thread and array");
+  const int kc0 = threadIdx.x / (D / 8), kc1 = kc0 + 256 / (D / 8), kd = 8 * (threadIdx.x % (D / 8));
+  const int vd0 = threadIdx.x / (KT / 8), vd1 = vd0 + 256 / (KT / 8), vk = 8 * (threadIdx.x % (KT / 8));
+  uint4 rkh0, rkh1, rkl0, rkl1, rvh0, rvh1, rvl0, rvl1;
+#define QDEC_FA_LOAD(k0)                                                    \
+  {                                                                         \
+    const size_t o0 = (size_t)min((k0) + kc0, T - 1) * D + kd;              \
+    const size_t o1 = (size_t)min((k0) + kc1, T - 1) * D + kd;              \
+    rkh0 = *reinterpret_cast<const uint4*>(kh_g + o0);                      \
+    rkh1 = *reinterpret_cast<const uint4*>(kh_g + o1);                      \
+    rkl0 = *reinterpret_cast<const uint4*>(kl_g + o0);                      \
+    rkl1 = *reinterpret_cast<const uint4*>(kl_g + o1);                      \
+    rvh0 = *reinterpret_cast<const uint4*>(vh_g + (size_t)vd0 * Tp + (k0) + vk); \
+    rvh1 = *reinterpret_cast<const uint4*>(vh_g + (size_t)vd1 * Tp + (k0) + vk); \
+    rvl0 = *reinterpret_cast<const uint4*>(vl_g + (size_t)vd0 * Tp + (k0) + vk); \
+    rvl1 = *reinterpret_cast<const uint4*>(vl_g + (size_t)vd1 * Tp + (k0) + vk); \
+  }
+#define QDEC_FA_STORE(b)                                           \
+  {                                                                \
+    *reinterpret_cast<uint4*>(&Kh[b][kc0 * KP + kd]) = rkh0;       \
+    *reinterpret_cast<uint4*>(&Kh[b][kc1 * KP + kd]) = rkh1;       \
+    *reinterpret_cast<uint4*>(&Kl[b][kc0 * KP + kd]) = rkl0;       \
+    *reinterpret_cast<uint4*>(&Kl[b][kc1 * KP + kd]) = rkl1;       \
+    *reinterpret_cast<uint4*>(&Vh[b][vd0 * VP + vk]) = rvh0;       \
+    *reinterpret_cast<uint4*>(&Vh[b][vd1 * VP + vk]) = rvh1;       \
+    *reinterpret_cast<uint4*>(&Vl[b][vd0 * VP + vk]) = rvl0;       \
+    *reinterpret_cast<uint4*>(&Vl[b][vd1 * VP + vk]) = rvl1;       \
+  }
+  const int kbeg = blockIdx.z * per * KT, kend = kt_end * KT;
+  if (kbeg < kend) {
+    QDEC_FA_LOAD(kbeg)
+    QDEC_FA_STORE(0)
+  }
+  __syncthreads();
+  for (int k0 = kbeg, buf = 0; k0 < kend; k0 += KT, buf ^= 1) {
+    // the next tile (the last iteration reloads its own: the store below
+    // then fills a buffer nobody reads)
+    const int kn = k0 + KT < kend ? k0 + KT : k0;
+    QDEC_FA_LOAD(kn)
 
     // S^T tile: KB key blocks of 16 x this wave's 16 queries, per head
     f32x4_t sc[VH][KB];
@@ -1092,8 +1117,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         const int off = (16 * j + c16) * KP + 32 * st + 8 * gq;
-        const bf16x8_t kh = *reinterpret_cast<const bf16x8_t*>(&Kh[off]);
-        const bf16x8_t kl = *reinterpret_cast<const bf16x8_t*>(&Kl[off]);
+        const bf16x8_t kh = *reinterpret_cast<const bf16x8_t*>(&Kh[buf][off]);
+        const bf16x8_t kl = *reinterpret_cast<const bf16x8_t*>(&Kl[buf][off]);
 #pragma unroll
         for (int hh = 0; hh < VH; ++hh) {
           sc[hh][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qh[hh][st], sc[hh][j], 0, 0, 0);
@@ -1155,8 +1180,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
       for (int c = 0; c < KH; ++c) {
         // keys 4 gq + e and 16 + 4 gq + e of the group sit together at 8 gq
         const int off = (16 * b + c16) * VP + 32 * c + 8 * gq;
-        const bf16x8_t vh = *reinterpret_cast<const bf16x8_t*>(&Vh[off]);
-        const bf16x8_t vl = *reinterpret_cast<const bf16x8_t*>(&Vl[off]);
+        const bf16x8_t vh = *reinterpret_cast<const bf16x8_t*>(&Vh[buf][off]);
+        const bf16x8_t vl = *reinterpret_cast<const bf16x8_t*>(&Vl[buf][off]);
 #pragma unroll
         for (int hh = 0; hh < VH; ++hh) {
           acc[hh][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vh, ph[hh][c], acc[hh][b], 0, 0, 0);
@@ -1164,7 +1189,12 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
           acc[hh][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vh, pl[hh][c], acc[hh][b], 0, 0, 0);
         }
       }
+    // the other buffer was last read before the previous barrier
+    QDEC_FA_STORE(buf ^ 1)
+    __syncthreads();
   }
+#undef QDEC_FA_LOAD
+#undef QDEC_FA_STORE
 
   if (S > 1) {
     // partial of split z: o (unnormalised), the exponent base m and the sum l
