@@ -982,6 +982,9 @@ constexpr int VP = KT + 8;      // bf16 pitch of a V^T row in LDS
 constexpr int KB = KT / 16;     // 16-key blocks per tile
 constexpr int KH = KT / 32;     // 32-key groups per tile
 }  // namespace fa
+// starting exponent base of the online softmax: finite, so that exp2 of a
+// masked score (-inf) minus the base is 0, and below any reachable score
+constexpr float kFaFloor = -1e30f;
 
 // GROUP query heads share each KV head; QS query blocks of 16 per wave (GROUP
 // x QS "virtual heads" v: head g GROUP + v % GROUP, queries 16 (w QS + v / GROUP)
@@ -1047,7 +1050,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
   f32x4_t acc[VH][D / 16];
 #pragma unroll
   for (int hh = 0; hh < VH; ++hh) {
-    m[hh] = -INFINITY;
+    m[hh] = kFaFloor;
     lsum[hh] = 0.f;
 #pragma unroll
     for (int b = 0; b < D / 16; ++b) acc[hh][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -1127,42 +1130,57 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
         }
       }
 
-    // online softmax per head; P^T operands per 32-key group
-    bf16x8_t ph[VH][KH], pl[VH][KH];
+    // online softmax per head; P^T operands per 32-key group. Only tiles
+    // that reach past this wave's first query (or past T) need the mask.
+    const bool full = k0 + KT <= T && (!causal || k0 + KT - 1 <= q0 + 16 * w * QS);
+    float mx[VH];
 #pragma unroll
     for (int hh = 0; hh < VH; ++hh) {
-      const int qlim = causal ? qpv[hh] : T - 1;  // this lane's last visible key
-      float mx = m[hh];
+      if (!full) {
+        const int qlim = causal ? qpv[hh] : T - 1;  // this lane's last visible key
 #pragma unroll
-      for (int j = 0; j < KB; ++j)
+        for (int j = 0; j < KB; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int key = k0 + 16 * j + 4 * gq + e;
-          if (key > qlim || key >= T) sc[hh][j][e] = -INFINITY;
-          mx = fmaxf(mx, sc[hh][j][e]);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      // The exponent base m moves only when a score passes it by more than 8
-      // (a factor of 256 in the probabilities): the normalised result is the
-      // same for any base, and most tiles then skip rescaling the output
-      // accumulators. Key 0 is visible to every query, so the first tile sets
-      // a finite base (m starts at -inf, where alpha is 0).
-      if (mx > m[hh] + 8.f) {
-        const float alpha = __builtin_amdgcn_exp2f(m[hh] - mx);
+          for (int e = 0; e < 4; ++e) {
+            const int key = k0 + 16 * j + 4 * gq + e;
+            if (key > qlim || key >= T) sc[hh][j][e] = -INFINITY;
+          }
+      }
+      float v = m[hh];
+#pragma unroll
+      for (int j = 0; j < KB; ++j) v = fmaxf(v, fmaxf(fmaxf(sc[hh][j][0], sc[hh][j][1]), fmaxf(sc[hh][j][2], sc[hh][j][3])));
+      v = fmaxf(v, __shfl_xor(v, 16, kWave));
+      mx[hh] = fmaxf(v, __shfl_xor(v, 32, kWave));
+    }
+    // The exponent base m moves only when a score passes it by more than 8
+    // (a factor of 256 in the probabilities): the normalised result is the
+    // same for any base, and most tiles then skip rescaling the output
+    // accumulators (the branch is taken by the whole wave or not at all). Key
+    // 0 is visible to every query, so the first tile sets the base; m starts
+    // at a finite floor, so a masked score (-inf) always gives p = 0.
+    bool move = false;
+#pragma unroll
+    for (int hh = 0; hh < VH; ++hh) move = move || mx[hh] > m[hh] + 8.f;
+    if (__builtin_amdgcn_ballot_w64(move) != 0) {
+#pragma unroll
+      for (int hh = 0; hh < VH; ++hh) {
+        const bool mv = mx[hh] > m[hh] + 8.f;
+        const float alpha = mv ? __builtin_amdgcn_exp2f(m[hh] - mx[hh]) : 1.f;
         lsum[hh] *= alpha;
 #pragma unroll
         for (int b = 0; b < D / 16; ++b) acc[hh][b] *= alpha;
-        m[hh] = mx;
+        m[hh] = mv ? mx[hh] : m[hh];
       }
+    }
+    bf16x8_t ph[VH][KH], pl[VH][KH];
+#pragma unroll
+    for (int hh = 0; hh < VH; ++hh) {
       float ps = 0.f;
 #pragma unroll
       for (int j = 0; j < KB; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          // a masked key counts 0 even while the base is still -inf (a key
-          // range that starts past this query sees no visible key)
-          const float p = sc[hh][j][e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[hh][j][e] - m[hh]);
+          const float p = __builtin_amdgcn_exp2f(sc[hh][j][e] - m[hh]);
           ps += p;
           const __bf16 h = (__bf16)p;
           ph[hh][j / 2][4 * (j % 2) + e] = h;
@@ -1210,7 +1228,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
           *reinterpret_cast<float4*>(pp + 16 * b + 4 * gq) =
               make_float4(acc[hh][b][0], acc[hh][b][1], acc[hh][b][2], acc[hh][b][3]);
         if (gq == 0) {
-          pp[D] = m[hh];
+          pp[D] = lsum[hh] > 0.f ? m[hh] : -INFINITY;  // no visible key: the merge skips it
           pp[D + 1] = lsum[hh];
         }
       }
