@@ -671,9 +671,15 @@ int run_layers(qdec_model* m, int T, float* X, float* QKV, float* Attn, float* Z
   const bool fuse_z = gemm_tiled_fits(bf, T, d.H, 2 * d.F);  // the split epilogue is the tiled kernel's
   uint16_t* zhi = (uint16_t*)Z;
   uint16_t* zlo = zhi + (size_t)T * d.F;
+  // a residual GEMM that splits K may apply the next RMSNorm in its
+  // reduction (bf16 only: the fp32 path's operand is not split)
+  auto resid_norm = [&](const float* gain) {
+    return RowNorm{gain, d.eps, (uint16_t*)A0, (uint16_t*)A1, false};
+  };
+  bool in_done = false;
   for (int l = 0; l < d.L; ++l) {
     const LayerW& w = m->layers[l];
-    LAUNCH(norm_in(X, d.H, w.in_norm));
+    if (!in_done) LAUNCH(norm_in(X, d.H, w.in_norm));
     LAUNCH(launch_gemm(bf, EPI_STORE, A0, A1, T, d.H, w.wqkv, d.qkv(), QKV, d.qkv(), st, nullptr, sk));
     if (int e = rope(l)) return e;
     if (fuse_o) {
@@ -682,17 +688,21 @@ int run_layers(qdec_model* m, int T, float* X, float* QKV, float* Attn, float* Z
       if (int e = attn(l, nullptr, nullptr)) return e;
       LAUNCH(norm_in(Attn, d.NQ * d.D, nullptr));
     }
-    LAUNCH(launch_gemm(bf, EPI_RESID, A0, A1, T, d.NQ * d.D, w.wo, d.H, X, d.H, st, nullptr, sk));
-    LAUNCH(norm_in(X, d.H, w.post_norm));
+    RowNorm post = resid_norm(w.post_norm);
+    LAUNCH(launch_gemm(bf, EPI_RESID, A0, A1, T, d.NQ * d.D, w.wo, d.H, X, d.H, st, nullptr, sk, bf ? &post : nullptr));
+    if (!post.done) LAUNCH(norm_in(X, d.H, w.post_norm));
+    RowNorm next = resid_norm(l + 1 < d.L ? m->layers[l + 1].in_norm : nullptr);
+    RowNorm* nx = bf && l + 1 < d.L ? &next : nullptr;
     if (fuse_z) {
       LAUNCH(launch_gemm_swiglu_split((const uint16_t*)A0, (const uint16_t*)A1, T, d.H, (const uint16_t*)w.wgu,
                                       2 * d.F, zhi, zlo, d.F, st));
-      LAUNCH(launch_gemm(bf, EPI_RESID, zhi, zlo, T, d.F, w.wd, d.H, X, d.H, st, nullptr, sk));
+      LAUNCH(launch_gemm(bf, EPI_RESID, zhi, zlo, T, d.F, w.wd, d.H, X, d.H, st, nullptr, sk, nx));
     } else {
       LAUNCH(launch_gemm(bf, EPI_SWIGLU, A0, A1, T, d.H, w.wgu, 2 * d.F, Z, d.F, st, nullptr, sk));
       LAUNCH(norm_in(Z, d.F, nullptr));
-      LAUNCH(launch_gemm(bf, EPI_RESID, A0, A1, T, d.F, w.wd, d.H, X, d.H, st, nullptr, sk));
+      LAUNCH(launch_gemm(bf, EPI_RESID, A0, A1, T, d.F, w.wd, d.H, X, d.H, st, nullptr, sk, nx));
     }
+    in_done = next.done;
   }
   return QDEC_OK;
 }
@@ -780,8 +790,11 @@ int run_prefill(qdec_state* s, int T, const float* audio, int a0, int La, float*
   // short prompts on the fused path: Q/K norm, RoPE, K/V append and the
   // attention in one launch per layer
   const bool small = fused && attn_small_fits(d, T);
+  // the matrix-core attention applies the Q/K norm and RoPE and appends K/V
+  // itself
+  const bool fold = !small && attn_prefill_ropes(d);
   auto rope = [&](int l) -> int {
-    if (small) return 0;  // inside the attention launch
+    if (small || fold) return 0;  // inside the attention launch
     const LayerW& w = m->layers[l];
     LAUNCH(launch_qk_rope_append(d, m->pQKV, T, 0, w.q_norm, w.k_norm, m->rope_cos, m->rope_sin, s->pt_dev, l, st));
     return 0;
@@ -793,7 +806,9 @@ int run_prefill(qdec_state* s, int T, const float* audio, int a0, int La, float*
                                st));
       return 0;
     }
-    LAUNCH(launch_attn_prefill(d, m->pQKV, T, m->pAttn, m->pKV, st, hi, lo, true, &m->split.sk));
+    const LayerW& w = m->layers[l];
+    const QkRope rp{fold ? 1 : 0, w.q_norm, w.k_norm, m->rope_cos, m->rope_sin, s->pt_dev, l, d.L, 0, d.eps};
+    LAUNCH(launch_attn_prefill(d, m->pQKV, T, m->pAttn, m->pKV, st, hi, lo, true, &m->split.sk, &rp));
     return 0;
   };
   if (fused) {

@@ -147,10 +147,26 @@ int kv_split_pad(int T);
 // causal = false (only where attn_prefill_uses_split): every query sees every key.
 // With a split-K workspace (sk) and few query blocks, each block's key range
 // is split and the partials merged by a second kernel.
+// Q/K-RMSNorm, RoPE and the K/V append of one layer, folded into the prefill
+// attention launch (norm = 0: the Q/K rows are used as they are and nothing
+// is appended). Rows t are positions pos0 + t.
+struct QkRope {
+  int norm;
+  const float* q_norm;
+  const float* k_norm;
+  const float* rcos;
+  const float* rsin;
+  const int64_t* page_table;
+  int layer, L, pos0;
+  float eps;
+};
 struct SplitK;
 hipError_t launch_attn_prefill(const Dims& d, const float* qkv, int T, float* out, uint16_t* const kv[4],
                                hipStream_t st, uint16_t* out_hi = nullptr, uint16_t* out_lo = nullptr,
-                               bool causal = true, SplitK* sk = nullptr);
+                               bool causal = true, SplitK* sk = nullptr, const QkRope* rope = nullptr);
+// Whether launch_attn_prefill applies a QkRope itself (else the caller runs
+// launch_qk_rope_append first).
+bool attn_prefill_ropes(const Dims& d);
 
 hipError_t launch_rms_split(const float* X, int T, int K, const float* gain, float eps, uint16_t* hi,
                             uint16_t* lo, hipStream_t st);
@@ -173,8 +189,20 @@ constexpr size_t kSplitKFloats = (size_t)16 << 20;  // 64 MB
 // below 128 tiles, splitting K).
 // bias (fp32 [N], bf16 weights only) is added to each output before the
 // epilogue (STORE, RESID, RELU); nullptr for none.
+// With norm set (RESID only), a split launch's reduction also applies the
+// next RMSNorm to each finished row and writes it as the next GEMM's bf16
+// hi/lo operand (as launch_rms_split would), and sets norm->done; otherwise
+// norm->done stays false and the caller runs the norm.
+struct RowNorm {
+  const float* gain;
+  float eps;
+  uint16_t* hi;
+  uint16_t* lo;
+  bool done;
+};
 hipError_t launch_gemm(bool bf16, Epi epi, const void* A0, const void* A1, int M, int K, const void* W, int N,
-                       float* C, int ldc, hipStream_t st, const float* bias = nullptr, SplitK* sk = nullptr);
+                       float* C, int ldc, hipStream_t st, const float* bias = nullptr, SplitK* sk = nullptr,
+                       RowNorm* norm = nullptr);
 // Whether launch_gemm takes the tiled MFMA kernel for this shape without a
 // split-K workspace.
 bool gemm_tiled_fits(bool bf16, int M, int K, int N);

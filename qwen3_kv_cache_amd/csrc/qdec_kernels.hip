@@ -920,22 +920,54 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const float* __restri
 // V^T columns are stored in the order the P^T operand takes its k-slots:
 // keys 4 q + e and 16 + 4 q + e (e = 0..3) at slots 8 q + e and 8 q + 4 + e,
 // so a lane's A operand of O^T = V^T P^T is one 16-byte LDS read. Block =
-// (64 tokens, head g).
+// (64 tokens, head g). With rp.norm set the keys arrive as projected: the
+// block applies the K-RMSNorm and RoPE of each key (the arithmetic of
+// qk_rope_append_vec_kernel) and appends K and V of positions rp.pos0 + t to
+// the state's pages.
 __global__ __launch_bounds__(256) void kv_split_kernel(const float* __restrict__ qkv, int T, int ld, int NQ,
                                                         int NKV, uint16_t* __restrict__ kh,
                                                         uint16_t* __restrict__ kl, uint16_t* __restrict__ vth,
-                                                        uint16_t* __restrict__ vtl, int Tp) {
-  constexpr int D = 128, TT = 64;
+                                                        uint16_t* __restrict__ vtl, int Tp, QkRope rp) {
+  constexpr int D = 128, TT = 64, HALF = D / 2;
   __shared__ float vs[D][TT + 1];
   const int g = blockIdx.y, t0 = blockIdx.x * TT;
   const float* kbase = qkv + (size_t)(NQ + g) * D;
   const float* vbase = qkv + (size_t)(NQ + NKV + g) * D;
 #pragma unroll
   for (int i = 0; i < TT * D / 4 / 256; ++i) {
+    // 32 threads per key (one half-wave), thread c % 32 holding columns d0..d0+3
     const int c = threadIdx.x + 256 * i, tl = c / (D / 4), d0 = 4 * (c % (D / 4));
     const int t = min(t0 + tl, T - 1);
-    const float4 k = *reinterpret_cast<const float4*>(kbase + (size_t)t * ld + d0);
+    float4 k = *reinterpret_cast<const float4*>(kbase + (size_t)t * ld + d0);
     const float4 v = *reinterpret_cast<const float4*>(vbase + (size_t)t * ld + d0);
+    if (rp.norm) {
+      // rotate-half partner columns d0 +- 64 sit 16 lanes away
+      float ss = k.x * k.x + k.y * k.y + k.z * k.z + k.w * k.w;
+#pragma unroll
+      for (int o = 1; o < D / 4; o <<= 1) ss += __shfl_xor(ss, o, kWave);
+      const float inv = 1.f / sqrtf(ss / (float)D + rp.eps);
+      const float4 gk = *reinterpret_cast<const float4*>(rp.k_norm + d0);
+      const float x[4] = {k.x * inv * gk.x, k.y * inv * gk.y, k.z * inv * gk.z, k.w * inv * gk.w};
+      float y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = __shfl_xor(x[e], 16, kWave);
+      const int pos = rp.pos0 + t, j0 = d0 % HALF;
+      const float4 cs = *reinterpret_cast<const float4*>(rp.rcos + (size_t)pos * HALF + j0);
+      const float4 sn = *reinterpret_cast<const float4*>(rp.rsin + (size_t)pos * HALF + j0);
+      const float cv[4] = {cs.x, cs.y, cs.z, cs.w}, sv[4] = {sn.x, sn.y, sn.z, sn.w};
+      float r[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        r[e] = d0 < HALF ? x[e] * cv[e] - y[e] * sv[e] : x[e] * cv[e] + y[e] * sv[e];
+      k = make_float4(r[0], r[1], r[2], r[3]);
+      if (t0 + tl < T) {
+        Dims dd{rp.L, 0, NQ, NKV, D, 0, 0, 0.f};
+        float* page = reinterpret_cast<float*>(rp.page_table[pos / kPage]);
+        const int slot = pos % kPage;
+        *reinterpret_cast<float4*>(page + page_offset(dd, rp.layer, 0, g, slot) + d0) = k;
+        *reinterpret_cast<float4*>(page + page_offset(dd, rp.layer, 1, g, slot) + d0) = v;
+      }
+    }
     vs[d0][tl] = v.x;
     vs[d0 + 1][tl] = v.y;
     vs[d0 + 2][tl] = v.z;
@@ -999,7 +1031,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
                                                                  float* __restrict__ out, int ldo, float qscale,
                                                                  uint16_t* __restrict__ ohi,
                                                                  uint16_t* __restrict__ olo, int causal,
-                                                                 float* __restrict__ part) {
+                                                                 float* __restrict__ part, QkRope rp) {
   using namespace fa;
   constexpr int VH = GROUP * QS, QTB = 64 * QS;  // virtual heads per wave, queries per block
   // two tile buffers: the next tile's global loads are in flight while the
@@ -1027,18 +1059,51 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
   for (int v = 0; v < VH; ++v) qpv[v] = q0 + 16 * (w * QS + v / GROUP) + c16;
 
   // Q^T operands (B of S^T = K Q^T): lane supplies Q[query c16][32 s + 8 gq + i]
+  // (with rp.norm: the Q-RMSNorm and RoPE of each query first; the lane's
+  // columns 32 st + 8 gq + i and their rotate-half partners (st +- 2) are
+  // its own, and the 4 lanes of a query share its sum of squares)
   bf16x8_t qh[VH][4], ql[VH][4];
 #pragma unroll
   for (int hh = 0; hh < VH; ++hh) {
-    const float* qsrc = qkv + (size_t)min(qpv[hh], T - 1) * ld + (size_t)(g * GROUP + hh % GROUP) * D + 8 * gq;
+    const int qrow = min(qpv[hh], T - 1);
+    const float* qsrc = qkv + (size_t)qrow * ld + (size_t)(g * GROUP + hh % GROUP) * D + 8 * gq;
+    float v[4][8];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const float4 a = *reinterpret_cast<const float4*>(qsrc + 32 * st);
       const float4 b = *reinterpret_cast<const float4*>(qsrc + 32 * st + 4);
-      const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      v[st][0] = a.x, v[st][1] = a.y, v[st][2] = a.z, v[st][3] = a.w;
+      v[st][4] = b.x, v[st][5] = b.y, v[st][6] = b.z, v[st][7] = b.w;
+    }
+    if (rp.norm) {
+      float ss = 0.f;
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss = fmaf(v[st][i], v[st][i], ss);
+      ss += __shfl_xor(ss, 16, kWave);
+      ss += __shfl_xor(ss, 32, kWave);
+      const float inv = 1.f / sqrtf(ss / (float)D + rp.eps);
+      float x[4][8];
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[st][i] = v[st][i] * inv * rp.q_norm[32 * st + 8 * gq + i];
+      const size_t rb = (size_t)(rp.pos0 + qrow) * (D / 2) + 8 * gq;
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float c = rp.rcos[rb + 32 * st + i], sn = rp.rsin[rb + 32 * st + i];
+          v[st][i] = x[st][i] * c - x[st + 2][i] * sn;
+          v[st + 2][i] = x[st + 2][i] * c + x[st][i] * sn;
+        }
+    }
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float x = v[i] * qscale;
+        const float x = v[st][i] * qscale;
         const __bf16 h = (__bf16)x;
         qh[hh][st][i] = h;
         ql[hh][st][i] = (__bf16)(x - (float)h);
@@ -1757,14 +1822,15 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(RowsGemm g) {
 }
 
 // Large-M GEMM (prefill): C[M, N] (+)= (Ahi + Alo)[M, K] . W[N, K]^T with
-// 128 x 128 output tiles and K steps of 32 staged in LDS (double buffered:
-// the next step's global loads are in flight while the current one is
-// multiplied). 4 waves in a 2 x 2 arrangement, each 64 x 64 = 4 x 4 MFMA
-// tiles of 16 x 16, two MFMAs (hi, lo) per tile and step. LDS rows are 64
+// 128 x 128 (or 64 x 128) output tiles and K steps of 32 staged in LDS
+// (double buffered: the next step's global loads are in flight while the
+// current one is multiplied). 4 waves in a 2 x 2 arrangement, each 64 x 64
+// (or 32 x 64) = 4 x 4 (or 2 x 4) MFMA tiles of 16 x 16, two MFMAs (hi, lo)
+// per tile and step. LDS rows are 64
 // bytes with XOR-swizzled 16-byte chunks (tg_sw). Epilogues as in
 // gemm_bf16x2_kernel.
 namespace tg {
-constexpr int BM = 128, BN = 128, BK = 32;
+constexpr int BN = 128, BK = 32;
 constexpr size_t kTiledWSliceBytes = size_t(3) << 20;  // W bytes per XCD column group
 constexpr int P = BK;  // bf16 pitch of an LDS row (chunks XOR-swizzled)
 // 16-byte chunk c of LDS row r sits at chunk c ^ ((r / 4) % 4): the 16 rows
@@ -1783,7 +1849,7 @@ struct TiledSplit {
   int kc;    // K per split (a multiple of BK)
 };
 
-template <int EPI>
+template <int EPI, int MW>
 __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint16_t* __restrict__ Ahi,
                                                           const uint16_t* __restrict__ Alo, int M, int K,
                                                           const uint16_t* __restrict__ W, int N,
@@ -1792,7 +1858,11 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint16_t* __restr
                                                           uint16_t* __restrict__ Zlo,
                                                           const float* __restrict__ bias, TiledSplit sp) {
   using namespace tg;
-  __shared__ uint16_t sAh[2][BM * P], sAl[2][BM * P], sW[2][BN * P];
+  // MW 16-row MFMA tiles per wave along M: 128-row tiles (MW = 4) or
+  // 64-row tiles (MW = 2, twice the workgroups for the same shape)
+  static_assert(MW == 4 || MW == 2, "128- or 64-row tiles");
+  constexpr int TM = 32 * MW;
+  __shared__ uint16_t sAh[2][TM * P], sAl[2][TM * P], sW[2][BN * P];
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   const int c16 = lane % 16, gq = lane / 16;
   const int wm = w / 2, wn = w % 2;
@@ -1813,10 +1883,11 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint16_t* __restr
       tile = ((x / gc) * rh + j / cw) * gridDim.x + (x % gc) * cw + j % cw;
     }
   }
-  const int n0 = (tile % gridDim.x) * BN, m0 = (tile / gridDim.x) * BM;
+  const int n0 = (tile % gridDim.x) * BN, m0 = (tile / gridDim.x) * TM;
 
-  // staging: 128 rows x 4 chunks of 16 bytes per matrix; thread t moves
-  // chunks t and t + 256 (rows t / 4 and t / 4 + 64, chunk t % 4)
+  // staging: rows of 4 chunks of 16 bytes per matrix; thread t moves chunks
+  // t and t + 256 (rows t / 4 and t / 4 + 64, chunk t % 4), the second A
+  // chunk only with 128-row tiles
   const int srow = threadIdx.x / 4, skc = threadIdx.x % 4;
   const size_t a0 = (size_t)min(m0 + srow, M - 1) * K + 8 * skc;
   const size_t a1 = (size_t)min(m0 + srow + 64, M - 1) * K + 8 * skc;
@@ -1826,22 +1897,26 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint16_t* __restr
   uint4 rh0, rh1, rl0, rl1, rw0, rw1;
 #define QDEC_TG_LOAD(k)                                         \
   rh0 = *reinterpret_cast<const uint4*>(Ahi + a0 + (k));        \
-  rh1 = *reinterpret_cast<const uint4*>(Ahi + a1 + (k));        \
   rl0 = *reinterpret_cast<const uint4*>(Alo + a0 + (k));        \
-  rl1 = *reinterpret_cast<const uint4*>(Alo + a1 + (k));        \
+  if constexpr (MW == 4) {                                      \
+    rh1 = *reinterpret_cast<const uint4*>(Ahi + a1 + (k));      \
+    rl1 = *reinterpret_cast<const uint4*>(Alo + a1 + (k));      \
+  }                                                             \
   rw0 = *reinterpret_cast<const uint4*>(W + w0 + (k));          \
   rw1 = *reinterpret_cast<const uint4*>(W + w1 + (k));
 #define QDEC_TG_STORE(buf)                                      \
   *reinterpret_cast<uint4*>(&sAh[buf][l0]) = rh0;               \
-  *reinterpret_cast<uint4*>(&sAh[buf][l1]) = rh1;               \
   *reinterpret_cast<uint4*>(&sAl[buf][l0]) = rl0;               \
-  *reinterpret_cast<uint4*>(&sAl[buf][l1]) = rl1;               \
+  if constexpr (MW == 4) {                                      \
+    *reinterpret_cast<uint4*>(&sAh[buf][l1]) = rh1;             \
+    *reinterpret_cast<uint4*>(&sAl[buf][l1]) = rl1;             \
+  }                                                             \
   *reinterpret_cast<uint4*>(&sW[buf][l0]) = rw0;                \
   *reinterpret_cast<uint4*>(&sW[buf][l1]) = rw1;
 
-  f32x4_t acc[4][4];
+  f32x4_t acc[MW][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MW; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
@@ -1855,10 +1930,10 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint16_t* __restr
     if (kt + 1 < nk) {
       QDEC_TG_LOAD((kt + 1) * BK)
     }
-    bf16x8_t ah[4], al[4], b[4];
+    bf16x8_t ah[MW], al[MW], b[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int off = tg_sw(wm * 64 + 16 * i + c16, gq);
+    for (int i = 0; i < MW; ++i) {
+      const int off = tg_sw(wm * 16 * MW + 16 * i + c16, gq);
       ah[i] = *reinterpret_cast<const bf16x8_t*>(&sAh[buf][off]);
       al[i] = *reinterpret_cast<const bf16x8_t*>(&sAl[buf][off]);
     }
@@ -1866,7 +1941,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint16_t* __restr
     for (int j = 0; j < 4; ++j)
       b[j] = *reinterpret_cast<const bf16x8_t*>(&sW[buf][tg_sw(wn * 64 + 16 * j + c16, gq)]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MW; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[i], b[j], acc[i][j], 0, 0, 0);
@@ -1883,13 +1958,13 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint16_t* __restr
   if (S > 1) {
     float* pz = sp.P + (size_t)kz * M * N;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MW; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int col = n0 + wn * 64 + 16 * j + c16;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int row = m0 + wm * 64 + 16 * i + 4 * gq + e;
+          const int row = m0 + wm * 16 * MW + 16 * i + 4 * gq + e;
           if (row < M) pz[(size_t)row * N + col] = acc[i][j][e];
         }
       }
@@ -1897,13 +1972,13 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint16_t* __restr
   }
 
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MW; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int col = n0 + wn * 64 + 16 * j + c16;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int row = m0 + wm * 64 + 16 * i + 4 * gq + e;
+        const int row = m0 + wm * 16 * MW + 16 * i + 4 * gq + e;
         const float v = acc[i][j][e];
         if (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SPLIT) {
           const float u = __shfl_xor(v, 8, kWave);
@@ -1975,6 +2050,63 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     c[1] = v.y;
     c[2] = v.z;
     c[3] = v.w;
+  }
+}
+
+// The split sum of splitk_reduce_kernel with the residual epilogue, fused
+// with the RMSNorm that follows it: block = one row of N <= 1024 R columns;
+// each element x = C + sum of the splits in order is stored to C, then
+// x * inv * gain (inv from the row's sum of squares) is written as bf16 hi
+// and lo, as rms_split_vec_kernel does.
+template <int R>
+__global__ __launch_bounds__(256) void splitk_resid_norm_kernel(const float* __restrict__ P, int S, int M, int N,
+                                                                float* __restrict__ C, int ldc,
+                                                                const float* __restrict__ gain, float eps,
+                                                                uint16_t* __restrict__ hi, uint16_t* __restrict__ lo) {
+  __shared__ float red[8];
+  const int t = blockIdx.x, nc = N / 4;
+  float4 v[R];
+  float ss = 0.f;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int c = threadIdx.x + 256 * r;
+    v[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c < nc) {
+      const size_t i = (size_t)t * N + 4 * c;
+      float4 a = *reinterpret_cast<const float4*>(P + i);
+      for (int z = 1; z < S; ++z) {
+        const float4 b = *reinterpret_cast<const float4*>(P + (size_t)z * M * N + i);
+        a.x += b.x;
+        a.y += b.y;
+        a.z += b.z;
+        a.w += b.w;
+      }
+      float* cp = C + (size_t)t * ldc + 4 * c;
+      v[r] = make_float4(cp[0] + a.x, cp[1] + a.y, cp[2] + a.z, cp[3] + a.w);
+      cp[0] = v[r].x;
+      cp[1] = v[r].y;
+      cp[2] = v[r].z;
+      cp[3] = v[r].w;
+    }
+    ss = fmaf(v[r].x, v[r].x, fmaf(v[r].y, v[r].y, fmaf(v[r].z, v[r].z, fmaf(v[r].w, v[r].w, ss))));
+  }
+  const float inv = 1.f / sqrtf(block_sum(ss, red) / (float)N + eps);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int c = threadIdx.x + 256 * r;
+    if (c < nc) {
+      const float4 g = reinterpret_cast<const float4*>(gain)[c];
+      const float e[4] = {v[r].x * inv * g.x, v[r].y * inv * g.y, v[r].z * inv * g.z, v[r].w * inv * g.w};
+      uint16_t h[4], l[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        h[k] = f32_to_bf16_rne(e[k]);
+        l[k] = f32_to_bf16_rne(e[k] - bf16_to_f32(h[k]));
+      }
+      const size_t o = (size_t)t * N + 4 * c;
+      *reinterpret_cast<uint2*>(hi + o) = make_uint2(h[0] | ((unsigned)h[1] << 16), h[2] | ((unsigned)h[3] << 16));
+      *reinterpret_cast<uint2*>(lo + o) = make_uint2(l[0] | ((unsigned)l[1] << 16), l[2] | ((unsigned)l[3] << 16));
+    }
   }
 }
 
@@ -2338,16 +2470,22 @@ bool attn_prefill_uses_split(const Dims& d) {
   return d.D == fa::D && (group == 1 || group == 2);
 }
 
+bool attn_prefill_ropes(const Dims& d) { return attn_prefill_uses_split(d); }
+
 hipError_t launch_attn_prefill(const Dims& d, const float* qkv, int T, float* out, uint16_t* const kv[4],
-                               hipStream_t st, uint16_t* out_hi, uint16_t* out_lo, bool causal, SplitK* sk) {
+                               hipStream_t st, uint16_t* out_hi, uint16_t* out_lo, bool causal, SplitK* sk,
+                               const QkRope* rope) {
   const int group = d.NQ / d.NKV;
   if ((out_hi != nullptr) != (out_lo != nullptr) || ((out_hi || !causal) && !attn_prefill_uses_split(d)))
     return hipErrorInvalidValue;
+  if (rope && rope->norm && !attn_prefill_ropes(d)) return hipErrorInvalidValue;
   const float scale = 1.f / sqrtf((float)d.D);
   if (attn_prefill_uses_split(d)) {
+    QkRope rp{};
+    if (rope) rp = *rope;
     const int Tp = kv_split_pad(T);
     kv_split_kernel<<<dim3(Tp / 64, d.NKV), 256, 0, st>>>(qkv, T, d.qkv(), d.NQ, d.NKV, kv[0], kv[1], kv[2], kv[3],
-                                                          Tp);
+                                                          Tp, rp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const float qs = scale * 1.4426950408889634f;  // scores in base 2
@@ -2370,13 +2508,13 @@ hipError_t launch_attn_prefill(const Dims& d, const float* qkv, int T, float* ou
     dim3 grid(nqb, d.NKV, S);
     if (group == 1 && !two)
       attn_prefill_mfma_kernel<1, 1><<<grid, 256, 0, st>>>(qkv, T, d.qkv(), kv[0], kv[1], kv[2], kv[3], Tp, out,
-                                                           d.NQ * d.D, qs, out_hi, out_lo, causal ? 1 : 0, part);
+                                                           d.NQ * d.D, qs, out_hi, out_lo, causal ? 1 : 0, part, rp);
     else if (group == 2)
       attn_prefill_mfma_kernel<2, 1><<<grid, 256, 0, st>>>(qkv, T, d.qkv(), kv[0], kv[1], kv[2], kv[3], Tp, out,
-                                                        d.NQ * d.D, qs, out_hi, out_lo, causal ? 1 : 0, part);
+                                                        d.NQ * d.D, qs, out_hi, out_lo, causal ? 1 : 0, part, rp);
     else
       attn_prefill_mfma_kernel<1, 2><<<grid, 256, 0, st>>>(qkv, T, d.qkv(), kv[0], kv[1], kv[2], kv[3], Tp, out,
-                                                        d.NQ * d.D, qs, out_hi, out_lo, causal ? 1 : 0, part);
+                                                        d.NQ * d.D, qs, out_hi, out_lo, causal ? 1 : 0, part, rp);
     if (S > 1) {
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
@@ -2501,35 +2639,46 @@ hipError_t launch_gemm_rows(Epi epi, bool norm, const RowsGemm& g0, hipStream_t 
                    : rows_dispatch<1, 1, uint16_t>(epi, norm, grid, g, st);
 }
 
+namespace {
+// Rows per output tile: 128, or 64 when 128-row tiles would give fewer than
+// kRows64Below workgroups (about two per CU): with one 4-wave workgroup per
+// CU nothing hides the load latency of a K step.
+constexpr int kRows64Below = 512;
+int tiled_rows(int M, int N) { return (N / tg::BN) * ((M + 127) / 128) < kRows64Below ? 64 : 128; }
+int tiled_tiles(int M, int N) {
+  const int r = tiled_rows(M, N);
+  return (N / tg::BN) * ((M + r - 1) / r);
+}
+}  // namespace
+
 // The tiled kernel needs M > 64 and whole column tiles, and is taken only with
 // at least 128 tiles: below that its few long-running workgroups leave most
 // CUs idle and the 64 x 64 small-M kernel is faster (measured on 183- to
 // 1024-row inputs: the 512-token prefill 8.05 -> 7.55 ms, the adaptor at 183
 // frames 0.49 -> 0.40 ms).
 bool gemm_tiled_fits(bool bf16, int M, int K, int N) {
-  return bf16 && M > 64 && N % tg::BN == 0 && K % tg::BK == 0 && (N / tg::BN) * ((M + tg::BM - 1) / tg::BM) >= 128;
+  return bf16 && M > 64 && N % tg::BN == 0 && K % tg::BK == 0 && tiled_tiles(M, N) >= 128;
 }
 
 namespace {
 
-// The tiled kernel's plan for a shape: splits (1: none) and K per split.
-// Below 128 tiles a workspace lets the K range split until about 256
-// workgroups run (at most 8 splits, at least four K steps each), for the
-// epilogues the reduction kernel applies (STORE, RESID, RELU).
+// The tiled kernel's plan for a shape: tile rows, splits (1: none) and K per
+// split. Below 256 tiles (one workgroup per CU) a workspace lets the K range
+// split until about 512 workgroups run (at most 8 splits, at least four K
+// steps each), for the epilogues the reduction kernel applies (STORE, RESID,
+// RELU); without a split the kernel is taken from 128 tiles on.
 struct TiledPlan {
   bool ok;
-  int S, kc;
+  int S, kc, rows;
 };
 TiledPlan tiled_plan(bool bf16, Epi epi, int M, int K, int N, const SplitK* sk) {
-  TiledPlan p{false, 1, K};
+  TiledPlan p{false, 1, K, 128};
   if (!bf16 || M <= 64 || N % tg::BN || K % tg::BK) return p;
-  const int tiles = (N / tg::BN) * ((M + tg::BM - 1) / tg::BM), nk = K / tg::BK;
-  if (tiles >= 128) {
-    p.ok = true;
-    return p;
-  }
-  if (!sk || (epi != EPI_STORE && epi != EPI_RESID && epi != EPI_RELU)) return p;
-  const int S = std::min(std::min(8, (256 + tiles - 1) / tiles), nk / 4);
+  p.rows = tiled_rows(M, N);
+  const int tiles = tiled_tiles(M, N), nk = K / tg::BK;
+  p.ok = tiles >= 128;
+  if (tiles >= 256 || !sk || (epi != EPI_STORE && epi != EPI_RESID && epi != EPI_RELU)) return p;
+  const int S = std::min(std::min(8, (512 + tiles - 1) / tiles), nk / 4);
   if (S < 2 || (size_t)S * M * N > sk->floats) return p;
   const int steps = (nk + S - 1) / S;
   p.ok = true;
@@ -2543,25 +2692,47 @@ TiledPlan tiled_plan(bool bf16, Epi epi, int M, int K, int N, const SplitK* sk) 
 hipError_t launch_gemm_swiglu_split(const uint16_t* A0, const uint16_t* A1, int M, int K, const uint16_t* W, int N,
                                     uint16_t* zhi, uint16_t* zlo, int ldz, hipStream_t st) {
   if (!gemm_tiled_fits(true, M, K, N)) return hipErrorInvalidValue;
-  const dim3 grid(N / tg::BN, (M + tg::BM - 1) / tg::BM);
-  gemm_tiled_kernel<EPI_SWIGLU_SPLIT><<<grid, 256, 0, st>>>(A0, A1, M, K, W, N, nullptr, ldz, zhi, zlo, nullptr,
-                                                            TiledSplit{nullptr, K});
+  const int rows = tiled_rows(M, N);
+  const dim3 grid(N / tg::BN, (M + rows - 1) / rows);
+  const TiledSplit t{nullptr, K};
+  if (rows == 128)
+    gemm_tiled_kernel<EPI_SWIGLU_SPLIT, 4><<<grid, 256, 0, st>>>(A0, A1, M, K, W, N, nullptr, ldz, zhi, zlo, nullptr, t);
+  else
+    gemm_tiled_kernel<EPI_SWIGLU_SPLIT, 2><<<grid, 256, 0, st>>>(A0, A1, M, K, W, N, nullptr, ldz, zhi, zlo, nullptr, t);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(bool bf16, Epi epi, const void* A0, const void* A1, int M, int K, const void* W, int N,
-                       float* C, int ldc, hipStream_t st, const float* bias, SplitK* sk) {
+                       float* C, int ldc, hipStream_t st, const float* bias, SplitK* sk, RowNorm* norm) {
+  if (norm) norm->done = false;
   if ((bias || epi == EPI_RELU) && (!bf16 || epi == EPI_SWIGLU)) return hipErrorInvalidValue;
   const TiledPlan p = tiled_plan(bf16, epi, M, K, N, sk);
   if (p.ok) {
-    const dim3 grid(N / tg::BN, (M + tg::BM - 1) / tg::BM, p.S);
+    const dim3 grid(N / tg::BN, (M + p.rows - 1) / p.rows, p.S);
     const uint16_t *hi = (const uint16_t*)A0, *lo = (const uint16_t*)A1, *w = (const uint16_t*)W;
     const TiledSplit t{p.S > 1 ? sk->P : nullptr, p.kc};
+#define QDEC_TILED(E, CC, LDC, B)                                                                          \
+  do {                                                                                                     \
+    if (p.rows == 128)                                                                                     \
+      gemm_tiled_kernel<E, 4><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, CC, LDC, nullptr, nullptr, B, t); \
+    else                                                                                                   \
+      gemm_tiled_kernel<E, 2><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, CC, LDC, nullptr, nullptr, B, t); \
+  } while (0)
     if (p.S > 1) {
       // partials first (no epilogue), then the ordered sum with the epilogue
-      gemm_tiled_kernel<EPI_STORE><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, nullptr, N, nullptr, nullptr, nullptr, t);
+      QDEC_TILED(EPI_STORE, nullptr, N, nullptr);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
+      if (epi == EPI_RESID && norm && !bias && N % 4 == 0 && N <= 4096) {
+        if (N <= 1024)
+          splitk_resid_norm_kernel<1><<<M, 256, 0, st>>>(sk->P, p.S, M, N, C, ldc, norm->gain, norm->eps, norm->hi,
+                                                         norm->lo);
+        else
+          splitk_resid_norm_kernel<4><<<M, 256, 0, st>>>(sk->P, p.S, M, N, C, ldc, norm->gain, norm->eps, norm->hi,
+                                                         norm->lo);
+        norm->done = true;
+        return hipGetLastError();
+      }
       const unsigned blocks = (unsigned)(((size_t)M * N / 4 + 255) / 256);
       if (epi == EPI_RESID)
         splitk_reduce_kernel<EPI_RESID><<<blocks, 256, 0, st>>>(sk->P, p.S, M, N, C, ldc, bias);
@@ -2572,13 +2743,14 @@ hipError_t launch_gemm(bool bf16, Epi epi, const void* A0, const void* A1, int M
       return hipGetLastError();
     }
     if (epi == EPI_STORE)
-      gemm_tiled_kernel<EPI_STORE><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc, nullptr, nullptr, bias, t);
+      QDEC_TILED(EPI_STORE, C, ldc, bias);
     else if (epi == EPI_RESID)
-      gemm_tiled_kernel<EPI_RESID><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc, nullptr, nullptr, bias, t);
+      QDEC_TILED(EPI_RESID, C, ldc, bias);
     else if (epi == EPI_RELU)
-      gemm_tiled_kernel<EPI_RELU><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc, nullptr, nullptr, bias, t);
+      QDEC_TILED(EPI_RELU, C, ldc, bias);
     else
-      gemm_tiled_kernel<EPI_SWIGLU><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, C, ldc, nullptr, nullptr, nullptr, t);
+      QDEC_TILED(EPI_SWIGLU, C, ldc, nullptr);
+#undef QDEC_TILED
     return hipGetLastError();
   }
   if (bf16) {
