@@ -1894,25 +1894,47 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint16_t* __restr
   const size_t w0 = (size_t)(n0 + srow) * K + 8 * skc;
   const size_t w1 = (size_t)(n0 + srow + 64) * K + 8 * skc;
   const int l0 = tg_sw(srow, skc), l1 = tg_sw(srow + 64, skc);
-  uint4 rh0, rh1, rl0, rl1, rw0, rw1;
-#define QDEC_TG_LOAD(k)                                         \
-  rh0 = *reinterpret_cast<const uint4*>(Ahi + a0 + (k));        \
-  rl0 = *reinterpret_cast<const uint4*>(Alo + a0 + (k));        \
-  if constexpr (MW == 4) {                                      \
-    rh1 = *reinterpret_cast<const uint4*>(Ahi + a1 + (k));      \
-    rl1 = *reinterpret_cast<const uint4*>(Alo + a1 + (k));      \
-  }                                                             \
-  rw0 = *reinterpret_cast<const uint4*>(W + w0 + (k));          \
-  rw1 = *reinterpret_cast<const uint4*>(W + w1 + (k));
-#define QDEC_TG_STORE(buf)                                      \
-  *reinterpret_cast<uint4*>(&sAh[buf][l0]) = rh0;               \
-  *reinterpret_cast<uint4*>(&sAl[buf][l0]) = rl0;               \
-  if constexpr (MW == 4) {                                      \
-    *reinterpret_cast<uint4*>(&sAh[buf][l1]) = rh1;             \
-    *reinterpret_cast<uint4*>(&sAl[buf][l1]) = rl1;             \
-  }                                                             \
-  *reinterpret_cast<uint4*>(&sW[buf][l0]) = rw0;                \
-  *reinterpret_cast<uint4*>(&sW[buf][l1]) = rw1;
+  // two register sets (X, Y) of one K step's chunks: with 64-row tiles a
+  // step's global loads are issued two steps before its LDS store, so they
+  // have two steps of MFMA work to land
+  uint4 rh0X, rh1X, rl0X, rl1X, rw0X, rw1X, rh0Y, rh1Y, rl0Y, rl1Y, rw0Y, rw1Y;
+#define QDEC_TG_LOAD(R, k)                                         \
+  {                                                                \
+    rh0##R = *reinterpret_cast<const uint4*>(Ahi + a0 + (k));      \
+    rl0##R = *reinterpret_cast<const uint4*>(Alo + a0 + (k));      \
+    if constexpr (MW == 4) {                                       \
+      rh1##R = *reinterpret_cast<const uint4*>(Ahi + a1 + (k));    \
+      rl1##R = *reinterpret_cast<const uint4*>(Alo + a1 + (k));    \
+    }                                                              \
+    rw0##R = *reinterpret_cast<const uint4*>(W + w0 + (k));        \
+    rw1##R = *reinterpret_cast<const uint4*>(W + w1 + (k));        \
+  }
+#define QDEC_TG_STORE(R, buf)                                      \
+  {                                                                \
+    *reinterpret_cast<uint4*>(&sAh[buf][l0]) = rh0##R;             \
+    *reinterpret_cast<uint4*>(&sAl[buf][l0]) = rl0##R;             \
+    if constexpr (MW == 4) {                                       \
+      *reinterpret_cast<uint4*>(&sAh[buf][l1]) = rh1##R;           \
+      *reinterpret_cast<uint4*>(&sAl[buf][l1]) = rl1##R;           \
+    }                                                              \
+    *reinterpret_cast<uint4*>(&sW[buf][l0]) = rw0##R;              \
+    *reinterpret_cast<uint4*>(&sW[buf][l1]) = rw1##R;              \
+  }
+#define QDEC_TG_MMA(buf)                                                                               \
+  {                                                                                                    \
+    bf16x8_t ah[MW], al[MW], b[4];                                                                     \
+    _Pragma("unroll") for (int i = 0; i < MW; ++i) {                                                   \
+      const int off = tg_sw(wm * 16 * MW + 16 * i + c16, gq);                                          \
+      ah[i] = *reinterpret_cast<const bf16x8_t*>(&sAh[buf][off]);                                      \
+      al[i] = *reinterpret_cast<const bf16x8_t*>(&sAl[buf][off]);                                      \
+    }                                                                                                  \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j) b[j] =                                               \
+        *reinterpret_cast<const bf16x8_t*>(&sW[buf][tg_sw(wn * 64 + 16 * j + c16, gq)]);               \
+    _Pragma("unroll") for (int i = 0; i < MW; ++i) _Pragma("unroll") for (int j = 0; j < 4; ++j) {     \
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[i], b[j], acc[i][j], 0, 0, 0);            \
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[i], b[j], acc[i][j], 0, 0, 0);            \
+    }                                                                                                  \
+  }
 
   f32x4_t acc[MW][4];
 #pragma unroll
@@ -1922,38 +1944,41 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint16_t* __restr
 
   const int S = gridDim.z, kz = blockIdx.z;
   const int kbeg = kz * (sp.kc / BK), nk = min(K / BK, kbeg + sp.kc / BK);
-  QDEC_TG_LOAD(kbeg * BK)
-  QDEC_TG_STORE(0)
-  __syncthreads();
-  for (int kt = kbeg; kt < nk; ++kt) {
-    const int buf = (kt - kbeg) & 1;
-    if (kt + 1 < nk) {
-      QDEC_TG_LOAD((kt + 1) * BK)
-    }
-    bf16x8_t ah[MW], al[MW], b[4];
-#pragma unroll
-    for (int i = 0; i < MW; ++i) {
-      const int off = tg_sw(wm * 16 * MW + 16 * i + c16, gq);
-      ah[i] = *reinterpret_cast<const bf16x8_t*>(&sAh[buf][off]);
-      al[i] = *reinterpret_cast<const bf16x8_t*>(&sAl[buf][off]);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      b[j] = *reinterpret_cast<const bf16x8_t*>(&sW[buf][tg_sw(wn * 64 + 16 * j + c16, gq)]);
-#pragma unroll
-    for (int i = 0; i < MW; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[i], b[j], acc[i][j], 0, 0, 0);
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[i], b[j], acc[i][j], 0, 0, 0);
-      }
-    if (kt + 1 < nk) {
-      QDEC_TG_STORE(buf ^ 1)
-    }
+  QDEC_TG_LOAD(X, kbeg * BK)
+  QDEC_TG_STORE(X, 0)
+  if constexpr (MW == 4) {
+    // 128-row tiles: one step ahead (a second register set would cost the
+    // third workgroup per CU)
     __syncthreads();
+    for (int kt = kbeg; kt < nk; ++kt) {
+      const int buf = (kt - kbeg) & 1;
+      if (kt + 1 < nk) QDEC_TG_LOAD(X, (kt + 1) * BK)
+      QDEC_TG_MMA(buf)
+      if (kt + 1 < nk) QDEC_TG_STORE(X, buf ^ 1)
+      __syncthreads();
+    }
+  } else {
+  // step kbeg in LDS buffer 0, step kbeg + 1 in set X (loads past the last
+  // step reread it: their stores are skipped)
+  QDEC_TG_LOAD(X, min(kbeg + 1, nk - 1) * BK)
+  __syncthreads();
+  for (int kt = kbeg; kt < nk; kt += 2) {
+    // buffer 0 holds step kt, set X step kt + 1
+    QDEC_TG_LOAD(Y, min(kt + 2, nk - 1) * BK)
+    QDEC_TG_MMA(0)
+    if (kt + 1 < nk) QDEC_TG_STORE(X, 1)
+    __syncthreads();
+    if (kt + 1 >= nk) break;
+    // buffer 1 holds step kt + 1, set Y step kt + 2
+    QDEC_TG_LOAD(X, min(kt + 3, nk - 1) * BK)
+    QDEC_TG_MMA(1)
+    if (kt + 2 < nk) QDEC_TG_STORE(Y, 0)
+    __syncthreads();
+  }
   }
 #undef QDEC_TG_LOAD
 #undef QDEC_TG_STORE
+#undef QDEC_TG_MMA
 
   if (S > 1) {
     float* pz = sp.P + (size_t)kz * M * N;
