@@ -920,15 +920,16 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const float* __restri
 // V^T columns are stored in the order the P^T operand takes its k-slots:
 // keys 4 q + e and 16 + 4 q + e (e = 0..3) at slots 8 q + e and 8 q + 4 + e,
 // so a lane's A operand of O^T = V^T P^T is one 16-byte LDS read. Block =
-// (64 tokens, head g). With rp.norm set the keys arrive as projected: the
+// (32 tokens, head g): at 1024 tokens that is 256 blocks. With rp.norm set the keys arrive as projected: the
 // block applies the K-RMSNorm and RoPE of each key (the arithmetic of
 // qk_rope_append_vec_kernel) and appends K and V of positions rp.pos0 + t to
 // the state's pages.
+constexpr int kKvTile = 32;  // tokens per kv_split block (one 32-key group)
 __global__ __launch_bounds__(256) void kv_split_kernel(const float* __restrict__ qkv, int T, int ld, int NQ,
                                                         int NKV, uint16_t* __restrict__ kh,
                                                         uint16_t* __restrict__ kl, uint16_t* __restrict__ vth,
                                                         uint16_t* __restrict__ vtl, int Tp, QkRope rp) {
-  constexpr int D = 128, TT = 64, HALF = D / 2;
+  constexpr int D = 128, TT = kKvTile, HALF = D / 2;
   __shared__ float vs[D][TT + 1];
   const int g = blockIdx.y, t0 = blockIdx.x * TT;
   const float* kbase = qkv + (size_t)(NQ + g) * D;
@@ -2509,7 +2510,7 @@ hipError_t launch_attn_prefill(const Dims& d, const float* qkv, int T, float* ou
     QkRope rp{};
     if (rope) rp = *rope;
     const int Tp = kv_split_pad(T);
-    kv_split_kernel<<<dim3(Tp / 64, d.NKV), 256, 0, st>>>(qkv, T, d.qkv(), d.NQ, d.NKV, kv[0], kv[1], kv[2], kv[3],
+    kv_split_kernel<<<dim3(Tp / kKvTile, d.NKV), 256, 0, st>>>(qkv, T, d.qkv(), d.NQ, d.NKV, kv[0], kv[1], kv[2], kv[3],
                                                           Tp, rp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
