@@ -518,7 +518,7 @@ int ensure_batch(qdec_model* m, int nsplit) {
         (e = dev_alloc(&m->bAttn, (size_t)B * d.NQ * d.D, "batch attention")) ||
         (e = dev_alloc(&m->bZ, (size_t)B * d.F, "batch FFN")) ||
         (e = dev_alloc(&m->bLogits, (size_t)B * d.V, "batch logits")) ||
-        (e = dev_alloc(&m->bKeys, (size_t)B, "batch keys")) || (e = dev_alloc(&m->bTok, (size_t)B, "batch tokens")) ||
+        (e = dev_alloc(&m->bKeys, (size_t)B * kKeySlots, "batch keys")) || (e = dev_alloc(&m->bTok, (size_t)B, "batch tokens")) ||
         (e = dev_alloc(&m->bAttnCnt, (size_t)B * d.NKV, "batch attention counters"))) {
       free_batch(m);
       return e;
@@ -953,7 +953,7 @@ int qdec_create(const qdec_config* cfg, const qdec_weights* w, void* hip_stream,
     return fail(QDEC_E_OOM, "cannot allocate packed weights");
   }
   if ((e = dev_alloc(&m->nbuf, norms_per_layer * d.L, "norm gains")) ||
-      (e = dev_alloc(&m->final_norm, d.H, "final norm")) || (e = dev_alloc(&m->keys, kMaxBatch, "argmax keys")) ||
+      (e = dev_alloc(&m->final_norm, d.H, "final norm")) || (e = dev_alloc(&m->keys, (size_t)kMaxBatch * kKeySlots, "argmax keys")) ||
       (e = dev_alloc(&m->argmax_tmp, kMaxBatch, "argmax scratch"))) {
     free_model(m);
     return e;

@@ -99,6 +99,11 @@ int rows_counters(int M, int K, int N);
 hipError_t launch_gemm_rows(Epi epi, bool norm, const RowsGemm& g, hipStream_t st);
 hipError_t launch_lm_head(const Dims& d, bool bf16, const void* E, const float* x, const float* gain,
                           float* logits, unsigned long long* key, hipStream_t st);
+// Argmax keys of a row are spread over kKeySlots words (key[row * kKeySlots
+// + slot], the slot picked by the producing block) so that thousands of
+// blocks do not all take their atomic max on one word; argmax_final reduces
+// the slots.
+constexpr int kKeySlots = 16;
 hipError_t launch_argmax_final(const unsigned long long* key, int n, int32_t* out, hipStream_t st);
 hipError_t launch_reset_keys(unsigned long long* key, int n, hipStream_t st);
 // key[r] = max(key[r], argmax key of logits row r), r < n

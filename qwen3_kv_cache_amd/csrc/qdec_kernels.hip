@@ -226,13 +226,17 @@ __global__ __launch_bounds__(256) void lm_head_kernel(const WT* __restrict__ E, 
   if (threadIdx.x == 0) {
     unsigned long long b = bkey[0];
     for (int i = 1; i < 4; ++i) b = bkey[i] > b ? bkey[i] : b;
-    atomicMax(key, b);
+    atomicMax(key + blockIdx.x % kKeySlots, b);
   }
 }
 
 __global__ void argmax_final_kernel(const unsigned long long* key, int n, int32_t* out) {
   const int i = threadIdx.x;
-  if (i < n) out[i] = (int32_t)(0xFFFFFFFFu - (uint32_t)(key[i] & 0xFFFFFFFFull));
+  if (i < n) {
+    unsigned long long b = key[i * kKeySlots];
+    for (int s = 1; s < kKeySlots; ++s) b = key[i * kKeySlots + s] > b ? key[i * kKeySlots + s] : b;
+    out[i] = (int32_t)(0xFFFFFFFFu - (uint32_t)(b & 0xFFFFFFFFull));
+  }
 }
 
 // key[r] = max over v of argmax_key(logits[r][v], v); grid (chunks, rows).
@@ -255,13 +259,12 @@ __global__ __launch_bounds__(256) void argmax_rows_kernel(const float* __restric
   __syncthreads();
   if (threadIdx.x == 0) {
     for (int w = 1; w < (int)(blockDim.x / kWave); ++w) best = wbest[w] > best ? wbest[w] : best;
-    atomicMax(key + r, best);
+    atomicMax(key + r * kKeySlots + blockIdx.x % kKeySlots, best);
   }
 }
 
 __global__ void reset_keys_kernel(unsigned long long* key, int n) {
-  const int i = threadIdx.x;
-  if (i < n) key[i] = 0ull;
+  for (int i = threadIdx.x; i < n * kKeySlots; i += blockDim.x) key[i] = 0ull;
 }
 
 // ------------------------------------------ per-head Q/K RMSNorm + RoPE + KV append
@@ -1818,7 +1821,7 @@ __global__ __launch_bounds__(256) void gemm_rows_kernel(RowsGemm g) {
       const unsigned long long kk = argmax_key(tv[threadIdx.x][ct], n0 + ct);
       best = kk > best ? kk : best;
     }
-    atomicMax(g.keys + m0 + threadIdx.x, best);
+    atomicMax(g.keys + (size_t)(m0 + threadIdx.x) * kKeySlots + tile % kKeySlots, best);
   }
 }
 
