@@ -28,6 +28,10 @@ MID = {
     # blocks per wave (one query head per KV head, T >= 1024), ragged last block
     "d128_g1_T1100": (synth.custom_shape(hidden=256, n_layer=1, n_q_head=2, n_kv_head=2, head_dim=128, ffn=512,
                                          vocab=1000, bf16=True), 1100, 8, 100, 4),
+    # MHA, D=128, a 200-token prompt: one 16-query block per wave with the
+    # Q/K norm and RoPE applied inside the matrix-core attention launch
+    "d128_g1_T200": (synth.custom_shape(hidden=256, n_layer=2, n_q_head=2, n_kv_head=2, head_dim=128, ffn=512,
+                                        vocab=1000, bf16=True), 200, 8, 100, 4),
     # a prompt made only of audio rows (span [0, T)): no id is read
     "d64_g2_allaudio": (synth.custom_shape(hidden=256, n_layer=2, n_q_head=4, n_kv_head=2, head_dim=64, ffn=768,
                                            vocab=5003, bf16=True), 40, 0, 40, 6),
