@@ -1013,8 +1013,13 @@ namespace fa {
 constexpr int D = 128;
 constexpr int QT = 64;          // query positions per block
 constexpr int KT = 32;          // keys per tile
-constexpr int KP = D + 8;       // bf16 pitch of a K row in LDS
-constexpr int VP = KT + 8;      // bf16 pitch of a V^T row in LDS
+// LDS layouts without bank conflicts on gfx950 (SQ_LDS_BANK_CONFLICT, 16
+// bytes per lane from 16 rows): K rows padded to 144 bf16 (288 bytes; 272
+// conflicts), V^T rows of 32 bf16 unpadded with chunk c of row r at
+// c ^ ((r / 2) % 4) (80-byte padded rows conflict)
+constexpr int KP = D + 16;      // bf16 pitch of a K row in LDS
+constexpr int VP = KT;          // bf16 pitch of a V^T row in LDS (chunks swizzled)
+__device__ __forceinline__ int vt_sw(int d, int chunk) { return d * VP + 8 * (chunk ^ ((d >> 1) & 3)); }
 constexpr int KB = KT / 16;     // 16-key blocks per tile
 constexpr int KH = KT / 32;     // 32-key groups per tile
 }  // namespace fa
@@ -1161,10 +1166,10 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
     *reinterpret_cast<uint4*>(&Kh[b][kc1 * KP + kd]) = rkh1;       \
     *reinterpret_cast<uint4*>(&Kl[b][kc0 * KP + kd]) = rkl0;       \
     *reinterpret_cast<uint4*>(&Kl[b][kc1 * KP + kd]) = rkl1;       \
-    *reinterpret_cast<uint4*>(&Vh[b][vd0 * VP + vk]) = rvh0;       \
-    *reinterpret_cast<uint4*>(&Vh[b][vd1 * VP + vk]) = rvh1;       \
-    *reinterpret_cast<uint4*>(&Vl[b][vd0 * VP + vk]) = rvl0;       \
-    *reinterpret_cast<uint4*>(&Vl[b][vd1 * VP + vk]) = rvl1;       \
+    *reinterpret_cast<uint4*>(&Vh[b][vt_sw(vd0, vk / 8)]) = rvh0;  \
+    *reinterpret_cast<uint4*>(&Vh[b][vt_sw(vd1, vk / 8)]) = rvh1;  \
+    *reinterpret_cast<uint4*>(&Vl[b][vt_sw(vd0, vk / 8)]) = rvl0;  \
+    *reinterpret_cast<uint4*>(&Vl[b][vt_sw(vd1, vk / 8)]) = rvl1;  \
   }
   const int kbeg = blockIdx.z * per * KT, kend = kt_end * KT;
   if (kbeg < kend) {
@@ -1266,7 +1271,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
 #pragma unroll
       for (int c = 0; c < KH; ++c) {
         // keys 4 gq + e and 16 + 4 gq + e of the group sit together at 8 gq
-        const int off = (16 * b + c16) * VP + 32 * c + 8 * gq;
+        const int off = vt_sw(16 * b + c16, 4 * c + gq);
         const bf16x8_t vh = *reinterpret_cast<const bf16x8_t*>(&Vh[buf][off]);
         const bf16x8_t vl = *reinterpret_cast<const bf16x8_t*>(&Vl[buf][off]);
 #pragma unroll
@@ -1837,11 +1842,14 @@ namespace tg {
 constexpr int BN = 128, BK = 32;
 constexpr size_t kTiledWSliceBytes = size_t(3) << 20;  // W bytes per XCD column group
 constexpr int P = BK;  // bf16 pitch of an LDS row (chunks XOR-swizzled)
-// 16-byte chunk c of LDS row r sits at chunk c ^ ((r / 4) % 4): the 16 rows
-// an MFMA operand read touches (one chunk each) then fall in distinct banks
+// 16-byte chunk c of LDS row r sits at chunk c ^ ((r / 2) % 4): an MFMA
+// operand read (16 rows, one chunk each) is then free of bank conflicts
 // without padding, which keeps the double-buffered tiles at 48 KB (three
-// workgroups per CU)
-__device__ __forceinline__ int tg_sw(int r, int c) { return r * P + 8 * (c ^ ((r >> 2) & 3)); }
+// workgroups per CU). Measured with the SQ_LDS_BANK_CONFLICT counter on
+// gfx950: a 16-byte-per-lane read of 64-byte rows conflicts (about 4 extra
+// cycles per read) unpadded, padded to 80 bytes, or swizzled by (r / 4) % 4,
+// and is conflict-free swizzled by (r / 2) % 4.
+__device__ __forceinline__ int tg_sw(int r, int c) { return r * P + 8 * (c ^ ((r >> 1) & 3)); }
 }  // namespace tg
 
 // Split-K of the tiled GEMM (grid z = split): split z covers K steps
