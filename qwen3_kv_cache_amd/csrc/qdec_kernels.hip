@@ -2610,17 +2610,21 @@ struct RowsPlan {
 };
 
 // 64 output columns per workgroup for the LM head (N >= 65536: 2374 instead
-// of 4748 workgroups over the vocabulary; batched decode +1.3%), 32 for other
-// wide outputs (each A load then feeds two column tiles), 16 otherwise; K is split into chunks (multiples of 128,
+// of 4748 workgroups over the vocabulary; batched decode +1.3%) and for wide
+// outputs of at least 33 rows (whose row tiles already give enough
+// workgroups: 48-token prefill 1.745 -> 1.72 ms; with 16 rows the same
+// width costs 9% of batched decode), 32 for other wide outputs (each A load
+// then feeds several column tiles), 16 otherwise; K is split into chunks (multiples of 128,
 // one k-step of 32 per wave at least) only until the launch has 128
 // workgroups, counting every 16-row tile: the split-K exchange costs more
 // than the extra weight parallelism gains beyond that (measured on batched
 // decode and 48-token prompts, where 48 rows already give three tiles)
 RowsPlan rows_plan(int K, int N, int M) {
   RowsPlan p;
-  p.nt = N % 64 == 0 && N >= 65536 ? 4 : (N % 32 == 0 && N >= 2048 ? 2 : 1);
-  p.tiles = N / (16 * p.nt);
   const int rt = (M + 15) / 16;
+  const bool wide = N >= 65536 || (N >= 2048 && rt >= 3);
+  p.nt = N % 64 == 0 && wide ? 4 : (N % 32 == 0 && N >= 2048 ? 2 : 1);
+  p.tiles = N / (16 * p.nt);
   const int want = std::max(1, (128 + p.tiles * rt - 1) / (p.tiles * rt));
   p.kc = std::max(128, ((K + want - 1) / want + 127) / 128 * 128);
   p.nkc = (K + p.kc - 1) / p.kc;
