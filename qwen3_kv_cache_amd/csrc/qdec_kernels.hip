@@ -1344,32 +1344,46 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
 // Merge of S key-range partials of the prefill attention: for query q and
 // head h, with bases m_z and sums l_z, o = sum_z 2^(m_z - M) o_z /
 // sum_z 2^(m_z - M) l_z, M = max_z m_z, in split order; written as fp32
-// (out) or as the O projection's bf16 hi / lo operand. One workgroup of D
-// threads per (query, head); a split that saw no key has m = -inf, l = 0.
-__global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict__ part, int S, int T, int nq,
+// (out) or as the O projection's bf16 hi / lo operand. A split that saw no
+// key has m = -inf, l = 0.
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ part, int S, int T, int nq,
                                                          float* __restrict__ out, uint16_t* __restrict__ ohi,
                                                          uint16_t* __restrict__ olo) {
+  // 8 (query, head) records per block, 32 threads per record, 4 dimensions
+  // per thread
   constexpr int D = fa::D;
-  const int q = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+  const int rec = blockIdx.x * 8 + threadIdx.x / 32, d = 4 * (threadIdx.x % 32);
+  if (rec >= T * nq) return;
+  const size_t zs = (size_t)T * nq * (D + 4);  // one split's records
+  const float* p0 = part + (size_t)rec * (D + 4);
   float mx = -INFINITY;
-  for (int z = 0; z < S; ++z) mx = fmaxf(mx, part[(((size_t)z * T + q) * nq + h) * (D + 4) + D]);
-  float o = 0.f, l = 0.f;
+  for (int z = 0; z < S; ++z) mx = fmaxf(mx, p0[z * zs + D]);
+  float o[4] = {0.f, 0.f, 0.f, 0.f}, l = 0.f;
   for (int z = 0; z < S; ++z) {
-    const float* pp = part + (((size_t)z * T + q) * nq + h) * (D + 4);
+    const float* pp = p0 + z * zs;
     const float mz = pp[D];
     const float wz = mz == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mz - mx);
-    o = fmaf(wz, pp[d], o);
+    const float4 v = *reinterpret_cast<const float4*>(pp + d);
+    o[0] = fmaf(wz, v.x, o[0]);
+    o[1] = fmaf(wz, v.y, o[1]);
+    o[2] = fmaf(wz, v.z, o[2]);
+    o[3] = fmaf(wz, v.w, o[3]);
     l = fmaf(wz, pp[D + 1], l);
   }
-  const float v = o / l;
-  const size_t idx = (size_t)q * nq * D + (size_t)h * D + d;
+  const size_t idx = (size_t)rec * D + d;
+  const float v[4] = {o[0] / l, o[1] / l, o[2] / l, o[3] / l};
   if (ohi) {
 #pragma clang fp contract(off)
-    const uint16_t hb = f32_to_bf16_rne(v);
-    ohi[idx] = hb;
-    olo[idx] = f32_to_bf16_rne(v - bf16_to_f32(hb));
+    uint16_t h[4], lo[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      h[e] = f32_to_bf16_rne(v[e]);
+      lo[e] = f32_to_bf16_rne(v[e] - bf16_to_f32(h[e]));
+    }
+    *reinterpret_cast<uint2*>(ohi + idx) = make_uint2(h[0] | ((unsigned)h[1] << 16), h[2] | ((unsigned)h[3] << 16));
+    *reinterpret_cast<uint2*>(olo + idx) = make_uint2(lo[0] | ((unsigned)lo[1] << 16), lo[2] | ((unsigned)lo[3] << 16));
   } else {
-    out[idx] = v;
+    *reinterpret_cast<float4*>(out + idx) = make_float4(v[0], v[1], v[2], v[3]);
   }
 }
 
@@ -2559,7 +2573,7 @@ hipError_t launch_attn_prefill(const Dims& d, const float* qkv, int T, float* ou
     if (S > 1) {
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      attn_merge_kernel<<<dim3(T, d.NQ), fa::D, 0, st>>>(part, S, T, d.NQ, out, out_hi, out_lo);
+      attn_merge_kernel<<<(T * d.NQ + 7) / 8, 256, 0, st>>>(part, S, T, d.NQ, out, out_hi, out_lo);
     }
     return hipGetLastError();
   }
