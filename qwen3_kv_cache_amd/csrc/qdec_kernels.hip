@@ -1879,7 +1879,7 @@ struct TiledSplit {
   int kc;    // K per split (a multiple of BK)
 };
 
-template <int EPI, int MW>
+template <int EPI, int MW, int SUBT>
 __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint16_t* __restrict__ Ahi,
                                                           const uint16_t* __restrict__ Alo, int M, int K,
                                                           const uint16_t* __restrict__ W, int N,
@@ -1892,7 +1892,11 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint16_t* __restr
   // 64-row tiles (MW = 2, twice the workgroups for the same shape)
   static_assert(MW == 4 || MW == 2, "128- or 64-row tiles");
   constexpr int TM = 32 * MW;
-  __shared__ uint16_t sAh[2][TM * P], sAl[2][TM * P], sW[2][BN * P];
+  // SUB K sub-steps of 32 per LDS buffer and barrier (64-row tiles: 2 where
+  // the K range allows, halving the barriers per MFMA)
+  constexpr int SUB = MW == 2 ? SUBT : 1;
+  constexpr int KS = BK * SUB;  // K per step
+  __shared__ uint16_t sAh[2][SUB][TM * P], sAl[2][SUB][TM * P], sW[2][SUB][BN * P];
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   const int c16 = lane % 16, gq = lane / 16;
   const int wm = w / 2, wn = w % 2;
@@ -1927,42 +1931,57 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint16_t* __restr
   // two register sets (X, Y) of one K step's chunks: with 64-row tiles a
   // step's global loads are issued two steps before its LDS store, so they
   // have two steps of MFMA work to land
-  uint4 rh0X, rh1X, rl0X, rl1X, rw0X, rw1X, rh0Y, rh1Y, rl0Y, rl1Y, rw0Y, rw1Y;
-#define QDEC_TG_LOAD(R, k)                                         \
-  {                                                                \
-    rh0##R = *reinterpret_cast<const uint4*>(Ahi + a0 + (k));      \
-    rl0##R = *reinterpret_cast<const uint4*>(Alo + a0 + (k));      \
-    if constexpr (MW == 4) {                                       \
-      rh1##R = *reinterpret_cast<const uint4*>(Ahi + a1 + (k));    \
-      rl1##R = *reinterpret_cast<const uint4*>(Alo + a1 + (k));    \
-    }                                                              \
-    rw0##R = *reinterpret_cast<const uint4*>(W + w0 + (k));        \
-    rw1##R = *reinterpret_cast<const uint4*>(W + w1 + (k));        \
+  // (named registers per sub-step, not arrays: arrays indexed in a macro's
+  // loop went to scratch)
+  uint4 rh0X0, rh1X0, rl0X0, rl1X0, rw0X0, rw1X0, rh0Y0, rh1Y0, rl0Y0, rl1Y0, rw0Y0, rw1Y0;
+  uint4 rh0X1, rh1X1, rl0X1, rl1X1, rw0X1, rw1X1, rh0Y1, rh1Y1, rl0Y1, rl1Y1, rw0Y1, rw1Y1;
+#define QDEC_TG_LD(R, S_, k)                                                  \
+  {                                                                           \
+    rh0##R##S_ = *reinterpret_cast<const uint4*>(Ahi + a0 + (k) + BK * S_);   \
+    rl0##R##S_ = *reinterpret_cast<const uint4*>(Alo + a0 + (k) + BK * S_);   \
+    if constexpr (MW == 4) {                                                  \
+      rh1##R##S_ = *reinterpret_cast<const uint4*>(Ahi + a1 + (k) + BK * S_); \
+      rl1##R##S_ = *reinterpret_cast<const uint4*>(Alo + a1 + (k) + BK * S_); \
+    }                                                                         \
+    rw0##R##S_ = *reinterpret_cast<const uint4*>(W + w0 + (k) + BK * S_);     \
+    rw1##R##S_ = *reinterpret_cast<const uint4*>(W + w1 + (k) + BK * S_);     \
   }
-#define QDEC_TG_STORE(R, buf)                                      \
-  {                                                                \
-    *reinterpret_cast<uint4*>(&sAh[buf][l0]) = rh0##R;             \
-    *reinterpret_cast<uint4*>(&sAl[buf][l0]) = rl0##R;             \
-    if constexpr (MW == 4) {                                       \
-      *reinterpret_cast<uint4*>(&sAh[buf][l1]) = rh1##R;           \
-      *reinterpret_cast<uint4*>(&sAl[buf][l1]) = rl1##R;           \
-    }                                                              \
-    *reinterpret_cast<uint4*>(&sW[buf][l0]) = rw0##R;              \
-    *reinterpret_cast<uint4*>(&sW[buf][l1]) = rw1##R;              \
+#define QDEC_TG_ST(R, S_, buf)                                                \
+  {                                                                           \
+    *reinterpret_cast<uint4*>(&sAh[buf][S_][l0]) = rh0##R##S_;                \
+    *reinterpret_cast<uint4*>(&sAl[buf][S_][l0]) = rl0##R##S_;                \
+    if constexpr (MW == 4) {                                                  \
+      *reinterpret_cast<uint4*>(&sAh[buf][S_][l1]) = rh1##R##S_;              \
+      *reinterpret_cast<uint4*>(&sAl[buf][S_][l1]) = rl1##R##S_;              \
+    }                                                                         \
+    *reinterpret_cast<uint4*>(&sW[buf][S_][l0]) = rw0##R##S_;                 \
+    *reinterpret_cast<uint4*>(&sW[buf][S_][l1]) = rw1##R##S_;                 \
+  }
+#define QDEC_TG_LOAD(R, k)               \
+  {                                      \
+    QDEC_TG_LD(R, 0, k)                  \
+    if constexpr (SUB == 2) QDEC_TG_LD(R, 1, k) \
+  }
+#define QDEC_TG_STORE(R, buf)            \
+  {                                      \
+    QDEC_TG_ST(R, 0, buf)                \
+    if constexpr (SUB == 2) QDEC_TG_ST(R, 1, buf) \
   }
 #define QDEC_TG_MMA(buf)                                                                               \
   {                                                                                                    \
-    bf16x8_t ah[MW], al[MW], b[4];                                                                     \
-    _Pragma("unroll") for (int i = 0; i < MW; ++i) {                                                   \
-      const int off = tg_sw(wm * 16 * MW + 16 * i + c16, gq);                                          \
-      ah[i] = *reinterpret_cast<const bf16x8_t*>(&sAh[buf][off]);                                      \
-      al[i] = *reinterpret_cast<const bf16x8_t*>(&sAl[buf][off]);                                      \
-    }                                                                                                  \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j) b[j] =                                               \
-        *reinterpret_cast<const bf16x8_t*>(&sW[buf][tg_sw(wn * 64 + 16 * j + c16, gq)]);               \
-    _Pragma("unroll") for (int i = 0; i < MW; ++i) _Pragma("unroll") for (int j = 0; j < 4; ++j) {     \
-      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[i], b[j], acc[i][j], 0, 0, 0);            \
-      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[i], b[j], acc[i][j], 0, 0, 0);            \
+    _Pragma("unroll") for (int s_ = 0; s_ < SUB; ++s_) {                                               \
+      bf16x8_t ah[MW], al[MW], b[4];                                                                   \
+      _Pragma("unroll") for (int i = 0; i < MW; ++i) {                                                 \
+        const int off = tg_sw(wm * 16 * MW + 16 * i + c16, gq);                                        \
+        ah[i] = *reinterpret_cast<const bf16x8_t*>(&sAh[buf][s_][off]);                                \
+        al[i] = *reinterpret_cast<const bf16x8_t*>(&sAl[buf][s_][off]);                                \
+      }                                                                                                \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j) b[j] =                                             \
+          *reinterpret_cast<const bf16x8_t*>(&sW[buf][s_][tg_sw(wn * 64 + 16 * j + c16, gq)]);         \
+      _Pragma("unroll") for (int i = 0; i < MW; ++i) _Pragma("unroll") for (int j = 0; j < 4; ++j) {   \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[i], b[j], acc[i][j], 0, 0, 0);          \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[i], b[j], acc[i][j], 0, 0, 0);          \
+      }                                                                                                \
     }                                                                                                  \
   }
 
@@ -1973,8 +1992,8 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint16_t* __restr
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int S = gridDim.z, kz = blockIdx.z;
-  const int kbeg = kz * (sp.kc / BK), nk = min(K / BK, kbeg + sp.kc / BK);
-  QDEC_TG_LOAD(X, kbeg * BK)
+  const int kbeg = kz * (sp.kc / KS), nk = min(K / KS, kbeg + sp.kc / KS);
+  QDEC_TG_LOAD(X, kbeg * KS)
   QDEC_TG_STORE(X, 0)
   if constexpr (MW == 4) {
     // 128-row tiles: one step ahead (a second register set would cost the
@@ -1982,7 +2001,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint16_t* __restr
     __syncthreads();
     for (int kt = kbeg; kt < nk; ++kt) {
       const int buf = (kt - kbeg) & 1;
-      if (kt + 1 < nk) QDEC_TG_LOAD(X, (kt + 1) * BK)
+      if (kt + 1 < nk) QDEC_TG_LOAD(X, (kt + 1) * KS)
       QDEC_TG_MMA(buf)
       if (kt + 1 < nk) QDEC_TG_STORE(X, buf ^ 1)
       __syncthreads();
@@ -1990,22 +2009,24 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint16_t* __restr
   } else {
   // step kbeg in LDS buffer 0, step kbeg + 1 in set X (loads past the last
   // step reread it: their stores are skipped)
-  QDEC_TG_LOAD(X, min(kbeg + 1, nk - 1) * BK)
+  QDEC_TG_LOAD(X, min(kbeg + 1, nk - 1) * KS)
   __syncthreads();
   for (int kt = kbeg; kt < nk; kt += 2) {
     // buffer 0 holds step kt, set X step kt + 1
-    QDEC_TG_LOAD(Y, min(kt + 2, nk - 1) * BK)
+    QDEC_TG_LOAD(Y, min(kt + 2, nk - 1) * KS)
     QDEC_TG_MMA(0)
     if (kt + 1 < nk) QDEC_TG_STORE(X, 1)
     __syncthreads();
     if (kt + 1 >= nk) break;
     // buffer 1 holds step kt + 1, set Y step kt + 2
-    QDEC_TG_LOAD(X, min(kt + 3, nk - 1) * BK)
+    QDEC_TG_LOAD(X, min(kt + 3, nk - 1) * KS)
     QDEC_TG_MMA(1)
     if (kt + 2 < nk) QDEC_TG_STORE(Y, 0)
     __syncthreads();
   }
   }
+#undef QDEC_TG_LD
+#undef QDEC_TG_ST
 #undef QDEC_TG_LOAD
 #undef QDEC_TG_STORE
 #undef QDEC_TG_MMA
@@ -2731,20 +2752,25 @@ namespace {
 // RELU); without a split the kernel is taken from 128 tiles on.
 struct TiledPlan {
   bool ok;
-  int S, kc, rows;
+  int S, kc, rows, sub;
 };
+// K sub-steps of 32 per barrier: 2 for 64-row tiles when K (and so every
+// split's range) is a multiple of 64
+int tiled_sub(int rows, int K) { return rows == 64 && K % (2 * tg::BK) == 0 ? 2 : 1; }
 TiledPlan tiled_plan(bool bf16, Epi epi, int M, int K, int N, const SplitK* sk) {
-  TiledPlan p{false, 1, K, 128};
+  TiledPlan p{false, 1, K, 128, 1};
   if (!bf16 || M <= 64 || N % tg::BN || K % tg::BK) return p;
   p.rows = tiled_rows(M, N);
-  const int tiles = tiled_tiles(M, N), nk = K / tg::BK;
+  p.sub = tiled_sub(p.rows, K);
+  const int ks = tg::BK * p.sub;  // K per step
+  const int tiles = tiled_tiles(M, N), nk = K / ks;
   p.ok = tiles >= 128;
   if (tiles >= 256 || !sk || (epi != EPI_STORE && epi != EPI_RESID && epi != EPI_RELU)) return p;
-  const int S = std::min(std::min(8, (512 + tiles - 1) / tiles), nk / 4);
+  const int S = std::min(std::min(8, (512 + tiles - 1) / tiles), nk * p.sub / 4);
   if (S < 2 || (size_t)S * M * N > sk->floats) return p;
   const int steps = (nk + S - 1) / S;
   p.ok = true;
-  p.kc = steps * tg::BK;
+  p.kc = steps * ks;
   p.S = (nk + steps - 1) / steps;
   return p;
 }
@@ -2758,9 +2784,11 @@ hipError_t launch_gemm_swiglu_split(const uint16_t* A0, const uint16_t* A1, int 
   const dim3 grid(N / tg::BN, (M + rows - 1) / rows);
   const TiledSplit t{nullptr, K};
   if (rows == 128)
-    gemm_tiled_kernel<EPI_SWIGLU_SPLIT, 4><<<grid, 256, 0, st>>>(A0, A1, M, K, W, N, nullptr, ldz, zhi, zlo, nullptr, t);
+    gemm_tiled_kernel<EPI_SWIGLU_SPLIT, 4, 1><<<grid, 256, 0, st>>>(A0, A1, M, K, W, N, nullptr, ldz, zhi, zlo, nullptr, t);
+  else if (tiled_sub(rows, K) == 2)
+    gemm_tiled_kernel<EPI_SWIGLU_SPLIT, 2, 2><<<grid, 256, 0, st>>>(A0, A1, M, K, W, N, nullptr, ldz, zhi, zlo, nullptr, t);
   else
-    gemm_tiled_kernel<EPI_SWIGLU_SPLIT, 2><<<grid, 256, 0, st>>>(A0, A1, M, K, W, N, nullptr, ldz, zhi, zlo, nullptr, t);
+    gemm_tiled_kernel<EPI_SWIGLU_SPLIT, 2, 1><<<grid, 256, 0, st>>>(A0, A1, M, K, W, N, nullptr, ldz, zhi, zlo, nullptr, t);
   return hipGetLastError();
 }
 
@@ -2776,9 +2804,11 @@ hipError_t launch_gemm(bool bf16, Epi epi, const void* A0, const void* A1, int M
 #define QDEC_TILED(E, CC, LDC, B)                                                                          \
   do {                                                                                                     \
     if (p.rows == 128)                                                                                     \
-      gemm_tiled_kernel<E, 4><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, CC, LDC, nullptr, nullptr, B, t); \
+      gemm_tiled_kernel<E, 4, 1><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, CC, LDC, nullptr, nullptr, B, t); \
+    else if (p.sub == 2)                                                                                   \
+      gemm_tiled_kernel<E, 2, 2><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, CC, LDC, nullptr, nullptr, B, t); \
     else                                                                                                   \
-      gemm_tiled_kernel<E, 2><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, CC, LDC, nullptr, nullptr, B, t); \
+      gemm_tiled_kernel<E, 2, 1><<<grid, 256, 0, st>>>(hi, lo, M, K, w, N, CC, LDC, nullptr, nullptr, B, t); \
   } while (0)
     if (p.S > 1) {
       // partials first (no epilogue), then the ordered sum with the epilogue
