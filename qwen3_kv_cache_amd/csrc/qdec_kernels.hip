@@ -1525,19 +1525,21 @@ __global__ __launch_bounds__(256) void gemm_bf16x2_kernel(const uint16_t* __rest
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const uint4 zero = make_uint4(0, 0, 0, 0);
+  // rows and columns past the edge repeat the last one: an MFMA output
+  // element depends only on its own A row and W row, and those are never
+  // stored (a select against zero here put the operands in scratch)
   for (int k = 0; k < K; k += 32) {
     uint4 ah[2], al[2], b[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int row = m0 + i * 16 + r;
-      ah[i] = row < M ? *reinterpret_cast<const uint4*>(Ahi + (size_t)row * K + k + kq) : zero;
-      al[i] = row < M ? *reinterpret_cast<const uint4*>(Alo + (size_t)row * K + k + kq) : zero;
+      const int row = min(m0 + i * 16 + r, M - 1);
+      ah[i] = *reinterpret_cast<const uint4*>(Ahi + (size_t)row * K + k + kq);
+      al[i] = *reinterpret_cast<const uint4*>(Alo + (size_t)row * K + k + kq);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int col = n0 + j * 16 + r;
-      b[j] = col < N ? *reinterpret_cast<const uint4*>(W + (size_t)col * K + k + kq) : zero;
+      const int col = min(n0 + j * 16 + r, N - 1);
+      b[j] = *reinterpret_cast<const uint4*>(W + (size_t)col * K + k + kq);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
