@@ -32,6 +32,10 @@ MID = {
     # Q/K norm and RoPE applied inside the matrix-core attention launch
     "d128_g1_T200": (synth.custom_shape(hidden=256, n_layer=2, n_q_head=2, n_kv_head=2, head_dim=128, ffn=512,
                                         vocab=1000, bf16=True), 200, 8, 100, 4),
+    # ffn 320: the down projection's K is five 64-wide steps, so its K
+    # splits are uneven (3 + 2 steps) on the 64-row, two-sub-step GEMM tiles
+    "d64_g2_ffn320_T150": (synth.custom_shape(hidden=256, n_layer=2, n_q_head=4, n_kv_head=2, head_dim=64, ffn=320,
+                                              vocab=1000, bf16=True), 150, 10, 60, 4),
     # a prompt made only of audio rows (span [0, T)): no id is read
     "d64_g2_allaudio": (synth.custom_shape(hidden=256, n_layer=2, n_q_head=4, n_kv_head=2, head_dim=64, ffn=768,
                                            vocab=5003, bf16=True), 40, 0, 40, 6),
