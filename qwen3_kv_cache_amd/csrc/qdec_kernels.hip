@@ -1035,7 +1035,7 @@ constexpr float kFaFloor = -1e30f;
 // x QS "virtual heads" v: head g GROUP + v % GROUP, queries 16 (w QS + v / GROUP)
 // + [0, 16) of the block). With one query head per KV head, two query blocks
 // per wave let every K/V fragment read from LDS feed twice the MFMAs.
-template <int GROUP, int QS>
+template <int GROUP, int QS, int ONEQ>
 __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* __restrict__ qkv, int T, int ld,
                                                                  const uint16_t* __restrict__ khs,
                                                                  const uint16_t* __restrict__ kls,
@@ -1046,7 +1046,11 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
                                                                  uint16_t* __restrict__ olo, int causal,
                                                                  float* __restrict__ part, QkRope rp) {
   using namespace fa;
-  constexpr int VH = GROUP * QS, QTB = 64 * QS;  // virtual heads per wave, queries per block
+  // ONEQ: the block takes one query head of the KV head's group (blockIdx.y
+  // over the query heads): twice the blocks for a short prompt, each with
+  // half the work per K/V tile
+  constexpr int GH = ONEQ ? 1 : GROUP;              // query heads per block
+  constexpr int VH = GH * QS, QTB = 64 * QS;  // virtual heads per wave, queries per block
   // two tile buffers: the next tile's global loads are in flight while the
   // current one is multiplied, one barrier per tile
   __shared__ __bf16 Kh[2][KT * KP], Kl[2][KT * KP];
@@ -1059,17 +1063,21 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
   // holding tiles of every head (at T = 8192 the prefill went from 54.3 to
   // 44.8 ms; at T = 1024, where all heads' K/V nearly fit, it measured 1%
   // slower, hence the 32-tile threshold).
-  int g = blockIdx.y, qb = blockIdx.x;
+  int hy = blockIdx.y, qb = blockIdx.x;
   if (gridDim.y % 8 == 0 && gridDim.x >= 32) {
-    const int lin = blockIdx.x + blockIdx.y * gridDim.x, j = lin / 8;
-    g = lin % 8 + 8 * (j / gridDim.x);
+    // (with ONEQ the query heads of KV head x stay on XCD x)
+    const int lin = blockIdx.x + blockIdx.y * gridDim.x, j = lin / 8, x = lin % 8, t = j / gridDim.x;
+    hy = ONEQ ? GROUP * (x + 8 * (t / GROUP)) + t % GROUP : x + 8 * t;
     qb = j % gridDim.x;
   }
+  const int g = ONEQ ? hy / GROUP : hy;  // KV head
+  // query head of virtual head v
+  auto qhead = [&](int v) __attribute__((always_inline)) { return ONEQ ? hy : g * GROUP + v % GROUP; };
   // heavier (later) query tiles first
   const int q0 = (gridDim.x - 1 - qb) * QTB;
   int qpv[VH];  // this lane's query position per virtual head
 #pragma unroll
-  for (int v = 0; v < VH; ++v) qpv[v] = q0 + 16 * (w * QS + v / GROUP) + c16;
+  for (int v = 0; v < VH; ++v) qpv[v] = q0 + 16 * (w * QS + v / GH) + c16;
 
   // Q^T operands (B of S^T = K Q^T): lane supplies Q[query c16][32 s + 8 gq + i]
   // (with rp.norm: the Q-RMSNorm and RoPE of each query first; the lane's
@@ -1079,7 +1087,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
 #pragma unroll
   for (int hh = 0; hh < VH; ++hh) {
     const int qrow = min(qpv[hh], T - 1);
-    const float* qsrc = qkv + (size_t)qrow * ld + (size_t)(g * GROUP + hh % GROUP) * D + 8 * gq;
+    const float* qsrc = qkv + (size_t)qrow * ld + (size_t)qhead(hh) * D + 8 * gq;
     float v[4][8];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
@@ -1300,7 +1308,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
 #pragma unroll
     for (int hh = 0; hh < VH; ++hh) {
       if (qpv[hh] < T) {
-        float* pp = part + (((size_t)blockIdx.z * T + qpv[hh]) * nq + g * GROUP + hh % GROUP) * (D + 4);
+        float* pp = part + (((size_t)blockIdx.z * T + qpv[hh]) * nq + qhead(hh)) * (D + 4);
 #pragma unroll
         for (int b = 0; b < D / 16; ++b)
           *reinterpret_cast<float4*>(pp + 16 * b + 4 * gq) =
@@ -1317,7 +1325,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(const float* 
   for (int hh = 0; hh < VH; ++hh) {
     if (qpv[hh] < T) {
       const float il = 1.f / lsum[hh];
-      const size_t o = (size_t)qpv[hh] * ldo + (size_t)(g * GROUP + hh % GROUP) * D + 4 * gq;
+      const size_t o = (size_t)qpv[hh] * ldo + (size_t)qhead(hh) * D + 4 * gq;
 #pragma unroll
       for (int b = 0; b < D / 16; ++b) {
         const float v[4] = {acc[hh][b][0] * il, acc[hh][b][1] * il, acc[hh][b][2] * il, acc[hh][b][3] * il};
@@ -2543,6 +2551,12 @@ hipError_t launch_attn_rows(const Dims& d, const AttnRows& args, int nsplit, hip
 
 int kv_split_pad(int T) { return (T + 63) / 64 * 64; }
 
+// GQA-2 prompts shorter than this take one query head per attention block
+// (512 tokens: 128 blocks in 2 key ranges instead of 64 in 4, whole prefill
+// 3.41 -> 3.29 ms; 1024 tokens: 256 blocks and no key-range split instead of
+// 128 in 2 ranges, even)
+constexpr int kOneQBelow = 2048;
+
 bool attn_prefill_uses_split(const Dims& d) {
   const int group = d.NQ / d.NKV;
   return d.D == fa::D && (group == 1 || group == 2);
@@ -2577,22 +2591,28 @@ hipError_t launch_attn_prefill(const Dims& d, const float* qkv, int T, float* ou
     // 256 run (at most 8 ranges of at least two tiles), partials merged
     // after; causal blocks also shorten their longest chain of key tiles
     // (the 1024-token prefill: 128 workgroups, 2 ranges, 6.6 -> 5.9 ms)
+    // GQA 2 below kOneQBelow positions: one query head per block
+    const bool oneq = group == 2 && T < kOneQBelow;
+    const int heads = oneq ? d.NQ : d.NKV;  // blocks along y
     int S = 1;
-    if (sk && nqb * d.NKV < 256) {
-      S = std::min(std::min(8, (256 + nqb * d.NKV - 1) / (nqb * d.NKV)), ntile / 2);
+    if (sk && nqb * heads < 256) {
+      S = std::min(std::min(8, (256 + nqb * heads - 1) / (nqb * heads)), ntile / 2);
       if (S < 2 || (size_t)S * T * d.NQ * (fa::D + 4) > sk->floats) S = 1;
     }
     float* part = S > 1 ? sk->P : nullptr;
-    dim3 grid(nqb, d.NKV, S);
+    dim3 grid(nqb, heads, S);
     if (group == 1 && !two)
-      attn_prefill_mfma_kernel<1, 1><<<grid, 256, 0, st>>>(qkv, T, d.qkv(), kv[0], kv[1], kv[2], kv[3], Tp, out,
-                                                           d.NQ * d.D, qs, out_hi, out_lo, causal ? 1 : 0, part, rp);
+      attn_prefill_mfma_kernel<1, 1, 0><<<grid, 256, 0, st>>>(qkv, T, d.qkv(), kv[0], kv[1], kv[2], kv[3], Tp, out,
+                                                              d.NQ * d.D, qs, out_hi, out_lo, causal ? 1 : 0, part, rp);
+    else if (oneq)
+      attn_prefill_mfma_kernel<2, 1, 1><<<grid, 256, 0, st>>>(qkv, T, d.qkv(), kv[0], kv[1], kv[2], kv[3], Tp, out,
+                                                              d.NQ * d.D, qs, out_hi, out_lo, causal ? 1 : 0, part, rp);
     else if (group == 2)
-      attn_prefill_mfma_kernel<2, 1><<<grid, 256, 0, st>>>(qkv, T, d.qkv(), kv[0], kv[1], kv[2], kv[3], Tp, out,
-                                                        d.NQ * d.D, qs, out_hi, out_lo, causal ? 1 : 0, part, rp);
+      attn_prefill_mfma_kernel<2, 1, 0><<<grid, 256, 0, st>>>(qkv, T, d.qkv(), kv[0], kv[1], kv[2], kv[3], Tp, out,
+                                                              d.NQ * d.D, qs, out_hi, out_lo, causal ? 1 : 0, part, rp);
     else
-      attn_prefill_mfma_kernel<1, 2><<<grid, 256, 0, st>>>(qkv, T, d.qkv(), kv[0], kv[1], kv[2], kv[3], Tp, out,
-                                                        d.NQ * d.D, qs, out_hi, out_lo, causal ? 1 : 0, part, rp);
+      attn_prefill_mfma_kernel<1, 2, 0><<<grid, 256, 0, st>>>(qkv, T, d.qkv(), kv[0], kv[1], kv[2], kv[3], Tp, out,
+                                                              d.NQ * d.D, qs, out_hi, out_lo, causal ? 1 : 0, part, rp);
     if (S > 1) {
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
