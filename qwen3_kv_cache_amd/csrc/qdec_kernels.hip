@@ -34,6 +34,19 @@ constexpr int kWave = 64;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
+// KV pages as global-address-space pointers. A pointer made from a page-table
+// entry is otherwise generic, and generic (flat) accesses count against the
+// LDS wait counter as well: every LDS read or cross-lane shuffle after them
+// would then also wait for the page loads and stores still in flight.
+typedef __attribute__((address_space(1))) float gfloat;
+typedef __attribute__((address_space(1))) f32x4_t gf32x4;
+__device__ __forceinline__ gfloat* page_at(const int64_t* table, int i) { return (gfloat*)table[i]; }
+__device__ __forceinline__ float4 gload4(const gfloat* p) {
+  const f32x4_t v = *(const gf32x4*)p;
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void gstore4(gfloat* p, float4 v) { *(gf32x4*)p = f32x4_t{v.x, v.y, v.z, v.w}; }
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 // float -> bf16 bits, round to nearest even (inputs here are finite).
@@ -300,10 +313,10 @@ __device__ __forceinline__ void qk_rope_row(float* __restrict__ qrow, int head, 
     if (!is_q) {
       const int kh = head - NQ;
       Dims d{L, 0, NQ, NKV, D, 0, 0, 0.f};
-      float* page = reinterpret_cast<float*>(page_table[pos / kPage]);
+      gfloat* page = page_at(page_table, pos / kPage);
       const int slot = pos % kPage;
-      float* kd = page + page_offset(d, layer, 0, kh, slot);
-      float* vd = page + page_offset(d, layer, 1, kh, slot);
+      gfloat* kd = page + page_offset(d, layer, 0, kh, slot);
+      gfloat* vd = page + page_offset(d, layer, 1, kh, slot);
       const float* vs = qrow + (size_t)(NQ + NKV + kh) * D;
       kd[lane] = ra;
       kd[lane + half] = rb;
@@ -363,15 +376,15 @@ __global__ __launch_bounds__(256) void qk_rope_append_vec_kernel(float* __restri
   if (!is_q) {
     const int kh = hd - NQ;
     Dims d{L, 0, NQ, NKV, D, 0, 0, 0.f};
-    float* page = reinterpret_cast<float*>(page_table[pos / kPage]);
+    gfloat* page = page_at(page_table, pos / kPage);
     const int slot = pos % kPage;
-    float* kd = page + page_offset(d, layer, 0, kh, slot);
-    float* vd = page + page_offset(d, layer, 1, kh, slot);
+    gfloat* kd = page + page_offset(d, layer, 0, kh, slot);
+    gfloat* vd = page + page_offset(d, layer, 1, kh, slot);
     const float* vs = rowp + (size_t)(NQ + NKV + kh) * D;
-    *reinterpret_cast<float4*>(kd + 4 * j) = ra4;
-    *reinterpret_cast<float4*>(kd + HALF + 4 * j) = rb4;
-    *reinterpret_cast<float4*>(vd + 4 * j) = *reinterpret_cast<const float4*>(vs + 4 * j);
-    *reinterpret_cast<float4*>(vd + HALF + 4 * j) = *reinterpret_cast<const float4*>(vs + HALF + 4 * j);
+    gstore4(kd + 4 * j, ra4);
+    gstore4(kd + HALF + 4 * j, rb4);
+    gstore4(vd + 4 * j, *reinterpret_cast<const float4*>(vs + 4 * j));
+    gstore4(vd + HALF + 4 * j, *reinterpret_cast<const float4*>(vs + HALF + 4 * j));
   }
 }
 
@@ -462,9 +475,9 @@ __global__ __launch_bounds__(512) void attn_small_kernel(const float* __restrict
         vl[t * D + pi] = v0[ps];
         vl[t * D + pi + HALF] = v1[ps];
         if (t >= q0) {
-          float* page = reinterpret_cast<float*>(page_table[t / kPage]);
-          float* kd = page + page_offset(d, layer, 0, g, t % kPage);
-          float* vd = page + page_offset(d, layer, 1, g, t % kPage);
+          gfloat* page = page_at(page_table, t / kPage);
+          gfloat* kd = page + page_offset(d, layer, 0, g, t % kPage);
+          gfloat* vd = page + page_offset(d, layer, 1, g, t % kPage);
           kd[pi] = r0;
           kd[pi + HALF] = r1;
           vd[pi] = v0[ps];
@@ -562,7 +575,7 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnRows a) {
   __shared__ float q_l[GROUP][D], k_l[D], v_l[D];
   __shared__ float sm_m[4][GROUP], sm_l[4][GROUP];
   __shared__ float sm_o[4][GROUP][D];
-  __shared__ const float* pg[kAttnChunk / kPage];
+  __shared__ const gfloat* pg[kAttnChunk / kPage];
   __shared__ int s_last;
   const int g = blockIdx.x, s = blockIdx.y, r = blockIdx.z, nsplit = gridDim.y;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
@@ -579,7 +592,7 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnRows a) {
   // the split's page pointers, so that each key load needs no dependent
   // global load first
   if (threadIdx.x < kAttnChunk / kPage && u0 < u1)
-    pg[threadIdx.x] = reinterpret_cast<const float*>(page_table[min(u0 / kPage + (int)threadIdx.x, (u1 - 1) / kPage)]);
+    pg[threadIdx.x] = page_at(page_table, min(u0 / kPage + (int)threadIdx.x, (u1 - 1) / kPage));
 
   // 1. QK-norm + RoPE: items 0..GROUP-1 are the query heads, GROUP the key head
   for (int it = wave; it <= GROUP; it += 4) {
@@ -609,9 +622,9 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnRows a) {
         v_l[lane] = v0;
         v_l[lane + HALF] = v1;
         if (has_cur) {
-          float* page = reinterpret_cast<float*>(page_table[pos / kPage]);
-          float* kd = page + page_offset(d, a.layer, 0, g, pos % kPage);
-          float* vd = page + page_offset(d, a.layer, 1, g, pos % kPage);
+          gfloat* page = page_at(page_table, pos / kPage);
+          gfloat* kd = page + page_offset(d, a.layer, 0, g, pos % kPage);
+          gfloat* vd = page + page_offset(d, a.layer, 1, g, pos % kPage);
           kd[lane] = r0;
           kd[lane + HALF] = r1;
           vd[lane] = v0;
@@ -627,12 +640,6 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnRows a) {
   for (int h = 0; h < GROUP; ++h)
 #pragma unroll
     for (int i = 0; i < DPL; ++i) qr[h][i] = q_l[h][part * DPL + i];
-  float kcur[DPL], vcur[DPL];
-#pragma unroll
-  for (int i = 0; i < DPL; ++i) {
-    kcur[i] = k_l[part * DPL + i];
-    vcur[i] = v_l[part * DPL + i];
-  }
 
   float m[GROUP], l[GROUP], acc[GROUP][DPL];
 #pragma unroll
@@ -647,31 +654,29 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnRows a) {
   // and are masked out; the key at pos comes from LDS
   auto load = [&](int base, float (&kv)[DPL], float (&vv)[DPL]) {
     const int u = min(base + slot, u1 - 1);
-    const float* page = pg[u / kPage - u0 / kPage];
-    const float* kp = page + page_offset(d, a.layer, 0, g, u % kPage) + part * DPL;
-    const float* vp = page + page_offset(d, a.layer, 1, g, u % kPage) + part * DPL;
+    const gfloat* page = pg[u / kPage - u0 / kPage];
+    const gfloat* kp = page + page_offset(d, a.layer, 0, g, u % kPage) + part * DPL;
+    const gfloat* vp = page + page_offset(d, a.layer, 1, g, u % kPage) + part * DPL;
 #pragma unroll
     for (int i = 0; i < DPL; i += 4) {
-      const float4 x = *reinterpret_cast<const float4*>(kp + i);
+      const float4 x = gload4(kp + i);
       kv[i] = x.x; kv[i + 1] = x.y; kv[i + 2] = x.z; kv[i + 3] = x.w;
-      const float4 y = *reinterpret_cast<const float4*>(vp + i);
+      const float4 y = gload4(vp + i);
       vv[i] = y.x; vv[i + 1] = y.y; vv[i + 2] = y.z; vv[i + 3] = y.w;
     }
   };
 
-  int base = u0 + wave * 8;
-  float kc[DPL], vc[DPL];
-  if (base < u1) load(base, kc, vc);
-  for (; base < u1; base += 32) {
-    float kn[DPL], vn[DPL];
-    load(base + 32, kn, vn);
+  // One step: the wave's 8 keys from base, already in (kc, vc).
+  auto step = [&](int base, float (&kc)[DPL], float (&vc)[DPL]) __attribute__((always_inline)) {
     const int u = base + slot;
     const bool valid = u < u1;
-    const bool cur = u == pos;
+    // the key at pos (its page store may not be visible yet) from LDS
+    if (base <= pos && pos < base + 8 && u == pos) {
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) {
-      kc[i] = cur ? kcur[i] : kc[i];
-      vc[i] = cur ? vcur[i] : vc[i];
+      for (int i = 0; i < DPL; ++i) {
+        kc[i] = k_l[part * DPL + i];
+        vc[i] = v_l[part * DPL + i];
+      }
     }
 #pragma unroll
     for (int h = 0; h < GROUP; ++h) {
@@ -696,10 +701,31 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnRows a) {
       for (int i = 0; i < DPL; ++i) acc[h][i] = fmaf(p, vc[i], acc[h][i] * alpha);
       m[h] = mn;
     }
+  };
+  // the wave's steps (at most kAttnChunk / 32) unrolled over two register
+  // sets, so the next step's loads stay in flight while the current one is
+  // used (a rolling copy from one set into the other would wait for them).
+  // The loads are unconditional (clamped keys) so that the wait before each
+  // step covers only that step's loads.
+  constexpr int NIT = kAttnChunk / 32;
+  const int b0 = u0 + wave * 8;
+  if (u0 < u1) {
+    float kA[DPL], vA[DPL], kB[DPL], vB[DPL];
+    load(b0, kA, vA);
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) {
-      kc[i] = kn[i];
-      vc[i] = vn[i];
+    for (int it = 0; it < NIT; ++it) {
+      const int base = b0 + 32 * it;
+      if (base >= u1) break;
+      // (the scheduler would otherwise sink the next loads below the step)
+      if (it % 2 == 0) {
+        if (it + 1 < NIT) load(base + 32, kB, vB);
+        __builtin_amdgcn_sched_barrier(0);
+        step(base, kA, vA);
+      } else {
+        if (it + 1 < NIT) load(base + 32, kA, vA);
+        __builtin_amdgcn_sched_barrier(0);
+        step(base, kB, vB);
+      }
     }
   }
   // sum the 8 key slots (same running max within the wave)
@@ -970,10 +996,10 @@ __global__ __launch_bounds__(256) void kv_split_kernel(const float* __restrict__
       k = make_float4(r[0], r[1], r[2], r[3]);
       if (t0 + tl < T) {
         Dims dd{rp.L, 0, NQ, NKV, D, 0, 0, 0.f};
-        float* page = reinterpret_cast<float*>(rp.page_table[pos / kPage]);
+        gfloat* page = page_at(rp.page_table, pos / kPage);
         const int slot = pos % kPage;
-        *reinterpret_cast<float4*>(page + page_offset(dd, rp.layer, 0, g, slot) + d0) = k;
-        *reinterpret_cast<float4*>(page + page_offset(dd, rp.layer, 1, g, slot) + d0) = v;
+        gstore4(page + page_offset(dd, rp.layer, 0, g, slot) + d0, k);
+        gstore4(page + page_offset(dd, rp.layer, 1, g, slot) + d0, v);
       }
     }
     vs[d0][tl] = v.x;
